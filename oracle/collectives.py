@@ -1,0 +1,267 @@
+"""CPU oracle of the ring reduce-scatter, all-gather and all-reduce.
+
+TEST INFRASTRUCTURE.  Only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run this module.  The HIP
+library never calls it, and it shares no code with the HIP library: no
+kernels, headers, helpers, tables or constants.  It is deliberately plain and
+slow: NumPy arrays, one Python loop per ring step, nothing blocked, fused or
+reordered beyond what the definitions state.
+
+Sources (web pages this follows):
+
+* [NC] NCCL 1.x ``src/reduce_scatter.cu`` (pytorch mirror, "Git at Google"):
+  the ``GetBlock`` schedule function, the reduce-scatter kernel's step 0
+  (copy own block to the next GPU), steps 1..W-2 (reduce received partial
+  with local input, pass on) and step W-1 (reduce into the output), and the
+  host launcher's 4-GPU block-vs-step table for ``userFromRing = {1,2,0,3}``.
+  Its op set is sum/prod/max/min and its ``recvcount`` is the per-rank output
+  length; the per-rank input is ``W * recvcount``.
+* [DP] "Distributed primitives" (notes): all-reduce is a reduction (sum, max
+  or average) followed by a broadcast; reduce-scatter reduces, then splits the
+  result so each node gets one segment; all-gather concatenates every node's
+  piece onto every node; Ring AllReduce = ReduceScatter + AllGather.
+* [SG] Apache SINGA ``src/io/communicator.cc``, ``fusedSynch``: tensors are
+  copied back to back into one fusion buffer, all-reduced, and copied out at
+  the same running offsets.  [HV] Horovod ``operations.cc``,
+  ``PerformOperation``: the same memcpy-in / all-reduce / memcpy-out on the
+  fused buffer.
+* [MX] "Add scatter reduce for JACCL#3901": a naive all-reduce is kept for
+  messages of at most 32 KB.
+
+Precision.  The pages fix it: the NCCL kernel reduces in the element type
+(``FuncSum<float>`` on ``float`` data), so fp32 is folded with fp32 IEEE
+round-to-nearest-even adds, one per ring step, and int32 with wrapping 32-bit
+adds.  bf16 data is widened exactly to fp32, folded in fp32 and rounded once
+to bf16 at the end (bf16 in, fp32 accumulate, bf16 out).
+
+Readings where the pages are silent (each listed again in the design doc):
+
+* ring = identity (``userFromRing[i] = i``): rank ``r`` is ring position ``r``;
+* the segment of a rank that does not divide evenly in an all-reduce is the
+  ceil split ``S = ceil(count / W)``, segment ``k = [min(kS,count), min((k+1)S,count))``;
+* max/min fold by compare-and-select, ``acc = x if x > acc else acc`` (``<``
+  for min): the earlier of two equal values (``+0``/``-0``) is kept, a NaN in
+  ``acc`` is kept, a later NaN is ignored;
+* ``avg`` = the sum fold, then one division by W in the accumulation type
+  (fp32 IEEE division; int32 division truncating toward zero);
+* bf16 rounding: round-to-nearest-even on the fp32 bits, NaN -> quiet NaN
+  with the sign kept (``sign | 0x7FC0``), overflow to +-inf as RNE gives;
+* the naive all-reduce folds in rank order 0..W-1;
+* fusion offsets are back to back in list order, with no padding.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+OPS = ("sum", "max", "min", "avg")
+DTYPES = ("f32", "bf16", "i32")
+
+# --------------------------------------------------------------- schedule ----
+
+
+def block_at_step(index: int, step: int, user_from_ring) -> int:
+    """Block that ring position ``index`` works on at ``step`` [NC ``GetBlock``].
+
+    The position ``index - 1 - step`` (mod W) of ``user_from_ring``: at the last
+    step a position holds its own block, and each earlier step holds the block
+    the next position will hold one step later.
+    """
+    w = len(user_from_ring)
+    return int(user_from_ring[(w + index - 1 - step) % w])
+
+
+def block_vs_step_table(user_from_ring) -> np.ndarray:
+    """Rows = steps 0..W-1, columns = ring positions 0..W-1 [NC host-launcher table]."""
+    w = len(user_from_ring)
+    return np.array([[block_at_step(i, s, user_from_ring) for i in range(w)]
+                     for s in range(w)], dtype=np.int64)
+
+
+def ring_fold_order(k: int, world: int) -> list[int]:
+    """Ranks whose inputs enter block ``k``, in the order the ring folds them.
+
+    Walk the schedule with the identity ring: at step 0 the position whose block
+    is ``k`` copies its input to the next position; at every later step the
+    position holding block ``k`` folds its own input into the partial it received.
+    """
+    ident = list(range(world))
+    order = []
+    for step in range(world):
+        holders = [i for i in range(world) if block_at_step(i, step, ident) == k]
+        assert len(holders) == 1
+        order.append(holders[0])
+    return order
+
+
+def naive_fold_order(world: int) -> list[int]:
+    """Rank order 0..W-1 for the naive (direct-sum) all-reduce [MX]."""
+    return list(range(world))
+
+
+def segment_bounds(count: int, world: int) -> list[tuple[int, int]]:
+    """All-reduce split of ``count`` elements into W segments (ceil split)."""
+    s = -(-count // world) if world > 0 else 0
+    return [(min(k * s, count), min((k + 1) * s, count)) for k in range(world)]
+
+
+# ------------------------------------------------------------- bf16 bits -----
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to fp32 exactly (they are the top 16 fp32 bits)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def f32_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 bit patterns, to nearest, ties to even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    keep_lsb = (u >> np.uint64(16)) & np.uint64(1)
+    out = ((u + np.uint64(0x7FFF) + keep_lsb) >> np.uint64(16)) & np.uint64(0xFFFF)
+    nan = np.isnan(x)
+    out[nan] = ((u[nan] >> np.uint64(16)) & np.uint64(0x8000)) | np.uint64(0x7FC0)
+    return out.astype(np.uint16)
+
+
+# ------------------------------------------------------------------ folds ----
+
+
+def _widen(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage -> accumulation type: bf16 bits -> fp32; fp32 and int32 as is."""
+    if dtype == "bf16":
+        return bf16_to_f32(x)
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32)
+    if dtype == "i32":
+        return np.asarray(x, dtype=np.int32)
+    raise ValueError(dtype)
+
+
+def _combine(op: str, acc: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """One ring step: partial received so far, combined with the local input."""
+    if op in ("sum", "avg"):
+        if acc.dtype == np.int32:  # two's-complement wrap, computed without overflow
+            return ((acc.astype(np.int64) + x.astype(np.int64)) & 0xFFFFFFFF).astype(np.uint32).view(np.int32)
+        return acc + x
+    if op == "max":
+        return np.where(x > acc, x, acc)
+    if op == "min":
+        return np.where(x < acc, x, acc)
+    raise ValueError(op)
+
+
+def _finish(op: str, acc: np.ndarray, world: int, dtype: str) -> np.ndarray:
+    """Average (if asked) in the accumulation type, then back to the storage type."""
+    if op == "avg":
+        if acc.dtype == np.int32:
+            a = acc.astype(np.int64)
+            acc = (np.sign(a) * (np.abs(a) // world)).astype(np.int32)
+        else:
+            acc = (acc / np.float32(world)).astype(np.float32)
+    if dtype == "bf16":
+        return f32_to_bf16(acc)
+    return acc
+
+
+def fold(inputs, order, op: str, dtype: str, lo: int = 0, hi: int | None = None) -> np.ndarray:
+    """Fold ``inputs[order[0]][lo:hi]``, then each later rank of ``order``, then finish."""
+    if op not in OPS:
+        raise ValueError(f"op {op!r}")
+    hi = len(inputs[0]) if hi is None else hi
+    acc = _widen(inputs[order[0]][lo:hi], dtype).copy()
+    for r in order[1:]:
+        acc = _combine(op, acc, _widen(inputs[r][lo:hi], dtype))
+    return _finish(op, acc, len(inputs), dtype)
+
+
+# ------------------------------------------------------------ collectives ----
+
+
+def reduce_scatter(inputs, op: str = "sum", dtype: str = "f32") -> list[np.ndarray]:
+    """Reduce-scatter: rank ``k`` receives block ``k`` of the reduction [NC, DP].
+
+    Every rank holds ``N = W * recvcount`` elements; block ``k`` is elements
+    ``[k*recvcount, (k+1)*recvcount)`` of every rank, folded in ring order.
+    """
+    w = len(inputs)
+    n = len(inputs[0])
+    if any(len(x) != n for x in inputs):
+        raise ValueError("ranks differ in length")
+    if n % w:
+        raise ValueError("reduce-scatter needs a per-rank length divisible by W")
+    s = n // w
+    return [fold(inputs, ring_fold_order(k, w), op, dtype, k * s, (k + 1) * s)
+            for k in range(w)]
+
+
+def all_gather(segments) -> list[np.ndarray]:
+    """All-gather: every rank receives the concatenation of all ranks' pieces [DP]."""
+    full = np.concatenate([np.asarray(s) for s in segments])
+    return [full.copy() for _ in segments]
+
+
+def all_reduce(inputs, op: str = "sum", dtype: str = "f32") -> list[np.ndarray]:
+    """Ring all-reduce = reduce-scatter, then all-gather [DP *In practice*].
+
+    Segment ``k`` of the ceil split is folded in ring order from rank
+    ``(k+1) % W`` round to rank ``k``; every rank then receives all segments.
+    """
+    w = len(inputs)
+    n = len(inputs[0])
+    segs = [fold(inputs, ring_fold_order(k, w), op, dtype, lo, hi)
+            for k, (lo, hi) in enumerate(segment_bounds(n, w))]
+    return all_gather(segs)
+
+
+def naive_all_reduce(inputs, op: str = "sum", dtype: str = "f32") -> list[np.ndarray]:
+    """Naive all-reduce: every element folded in rank order, result on every rank [MX]."""
+    out = fold(inputs, naive_fold_order(len(inputs)), op, dtype)
+    return [out.copy() for _ in inputs]
+
+
+def bucketed_all_reduce(inputs, bucket: int, op: str = "sum", dtype: str = "f32") -> list[np.ndarray]:
+    """All-reduce of consecutive buckets of ``bucket`` elements, one after another.
+
+    Each bucket is an all-reduce of its own, with its own segments ["Distributed
+    primitives", bucketed ring all-reduce].
+    """
+    n = len(inputs[0])
+    outs = [np.empty_like(np.asarray(x)) for x in inputs]
+    start = 0
+    while start < n:
+        stop = min(start + bucket, n)
+        part = all_reduce([x[start:stop] for x in inputs], op, dtype)
+        for r in range(len(inputs)):
+            outs[r][start:stop] = part[r]
+        start = stop
+    return outs
+
+
+# ------------------------------------------------------------------ fusion ---
+
+
+def fuse_offsets(counts) -> list[int]:
+    """Element offset of each tensor in the fusion buffer: running sum, no padding [SG, HV]."""
+    offs, run = [], 0
+    for c in counts:
+        offs.append(run)
+        run += int(c)
+    return offs
+
+
+def fuse_pack(tensors) -> np.ndarray:
+    """Copy tensors back to back, in list order, into one buffer [SG ``fusedSynch``]."""
+    return np.concatenate([np.asarray(t).ravel() for t in tensors]) if len(tensors) else np.empty(0)
+
+
+def fuse_unpack(fused: np.ndarray, counts) -> list[np.ndarray]:
+    """Split a fusion buffer back into tensors of ``counts`` elements at the same offsets."""
+    return [np.asarray(fused)[o:o + int(c)].copy() for o, c in zip(fuse_offsets(counts), counts)]
+
+
+def fused_all_reduce(tensors_per_rank, op: str = "sum", dtype: str = "f32") -> list[list[np.ndarray]]:
+    """pack -> all-reduce of the fusion buffers -> unpack, per rank [HV ``PerformOperation``]."""
+    counts = [len(t) for t in tensors_per_rank[0]]
+    fused = [fuse_pack(ts) for ts in tensors_per_rank]
+    red = all_reduce(fused, op, dtype)
+    return [fuse_unpack(f, counts) for f in red]
