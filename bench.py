@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""Reduce-scatter throughput on one MI355X: effective HBM GB/s and % of peak.
+
+Workload: reduce-scatter sum, fp32, W = 8 virtual ranks of 67,108,864
+elements (256 MiB) each, N(0, 1e-3) from per-rank seeds; each block of
+8,388,608 elements folded in ring order (k+1)%8, ..., k.  One step = one
+reduce-scatter launch over inputs already resident in HBM.
+
+Effective bytes per step = every input read once + every output written once
+= 8 * 256 MiB + 8 * 32 MiB = 2,415,919,104 B.  Peak HBM3E bandwidth of the
+MI355X: 8 TB/s.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_reduce_scatter_w8_64Mi_f32.json")
+KERNEL_SOURCES = ("fold_impl.h", "fold_f32.hip", "rsx_internal.h")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "collective_reduction_ring_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if the
+    kernel sources are unchanged since they were taken; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(xs, reps_budget_s: float):
+    """Time the oracle on the host (single-threaded NumPy) over the same workload."""
+    import numpy as np  # noqa: F401
+
+    import oracle
+
+    times, out = [], None
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        out = oracle.reduce_scatter(xs, "sum", "f32")
+        times.append(time.perf_counter() - t0)
+        log(f"oracle pass {len(times)}: {times[-1]:.2f} s")
+        if time.perf_counter() - t_start >= reps_budget_s or len(times) >= 20:
+            break
+    return out, statistics.median(times), len(times)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="host time budget of the oracle baseline (whole passes)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        log(f"bench.py measures one GPU only: the W ranks are buffers of a single MI355X; "
+            f"--gpus {args.gpus} is not supported")
+        return 2
+
+    import numpy as np
+    import torch
+
+    sys.path.insert(0, ROOT)
+    import collective_reduction_ring_amd as rsx
+    from collective_reduction_ring_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 2
+
+    w = wl.WORKLOADS[2]
+    world, n = w.world, w.n
+    seg = n // world
+    bytes_per_step = world * n * 4 + world * seg * 4
+
+    log(f"generating inputs: W={world}, {n} fp32 per rank")
+    xs = wl.rank_inputs(2)
+    dev = [torch.from_numpy(x).to("cuda:0") for x in xs]
+    out = [torch.empty(seg, dtype=torch.float32, device="cuda:0") for _ in range(world)]
+    plan = rsx.ReduceScatter(dev, out, "sum")
+    stream = torch.cuda.current_stream()
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        plan()
+    torch.cuda.synchronize()
+
+    k = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(k)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(k)]
+    log(f"timing {k} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(k):
+        starts[i].record(stream)
+        plan()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    elapsed = t1 - t0
+    avg_launch_s = statistics.mean(launch_ms) / 1e3
+    value = bytes_per_step * k / elapsed / 1e9
+    achieved = bytes_per_step / avg_launch_s / 1e9
+    log(f"wall {elapsed * 1e3 / k:.1f} us/step ({value:.0f} GB/s); kernel avg "
+        f"{avg_launch_s * 1e6:.1f} us, median {statistics.median(launch_ms) * 1e3:.1f} us, "
+        f"min {min(launch_ms) * 1e3:.1f} us ({achieved:.0f} GB/s)")
+
+    got = [o.cpu().numpy() for o in out]
+    del dev
+
+    result = {
+        "metric": "reduce-scatter effective HBM GB/s (W=8, 64Mi fp32/rank)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": k,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / k, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: N(0, 1e-3) fp32, numpy default_rng((2, rank)) per rank",
+        "config": {
+            "workload": "reduce_scatter sum fp32, W=8 virtual ranks, 67,108,864 elements/rank, "
+                        "ring order",
+            "world": world,
+            "elements_per_rank": n,
+            "recvcount": seg,
+            "bytes_per_step": bytes_per_step,
+            "parallelism": "one GPU; W ranks = W HBM buffers",
+        },
+        "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": recorded_traffic(),
+            "kernel": "rsx::fold_kernel<F32T, RSX_SUM, 8, rs, dwordx4>",
+            "avg_launch_us": round(avg_launch_s * 1e6, 2),
+            "algorithmic_bytes_per_launch": bytes_per_step,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        log(f"oracle baseline on the host, ~{args.cpu_seconds:.0f} s")
+        want, t_med, reps = cpu_baseline(xs, args.cpu_seconds)
+        result["cpu_baseline"] = {
+            "value": round(bytes_per_step / t_med / 1e9, 3),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"the whole workload (one reduce-scatter of 8 x 67,108,864 fp32), "
+                      f"{reps} passes, median {t_med:.2f} s; single-threaded NumPy",
+        }
+        bad = sum(int(np.count_nonzero(g.view(np.uint32) != o.view(np.uint32)))
+                  for g, o in zip(got, want))
+        result["parity"] = {"checked_elements": int(sum(g.size for g in got)),
+                            "mismatches": bad, "rule": "bit-exact fp32"}
+        if bad:
+            log(f"PARITY FAILURE: {bad} elements differ from the oracle")
+    print(json.dumps(result), flush=True)
+    return 1 if result.get("parity", {}).get("mismatches") else 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

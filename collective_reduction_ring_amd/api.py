@@ -1,0 +1,212 @@
+"""PyTorch-facing wrappers of librsx: lists of device tensors in, kernels out.
+
+PyTorch supplies device memory and the current HIP stream; every element is
+computed by the library's HIP kernels.  The wrappers check what the C ABI
+cannot see (tensor sizes, dtypes, devices, contiguity) so that a wrong shape
+is a Python error and never an out-of-bounds kernel access, then pass raw
+pointers and counts.
+
+Semantics (see include/rsx.h): W virtual ranks are W tensors on one GPU.
+``reduce_scatter`` folds block k of every rank in ring order (k+1)%W, ..., k
+(NCCL 1.x ring reduce-scatter, GetBlock); ``all_reduce`` is reduce-scatter then
+all-gather ("Distributed primitives", Ring AllReduce) in one pass.
+"""
+from __future__ import annotations
+
+from typing import Sequence
+
+import torch
+
+from . import _lib as L
+
+DTYPES = {torch.float32: L.RSX_FLOAT32, torch.bfloat16: L.RSX_BFLOAT16, torch.int32: L.RSX_INT32}
+OPS = {"sum": L.RSX_SUM, "max": L.RSX_MAX, "min": L.RSX_MIN, "avg": L.RSX_AVG}
+ALGOS = {"ring": L.RSX_ALGO_RING, "naive": L.RSX_ALGO_NAIVE, "auto": L.RSX_ALGO_AUTO}
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(ts: Sequence[torch.Tensor], numel: int, what: str, dtype=None, device=None):
+    for i, t in enumerate(ts):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{what}[{i}] is not a tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{what}[{i}] is not on a GPU")
+        if device is not None and t.device != device:
+            raise ValueError(f"{what}[{i}] is on {t.device}, expected {device}")
+        if dtype is not None and t.dtype != dtype:
+            raise ValueError(f"{what}[{i}] has dtype {t.dtype}, expected {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{what}[{i}] is not contiguous")
+        if t.numel() != numel:
+            raise ValueError(f"{what}[{i}] has {t.numel()} elements, expected {numel}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return DTYPES[t.dtype]
+    except KeyError:
+        raise ValueError(f"unsupported dtype {t.dtype}; use float32, bfloat16 or int32") from None
+
+
+def _op_code(op: str) -> int:
+    try:
+        return OPS[op]
+    except KeyError:
+        raise ValueError(f"unknown op {op!r}; one of {sorted(OPS)}") from None
+
+
+def _ranks(inputs) -> int:
+    w = len(inputs)
+    if not 1 <= w <= L.RSX_MAX_RANKS:
+        raise ValueError(f"need 1..{L.RSX_MAX_RANKS} ranks, got {w}")
+    return w
+
+
+class ReduceScatter:
+    """A prepared reduce-scatter over fixed tensors; calling it enqueues one launch.
+
+    ``inputs[r]`` has W*recvcount elements, ``outputs[k]`` recvcount.
+    """
+
+    def __init__(self, inputs, outputs, op: str = "sum"):
+        w = _ranks(inputs)
+        if len(outputs) != w:
+            raise ValueError("need one output per rank")
+        recvcount = outputs[0].numel()
+        dev, dt = inputs[0].device, inputs[0].dtype
+        _check(inputs, w * recvcount, "inputs", dt, dev)
+        _check(outputs, recvcount, "outputs", dt, dev)
+        self.device = dev
+        self.args = (L.ptr_array([t.data_ptr() for t in inputs]),
+                     L.ptr_array([t.data_ptr() for t in outputs]),
+                     w, recvcount, _dtype_code(inputs[0]), _op_code(op))
+        self.fn = L.lib().rsx_reduce_scatter
+        self.keep = (list(inputs), list(outputs))
+
+    def __call__(self, stream=None) -> None:
+        with torch.cuda.device(self.device):
+            L.check("rsx_reduce_scatter", self.fn(*self.args, _stream_handle(stream)))
+
+
+class AllReduce:
+    """A prepared all-reduce (``algo`` ring / naive / auto); every tensor has ``count`` elements."""
+
+    def __init__(self, inputs, outputs=None, op: str = "sum", algo: str = "ring"):
+        w = _ranks(inputs)
+        outputs = inputs if outputs is None else outputs
+        if len(outputs) != w:
+            raise ValueError("need one output per rank")
+        count = inputs[0].numel()
+        dev, dt = inputs[0].device, inputs[0].dtype
+        _check(inputs, count, "inputs", dt, dev)
+        _check(outputs, count, "outputs", dt, dev)
+        if algo not in ALGOS:
+            raise ValueError(f"unknown algo {algo!r}")
+        self.device = dev
+        self.args = (L.ptr_array([t.data_ptr() for t in inputs]),
+                     L.ptr_array([t.data_ptr() for t in outputs]),
+                     w, count, _dtype_code(inputs[0]), _op_code(op), ALGOS[algo])
+        self.fn = L.lib().rsx_all_reduce
+        self.keep = (list(inputs), list(outputs))
+
+    def __call__(self, stream=None) -> None:
+        with torch.cuda.device(self.device):
+            L.check("rsx_all_reduce", self.fn(*self.args, _stream_handle(stream)))
+
+
+def reduce_scatter(inputs, outputs, op: str = "sum", stream=None) -> None:
+    """Reduce-scatter ``inputs`` (W tensors of W*n) into ``outputs`` (W tensors of n)."""
+    ReduceScatter(inputs, outputs, op)(stream)
+
+
+def all_gather(inputs, outputs, stream=None) -> None:
+    """All-gather: ``outputs[r][k*n:(k+1)*n] = inputs[k]`` for every r, k."""
+    w = _ranks(inputs)
+    if len(outputs) != w:
+        raise ValueError("need one output per rank")
+    n = inputs[0].numel()
+    dev, dt = inputs[0].device, inputs[0].dtype
+    _check(inputs, n, "inputs", dt, dev)
+    _check(outputs, w * n, "outputs", dt, dev)
+    with torch.cuda.device(dev):
+        st = L.lib().rsx_all_gather(L.ptr_array([t.data_ptr() for t in inputs]),
+                                    L.ptr_array([t.data_ptr() for t in outputs]),
+                                    w, n, _dtype_code(inputs[0]), _stream_handle(stream))
+    L.check("rsx_all_gather", st)
+
+
+def all_reduce(inputs, outputs=None, op: str = "sum", algo: str = "ring", stream=None) -> None:
+    """All-reduce; ``outputs=None`` reduces in place."""
+    AllReduce(inputs, outputs, op, algo)(stream)
+
+
+def all_reduce_bucketed(inputs, outputs=None, bucket_elems: int = 13_107_200, op: str = "sum",
+                        algo: str = "ring", stream=None) -> None:
+    """All-reduce consecutive buckets of ``bucket_elems`` elements, one launch per bucket,
+    in order on one stream ("Distributed primitives", bucketed ring all-reduce).
+
+    Each bucket is an all-reduce of its own with its own segment split.
+    """
+    outputs = inputs if outputs is None else outputs
+    n = inputs[0].numel()
+    if bucket_elems <= 0:
+        raise ValueError("bucket_elems must be positive")
+    for start in range(0, n, bucket_elems):
+        stop = min(start + bucket_elems, n)
+        AllReduce([t[start:stop] for t in inputs], [t[start:stop] for t in outputs], op, algo)(stream)
+
+
+def fuse_pack(tensors, fused: torch.Tensor, stream=None) -> None:
+    """Copy ``tensors`` back to back into ``fused`` (SINGA fusedSynch / Horovod memcpy in)."""
+    counts = [t.numel() for t in tensors]
+    _check([fused], sum(counts), "fused", None, None)
+    for i, t in enumerate(tensors):
+        _check([t], counts[i], f"tensors[{i}]", fused.dtype, fused.device)
+    with torch.cuda.device(fused.device):
+        st = L.lib().rsx_fuse_pack(L.ptr_array([t.data_ptr() for t in tensors]),
+                                   L.size_array(counts), len(tensors), fused.data_ptr(),
+                                   _dtype_code(fused), _stream_handle(stream))
+    L.check("rsx_fuse_pack", st)
+
+
+def fuse_unpack(fused: torch.Tensor, tensors, stream=None) -> None:
+    """Copy ``fused`` back out into ``tensors`` at the same running offsets."""
+    counts = [t.numel() for t in tensors]
+    _check([fused], sum(counts), "fused", None, None)
+    for i, t in enumerate(tensors):
+        _check([t], counts[i], f"tensors[{i}]", fused.dtype, fused.device)
+    with torch.cuda.device(fused.device):
+        st = L.lib().rsx_fuse_unpack(fused.data_ptr(), L.ptr_array([t.data_ptr() for t in tensors]),
+                                     L.size_array(counts), len(tensors), _dtype_code(fused),
+                                     _stream_handle(stream))
+    L.check("rsx_fuse_unpack", st)
+
+
+def fused_all_reduce(tensors_per_rank, fused_per_rank, outputs_per_rank=None, op: str = "sum",
+                     algo: str = "ring", stream=None) -> None:
+    """pack -> in-place all-reduce of the fusion buffers -> unpack (Horovod PerformOperation).
+
+    ``outputs_per_rank=None`` writes the results back into the input tensors.
+    """
+    outputs_per_rank = tensors_per_rank if outputs_per_rank is None else outputs_per_rank
+    for ts, f in zip(tensors_per_rank, fused_per_rank):
+        fuse_pack(ts, f, stream)
+    all_reduce(list(fused_per_rank), None, op, algo, stream)
+    for f, ts in zip(fused_per_rank, outputs_per_rank):
+        fuse_unpack(f, ts, stream)
+
+
+def segment_begin(count: int, nranks: int, k: int) -> int:
+    """First element of segment k of a ring all-reduce of ``count`` elements."""
+    return int(L.lib().rsx_segment_begin(count, nranks, k))
+
+
+def version() -> int:
+    return int(L.lib().rsx_version())

@@ -1,0 +1,11 @@
+// Fold kernels instantiated for one element type (see fold_impl.h).
+#include "fold_impl.h"
+
+namespace rsx {
+
+hipError_t launch_fold_i32(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid,
+                         hipStream_t s) {
+  return launch_fold<I32T>(op, world, rs, vec, a, grid, s);
+}
+
+}  // namespace rsx

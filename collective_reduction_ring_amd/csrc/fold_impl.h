@@ -1,0 +1,314 @@
+// Ring-order fold kernels: reduce-scatter, all-reduce (reduce-scatter and
+// all-gather in one pass) and the naive all-reduce, for one element type.
+//
+// What is computed (NCCL 1.x src/reduce_scatter.cu, the ring kernel and
+// GetBlock; "Distributed primitives", Ring AllReduce): block k of the result
+// is the fold of every rank's block k, starting from the rank after k and
+// going round the ring to rank k.  On W GPUs that fold is spread over W steps,
+// each GPU adding its own input to the partial it received and passing it on.
+// Here the W ranks are W buffers of one GPU, so a lane loads element i of
+// block k from all W buffers and folds them in registers in the same order:
+// the partial never leaves the register file, the flags and the staging
+// buffers of the multi-GPU kernel have nothing left to guard, and HBM sees
+// each input once and each output once.
+//
+// Layout of one launch: grid.y = segment k (uniform per workgroup, so the
+// ring rotation and the W source pointers are scalar), grid.x = tile of
+// U * 256 dwordx4 (or elements, for the unaligned kernel) within segment k.
+// A lane issues all W*U loads before the first combine.
+#pragma once
+
+#include "rsx_internal.h"
+
+namespace rsx {
+
+// ------------------------------------------------------------ element types
+
+struct F32T {
+  using S = float;   // storage
+  using A = float;   // accumulation
+  static constexpr int kVL = 4;  // elements per dwordx4
+};
+struct I32T {
+  using S = int32_t;
+  using A = int32_t;
+  static constexpr int kVL = 4;
+};
+struct BF16T {
+  using S = uint16_t;
+  using A = float;
+  static constexpr int kVL = 8;
+};
+
+// bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 bits.
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even; a NaN becomes the quiet NaN
+// with the sign kept.  Overflow goes to +-inf, as the rounding rule gives.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <class D>
+struct Elem;
+
+template <>
+struct Elem<F32T> {
+  __device__ static float widen(float x) { return x; }
+  __device__ static float narrow(float a) { return a; }
+  __device__ static void unpack(const uint4& v, float (&a)[4]) {
+    a[0] = __uint_as_float(v.x);
+    a[1] = __uint_as_float(v.y);
+    a[2] = __uint_as_float(v.z);
+    a[3] = __uint_as_float(v.w);
+  }
+  __device__ static uint4 pack(const float (&a)[4]) {
+    return make_uint4(__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]),
+                      __float_as_uint(a[3]));
+  }
+};
+
+template <>
+struct Elem<I32T> {
+  __device__ static int32_t widen(int32_t x) { return x; }
+  __device__ static int32_t narrow(int32_t a) { return a; }
+  __device__ static void unpack(const uint4& v, int32_t (&a)[4]) {
+    a[0] = static_cast<int32_t>(v.x);
+    a[1] = static_cast<int32_t>(v.y);
+    a[2] = static_cast<int32_t>(v.z);
+    a[3] = static_cast<int32_t>(v.w);
+  }
+  __device__ static uint4 pack(const int32_t (&a)[4]) {
+    return make_uint4(static_cast<uint32_t>(a[0]), static_cast<uint32_t>(a[1]),
+                      static_cast<uint32_t>(a[2]), static_cast<uint32_t>(a[3]));
+  }
+};
+
+template <>
+struct Elem<BF16T> {
+  __device__ static float widen(uint16_t h) { return bf16_bits_to_f32(h); }
+  __device__ static uint16_t narrow(float a) { return static_cast<uint16_t>(f32_to_bf16_bits(a)); }
+  __device__ static void unpack_word(uint32_t w, float& lo, float& hi) {
+    lo = __uint_as_float(w << 16);
+    hi = __uint_as_float(w & 0xffff0000u);
+  }
+  __device__ static void unpack(const uint4& v, float (&a)[8]) {
+    unpack_word(v.x, a[0], a[1]);
+    unpack_word(v.y, a[2], a[3]);
+    unpack_word(v.z, a[4], a[5]);
+    unpack_word(v.w, a[6], a[7]);
+  }
+  __device__ static uint32_t pack_word(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  }
+  __device__ static uint4 pack(const float (&a)[8]) {
+    return make_uint4(pack_word(a[0], a[1]), pack_word(a[2], a[3]), pack_word(a[4], a[5]),
+                      pack_word(a[6], a[7]));
+  }
+};
+
+// ------------------------------------------------------------------- ops
+
+__device__ __forceinline__ float add_op(float a, float b) { return a + b; }
+__device__ __forceinline__ int32_t add_op(int32_t a, int32_t b) {
+  return static_cast<int32_t>(static_cast<uint32_t>(a) + static_cast<uint32_t>(b));
+}
+
+// One ring step: the partial folded so far, combined with the next rank's value.
+// max/min keep the partial unless the new value compares strictly greater /
+// smaller (a compare and a select, never a hardware max/min instruction, so
+// +-0 ties and NaNs follow the fold order).
+template <int OP, class A>
+__device__ __forceinline__ A combine(A acc, A x) {
+  if constexpr (OP == RSX_MAX) {
+    return (x > acc) ? x : acc;
+  } else if constexpr (OP == RSX_MIN) {
+    return (x < acc) ? x : acc;
+  } else {
+    return add_op(acc, x);
+  }
+}
+
+// avg: one division by W in the accumulation type (int32 truncates toward zero).
+template <int OP, int W, class A>
+__device__ __forceinline__ A finish(A acc) {
+  if constexpr (OP == RSX_AVG) {
+    return acc / static_cast<A>(W);
+  } else {
+    return acc;
+  }
+}
+
+// ------------------------------------------------------------------ kernel
+
+template <class D, int OP, int W, bool RS, bool VEC>
+__global__ __launch_bounds__(kBlock) void fold_kernel(const FoldArgs a) {
+  using S = typename D::S;
+  using A = typename D::A;
+  constexpr int U = fold_units(W);
+  constexpr int VL = D::kVL;
+
+  const uint32_t k = blockIdx.y;
+  const uint64_t b = min(static_cast<uint64_t>(k) * a.seg, a.count);
+  const uint64_t e = min(b + a.seg, a.count);
+
+  // Ring rotation: source j of segment k is rank (k + rot + j) mod W.
+  uint32_t first = (k + a.rot) % W;
+  const S* src[W];
+#pragma unroll
+  for (int j = 0; j < W; ++j) {
+    uint32_t r = first + j;
+    if (r >= static_cast<uint32_t>(W)) r -= W;
+    src[j] = static_cast<const S*>(a.src[r]);
+  }
+
+  // Fold and store one element (head, tail and the unaligned kernel).
+  auto fold_element = [&](uint64_t idx) {
+    S x[W];
+#pragma unroll
+    for (int j = 0; j < W; ++j) x[j] = src[j][idx];
+    A acc = Elem<D>::widen(x[0]);
+#pragma unroll
+    for (int j = 1; j < W; ++j) acc = combine<OP>(acc, Elem<D>::widen(x[j]));
+    const S out = Elem<D>::narrow(finish<OP, W>(acc));
+    if constexpr (RS) {
+      static_cast<S*>(a.dst[k])[idx - b] = out;
+    } else {
+#pragma unroll
+      for (int r = 0; r < W; ++r) static_cast<S*>(a.dst[r])[idx] = out;
+    }
+  };
+
+  const uint32_t tid = threadIdx.x;
+
+  if constexpr (VEC) {
+    // Body: whole dwordx4 vectors of [b, e).  All base pointers are 16-byte
+    // aligned (checked on the host), so element offsets divisible by VL are
+    // too.  Reduce-scatter segments start at such an offset (host check);
+    // all-reduce segments may not, and take a scalar head and tail.
+    const uint64_t hb = min((b + VL - 1) / VL * VL, e);
+    const uint64_t be = max(hb, e / VL * VL);
+    const uint64_t nv = (be - hb) / VL;
+    const uint64_t v0 = static_cast<uint64_t>(blockIdx.x) * (U * kBlock);
+    if (v0 < nv) {
+      const bool full = v0 + U * kBlock <= nv;
+      uint4 v[W][U];
+#pragma unroll
+      for (int j = 0; j < W; ++j) {
+        const uint4* p = reinterpret_cast<const uint4*>(src[j] + hb) + v0 + tid;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (full || v0 + u * kBlock + tid < nv) v[j][u] = p[u * kBlock];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint64_t vi = v0 + u * kBlock + tid;
+        if (!full && vi >= nv) continue;
+        A acc[VL];
+        Elem<D>::unpack(v[0][u], acc);
+#pragma unroll
+        for (int j = 1; j < W; ++j) {
+          A x[VL];
+          Elem<D>::unpack(v[j][u], x);
+#pragma unroll
+          for (int l = 0; l < VL; ++l) acc[l] = combine<OP>(acc[l], x[l]);
+        }
+#pragma unroll
+        for (int l = 0; l < VL; ++l) acc[l] = finish<OP, W>(acc[l]);
+        const uint4 o = Elem<D>::pack(acc);
+        if constexpr (RS) {
+          reinterpret_cast<uint4*>(static_cast<S*>(a.dst[k]) + (hb - b))[vi] = o;
+        } else {
+#pragma unroll
+          for (int r = 0; r < W; ++r) reinterpret_cast<uint4*>(static_cast<S*>(a.dst[r]) + hb)[vi] = o;
+        }
+      }
+    }
+    if (blockIdx.x == 0) {
+      const uint32_t nh = static_cast<uint32_t>(hb - b);
+      const uint32_t nt = static_cast<uint32_t>(e - be);
+      if (tid < nh) {
+        fold_element(b + tid);
+      } else if (tid < nh + nt) {
+        fold_element(be + (tid - nh));
+      }
+    }
+  } else {
+    // Unaligned kernel: one element per lane per unit, still coalesced.
+    const uint64_t t0 = b + static_cast<uint64_t>(blockIdx.x) * (U * kBlock);
+    if (t0 >= e) return;
+    const bool full = t0 + U * kBlock <= e;
+    S x[W][U];
+#pragma unroll
+    for (int j = 0; j < W; ++j)
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (full || t0 + u * kBlock + tid < e) x[j][u] = src[j][t0 + u * kBlock + tid];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t idx = t0 + u * kBlock + tid;
+      if (!full && idx >= e) continue;
+      A acc = Elem<D>::widen(x[0][u]);
+#pragma unroll
+      for (int j = 1; j < W; ++j) acc = combine<OP>(acc, Elem<D>::widen(x[j][u]));
+      const S out = Elem<D>::narrow(finish<OP, W>(acc));
+      if constexpr (RS) {
+        static_cast<S*>(a.dst[k])[idx - b] = out;
+      } else {
+#pragma unroll
+        for (int r = 0; r < W; ++r) static_cast<S*>(a.dst[r])[idx] = out;
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------- dispatch
+
+template <class D, int OP, int W>
+hipError_t launch_world(bool rs, bool vec, const FoldArgs& a, dim3 grid, hipStream_t s) {
+  void* args[] = {const_cast<FoldArgs*>(&a)};
+  const void* fn;
+  if (rs) {
+    fn = vec ? reinterpret_cast<const void*>(&fold_kernel<D, OP, W, true, true>)
+             : reinterpret_cast<const void*>(&fold_kernel<D, OP, W, true, false>);
+  } else {
+    fn = vec ? reinterpret_cast<const void*>(&fold_kernel<D, OP, W, false, true>)
+             : reinterpret_cast<const void*>(&fold_kernel<D, OP, W, false, false>);
+  }
+  return hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, s);
+}
+
+template <class D, int OP>
+hipError_t launch_op(int world, bool rs, bool vec, const FoldArgs& a, dim3 grid, hipStream_t s) {
+  switch (world) {
+#define RSX_W(n) \
+  case n:        \
+    return launch_world<D, OP, n>(rs, vec, a, grid, s);
+    RSX_W(1) RSX_W(2) RSX_W(3) RSX_W(4) RSX_W(5) RSX_W(6) RSX_W(7) RSX_W(8)
+    RSX_W(9) RSX_W(10) RSX_W(11) RSX_W(12) RSX_W(13) RSX_W(14) RSX_W(15) RSX_W(16)
+#undef RSX_W
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+template <class D>
+hipError_t launch_fold(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid,
+                       hipStream_t s) {
+  switch (op) {
+    case RSX_SUM:
+      return launch_op<D, RSX_SUM>(world, rs, vec, a, grid, s);
+    case RSX_MAX:
+      return launch_op<D, RSX_MAX>(world, rs, vec, a, grid, s);
+    case RSX_MIN:
+      return launch_op<D, RSX_MIN>(world, rs, vec, a, grid, s);
+    case RSX_AVG:
+      return launch_op<D, RSX_AVG>(world, rs, vec, a, grid, s);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace rsx

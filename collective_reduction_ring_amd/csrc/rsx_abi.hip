@@ -1,0 +1,381 @@
+// C ABI of librsx.so (declared in include/rsx.h): argument validation,
+// aliasing rules, launch geometry and dispatch to the kernel launchers.
+//
+// Every check runs before the first HIP call, so a rejected call has no side
+// effect and the error paths can be exercised on a machine without a GPU.
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "rsx_internal.h"
+
+namespace rsx {
+namespace {
+
+thread_local char g_hip_error[256] = "HIP error";
+
+rsx_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return RSX_SUCCESS;
+  snprintf(g_hip_error, sizeof(g_hip_error), "HIP error %d: %s", static_cast<int>(e),
+           hipGetErrorString(e));
+  return RSX_ERR_HIP;
+}
+
+size_t esize_of(int dtype) {
+  switch (dtype) {
+    case RSX_FLOAT32:
+      return 4;
+    case RSX_BFLOAT16:
+      return 2;
+    case RSX_INT32:
+      return 4;
+    default:
+      return 0;
+  }
+}
+
+bool valid_op(int op) { return op >= RSX_SUM && op <= RSX_AVG; }
+
+// a * b without wrapping; false on overflow.
+bool mul_ok(size_t a, size_t b, size_t* out) {
+  if (a != 0 && b > SIZE_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Range range_of(const void* p, size_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return {lo, lo + bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.hi && b.lo < b.hi; }
+bool same(Range a, Range b) { return a.lo == b.lo && a.hi == b.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Buffers that are only read may coincide exactly; partial overlap is refused
+// because no element index can then be tied to a single lane.
+bool reads_consistent(const Range* r, int n) {
+  for (int i = 0; i < n; ++i)
+    for (int j = i + 1; j < n; ++j)
+      if (overlap(r[i], r[j]) && !same(r[i], r[j])) return false;
+  return true;
+}
+bool pairwise_disjoint(const Range* r, int n) {
+  for (int i = 0; i < n; ++i)
+    for (int j = i + 1; j < n; ++j)
+      if (overlap(r[i], r[j])) return false;
+  return true;
+}
+
+// Workgroups along one segment of `seg` elements.
+uint64_t fold_tiles(uint64_t seg, int world, bool vec, int vl) {
+  const uint64_t per = static_cast<uint64_t>(fold_units(world)) * kBlock;
+  const uint64_t units = vec ? seg / vl : seg;
+  return std::max<uint64_t>(1, (units + per - 1) / per);
+}
+
+rsx_status_t launch_fold_any(int dtype, int op, int world, bool rs, bool vec, const FoldArgs& a,
+                             uint64_t tiles, uint32_t nseg, hipStream_t s) {
+  if (tiles > 0x7fffffffull) return RSX_ERR_UNSUPPORTED;
+  const dim3 grid(static_cast<uint32_t>(tiles), nseg);
+  hipError_t e;
+  switch (dtype) {
+    case RSX_FLOAT32:
+      e = launch_fold_f32(op, world, rs, vec, a, grid, s);
+      break;
+    case RSX_BFLOAT16:
+      e = launch_fold_bf16(op, world, rs, vec, a, grid, s);
+      break;
+    default:
+      e = launch_fold_i32(op, world, rs, vec, a, grid, s);
+      break;
+  }
+  return hip_status(e);
+}
+
+// Shared validation of the pointer arrays and enums of the collectives.
+rsx_status_t check_common(const void* const* sendbufs, void* const* recvbufs, int nranks,
+                          int dtype) {
+  if (sendbufs == nullptr || recvbufs == nullptr) return RSX_ERR_INVALID_ARGUMENT;
+  if (nranks < 1 || nranks > RSX_MAX_RANKS) return RSX_ERR_INVALID_ARGUMENT;
+  if (esize_of(dtype) == 0) return RSX_ERR_INVALID_TYPE;
+  return RSX_SUCCESS;
+}
+
+rsx_status_t check_device_ptrs(const void* const* sendbufs, void* const* recvbufs, int nranks) {
+  for (int r = 0; r < nranks; ++r)
+    if (sendbufs[r] == nullptr || recvbufs[r] == nullptr) return RSX_ERR_INVALID_ARGUMENT;
+  return RSX_SUCCESS;
+}
+
+// Pack (tensors -> fused) or unpack (fused -> tensors) at running offsets.
+rsx_status_t fuse_copy(const void* const* tens, const size_t* counts, int ntensors,
+                       const void* fused, bool pack, int dtype, hipStream_t stream) {
+  if (counts == nullptr || ntensors < 0) return RSX_ERR_INVALID_ARGUMENT;
+  const size_t es = esize_of(dtype);
+  if (es == 0) return RSX_ERR_INVALID_TYPE;
+  size_t total = 0;
+  for (int i = 0; i < ntensors; ++i) {
+    size_t b;
+    if (!mul_ok(counts[i], es, &b) || total + b < total) return RSX_ERR_UNSUPPORTED;
+    total += b;
+  }
+  if (total == 0) return RSX_SUCCESS;
+  if (tens == nullptr || fused == nullptr) return RSX_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < ntensors; ++i)
+    if (counts[i] != 0 && tens[i] == nullptr) return RSX_ERR_INVALID_ARGUMENT;
+  const Range fr = range_of(fused, total);
+  for (int i = 0; i < ntensors; ++i) {
+    if (counts[i] == 0) continue;
+    const Range ti = range_of(tens[i], counts[i] * es);
+    if (overlap(fr, ti)) return RSX_ERR_ALIASING;
+    if (!pack) {  // unpack writes the tensors: they must not overlap each other
+      for (int j = i + 1; j < ntensors; ++j)
+        if (counts[j] != 0 && overlap(ti, range_of(tens[j], counts[j] * es))) return RSX_ERR_ALIASING;
+    }
+  }
+
+  // Batches of RSX_FUSE_BATCH descriptors per launch.
+  const uint64_t per = static_cast<uint64_t>(kCopyUnits) * kBlock;
+  size_t off = 0;
+  int i = 0;
+  while (i < ntensors) {
+    MultiCopyArgs a;
+    memset(&a, 0, sizeof(a));
+    uint64_t blocks = 0;
+    while (i < ntensors && a.n < RSX_FUSE_BATCH) {
+      const size_t bytes = counts[i] * es;
+      if (bytes != 0) {
+        const char* fz = static_cast<const char*>(fused) + off;
+        const void* s = pack ? tens[i] : static_cast<const void*>(fz);
+        void* d = pack ? const_cast<char*>(fz) : const_cast<void*>(tens[i]);
+        const uintptr_t x = reinterpret_cast<uintptr_t>(s) ^ reinterpret_cast<uintptr_t>(d);
+        CopyDesc& c = a.d[a.n];
+        c.src = s;
+        c.dst = d;
+        c.bytes = bytes;
+        uint64_t units;
+        if ((x & 15u) == 0) {
+          c.path = 0;
+          units = bytes / 16;
+        } else if ((x & 3u) == 0) {
+          c.path = 1;
+          units = bytes / 4;
+        } else {
+          c.path = 2;
+          units = bytes / es;
+        }
+        const uint64_t tiles = std::max<uint64_t>(1, (units + per - 1) / per);
+        if (blocks + tiles > 0x7fffffffull) return RSX_ERR_UNSUPPORTED;
+        c.tiles = static_cast<uint32_t>(tiles);
+        a.tile_start[a.n] = static_cast<uint32_t>(blocks);
+        blocks += tiles;
+        a.n += 1;
+      }
+      off += bytes;
+      ++i;
+    }
+    if (a.n == 0) continue;
+    a.tile_start[a.n] = static_cast<uint32_t>(blocks);
+    const rsx_status_t st =
+        hip_status(launch_multicopy(static_cast<int>(es), a, static_cast<uint32_t>(blocks), stream));
+    if (st != RSX_SUCCESS) return st;
+  }
+  return RSX_SUCCESS;
+}
+
+}  // namespace
+}  // namespace rsx
+
+using namespace rsx;
+
+extern "C" {
+
+rsx_status_t rsx_reduce_scatter(const void* const* sendbufs, void* const* recvbufs, int nranks,
+                                size_t recvcount, rsx_dtype_t dtype, rsx_op_t op,
+                                hipStream_t stream) {
+  rsx_status_t st = check_common(sendbufs, recvbufs, nranks, dtype);
+  if (st != RSX_SUCCESS) return st;
+  if (!valid_op(op)) return RSX_ERR_INVALID_OP;
+  if (recvcount == 0) return RSX_SUCCESS;
+  if ((st = check_device_ptrs(sendbufs, recvbufs, nranks)) != RSX_SUCCESS) return st;
+  const size_t es = esize_of(dtype);
+  size_t n, seg_bytes, in_bytes;
+  if (!mul_ok(recvcount, static_cast<size_t>(nranks), &n) || !mul_ok(recvcount, es, &seg_bytes) ||
+      !mul_ok(n, es, &in_bytes))
+    return RSX_ERR_UNSUPPORTED;
+
+  Range in[RSX_MAX_RANKS], out[RSX_MAX_RANKS];
+  bool in_place_all = true;
+  for (int r = 0; r < nranks; ++r) {
+    in[r] = range_of(sendbufs[r], in_bytes);
+    out[r] = range_of(recvbufs[r], seg_bytes);
+  }
+  if (!reads_consistent(in, nranks) || !pairwise_disjoint(out, nranks)) return RSX_ERR_ALIASING;
+  for (int k = 0; k < nranks; ++k) {
+    const bool in_place = out[k].lo == in[k].lo + k * seg_bytes;
+    in_place_all = in_place_all && in_place;
+    if (in_place) continue;
+    for (int r = 0; r < nranks; ++r)
+      if (overlap(out[k], in[r])) return RSX_ERR_ALIASING;
+  }
+  if (nranks == 1 && in_place_all) return RSX_SUCCESS;
+
+  bool vec = (seg_bytes % kVecBytes) == 0;
+  for (int r = 0; r < nranks; ++r) vec = vec && aligned16(sendbufs[r]) && aligned16(recvbufs[r]);
+
+  FoldArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int r = 0; r < nranks; ++r) {
+    a.src[r] = sendbufs[r];
+    a.dst[r] = recvbufs[r];
+  }
+  a.count = n;
+  a.seg = recvcount;
+  a.rot = 1;
+  const int vl = static_cast<int>(kVecBytes / es);
+  return launch_fold_any(dtype, op, nranks, true, vec, a, fold_tiles(recvcount, nranks, vec, vl),
+                         static_cast<uint32_t>(nranks), stream);
+}
+
+rsx_status_t rsx_all_gather(const void* const* sendbufs, void* const* recvbufs, int nranks,
+                            size_t sendcount, rsx_dtype_t dtype, hipStream_t stream) {
+  rsx_status_t st = check_common(sendbufs, recvbufs, nranks, dtype);
+  if (st != RSX_SUCCESS) return st;
+  if (sendcount == 0) return RSX_SUCCESS;
+  if ((st = check_device_ptrs(sendbufs, recvbufs, nranks)) != RSX_SUCCESS) return st;
+  const size_t es = esize_of(dtype);
+  size_t piece_bytes, out_bytes;
+  if (!mul_ok(sendcount, es, &piece_bytes) ||
+      !mul_ok(piece_bytes, static_cast<size_t>(nranks), &out_bytes))
+    return RSX_ERR_UNSUPPORTED;
+  Range in[RSX_MAX_RANKS], out[RSX_MAX_RANKS];
+  for (int r = 0; r < nranks; ++r) {
+    in[r] = range_of(sendbufs[r], piece_bytes);
+    out[r] = range_of(recvbufs[r], out_bytes);
+  }
+  if (!pairwise_disjoint(out, nranks)) return RSX_ERR_ALIASING;
+  bool in_place_all = true;
+  for (int k = 0; k < nranks; ++k) {
+    const bool in_place = in[k].lo == out[k].lo + k * piece_bytes;
+    in_place_all = in_place_all && in_place;
+    if (in_place) continue;
+    for (int r = 0; r < nranks; ++r)
+      if (overlap(in[k], out[r])) return RSX_ERR_ALIASING;
+  }
+  if (nranks == 1 && in_place_all) return RSX_SUCCESS;
+
+  bool vec = (piece_bytes % kVecBytes) == 0;
+  for (int r = 0; r < nranks; ++r) vec = vec && aligned16(sendbufs[r]) && aligned16(recvbufs[r]);
+  GatherArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int r = 0; r < nranks; ++r) {
+    a.src[r] = sendbufs[r];
+    a.dst[r] = recvbufs[r];
+  }
+  a.n = sendcount;
+  a.world = nranks;
+  const uint64_t units = vec ? piece_bytes / kVecBytes : sendcount;
+  const uint64_t per = static_cast<uint64_t>(kCopyUnits) * kBlock;
+  const uint64_t tiles = std::max<uint64_t>(1, (units + per - 1) / per);
+  if (tiles > 0x7fffffffull) return RSX_ERR_UNSUPPORTED;
+  return hip_status(launch_gather(static_cast<int>(es), vec, a,
+                                  dim3(static_cast<uint32_t>(tiles), static_cast<uint32_t>(nranks)),
+                                  stream));
+}
+
+rsx_status_t rsx_all_reduce(const void* const* sendbufs, void* const* recvbufs, int nranks,
+                            size_t count, rsx_dtype_t dtype, rsx_op_t op, rsx_algo_t algo,
+                            hipStream_t stream) {
+  rsx_status_t st = check_common(sendbufs, recvbufs, nranks, dtype);
+  if (st != RSX_SUCCESS) return st;
+  if (!valid_op(op)) return RSX_ERR_INVALID_OP;
+  if (algo != RSX_ALGO_RING && algo != RSX_ALGO_NAIVE && algo != RSX_ALGO_AUTO)
+    return RSX_ERR_INVALID_ARGUMENT;
+  if (count == 0) return RSX_SUCCESS;
+  if ((st = check_device_ptrs(sendbufs, recvbufs, nranks)) != RSX_SUCCESS) return st;
+  const size_t es = esize_of(dtype);
+  size_t bytes;
+  if (!mul_ok(count, es, &bytes)) return RSX_ERR_UNSUPPORTED;
+  Range in[RSX_MAX_RANKS], out[RSX_MAX_RANKS];
+  bool in_place_all = true;
+  for (int r = 0; r < nranks; ++r) {
+    in[r] = range_of(sendbufs[r], bytes);
+    out[r] = range_of(recvbufs[r], bytes);
+  }
+  if (!reads_consistent(in, nranks) || !pairwise_disjoint(out, nranks)) return RSX_ERR_ALIASING;
+  for (int r = 0; r < nranks; ++r) {
+    in_place_all = in_place_all && same(out[r], in[r]);
+    for (int j = 0; j < nranks; ++j)
+      if (overlap(out[r], in[j]) && !same(out[r], in[j])) return RSX_ERR_ALIASING;
+  }
+  if (nranks == 1 && in_place_all) return RSX_SUCCESS;
+
+  const bool naive = algo == RSX_ALGO_NAIVE || (algo == RSX_ALGO_AUTO && bytes <= RSX_NAIVE_MAX_BYTES);
+  bool vec = true;
+  for (int r = 0; r < nranks; ++r) vec = vec && aligned16(sendbufs[r]) && aligned16(recvbufs[r]);
+
+  FoldArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int r = 0; r < nranks; ++r) {
+    a.src[r] = sendbufs[r];
+    a.dst[r] = recvbufs[r];
+  }
+  a.count = count;
+  const uint64_t seg = naive ? count : (count + nranks - 1) / nranks;
+  a.seg = seg;
+  a.rot = naive ? 0 : 1;
+  const uint32_t nseg = naive ? 1 : static_cast<uint32_t>(nranks);
+  const int vl = static_cast<int>(kVecBytes / es);
+  return launch_fold_any(dtype, op, nranks, false, vec, a, fold_tiles(seg, nranks, vec, vl), nseg,
+                         stream);
+}
+
+rsx_status_t rsx_fuse_pack(const void* const* tensors, const size_t* counts, int ntensors,
+                           void* fused, rsx_dtype_t dtype, hipStream_t stream) {
+  return fuse_copy(tensors, counts, ntensors, fused, true, dtype, stream);
+}
+
+rsx_status_t rsx_fuse_unpack(const void* fused, void* const* tensors, const size_t* counts,
+                             int ntensors, rsx_dtype_t dtype, hipStream_t stream) {
+  return fuse_copy(tensors, counts, ntensors, fused, false, dtype, stream);
+}
+
+size_t rsx_segment_begin(size_t count, int nranks, int k) {
+  if (nranks < 1 || k < 0) return 0;
+  const size_t seg = count / nranks + (count % nranks != 0);
+  const size_t kk = static_cast<size_t>(k);
+  if (seg != 0 && kk > count / seg) return count;
+  return std::min(kk * seg, count);
+}
+
+size_t rsx_dtype_size(rsx_dtype_t dtype) { return esize_of(dtype); }
+
+const char* rsx_status_string(rsx_status_t status) {
+  switch (status) {
+    case RSX_SUCCESS:
+      return "success";
+    case RSX_ERR_INVALID_ARGUMENT:
+      return "invalid argument";
+    case RSX_ERR_INVALID_TYPE:
+      return "invalid data type";
+    case RSX_ERR_INVALID_OP:
+      return "invalid reduction operation";
+    case RSX_ERR_UNSUPPORTED:
+      return "unsupported size";
+    case RSX_ERR_ALIASING:
+      return "buffers overlap in an unsupported way";
+    case RSX_ERR_HIP:
+      return g_hip_error;
+    default:
+      return "unknown status";
+  }
+}
+
+int rsx_version(void) { return RSX_VERSION; }
+
+}  // extern "C"

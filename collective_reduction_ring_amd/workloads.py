@@ -20,6 +20,8 @@ messages of at most 32 KB ("Add scatter reduce for JACCL#3901").
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -75,7 +77,8 @@ def draw(dist: str, rng: np.random.Generator, n: int) -> np.ndarray:
     """Draw ``n`` values of distribution ``dist``.
 
     Returns float32 for the float distributions, int32 for ``int_2e20`` and
-    uint16 bf16 bit patterns for ``normal_bf16``.
+    ``int_full`` (the whole int32 range, so sums wrap) and uint16 bf16 bit
+    patterns for ``normal_bf16``.
     """
     if dist == "uniform":
         return rng.uniform(-1.0, 1.0, n).astype(np.float32)
@@ -85,6 +88,8 @@ def draw(dist: str, rng: np.random.Generator, n: int) -> np.ndarray:
         return rng.standard_normal(n, dtype=np.float32)
     if dist == "int_2e20":
         return rng.integers(-(2 ** 20), 2 ** 20, n, dtype=np.int32, endpoint=True)
+    if dist == "int_full":
+        return rng.integers(-(2 ** 31), 2 ** 31, n, dtype=np.int64).astype(np.int32)
     if dist == "normal_bf16":
         return to_bf16_bits_torch(rng.standard_normal(n, dtype=np.float32))
     raise ValueError(f"unknown distribution {dist!r}")
@@ -105,7 +110,11 @@ def rank_inputs(cfg: int, n: int | None = None, world: int | None = None,
     n = w.n if n is None else n
     world = w.world if world is None else world
     dist = w.dist if dist is None else dist
-    return [draw(dist, rng_for(cfg, r), n) for r in range(world)]
+    # Each rank has its own generator, so drawing them on threads (NumPy
+    # releases the GIL for bulk draws) gives the same values as a loop.
+    workers = max(1, min(world, 16, os.cpu_count() or 1))
+    with ThreadPoolExecutor(workers) as ex:
+        return list(ex.map(lambda r: draw(dist, rng_for(cfg, r), n), range(world)))
 
 
 # ------------------------------------------------------ fused-tensor inputs --

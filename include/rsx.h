@@ -1,0 +1,176 @@
+/*
+ * rsx -- ring reduce-scatter / all-gather / all-reduce on one MI355X (gfx950).
+ *
+ * C ABI of librsx.so.  One process drives W "virtual ranks": rank r is a
+ * buffer in the one GPU's HBM, and each call takes a host array of W device
+ * pointers where a communicator-based library would take one buffer and a
+ * communicator.  Every entry point enqueues its kernels on `stream` and
+ * returns without synchronising the host.
+ *
+ * Sources of the semantics (web pages):
+ *   [NC] NCCL 1.x src/reduce_scatter.cu (pytorch mirror, "Git at Google"):
+ *        ncclReduceScatter, the ring kernel and GetBlock, its host launcher
+ *        (count 0 -> success; one device -> plain copy) and its op/type
+ *        dispatch (unknown op / type -> an error code).
+ *   [DP] "Distributed primitives": reduce-scatter, all-gather, all-reduce,
+ *        Ring AllReduce = ReduceScatter + AllGather, bucketed ring all-reduce.
+ *   [SG] Apache SINGA src/io/communicator.cc, fusedSynch / synch: tensors
+ *        packed back to back into a fusion buffer, all-reduced, unpacked;
+ *        in-place all-reduce of a tensor.
+ *   [HV] Horovod horovod/common/operations.cc, PerformOperation: memcpy into
+ *        the fusion buffer at running offsets, in-place all-reduce, memcpy out.
+ *   [MX] "Add scatter reduce for JACCL#3901": naive all-reduce for messages
+ *        of at most 32 KB.
+ *
+ * Common conventions
+ *   - Pointer arrays (`sendbufs`, `recvbufs`, `tensors`, `counts`) are HOST
+ *     arrays, read during the call only.  The device buffers they point to
+ *     are owned by the caller and must stay valid until the stream work ends.
+ *   - The library allocates no device or pinned memory and does not
+ *     synchronise; it launches kernels on `stream` (0 = the null stream) on
+ *     the calling thread's current HIP device, which must hold every buffer.
+ *   - Validation (null pointers, rank count, enum ranges, size overflow,
+ *     illegal buffer overlap) happens before any HIP call; a rejected call
+ *     has no effect.  A failed launch returns RSX_ERR_HIP, and
+ *     rsx_status_string(RSX_ERR_HIP) then names the HIP error (per thread).
+ *   - Counts are elements, not bytes.  A count of 0 returns RSX_SUCCESS
+ *     without launching anything [NC host launcher].
+ *   - Buffers of 16-byte-aligned address take the dwordx4 kernels; other
+ *     alignments are correct but slower.
+ */
+#ifndef RSX_H
+#define RSX_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RSX_VERSION 100          /* 1.0.0 */
+#define RSX_MAX_RANKS 16         /* largest W a call accepts */
+#define RSX_NAIVE_MAX_BYTES 32768 /* RSX_ALGO_AUTO picks naive at or below this, per rank [MX] */
+#define RSX_FUSE_BATCH 32        /* tensors per pack/unpack launch */
+
+typedef enum {
+  RSX_FLOAT32 = 0,   /* fp32 in, fp32 fold, fp32 out */
+  RSX_BFLOAT16 = 1,  /* bf16 in, widened exactly to fp32, fp32 fold, one RNE rounding to bf16 out */
+  RSX_INT32 = 2      /* int32, two's-complement wrapping sum */
+} rsx_dtype_t;
+
+typedef enum {
+  RSX_SUM = 0,
+  RSX_MAX = 1,       /* compare-select fold: a later value replaces the partial only if greater */
+  RSX_MIN = 2,       /* compare-select fold: a later value replaces the partial only if smaller */
+  RSX_AVG = 3        /* sum fold, then one division by W in the fold type (int32: toward zero) */
+} rsx_op_t;
+
+typedef enum {
+  RSX_ALGO_RING = 0,  /* segment k folded in ring order (k+1)%W, ..., k; then gathered */
+  RSX_ALGO_NAIVE = 1, /* every element folded in rank order 0..W-1 [MX] */
+  RSX_ALGO_AUTO = 2   /* NAIVE when count * element size <= RSX_NAIVE_MAX_BYTES, else RING */
+} rsx_algo_t;
+
+typedef enum {
+  RSX_SUCCESS = 0,
+  RSX_ERR_INVALID_ARGUMENT = 1, /* null pointer, rank count out of [1, RSX_MAX_RANKS], bad algo */
+  RSX_ERR_INVALID_TYPE = 2,     /* dtype outside rsx_dtype_t [NC: invalid type] */
+  RSX_ERR_INVALID_OP = 3,       /* op outside rsx_op_t [NC: invalid operation] */
+  RSX_ERR_UNSUPPORTED = 4,      /* sizes whose byte count or launch grid overflows */
+  RSX_ERR_ALIASING = 5,         /* buffers overlap in a way other than the in-place forms */
+  RSX_ERR_HIP = 6               /* a HIP launch failed; see rsx_status_string */
+} rsx_status_t;
+
+/*
+ * Reduce-scatter [NC ncclReduceScatter; DP "Reduce-Scatter"].
+ *
+ * sendbufs[r]  device array of W*recvcount elements, rank r's input.
+ * recvbufs[k]  device array of recvcount elements, receives block k:
+ *              recvbufs[k][i] = fold of sendbufs[r][k*recvcount + i] over
+ *              r = (k+1)%W, (k+2)%W, ..., k, in that order (the ring's order:
+ *              block k leaves the position after k at step 0 and ends on
+ *              position k at step W-1, per GetBlock with the identity ring).
+ * nranks       W, 1..RSX_MAX_RANKS.  W = 1 is a copy (nothing if in place).
+ * In place: recvbufs[k] == (char*)sendbufs[k] + k*recvcount*size is allowed.
+ * Any other overlap of a recv buffer with a send buffer or another recv
+ * buffer returns RSX_ERR_ALIASING.  Send buffers may alias each other only
+ * when identical.
+ */
+rsx_status_t rsx_reduce_scatter(const void* const* sendbufs, void* const* recvbufs,
+                                int nranks, size_t recvcount, rsx_dtype_t dtype,
+                                rsx_op_t op, hipStream_t stream);
+
+/*
+ * All-gather [DP "All-Gather"; the gather half of Ring AllReduce].
+ *
+ * sendbufs[k]  device array of sendcount elements, rank k's piece.
+ * recvbufs[r]  device array of W*sendcount elements; on return
+ *              recvbufs[r][k*sendcount + i] = sendbufs[k][i] for every r, k.
+ * In place: sendbufs[k] == (char*)recvbufs[k] + k*sendcount*size is allowed.
+ * Other overlaps return RSX_ERR_ALIASING.
+ */
+rsx_status_t rsx_all_gather(const void* const* sendbufs, void* const* recvbufs,
+                            int nranks, size_t sendcount, rsx_dtype_t dtype,
+                            hipStream_t stream);
+
+/*
+ * All-reduce [DP Ring AllReduce = ReduceScatter + AllGather; SG synch; HV
+ * PerformOperation].
+ *
+ * sendbufs[r], recvbufs[r]  device arrays of `count` elements.
+ * RSX_ALGO_RING: the `count` elements are split into W segments of
+ *   S = ceil(count/W): segment k = [min(kS,count), min((k+1)S,count)), see
+ *   rsx_segment_begin.  Segment k is folded in ring order (k+1)%W, ..., k and
+ *   written to every rank: the result equals rsx_all_gather applied to the
+ *   reduce-scatter output whenever W divides count, in one pass that keeps
+ *   the partials in registers.
+ * RSX_ALGO_NAIVE: every element folded in rank order 0..W-1 [MX].
+ * In place: recvbufs[r] == sendbufs[r] for every r (or a permutation of the
+ * send buffers) is allowed; other overlaps return RSX_ERR_ALIASING.
+ */
+rsx_status_t rsx_all_reduce(const void* const* sendbufs, void* const* recvbufs,
+                            int nranks, size_t count, rsx_dtype_t dtype, rsx_op_t op,
+                            rsx_algo_t algo, hipStream_t stream);
+
+/*
+ * Tensor-fusion pack [SG fusedSynch(send=false); HV PerformOperation memcpy in].
+ *
+ * Copies tensors[i] (device, counts[i] elements) to
+ * fused + (counts[0] + ... + counts[i-1]) elements: back to back, in list
+ * order, with no padding.  `fused` must hold the sum of counts and must not
+ * overlap any tensor (RSX_ERR_ALIASING).  ntensors >= 0; zero-count tensors
+ * are skipped and may be null.  Launches ceil(ntensors / RSX_FUSE_BATCH) kernels.
+ */
+rsx_status_t rsx_fuse_pack(const void* const* tensors, const size_t* counts, int ntensors,
+                           void* fused, rsx_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Tensor-fusion unpack [SG fusedSynch(send=true) copy-out; HV memcpy out]:
+ * the inverse of rsx_fuse_pack, same offsets and rules.
+ */
+rsx_status_t rsx_fuse_unpack(const void* fused, void* const* tensors, const size_t* counts,
+                             int ntensors, rsx_dtype_t dtype, hipStream_t stream);
+
+/*
+ * First element of segment k in RSX_ALGO_RING all-reduce of `count`
+ * elements over `nranks` ranks: min(k * ceil(count/nranks), count).
+ * k may be 0..nranks (k = nranks gives count).  Returns 0 for nranks < 1.
+ */
+size_t rsx_segment_begin(size_t count, int nranks, int k);
+
+/* Size in bytes of one element of `dtype`, 0 if it is not a valid dtype. */
+size_t rsx_dtype_size(rsx_dtype_t dtype);
+
+/* Static description of a status; for RSX_ERR_HIP the calling thread's last
+ * HIP error text.  Never NULL. */
+const char* rsx_status_string(rsx_status_t status);
+
+/* RSX_VERSION of the built library. */
+int rsx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RSX_H */

@@ -1,0 +1,229 @@
+"""C-ABI tests that need no GPU: symbols, enums, host-side validation.
+
+The validation tests pass made-up device addresses: every such case must be
+rejected before the library makes a HIP call.  They are skipped where a GPU
+is visible, so a validation bug can never turn them into a real launch on
+fake pointers; the GPU suite covers the same error paths with real tensors.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from collective_reduction_ring_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rsx.h")
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+fake_ptrs = pytest.mark.skipif(_gpu_visible(), reason="fake device pointers only where no GPU exists")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("librsx.so is not built; run `python -m collective_reduction_ring_amd.build`")
+    return L.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rsx_[a-z_]+)\s*\(", text)))
+
+
+def _header_int(name):
+    m = re.search(rf"#define\s+{name}\s+(\d+)", open(HEADER).read())
+    return int(m.group(1))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert "rsx_reduce_scatter" in names and len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.SIGNATURES)
+
+
+def test_enum_and_macro_values_match_binding(lib):
+    text = open(HEADER).read()
+    for name, val in [("RSX_FLOAT32", L.RSX_FLOAT32), ("RSX_BFLOAT16", L.RSX_BFLOAT16),
+                      ("RSX_INT32", L.RSX_INT32), ("RSX_SUM", L.RSX_SUM), ("RSX_MAX", L.RSX_MAX),
+                      ("RSX_MIN", L.RSX_MIN), ("RSX_AVG", L.RSX_AVG),
+                      ("RSX_ALGO_RING", L.RSX_ALGO_RING), ("RSX_ALGO_NAIVE", L.RSX_ALGO_NAIVE),
+                      ("RSX_ALGO_AUTO", L.RSX_ALGO_AUTO)]:
+        assert re.search(rf"\b{name}\s*=\s*{val}\b", text), name
+    for code, name in L.STATUS.items():
+        assert re.search(rf"\b{name}\s*=\s*{code}\b", text), name
+    assert _header_int("RSX_MAX_RANKS") == L.RSX_MAX_RANKS
+    assert _header_int("RSX_NAIVE_MAX_BYTES") == L.RSX_NAIVE_MAX_BYTES
+    assert _header_int("RSX_FUSE_BATCH") == L.RSX_FUSE_BATCH
+    assert lib.rsx_version() == _header_int("RSX_VERSION")
+
+
+def test_dtype_size_and_status_strings(lib):
+    assert [lib.rsx_dtype_size(d) for d in (0, 1, 2, 3, -1)] == [4, 2, 4, 0, 0]
+    for code in range(7):
+        assert lib.rsx_status_string(code)
+    assert lib.rsx_status_string(99) == b"unknown status"
+
+
+def test_segment_begin_ceil_split(lib):
+    import oracle
+    for count in (0, 1, 2, 3, 10, 17, 4096, 25_165_823, 2 ** 40 + 3):
+        for w in (1, 2, 3, 4, 7, 8, 16):
+            bounds = oracle.segment_bounds(count, w) if count < 10 ** 6 else None
+            for k in range(w + 1):
+                got = lib.rsx_segment_begin(count, w, k)
+                s = -(-count // w)
+                assert got == min(k * s, count)
+                if bounds is not None and k < w:
+                    assert got == bounds[k][0]
+    assert lib.rsx_segment_begin(10, 0, 1) == 0
+    assert lib.rsx_segment_begin(10, 4, -1) == 0
+
+
+# ------------------------------------------------------ validation paths --
+
+A = 0x7F0000000000  # made-up, 16-byte aligned device addresses (never dereferenced)
+MB = 1 << 20
+
+
+def _arr(vals):
+    return L.ptr_array(vals)
+
+
+def _rs(lib, sends, recvs, w, n, dt=0, op=0):
+    return lib.rsx_reduce_scatter(_arr(sends), _arr(recvs), w, n, dt, op, None)
+
+
+def _ar(lib, sends, recvs, w, n, dt=0, op=0, algo=0):
+    return lib.rsx_all_reduce(_arr(sends), _arr(recvs), w, n, dt, op, algo, None)
+
+
+def _ag(lib, sends, recvs, w, n, dt=0):
+    return lib.rsx_all_gather(_arr(sends), _arr(recvs), w, n, dt, None)
+
+
+@fake_ptrs
+def test_null_arrays_and_rank_range(lib):
+    assert lib.rsx_reduce_scatter(None, _arr([A]), 1, 4, 0, 0, None) == 1
+    assert lib.rsx_all_reduce(_arr([A]), None, 1, 4, 0, 0, 0, None) == 1
+    assert lib.rsx_all_gather(None, None, 1, 4, 0, None) == 1
+    s = [A + i * MB for i in range(17)]
+    r = [A + 64 * MB + i * MB for i in range(17)]
+    assert _rs(lib, s, r, 0, 4) == 1
+    assert _rs(lib, s, r, 17, 4) == 1
+    assert _ar(lib, s, r, -1, 4) == 1
+    assert _ag(lib, s, r, 17, 4) == 1
+
+
+@fake_ptrs
+def test_bad_enums(lib):
+    s, r = [A, A + MB], [A + 2 * MB, A + 3 * MB]
+    assert _rs(lib, s, r, 2, 4, dt=3) == 2
+    assert _rs(lib, s, r, 2, 4, dt=-1) == 2
+    assert _rs(lib, s, r, 2, 4, op=4) == 3
+    assert _ar(lib, s, r, 2, 4, op=-1) == 3
+    assert _ar(lib, s, r, 2, 4, algo=3) == 1
+    assert _ag(lib, s, r, 2, 4, dt=5) == 2
+    # type is checked before op, as the page's dispatch switches on type first
+    assert _rs(lib, s, r, 2, 4, dt=9, op=9) == 2
+
+
+@fake_ptrs
+def test_zero_count_is_success_without_launch(lib):
+    assert _rs(lib, [A, A], [None, None], 2, 0) == 0
+    assert _ar(lib, [None] * 3, [None] * 3, 3, 0) == 0
+    assert _ag(lib, [A], [A], 1, 0) == 0
+
+
+@fake_ptrs
+def test_null_device_pointer(lib):
+    assert _rs(lib, [A, None], [A + 4 * MB, A + 5 * MB], 2, 4) == 1
+    assert _ar(lib, [A, A + MB], [A + 2 * MB, None], 2, 4) == 1
+
+
+@fake_ptrs
+def test_single_rank_in_place_is_a_no_op(lib):
+    assert _rs(lib, [A], [A], 1, 100) == 0
+    assert _ar(lib, [A], [A], 1, 100) == 0
+    assert _ag(lib, [A], [A], 1, 100) == 0
+
+
+@fake_ptrs
+def test_size_overflow(lib):
+    s, r = [A, A + MB], [A + 2 * MB, A + 3 * MB]
+    assert _rs(lib, s, r, 2, 2 ** 63) == 4
+    assert _ar(lib, s, r, 2, 2 ** 62 + 1) == 4
+    assert _ag(lib, s, r, 2, 2 ** 62) == 4
+
+
+@fake_ptrs
+def test_reduce_scatter_aliasing(lib):
+    n = 1024  # recvcount; inputs are 4*n fp32 = 16 KiB
+    s = [A + i * MB for i in range(4)]
+    # output overlapping another rank's input
+    assert _rs(lib, s, [A + 2 * MB + 64, A + 8 * MB, A + 9 * MB, A + 10 * MB], 4, n) == 5
+    # outputs overlapping each other
+    assert _rs(lib, s, [A + 8 * MB, A + 8 * MB + 16, A + 9 * MB, A + 10 * MB], 4, n) == 5
+    # inputs partially overlapping
+    s2 = [A, A + 64, A + 2 * MB, A + 3 * MB]
+    assert _rs(lib, s2, [A + 8 * MB + i * MB for i in range(4)], 4, n) == 5
+    # in place, but at the wrong block of rank 1
+    r = [s[0], s[1] + 2 * n * 4, s[2] + 2 * n * 4, s[3] + 3 * n * 4]
+    assert _rs(lib, s, r, 4, n) == 5
+
+
+@fake_ptrs
+def test_all_reduce_aliasing(lib):
+    n = 1000
+    s = [A + i * MB for i in range(3)]
+    assert _ar(lib, s, [s[0] + 8, A + 8 * MB, A + 9 * MB], 3, n) == 5   # shifted onto input
+    assert _ar(lib, s, [A + 8 * MB, A + 8 * MB, A + 9 * MB], 3, n) == 5  # shared output
+    assert _ar(lib, [A, A + 4, A + 2 * MB], [A + 8 * MB + i * MB for i in range(3)], 3, n) == 5
+
+
+@fake_ptrs
+def test_all_gather_aliasing(lib):
+    n = 256
+    r = [A + i * MB for i in range(4)]
+    # piece 1 inside rank 0's output
+    assert _ag(lib, [A + 8 * MB, r[0] + 8, A + 9 * MB, A + 10 * MB], r, 4, n) == 5
+    # overlapping outputs
+    assert _ag(lib, [A + 8 * MB + i * MB for i in range(4)], [A, A + 16, A + 2 * MB, A + 3 * MB],
+               4, n) == 5
+
+
+@fake_ptrs
+def test_fuse_validation(lib):
+    counts = L.size_array([10, 0, 5])
+    ts = _arr([A, None, A + MB])
+    assert lib.rsx_fuse_pack(ts, None, 3, A + 4 * MB, 0, None) == 1       # counts missing
+    assert lib.rsx_fuse_pack(ts, counts, -1, A + 4 * MB, 0, None) == 1
+    assert lib.rsx_fuse_pack(ts, counts, 3, A + 4 * MB, 7, None) == 2     # bad dtype
+    assert lib.rsx_fuse_pack(ts, counts, 3, None, 0, None) == 1           # no fused buffer
+    assert lib.rsx_fuse_pack(ts, counts, 3, A + 36, 0, None) == 5         # fused overlaps t0
+    assert lib.rsx_fuse_unpack(A + MB - 8, ts, counts, 3, 0, None) == 5   # fused overlaps t2
+    assert lib.rsx_fuse_unpack(A + 4 * MB, _arr([A, None, A + 8]), counts, 3, 0, None) == 5
+    zero = L.size_array([0, 0])
+    assert lib.rsx_fuse_pack(_arr([None, None]), zero, 2, None, 0, None) == 0
+    assert lib.rsx_fuse_unpack(None, _arr([None, None]), zero, 2, 0, None) == 0
+    assert lib.rsx_fuse_pack(None, zero, 0, None, 0, None) == 0
+    assert lib.rsx_fuse_pack(_arr([A]), L.size_array([2 ** 62]), 1, A + MB, 0, None) == 4
+
+
+def test_binding_refuses_missing_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(L, "_lib", None)
+    with pytest.raises(RuntimeError, match="not found"):
+        L.lib()

@@ -1,0 +1,388 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+fp32 and int32 must match bit for bit, bf16 within one bf16 ulp (NaN where
+NaN).  Sizes span several workgroup tiles plus a ragged tail; every rank
+count 1..16 class, every op and dtype, both the dwordx4 and the unaligned
+kernels, in-place forms, the naive algorithm, all-gather and the fusion path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import collective_reduction_ring_amd as rsx
+import oracle
+from collective_reduction_ring_amd import workloads as wl
+from parity_util import assert_parity, empty, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+DIST = {"f32": "normal", "bf16": "normal_bf16", "i32": "int_full"}
+VL = {"f32": 4, "bf16": 8, "i32": 4}
+
+
+def units(w):  # dwordx4 per lane per source in the fold kernels
+    return 8 if w <= 2 else 4 if w <= 4 else 2 if w <= 8 else 1
+
+
+def tile_elems(w, dtype):
+    return units(w) * 256 * VL[dtype]
+
+
+def inputs(seed, w, n, dtype, dist=None):
+    return [wl.draw(dist or DIST[dtype], np.random.default_rng((seed, w, r)), n) for r in range(w)]
+
+
+def run_rs(xs, dtype, op, recvcount):
+    dev = [to_dev(x, dtype) for x in xs]
+    out = [empty(recvcount, dtype, fill=0x55) for _ in xs]
+    rsx.reduce_scatter(dev, out, op)
+    torch.cuda.synchronize()
+    return [to_host(o, dtype) for o in out]
+
+
+def run_ar(xs, dtype, op, algo="ring", in_place=False):
+    dev = [to_dev(x, dtype) for x in xs]
+    out = None if in_place else [empty(len(xs[0]), dtype, fill=0x55) for _ in xs]
+    rsx.all_reduce(dev, out, op, algo)
+    torch.cuda.synchronize()
+    return [to_host(o, dtype) for o in (dev if in_place else out)]
+
+
+OPS = ["sum", "max", "min", "avg"]
+WORLDS = [1, 2, 3, 4, 5, 8, 13, 16]
+
+
+# ------------------------------------------------------- reduce-scatter ----
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("op", OPS)
+@pytest.mark.parametrize("w", WORLDS)
+@pytest.mark.parametrize("aligned", [True, False])
+def test_reduce_scatter(w, op, dtype, aligned):
+    te = tile_elems(w, dtype)
+    recvcount = 2 * te + te // 2 + 3 * VL[dtype] + (0 if aligned else 1)
+    xs = inputs(1, w, w * recvcount, dtype)
+    say(f"rs w={w} op={op} dtype={dtype} recvcount={recvcount}")
+    got = run_rs(xs, dtype, op, recvcount)
+    want = oracle.reduce_scatter(xs, op, dtype)
+    for k in range(w):
+        assert_parity(got[k], want[k], dtype, f"block {k}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("op", OPS)
+@pytest.mark.parametrize("w", WORLDS)
+@pytest.mark.parametrize("algo", ["ring", "naive"])
+def test_all_reduce(w, op, dtype, algo):
+    te = tile_elems(w, dtype)
+    count = w * (2 * te + te // 3) + 5   # divisible by neither W nor the vector width
+    xs = inputs(2, w, count, dtype)
+    say(f"ar w={w} op={op} dtype={dtype} algo={algo} count={count}")
+    got = run_ar(xs, dtype, op, algo)
+    want = (oracle.all_reduce if algo == "ring" else oracle.naive_all_reduce)(xs, op, dtype)
+    for r in range(w):
+        assert_parity(got[r], want[r], dtype, f"rank {r}")
+
+
+@pytest.mark.parametrize("count", [1, 2, 3, 7, 8, 9, 15, 16, 17, 31, 33, 100, 1023])
+@pytest.mark.parametrize("w", [2, 4, 16])
+def test_all_reduce_small_and_ragged(w, count):
+    for dtype in ("f32", "bf16"):
+        xs = inputs(3, w, count, dtype)
+        say(f"ar small w={w} count={count} dtype={dtype}")
+        got = run_ar(xs, dtype, "sum", "ring")
+        want = oracle.all_reduce(xs, "sum", dtype)
+        for r in range(w):
+            assert_parity(got[r], want[r], dtype, f"rank {r}")
+
+
+def test_ring_order_probe():
+    # Segment 0 at W=4 with x0=1, x1=2^24, x2=1, x3=-2^24: only ring order
+    # 1,2,3,0 gives 1; rank order gives 0; reverse ring order gives 2.
+    big = np.float32(2.0 ** 24)
+    s = 1024
+    xs = [np.zeros(4 * s, np.float32) for _ in range(4)]
+    for k in range(4):  # same probe in every block k, at its element 5
+        xs[(k + 1) % 4][k * s + 5], xs[(k + 2) % 4][k * s + 5] = big, 1.0
+        xs[(k + 3) % 4][k * s + 5], xs[k][k * s + 5] = -big, 1.0
+    say("ring-order probe")
+    rs = run_rs(xs, "f32", "sum", s)
+    assert [rs[k][5] for k in range(4)] == [1.0] * 4
+    ar = run_ar(xs, "f32", "sum", "ring")
+    assert all(ar[r][k * s + 5] == 1.0 for r in range(4) for k in range(4))
+    nv = run_ar(xs, "f32", "sum", "naive")
+    # rank order: block 0 gives 0 (as above); blocks 1..3 start elsewhere
+    want = oracle.naive_all_reduce(xs, "sum", "f32")
+    assert nv[0][5] == 0.0
+    assert_parity(nv[0], want[0], "f32", "naive")
+
+
+def test_max_min_ties_and_nans():
+    nan = np.float32("nan")
+    base0 = np.array([-0.0, 0.0, nan, 1.0, -np.inf, 3.0, nan, 0.0], np.float32)
+    base1 = np.array([0.0, -0.0, 1.0, nan, np.inf, 3.0, nan, -0.0], np.float32)
+    xs = [np.tile(base0, 128), np.tile(base1, 128)]   # 1024 elements, two ranks
+    for op in ("max", "min"):
+        say(f"ties/NaN op={op}")
+        got = run_rs(xs, "f32", op, 512)
+        want = oracle.reduce_scatter(xs, op, "f32")
+        for k in range(2):
+            assert_parity(got[k], want[k], "f32", f"{op} block {k}")
+            assert np.array_equal(np.signbit(got[k]), np.signbit(want[k]))
+
+
+def test_bf16_specials_and_rounding_ties():
+    # Tie cases and specials: 1+2^-8 pairs (rounds to even), large values
+    # overflowing to inf, NaN, +-0.
+    vals = [0x3F80, 0x3B80, 0x3B80, 0x7F7F, 0x7F7F, 0x7FC0, 0x8000, 0x0000]
+    xs = [np.tile(np.array(vals, np.uint16), 64) for _ in range(4)]
+    xs[1] = np.roll(xs[1], 1)
+    xs[2] = np.roll(xs[2], 2)
+    for op in OPS:
+        say(f"bf16 specials op={op}")
+        got = run_ar(xs, "bf16", op, "ring")
+        want = oracle.all_reduce(xs, op, "bf16")
+        assert_parity(got[0], want[0], "bf16", op)
+
+
+# ----------------------------------------------------------- in place -------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("w", [1, 2, 4, 8])
+def test_in_place(w, dtype):
+    te = tile_elems(w, dtype)
+    s = te + 2 * VL[dtype]
+    xs = inputs(4, w, w * s, dtype)
+    dev = [to_dev(x, dtype) for x in xs]
+    say(f"in-place rs w={w} dtype={dtype}")
+    rsx.reduce_scatter(dev, [dev[k][k * s:(k + 1) * s] for k in range(w)], "sum")
+    torch.cuda.synchronize()
+    want = oracle.reduce_scatter(xs, "sum", dtype)
+    for k in range(w):
+        assert_parity(to_host(dev[k][k * s:(k + 1) * s], dtype), want[k], dtype, f"rs block {k}")
+    say(f"in-place ar w={w} dtype={dtype}")
+    got = run_ar(xs, dtype, "avg", "ring", in_place=True)
+    want = oracle.all_reduce(xs, "avg", dtype)
+    for r in range(w):
+        assert_parity(got[r], want[r], dtype, f"ar rank {r}")
+
+
+def test_unaligned_pointers():
+    w, s = 4, 3000
+    xs = inputs(5, w, w * s, "f32")
+    bases = [to_dev(np.concatenate([np.zeros(1, np.float32), x]), "f32") for x in xs]
+    dev = [b[1:] for b in bases]                      # 4-byte offset: not 16-byte aligned
+    outs = [empty(s + 3, "f32")[3:] for _ in range(w)]
+    say("unaligned rs")
+    rsx.reduce_scatter(dev, outs, "sum")
+    torch.cuda.synchronize()
+    want = oracle.reduce_scatter(xs, "sum", "f32")
+    for k in range(w):
+        assert_parity(to_host(outs[k], "f32"), want[k], "f32", f"block {k}")
+    say("unaligned ar")
+    outs = [empty(w * s + 1, "f32")[1:] for _ in range(w)]
+    rsx.all_reduce(dev, outs, "max")
+    torch.cuda.synchronize()
+    want = oracle.all_reduce(xs, "max", "f32")
+    for r in range(w):
+        assert_parity(to_host(outs[r], "f32"), want[r], "f32", f"rank {r}")
+
+
+def test_side_stream_and_repeat():
+    w, s = 8, 8192
+    xs = inputs(6, w, w * s, "f32")
+    dev = [to_dev(x, "f32") for x in xs]
+    out = [empty(s, "f32") for _ in range(w)]
+    plan = rsx.ReduceScatter(dev, out, "sum")
+    st = torch.cuda.Stream()
+    say("side stream rs x5")
+    with torch.cuda.stream(st):
+        for _ in range(5):
+            plan()
+    st.synchronize()
+    want = oracle.reduce_scatter(xs, "sum", "f32")
+    for k in range(w):
+        assert_parity(to_host(out[k], "f32"), want[k], "f32", f"block {k}")
+
+
+# ---------------------------------------------------------- all-gather ------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("w", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("n", [1, 5, 8, 4096 + 8, 4096 + 3])
+def test_all_gather(w, n, dtype):
+    pieces = inputs(7, w, n, dtype)
+    dev = [to_dev(p, dtype) for p in pieces]
+    out = [empty(w * n, dtype, fill=0x11) for _ in range(w)]
+    say(f"ag w={w} n={n} dtype={dtype}")
+    rsx.all_gather(dev, out)
+    torch.cuda.synchronize()
+    want = oracle.all_gather(pieces)
+    for r in range(w):
+        assert_parity(to_host(out[r], dtype), want[r], dtype, f"rank {r}")
+
+
+def test_all_gather_in_place_and_composition():
+    w, n = 4, 10_000
+    xs = inputs(8, w, w * n, "f32")
+    dev = [to_dev(x, "f32") for x in xs]
+    say("rs in place then ag in place")
+    rsx.reduce_scatter(dev, [dev[k][k * n:(k + 1) * n] for k in range(w)], "sum")
+    rsx.all_gather([dev[k][k * n:(k + 1) * n] for k in range(w)], dev)
+    torch.cuda.synchronize()
+    want = oracle.all_reduce(xs, "sum", "f32")   # AG(RS) == AR when W divides N
+    for r in range(w):
+        assert_parity(to_host(dev[r], "f32"), want[r], "f32", f"rank {r}")
+
+
+# --------------------------------------------------------------- fusion -----
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fused_pack_allreduce_unpack(dtype):
+    w = 4
+    sizes = wl.fused_sizes(count=70, lo=1, hi=70_000)
+    per_rank = [[wl.draw(DIST[dtype], np.random.default_rng((9, r, i)), int(s))
+                 for i, s in enumerate(sizes)] for r in range(w)]
+    tens = [[to_dev(t, dtype) for t in ts] for ts in per_rank]
+    total = int(sizes.sum())
+    fused = [empty(total, dtype) for _ in range(w)]
+    say(f"fused dtype={dtype} tensors={len(sizes)} total={total}")
+    for r in range(w):
+        rsx.fuse_pack(tens[r], fused[r])
+    torch.cuda.synchronize()
+    for r in range(w):
+        assert_parity(to_host(fused[r], dtype), oracle.fuse_pack(per_rank[r]), dtype, "pack")
+    outs = [[empty(int(s), dtype) for s in sizes] for _ in range(w)]
+    rsx.fused_all_reduce(tens, fused, outs, "sum")
+    torch.cuda.synchronize()
+    want = oracle.fused_all_reduce(per_rank, "sum", dtype)
+    for r in range(w):
+        for i in range(len(sizes)):
+            assert_parity(to_host(outs[r][i], dtype), want[r][i], dtype, f"rank {r} tensor {i}")
+
+
+@pytest.mark.parametrize("kib", wl.SWEEP_KIB)
+def test_sweep_naive_ring_auto(kib):
+    xs = wl.sweep_inputs(kib)
+    for algo, ref in (("naive", oracle.naive_all_reduce), ("ring", oracle.all_reduce),
+                      ("auto", oracle.naive_all_reduce)):
+        say(f"sweep {kib} KiB algo={algo}")
+        got = run_ar(xs, "f32", "sum", algo)
+        want = ref(xs, "sum", "f32")
+        for r in range(4):
+            assert_parity(got[r], want[r], "f32", f"{algo} rank {r}")
+
+
+def test_auto_switches_to_ring_above_32k():
+    xs = wl.sweep_inputs(64)   # 64 KiB per rank -> ring
+    got = run_ar(xs, "f32", "sum", "auto")
+    want = oracle.all_reduce(xs, "sum", "f32")
+    assert_parity(got[0], want[0], "f32", "auto 64 KiB")
+
+
+# --------------------------------------------------------- error paths ------
+
+def test_errors_with_real_tensors():
+    # Each case is refused by the binding or the library's validation, before
+    # any kernel is launched.
+    x = [torch.zeros(64, device="cuda:0") for _ in range(4)]
+    big = torch.zeros(128, device="cuda:0")
+    with pytest.raises(rsx.RsxError) as e:   # output shifted by 8 elements onto input 0
+        rsx.all_reduce([big[:64], x[1]], [big[8:72], x[2]], "sum")
+    assert e.value.status == 5
+    with pytest.raises(rsx.RsxError) as e:   # two ranks share one output
+        rsx.all_reduce([x[0], x[1]], [x[2], x[2]], "sum")
+    assert e.value.status == 5
+    with pytest.raises(rsx.RsxError) as e:   # block 1 written over rank 0's input
+        rsx.reduce_scatter([big[:64], x[1]], [x[2][:32], big[32:64]], "sum")
+    assert e.value.status == 5
+    with pytest.raises(ValueError):
+        rsx.reduce_scatter(x, [torch.zeros(15, device="cuda:0")] * 4)
+    with pytest.raises(ValueError):
+        rsx.all_reduce([torch.zeros(8, dtype=torch.float64, device="cuda:0")] * 2)
+    with pytest.raises(ValueError):
+        rsx.all_reduce(x, op="prod")
+    with pytest.raises(ValueError):
+        rsx.all_reduce([torch.zeros(8, device="cuda:0")] * 17)
+    with pytest.raises(ValueError):
+        rsx.all_reduce([x[0], torch.zeros(64, device="cuda:0", dtype=torch.int32)])
+
+
+# ------------------------------------------------- full-size workloads ------
+
+def _full_rs(cfg, op, dtype):
+    w = wl.WORKLOADS[cfg]
+    say(f"full cfg={cfg} rs op={op}: generating")
+    xs = wl.rank_inputs(cfg)
+    dev = [to_dev(x, dtype) for x in xs]
+    s = w.n // w.world
+    out = [empty(s, dtype) for _ in range(w.world)]
+    say(f"full cfg={cfg} rs op={op}: launching")
+    rsx.reduce_scatter(dev, out, op)
+    torch.cuda.synchronize()
+    got = [to_host(o, dtype) for o in out]
+    del dev
+    say(f"full cfg={cfg} rs op={op}: oracle")
+    want = oracle.reduce_scatter(xs, op, dtype)
+    for k in range(w.world):
+        assert_parity(got[k], want[k], dtype, f"block {k}")
+    return xs
+
+
+def test_full_c1_rs_and_ar():
+    xs = _full_rs(1, "sum", "f32")
+    got = run_ar(xs, "f32", "sum", "ring")
+    want = oracle.all_reduce(xs, "sum", "f32")
+    for r in range(4):
+        assert_parity(got[r], want[r], "f32", f"ar rank {r}")
+
+
+def test_full_c2_rs_sum_fp32():
+    _full_rs(2, "sum", "f32")
+
+
+@pytest.mark.parametrize("op", ["sum", "max"])
+def test_full_c4_int32(op):
+    xs = _full_rs(4, op, "i32")
+    w = wl.WORKLOADS[4]
+    say(f"full cfg=4 ar op={op}")
+    dev = [to_dev(x, "i32") for x in xs]
+    rsx.all_reduce(dev, None, op, "ring")
+    torch.cuda.synchronize()
+    # sampled ranks only: every rank receives the same result
+    want = oracle.all_reduce(xs, op, "i32")
+    for r in (0, 7, w.world - 1):
+        assert_parity(to_host(dev[r], "i32"), want[r], "i32", f"ar rank {r}")
+
+
+def test_full_c3_bf16_bucketed_avg():
+    w = wl.WORKLOADS[3]
+    say("full cfg=3: generating")
+    xs = wl.rank_inputs(3)
+    dev = [to_dev(x, "bf16") for x in xs]
+    out = [empty(w.n, "bf16") for _ in range(w.world)]
+    say("full cfg=3: 11 bucketed all-reduces")
+    rsx.all_reduce_bucketed(dev, out, w.extra["bucket_elems"], "avg")
+    torch.cuda.synchronize()
+    got = [to_host(out[r], "bf16") for r in (0, 3, 7)]
+    del dev, out
+    say("full cfg=3: oracle")
+    want = oracle.bucketed_all_reduce(xs, w.extra["bucket_elems"], "avg", "bf16")
+    stats = [assert_parity(g, want[r], "bf16", f"rank {r}") for g, r in zip(got, (0, 3, 7))]
+    say(f"bf16 exact fraction {stats[0]['exact'] / stats[0]['n']:.6f}")
+
+
+def test_full_c5_fused_200_tensors():
+    w = 4
+    sizes = wl.fused_sizes()
+    per_rank = wl.fused_tensors(w, sizes)
+    tens = [[to_dev(t, "f32") for t in ts] for ts in per_rank]
+    total = int(sizes.sum())
+    fused = [empty(total, "f32") for _ in range(w)]
+    say(f"full cfg=5: total {total} elements per rank")
+    rsx.fused_all_reduce(tens, fused, None, "sum")
+    torch.cuda.synchronize()
+    want = oracle.fused_all_reduce(per_rank, "sum", "f32")
+    for r in range(w):
+        for i in range(len(sizes)):
+            assert_parity(to_host(tens[r][i], "f32"), want[r][i], "f32", f"rank {r} tensor {i}")
