@@ -65,7 +65,8 @@ def cpu_baseline(xs, reps_budget_s: float):
         t0 = time.perf_counter()
         out = oracle.reduce_scatter(xs, "sum", "f32")
         times.append(time.perf_counter() - t0)
-        log(f"oracle pass {len(times)}: {times[-1]:.2f} s")
+        if len(times) % 10 == 1:
+            log(f"oracle pass {len(times)}: {times[-1]:.2f} s")
         if time.perf_counter() - t_start >= reps_budget_s or len(times) >= 500:
             break
     return out, statistics.median(times), len(times)

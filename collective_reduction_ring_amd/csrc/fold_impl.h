@@ -12,12 +12,14 @@
 // buffers of the multi-GPU kernel have nothing left to guard, and HBM sees
 // each input once and each output once.
 //
-// Layout of one launch: grid.y = segment k (uniform per workgroup, so the
-// ring rotation and the W source pointers are scalar), grid.x = tile of
-// U * 256 dwordx4 (or elements, for the unaligned kernel) within segment k.
-// A lane issues all W*U loads before the first combine.
+// Layout of one launch: a 1-D grid of tiles of U * 256 dwordx4 (or
+// elements, for the unaligned kernel), segment-major, mapped XCD-contiguous
+// (xcd_tile).  A workgroup works inside one segment k, so the ring rotation
+// and the W source pointers are scalar.  A lane issues all W*U loads before
+// the first combine.
 #pragma once
 
+#include "mem.h"
 #include "rsx_internal.h"
 
 namespace rsx {
@@ -150,12 +152,15 @@ __global__ __launch_bounds__(kBlock) void fold_kernel(const FoldArgs a) {
   constexpr int U = fold_units(W);
   constexpr int VL = D::kVL;
 
-  const uint32_t k = blockIdx.y;
+  const uint32_t t = xcd_tile(blockIdx.x, gridDim.x);
+  if (t >= a.tiles_total) return;
+  const uint32_t k = t / a.tiles_per_seg;
+  const uint32_t tile = t - k * a.tiles_per_seg;
   const uint64_t b = min(static_cast<uint64_t>(k) * a.seg, a.count);
   const uint64_t e = min(b + a.seg, a.count);
 
   // Ring rotation: source j of segment k is rank (k + rot + j) mod W.
-  uint32_t first = (k + a.rot) % W;
+  const uint32_t first = (k + a.rot) % W;
   const S* src[W];
 #pragma unroll
   for (int j = 0; j < W; ++j) {
@@ -191,21 +196,24 @@ __global__ __launch_bounds__(kBlock) void fold_kernel(const FoldArgs a) {
     const uint64_t hb = min((b + VL - 1) / VL * VL, e);
     const uint64_t be = max(hb, e / VL * VL);
     const uint64_t nv = (be - hb) / VL;
-    const uint64_t v0 = static_cast<uint64_t>(blockIdx.x) * (U * kBlock);
+    const uint64_t v0 = static_cast<uint64_t>(tile) * (U * kBlock);
     if (v0 < nv) {
-      const bool full = v0 + U * kBlock <= nv;
+      // This tile's vectors, [v0, v0 + nvt), as a byte range per buffer;
+      // lanes past the range read zeros and their stores are dropped.
+      const uint32_t nvt = static_cast<uint32_t>(min<uint64_t>(U * kBlock, nv - v0));
+      const uint32_t bytes = nvt * kVecBytes;
+      const uint64_t e0 = hb + v0 * VL;
+      const uint32_t voff = tid * kVecBytes;
       uint4 v[W][U];
 #pragma unroll
       for (int j = 0; j < W; ++j) {
-        const uint4* p = reinterpret_cast<const uint4*>(src[j] + hb) + v0 + tid;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(src[j] + e0, bytes);
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-          if (full || v0 + u * kBlock + tid < nv) v[j][u] = p[u * kBlock];
+        for (int u = 0; u < U; ++u) v[j][u] = load_stream(r, voff, u * kBlock * kVecBytes);
       }
+      uint4 o[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const uint64_t vi = v0 + u * kBlock + tid;
-        if (!full && vi >= nv) continue;
         A acc[VL];
         Elem<D>::unpack(v[0][u], acc);
 #pragma unroll
@@ -217,16 +225,22 @@ __global__ __launch_bounds__(kBlock) void fold_kernel(const FoldArgs a) {
         }
 #pragma unroll
         for (int l = 0; l < VL; ++l) acc[l] = finish<OP, W>(acc[l]);
-        const uint4 o = Elem<D>::pack(acc);
-        if constexpr (RS) {
-          reinterpret_cast<uint4*>(static_cast<S*>(a.dst[k]) + (hb - b))[vi] = o;
-        } else {
+        o[u] = Elem<D>::pack(acc);
+      }
+      if constexpr (RS) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(static_cast<S*>(a.dst[k]) + (e0 - b), bytes);
 #pragma unroll
-          for (int r = 0; r < W; ++r) reinterpret_cast<uint4*>(static_cast<S*>(a.dst[r]) + hb)[vi] = o;
+        for (int u = 0; u < U; ++u) store_through(r, voff, u * kBlock * kVecBytes, o[u]);
+      } else {
+#pragma unroll
+        for (int d = 0; d < W; ++d) {
+          const __amdgpu_buffer_rsrc_t r = make_rsrc(static_cast<S*>(a.dst[d]) + e0, bytes);
+#pragma unroll
+          for (int u = 0; u < U; ++u) store_through(r, voff, u * kBlock * kVecBytes, o[u]);
         }
       }
     }
-    if (blockIdx.x == 0) {
+    if (tile == 0) {
       const uint32_t nh = static_cast<uint32_t>(hb - b);
       const uint32_t nt = static_cast<uint32_t>(e - be);
       if (tid < nh) {
@@ -237,7 +251,7 @@ __global__ __launch_bounds__(kBlock) void fold_kernel(const FoldArgs a) {
     }
   } else {
     // Unaligned kernel: one element per lane per unit, still coalesced.
-    const uint64_t t0 = b + static_cast<uint64_t>(blockIdx.x) * (U * kBlock);
+    const uint64_t t0 = b + static_cast<uint64_t>(tile) * (U * kBlock);
     if (t0 >= e) return;
     const bool full = t0 + U * kBlock <= e;
     S x[W][U];

@@ -1,0 +1,54 @@
+// Memory-access helpers for gfx950 streaming kernels.
+//
+// Buffer resource descriptors give every workgroup a byte range checked by
+// the hardware: a dwordx4 lane whose offset lies outside the range loads
+// zeros and its store is dropped, so the ragged last tile of a segment needs
+// no per-lane predicate.  Loads carry the non-temporal hint (the data is
+// read exactly once, so it should not displace anything in L2 or the MALL),
+// stores the sc1 scope bit (written through instead of lingering dirty in the
+// XCD-private L2).  Both hints change speed only, never results.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rsx_internal.h"
+
+namespace rsx {
+
+// `aux` cache-policy operand of the buffer intrinsics on gfx950:
+// bit 0 = sc0, bit 1 = nt, bit 4 = sc1.
+constexpr int kLoadStream = 2;      // nt
+constexpr int kStoreThrough = 16;   // sc1
+// Descriptor word 3 of a raw (stride 0, untyped) buffer: 32-bit data format.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Tile run by workgroup `b` of an `nblocks` grid (a multiple of kXcds):
+// workgroup b lands on XCD b % 8, and the workgroups of one XCD take one
+// contiguous range of tiles, so each XCD streams through its own contiguous
+// region of every buffer (fewer pages per XCD translation cache, whole DRAM
+// rows per XCD).
+__device__ __forceinline__ uint32_t xcd_tile(uint32_t b, uint32_t nblocks) {
+  const uint32_t per = nblocks / kXcds;
+  return (b % kXcds) * per + b / kXcds;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           kRawBufferWord3);
+}
+
+__device__ __forceinline__ uint4 load_stream(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kLoadStream);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store_through(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                              const uint4& v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, kStoreThrough);
+}
+
+}  // namespace rsx

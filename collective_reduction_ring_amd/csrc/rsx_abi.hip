@@ -78,10 +78,13 @@ uint64_t fold_tiles(uint64_t seg, int world, bool vec, int vl) {
   return std::max<uint64_t>(1, (units + per - 1) / per);
 }
 
-rsx_status_t launch_fold_any(int dtype, int op, int world, bool rs, bool vec, const FoldArgs& a,
-                             uint64_t tiles, uint32_t nseg, hipStream_t s) {
-  if (tiles > 0x7fffffffull) return RSX_ERR_UNSUPPORTED;
-  const dim3 grid(static_cast<uint32_t>(tiles), nseg);
+rsx_status_t launch_fold_any(int dtype, int op, int world, bool rs, bool vec, FoldArgs a,
+                             uint64_t tiles_per_seg, uint32_t nseg, hipStream_t s) {
+  const uint64_t total = tiles_per_seg * nseg;
+  if (total > 0x7ffffff0ull) return RSX_ERR_UNSUPPORTED;
+  a.tiles_per_seg = static_cast<uint32_t>(tiles_per_seg);
+  a.tiles_total = static_cast<uint32_t>(total);
+  const dim3 grid(static_cast<uint32_t>(xcd_grid(total)));
   hipError_t e;
   switch (dtype) {
     case RSX_FLOAT32:

@@ -21,12 +21,18 @@ constexpr int kVecBytes = 16;      // one dwordx4 per lane per source
 // after it in ring order, so rot=1 is the ring (the block a ring position
 // starts at step 0 is the one owned by the position before it) and
 // rot=0 with one segment is rank order.
+//
+// Workgroups: `tiles_per_seg` tiles per segment, `tiles_total` = nseg *
+// tiles_per_seg in all, launched as a 1-D grid rounded up to a multiple of
+// the XCD count (see xcd_tile).
 struct FoldArgs {
   const void* src[RSX_MAX_RANKS];
   void* dst[RSX_MAX_RANKS];
   uint64_t count;
   uint64_t seg;
   uint32_t rot;
+  uint32_t tiles_per_seg;
+  uint32_t tiles_total;
 };
 
 // All-gather: dst[r][k*n + i] = src[k][i].
@@ -54,9 +60,16 @@ struct MultiCopyArgs {
   int n;
 };
 
-// Elements per thread per source in the fold kernels, by rank count: enough
-// dwordx4 loads in flight per lane to cover HBM latency without spilling.
-constexpr int fold_units(int world) { return world <= 2 ? 8 : world <= 4 ? 4 : world <= 8 ? 2 : 1; }
+// MI355X: 256 CUs in 8 XCDs, each XCD with its own L2.  Workgroups of one
+// launch are handed to the XCDs round-robin by workgroup id.
+constexpr uint32_t kXcds = 8;
+
+// dwordx4 per lane per source in the fold kernels, by rank count: with W
+// sources a lane already has W loads in flight; fewer sources get more units.
+constexpr int fold_units(int world) { return world <= 2 ? 4 : world <= 4 ? 2 : 1; }
+
+// Grid size for `tiles` tiles: a multiple of the XCD count.
+inline uint64_t xcd_grid(uint64_t tiles) { return (tiles + kXcds - 1) / kXcds * kXcds; }
 
 // Copy kernels: 16-byte units per thread per tile.
 constexpr int kCopyUnits = 4;
