@@ -10,12 +10,19 @@ Effective bytes per step = every input read once + every output written once
 = 8 * 256 MiB + 8 * 32 MiB = 2,415,919,104 B.  Peak HBM3E bandwidth of the
 MI355X: 8 TB/s.
 
+Layout: the W rank buffers are consecutive slices of one HBM allocation, as
+a flat gradient buffer per virtual rank would be (``--layout separate`` puts
+each rank in its own PyTorch allocation instead).
+
 Prints ONE JSON line on stdout; progress goes to stderr.
+
+``--calibrate-copy`` instead runs a plain 1 GiB device copy (the library's
+all-gather over one rank) a few times: the reference kernel of known size that
+rocprofv3's FETCH_SIZE / WRITE_SIZE counters are scaled by.
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import statistics
@@ -25,19 +32,10 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_reduce_scatter_w8_64Mi_f32.json")
-KERNEL_SOURCES = ("fold_impl.h", "fold_f32.hip", "rsx_internal.h")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def kernel_source_digest() -> str:
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "collective_reduction_ring_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()
 
 
 def recorded_traffic():
@@ -48,6 +46,9 @@ def recorded_traffic():
             rec = json.load(f)
     except (OSError, ValueError):
         return None
+    sys.path.insert(0, ROOT)
+    from collective_reduction_ring_amd.profiling import kernel_source_digest
+
     if rec.get("kernel_source_sha256") != kernel_source_digest():
         return None
     return rec.get("traffic_bytes_per_launch")
@@ -72,6 +73,20 @@ def cpu_baseline(xs, reps_budget_s: float):
     return out, statistics.median(times), len(times)
 
 
+def calibrate_copy(rsx, torch) -> int:
+    """Plain copy of 1 GiB (one-rank all-gather), 20 launches: counter calibration."""
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(20):
+        rsx.all_gather([src], [dst])
+    torch.cuda.synchronize()
+    ok = bool(torch.equal(src, dst))
+    print(json.dumps({"calibration": "copy", "bytes_read_per_launch": nbytes,
+                      "bytes_written_per_launch": nbytes, "launches": 20, "copy_ok": ok}), flush=True)
+    return 0 if ok else 1
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -80,6 +95,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="host time budget of the oracle baseline (whole passes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layout", choices=("arena", "separate"), default="arena")
+    ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -98,15 +115,26 @@ def main() -> int:
         log("no GPU visible")
         return 2
 
+    if args.calibrate_copy:
+        return calibrate_copy(rsx, torch)
+
     w = wl.WORKLOADS[2]
     world, n = w.world, w.n
     seg = n // world
     bytes_per_step = world * n * 4 + world * seg * 4
 
-    log(f"generating inputs: W={world}, {n} fp32 per rank")
+    log(f"generating inputs: W={world}, {n} fp32 per rank, layout {args.layout}")
     xs = wl.rank_inputs(2)
-    dev = [torch.from_numpy(x).to("cuda:0") for x in xs]
-    out = [torch.empty(seg, dtype=torch.float32, device="cuda:0") for _ in range(world)]
+    if args.layout == "arena":
+        arena_in = torch.empty(world * n, dtype=torch.float32, device="cuda:0")
+        arena_out = torch.empty(world * seg, dtype=torch.float32, device="cuda:0")
+        dev = [arena_in[r * n:(r + 1) * n] for r in range(world)]
+        out = [arena_out[r * seg:(r + 1) * seg] for r in range(world)]
+        for d, x in zip(dev, xs):
+            d.copy_(torch.from_numpy(x))
+    else:
+        dev = [torch.from_numpy(x).to("cuda:0") for x in xs]
+        out = [torch.empty(seg, dtype=torch.float32, device="cuda:0") for _ in range(world)]
     plan = rsx.ReduceScatter(dev, out, "sum")
     stream = torch.cuda.current_stream()
 
@@ -137,7 +165,7 @@ def main() -> int:
         f"min {min(launch_ms) * 1e3:.1f} us ({achieved:.0f} GB/s)")
 
     got = [o.cpu().numpy() for o in out]
-    del dev
+    del dev, out
 
     result = {
         "metric": "reduce-scatter effective HBM GB/s (W=8, 64Mi fp32/rank)",
@@ -160,6 +188,8 @@ def main() -> int:
             "recvcount": seg,
             "bytes_per_step": bytes_per_step,
             "parallelism": "one GPU; W ranks = W HBM buffers",
+            "layout": ("W rank buffers consecutive in one allocation" if args.layout == "arena"
+                       else "each rank buffer a separate PyTorch allocation"),
         },
         "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
         "roofline": {

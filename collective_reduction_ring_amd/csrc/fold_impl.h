@@ -152,22 +152,24 @@ __global__ __launch_bounds__(kBlock) void fold_kernel(const FoldArgs a) {
   constexpr int U = fold_units(W);
   constexpr int VL = D::kVL;
 
+  // Read every scalar argument up front: one round of kernarg loads.
+  const uint32_t tiles_total = a.tiles_total, magic = a.tps_magic, shift = a.tps_shift;
+  const uint32_t tps = a.tiles_per_seg, rot = a.rot;
   const uint32_t t = xcd_tile(blockIdx.x, gridDim.x);
-  if (t >= a.tiles_total) return;
-  const uint32_t k = t / a.tiles_per_seg;
-  const uint32_t tile = t - k * a.tiles_per_seg;
-  const uint64_t b = min(static_cast<uint64_t>(k) * a.seg, a.count);
-  const uint64_t e = min(b + a.seg, a.count);
+  if (t >= tiles_total) return;
+  const uint32_t k = static_cast<uint32_t>((static_cast<uint64_t>(t) * magic) >> shift);
+  const uint32_t tile = t - k * tps;
+  // Reduce-scatter segments are whole (count = W * seg); all-reduce ones are
+  // clipped to count.
+  const uint64_t b = RS ? static_cast<uint64_t>(k) * a.seg : min(static_cast<uint64_t>(k) * a.seg, a.count);
+  const uint64_t e = RS ? b + a.seg : min(b + a.seg, a.count);
 
-  // Ring rotation: source j of segment k is rank (k + rot + j) mod W.
-  const uint32_t first = (k + a.rot) % W;
+  // Ring rotation: source j of segment k is rank (k + rot + j) mod W, entry
+  // first + j of the doubled pointer table.
+  const uint32_t first = (k + rot) % W;
   const S* src[W];
 #pragma unroll
-  for (int j = 0; j < W; ++j) {
-    uint32_t r = first + j;
-    if (r >= static_cast<uint32_t>(W)) r -= W;
-    src[j] = static_cast<const S*>(a.src[r]);
-  }
+  for (int j = 0; j < W; ++j) src[j] = static_cast<const S*>(a.src[first + j]);
 
   // Fold and store one element (head, tail and the unaligned kernel).
   auto fold_element = [&](uint64_t idx) {
@@ -193,8 +195,9 @@ __global__ __launch_bounds__(kBlock) void fold_kernel(const FoldArgs a) {
     // aligned (checked on the host), so element offsets divisible by VL are
     // too.  Reduce-scatter segments start at such an offset (host check);
     // all-reduce segments may not, and take a scalar head and tail.
-    const uint64_t hb = min((b + VL - 1) / VL * VL, e);
-    const uint64_t be = max(hb, e / VL * VL);
+    // (For reduce-scatter the host guarantees seg % VL == 0: no head or tail.)
+    const uint64_t hb = RS ? b : min((b + VL - 1) / VL * VL, e);
+    const uint64_t be = RS ? e : max(hb, e / VL * VL);
     const uint64_t nv = (be - hb) / VL;
     const uint64_t v0 = static_cast<uint64_t>(tile) * (U * kBlock);
     if (v0 < nv) {
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(kBlock) void fold_kernel(const FoldArgs a) {
         }
       }
     }
-    if (tile == 0) {
+    if (!RS && tile == 0) {
       const uint32_t nh = static_cast<uint32_t>(hb - b);
       const uint32_t nt = static_cast<uint32_t>(e - be);
       if (tid < nh) {

@@ -84,6 +84,7 @@ rsx_status_t launch_fold_any(int dtype, int op, int world, bool rs, bool vec, Fo
   if (total > 0x7ffffff0ull) return RSX_ERR_UNSUPPORTED;
   a.tiles_per_seg = static_cast<uint32_t>(tiles_per_seg);
   a.tiles_total = static_cast<uint32_t>(total);
+  split_magic(a.tiles_per_seg, &a.tps_magic, &a.tps_shift);
   const dim3 grid(static_cast<uint32_t>(xcd_grid(total)));
   hipError_t e;
   switch (dtype) {
@@ -235,6 +236,7 @@ rsx_status_t rsx_reduce_scatter(const void* const* sendbufs, void* const* recvbu
   memset(&a, 0, sizeof(a));
   for (int r = 0; r < nranks; ++r) {
     a.src[r] = sendbufs[r];
+    a.src[r + nranks] = sendbufs[r];
     a.dst[r] = recvbufs[r];
   }
   a.count = n;
@@ -326,6 +328,7 @@ rsx_status_t rsx_all_reduce(const void* const* sendbufs, void* const* recvbufs, 
   memset(&a, 0, sizeof(a));
   for (int r = 0; r < nranks; ++r) {
     a.src[r] = sendbufs[r];
+    a.src[r + nranks] = sendbufs[r];
     a.dst[r] = recvbufs[r];
   }
   a.count = count;

@@ -24,16 +24,33 @@ constexpr int kVecBytes = 16;      // one dwordx4 per lane per source
 //
 // Workgroups: `tiles_per_seg` tiles per segment, `tiles_total` = nseg *
 // tiles_per_seg in all, launched as a 1-D grid rounded up to a multiple of
-// the XCD count (see xcd_tile).
+// the XCD count (see xcd_tile).  Tile t lies in segment
+// (t * tps_magic) >> tps_shift = t / tiles_per_seg (see split_magic).
 struct FoldArgs {
-  const void* src[RSX_MAX_RANKS];
-  void* dst[RSX_MAX_RANKS];
   uint64_t count;
   uint64_t seg;
   uint32_t rot;
   uint32_t tiles_per_seg;
   uint32_t tiles_total;
+  uint32_t tps_magic;
+  uint32_t tps_shift;
+  uint32_t pad_;
+  // src[r] and src[r + W] both hold rank r's buffer, so the W sources of a
+  // segment are the W consecutive entries from its first rank on.
+  const void* src[2 * RSX_MAX_RANKS];
+  void* dst[RSX_MAX_RANKS];
 };
+
+// Division of t < 2^31 by a fixed d in [1, 2^31) as a multiply and a shift:
+// with l = ceil(log2 d) and m = ceil(2^(31+l) / d) < 2^32, the error term of
+// t*m / 2^(31+l) against t/d is below t/2^(31+l) < 2^-l <= 1/d, too small to
+// reach the next integer, so floor(t*m / 2^(31+l)) = floor(t/d).
+inline void split_magic(uint32_t d, uint32_t* magic, uint32_t* shift) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  *magic = static_cast<uint32_t>(((1ull << (31 + l)) + d - 1) / d);
+  *shift = 31 + l;
+}
 
 // All-gather: dst[r][k*n + i] = src[k][i].
 struct GatherArgs {

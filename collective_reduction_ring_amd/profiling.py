@@ -1,0 +1,154 @@
+"""Turn rocprofv3 CSV output into the short summaries kept under ``profiles/``.
+
+* ``ktrace``: per-kernel duration statistics of a ``--kernel-trace --stats``
+  run, plus the mean over the last ``--timed`` dispatches of the named kernel
+  (the bench's timed window, after its warmup launches).
+* ``traffic``: HBM bytes per dispatch of a kernel from two ``--pmc`` runs
+  (FETCH_SIZE, then WRITE_SIZE, both in KiB per dispatch), each scaled by what
+  the same counter reads for a plain copy kernel of known size.  The record
+  carries a digest of the kernel's sources so that ``bench.py`` reports it
+  only while the kernel is unchanged.
+
+Usage::
+
+    python -m collective_reduction_ring_amd.profiling ktrace --trace T.csv --stats S.csv \\
+        --kernel fold_kernel --timed 100 --command "..." --out profiles/x.md
+    python -m collective_reduction_ring_amd.profiling traffic --fetch F.csv --write W.csv \\
+        --cal-fetch CF.csv --cal-write CW.csv --kernel fold_kernel --cal-kernel gather_kernel \\
+        --cal-bytes 1073741824 --algorithmic-bytes 2415919104 --commands "..." --out profiles/x.json
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import statistics
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+
+# Sources that determine the reduce-scatter fold kernel's machine code.
+FOLD_SOURCES = ("fold_impl.h", "fold_f32.hip", "mem.h", "rsx_internal.h")
+
+
+def kernel_source_digest(files=FOLD_SOURCES) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def counter_per_dispatch(path: str, counter: str, kernel: str) -> list[float]:
+    """Values of `counter` for every dispatch whose name contains `kernel`."""
+    return [float(r["Counter_Value"]) for r in _rows(path)
+            if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]]
+
+
+def ktrace_summary(trace: str, stats: str, kernel: str, timed: int, command: str) -> str:
+    srows = _rows(stats)
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            for r in _rows(trace) if kernel in r["Kernel_Name"]]
+    last = durs[-timed:] if timed else durs
+    lines = [
+        "# rocprofv3 kernel trace summary",
+        "",
+        "Command:",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        "| kernel | calls | average (us) | min (us) | max (us) | share |",
+        "|---|---|---|---|---|---|",
+    ]
+    for r in srows:
+        lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    lines += [
+        "",
+        f"`{kernel}`: {len(durs)} dispatches; mean of the last {len(last)} (the timed window): "
+        f"**{statistics.mean(last):.1f} us**, median {statistics.median(last):.1f} us, "
+        f"min {min(last):.1f} us.",
+        "",
+    ]
+    return "\n".join(lines)
+
+
+def traffic_record(fetch: str, write: str, cal_fetch: str, cal_write: str, kernel: str,
+                   cal_kernel: str, cal_bytes: int, algorithmic_bytes: int, commands: str) -> dict:
+    f = counter_per_dispatch(fetch, "FETCH_SIZE", kernel)
+    w = counter_per_dispatch(write, "WRITE_SIZE", kernel)
+    cf = counter_per_dispatch(cal_fetch, "FETCH_SIZE", cal_kernel)
+    cw = counter_per_dispatch(cal_write, "WRITE_SIZE", cal_kernel)
+    if not (f and w and cf and cw):
+        raise SystemExit("missing counter rows for the kernel or the calibration kernel")
+    fk, wk = statistics.mean(f), statistics.mean(w)
+    cfk, cwk = statistics.mean(cf), statistics.mean(cw)
+    f_scale = cal_bytes / (cfk * 1024.0)
+    w_scale = cal_bytes / (cwk * 1024.0)
+    fetch_b = fk * 1024.0 * f_scale
+    write_b = wk * 1024.0 * w_scale
+    return {
+        "kernel": kernel,
+        "kernel_source_sha256": kernel_source_digest(),
+        "dispatches": {"fetch": len(f), "write": len(w)},
+        "FETCH_SIZE_KiB_per_dispatch": round(fk, 3),
+        "WRITE_SIZE_KiB_per_dispatch": round(wk, 3),
+        "calibration": {
+            "kernel": cal_kernel,
+            "bytes_read_and_written_per_dispatch": cal_bytes,
+            "FETCH_SIZE_KiB_per_dispatch": round(cfk, 3),
+            "WRITE_SIZE_KiB_per_dispatch": round(cwk, 3),
+            "fetch_scale": round(f_scale, 6),
+            "write_scale": round(w_scale, 6),
+        },
+        "fetch_bytes_per_launch": round(fetch_b),
+        "write_bytes_per_launch": round(write_b),
+        "traffic_bytes_per_launch": round(fetch_b + write_b),
+        "algorithmic_bytes_per_launch": algorithmic_bytes,
+        "traffic_over_algorithmic": round((fetch_b + write_b) / algorithmic_bytes, 5),
+        "commands": commands,
+    }
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    k = sub.add_parser("ktrace")
+    k.add_argument("--trace", required=True)
+    k.add_argument("--stats", required=True)
+    k.add_argument("--kernel", required=True)
+    k.add_argument("--timed", type=int, default=0)
+    k.add_argument("--command", required=True)
+    k.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    for name in ("fetch", "write", "cal-fetch", "cal-write", "kernel", "cal-kernel", "commands", "out"):
+        t.add_argument(f"--{name}", required=True)
+    t.add_argument("--cal-bytes", type=int, required=True)
+    t.add_argument("--algorithmic-bytes", type=int, required=True)
+    a = ap.parse_args()
+    if a.cmd == "ktrace":
+        text = ktrace_summary(a.trace, a.stats, a.kernel, a.timed, a.command)
+        with open(a.out, "w") as f:
+            f.write(text)
+        print(text)
+    else:
+        rec = traffic_record(a.fetch, a.write, a.cal_fetch, a.cal_write, a.kernel, a.cal_kernel,
+                             a.cal_bytes, a.algorithmic_bytes, a.commands)
+        with open(a.out, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(json.dumps(rec, indent=1))
+
+
+if __name__ == "__main__":
+    main()
