@@ -87,6 +87,167 @@ def calibrate_copy(rsx, torch) -> int:
     return 0 if ok else 1
 
 
+def time_launches(fn, reps: int, warmup: int, torch) -> list:
+    """Per-call durations (ms) of `fn`, HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    st = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    en = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        st[i].record()
+        fn()
+        en[i].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in zip(st, en)]
+
+
+def graph_us_per_call(fn, inner: int, reps: int, torch) -> float:
+    """Device time per call: `inner` calls captured in one HIP graph, replayed
+    `reps` times; the median replay divided by `inner`."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(inner):
+            fn()
+    ms = time_launches(g.replay, reps, 2, torch)
+    return round(statistics.median(ms) * 1e3 / inner, 3)
+
+
+def _stat(ms: list, nbytes: int) -> dict:
+    avg = statistics.mean(ms)
+    return {"avg_us": round(avg * 1e3, 2), "median_us": round(statistics.median(ms) * 1e3, 2),
+            "min_us": round(min(ms) * 1e3, 2), "bytes": nbytes,
+            "GBps": round(nbytes / (avg * 1e-3) / 1e9, 1),
+            "pct_of_peak_hbm": round(100 * nbytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+
+
+def _arena(torch, dtype, world, n):
+    a = torch.empty(world * n, dtype=dtype, device="cuda:0")
+    return a, [a[r * n:(r + 1) * n] for r in range(world)]
+
+
+def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
+    """Timings of the workloads other than the headline one (one JSON line each)."""
+    reps, warm = args.steps, args.warmup
+    if name == "small":  # W=4, 4096 fp32 per rank: latency
+        xs = wl.rank_inputs(1)
+        _, dev = _arena(torch, torch.float32, 4, 4096)
+        for d, x in zip(dev, xs):
+            d.copy_(torch.from_numpy(x))
+        _, out = _arena(torch, torch.float32, 4, 1024)
+        _, ar = _arena(torch, torch.float32, 4, 4096)
+        rs = rsx.ReduceScatter(dev, out, "sum")
+        arp = rsx.AllReduce(dev, ar, "sum", "ring")
+        res = {"workload": "rs+ar sum fp32, W=4, 4096/rank",
+               "reduce_scatter": _stat(time_launches(rs, reps, warm, torch), 4 * 4096 * 4 + 4 * 1024 * 4),
+               "all_reduce": _stat(time_launches(arp, reps, warm, torch), 2 * 4 * 4096 * 4)}
+        res["reduce_scatter"]["graph_us_per_call"] = graph_us_per_call(rs, 100, 20, torch)
+        res["all_reduce"]["graph_us_per_call"] = graph_us_per_call(arp, 100, 20, torch)
+        return res
+    if name == "bf16_bucketed":
+        w = wl.WORKLOADS[3]
+        world, n, bucket = w.world, w.n, w.extra["bucket_elems"]
+        log("generating bf16 inputs")
+        xs = wl.rank_inputs(3)
+        _, dev = _arena(torch, torch.bfloat16, world, n)
+        for d, x in zip(dev, xs):
+            d.copy_(torch.from_numpy(x.view(np.int16)).view(torch.bfloat16))
+        del xs
+        _, out = _arena(torch, torch.bfloat16, world, n)
+        plans = []
+        for b0 in range(0, n, bucket):
+            b1 = min(b0 + bucket, n)
+            plans.append(rsx.AllReduce([d[b0:b1] for d in dev], [o[b0:b1] for o in out], "avg", "ring"))
+        step = lambda: [p() for p in plans]  # noqa: E731
+        res = {"workload": "all-reduce avg bf16 (fp32 accumulate), W=8, 134,217,728/rank, "
+                           f"{len(plans)} buckets of <= 25 MiB in sequence on one stream",
+               "ring_one_pass": _stat(time_launches(step, reps // 4 or 1, warm, torch), 2 * world * n * 2)}
+        # The same all-reduce composed of a reduce-scatter into a bf16 buffer of
+        # W segments, then an all-gather: more traffic, same bits.
+        _, seg_buf = _arena(torch, torch.bfloat16, world, bucket // world)
+        comp = []
+        for b0 in range(0, n, bucket):
+            b1 = min(b0 + bucket, n)
+            s = (b1 - b0) // world
+            segs = [t[:s] for t in seg_buf]
+            comp.append((rsx.ReduceScatter([d[b0:b1] for d in dev], segs, "avg"),
+                         segs, [o[b0:b1] for o in out]))
+
+        def step2():
+            for rs, segs, outs in comp:
+                rs()
+                rsx.all_gather(segs, outs)
+        st = _stat(time_launches(step2, reps // 4 or 1, warm, torch), 2 * world * n * 2)
+        st["actual_bytes"] = 2 * world * n * 2 + 2 * world * (n // world) * 2
+        res["rs_then_ag"] = st
+        return res
+    if name == "int32_w16":
+        w = wl.WORKLOADS[4]
+        world, n = w.world, w.n
+        seg = n // world
+        xs = wl.rank_inputs(4)
+        _, dev = _arena(torch, torch.int32, world, n)
+        for d, x in zip(dev, xs):
+            d.copy_(torch.from_numpy(x))
+        del xs
+        _, out = _arena(torch, torch.int32, world, seg)
+        _, ar = _arena(torch, torch.int32, world, n)
+        res = {"workload": "int32 W=16, 33,554,432/rank"}
+        for op in ("sum", "max"):
+            res[f"reduce_scatter_{op}"] = _stat(time_launches(rsx.ReduceScatter(dev, out, op), reps, warm, torch),
+                                                world * n * 4 + world * seg * 4)
+            res[f"all_reduce_{op}"] = _stat(time_launches(rsx.AllReduce(dev, ar, op, "ring"), reps, warm, torch),
+                                            2 * world * n * 4)
+        return res
+    if name == "fused":
+        world = 4
+        sizes = wl.fused_sizes()
+        per_rank = wl.fused_tensors(world, sizes)
+        tens = [[torch.from_numpy(t).to("cuda:0") for t in ts] for ts in per_rank]
+        total = int(sizes.sum())
+        _, fused = _arena(torch, torch.float32, world, total)
+        plan = rsx.FusedAllReduce(tens, fused, None, "sum", "ring")
+        pack = lambda: [p() for p in plan.packs]  # noqa: E731
+        arp = plan.reduce
+        unpack = lambda: [u() for u in plan.unpacks]  # noqa: E731
+        e2e = plan
+        nb = world * total * 4
+        return {"workload": f"fused: W=4, {len(sizes)} fp32 tensors, {total} elements/rank",
+                "pack": _stat(time_launches(pack, reps, warm, torch), 2 * nb),
+                "all_reduce": _stat(time_launches(arp, reps, warm, torch), 2 * nb),
+                "unpack": _stat(time_launches(unpack, reps, warm, torch), 2 * nb),
+                "end_to_end": _stat(time_launches(e2e, reps, warm, torch), 6 * nb)}
+    if name == "sweep":
+        res = {"workload": "all-reduce sum fp32, W=4, 1-32 KiB per rank: naive vs ring"}
+        for kib in wl.SWEEP_KIB:
+            xs = wl.sweep_inputs(kib)
+            n = len(xs[0])
+            _, dev = _arena(torch, torch.float32, 4, n)
+            for d, x in zip(dev, xs):
+                d.copy_(torch.from_numpy(x))
+            _, out = _arena(torch, torch.float32, 4, n)
+            row = {}
+            for algo in ("naive", "ring"):
+                p = rsx.AllReduce(dev, out, "sum", algo)
+                row[algo] = _stat(time_launches(p, 200, 20, torch), 2 * 4 * n * 4)
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(1000):
+                    p()
+                torch.cuda.synchronize()
+                row[algo]["wall_us_per_call"] = round((time.perf_counter() - t0) * 1e3, 2)
+                row[algo]["graph_us_per_call"] = graph_us_per_call(p, 100, 20, torch)
+            res[f"{kib}KiB"] = row
+        return res
+    raise SystemExit(f"unknown workload {name}")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,6 +258,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layout", choices=("arena", "separate"), default="arena")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--workload", default="rs_w8_f32",
+                    choices=("rs_w8_f32", "small", "bf16_bucketed", "int32_w16", "fused", "sweep"),
+                    help="rs_w8_f32 (default) is the headline line; the others print timings only")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -117,6 +281,9 @@ def main() -> int:
 
     if args.calibrate_copy:
         return calibrate_copy(rsx, torch)
+    if args.workload != "rs_w8_f32":
+        print(json.dumps(other_workload(args.workload, args, rsx, wl, torch, np)), flush=True)
+        return 0
 
     w = wl.WORKLOADS[2]
     world, n = w.world, w.n

@@ -163,44 +163,82 @@ def all_reduce_bucketed(inputs, outputs=None, bucket_elems: int = 13_107_200, op
         AllReduce([t[start:stop] for t in inputs], [t[start:stop] for t in outputs], op, algo)(stream)
 
 
+class _FuseCopy:
+    """A prepared pack (tensors -> fused) or unpack (fused -> tensors)."""
+
+    def __init__(self, tensors, fused: torch.Tensor, pack: bool):
+        counts = [t.numel() for t in tensors]
+        _check([fused], sum(counts), "fused", None, None)
+        for i, t in enumerate(tensors):
+            _check([t], counts[i], f"tensors[{i}]", fused.dtype, fused.device)
+        self.device = fused.device
+        self.pack = pack
+        lib = L.lib()
+        ptrs = L.ptr_array([t.data_ptr() for t in tensors])
+        sizes = L.size_array(counts)
+        code = _dtype_code(fused)
+        if pack:
+            self.fn, self.name = lib.rsx_fuse_pack, "rsx_fuse_pack"
+            self.args = (ptrs, sizes, len(tensors), fused.data_ptr(), code)
+        else:
+            self.fn, self.name = lib.rsx_fuse_unpack, "rsx_fuse_unpack"
+            self.args = (fused.data_ptr(), ptrs, sizes, len(tensors), code)
+        self.keep = (list(tensors), fused)
+
+    def __call__(self, stream=None) -> None:
+        with torch.cuda.device(self.device):
+            L.check(self.name, self.fn(*self.args, _stream_handle(stream)))
+
+
+class FusePack(_FuseCopy):
+    """Prepared copy of ``tensors`` back to back into ``fused`` (SINGA fusedSynch /
+    Horovod memcpy into the fusion buffer)."""
+
+    def __init__(self, tensors, fused):
+        super().__init__(tensors, fused, True)
+
+
+class FuseUnpack(_FuseCopy):
+    """Prepared copy of ``fused`` out into ``tensors`` at the same running offsets."""
+
+    def __init__(self, fused, tensors):
+        super().__init__(tensors, fused, False)
+
+
+class FusedAllReduce:
+    """Prepared pack -> in-place all-reduce of the fusion buffers -> unpack
+    (Horovod PerformOperation).  ``outputs_per_rank=None`` writes the results
+    back into the input tensors."""
+
+    def __init__(self, tensors_per_rank, fused_per_rank, outputs_per_rank=None, op: str = "sum",
+                 algo: str = "ring"):
+        outputs_per_rank = tensors_per_rank if outputs_per_rank is None else outputs_per_rank
+        self.packs = [FusePack(ts, f) for ts, f in zip(tensors_per_rank, fused_per_rank)]
+        self.reduce = AllReduce(list(fused_per_rank), None, op, algo)
+        self.unpacks = [FuseUnpack(f, ts) for f, ts in zip(fused_per_rank, outputs_per_rank)]
+
+    def __call__(self, stream=None) -> None:
+        for p in self.packs:
+            p(stream)
+        self.reduce(stream)
+        for u in self.unpacks:
+            u(stream)
+
+
 def fuse_pack(tensors, fused: torch.Tensor, stream=None) -> None:
-    """Copy ``tensors`` back to back into ``fused`` (SINGA fusedSynch / Horovod memcpy in)."""
-    counts = [t.numel() for t in tensors]
-    _check([fused], sum(counts), "fused", None, None)
-    for i, t in enumerate(tensors):
-        _check([t], counts[i], f"tensors[{i}]", fused.dtype, fused.device)
-    with torch.cuda.device(fused.device):
-        st = L.lib().rsx_fuse_pack(L.ptr_array([t.data_ptr() for t in tensors]),
-                                   L.size_array(counts), len(tensors), fused.data_ptr(),
-                                   _dtype_code(fused), _stream_handle(stream))
-    L.check("rsx_fuse_pack", st)
+    """Copy ``tensors`` back to back into ``fused``."""
+    FusePack(tensors, fused)(stream)
 
 
 def fuse_unpack(fused: torch.Tensor, tensors, stream=None) -> None:
     """Copy ``fused`` back out into ``tensors`` at the same running offsets."""
-    counts = [t.numel() for t in tensors]
-    _check([fused], sum(counts), "fused", None, None)
-    for i, t in enumerate(tensors):
-        _check([t], counts[i], f"tensors[{i}]", fused.dtype, fused.device)
-    with torch.cuda.device(fused.device):
-        st = L.lib().rsx_fuse_unpack(fused.data_ptr(), L.ptr_array([t.data_ptr() for t in tensors]),
-                                     L.size_array(counts), len(tensors), _dtype_code(fused),
-                                     _stream_handle(stream))
-    L.check("rsx_fuse_unpack", st)
+    FuseUnpack(fused, tensors)(stream)
 
 
 def fused_all_reduce(tensors_per_rank, fused_per_rank, outputs_per_rank=None, op: str = "sum",
                      algo: str = "ring", stream=None) -> None:
-    """pack -> in-place all-reduce of the fusion buffers -> unpack (Horovod PerformOperation).
-
-    ``outputs_per_rank=None`` writes the results back into the input tensors.
-    """
-    outputs_per_rank = tensors_per_rank if outputs_per_rank is None else outputs_per_rank
-    for ts, f in zip(tensors_per_rank, fused_per_rank):
-        fuse_pack(ts, f, stream)
-    all_reduce(list(fused_per_rank), None, op, algo, stream)
-    for f, ts in zip(fused_per_rank, outputs_per_rank):
-        fuse_unpack(f, ts, stream)
+    """pack -> in-place all-reduce of the fusion buffers -> unpack."""
+    FusedAllReduce(tensors_per_rank, fused_per_rank, outputs_per_rank, op, algo)(stream)
 
 
 def segment_begin(count: int, nranks: int, k: int) -> int:

@@ -8,10 +8,13 @@
 // Pack/unpack (Apache SINGA communicator.cc fusedSynch; Horovod
 // operations.cc PerformOperation) copy many tensors to or from running
 // offsets of one fusion buffer.  One launch carries up to RSX_FUSE_BATCH
-// (src, dst, bytes) descriptors in its kernel arguments; workgroup b finds its
+// (src, dst, bytes) descriptors in its kernel arguments; a workgroup finds its
 // descriptor from the prefix sums of per-descriptor tile counts.  Offsets in
-// the fusion buffer are back to back, so a descriptor's src and dst need not
-// share 16-byte alignment: the host picks the widest unit both allow.
+// the fusion buffer are back to back, so src and dst of one copy are often
+// not 16-byte aligned relative to each other: every lane still stores
+// aligned dwordx4 vectors, assembling each from the two aligned source
+// vectors it straddles (v_alignbyte), so both sides move in 16-byte units.
+#include "mem.h"
 #include "rsx_internal.h"
 
 namespace rsx {
@@ -33,25 +36,45 @@ template <int ES, bool VEC>
 __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a) {
   using T = typename std::conditional<VEC, uint4, typename Unit<ES>::T>::type;
   constexpr int U = kCopyUnits;
-  const uint32_t k = blockIdx.y;
+  const uint32_t t = xcd_tile(blockIdx.x, gridDim.x);
+  if (t >= a.tiles_total) return;
+  const uint32_t k = static_cast<uint32_t>((static_cast<uint64_t>(t) * a.tps_magic) >> a.tps_shift);
+  const uint32_t tile = t - k * a.tiles_per_piece;
   const uint64_t nbytes = a.n * ES;
   const uint64_t nu = nbytes / sizeof(T);
-  const uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * (U * kBlock);
+  const uint64_t t0 = static_cast<uint64_t>(tile) * (U * kBlock);
   if (t0 >= nu) return;
-  const bool full = t0 + U * kBlock <= nu;
   const uint32_t tid = threadIdx.x;
-  const T* src = static_cast<const T*>(a.src[k]) + t0 + tid;
-  T v[U];
+  const char* srcb = static_cast<const char*>(a.src[k]);
+  if constexpr (VEC) {
+    // Whole 16-byte vectors; the descriptor range drops lanes past the piece.
+    const uint32_t bytes = static_cast<uint32_t>(min<uint64_t>(U * kBlock, nu - t0)) * kVecBytes;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(srcb + t0 * kVecBytes, bytes);
+    uint4 v[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u)
-    if (full || t0 + u * kBlock + tid < nu) v[u] = src[u * kBlock];
-  for (int r = 0; r < a.world; ++r) {
-    char* base = static_cast<char*>(a.dst[r]) + k * nbytes;
-    if (base == static_cast<const char*>(a.src[k])) continue;  // in-place piece
-    T* dst = reinterpret_cast<T*>(base) + t0 + tid;
+    for (int u = 0; u < U; ++u) v[u] = load_stream(rs, tid * kVecBytes, u * kBlock * kVecBytes);
+    for (int r = 0; r < a.world; ++r) {
+      char* base = static_cast<char*>(a.dst[r]) + k * nbytes;
+      if (base == srcb) continue;  // in-place piece
+      const __amdgpu_buffer_rsrc_t rd = make_rsrc(base + t0 * kVecBytes, bytes);
+#pragma unroll
+      for (int u = 0; u < U; ++u) store_b128<kStoreStream>(rd, tid * kVecBytes, u * kBlock * kVecBytes, v[u]);
+    }
+  } else {
+    const bool full = t0 + U * kBlock <= nu;
+    const T* src = reinterpret_cast<const T*>(srcb) + t0 + tid;
+    T v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (full || t0 + u * kBlock + tid < nu) dst[u * kBlock] = v[u];
+      if (full || t0 + u * kBlock + tid < nu) v[u] = src[u * kBlock];
+    for (int r = 0; r < a.world; ++r) {
+      char* base = static_cast<char*>(a.dst[r]) + k * nbytes;
+      if (base == srcb) continue;  // in-place piece
+      T* dst = reinterpret_cast<T*>(base) + t0 + tid;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (full || t0 + u * kBlock + tid < nu) dst[u * kBlock] = v[u];
+    }
   }
 }
 
@@ -72,70 +95,95 @@ hipError_t launch_gather(int esize, bool vec, const GatherArgs& a, dim3 grid, hi
 
 // -------------------------------------------------------- pack / unpack
 
-// Copy `n` units of type T from s to d, tile `t` of U*256 units.
-template <class T>
-__device__ __forceinline__ void copy_tile(const T* s, T* d, uint64_t n, uint32_t t) {
-  constexpr int U = kCopyUnits;
-  const uint64_t t0 = static_cast<uint64_t>(t) * (U * kBlock);
-  if (t0 >= n) return;
-  const bool full = t0 + U * kBlock <= n;
-  const uint32_t tid = threadIdx.x;
-  T v[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-    if (full || t0 + u * kBlock + tid < n) v[u] = s[t0 + u * kBlock + tid];
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-    if (full || t0 + u * kBlock + tid < n) d[t0 + u * kBlock + tid] = v[u];
+// Bytes [delta, delta + 16) of the 32-byte concatenation lo:hi, delta a
+// multiple of 2 in [2, 14] (Q = delta / 4 whole words, then r bytes).
+template <int Q>
+__device__ __forceinline__ uint4 funnel_q(const uint32_t (&w)[8], uint32_t r) {
+  return make_uint4(__builtin_amdgcn_alignbyte(w[Q + 1], w[Q], r),
+                    __builtin_amdgcn_alignbyte(w[Q + 2], w[Q + 1], r),
+                    __builtin_amdgcn_alignbyte(w[Q + 3], w[Q + 2], r),
+                    __builtin_amdgcn_alignbyte(w[Q + 4], w[Q + 3], r));
 }
 
-// Copy a body of `W`-byte units aligned on both sides, with an element-size
-// head and tail; tile 0 of the descriptor also copies the head and tail.
-template <int ES, class W>
-__device__ __forceinline__ void copy_aligned(const char* s, char* d, uint64_t bytes, uint32_t t) {
-  using E = typename Unit<ES>::T;
-  constexpr uint64_t WB = sizeof(W);
-  const uint64_t head = min((WB - (reinterpret_cast<uintptr_t>(s) & (WB - 1))) & (WB - 1), bytes);
-  const uint64_t body = (bytes - head) / WB;
-  const uint64_t tail = bytes - head - body * WB;
-  copy_tile<W>(reinterpret_cast<const W*>(s + head), reinterpret_cast<W*>(d + head), body, t);
-  if (t == 0) {
-    const uint32_t nh = static_cast<uint32_t>(head / ES);
-    const uint32_t nt = static_cast<uint32_t>(tail / ES);
-    const uint32_t tid = threadIdx.x;
-    if (tid < nh) {
-      reinterpret_cast<E*>(d)[tid] = reinterpret_cast<const E*>(s)[tid];
-    } else if (tid < nh + nt) {
-      const uint64_t off = head + body * WB;
-      reinterpret_cast<E*>(d + off)[tid - nh] = reinterpret_cast<const E*>(s + off)[tid - nh];
-    }
+__device__ __forceinline__ uint4 funnel(const uint4& lo, const uint4& hi, uint32_t delta) {
+  const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  const uint32_t r = delta & 3u;
+  switch (delta >> 2) {  // uniform per copy
+    case 0:
+      return funnel_q<0>(w, r);
+    case 1:
+      return funnel_q<1>(w, r);
+    case 2:
+      return funnel_q<2>(w, r);
+    default:
+      return funnel_q<3>(w, r);
   }
 }
 
 template <int ES>
 __global__ __launch_bounds__(kBlock) void multicopy_kernel(const MultiCopyArgs a) {
-  // Descriptor of this workgroup: the last i with tile_start[i] <= blockIdx.x.
-  const uint32_t b = blockIdx.x;
+  using E = typename Unit<ES>::T;
+  constexpr int U = kCopyUnits;
+  const uint32_t t = xcd_tile(blockIdx.x, gridDim.x);
+  if (t >= a.tile_start[a.n]) return;
+  // Descriptor of this tile: the last i with tile_start[i] <= t.
   int lo = 0, hi = a.n - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) / 2;
-    if (a.tile_start[mid] <= b) lo = mid; else hi = mid - 1;
+    if (a.tile_start[mid] <= t) lo = mid; else hi = mid - 1;
   }
-  const CopyDesc& d = a.d[lo];
-  const uint32_t t = b - a.tile_start[lo];
-  const char* s = static_cast<const char*>(d.src);
-  char* o = static_cast<char*>(d.dst);
-  if (d.path == 0) {
-    copy_aligned<ES, uint4>(s, o, d.bytes, t);
-  } else if (d.path == 1) {
-    copy_aligned<ES, uint32_t>(s, o, d.bytes, t);
-  } else {
-    using E = typename Unit<ES>::T;
-    copy_tile<E>(reinterpret_cast<const E*>(s), reinterpret_cast<E*>(o), d.bytes / ES, t);
+  const char* s = static_cast<const char*>(a.d[lo].src);
+  char* o = static_cast<char*>(a.d[lo].dst);
+  const uint64_t n = a.d[lo].bytes;
+  const uint32_t tile = t - a.tile_start[lo];
+  const uint32_t tid = threadIdx.x;
+
+  // [0, h): head bytes up to the first aligned destination byte;
+  // [h, h + 16 m): m aligned destination vectors; then a tail below 16 bytes.
+  const uint64_t h = min<uint64_t>((16u - (reinterpret_cast<uintptr_t>(o) & 15u)) & 15u, n);
+  const uint64_t m = (n - h) / 16;
+  const uint64_t j0 = static_cast<uint64_t>(tile) * (U * kBlock);
+  if (j0 < m) {
+    const uint32_t nvt = static_cast<uint32_t>(min<uint64_t>(U * kBlock, m - j0));
+    const char* s1 = s + h + 16 * j0;
+    char* o1 = o + h + 16 * j0;
+    const uint32_t delta = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s1) & 15u);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(o1, nvt * 16);
+    uint4 v[U];
+    if (delta == 0) {
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(s1, nvt * 16);
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = load_stream(rs, tid * 16, u * kBlock * 16);
+    } else {
+      // The aligned 16-byte source chunks overlapping this tile's bytes:
+      // nvt + 1 of them, starting delta bytes before s1.  They lie in the
+      // pages of the source bytes, and the descriptor range ends with them.
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(s1 - delta, (nvt + 1) * 16);
+      uint4 x0[U], x1[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        x0[u] = load_stream(rs, tid * 16, u * kBlock * 16);
+        x1[u] = load_stream(rs, tid * 16 + 16, u * kBlock * 16);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = funnel(x0[u], x1[u], delta);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) store_b128<0>(rd, tid * 16, u * kBlock * 16, v[u]);
+  }
+  if (tile == 0) {
+    const uint32_t nh = static_cast<uint32_t>(h / ES);
+    const uint32_t nt = static_cast<uint32_t>((n - h - 16 * m) / ES);
+    if (tid < nh) {
+      reinterpret_cast<E*>(o)[tid] = reinterpret_cast<const E*>(s)[tid];
+    } else if (tid < nh + nt) {
+      const uint64_t off = h + 16 * m;
+      reinterpret_cast<E*>(o + off)[tid - nh] = reinterpret_cast<const E*>(s + off)[tid - nh];
+    }
   }
 }
 
-hipError_t launch_multicopy(int esize, const MultiCopyArgs& a, uint32_t blocks, hipStream_t s) {
+hipError_t launch_multicopy(int esize, const MultiCopyArgs& a, hipStream_t s) {
   void* args[] = {const_cast<MultiCopyArgs*>(&a)};
   const void* fn;
   if (esize == 2) {
@@ -145,7 +193,8 @@ hipError_t launch_multicopy(int esize, const MultiCopyArgs& a, uint32_t blocks, 
   } else {
     return hipErrorInvalidValue;
   }
-  return hipLaunchKernel(fn, dim3(blocks), dim3(kBlock), args, 0, s);
+  const uint64_t tiles = a.tile_start[a.n];
+  return hipLaunchKernel(fn, dim3(static_cast<uint32_t>(xcd_grid(tiles))), dim3(kBlock), args, 0, s);
 }
 
 }  // namespace rsx

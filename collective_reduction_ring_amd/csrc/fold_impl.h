@@ -233,13 +233,13 @@ __global__ __launch_bounds__(kBlock) void fold_kernel(const FoldArgs a) {
       if constexpr (RS) {
         const __amdgpu_buffer_rsrc_t r = make_rsrc(static_cast<S*>(a.dst[k]) + (e0 - b), bytes);
 #pragma unroll
-        for (int u = 0; u < U; ++u) store_through(r, voff, u * kBlock * kVecBytes, o[u]);
+        for (int u = 0; u < U; ++u) store_b128<kStoreThrough>(r, voff, u * kBlock * kVecBytes, o[u]);
       } else {
 #pragma unroll
         for (int d = 0; d < W; ++d) {
           const __amdgpu_buffer_rsrc_t r = make_rsrc(static_cast<S*>(a.dst[d]) + e0, bytes);
 #pragma unroll
-          for (int u = 0; u < U; ++u) store_through(r, voff, u * kBlock * kVecBytes, o[u]);
+          for (int u = 0; u < U; ++u) store_b128<kStoreStream>(r, voff, u * kBlock * kVecBytes, o[u]);
         }
       }
     }

@@ -4,9 +4,14 @@
 // the hardware: a dwordx4 lane whose offset lies outside the range loads
 // zeros and its store is dropped, so the ragged last tile of a segment needs
 // no per-lane predicate.  Loads carry the non-temporal hint (the data is
-// read exactly once, so it should not displace anything in L2 or the MALL),
-// stores the sc1 scope bit (written through instead of lingering dirty in the
-// XCD-private L2).  Both hints change speed only, never results.
+// read exactly once, so it should not displace anything in L2 or the MALL).
+// Stores take one of two hints, by how much a kernel writes: a small output
+// (a reduce-scatter writes 1/W of what it reads) is written with the sc1
+// scope bit, through the XCD-private L2 into the memory-side cache, while a
+// large one (an all-reduce writes as much as it reads, far more than the
+// 256 MB MALL) streams past the caches with the non-temporal hint.  Measured
+// on MI355X, each choice is the faster one for its kernel.  The hints change
+// speed only, never results.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,6 +25,7 @@ namespace rsx {
 // bit 0 = sc0, bit 1 = nt, bit 4 = sc1.
 constexpr int kLoadStream = 2;      // nt
 constexpr int kStoreThrough = 16;   // sc1
+constexpr int kStoreStream = 2;     // nt
 // Descriptor word 3 of a raw (stride 0, untyped) buffer: 32-bit data format.
 constexpr int kRawBufferWord3 = 0x00020000;
 
@@ -45,10 +51,11 @@ __device__ __forceinline__ uint4 load_stream(__amdgpu_buffer_rsrc_t r, uint32_t 
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-__device__ __forceinline__ void store_through(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
-                                              const uint4& v) {
+template <int AUX>
+__device__ __forceinline__ void store_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                           const uint4& v) {
   const u32x4 w = {v.x, v.y, v.z, v.w};
-  __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, kStoreThrough);
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, AUX);
 }
 
 }  // namespace rsx

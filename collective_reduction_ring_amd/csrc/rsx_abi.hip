@@ -144,49 +144,31 @@ rsx_status_t fuse_copy(const void* const* tens, const size_t* counts, int ntenso
   }
 
   // Batches of RSX_FUSE_BATCH descriptors per launch.
-  const uint64_t per = static_cast<uint64_t>(kCopyUnits) * kBlock;
   size_t off = 0;
   int i = 0;
   while (i < ntensors) {
     MultiCopyArgs a;
     memset(&a, 0, sizeof(a));
-    uint64_t blocks = 0;
+    uint64_t tiles = 0;
     while (i < ntensors && a.n < RSX_FUSE_BATCH) {
       const size_t bytes = counts[i] * es;
       if (bytes != 0) {
         const char* fz = static_cast<const char*>(fused) + off;
-        const void* s = pack ? tens[i] : static_cast<const void*>(fz);
-        void* d = pack ? const_cast<char*>(fz) : const_cast<void*>(tens[i]);
-        const uintptr_t x = reinterpret_cast<uintptr_t>(s) ^ reinterpret_cast<uintptr_t>(d);
         CopyDesc& c = a.d[a.n];
-        c.src = s;
-        c.dst = d;
+        c.src = pack ? tens[i] : static_cast<const void*>(fz);
+        c.dst = pack ? const_cast<char*>(fz) : const_cast<void*>(tens[i]);
         c.bytes = bytes;
-        uint64_t units;
-        if ((x & 15u) == 0) {
-          c.path = 0;
-          units = bytes / 16;
-        } else if ((x & 3u) == 0) {
-          c.path = 1;
-          units = bytes / 4;
-        } else {
-          c.path = 2;
-          units = bytes / es;
-        }
-        const uint64_t tiles = std::max<uint64_t>(1, (units + per - 1) / per);
-        if (blocks + tiles > 0x7fffffffull) return RSX_ERR_UNSUPPORTED;
-        c.tiles = static_cast<uint32_t>(tiles);
-        a.tile_start[a.n] = static_cast<uint32_t>(blocks);
-        blocks += tiles;
+        a.tile_start[a.n] = static_cast<uint32_t>(tiles);
+        tiles += copy_tiles(c.dst, bytes);
+        if (tiles > 0x7ffffff0ull) return RSX_ERR_UNSUPPORTED;
         a.n += 1;
       }
       off += bytes;
       ++i;
     }
     if (a.n == 0) continue;
-    a.tile_start[a.n] = static_cast<uint32_t>(blocks);
-    const rsx_status_t st =
-        hip_status(launch_multicopy(static_cast<int>(es), a, static_cast<uint32_t>(blocks), stream));
+    a.tile_start[a.n] = static_cast<uint32_t>(tiles);
+    const rsx_status_t st = hip_status(launch_multicopy(static_cast<int>(es), a, stream));
     if (st != RSX_SUCCESS) return st;
   }
   return RSX_SUCCESS;
@@ -287,10 +269,13 @@ rsx_status_t rsx_all_gather(const void* const* sendbufs, void* const* recvbufs, 
   const uint64_t units = vec ? piece_bytes / kVecBytes : sendcount;
   const uint64_t per = static_cast<uint64_t>(kCopyUnits) * kBlock;
   const uint64_t tiles = std::max<uint64_t>(1, (units + per - 1) / per);
-  if (tiles > 0x7fffffffull) return RSX_ERR_UNSUPPORTED;
+  const uint64_t total = tiles * static_cast<uint64_t>(nranks);
+  if (total > 0x7ffffff0ull) return RSX_ERR_UNSUPPORTED;
+  a.tiles_per_piece = static_cast<uint32_t>(tiles);
+  a.tiles_total = static_cast<uint32_t>(total);
+  split_magic(a.tiles_per_piece, &a.tps_magic, &a.tps_shift);
   return hip_status(launch_gather(static_cast<int>(es), vec, a,
-                                  dim3(static_cast<uint32_t>(tiles), static_cast<uint32_t>(nranks)),
-                                  stream));
+                                  dim3(static_cast<uint32_t>(xcd_grid(total))), stream));
 }
 
 rsx_status_t rsx_all_reduce(const void* const* sendbufs, void* const* recvbufs, int nranks,

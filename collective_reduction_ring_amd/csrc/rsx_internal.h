@@ -52,25 +52,28 @@ inline void split_magic(uint32_t d, uint32_t* magic, uint32_t* shift) {
   *shift = 31 + l;
 }
 
-// All-gather: dst[r][k*n + i] = src[k][i].
+// All-gather: dst[r][k*n + i] = src[k][i].  Tiles as in FoldArgs: piece k
+// owns tiles [k*tiles_per_piece, (k+1)*tiles_per_piece).
 struct GatherArgs {
   const void* src[RSX_MAX_RANKS];
   void* dst[RSX_MAX_RANKS];
   uint64_t n;
   int world;
+  uint32_t tiles_per_piece;
+  uint32_t tiles_total;
+  uint32_t tps_magic;
+  uint32_t tps_shift;
 };
 
-// One copy of a pack/unpack batch.  `path` is chosen on the host from the
-// relative alignment of src and dst: 0 = dwordx4 body with element-size head
-// and tail, 1 = dword body, 2 = element-size (2-byte) copies.
+// One copy of a pack/unpack batch: `bytes` from src to dst, cut into
+// `copy_tiles(...)` tiles of 16-byte destination vectors.
 struct CopyDesc {
   const void* src;
   void* dst;
   uint64_t bytes;
-  uint32_t path;
-  uint32_t tiles;
 };
 
+// A batch of copies; descriptor i owns tiles [tile_start[i], tile_start[i+1]).
 struct MultiCopyArgs {
   CopyDesc d[RSX_FUSE_BATCH];
   uint32_t tile_start[RSX_FUSE_BATCH + 1];
@@ -91,6 +94,18 @@ inline uint64_t xcd_grid(uint64_t tiles) { return (tiles + kXcds - 1) / kXcds * 
 // Copy kernels: 16-byte units per thread per tile.
 constexpr int kCopyUnits = 4;
 
+// Bytes before the first 16-byte-aligned destination byte, at most `bytes`.
+inline uint64_t copy_head(const void* dst, uint64_t bytes) {
+  const uint64_t h = (16 - (reinterpret_cast<uintptr_t>(dst) & 15u)) & 15u;
+  return h < bytes ? h : bytes;
+}
+// Tiles of a copy: whole aligned destination vectors, kCopyUnits per lane.
+inline uint64_t copy_tiles(const void* dst, uint64_t bytes) {
+  const uint64_t vecs = (bytes - copy_head(dst, bytes)) / 16;
+  const uint64_t per = static_cast<uint64_t>(kCopyUnits) * kBlock;
+  return vecs == 0 ? 1 : (vecs + per - 1) / per;
+}
+
 // Launchers, one per dtype translation unit.  `rs` selects the reduce-scatter
 // store (block k to dst[k]) over the all-reduce store (every element to every
 // dst[r]); `vec` selects the dwordx4 kernel.  Return the launch status.
@@ -102,6 +117,6 @@ hipError_t launch_fold_i32(int op, int world, bool rs, bool vec, const FoldArgs&
                            dim3 grid, hipStream_t s);
 
 hipError_t launch_gather(int esize, bool vec, const GatherArgs& a, dim3 grid, hipStream_t s);
-hipError_t launch_multicopy(int esize, const MultiCopyArgs& a, uint32_t blocks, hipStream_t s);
+hipError_t launch_multicopy(int esize, const MultiCopyArgs& a, hipStream_t s);
 
 }  // namespace rsx

@@ -205,6 +205,40 @@ def test_side_stream_and_repeat():
         assert_parity(to_host(out[k], "f32"), want[k], "f32", f"block {k}")
 
 
+def test_graph_capture_replays():
+    # Library launches captured in a HIP graph: every replay, with eager work
+    # and synchronisation in between, must equal the eager result.
+    w, n = 4, 4 * 1024 + 12
+    xs = inputs(10, w, n, "f32")
+    dev = [to_dev(x, "f32") for x in xs]
+    out_rs = [empty(n // w, "f32") for _ in range(w)]
+    out_ar = [empty(n, "f32") for _ in range(w)]
+    rs = rsx.ReduceScatter(dev, out_rs, "sum")
+    ar = rsx.AllReduce(dev, out_ar, "max", "ring")
+    want_rs = oracle.reduce_scatter(xs, "sum", "f32")
+    want_ar = oracle.all_reduce(xs, "max", "f32")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        rs()
+        ar()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    say("graph capture rs + ar")
+    with torch.cuda.graph(g):
+        rs()
+        ar()
+    for rep in range(4):
+        for o in out_rs + out_ar:
+            o.fill_(-7.0)                     # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in range(w):
+            assert_parity(to_host(out_rs[k], "f32"), want_rs[k], "f32", f"replay {rep} rs {k}")
+            assert_parity(to_host(out_ar[k], "f32"), want_ar[k], "f32", f"replay {rep} ar {k}")
+
+
 # ---------------------------------------------------------- all-gather ------
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
