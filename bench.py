@@ -259,7 +259,8 @@ def main() -> int:
     ap.add_argument("--layout", choices=("arena", "separate"), default="arena")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--workload", default="rs_w8_f32",
-                    choices=("rs_w8_f32", "small", "bf16_bucketed", "int32_w16", "fused", "sweep"),
+                    choices=("rs_w8_f32", "small", "bf16_bucketed", "int32_w16", "fused", "sweep",
+                             "ceilings"),
                     help="rs_w8_f32 (default) is the headline line; the others print timings only")
     args = ap.parse_args()
 
@@ -267,6 +268,15 @@ def main() -> int:
         log(f"bench.py measures one GPU only: the W ranks are buffers of a single MI355X; "
             f"--gpus {args.gpus} is not supported")
         return 2
+
+    if args.workload == "ceilings":
+        # A child process of its own, started before this one touches the GPU.
+        import subprocess
+        tool = os.path.join(ROOT, "collective_reduction_ring_amd", "tools", "hbm_ceiling")
+        if not os.path.exists(tool):
+            log(f"{tool} is not built; run `python -m collective_reduction_ring_amd.build`")
+            return 2
+        return subprocess.run([tool]).returncode
 
     import numpy as np
     import torch
@@ -311,25 +321,28 @@ def main() -> int:
     torch.cuda.synchronize()
 
     k = args.steps
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(k)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(k)]
+    # Timed region: K launches back to back on the launch stream, bracketed by
+    # one pair of HIP events (device time) and the host clock (wall time).
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     log(f"timing {k} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(k):
-        starts[i].record(stream)
+    ev0.record(stream)
+    for _ in range(k):
         plan()
-        ends[i].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     elapsed = t1 - t0
-    avg_launch_s = statistics.mean(launch_ms) / 1e3
+    avg_launch_s = ev0.elapsed_time(ev1) / 1e3 / k
     value = bytes_per_step * k / elapsed / 1e9
     achieved = bytes_per_step / avg_launch_s / 1e9
-    log(f"wall {elapsed * 1e6 / k:.1f} us/step ({value:.0f} GB/s); kernel avg "
-        f"{avg_launch_s * 1e6:.1f} us, median {statistics.median(launch_ms) * 1e3:.1f} us, "
-        f"min {min(launch_ms) * 1e3:.1f} us ({achieved:.0f} GB/s)")
+    # Spread of single launches (each between its own pair of events), after the timed region.
+    launch_ms = time_launches(plan, 20, 0, torch)
+    log(f"wall {elapsed * 1e6 / k:.1f} us/step ({value:.0f} GB/s); kernel avg {avg_launch_s * 1e6:.1f} us "
+        f"({achieved:.0f} GB/s); single launches median {statistics.median(launch_ms) * 1e3:.1f} us, "
+        f"min {min(launch_ms) * 1e3:.1f} us")
 
     got = [o.cpu().numpy() for o in out]
     del dev, out
@@ -368,6 +381,7 @@ def main() -> int:
             "traffic": recorded_traffic(),
             "kernel": "rsx::fold_kernel<F32T, RSX_SUM, 8, rs, dwordx4>",
             "avg_launch_us": round(avg_launch_s * 1e6, 2),
+            "single_launch_median_us": round(statistics.median(launch_ms) * 1e3, 2),
             "algorithmic_bytes_per_launch": bytes_per_step,
         },
     }

@@ -18,7 +18,7 @@ RSX_SUM, RSX_MAX, RSX_MIN, RSX_AVG = 0, 1, 2, 3
 RSX_ALGO_RING, RSX_ALGO_NAIVE, RSX_ALGO_AUTO = 0, 1, 2
 RSX_MAX_RANKS = 16
 RSX_NAIVE_MAX_BYTES = 32768
-RSX_FUSE_BATCH = 32
+RSX_FUSE_BATCH = 64
 
 STATUS = {
     0: "RSX_SUCCESS",

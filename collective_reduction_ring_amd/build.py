@@ -19,6 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librsx.so")
 ARCH = os.environ.get("RSX_OFFLOAD_ARCH", "gfx950")
+TOOL_SRC = os.path.join(PKG, "tools", "hbm_ceiling.cpp")
+TOOL = os.path.join(PKG, "tools", "hbm_ceiling")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
@@ -64,6 +66,11 @@ def build(verbose: bool = True, jobs: int | None = None) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    # HBM ceiling microbenchmark (a standalone executable, run by bench.py).
+    cmd = [HIPCC, *CFLAGS, "-x", "hip", TOOL_SRC, "-o", TOOL]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {TOOL_SRC}:\n{r.stdout}\n{r.stderr}")
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources", file=sys.stderr)
     return LIB

@@ -1,8 +1,9 @@
 """Turn rocprofv3 CSV output into the short summaries kept under ``profiles/``.
 
 * ``ktrace``: per-kernel duration statistics of a ``--kernel-trace --stats``
-  run, plus the mean over the last ``--timed`` dispatches of the named kernel
-  (the bench's timed window, after its warmup launches).
+  run, plus the mean over dispatches ``[skip, skip + timed)`` of the named
+  kernel (the bench's timed window: after its warmup launches, before the
+  launches it times one by one).
 * ``traffic``: HBM bytes per dispatch of a kernel from two ``--pmc`` runs
   (FETCH_SIZE, then WRITE_SIZE, both in KiB per dispatch), each scaled by what
   the same counter reads for a plain copy kernel of known size.  The record
@@ -12,7 +13,7 @@
 Usage::
 
     python -m collective_reduction_ring_amd.profiling ktrace --trace T.csv --stats S.csv \\
-        --kernel fold_kernel --timed 100 --command "..." --out profiles/x.md
+        --kernel fold_kernel --skip 10 --timed 100 --command "..." --out profiles/x.md
     python -m collective_reduction_ring_amd.profiling traffic --fetch F.csv --write W.csv \\
         --cal-fetch CF.csv --cal-write CW.csv --kernel fold_kernel --cal-kernel gather_kernel \\
         --cal-bytes 1073741824 --algorithmic-bytes 2415919104 --commands "..." --out profiles/x.json
@@ -52,11 +53,12 @@ def counter_per_dispatch(path: str, counter: str, kernel: str) -> list[float]:
             if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]]
 
 
-def ktrace_summary(trace: str, stats: str, kernel: str, timed: int, command: str) -> str:
+def ktrace_summary(trace: str, stats: str, kernel: str, skip: int, timed: int, command: str) -> str:
     srows = _rows(stats)
-    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-            for r in _rows(trace) if kernel in r["Kernel_Name"]]
-    last = durs[-timed:] if timed else durs
+    rows = sorted((r for r in _rows(trace) if kernel in r["Kernel_Name"]),
+                  key=lambda r: int(r["Start_Timestamp"]))
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+    last = durs[skip:skip + timed] if timed else durs[skip:]
     lines = [
         "# rocprofv3 kernel trace summary",
         "",
@@ -75,7 +77,8 @@ def ktrace_summary(trace: str, stats: str, kernel: str, timed: int, command: str
                      f"{float(r['Percentage']):.1f}% |")
     lines += [
         "",
-        f"`{kernel}`: {len(durs)} dispatches; mean of the last {len(last)} (the timed window): "
+        f"`{kernel}`: {len(durs)} dispatches; mean of dispatches {skip}..{skip + len(last) - 1} "
+        f"(the timed window): "
         f"**{statistics.mean(last):.1f} us**, median {statistics.median(last):.1f} us, "
         f"min {min(last):.1f} us.",
         "",
@@ -127,6 +130,7 @@ def main() -> None:
     k.add_argument("--trace", required=True)
     k.add_argument("--stats", required=True)
     k.add_argument("--kernel", required=True)
+    k.add_argument("--skip", type=int, default=0)
     k.add_argument("--timed", type=int, default=0)
     k.add_argument("--command", required=True)
     k.add_argument("--out", required=True)
@@ -137,7 +141,7 @@ def main() -> None:
     t.add_argument("--algorithmic-bytes", type=int, required=True)
     a = ap.parse_args()
     if a.cmd == "ktrace":
-        text = ktrace_summary(a.trace, a.stats, a.kernel, a.timed, a.command)
+        text = ktrace_summary(a.trace, a.stats, a.kernel, a.skip, a.timed, a.command)
         with open(a.out, "w") as f:
             f.write(text)
         print(text)

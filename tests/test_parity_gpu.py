@@ -420,3 +420,57 @@ def test_full_c5_fused_200_tensors():
     for r in range(w):
         for i in range(len(sizes)):
             assert_parity(to_host(tens[r][i], "f32"), want[r][i], "f32", f"rank {r} tensor {i}")
+
+
+# ------------------------------------------------- beyond 32-bit offsets ----
+
+def _sample_positions(rng, n, bounds, extra=20000):
+    pos = set(rng.integers(0, n, extra).tolist())
+    for b in bounds:
+        for d in (-2, -1, 0, 1, 2):
+            if 0 <= b + d < n:
+                pos.add(b + d)
+    for v in (2 ** 31 - 1, 2 ** 31, 2 ** 31 + 1, 2 ** 30 - 1, 2 ** 30, n - 1):
+        if 0 <= v < n:
+            pos.add(v)
+    return np.array(sorted(pos), dtype=np.int64)
+
+
+def test_rank_buffers_beyond_2_pow_31_elements():
+    # W=2 ranks of 2^31 + 4096 fp32 (8 GiB each): element indices above 2^31,
+    # byte offsets above 8 GiB, reduce-scatter segments above 4 GiB.  Inputs
+    # from a seeded device generator; outputs checked at sampled positions,
+    # including every segment boundary, against the oracle's fold.
+    w, n = 2, 2 ** 31 + 4096
+    s = n // w
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(2024)
+    say("large: generating 2 x 8 GiB on the device")
+    xs = [torch.randn(n, device="cuda:0", generator=gen) for _ in range(w)]
+    rng = np.random.default_rng(11)
+
+    out = [empty(s, "f32") for _ in range(w)]
+    say("large: reduce-scatter")
+    rsx.reduce_scatter(xs, out, "sum")
+    torch.cuda.synchronize()
+    pos = _sample_positions(rng, s, [0, s - 1])
+    ti = torch.from_numpy(pos).to("cuda:0")
+    for k in range(w):
+        vals = [x[k * s + ti].cpu().numpy() for x in xs]
+        want = oracle.fold(vals, oracle.ring_fold_order(k, w), "sum", "f32")
+        assert_parity(out[k][ti].cpu().numpy(), want, "f32", f"rs block {k}")
+    del out
+
+    say("large: all-reduce in place")
+    pos = _sample_positions(rng, n, [oracle.segment_bounds(n, w)[k][0] for k in range(w)])
+    ti = torch.from_numpy(pos).to("cuda:0")
+    before = [x[ti].cpu().numpy() for x in xs]
+    rsx.all_reduce(xs, None, "max", "ring")
+    torch.cuda.synchronize()
+    segs = oracle.segment_bounds(n, w)
+    for k, (lo, hi) in enumerate(segs):
+        m = (pos >= lo) & (pos < hi)
+        want = oracle.fold([b[m] for b in before], oracle.ring_fold_order(k, w), "max", "f32")
+        for r in range(w):
+            assert_parity(xs[r][ti[torch.from_numpy(m).to("cuda:0")]].cpu().numpy(), want, "f32",
+                          f"ar segment {k} rank {r}")
