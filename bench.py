@@ -168,6 +168,10 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
         res = {"workload": "all-reduce avg bf16 (fp32 accumulate), W=8, 134,217,728/rank, "
                            f"{len(plans)} buckets of <= 25 MiB in sequence on one stream",
                "ring_one_pass": _stat(time_launches(step, reps // 4 or 1, warm, torch), 2 * world * n * 2)}
+        res["ring_one_pass"]["graph_us_per_step"] = graph_us_per_call(step, 1, 10, torch)
+        # For comparison only: the same bytes as one all-reduce without buckets.
+        whole = rsx.AllReduce(dev, out, "avg", "ring")
+        res["unbucketed_one_launch"] = _stat(time_launches(whole, reps // 4 or 1, warm, torch), 2 * world * n * 2)
         # The same all-reduce composed of a reduce-scatter into a bf16 buffer of
         # W segments, then an all-gather: more traffic, same bits.
         _, seg_buf = _arena(torch, torch.bfloat16, world, bucket // world)
@@ -211,14 +215,18 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
         per_rank = wl.fused_tensors(world, sizes)
         tens = [[torch.from_numpy(t).to("cuda:0") for t in ts] for ts in per_rank]
         total = int(sizes.sum())
-        _, fused = _arena(torch, torch.float32, world, total)
+        stride = (total + 63) // 64 * 64        # 256-byte aligned fusion buffers
+        fz = torch.empty(world * stride, dtype=torch.float32, device="cuda:0")
+        fused = [fz[r * stride:r * stride + total] for r in range(world)]
         plan = rsx.FusedAllReduce(tens, fused, None, "sum", "ring")
         pack = lambda: [p() for p in plan.packs]  # noqa: E731
         arp = plan.reduce
         unpack = lambda: [u() for u in plan.unpacks]  # noqa: E731
         e2e = plan
         nb = world * total * 4
+        direct = rsx.TensorFusionAllReduce(tens, None, "sum", "ring")
         return {"workload": f"fused: W=4, {len(sizes)} fp32 tensors, {total} elements/rank",
+                "direct_tensor_fusion_all_reduce": _stat(time_launches(direct, reps, warm, torch), 2 * nb),
                 "pack": _stat(time_launches(pack, reps, warm, torch), 2 * nb),
                 "all_reduce": _stat(time_launches(arp, reps, warm, torch), 2 * nb),
                 "unpack": _stat(time_launches(unpack, reps, warm, torch), 2 * nb),

@@ -41,6 +41,7 @@ SIGNATURES = {
     "rsx_all_reduce": (_I, [_PP, _PP, _I, _SZ, _I, _I, _I, _P]),
     "rsx_fuse_pack": (_I, [_PP, ctypes.POINTER(_SZ), _I, _P, _I, _P]),
     "rsx_fuse_unpack": (_I, [_P, _PP, ctypes.POINTER(_SZ), _I, _I, _P]),
+    "rsx_fused_all_reduce": (_I, [_PP, _PP, ctypes.POINTER(_SZ), _I, _I, _I, _I, _I, _P]),
     "rsx_segment_begin": (_SZ, [_SZ, _I, _I]),
     "rsx_dtype_size": (_SZ, [_I]),
     "rsx_status_string": (ctypes.c_char_p, [_I]),

@@ -225,6 +225,48 @@ class FusedAllReduce:
             u(stream)
 
 
+class TensorFusionAllReduce:
+    """Prepared all-reduce of every rank's tensor list with tensor-fusion
+    semantics, without a fusion buffer (``rsx_fused_all_reduce``).
+
+    ``tensors_per_rank[r][i]`` is rank r's tensor i; every rank lists tensors of
+    the same sizes.  The result equals, bit for bit, packing each rank's list
+    back to back, all-reducing the W fused buffers with ``algo`` and unpacking
+    (SINGA fusedSynch / Horovod PerformOperation), but only the tensors
+    themselves are read and written.  ``outputs_per_rank=None`` is in place.
+    """
+
+    def __init__(self, tensors_per_rank, outputs_per_rank=None, op: str = "sum", algo: str = "ring"):
+        w = _ranks(tensors_per_rank)
+        outputs_per_rank = tensors_per_rank if outputs_per_rank is None else outputs_per_rank
+        if len(outputs_per_rank) != w:
+            raise ValueError("need one output list per rank")
+        counts = [t.numel() for t in tensors_per_rank[0]]
+        first = next((t for ts in tensors_per_rank for t in ts), None)
+        if first is None:
+            raise ValueError("empty tensor lists")
+        dev, dt = first.device, first.dtype
+        for r in range(w):
+            if len(tensors_per_rank[r]) != len(counts) or len(outputs_per_rank[r]) != len(counts):
+                raise ValueError("every rank needs the same number of tensors")
+            for i, c in enumerate(counts):
+                _check([tensors_per_rank[r][i]], c, f"tensors[{r}][{i}]", dt, dev)
+                _check([outputs_per_rank[r][i]], c, f"outputs[{r}][{i}]", dt, dev)
+        if algo not in ALGOS:
+            raise ValueError(f"unknown algo {algo!r}")
+        self.device = dev
+        self.args = (L.ptr_array([t.data_ptr() for ts in tensors_per_rank for t in ts]),
+                     L.ptr_array([t.data_ptr() for ts in outputs_per_rank for t in ts]),
+                     L.size_array(counts), len(counts), w, _dtype_code(first), _op_code(op),
+                     ALGOS[algo])
+        self.fn = L.lib().rsx_fused_all_reduce
+        self.keep = (tensors_per_rank, outputs_per_rank)
+
+    def __call__(self, stream=None) -> None:
+        with torch.cuda.device(self.device):
+            L.check("rsx_fused_all_reduce", self.fn(*self.args, _stream_handle(stream)))
+
+
 def fuse_pack(tensors, fused: torch.Tensor, stream=None) -> None:
     """Copy ``tensors`` back to back into ``fused``."""
     FusePack(tensors, fused)(stream)

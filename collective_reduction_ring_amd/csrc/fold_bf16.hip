@@ -8,4 +8,8 @@ hipError_t launch_fold_bf16(int op, int world, bool rs, bool vec, const FoldArgs
   return launch_fold<BF16T>(op, world, rs, vec, a, grid, s);
 }
 
+hipError_t launch_list_bf16(int op, int world, const ListArgs& a, dim3 grid, hipStream_t s) {
+  return launch_list<BF16T>(op, world, a, grid, s);
+}
+
 }  // namespace rsx

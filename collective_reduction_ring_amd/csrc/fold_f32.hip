@@ -8,4 +8,8 @@ hipError_t launch_fold_f32(int op, int world, bool rs, bool vec, const FoldArgs&
   return launch_fold<F32T>(op, world, rs, vec, a, grid, s);
 }
 
+hipError_t launch_list_f32(int op, int world, const ListArgs& a, dim3 grid, hipStream_t s) {
+  return launch_list<F32T>(op, world, a, grid, s);
+}
+
 }  // namespace rsx

@@ -47,10 +47,13 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as
 
 // fp32 -> bf16, round to nearest, ties to even; a NaN becomes the quiet NaN
 // with the sign kept.  Overflow goes to +-inf, as the rounding rule gives.
+// Written as a select, not an early return, so it compiles to a compare and
+// a v_cndmask instead of a branch per element.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet_nan = ((u >> 16) & 0x8000u) | 0x7fc0u;
+  return (u & 0x7fffffffu) > 0x7f800000u ? quiet_nan : rounded;
 }
 
 template <class D>
@@ -143,14 +146,128 @@ __device__ __forceinline__ A finish(A acc) {
   }
 }
 
-// ------------------------------------------------------------------ kernel
+// ------------------------------------------------------------ tile body
 
+// Fold one element: the W values in fold order, then finish and narrow.
+template <class D, int OP, int W>
+__device__ __forceinline__ typename D::S fold_values(const typename D::S (&x)[W]) {
+  typename D::A acc = Elem<D>::widen(x[0]);
+#pragma unroll
+  for (int j = 1; j < W; ++j) acc = combine<OP>(acc, Elem<D>::widen(x[j]));
+  return Elem<D>::narrow(finish<OP, W>(acc));
+}
+
+// Fold one dwordx4 of each of the W sources (in fold order), lane-wise.
+template <class D, int OP, int W>
+__device__ __forceinline__ uint4 fold_vectors(const uint4 (&v)[W]) {
+  using A = typename D::A;
+  constexpr int VL = D::kVL;
+  A acc[VL];
+  Elem<D>::unpack(v[0], acc);
+#pragma unroll
+  for (int j = 1; j < W; ++j) {
+    A x[VL];
+    Elem<D>::unpack(v[j], x);
+#pragma unroll
+    for (int l = 0; l < VL; ++l) acc[l] = combine<OP>(acc[l], x[l]);
+  }
+#pragma unroll
+  for (int l = 0; l < VL; ++l) acc[l] = finish<OP, W>(acc[l]);
+  return Elem<D>::pack(acc);
+}
+
+// Tile `tile` of the element range [b, e) of W sources given in fold order.
+// Element idx goes to dst[d][idx - shift] for each of the ND destinations
+// (one reduce-scatter block, or every all-reduce rank).
+//
+// VEC: all source and destination bases are 16-byte aligned, so element
+// offsets divisible by VL are too; the tile is U*256 whole vectors of the
+// range and tile 0 also folds the unaligned head and tail elements (none
+// when WHOLE, i.e. b and e are multiples of VL).  Otherwise the tile is
+// U*256 elements, one per lane per unit, still coalesced.
+template <class D, int OP, int W, int ND, int STORE_AUX, bool VEC, bool WHOLE>
+__device__ __forceinline__ void fold_tile(const typename D::S* const (&src)[W],
+                                          typename D::S* const (&dst)[ND], uint64_t shift,
+                                          uint64_t b, uint64_t e, uint32_t tile) {
+  using S = typename D::S;
+  constexpr int U = fold_units(W);
+  constexpr int VL = D::kVL;
+  const uint32_t tid = threadIdx.x;
+
+  auto fold_element = [&](uint64_t idx) {
+    S x[W];
+#pragma unroll
+    for (int j = 0; j < W; ++j) x[j] = src[j][idx];
+    const S out = fold_values<D, OP, W>(x);
+#pragma unroll
+    for (int d = 0; d < ND; ++d) dst[d][idx - shift] = out;
+  };
+
+  if constexpr (VEC) {
+    const uint64_t hb = WHOLE ? b : min((b + VL - 1) / VL * VL, e);
+    const uint64_t be = WHOLE ? e : max(hb, e / VL * VL);
+    const uint64_t nv = (be - hb) / VL;
+    const uint64_t v0 = static_cast<uint64_t>(tile) * (U * kBlock);
+    if (v0 < nv) {
+      // This tile's vectors, [v0, v0 + nvt), as a byte range per buffer;
+      // lanes past the range read zeros and their stores are dropped.
+      const uint32_t nvt = static_cast<uint32_t>(min<uint64_t>(U * kBlock, nv - v0));
+      const uint32_t bytes = nvt * kVecBytes;
+      const uint64_t e0 = hb + v0 * VL;
+      const uint32_t voff = tid * kVecBytes;
+      uint4 v[U][W];
+#pragma unroll
+      for (int j = 0; j < W; ++j) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(src[j] + e0, bytes);
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u][j] = load_stream(r, voff, u * kBlock * kVecBytes);
+      }
+      uint4 o[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) o[u] = fold_vectors<D, OP, W>(v[u]);
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(dst[d] + (e0 - shift), bytes);
+#pragma unroll
+        for (int u = 0; u < U; ++u) store_b128<STORE_AUX>(r, voff, u * kBlock * kVecBytes, o[u]);
+      }
+    }
+    if (!WHOLE && tile == 0) {
+      const uint32_t nh = static_cast<uint32_t>(hb - b);
+      const uint32_t nt = static_cast<uint32_t>(e - be);
+      if (tid < nh) {
+        fold_element(b + tid);
+      } else if (tid < nh + nt) {
+        fold_element(be + (tid - nh));
+      }
+    }
+  } else {
+    const uint64_t t0 = b + static_cast<uint64_t>(tile) * (U * kBlock);
+    if (t0 >= e) return;
+    const bool full = t0 + U * kBlock <= e;
+    S x[U][W];
+#pragma unroll
+    for (int j = 0; j < W; ++j)
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (full || t0 + u * kBlock + tid < e) x[u][j] = src[j][t0 + u * kBlock + tid];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t idx = t0 + u * kBlock + tid;
+      if (!full && idx >= e) continue;
+      const S out = fold_values<D, OP, W>(x[u]);
+#pragma unroll
+      for (int d = 0; d < ND; ++d) dst[d][idx - shift] = out;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ kernels
+
+// Reduce-scatter (RS) or all-reduce over W rank buffers (FoldArgs).
 template <class D, int OP, int W, bool RS, bool VEC>
 __global__ __launch_bounds__(kBlock) void fold_kernel(const FoldArgs a) {
   using S = typename D::S;
-  using A = typename D::A;
-  constexpr int U = fold_units(W);
-  constexpr int VL = D::kVL;
 
   // Read every scalar argument up front: one round of kernarg loads.
   const uint32_t tiles_total = a.tiles_total, magic = a.tps_magic, shift = a.tps_shift;
@@ -159,8 +276,8 @@ __global__ __launch_bounds__(kBlock) void fold_kernel(const FoldArgs a) {
   if (t >= tiles_total) return;
   const uint32_t k = static_cast<uint32_t>((static_cast<uint64_t>(t) * magic) >> shift);
   const uint32_t tile = t - k * tps;
-  // Reduce-scatter segments are whole (count = W * seg); all-reduce ones are
-  // clipped to count.
+  // Reduce-scatter segments are whole (count = W * seg, seg % VL == 0 for
+  // the dwordx4 kernel); all-reduce ones are clipped to count.
   const uint64_t b = RS ? static_cast<uint64_t>(k) * a.seg : min(static_cast<uint64_t>(k) * a.seg, a.count);
   const uint64_t e = RS ? b + a.seg : min(b + a.seg, a.count);
 
@@ -171,113 +288,47 @@ __global__ __launch_bounds__(kBlock) void fold_kernel(const FoldArgs a) {
 #pragma unroll
   for (int j = 0; j < W; ++j) src[j] = static_cast<const S*>(a.src[first + j]);
 
-  // Fold and store one element (head, tail and the unaligned kernel).
-  auto fold_element = [&](uint64_t idx) {
-    S x[W];
-#pragma unroll
-    for (int j = 0; j < W; ++j) x[j] = src[j][idx];
-    A acc = Elem<D>::widen(x[0]);
-#pragma unroll
-    for (int j = 1; j < W; ++j) acc = combine<OP>(acc, Elem<D>::widen(x[j]));
-    const S out = Elem<D>::narrow(finish<OP, W>(acc));
-    if constexpr (RS) {
-      static_cast<S*>(a.dst[k])[idx - b] = out;
-    } else {
-#pragma unroll
-      for (int r = 0; r < W; ++r) static_cast<S*>(a.dst[r])[idx] = out;
-    }
-  };
-
-  const uint32_t tid = threadIdx.x;
-
-  if constexpr (VEC) {
-    // Body: whole dwordx4 vectors of [b, e).  All base pointers are 16-byte
-    // aligned (checked on the host), so element offsets divisible by VL are
-    // too.  Reduce-scatter segments start at such an offset (host check);
-    // all-reduce segments may not, and take a scalar head and tail.
-    // (For reduce-scatter the host guarantees seg % VL == 0: no head or tail.)
-    const uint64_t hb = RS ? b : min((b + VL - 1) / VL * VL, e);
-    const uint64_t be = RS ? e : max(hb, e / VL * VL);
-    const uint64_t nv = (be - hb) / VL;
-    const uint64_t v0 = static_cast<uint64_t>(tile) * (U * kBlock);
-    if (v0 < nv) {
-      // This tile's vectors, [v0, v0 + nvt), as a byte range per buffer;
-      // lanes past the range read zeros and their stores are dropped.
-      const uint32_t nvt = static_cast<uint32_t>(min<uint64_t>(U * kBlock, nv - v0));
-      const uint32_t bytes = nvt * kVecBytes;
-      const uint64_t e0 = hb + v0 * VL;
-      const uint32_t voff = tid * kVecBytes;
-      uint4 v[W][U];
-#pragma unroll
-      for (int j = 0; j < W; ++j) {
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(src[j] + e0, bytes);
-#pragma unroll
-        for (int u = 0; u < U; ++u) v[j][u] = load_stream(r, voff, u * kBlock * kVecBytes);
-      }
-      uint4 o[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        A acc[VL];
-        Elem<D>::unpack(v[0][u], acc);
-#pragma unroll
-        for (int j = 1; j < W; ++j) {
-          A x[VL];
-          Elem<D>::unpack(v[j][u], x);
-#pragma unroll
-          for (int l = 0; l < VL; ++l) acc[l] = combine<OP>(acc[l], x[l]);
-        }
-#pragma unroll
-        for (int l = 0; l < VL; ++l) acc[l] = finish<OP, W>(acc[l]);
-        o[u] = Elem<D>::pack(acc);
-      }
-      if constexpr (RS) {
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(static_cast<S*>(a.dst[k]) + (e0 - b), bytes);
-#pragma unroll
-        for (int u = 0; u < U; ++u) store_b128<kStoreThrough>(r, voff, u * kBlock * kVecBytes, o[u]);
-      } else {
-#pragma unroll
-        for (int d = 0; d < W; ++d) {
-          const __amdgpu_buffer_rsrc_t r = make_rsrc(static_cast<S*>(a.dst[d]) + e0, bytes);
-#pragma unroll
-          for (int u = 0; u < U; ++u) store_b128<kStoreStream>(r, voff, u * kBlock * kVecBytes, o[u]);
-        }
-      }
-    }
-    if (!RS && tile == 0) {
-      const uint32_t nh = static_cast<uint32_t>(hb - b);
-      const uint32_t nt = static_cast<uint32_t>(e - be);
-      if (tid < nh) {
-        fold_element(b + tid);
-      } else if (tid < nh + nt) {
-        fold_element(be + (tid - nh));
-      }
-    }
+  if constexpr (RS) {
+    S* const dst[1] = {static_cast<S*>(a.dst[k])};
+    fold_tile<D, OP, W, 1, kStoreThrough, VEC, true>(src, dst, b, b, e, tile);
   } else {
-    // Unaligned kernel: one element per lane per unit, still coalesced.
-    const uint64_t t0 = b + static_cast<uint64_t>(tile) * (U * kBlock);
-    if (t0 >= e) return;
-    const bool full = t0 + U * kBlock <= e;
-    S x[W][U];
+    S* dst[W];
 #pragma unroll
-    for (int j = 0; j < W; ++j)
+    for (int d = 0; d < W; ++d) dst[d] = static_cast<S*>(a.dst[d]);
+    fold_tile<D, OP, W, W, kStoreStream, VEC, false>(src, dst, 0, b, e, tile);
+  }
+}
+
+// Tensor-list all-reduce (ListArgs): one piece of one tensor per workgroup.
+template <class D, int OP, int W>
+__global__ __launch_bounds__(kBlock) void list_fold_kernel(const ListArgs a) {
+  using S = typename D::S;
+  const uint32_t n = a.npieces;
+  const uint32_t t = xcd_tile(blockIdx.x, gridDim.x);
+  if (t >= a.tile_start[n]) return;
+  // Piece of this tile: the last i with tile_start[i] <= t.
+  uint32_t lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi + 1) / 2;
+    if (a.tile_start[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const ListPiece& pc = a.piece[lo];
+  const uint32_t tile = t - a.tile_start[lo];
+  const uint32_t base = pc.tensor * (2 * W);
+  const uint32_t first = (pc.seg + a.rot) % W;
+  const S* src[W];
+  S* dst[W];
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (full || t0 + u * kBlock + tid < e) x[j][u] = src[j][t0 + u * kBlock + tid];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint64_t idx = t0 + u * kBlock + tid;
-      if (!full && idx >= e) continue;
-      A acc = Elem<D>::widen(x[0][u]);
-#pragma unroll
-      for (int j = 1; j < W; ++j) acc = combine<OP>(acc, Elem<D>::widen(x[j][u]));
-      const S out = Elem<D>::narrow(finish<OP, W>(acc));
-      if constexpr (RS) {
-        static_cast<S*>(a.dst[k])[idx - b] = out;
-      } else {
-#pragma unroll
-        for (int r = 0; r < W; ++r) static_cast<S*>(a.dst[r])[idx] = out;
-      }
-    }
+  for (int j = 0; j < W; ++j) {
+    uint32_t r = first + j;
+    if (r >= static_cast<uint32_t>(W)) r -= W;
+    src[j] = static_cast<const S*>(a.ptr[base + r]);
+    dst[j] = static_cast<S*>(a.ptr[base + W + j]);
+  }
+  if (pc.vec) {
+    fold_tile<D, OP, W, W, kStoreStream, true, false>(src, dst, 0, pc.lo, pc.hi, tile);
+  } else {
+    fold_tile<D, OP, W, W, kStoreStream, false, false>(src, dst, 0, pc.lo, pc.hi, tile);
   }
 }
 
@@ -306,6 +357,40 @@ hipError_t launch_op(int world, bool rs, bool vec, const FoldArgs& a, dim3 grid,
     RSX_W(1) RSX_W(2) RSX_W(3) RSX_W(4) RSX_W(5) RSX_W(6) RSX_W(7) RSX_W(8)
     RSX_W(9) RSX_W(10) RSX_W(11) RSX_W(12) RSX_W(13) RSX_W(14) RSX_W(15) RSX_W(16)
 #undef RSX_W
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+template <class D, int OP>
+hipError_t launch_list_op(int world, const ListArgs& a, dim3 grid, hipStream_t s) {
+  void* args[] = {const_cast<ListArgs*>(&a)};
+  const void* fn;
+  switch (world) {
+#define RSX_W(n)                                                            \
+  case n:                                                                   \
+    fn = reinterpret_cast<const void*>(&list_fold_kernel<D, OP, n>);        \
+    break;
+    RSX_W(1) RSX_W(2) RSX_W(3) RSX_W(4) RSX_W(5) RSX_W(6) RSX_W(7) RSX_W(8)
+    RSX_W(9) RSX_W(10) RSX_W(11) RSX_W(12) RSX_W(13) RSX_W(14) RSX_W(15) RSX_W(16)
+#undef RSX_W
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, s);
+}
+
+template <class D>
+hipError_t launch_list(int op, int world, const ListArgs& a, dim3 grid, hipStream_t s) {
+  switch (op) {
+    case RSX_SUM:
+      return launch_list_op<D, RSX_SUM>(world, a, grid, s);
+    case RSX_MAX:
+      return launch_list_op<D, RSX_MAX>(world, a, grid, s);
+    case RSX_MIN:
+      return launch_list_op<D, RSX_MIN>(world, a, grid, s);
+    case RSX_AVG:
+      return launch_list_op<D, RSX_AVG>(world, a, grid, s);
     default:
       return hipErrorInvalidValue;
   }

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <vector>
 
 #include "rsx_internal.h"
 
@@ -174,6 +175,44 @@ rsx_status_t fuse_copy(const void* const* tens, const size_t* counts, int ntenso
   return RSX_SUCCESS;
 }
 
+// Overlap rules of the tensor-list all-reduce, in O(n log n) for n buffers.
+// Sources may coincide exactly but not overlap partially; destinations are
+// pairwise disjoint; a destination may coincide with sources only when all of
+// them belong to the same tensor index (each element is then read and
+// written by the same lane).
+struct Span {
+  uintptr_t lo, hi;
+  int tensor;
+};
+bool list_aliasing_ok(std::vector<Span>& sends, std::vector<Span>& recvs) {
+  auto by_lo = [](const Span& a, const Span& b) { return a.lo < b.lo || (a.lo == b.lo && a.hi < b.hi); };
+  std::sort(sends.begin(), sends.end(), by_lo);
+  std::sort(recvs.begin(), recvs.end(), by_lo);
+  // Unique source spans (sorted, pairwise disjoint after this check), each
+  // with its tensor index or -1 when spans of several tensors coincide.
+  std::vector<Span> uniq;
+  for (const Span& x : sends) {
+    if (!uniq.empty() && uniq.back().lo == x.lo && uniq.back().hi == x.hi) {
+      if (uniq.back().tensor != x.tensor) uniq.back().tensor = -1;
+      continue;
+    }
+    if (!uniq.empty() && x.lo < uniq.back().hi) return false;  // partial overlap of sources
+    uniq.push_back(x);
+  }
+  for (size_t i = 1; i < recvs.size(); ++i)
+    if (recvs[i].lo < recvs[i - 1].hi) return false;  // destinations overlap
+  for (const Span& r : recvs) {
+    // first unique source ending after r.lo
+    size_t a = std::partition_point(uniq.begin(), uniq.end(),
+                                    [&](const Span& u) { return u.hi <= r.lo; }) - uniq.begin();
+    for (size_t j = a; j < uniq.size() && uniq[j].lo < r.hi; ++j) {
+      const Span& u = uniq[j];
+      if (u.lo != r.lo || u.hi != r.hi || u.tensor != r.tensor) return false;
+    }
+  }
+  return true;
+}
+
 }  // namespace
 }  // namespace rsx
 
@@ -334,6 +373,123 @@ rsx_status_t rsx_fuse_pack(const void* const* tensors, const size_t* counts, int
 rsx_status_t rsx_fuse_unpack(const void* fused, void* const* tensors, const size_t* counts,
                              int ntensors, rsx_dtype_t dtype, hipStream_t stream) {
   return fuse_copy(tensors, counts, ntensors, fused, false, dtype, stream);
+}
+
+rsx_status_t rsx_fused_all_reduce(const void* const* sendtensors, void* const* recvtensors,
+                                  const size_t* counts, int ntensors, int nranks,
+                                  rsx_dtype_t dtype, rsx_op_t op, rsx_algo_t algo,
+                                  hipStream_t stream) {
+  if (nranks < 1 || nranks > RSX_MAX_RANKS || ntensors < 0) return RSX_ERR_INVALID_ARGUMENT;
+  const size_t es = esize_of(dtype);
+  if (es == 0) return RSX_ERR_INVALID_TYPE;
+  if (!valid_op(op)) return RSX_ERR_INVALID_OP;
+  if (algo != RSX_ALGO_RING && algo != RSX_ALGO_NAIVE && algo != RSX_ALGO_AUTO)
+    return RSX_ERR_INVALID_ARGUMENT;
+  if (ntensors > 0 && counts == nullptr) return RSX_ERR_INVALID_ARGUMENT;
+  size_t total = 0;
+  for (int i = 0; i < ntensors; ++i) {
+    size_t b;
+    if (!mul_ok(counts[i], es, &b) || total + counts[i] < total) return RSX_ERR_UNSUPPORTED;
+    total += counts[i];
+  }
+  size_t total_bytes;
+  if (!mul_ok(total, es, &total_bytes)) return RSX_ERR_UNSUPPORTED;
+  if (total == 0) return RSX_SUCCESS;
+  if (sendtensors == nullptr || recvtensors == nullptr) return RSX_ERR_INVALID_ARGUMENT;
+
+  const int w = nranks;
+  std::vector<Span> sends, recvs;
+  bool in_place_all = true;
+  for (int r = 0; r < w; ++r) {
+    for (int i = 0; i < ntensors; ++i) {
+      if (counts[i] == 0) continue;
+      const void* sp = sendtensors[static_cast<size_t>(r) * ntensors + i];
+      const void* rp = recvtensors[static_cast<size_t>(r) * ntensors + i];
+      if (sp == nullptr || rp == nullptr) return RSX_ERR_INVALID_ARGUMENT;
+      const Range sr = range_of(sp, counts[i] * es), rr = range_of(rp, counts[i] * es);
+      sends.push_back({sr.lo, sr.hi, i});
+      recvs.push_back({rr.lo, rr.hi, i});
+      in_place_all = in_place_all && sp == rp;
+    }
+  }
+  if (!list_aliasing_ok(sends, recvs)) return RSX_ERR_ALIASING;
+  if (w == 1 && in_place_all) return RSX_SUCCESS;
+
+  const bool naive = algo == RSX_ALGO_NAIVE || (algo == RSX_ALGO_AUTO && total_bytes <= RSX_NAIVE_MAX_BYTES);
+  const uint64_t seg = naive ? total : (total + w - 1) / w;
+  const uint64_t per = static_cast<uint64_t>(fold_units(w)) * kBlock;
+  const int vl = static_cast<int>(kVecBytes / es);
+
+  ListArgs a;
+  uint64_t tiles = 0;
+  int ntens = 0;  // tensors in the current launch
+  auto reset = [&]() {
+    memset(&a, 0, sizeof(a));
+    a.rot = naive ? 0 : 1;
+    tiles = 0;
+    ntens = 0;
+  };
+  auto flush = [&]() -> rsx_status_t {
+    if (a.npieces == 0) return RSX_SUCCESS;
+    a.tile_start[a.npieces] = static_cast<uint32_t>(tiles);
+    const dim3 grid(static_cast<uint32_t>(xcd_grid(tiles)));
+    hipError_t e;
+    switch (dtype) {
+      case RSX_FLOAT32:
+        e = launch_list_f32(op, w, a, grid, stream);
+        break;
+      case RSX_BFLOAT16:
+        e = launch_list_bf16(op, w, a, grid, stream);
+        break;
+      default:
+        e = launch_list_i32(op, w, a, grid, stream);
+        break;
+    }
+    const rsx_status_t st = hip_status(e);
+    reset();
+    return st;
+  };
+  reset();
+  uint64_t off = 0;  // fused offset of tensor i
+  for (int i = 0; i < ntensors; ++i) {
+    const uint64_t c = counts[i];
+    if (c == 0) continue;
+    const uint32_t k0 = naive ? 0 : static_cast<uint32_t>(off / seg);
+    const uint32_t k1 = naive ? 0 : static_cast<uint32_t>((off + c - 1) / seg);
+    const uint32_t npc = k1 - k0 + 1;
+    if ((ntens + 1) * 2 * w > kListPtrs || a.npieces + npc > static_cast<uint32_t>(kListPieces)) {
+      const rsx_status_t st = flush();
+      if (st != RSX_SUCCESS) return st;
+    }
+    bool vec = true;
+    for (int r = 0; r < w; ++r) {
+      void* sp = const_cast<void*>(sendtensors[static_cast<size_t>(r) * ntensors + i]);
+      void* rp = recvtensors[static_cast<size_t>(r) * ntensors + i];
+      a.ptr[ntens * 2 * w + r] = sp;
+      a.ptr[ntens * 2 * w + w + r] = rp;
+      vec = vec && aligned16(sp) && aligned16(rp);
+    }
+    for (uint32_t k = k0; k <= k1; ++k) {
+      ListPiece& pc = a.piece[a.npieces];
+      const uint64_t slo = naive ? 0 : static_cast<uint64_t>(k) * seg;
+      const uint64_t shi = naive ? total : std::min<uint64_t>(slo + seg, total);
+      pc.lo = std::max(off, slo) - off;
+      pc.hi = std::min(off + c, shi) - off;
+      pc.tensor = static_cast<uint32_t>(ntens);
+      pc.seg = static_cast<uint16_t>(k);
+      pc.vec = vec ? 1 : 0;
+      const uint64_t len = pc.hi - pc.lo;
+      const uint64_t units = vec ? len / vl : len;
+      const uint64_t nt = std::max<uint64_t>(1, (units + per - 1) / per);
+      a.tile_start[a.npieces] = static_cast<uint32_t>(tiles);
+      tiles += nt;
+      if (tiles > 0x7ffffff0ull) return RSX_ERR_UNSUPPORTED;
+      a.npieces += 1;
+    }
+    ntens += 1;
+    off += c;
+  }
+  return flush();
 }
 
 size_t rsx_segment_begin(size_t count, int nranks, int k) {

@@ -106,6 +106,29 @@ inline uint64_t copy_tiles(const void* dst, uint64_t bytes) {
   return vecs == 0 ? 1 : (vecs + per - 1) / per;
 }
 
+// Tensor-list all-reduce: the result of packing every rank's tensor list
+// back to back, all-reducing the W fused buffers and unpacking, computed on
+// the tensors themselves.  Each launch carries up to kListPieces pieces; a
+// piece is the part of one tensor that lies in one segment of the fused
+// layout, so its fold order is uniform.
+constexpr int kListPtrs = 256;   // pointer slots per launch, 2*W per tensor
+constexpr int kListPieces = 48;  // pieces per launch
+struct ListPiece {
+  uint64_t lo, hi;   // tensor-local element range
+  uint32_t tensor;   // the tensor's pointers start at slot tensor * 2W
+  uint16_t seg;      // segment of the fused layout (fold starts at rank seg + rot)
+  uint16_t vec;      // 1: all 2W buffers of the tensor are 16-byte aligned
+};
+struct ListArgs {
+  uint32_t npieces;
+  uint32_t rot;
+  uint32_t tile_start[kListPieces + 1];  // piece i owns tiles [tile_start[i], tile_start[i+1])
+  ListPiece piece[kListPieces];
+  // tensor t: sources of ranks 0..W-1 at slots [t*2W, t*2W + W), destinations
+  // at [t*2W + W, t*2W + 2W).
+  void* ptr[kListPtrs];
+};
+
 // Launchers, one per dtype translation unit.  `rs` selects the reduce-scatter
 // store (block k to dst[k]) over the all-reduce store (every element to every
 // dst[r]); `vec` selects the dwordx4 kernel.  Return the launch status.
@@ -115,6 +138,10 @@ hipError_t launch_fold_bf16(int op, int world, bool rs, bool vec, const FoldArgs
                             dim3 grid, hipStream_t s);
 hipError_t launch_fold_i32(int op, int world, bool rs, bool vec, const FoldArgs& a,
                            dim3 grid, hipStream_t s);
+
+hipError_t launch_list_f32(int op, int world, const ListArgs& a, dim3 grid, hipStream_t s);
+hipError_t launch_list_bf16(int op, int world, const ListArgs& a, dim3 grid, hipStream_t s);
+hipError_t launch_list_i32(int op, int world, const ListArgs& a, dim3 grid, hipStream_t s);
 
 hipError_t launch_gather(int esize, bool vec, const GatherArgs& a, dim3 grid, hipStream_t s);
 hipError_t launch_multicopy(int esize, const MultiCopyArgs& a, hipStream_t s);

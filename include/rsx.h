@@ -153,6 +153,29 @@ rsx_status_t rsx_fuse_unpack(const void* fused, void* const* tensors, const size
                              int ntensors, rsx_dtype_t dtype, hipStream_t stream);
 
 /*
+ * Tensor-fusion all-reduce without a fusion buffer [SG fusedSynch; HV
+ * PerformOperation; DP Ring AllReduce].
+ *
+ * sendtensors[r*ntensors + i], recvtensors[r*ntensors + i]: device arrays of
+ * rank r's tensor i, counts[i] elements each (the same count on every rank).
+ * The result is, bit for bit, that of rsx_fuse_pack of each rank's list into
+ * a buffer of F = counts[0] + ... + counts[n-1] elements, rsx_all_reduce of
+ * the W buffers with `algo`, then rsx_fuse_unpack into recvtensors: element
+ * j of tensor i sits at fused offset counts[0] + ... + counts[i-1] + j and is
+ * folded in the order of the fused segment holding that offset.  No fusion
+ * buffer is read or written, so HBM traffic is one all-reduce of the tensors.
+ * RSX_ALGO_AUTO picks naive when F * element size <= RSX_NAIVE_MAX_BYTES.
+ * In place: recvtensors[r*n + i] == sendtensors[r2*n + i] (same tensor index)
+ * is allowed; any other overlap of a destination returns RSX_ERR_ALIASING.
+ * Zero-count tensors are skipped and may be null.  Launches about one kernel
+ * per 256 / (2W) tensors.
+ */
+rsx_status_t rsx_fused_all_reduce(const void* const* sendtensors, void* const* recvtensors,
+                                  const size_t* counts, int ntensors, int nranks,
+                                  rsx_dtype_t dtype, rsx_op_t op, rsx_algo_t algo,
+                                  hipStream_t stream);
+
+/*
  * First element of segment k in RSX_ALGO_RING all-reduce of `count`
  * elements over `nranks` ranks: min(k * ceil(count/nranks), count).
  * k may be 0..nranks (k = nranks gives count).  Returns 0 for nranks < 1.

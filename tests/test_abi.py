@@ -227,3 +227,44 @@ def test_binding_refuses_missing_library(tmp_path, monkeypatch):
     monkeypatch.setattr(L, "_lib", None)
     with pytest.raises(RuntimeError, match="not found"):
         L.lib()
+
+
+def _far(lib, sends, recvs, counts, w, dt=0, op=0, algo=0):
+    n = len(counts)
+    return lib.rsx_fused_all_reduce(_arr(sends), _arr(recvs), L.size_array(counts), n, w, dt, op,
+                                    algo, None)
+
+
+@fake_ptrs
+def test_fused_all_reduce_validation(lib):
+    c = [100, 0, 37]
+    s = [A + i * MB for i in range(6)]               # rank-major: rank 0 tensors 0..2, rank 1 ...
+    r = [A + 16 * MB + i * MB for i in range(6)]
+    assert lib.rsx_fused_all_reduce(_arr(s), _arr(r), None, 3, 2, 0, 0, 0, None) == 1   # counts
+    assert _far(lib, s, r, c, 0) == 1 and _far(lib, s, r, c, 17) == 1
+    assert _far(lib, s, r, c, 2, dt=3) == 2
+    assert _far(lib, s, r, c, 2, op=7) == 3
+    assert _far(lib, s, r, c, 2, algo=9) == 1
+    assert _far(lib, s, r, [0, 0, 0], 2) == 0                      # nothing to do, no launch
+    assert lib.rsx_fused_all_reduce(None, None, L.size_array([0]), 1, 2, 0, 0, 0, None) == 0
+    assert _far(lib, s, r, [2 ** 62, 1, 1], 2) == 4                 # bytes overflow
+    s_null = list(s)
+    s_null[3] = None                                                # rank 1 tensor 0 (count 100)
+    assert _far(lib, s_null, r, c, 2) == 1
+
+
+@fake_ptrs
+def test_fused_all_reduce_aliasing(lib):
+    c = [100, 50]
+    s = [A, A + MB, A + 2 * MB, A + 3 * MB]
+    r = [A + 8 * MB, A + 9 * MB, A + 10 * MB, A + 11 * MB]
+    # destination overlapping a source partially
+    assert _far(lib, s, [A + 8, r[1], r[2], r[3]], c, 2) == 5
+    # two destinations overlapping
+    assert _far(lib, s, [r[0], r[0] + 16, r[2], r[3]], c, 2) == 5
+    # sources overlapping partially
+    assert _far(lib, [A, A + 200, s[2], s[3]], r, c, 2) == 5
+    # destination equal to a source of another tensor index
+    assert _far(lib, s, [s[1], r[1], r[2], r[3]], [50, 50], 2) == 5
+    # single rank, every destination its own source: nothing to do
+    assert _far(lib, [A, A + MB], [A, A + MB], c, 1) == 0

@@ -295,6 +295,91 @@ def test_fused_pack_allreduce_unpack(dtype):
             assert_parity(to_host(outs[r][i], dtype), want[r][i], dtype, f"rank {r} tensor {i}")
 
 
+def _list_case(seed, w, sizes, dtype):
+    return [[wl.draw(DIST[dtype], np.random.default_rng((seed, r, i)), int(n))
+             for i, n in enumerate(sizes)] for r in range(w)]
+
+
+LIST_SIZES = [0, 1, 3, 4096 + 5, 7, 0, 20_000, 1, 1024, 33, 65_536 + 3, 2, 9_999]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("op", OPS)
+@pytest.mark.parametrize("w", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("algo", ["ring", "naive"])
+def test_tensor_fusion_all_reduce(w, op, dtype, algo):
+    # Ring segments of the fused layout end inside tensors and inside vectors.
+    per_rank = _list_case(20, w, LIST_SIZES, dtype)
+    tens = [[to_dev(t, dtype) for t in ts] for ts in per_rank]
+    outs = [[empty(len(t), dtype, fill=0x33) for t in ts] for ts in per_rank]
+    say(f"tensor-fusion ar w={w} op={op} dtype={dtype} algo={algo}")
+    rsx.TensorFusionAllReduce(tens, outs, op, algo)()
+    torch.cuda.synchronize()
+    want = oracle.fused_all_reduce(per_rank, op, dtype) if algo == "ring" else [
+        oracle.fuse_unpack(f, LIST_SIZES) for f in oracle.naive_all_reduce(
+            [oracle.fuse_pack(ts) for ts in per_rank], op, dtype)]
+    for r in range(w):
+        for i in range(len(LIST_SIZES)):
+            assert_parity(to_host(outs[r][i], dtype), want[r][i], dtype, f"rank {r} tensor {i}")
+
+
+def test_tensor_fusion_matches_pipeline_many_launches_in_place():
+    # W=16: 2W pointers per tensor, so 120 tensors take several launches.
+    w = 16
+    sizes = wl.fused_sizes(count=120, lo=1, hi=30_000)
+    per_rank = _list_case(21, w, sizes, "f32")
+    a = [[to_dev(t, "f32") for t in ts] for ts in per_rank]
+    b = [[to_dev(t, "f32") for t in ts] for ts in per_rank]
+    fused = [empty(int(sizes.sum()), "f32") for _ in range(w)]
+    say("tensor-fusion vs pipeline, W=16, 120 tensors")
+    rsx.TensorFusionAllReduce(a, None, "sum", "ring")()                 # in place, no buffer
+    rsx.FusedAllReduce(b, fused, None, "sum", "ring")()                 # pack -> ar -> unpack
+    torch.cuda.synchronize()
+    for r in range(w):
+        for i in range(len(sizes)):
+            assert to_host(a[r][i], "f32").tobytes() == to_host(b[r][i], "f32").tobytes()
+    want = oracle.fused_all_reduce(per_rank, "sum", "f32")
+    for r in (0, 9, 15):
+        for i in range(len(sizes)):
+            assert_parity(to_host(a[r][i], "f32"), want[r][i], "f32", f"rank {r} tensor {i}")
+
+
+def test_tensor_fusion_unaligned_views():
+    w = 4
+    sizes = [5, 4096, 3, 777]
+    per_rank = _list_case(22, w, sizes, "bf16")
+    tens, outs = [], []
+    for ts in per_rank:
+        row, orow = [], []
+        for t in ts:
+            base = to_dev(np.concatenate([np.zeros(1, np.uint16), t]), "bf16")
+            row.append(base[1:])                      # 2-byte offset
+            orow.append(empty(len(t) + 3, "bf16")[3:])
+        tens.append(row)
+        outs.append(orow)
+    say("tensor-fusion unaligned bf16")
+    rsx.TensorFusionAllReduce(tens, outs, "avg", "ring")()
+    torch.cuda.synchronize()
+    want = oracle.fused_all_reduce(per_rank, "avg", "bf16")
+    for r in range(w):
+        for i in range(len(sizes)):
+            assert_parity(to_host(outs[r][i], "bf16"), want[r][i], "bf16", f"rank {r} tensor {i}")
+
+
+def test_full_c5_tensor_fusion_direct():
+    w = 4
+    sizes = wl.fused_sizes()
+    per_rank = wl.fused_tensors(w, sizes)
+    tens = [[to_dev(t, "f32") for t in ts] for ts in per_rank]
+    say(f"full cfg=5 direct: {int(sizes.sum())} elements per rank")
+    rsx.TensorFusionAllReduce(tens, None, "sum", "ring")()
+    torch.cuda.synchronize()
+    want = oracle.fused_all_reduce(per_rank, "sum", "f32")
+    for r in range(w):
+        for i in range(len(sizes)):
+            assert_parity(to_host(tens[r][i], "f32"), want[r][i], "f32", f"rank {r} tensor {i}")
+
+
 @pytest.mark.parametrize("kib", wl.SWEEP_KIB)
 def test_sweep_naive_ring_auto(kib):
     xs = wl.sweep_inputs(kib)
