@@ -24,6 +24,15 @@ OPS = {"sum": L.RSX_SUM, "max": L.RSX_MAX, "min": L.RSX_MIN, "avg": L.RSX_AVG}
 ALGOS = {"ring": L.RSX_ALGO_RING, "naive": L.RSX_ALGO_NAIVE, "auto": L.RSX_ALGO_AUTO}
 
 
+def _launch(plan, name: str, stream) -> None:
+    """Call a prepared entry point on the plan's device and the given (or current) stream."""
+    if torch.cuda.current_device() == plan.device.index:
+        L.check(name, plan.fn(*plan.args, _stream_handle(stream)))
+    else:
+        with torch.cuda.device(plan.device):
+            L.check(name, plan.fn(*plan.args, _stream_handle(stream)))
+
+
 def _stream_handle(stream) -> int:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -91,8 +100,7 @@ class ReduceScatter:
         self.keep = (list(inputs), list(outputs))
 
     def __call__(self, stream=None) -> None:
-        with torch.cuda.device(self.device):
-            L.check("rsx_reduce_scatter", self.fn(*self.args, _stream_handle(stream)))
+        _launch(self, "rsx_reduce_scatter", stream)
 
 
 class AllReduce:
@@ -117,8 +125,7 @@ class AllReduce:
         self.keep = (list(inputs), list(outputs))
 
     def __call__(self, stream=None) -> None:
-        with torch.cuda.device(self.device):
-            L.check("rsx_all_reduce", self.fn(*self.args, _stream_handle(stream)))
+        _launch(self, "rsx_all_reduce", stream)
 
 
 def reduce_scatter(inputs, outputs, op: str = "sum", stream=None) -> None:
@@ -186,8 +193,7 @@ class _FuseCopy:
         self.keep = (list(tensors), fused)
 
     def __call__(self, stream=None) -> None:
-        with torch.cuda.device(self.device):
-            L.check(self.name, self.fn(*self.args, _stream_handle(stream)))
+        _launch(self, self.name, stream)
 
 
 class FusePack(_FuseCopy):
@@ -263,8 +269,7 @@ class TensorFusionAllReduce:
         self.keep = (tensors_per_rank, outputs_per_rank)
 
     def __call__(self, stream=None) -> None:
-        with torch.cuda.device(self.device):
-            L.check("rsx_fused_all_reduce", self.fn(*self.args, _stream_handle(stream)))
+        _launch(self, "rsx_fused_all_reduce", stream)
 
 
 def fuse_pack(tensors, fused: torch.Tensor, stream=None) -> None:

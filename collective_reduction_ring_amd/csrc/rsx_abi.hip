@@ -52,6 +52,8 @@ Range range_of(const void* p, size_t bytes) {
   const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
   return {lo, lo + bytes};
 }
+// A buffer whose end would wrap past the top of the address space.
+bool wraps(Range r) { return r.hi < r.lo; }
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.hi && b.lo < b.hi; }
 bool same(Range a, Range b) { return a.lo == b.lo && a.hi == b.hi; }
 
@@ -134,9 +136,11 @@ rsx_status_t fuse_copy(const void* const* tens, const size_t* counts, int ntenso
   for (int i = 0; i < ntensors; ++i)
     if (counts[i] != 0 && tens[i] == nullptr) return RSX_ERR_INVALID_ARGUMENT;
   const Range fr = range_of(fused, total);
+  if (wraps(fr)) return RSX_ERR_INVALID_ARGUMENT;
   for (int i = 0; i < ntensors; ++i) {
     if (counts[i] == 0) continue;
     const Range ti = range_of(tens[i], counts[i] * es);
+    if (wraps(ti)) return RSX_ERR_INVALID_ARGUMENT;
     if (overlap(fr, ti)) return RSX_ERR_ALIASING;
     if (!pack) {  // unpack writes the tensors: they must not overlap each other
       for (int j = i + 1; j < ntensors; ++j)
@@ -239,6 +243,7 @@ rsx_status_t rsx_reduce_scatter(const void* const* sendbufs, void* const* recvbu
   for (int r = 0; r < nranks; ++r) {
     in[r] = range_of(sendbufs[r], in_bytes);
     out[r] = range_of(recvbufs[r], seg_bytes);
+    if (wraps(in[r]) || wraps(out[r])) return RSX_ERR_INVALID_ARGUMENT;
   }
   if (!reads_consistent(in, nranks) || !pairwise_disjoint(out, nranks)) return RSX_ERR_ALIASING;
   for (int k = 0; k < nranks; ++k) {
@@ -283,6 +288,7 @@ rsx_status_t rsx_all_gather(const void* const* sendbufs, void* const* recvbufs, 
   for (int r = 0; r < nranks; ++r) {
     in[r] = range_of(sendbufs[r], piece_bytes);
     out[r] = range_of(recvbufs[r], out_bytes);
+    if (wraps(in[r]) || wraps(out[r])) return RSX_ERR_INVALID_ARGUMENT;
   }
   if (!pairwise_disjoint(out, nranks)) return RSX_ERR_ALIASING;
   bool in_place_all = true;
@@ -335,6 +341,7 @@ rsx_status_t rsx_all_reduce(const void* const* sendbufs, void* const* recvbufs, 
   for (int r = 0; r < nranks; ++r) {
     in[r] = range_of(sendbufs[r], bytes);
     out[r] = range_of(recvbufs[r], bytes);
+    if (wraps(in[r]) || wraps(out[r])) return RSX_ERR_INVALID_ARGUMENT;
   }
   if (!reads_consistent(in, nranks) || !pairwise_disjoint(out, nranks)) return RSX_ERR_ALIASING;
   for (int r = 0; r < nranks; ++r) {
@@ -407,6 +414,7 @@ rsx_status_t rsx_fused_all_reduce(const void* const* sendtensors, void* const* r
       const void* rp = recvtensors[static_cast<size_t>(r) * ntensors + i];
       if (sp == nullptr || rp == nullptr) return RSX_ERR_INVALID_ARGUMENT;
       const Range sr = range_of(sp, counts[i] * es), rr = range_of(rp, counts[i] * es);
+      if (wraps(sr) || wraps(rr)) return RSX_ERR_INVALID_ARGUMENT;
       sends.push_back({sr.lo, sr.hi, i});
       recvs.push_back({rr.lo, rr.hi, i});
       in_place_all = in_place_all && sp == rp;

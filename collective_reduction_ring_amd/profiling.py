@@ -55,7 +55,7 @@ def counter_per_dispatch(path: str, counter: str, kernel: str) -> list[float]:
 
 def ktrace_summary(trace: str, stats: str, kernel: str, skip: int, timed: int, command: str) -> str:
     srows = _rows(stats)
-    rows = sorted((r for r in _rows(trace) if kernel in r["Kernel_Name"]),
+    rows = sorted((r for r in _rows(trace) if kernel and kernel in r["Kernel_Name"]),
                   key=lambda r: int(r["Start_Timestamp"]))
     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
     last = durs[skip:skip + timed] if timed else durs[skip:]
@@ -75,6 +75,8 @@ def ktrace_summary(trace: str, stats: str, kernel: str, skip: int, timed: int, c
         lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                      f"{float(r['Percentage']):.1f}% |")
+    if not kernel:
+        return "\n".join(lines + [""])
     lines += [
         "",
         f"`{kernel}`: {len(durs)} dispatches; mean of dispatches {skip}..{skip + len(last) - 1} "
@@ -129,7 +131,7 @@ def main() -> None:
     k = sub.add_parser("ktrace")
     k.add_argument("--trace", required=True)
     k.add_argument("--stats", required=True)
-    k.add_argument("--kernel", required=True)
+    k.add_argument("--kernel", default="", help="kernel whose timed window to summarise")
     k.add_argument("--skip", type=int, default=0)
     k.add_argument("--timed", type=int, default=0)
     k.add_argument("--command", required=True)

@@ -268,3 +268,13 @@ def test_fused_all_reduce_aliasing(lib):
     assert _far(lib, s, [s[1], r[1], r[2], r[3]], [50, 50], 2) == 5
     # single rank, every destination its own source: nothing to do
     assert _far(lib, [A, A + MB], [A, A + MB], c, 1) == 0
+
+
+@fake_ptrs
+def test_buffers_wrapping_the_address_space(lib):
+    top = 2 ** 64 - 4096
+    assert _rs(lib, [top, A], [A + MB, A + 2 * MB], 2, 1024) == 1
+    assert _ar(lib, [A, A + MB], [A + 2 * MB, top], 2, 4096) == 1
+    assert _ag(lib, [A, A + MB], [top, A + 4 * MB], 2, 1024) == 1
+    assert lib.rsx_fuse_pack(_arr([A]), L.size_array([4096]), 1, top, 0, None) == 1
+    assert _far(lib, [top, A + MB], [A + 2 * MB, A + 3 * MB], [4096], 2) == 1
