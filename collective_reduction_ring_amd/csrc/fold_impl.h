@@ -314,7 +314,9 @@ __global__ __launch_bounds__(kBlock) void list_fold_kernel(const ListArgs a) {
   }
   const ListPiece& pc = a.piece[lo];
   const uint32_t tile = t - a.tile_start[lo];
-  const uint32_t base = pc.tensor * (2 * W);
+  const bool in_place = a.in_place != 0;
+  const uint32_t base = pc.tensor * (in_place ? W : 2 * W);
+  const uint32_t dbase = in_place ? base : base + W;
   const uint32_t first = (pc.seg + a.rot) % W;
   const S* src[W];
   S* dst[W];
@@ -323,7 +325,7 @@ __global__ __launch_bounds__(kBlock) void list_fold_kernel(const ListArgs a) {
     uint32_t r = first + j;
     if (r >= static_cast<uint32_t>(W)) r -= W;
     src[j] = static_cast<const S*>(a.ptr[base + r]);
-    dst[j] = static_cast<S*>(a.ptr[base + W + j]);
+    dst[j] = static_cast<S*>(a.ptr[dbase + j]);
   }
   if (pc.vec) {
     fold_tile<D, OP, W, W, kStoreStream, true, false>(src, dst, 0, pc.lo, pc.hi, tile);

@@ -428,12 +428,15 @@ rsx_status_t rsx_fused_all_reduce(const void* const* sendtensors, void* const* r
   const uint64_t per = static_cast<uint64_t>(fold_units(w)) * kBlock;
   const int vl = static_cast<int>(kVecBytes / es);
 
+  // In place, a tensor needs W pointer slots instead of 2W.
+  const int slots = in_place_all ? w : 2 * w;
   ListArgs a;
   uint64_t tiles = 0;
   int ntens = 0;  // tensors in the current launch
   auto reset = [&]() {
     memset(&a, 0, sizeof(a));
     a.rot = naive ? 0 : 1;
+    a.in_place = in_place_all ? 1 : 0;
     tiles = 0;
     ntens = 0;
   };
@@ -465,7 +468,7 @@ rsx_status_t rsx_fused_all_reduce(const void* const* sendtensors, void* const* r
     const uint32_t k0 = naive ? 0 : static_cast<uint32_t>(off / seg);
     const uint32_t k1 = naive ? 0 : static_cast<uint32_t>((off + c - 1) / seg);
     const uint32_t npc = k1 - k0 + 1;
-    if ((ntens + 1) * 2 * w > kListPtrs || a.npieces + npc > static_cast<uint32_t>(kListPieces)) {
+    if ((ntens + 1) * slots > kListPtrs || a.npieces + npc > static_cast<uint32_t>(kListPieces)) {
       const rsx_status_t st = flush();
       if (st != RSX_SUCCESS) return st;
     }
@@ -473,8 +476,8 @@ rsx_status_t rsx_fused_all_reduce(const void* const* sendtensors, void* const* r
     for (int r = 0; r < w; ++r) {
       void* sp = const_cast<void*>(sendtensors[static_cast<size_t>(r) * ntensors + i]);
       void* rp = recvtensors[static_cast<size_t>(r) * ntensors + i];
-      a.ptr[ntens * 2 * w + r] = sp;
-      a.ptr[ntens * 2 * w + w + r] = rp;
+      a.ptr[ntens * slots + r] = sp;
+      if (!in_place_all) a.ptr[ntens * slots + w + r] = rp;
       vec = vec && aligned16(sp) && aligned16(rp);
     }
     for (uint32_t k = k0; k <= k1; ++k) {

@@ -84,9 +84,11 @@ struct MultiCopyArgs {
 // launch are handed to the XCDs round-robin by workgroup id.
 constexpr uint32_t kXcds = 8;
 
-// dwordx4 per lane per source in the fold kernels, by rank count: with W
-// sources a lane already has W loads in flight; fewer sources get more units.
-constexpr int fold_units(int world) { return world <= 2 ? 4 : world <= 4 ? 2 : 1; }
+// dwordx4 per lane per source in the fold kernels.  One, for every W: a lane
+// already has W loads in flight, and on MI355X more resident waves with one
+// vector each beat fewer waves with several (measured for W = 2, 4, 8, 16,
+// reduce-scatter and all-reduce alike).
+constexpr int fold_units(int /*world*/) { return 1; }
 
 // Grid size for `tiles` tiles: a multiple of the XCD count.
 inline uint64_t xcd_grid(uint64_t tiles) { return (tiles + kXcds - 1) / kXcds * kXcds; }
@@ -115,17 +117,18 @@ constexpr int kListPtrs = 256;   // pointer slots per launch, 2*W per tensor
 constexpr int kListPieces = 48;  // pieces per launch
 struct ListPiece {
   uint64_t lo, hi;   // tensor-local element range
-  uint32_t tensor;   // the tensor's pointers start at slot tensor * 2W
+  uint32_t tensor;   // the tensor's pointers start at slot tensor * 2W (tensor * W in place)
   uint16_t seg;      // segment of the fused layout (fold starts at rank seg + rot)
   uint16_t vec;      // 1: all 2W buffers of the tensor are 16-byte aligned
 };
 struct ListArgs {
   uint32_t npieces;
   uint32_t rot;
+  uint32_t in_place;  // 1: every destination is its own source; W slots per tensor
   uint32_t tile_start[kListPieces + 1];  // piece i owns tiles [tile_start[i], tile_start[i+1])
   ListPiece piece[kListPieces];
   // tensor t: sources of ranks 0..W-1 at slots [t*2W, t*2W + W), destinations
-  // at [t*2W + W, t*2W + 2W).
+  // at [t*2W + W, t*2W + 2W); in place, sources only, at [t*W, t*W + W).
   void* ptr[kListPtrs];
 };
 

@@ -168,7 +168,7 @@ rsx_status_t rsx_fuse_unpack(const void* fused, void* const* tensors, const size
  * In place: recvtensors[r*n + i] == sendtensors[r2*n + i] (same tensor index)
  * is allowed; any other overlap of a destination returns RSX_ERR_ALIASING.
  * Zero-count tensors are skipped and may be null.  Launches about one kernel
- * per 256 / (2W) tensors.
+ * per 256 / (2W) tensors (256 / W when every destination is its own source).
  */
 rsx_status_t rsx_fused_all_reduce(const void* const* sendtensors, void* const* recvtensors,
                                   const size_t* counts, int ntensors, int nranks,

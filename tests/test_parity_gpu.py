@@ -21,7 +21,7 @@ VL = {"f32": 4, "bf16": 8, "i32": 4}
 
 
 def units(w):  # dwordx4 per lane per source in the fold kernels
-    return 8 if w <= 2 else 4 if w <= 4 else 2 if w <= 8 else 1
+    return 1
 
 
 def tile_elems(w, dtype):
