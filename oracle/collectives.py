@@ -259,9 +259,43 @@ def fuse_unpack(fused: np.ndarray, counts) -> list[np.ndarray]:
     return [np.asarray(fused)[o:o + int(c)].copy() for o, c in zip(fuse_offsets(counts), counts)]
 
 
+def fusion_groups(sizes_bytes, dtypes, threshold: int) -> list[tuple[int, int]]:
+    """Horovod's fusion of consecutive all-reduce requests [HV BackgroundThreadLoop].
+
+    Walk the tensors in order.  A group starts at the first tensor not yet
+    grouped and keeps taking the next tensor while it has the same dtype and
+    the group's bytes plus the next tensor's bytes stay at or below
+    ``threshold``; at the first tensor that does not fit, the group ends (no
+    tensor is skipped to fill a group).  Returns [start, end) index ranges.
+    """
+    groups = []
+    i, n = 0, len(sizes_bytes)
+    while i < n:
+        total = int(sizes_bytes[i])
+        j = i + 1
+        while j < n and dtypes[j] == dtypes[i] and total + int(sizes_bytes[j]) <= threshold:
+            total += int(sizes_bytes[j])
+            j += 1
+        groups.append((i, j))
+        i = j
+    return groups
+
+
 def fused_all_reduce(tensors_per_rank, op: str = "sum", dtype: str = "f32") -> list[list[np.ndarray]]:
     """pack -> all-reduce of the fusion buffers -> unpack, per rank [HV ``PerformOperation``]."""
     counts = [len(t) for t in tensors_per_rank[0]]
     fused = [fuse_pack(ts) for ts in tensors_per_rank]
     red = all_reduce(fused, op, dtype)
     return [fuse_unpack(f, counts) for f in red]
+
+
+def grouped_all_reduce(tensors_per_rank, threshold: int, op: str = "sum",
+                       dtype: str = "f32") -> list[list[np.ndarray]]:
+    """Fusion groups of the tensor list, each all-reduced as one fusion buffer."""
+    sizes = [np.asarray(t).nbytes for t in tensors_per_rank[0]]
+    out = [[None] * len(sizes) for _ in tensors_per_rank]
+    for lo, hi in fusion_groups(sizes, [dtype] * len(sizes), threshold):
+        part = fused_all_reduce([ts[lo:hi] for ts in tensors_per_rank], op, dtype)
+        for r in range(len(tensors_per_rank)):
+            out[r][lo:hi] = part[r]
+    return out

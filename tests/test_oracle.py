@@ -339,3 +339,33 @@ def test_brute_force_scalar_loop(w):
             for j in range(2, w + 1):
                 acc = np.float32(acc + xs[(k + j) % w][k * s + i])
             assert rs[k][i] == acc
+
+
+# --------------------------------------------- fusion planner (Horovod) ----
+
+def test_fusion_groups_hand_cases():
+    f32 = "f32"
+    # equality with the threshold still fuses: 10 + 20 + 30 = 60 <= 60
+    assert oracle.fusion_groups([10, 20, 30, 40], [f32] * 4, 60) == [(0, 3), (3, 4)]
+    assert oracle.fusion_groups([10, 20, 30, 40], [f32] * 4, 59) == [(0, 2), (2, 3), (3, 4)]
+    # a tensor above the threshold is a group of its own
+    assert oracle.fusion_groups([100, 1, 1], [f32] * 3, 50) == [(0, 1), (1, 3)]
+    # a dtype change ends a group
+    assert oracle.fusion_groups([1, 1, 1], [f32, "i32", f32], 10 ** 9) == [(0, 1), (1, 2), (2, 3)]
+    # no tensor is skipped to fill a group
+    assert oracle.fusion_groups([10, 100, 10], [f32] * 3, 50) == [(0, 1), (1, 2), (2, 3)]
+    # threshold 0: only zero-byte tensors fuse
+    assert oracle.fusion_groups([4, 4], [f32] * 2, 0) == [(0, 1), (1, 2)]
+    assert oracle.fusion_groups([0, 0, 5], [f32] * 3, 4) == [(0, 2), (2, 3)]
+    assert oracle.fusion_groups([], [], 64) == []
+
+
+def test_grouped_all_reduce_int_sum_is_per_tensor_sum():
+    rng = np.random.default_rng(4)
+    counts = [5, 17, 3, 40, 1, 9]
+    per_rank = [[rng.integers(-100, 100, c).astype(np.int32) for c in counts] for _ in range(3)]
+    out = oracle.grouped_all_reduce(per_rank, threshold=4 * 30, op="sum", dtype="i32")
+    for i in range(len(counts)):
+        want = np.sum([per_rank[r][i] for r in range(3)], axis=0).astype(np.int32)
+        for r in range(3):
+            assert np.array_equal(out[r][i], want)
