@@ -225,8 +225,11 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
         e2e = plan
         nb = world * total * 4
         direct = rsx.TensorFusionAllReduce(tens, None, "sum", "ring")
+        grouped = rsx.GroupedAllReduce(tens, None, "sum", "ring", 64 * 2 ** 20)
         return {"workload": f"fused: W=4, {len(sizes)} fp32 tensors, {total} elements/rank",
                 "direct_tensor_fusion_all_reduce": _stat(time_launches(direct, reps, warm, torch), 2 * nb),
+                "grouped_64MiB_threshold": dict(
+                    _stat(time_launches(grouped, reps, warm, torch), 2 * nb), groups=len(grouped.groups)),
                 "pack": _stat(time_launches(pack, reps, warm, torch), 2 * nb),
                 "all_reduce": _stat(time_launches(arp, reps, warm, torch), 2 * nb),
                 "unpack": _stat(time_launches(unpack, reps, warm, torch), 2 * nb),

@@ -6,7 +6,7 @@ Python layer only marshals tensors into pointers and counts.
 """
 from .api import (  # noqa: F401
     ALGOS, DTYPES, OPS, AllReduce, FusedAllReduce, FusePack, FuseUnpack, ReduceScatter,
-    TensorFusionAllReduce,
+    GroupedAllReduce, TensorFusionAllReduce, fusion_groups, fusion_threshold,
     all_gather, all_reduce,
     all_reduce_bucketed, fuse_pack, fuse_unpack, fused_all_reduce, reduce_scatter,
     segment_begin, version,

@@ -19,6 +19,7 @@ RSX_ALGO_RING, RSX_ALGO_NAIVE, RSX_ALGO_AUTO = 0, 1, 2
 RSX_MAX_RANKS = 16
 RSX_NAIVE_MAX_BYTES = 32768
 RSX_FUSE_BATCH = 64
+RSX_FUSION_THRESHOLD_DEFAULT = 64 * 1024 * 1024   # Horovod's default tensor_fusion_threshold
 
 STATUS = {
     0: "RSX_SUCCESS",
@@ -42,6 +43,7 @@ SIGNATURES = {
     "rsx_fuse_pack": (_I, [_PP, ctypes.POINTER(_SZ), _I, _P, _I, _P]),
     "rsx_fuse_unpack": (_I, [_P, _PP, ctypes.POINTER(_SZ), _I, _I, _P]),
     "rsx_fused_all_reduce": (_I, [_PP, _PP, ctypes.POINTER(_SZ), _I, _I, _I, _I, _I, _P]),
+    "rsx_fusion_plan": (_I, [ctypes.POINTER(_SZ), ctypes.POINTER(_I), _I, _SZ, ctypes.POINTER(_I)]),
     "rsx_segment_begin": (_SZ, [_SZ, _I, _I]),
     "rsx_dtype_size": (_SZ, [_I]),
     "rsx_status_string": (ctypes.c_char_p, [_I]),

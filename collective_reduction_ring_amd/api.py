@@ -13,6 +13,8 @@ all-gather ("Distributed primitives", Ring AllReduce) in one pass.
 """
 from __future__ import annotations
 
+import ctypes
+import os
 from typing import Sequence
 
 import torch
@@ -270,6 +272,48 @@ class TensorFusionAllReduce:
 
     def __call__(self, stream=None) -> None:
         _launch(self, "rsx_fused_all_reduce", stream)
+
+
+def fusion_threshold() -> int:
+    """Fusion threshold in bytes: ``RSX_FUSION_THRESHOLD`` if set, else 64 MiB
+    (Horovod's default, overridable from the environment in the same way)."""
+    v = os.environ.get("RSX_FUSION_THRESHOLD")
+    return int(v) if v is not None else L.RSX_FUSION_THRESHOLD_DEFAULT
+
+
+def fusion_groups(tensors, threshold: int | None = None) -> list[tuple[int, int]]:
+    """Horovod's grouping of consecutive same-dtype tensors under a byte threshold,
+    computed by ``rsx_fusion_plan``; returns [start, end) index ranges."""
+    threshold = fusion_threshold() if threshold is None else int(threshold)
+    n = len(tensors)
+    if n == 0:
+        return []
+    counts = L.size_array([t.numel() for t in tensors])
+    dts = (ctypes.c_int * n)(*[_dtype_code(t) for t in tensors])
+    ends = (ctypes.c_int * n)()
+    g = L.lib().rsx_fusion_plan(counts, dts, n, threshold, ends)
+    if g < 0:
+        raise ValueError("rsx_fusion_plan rejected its arguments")
+    starts = [0] + [ends[k] for k in range(g - 1)]
+    return [(starts[k], ends[k]) for k in range(g)]
+
+
+class GroupedAllReduce:
+    """Prepared all-reduce of tensor lists in Horovod fusion groups: each group of
+    consecutive same-dtype tensors under the byte threshold is all-reduced as one
+    fusion buffer would be (one ``rsx_fused_all_reduce`` per group)."""
+
+    def __init__(self, tensors_per_rank, outputs_per_rank=None, op: str = "sum", algo: str = "ring",
+                 threshold: int | None = None):
+        outputs_per_rank = tensors_per_rank if outputs_per_rank is None else outputs_per_rank
+        self.groups = fusion_groups(tensors_per_rank[0], threshold)
+        self.plans = [TensorFusionAllReduce([ts[lo:hi] for ts in tensors_per_rank],
+                                            [os_[lo:hi] for os_ in outputs_per_rank], op, algo)
+                      for lo, hi in self.groups]
+
+    def __call__(self, stream=None) -> None:
+        for p in self.plans:
+            p(stream)
 
 
 def fuse_pack(tensors, fused: torch.Tensor, stream=None) -> None:

@@ -503,6 +503,35 @@ rsx_status_t rsx_fused_all_reduce(const void* const* sendtensors, void* const* r
   return flush();
 }
 
+int rsx_fusion_plan(const size_t* counts, const rsx_dtype_t* dtypes, int ntensors,
+                    size_t threshold_bytes, int* group_end) {
+  if (ntensors < 0) return -1;
+  if (ntensors == 0) return 0;
+  if (counts == nullptr || dtypes == nullptr || group_end == nullptr) return -1;
+  for (int i = 0; i < ntensors; ++i)
+    if (esize_of(dtypes[i]) == 0) return -1;
+  // Bytes of tensor i, saturating (a tensor that large is a group of its own).
+  auto bytes_of = [&](int i) {
+    size_t b;
+    return mul_ok(counts[i], esize_of(dtypes[i]), &b) ? b : SIZE_MAX;
+  };
+  int ngroups = 0;
+  int i = 0;
+  while (i < ntensors) {
+    size_t total = bytes_of(i);
+    int j = i + 1;
+    while (j < ntensors && dtypes[j] == dtypes[i]) {
+      const size_t b = bytes_of(j);
+      if (b > threshold_bytes || total > threshold_bytes - b) break;
+      total += b;
+      ++j;
+    }
+    group_end[ngroups++] = j;
+    i = j;
+  }
+  return ngroups;
+}
+
 size_t rsx_segment_begin(size_t count, int nranks, int k) {
   if (nranks < 1 || k < 0) return 0;
   const size_t seg = count / nranks + (count % nranks != 0);

@@ -176,6 +176,25 @@ rsx_status_t rsx_fused_all_reduce(const void* const* sendtensors, void* const* r
                                   hipStream_t stream);
 
 /*
+ * Tensor-fusion planner [HV BackgroundThreadLoop, fusion of consecutive
+ * all-reduce requests; HorovodGlobalState tensor_fusion_threshold, default
+ * 64 MiB, overridden by an environment variable].
+ *
+ * Groups tensors 0..ntensors-1 in order: a group starts at the first tensor
+ * not yet grouped and takes each next tensor while that tensor has the
+ * group's dtype and the group's bytes plus its bytes stay <= threshold_bytes.
+ * A tensor that does not fit ends the group; none is skipped.  A tensor
+ * larger than the threshold is a group of its own.
+ * counts[i], dtypes[i]: tensor i's element count and type (host arrays).
+ * group_end: host array of at least ntensors ints; group g is tensors
+ *   [group_end[g-1], group_end[g]) (group_end[-1] taken as 0).
+ * Returns the number of groups (0 for no tensors), or -1 for a null array, a
+ * negative ntensors or an invalid dtype.  Host logic only: no HIP call.
+ */
+int rsx_fusion_plan(const size_t* counts, const rsx_dtype_t* dtypes, int ntensors,
+                    size_t threshold_bytes, int* group_end);
+
+/*
  * First element of segment k in RSX_ALGO_RING all-reduce of `count`
  * elements over `nranks` ranks: min(k * ceil(count/nranks), count).
  * k may be 0..nranks (k = nranks gives count).  Returns 0 for nranks < 1.

@@ -278,3 +278,42 @@ def test_buffers_wrapping_the_address_space(lib):
     assert _ag(lib, [A, A + MB], [top, A + 4 * MB], 2, 1024) == 1
     assert lib.rsx_fuse_pack(_arr([A]), L.size_array([4096]), 1, top, 0, None) == 1
     assert _far(lib, [top, A + MB], [A + 2 * MB, A + 3 * MB], [4096], 2) == 1
+
+
+def _plan(lib, counts, dtypes, threshold):
+    n = len(counts)
+    ends = (ctypes.c_int * max(1, n))()
+    dts = (ctypes.c_int * max(1, n))(*dtypes)
+    g = lib.rsx_fusion_plan(L.size_array(counts), dts, n, threshold, ends)
+    if g < 0:
+        return None
+    starts = [0] + [ends[k] for k in range(g - 1)]
+    return [(starts[k], ends[k]) for k in range(g)]
+
+
+def test_fusion_plan_matches_oracle(lib):
+    import numpy as np
+
+    import oracle
+    es = {0: 4, 1: 2, 2: 4}
+    rng = np.random.default_rng(8)
+    for trial in range(400):
+        n = int(rng.integers(0, 40))
+        counts = [int(c) for c in rng.integers(0, 5000, n)]
+        if trial % 5 == 0:
+            counts = [int(c) for c in rng.integers(0, 3, n)]
+        dts = [int(d) for d in rng.choice([0, 0, 0, 1, 2], n)]
+        th = int(rng.choice([0, 1, 100, 4000, 16000, 64 * 2 ** 20]))
+        got = _plan(lib, counts, dts, th)
+        want = oracle.fusion_groups([c * es[d] for c, d in zip(counts, dts)], dts, th)
+        assert got == want, (counts, dts, th)
+
+
+def test_fusion_plan_validation(lib):
+    assert lib.rsx_fusion_plan(None, None, 0, 10, None) == 0
+    assert lib.rsx_fusion_plan(None, None, -1, 10, None) == -1
+    ends = (ctypes.c_int * 2)()
+    assert lib.rsx_fusion_plan(L.size_array([1, 2]), (ctypes.c_int * 2)(0, 7), 2, 10, ends) == -1
+    assert lib.rsx_fusion_plan(L.size_array([1, 2]), None, 2, 10, ends) == -1
+    # a tensor whose byte count overflows is a group of its own
+    assert _plan(lib, [2 ** 63, 1, 1], [0, 0, 0], 2 ** 40) == [(0, 1), (1, 3)]

@@ -366,6 +366,24 @@ def test_tensor_fusion_unaligned_views():
             assert_parity(to_host(outs[r][i], "bf16"), want[r][i], "bf16", f"rank {r} tensor {i}")
 
 
+@pytest.mark.parametrize("threshold", [0, 4 * 5000, 4 * 60_000, 64 * 2 ** 20])
+def test_grouped_all_reduce(threshold):
+    w = 4
+    sizes = wl.fused_sizes(count=40, lo=1, hi=50_000)
+    per_rank = _list_case(23, w, sizes, "f32")
+    tens = [[to_dev(t, "f32") for t in ts] for ts in per_rank]
+    plan = rsx.GroupedAllReduce(tens, None, "sum", "ring", threshold)
+    assert plan.groups == oracle.fusion_groups([4 * int(n) for n in sizes], ["f32"] * len(sizes),
+                                               threshold)
+    say(f"grouped all-reduce threshold={threshold}: {len(plan.groups)} groups")
+    plan()
+    torch.cuda.synchronize()
+    want = oracle.grouped_all_reduce(per_rank, threshold, "sum", "f32")
+    for r in range(w):
+        for i in range(len(sizes)):
+            assert_parity(to_host(tens[r][i], "f32"), want[r][i], "f32", f"rank {r} tensor {i}")
+
+
 def test_full_c5_tensor_fusion_direct():
     w = 4
     sizes = wl.fused_sizes()
