@@ -29,10 +29,12 @@ Sources (web pages this follows):
   messages of at most 32 KB.
 
 Precision.  The pages fix it: the NCCL kernel reduces in the element type
-(``FuncSum<float>`` on ``float`` data), so fp32 is folded with fp32 IEEE
-round-to-nearest-even adds, one per ring step, and int32 with wrapping 32-bit
-adds.  bf16 data is widened exactly to fp32, folded in fp32 and rounded once
-to bf16 at the end (bf16 in, fp32 accumulate, bf16 out).
+(``FuncSum<float>`` on ``float`` data), so fp32 and fp64 are folded with IEEE
+round-to-nearest-even operations in their own type, one per ring step, and
+int8 / int32 / int64 / uint64 with wrapping integer arithmetic.  bf16 data is
+widened exactly to fp32, folded in fp32 and rounded once to bf16 at the end
+(bf16 in, fp32 accumulate, bf16 out); fp16 (the page's ``half``) is read the
+same way.
 
 Readings where the pages are silent (each listed again in the design doc):
 
@@ -43,7 +45,11 @@ Readings where the pages are silent (each listed again in the design doc):
   for min): the earlier of two equal values (``+0``/``-0``) is kept, a NaN in
   ``acc`` is kept, a later NaN is ignored;
 * ``avg`` = the sum fold, then one division by W in the accumulation type
-  (fp32 IEEE division; int32 division truncating toward zero);
+  (IEEE division for floats; signed integers truncate toward zero, uint64
+  floors);
+* ``prod`` multiplies in the accumulation type (integers wrap);
+* fp16 (the page's ``half``, whose functor is off-page) folds in fp32 and is
+  rounded once, like bf16;
 * bf16 rounding: round-to-nearest-even on the fp32 bits, NaN -> quiet NaN
   with the sign kept (``sign | 0x7FC0``), overflow to +-inf as RNE gives;
 * the naive all-reduce folds in rank order 0..W-1;
@@ -53,8 +59,15 @@ from __future__ import annotations
 
 import numpy as np
 
-OPS = ("sum", "max", "min", "avg")
-DTYPES = ("f32", "bf16", "i32")
+OPS = ("sum", "prod", "max", "min", "avg")
+DTYPES = ("f32", "bf16", "i32", "f64", "f16", "i64", "u64", "i8")
+
+# storage type of each dtype (bf16 and f16 as their 16-bit patterns)
+STORAGE = {"f32": np.float32, "bf16": np.uint16, "i32": np.int32, "f64": np.float64,
+           "f16": np.uint16, "i64": np.int64, "u64": np.uint64, "i8": np.int8}
+# integer types and the unsigned type of the same width (wrap-around arithmetic)
+_UNSIGNED = {np.dtype(np.int8): np.uint8, np.dtype(np.int32): np.uint32,
+             np.dtype(np.int64): np.uint64, np.dtype(np.uint64): np.uint64}
 
 # --------------------------------------------------------------- schedule ----
 
@@ -126,23 +139,40 @@ def f32_to_bf16(x: np.ndarray) -> np.ndarray:
 # ------------------------------------------------------------------ folds ----
 
 
+def f16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen IEEE half bit patterns to fp32 (exact)."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def f32_to_f16(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to IEEE half bit patterns, to nearest, ties to even (NumPy's conversion)."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
 def _widen(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Storage -> accumulation type: bf16 bits -> fp32; fp32 and int32 as is."""
+    """Storage -> accumulation type: bf16 and f16 bits -> fp32; every other type as is."""
     if dtype == "bf16":
         return bf16_to_f32(x)
-    if dtype == "f32":
-        return np.asarray(x, dtype=np.float32)
-    if dtype == "i32":
-        return np.asarray(x, dtype=np.int32)
+    if dtype == "f16":
+        return f16_to_f32(x)
+    if dtype in STORAGE:
+        return np.asarray(x, dtype=STORAGE[dtype])
     raise ValueError(dtype)
 
 
 def _combine(op: str, acc: np.ndarray, x: np.ndarray) -> np.ndarray:
-    """One ring step: partial received so far, combined with the local input."""
-    if op in ("sum", "avg"):
-        if acc.dtype == np.int32:  # two's-complement wrap, computed without overflow
-            return ((acc.astype(np.int64) + x.astype(np.int64)) & 0xFFFFFFFF).astype(np.uint32).view(np.int32)
-        return acc + x
+    """One ring step: partial received so far, combined with the local input.
+
+    Integer sums and products wrap modulo 2^bits: they are computed in the
+    unsigned type of the same width, whose low bits equal the two's-complement
+    result.
+    """
+    if op in ("sum", "avg", "prod"):
+        u = _UNSIGNED.get(acc.dtype)
+        if u is not None:
+            a, b = acc.view(u), x.astype(acc.dtype).view(u)
+            return (a * b if op == "prod" else a + b).astype(u).view(acc.dtype)
+        return acc * x if op == "prod" else acc + x
     if op == "max":
         return np.where(x > acc, x, acc)
     if op == "min":
@@ -153,13 +183,18 @@ def _combine(op: str, acc: np.ndarray, x: np.ndarray) -> np.ndarray:
 def _finish(op: str, acc: np.ndarray, world: int, dtype: str) -> np.ndarray:
     """Average (if asked) in the accumulation type, then back to the storage type."""
     if op == "avg":
-        if acc.dtype == np.int32:
-            a = acc.astype(np.int64)
-            acc = (np.sign(a) * (np.abs(a) // world)).astype(np.int32)
+        if acc.dtype.kind == "i":          # signed: truncate toward zero
+            q = acc // acc.dtype.type(world)
+            fix = (acc < 0) & (acc % acc.dtype.type(world) != 0)
+            acc = (q + fix.astype(acc.dtype)).astype(acc.dtype)
+        elif acc.dtype.kind == "u":
+            acc = acc // acc.dtype.type(world)
         else:
-            acc = (acc / np.float32(world)).astype(np.float32)
+            acc = (acc / acc.dtype.type(world)).astype(acc.dtype)
     if dtype == "bf16":
         return f32_to_bf16(acc)
+    if dtype == "f16":
+        return f32_to_f16(acc)
     return acc
 
 

@@ -369,3 +369,110 @@ def test_grouped_all_reduce_int_sum_is_per_tensor_sum():
         want = np.sum([per_rank[r][i] for r in range(3)], axis=0).astype(np.int32)
         for r in range(3):
             assert np.array_equal(out[r][i], want)
+
+
+# ------------------------------------- wider types and prod (next rows) ----
+
+INT_TYPES = {"i8": (np.int8, 8, True), "i32": (np.int32, 32, True),
+             "i64": (np.int64, 64, True), "u64": (np.uint64, 64, False)}
+
+
+def _wrap(v, bits, signed):
+    v %= 2 ** bits
+    return v - 2 ** bits if signed and v >= 2 ** (bits - 1) else v
+
+
+@pytest.mark.parametrize("dt", list(INT_TYPES))
+@pytest.mark.parametrize("op", ["sum", "prod"])
+def test_integer_sum_prod_wrap_like_python_ints(dt, op):
+    # Big-integer sum / product, reduced mod 2^bits: order-free and exact.
+    np_t, bits, signed = INT_TYPES[dt]
+    info = np.iinfo(np_t)
+    rng = np.random.default_rng(bits)
+    w, s = 5, 11
+    xs = [rng.integers(info.min, info.max, w * s, dtype=np_t, endpoint=True) for _ in range(w)]
+    got = np.concatenate(oracle.reduce_scatter(xs, op, dt))
+    for e in range(w * s):
+        vals = [int(x[e]) for x in xs]
+        acc = 0 if op == "sum" else 1
+        for v in vals:
+            acc = acc + v if op == "sum" else acc * v
+        assert int(got[e]) == _wrap(acc, bits, signed)
+
+
+@pytest.mark.parametrize("dt", list(INT_TYPES))
+def test_integer_max_min_avg(dt):
+    np_t, bits, signed = INT_TYPES[dt]
+    info = np.iinfo(np_t)
+    rng = np.random.default_rng(100 + bits)
+    xs = [rng.integers(info.min, info.max, 36, dtype=np_t, endpoint=True) for _ in range(4)]
+    assert np.array_equal(np.concatenate(oracle.reduce_scatter(xs, "max", dt)), np.maximum.reduce(xs))
+    assert np.array_equal(np.concatenate(oracle.reduce_scatter(xs, "min", dt)), np.minimum.reduce(xs))
+    # avg: wrapped sum, then division toward zero (floor for unsigned)
+    got = np.concatenate(oracle.reduce_scatter(xs, "avg", dt))
+    for e in range(36):
+        tot = _wrap(sum(int(x[e]) for x in xs), bits, signed)
+        q = abs(tot) // 4
+        assert int(got[e]) == (q if tot >= 0 else -q)
+
+
+def test_signed_avg_hand_cases():
+    xs = [np.array([-7, 7, -8, -128], np.int8), np.zeros(4, np.int8),
+          np.zeros(4, np.int8), np.zeros(4, np.int8)]
+    assert list(oracle.naive_all_reduce(xs, "avg", "i8")[0]) == [-1, 1, -2, -32]
+    big = np.array([np.iinfo(np.int64).min], np.int64)
+    assert oracle.naive_all_reduce([big, np.zeros(1, np.int64)], "avg", "i64")[0][0] == -(2 ** 62)
+    u = [np.array([7], np.uint64), np.zeros(1, np.uint64), np.zeros(1, np.uint64), np.zeros(1, np.uint64)]
+    assert oracle.naive_all_reduce(u, "avg", "u64")[0][0] == 1
+
+
+def test_f64_probe_and_exact_sums():
+    big = 2.0 ** 53
+    # segment 0 at W=4: ring 1,2,3,0 over (x0..x3) = (1, 2^53, 1, -2^53) gives 1, rank order 0
+    xs = [np.zeros(8) for _ in range(4)]
+    for r, v in enumerate([1.0, big, 1.0, -big]):
+        xs[r][0] = v
+    assert oracle.reduce_scatter(xs, "sum", "f64")[0][0] == 1.0
+    assert oracle.naive_all_reduce(xs, "sum", "f64")[0][0] == 0.0
+    rng = np.random.default_rng(9)
+    xi = [rng.integers(-2 ** 40, 2 ** 40, 64) for _ in range(8)]
+    got = np.concatenate(oracle.reduce_scatter([x.astype(np.float64) for x in xi], "sum", "f64"))
+    assert np.array_equal(got, np.sum(xi, axis=0).astype(np.float64))
+
+
+def test_float_prod_powers_of_two_exact_and_bounded():
+    rng = np.random.default_rng(12)
+    e = [rng.integers(-20, 20, 42) for _ in range(6)]
+    xs = [np.ldexp(np.float32(1), ei).astype(np.float32) * np.where(ei % 3 == 0, -1, 1).astype(np.float32)
+          for ei in e]
+    got = np.concatenate(oracle.reduce_scatter(xs, "prod", "f32"))
+    want = np.prod(np.stack(xs).astype(np.float64), axis=0)
+    assert np.array_equal(got.astype(np.float64), want)
+    xs = [rng.standard_normal(60).astype(np.float32) for _ in range(6)]
+    got = np.concatenate(oracle.reduce_scatter(xs, "prod", "f32")).astype(np.float64)
+    exact = np.prod(np.stack(xs).astype(np.float64), axis=0)
+    assert np.all(np.abs(got - exact) <= ((1 + 2.0 ** -24) ** 5 - 1) * np.abs(exact) * (1 + 1e-9))
+
+
+def test_f16_rounding_hand_ties_and_torch_cast():
+    f = np.float32
+    got = oracle.f32_to_f16(np.array([1 + 2 ** -11, 1 + 3 * 2 ** -11, 65520.0, 65519.0,
+                                      2.0 ** -25, 3 * 2.0 ** -25, -0.0], f))
+    # 1+2^-11 ties to 1.0; 1+3*2^-11 ties to 1+2^-9; 65520 ties to inf (65504 has an
+    # odd significand); 65519 rounds down to 65504; 2^-25 ties to 0; 1.5*2^-24 ties to 2^-23
+    assert list(got) == [0x3C00, 0x3C02, 0x7C00, 0x7BFF, 0x0000, 0x0002, 0x8000]
+    rng = np.random.default_rng(13)
+    x = np.concatenate([rng.standard_normal(100_000).astype(f),
+                        (rng.standard_normal(50_000) * 1e5).astype(f),
+                        (rng.standard_normal(50_000) * 1e-6).astype(f)])
+    want = torch.from_numpy(x).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.f32_to_f16(x), want)
+    assert np.array_equal(oracle.f16_to_f32(want), torch.from_numpy(want.view(np.int16)).view(torch.float16).float().numpy())
+
+
+def test_f16_accumulates_in_fp32():
+    # rank order: 1 + 2^-11 + 2^-11 = 1 + 2^-10 exactly in fp32 -> half 0x3C01;
+    # rounding each partial to half would give 1.0 (1 + 2^-11 ties to 1.0)
+    xs = [np.array([0x3C00], np.uint16), np.array([0x1000], np.uint16), np.array([0x1000], np.uint16)]
+    assert oracle.f16_to_f32(np.array([0x1000], np.uint16))[0] == 2.0 ** -11
+    assert oracle.naive_all_reduce(xs, "sum", "f16")[0][0] == 0x3C01
