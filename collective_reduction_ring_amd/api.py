@@ -21,8 +21,10 @@ import torch
 
 from . import _lib as L
 
-DTYPES = {torch.float32: L.RSX_FLOAT32, torch.bfloat16: L.RSX_BFLOAT16, torch.int32: L.RSX_INT32}
-OPS = {"sum": L.RSX_SUM, "max": L.RSX_MAX, "min": L.RSX_MIN, "avg": L.RSX_AVG}
+DTYPES = {torch.float32: L.RSX_FLOAT32, torch.bfloat16: L.RSX_BFLOAT16, torch.int32: L.RSX_INT32,
+          torch.float64: L.RSX_FLOAT64, torch.float16: L.RSX_FLOAT16, torch.int64: L.RSX_INT64,
+          torch.uint64: L.RSX_UINT64, torch.int8: L.RSX_INT8}
+OPS = {"sum": L.RSX_SUM, "max": L.RSX_MAX, "min": L.RSX_MIN, "avg": L.RSX_AVG, "prod": L.RSX_PROD}
 ALGOS = {"ring": L.RSX_ALGO_RING, "naive": L.RSX_ALGO_NAIVE, "auto": L.RSX_ALGO_AUTO}
 
 
@@ -63,7 +65,7 @@ def _dtype_code(t: torch.Tensor) -> int:
     try:
         return DTYPES[t.dtype]
     except KeyError:
-        raise ValueError(f"unsupported dtype {t.dtype}; use float32, bfloat16 or int32") from None
+        raise ValueError(f"unsupported dtype {t.dtype}; one of {sorted(str(d) for d in DTYPES)}") from None
 
 
 def _op_code(op: str) -> int:

@@ -22,12 +22,20 @@ namespace rsx {
 template <int ES>
 struct Unit;
 template <>
+struct Unit<1> {
+  using T = uint8_t;
+};
+template <>
 struct Unit<2> {
   using T = uint16_t;
 };
 template <>
 struct Unit<4> {
   using T = uint32_t;
+};
+template <>
+struct Unit<8> {
+  using T = uint64_t;
 };
 
 // ------------------------------------------------------------ all-gather
@@ -81,22 +89,24 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a) {
 hipError_t launch_gather(int esize, bool vec, const GatherArgs& a, dim3 grid, hipStream_t s) {
   void* args[] = {const_cast<GatherArgs*>(&a)};
   const void* fn;
-  if (esize == 2) {
-    fn = vec ? reinterpret_cast<const void*>(&gather_kernel<2, true>)
-             : reinterpret_cast<const void*>(&gather_kernel<2, false>);
-  } else if (esize == 4) {
-    fn = vec ? reinterpret_cast<const void*>(&gather_kernel<4, true>)
-             : reinterpret_cast<const void*>(&gather_kernel<4, false>);
-  } else {
-    return hipErrorInvalidValue;
+  switch (esize) {
+#define RSX_ES(n)                                                              \
+  case n:                                                                      \
+    fn = vec ? reinterpret_cast<const void*>(&gather_kernel<n, true>)          \
+             : reinterpret_cast<const void*>(&gather_kernel<n, false>);        \
+    break;
+    RSX_ES(1) RSX_ES(2) RSX_ES(4) RSX_ES(8)
+#undef RSX_ES
+    default:
+      return hipErrorInvalidValue;
   }
   return hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, s);
 }
 
 // -------------------------------------------------------- pack / unpack
 
-// Bytes [delta, delta + 16) of the 32-byte concatenation lo:hi, delta a
-// multiple of 2 in [2, 14] (Q = delta / 4 whole words, then r bytes).
+// Bytes [delta, delta + 16) of the 32-byte concatenation lo:hi, delta in
+// [1, 15] (Q = delta / 4 whole words, then r bytes).
 template <int Q>
 __device__ __forceinline__ uint4 funnel_q(const uint32_t (&w)[8], uint32_t r) {
   return make_uint4(__builtin_amdgcn_alignbyte(w[Q + 1], w[Q], r),
@@ -186,12 +196,21 @@ __global__ __launch_bounds__(kBlock) void multicopy_kernel(const MultiCopyArgs a
 hipError_t launch_multicopy(int esize, const MultiCopyArgs& a, hipStream_t s) {
   void* args[] = {const_cast<MultiCopyArgs*>(&a)};
   const void* fn;
-  if (esize == 2) {
-    fn = reinterpret_cast<const void*>(&multicopy_kernel<2>);
-  } else if (esize == 4) {
-    fn = reinterpret_cast<const void*>(&multicopy_kernel<4>);
-  } else {
-    return hipErrorInvalidValue;
+  switch (esize) {
+    case 1:
+      fn = reinterpret_cast<const void*>(&multicopy_kernel<1>);
+      break;
+    case 2:
+      fn = reinterpret_cast<const void*>(&multicopy_kernel<2>);
+      break;
+    case 4:
+      fn = reinterpret_cast<const void*>(&multicopy_kernel<4>);
+      break;
+    case 8:
+      fn = reinterpret_cast<const void*>(&multicopy_kernel<8>);
+      break;
+    default:
+      return hipErrorInvalidValue;
   }
   const uint64_t tiles = a.tile_start[a.n];
   return hipLaunchKernel(fn, dim3(static_cast<uint32_t>(xcd_grid(tiles))), dim3(kBlock), args, 0, s);

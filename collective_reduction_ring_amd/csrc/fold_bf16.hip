@@ -4,7 +4,7 @@
 namespace rsx {
 
 hipError_t launch_fold_bf16(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid,
-                         hipStream_t s) {
+                           hipStream_t s) {
   return launch_fold<BF16T>(op, world, rs, vec, a, grid, s);
 }
 

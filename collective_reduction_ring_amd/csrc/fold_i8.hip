@@ -1,0 +1,15 @@
+// Fold kernels instantiated for one element type (see fold_impl.h).
+#include "fold_impl.h"
+
+namespace rsx {
+
+hipError_t launch_fold_i8(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid,
+                           hipStream_t s) {
+  return launch_fold<I8T>(op, world, rs, vec, a, grid, s);
+}
+
+hipError_t launch_list_i8(int op, int world, const ListArgs& a, dim3 grid, hipStream_t s) {
+  return launch_list<I8T>(op, world, a, grid, s);
+}
+
+}  // namespace rsx

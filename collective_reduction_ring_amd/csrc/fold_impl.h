@@ -19,6 +19,8 @@
 // the first combine.
 #pragma once
 
+#include <type_traits>
+
 #include "mem.h"
 #include "rsx_internal.h"
 
@@ -40,6 +42,31 @@ struct BF16T {
   using S = uint16_t;
   using A = float;
   static constexpr int kVL = 8;
+};
+struct F64T {
+  using S = double;
+  using A = double;
+  static constexpr int kVL = 2;
+};
+struct F16T {
+  using S = uint16_t;  // IEEE half bit patterns
+  using A = float;
+  static constexpr int kVL = 8;
+};
+struct I64T {
+  using S = int64_t;
+  using A = int64_t;
+  static constexpr int kVL = 2;
+};
+struct U64T {
+  using S = uint64_t;
+  using A = uint64_t;
+  static constexpr int kVL = 2;
+};
+struct I8T {
+  using S = int8_t;
+  using A = int8_t;
+  static constexpr int kVL = 16;
 };
 
 // bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 bits.
@@ -114,11 +141,118 @@ struct Elem<BF16T> {
   }
 };
 
+// 64-bit elements: two per dwordx4, low word first.
+template <class T>
+struct Elem64 {
+  __device__ static T widen(T x) { return x; }
+  __device__ static T narrow(T a) { return a; }
+  __device__ static void unpack(const uint4& v, T (&a)[2]) {
+    a[0] = __builtin_bit_cast(T, (static_cast<uint64_t>(v.y) << 32) | v.x);
+    a[1] = __builtin_bit_cast(T, (static_cast<uint64_t>(v.w) << 32) | v.z);
+  }
+  __device__ static uint4 pack(const T (&a)[2]) {
+    const uint64_t lo = __builtin_bit_cast(uint64_t, a[0]), hi = __builtin_bit_cast(uint64_t, a[1]);
+    return make_uint4(static_cast<uint32_t>(lo), static_cast<uint32_t>(lo >> 32),
+                      static_cast<uint32_t>(hi), static_cast<uint32_t>(hi >> 32));
+  }
+};
+template <>
+struct Elem<F64T> : Elem64<double> {};
+template <>
+struct Elem<I64T> : Elem64<int64_t> {};
+template <>
+struct Elem<U64T> : Elem64<uint64_t> {};
+
+// IEEE half: widened exactly to fp32 and narrowed with round-to-nearest-even
+// (the hardware conversions, which implement both).
+template <>
+struct Elem<F16T> {
+  __device__ static float widen(uint16_t h) { return static_cast<float>(__builtin_bit_cast(_Float16, h)); }
+  // The fold's fp32 result is rounded to half once, by itself.  The empty asm
+  // pins `a` as an fp32 register value: without it the compiler fuses the
+  // last fp32 add or multiply with this conversion into one mixed-precision
+  // FMA that rounds the exact result straight to half, which differs from
+  // fp32-then-half rounding whenever the fp32 value lands on a half tie.
+  __device__ static uint16_t narrow(float a) {
+    asm volatile("" : "+v"(a));
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(a));
+  }
+  __device__ static void unpack(const uint4& v, float (&a)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[2 * i] = widen(static_cast<uint16_t>(w[i]));
+      a[2 * i + 1] = widen(static_cast<uint16_t>(w[i] >> 16));
+    }
+  }
+  __device__ static uint4 pack(const float (&a)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = narrow(a[2 * i]) | (static_cast<uint32_t>(narrow(a[2 * i + 1])) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+
+// int8: sixteen per dwordx4, byte i of word i / 4 at bit 8 * (i % 4).
+template <>
+struct Elem<I8T> {
+  __device__ static int8_t widen(int8_t x) { return x; }
+  __device__ static int8_t narrow(int8_t a) { return a; }
+  __device__ static void unpack(const uint4& v, int8_t (&a)[16]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a[i] = static_cast<int8_t>(w[i / 4] >> (8 * (i % 4)));
+  }
+  __device__ static uint4 pack(const int8_t (&a)[16]) {
+    uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i / 4] |= static_cast<uint32_t>(static_cast<uint8_t>(a[i])) << (8 * (i % 4));
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+
 // ------------------------------------------------------------------- ops
 
-__device__ __forceinline__ float add_op(float a, float b) { return a + b; }
-__device__ __forceinline__ int32_t add_op(int32_t a, int32_t b) {
-  return static_cast<int32_t>(static_cast<uint32_t>(a) + static_cast<uint32_t>(b));
+// Sums and products: IEEE in the float types; integers wrap, computed in the
+// unsigned type of the same width (whose low bits are the two's-complement
+// result, without signed-overflow undefined behaviour).
+template <class T>
+struct Unsigned;
+template <>
+struct Unsigned<int8_t> {
+  using T = uint8_t;
+};
+template <>
+struct Unsigned<int32_t> {
+  using T = uint32_t;
+};
+template <>
+struct Unsigned<int64_t> {
+  using T = uint64_t;
+};
+template <>
+struct Unsigned<uint64_t> {
+  using T = uint64_t;
+};
+
+template <class A>
+__device__ __forceinline__ A add_op(A a, A b) {
+  if constexpr (std::is_floating_point<A>::value) {
+    return a + b;
+  } else {
+    using U = typename Unsigned<A>::T;
+    return static_cast<A>(static_cast<U>(static_cast<U>(a) + static_cast<U>(b)));
+  }
+}
+
+template <class A>
+__device__ __forceinline__ A mul_op(A a, A b) {
+  if constexpr (std::is_floating_point<A>::value) {
+    return a * b;
+  } else {
+    using U = typename Unsigned<A>::T;
+    return static_cast<A>(static_cast<U>(static_cast<U>(a) * static_cast<U>(b)));
+  }
 }
 
 // One ring step: the partial folded so far, combined with the next rank's value.
@@ -131,16 +265,19 @@ __device__ __forceinline__ A combine(A acc, A x) {
     return (x > acc) ? x : acc;
   } else if constexpr (OP == RSX_MIN) {
     return (x < acc) ? x : acc;
+  } else if constexpr (OP == RSX_PROD) {
+    return mul_op(acc, x);
   } else {
     return add_op(acc, x);
   }
 }
 
-// avg: one division by W in the accumulation type (int32 truncates toward zero).
+// avg: one division by W in the accumulation type (IEEE for floats; C
+// integer division: toward zero for signed types, floor for uint64).
 template <int OP, int W, class A>
 __device__ __forceinline__ A finish(A acc) {
   if constexpr (OP == RSX_AVG) {
-    return acc / static_cast<A>(W);
+    return static_cast<A>(acc / static_cast<A>(W));
   } else {
     return acc;
   }
@@ -393,6 +530,8 @@ hipError_t launch_list(int op, int world, const ListArgs& a, dim3 grid, hipStrea
       return launch_list_op<D, RSX_MIN>(world, a, grid, s);
     case RSX_AVG:
       return launch_list_op<D, RSX_AVG>(world, a, grid, s);
+    case RSX_PROD:
+      return launch_list_op<D, RSX_PROD>(world, a, grid, s);
     default:
       return hipErrorInvalidValue;
   }
@@ -410,6 +549,8 @@ hipError_t launch_fold(int op, int world, bool rs, bool vec, const FoldArgs& a, 
       return launch_op<D, RSX_MIN>(world, rs, vec, a, grid, s);
     case RSX_AVG:
       return launch_op<D, RSX_AVG>(world, rs, vec, a, grid, s);
+    case RSX_PROD:
+      return launch_op<D, RSX_PROD>(world, rs, vec, a, grid, s);
     default:
       return hipErrorInvalidValue;
   }

@@ -26,17 +26,72 @@ rsx_status_t hip_status(hipError_t e) {
 size_t esize_of(int dtype) {
   switch (dtype) {
     case RSX_FLOAT32:
-      return 4;
-    case RSX_BFLOAT16:
-      return 2;
     case RSX_INT32:
       return 4;
+    case RSX_BFLOAT16:
+    case RSX_FLOAT16:
+      return 2;
+    case RSX_FLOAT64:
+    case RSX_INT64:
+    case RSX_UINT64:
+      return 8;
+    case RSX_INT8:
+      return 1;
     default:
       return 0;
   }
 }
 
-bool valid_op(int op) { return op >= RSX_SUM && op <= RSX_AVG; }
+bool valid_op(int op) { return op >= RSX_SUM && op <= RSX_PROD; }
+
+// Per element type launchers (one translation unit each).
+hipError_t launch_fold_by_type(int dtype, int op, int world, bool rs, bool vec, const FoldArgs& a,
+                               dim3 grid, hipStream_t s) {
+  switch (dtype) {
+    case RSX_FLOAT32:
+      return launch_fold_f32(op, world, rs, vec, a, grid, s);
+    case RSX_BFLOAT16:
+      return launch_fold_bf16(op, world, rs, vec, a, grid, s);
+    case RSX_INT32:
+      return launch_fold_i32(op, world, rs, vec, a, grid, s);
+    case RSX_FLOAT64:
+      return launch_fold_f64(op, world, rs, vec, a, grid, s);
+    case RSX_FLOAT16:
+      return launch_fold_f16(op, world, rs, vec, a, grid, s);
+    case RSX_INT64:
+      return launch_fold_i64(op, world, rs, vec, a, grid, s);
+    case RSX_UINT64:
+      return launch_fold_u64(op, world, rs, vec, a, grid, s);
+    case RSX_INT8:
+      return launch_fold_i8(op, world, rs, vec, a, grid, s);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_list_by_type(int dtype, int op, int world, const ListArgs& a, dim3 grid,
+                               hipStream_t s) {
+  switch (dtype) {
+    case RSX_FLOAT32:
+      return launch_list_f32(op, world, a, grid, s);
+    case RSX_BFLOAT16:
+      return launch_list_bf16(op, world, a, grid, s);
+    case RSX_INT32:
+      return launch_list_i32(op, world, a, grid, s);
+    case RSX_FLOAT64:
+      return launch_list_f64(op, world, a, grid, s);
+    case RSX_FLOAT16:
+      return launch_list_f16(op, world, a, grid, s);
+    case RSX_INT64:
+      return launch_list_i64(op, world, a, grid, s);
+    case RSX_UINT64:
+      return launch_list_u64(op, world, a, grid, s);
+    case RSX_INT8:
+      return launch_list_i8(op, world, a, grid, s);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
 
 // a * b without wrapping; false on overflow.
 bool mul_ok(size_t a, size_t b, size_t* out) {
@@ -89,19 +144,7 @@ rsx_status_t launch_fold_any(int dtype, int op, int world, bool rs, bool vec, Fo
   a.tiles_total = static_cast<uint32_t>(total);
   split_magic(a.tiles_per_seg, &a.tps_magic, &a.tps_shift);
   const dim3 grid(static_cast<uint32_t>(xcd_grid(total)));
-  hipError_t e;
-  switch (dtype) {
-    case RSX_FLOAT32:
-      e = launch_fold_f32(op, world, rs, vec, a, grid, s);
-      break;
-    case RSX_BFLOAT16:
-      e = launch_fold_bf16(op, world, rs, vec, a, grid, s);
-      break;
-    default:
-      e = launch_fold_i32(op, world, rs, vec, a, grid, s);
-      break;
-  }
-  return hip_status(e);
+  return hip_status(launch_fold_by_type(dtype, op, world, rs, vec, a, grid, s));
 }
 
 // Shared validation of the pointer arrays and enums of the collectives.
@@ -444,19 +487,7 @@ rsx_status_t rsx_fused_all_reduce(const void* const* sendtensors, void* const* r
     if (a.npieces == 0) return RSX_SUCCESS;
     a.tile_start[a.npieces] = static_cast<uint32_t>(tiles);
     const dim3 grid(static_cast<uint32_t>(xcd_grid(tiles)));
-    hipError_t e;
-    switch (dtype) {
-      case RSX_FLOAT32:
-        e = launch_list_f32(op, w, a, grid, stream);
-        break;
-      case RSX_BFLOAT16:
-        e = launch_list_bf16(op, w, a, grid, stream);
-        break;
-      default:
-        e = launch_list_i32(op, w, a, grid, stream);
-        break;
-    }
-    const rsx_status_t st = hip_status(e);
+    const rsx_status_t st = hip_status(launch_list_by_type(dtype, op, w, a, grid, stream));
     reset();
     return st;
   };

@@ -76,9 +76,11 @@ def rng_for(cfg: int, rank: int) -> np.random.Generator:
 def draw(dist: str, rng: np.random.Generator, n: int) -> np.ndarray:
     """Draw ``n`` values of distribution ``dist``.
 
-    Returns float32 for the float distributions, int32 for ``int_2e20`` and
-    ``int_full`` (the whole int32 range, so sums wrap) and uint16 bf16 bit
-    patterns for ``normal_bf16``.
+    Returns float32 for the fp32 distributions, float64 for ``normal_f64``,
+    int32 for ``int_2e20`` and ``int_full``, int64 / uint64 / int8 over their
+    whole range for ``int64_full`` / ``uint64_full`` / ``int8_full`` (so sums
+    and products wrap), and uint16 bit patterns for ``normal_bf16`` (bf16)
+    and ``normal_f16`` (IEEE half).
     """
     if dist == "uniform":
         return rng.uniform(-1.0, 1.0, n).astype(np.float32)
@@ -90,6 +92,17 @@ def draw(dist: str, rng: np.random.Generator, n: int) -> np.ndarray:
         return rng.integers(-(2 ** 20), 2 ** 20, n, dtype=np.int32, endpoint=True)
     if dist == "int_full":
         return rng.integers(-(2 ** 31), 2 ** 31, n, dtype=np.int64).astype(np.int32)
+    if dist == "int64_full":
+        return rng.integers(np.iinfo(np.int64).min, np.iinfo(np.int64).max, n, dtype=np.int64,
+                            endpoint=True)
+    if dist == "uint64_full":
+        return rng.integers(0, np.iinfo(np.uint64).max, n, dtype=np.uint64, endpoint=True)
+    if dist == "int8_full":
+        return rng.integers(-128, 127, n, dtype=np.int8, endpoint=True)
+    if dist == "normal_f64":
+        return rng.standard_normal(n)
+    if dist == "normal_f16":
+        return to_f16_bits_torch(rng.standard_normal(n, dtype=np.float32))
     if dist == "normal_bf16":
         return to_bf16_bits_torch(rng.standard_normal(n, dtype=np.float32))
     raise ValueError(f"unknown distribution {dist!r}")
@@ -100,6 +113,14 @@ def to_bf16_bits_torch(x: np.ndarray) -> np.ndarray:
     import torch
 
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def to_f16_bits_torch(x: np.ndarray) -> np.ndarray:
+    """fp32 -> IEEE half bit patterns through PyTorch's CPU cast (input generation only)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float16)
     return t.view(torch.int16).numpy().view(np.uint16).copy()
 
 

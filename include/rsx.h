@@ -56,14 +56,20 @@ extern "C" {
 typedef enum {
   RSX_FLOAT32 = 0,   /* fp32 in, fp32 fold, fp32 out */
   RSX_BFLOAT16 = 1,  /* bf16 in, widened exactly to fp32, fp32 fold, one RNE rounding to bf16 out */
-  RSX_INT32 = 2      /* int32, two's-complement wrapping sum */
+  RSX_INT32 = 2,     /* int32, two's-complement wrapping sum and product */
+  RSX_FLOAT64 = 3,   /* fp64 in, fp64 fold, fp64 out */
+  RSX_FLOAT16 = 4,   /* IEEE half in, widened exactly to fp32, fp32 fold, one RNE rounding out */
+  RSX_INT64 = 5,     /* int64, wrapping */
+  RSX_UINT64 = 6,    /* uint64, wrapping */
+  RSX_INT8 = 7       /* int8 (the page's char), wrapping */
 } rsx_dtype_t;
 
 typedef enum {
   RSX_SUM = 0,
   RSX_MAX = 1,       /* compare-select fold: a later value replaces the partial only if greater */
   RSX_MIN = 2,       /* compare-select fold: a later value replaces the partial only if smaller */
-  RSX_AVG = 3        /* sum fold, then one division by W in the fold type (int32: toward zero) */
+  RSX_AVG = 3,       /* sum fold, then one division by W in the fold type (signed: toward zero) */
+  RSX_PROD = 4       /* product fold (integers wrap) [NC FuncProd] */
 } rsx_op_t;
 
 typedef enum {

@@ -10,8 +10,14 @@ import sys
 import numpy as np
 import torch
 
-TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32}
-NP_DTYPE = {"f32": np.float32, "bf16": np.uint16, "i32": np.int32}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32,
+               "f64": torch.float64, "f16": torch.float16, "i64": torch.int64,
+               "u64": torch.uint64, "i8": torch.int8}
+NP_DTYPE = {"f32": np.float32, "bf16": np.uint16, "i32": np.int32, "f64": np.float64,
+            "f16": np.uint16, "i64": np.int64, "u64": np.uint64, "i8": np.int8}
+# a signed integer type of the same width, for filling and viewing raw bits
+_BITS_T = {1: torch.int8, 2: torch.int16, 4: torch.int32, 8: torch.int64}
+_BITS_NP = {1: np.uint8, 2: np.uint16, 4: np.uint32, 8: np.uint64}
 
 
 def say(*a):
@@ -19,22 +25,27 @@ def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _width(dtype: str) -> int:
+    return np.dtype(NP_DTYPE[dtype]).itemsize
+
+
 def to_dev(x: np.ndarray, dtype: str, device="cuda:0") -> torch.Tensor:
-    if dtype == "bf16":
-        return torch.from_numpy(np.ascontiguousarray(x, np.uint16).view(np.int16)).to(device).view(torch.bfloat16)
-    return torch.from_numpy(np.ascontiguousarray(x, NP_DTYPE[dtype])).to(device)
+    """Host array (bit patterns for bf16/f16) -> device tensor of the dtype, bit for bit."""
+    w = _width(dtype)
+    raw = np.ascontiguousarray(x, NP_DTYPE[dtype]).view(_BITS_NP[w]).view(np.dtype(f"i{w}"))
+    return torch.from_numpy(raw).to(device).view(TORCH_DTYPE[dtype])
 
 
 def to_host(t: torch.Tensor, dtype: str) -> np.ndarray:
-    if dtype == "bf16":
-        return t.view(torch.int16).cpu().numpy().view(np.uint16)
-    return t.cpu().numpy()
+    """Device tensor -> host array of NP_DTYPE (bit patterns for bf16/f16)."""
+    w = _width(dtype)
+    return t.view(_BITS_T[w]).cpu().numpy().view(NP_DTYPE[dtype])
 
 
 def empty(n: int, dtype: str, device="cuda:0", fill=None) -> torch.Tensor:
     t = torch.empty(n, dtype=TORCH_DTYPE[dtype], device=device)
     if fill is not None:
-        t.view(torch.int16 if dtype == "bf16" else t.dtype).fill_(fill)
+        t.view(_BITS_T[_width(dtype)]).fill_(fill)
     return t
 
 
@@ -45,19 +56,22 @@ def _bf16_ordered(bits: np.ndarray) -> np.ndarray:
 
 
 def assert_parity(got: np.ndarray, want: np.ndarray, dtype: str, what: str = "") -> dict:
-    """fp32 / int32: bit-exact.  bf16: at most 1 bf16 ulp apart, NaN where NaN.
+    """Every type but bf16: bit-exact.  bf16: at most 1 bf16 ulp apart.  NaN where NaN.
 
     Returns {"n": elements, "exact": bit-identical elements, "max_ulp": ...}.
     """
     got = np.asarray(got)
     want = np.asarray(want)
     assert got.shape == want.shape, (what, got.shape, want.shape)
-    if dtype in ("f32", "i32"):
-        g = got.view(np.uint32)
-        w = want.view(np.uint32)
+    if dtype != "bf16":
+        bits = _BITS_NP[_width(dtype)]
+        g = got.view(bits)
+        w = want.view(bits)
         bad = np.flatnonzero(g != w)
-        if dtype == "f32":  # NaN payloads are not pinned: any NaN matches any NaN
-            bad = bad[~(np.isnan(got[bad]) & np.isnan(want[bad]))]
+        if dtype in ("f32", "f64", "f16"):  # NaN payloads are not pinned: any NaN matches any NaN
+            gf = got.view(np.float16) if dtype == "f16" else got
+            wf = want.view(np.float16) if dtype == "f16" else want
+            bad = bad[~(np.isnan(gf[bad]) & np.isnan(wf[bad]))]
         assert bad.size == 0, (
             f"{what}: {bad.size} of {got.size} differ; first at {bad[:5].tolist()}: "
             f"got {got[bad[:5]].tolist()} want {want[bad[:5]].tolist()}")

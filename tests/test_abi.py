@@ -57,8 +57,11 @@ def test_exports_every_declared_symbol(lib):
 def test_enum_and_macro_values_match_binding(lib):
     text = open(HEADER).read()
     for name, val in [("RSX_FLOAT32", L.RSX_FLOAT32), ("RSX_BFLOAT16", L.RSX_BFLOAT16),
-                      ("RSX_INT32", L.RSX_INT32), ("RSX_SUM", L.RSX_SUM), ("RSX_MAX", L.RSX_MAX),
-                      ("RSX_MIN", L.RSX_MIN), ("RSX_AVG", L.RSX_AVG),
+                      ("RSX_INT32", L.RSX_INT32), ("RSX_FLOAT64", L.RSX_FLOAT64),
+                      ("RSX_FLOAT16", L.RSX_FLOAT16), ("RSX_INT64", L.RSX_INT64),
+                      ("RSX_UINT64", L.RSX_UINT64), ("RSX_INT8", L.RSX_INT8),
+                      ("RSX_SUM", L.RSX_SUM), ("RSX_MAX", L.RSX_MAX),
+                      ("RSX_MIN", L.RSX_MIN), ("RSX_AVG", L.RSX_AVG), ("RSX_PROD", L.RSX_PROD),
                       ("RSX_ALGO_RING", L.RSX_ALGO_RING), ("RSX_ALGO_NAIVE", L.RSX_ALGO_NAIVE),
                       ("RSX_ALGO_AUTO", L.RSX_ALGO_AUTO)]:
         assert re.search(rf"\b{name}\s*=\s*{val}\b", text), name
@@ -71,7 +74,7 @@ def test_enum_and_macro_values_match_binding(lib):
 
 
 def test_dtype_size_and_status_strings(lib):
-    assert [lib.rsx_dtype_size(d) for d in (0, 1, 2, 3, -1)] == [4, 2, 4, 0, 0]
+    assert [lib.rsx_dtype_size(d) for d in (0, 1, 2, 3, 4, 5, 6, 7, 8, -1)] == [4, 2, 4, 8, 2, 8, 8, 1, 0, 0]
     for code in range(7):
         assert lib.rsx_status_string(code)
     assert lib.rsx_status_string(99) == b"unknown status"
@@ -130,12 +133,12 @@ def test_null_arrays_and_rank_range(lib):
 @fake_ptrs
 def test_bad_enums(lib):
     s, r = [A, A + MB], [A + 2 * MB, A + 3 * MB]
-    assert _rs(lib, s, r, 2, 4, dt=3) == 2
+    assert _rs(lib, s, r, 2, 4, dt=8) == 2
     assert _rs(lib, s, r, 2, 4, dt=-1) == 2
-    assert _rs(lib, s, r, 2, 4, op=4) == 3
+    assert _rs(lib, s, r, 2, 4, op=5) == 3
     assert _ar(lib, s, r, 2, 4, op=-1) == 3
     assert _ar(lib, s, r, 2, 4, algo=3) == 1
-    assert _ag(lib, s, r, 2, 4, dt=5) == 2
+    assert _ag(lib, s, r, 2, 4, dt=9) == 2
     # type is checked before op, as the page's dispatch switches on type first
     assert _rs(lib, s, r, 2, 4, dt=9, op=9) == 2
 
@@ -210,7 +213,7 @@ def test_fuse_validation(lib):
     ts = _arr([A, None, A + MB])
     assert lib.rsx_fuse_pack(ts, None, 3, A + 4 * MB, 0, None) == 1       # counts missing
     assert lib.rsx_fuse_pack(ts, counts, -1, A + 4 * MB, 0, None) == 1
-    assert lib.rsx_fuse_pack(ts, counts, 3, A + 4 * MB, 7, None) == 2     # bad dtype
+    assert lib.rsx_fuse_pack(ts, counts, 3, A + 4 * MB, 9, None) == 2     # bad dtype
     assert lib.rsx_fuse_pack(ts, counts, 3, None, 0, None) == 1           # no fused buffer
     assert lib.rsx_fuse_pack(ts, counts, 3, A + 36, 0, None) == 5         # fused overlaps t0
     assert lib.rsx_fuse_unpack(A + MB - 8, ts, counts, 3, 0, None) == 5   # fused overlaps t2
@@ -242,7 +245,7 @@ def test_fused_all_reduce_validation(lib):
     r = [A + 16 * MB + i * MB for i in range(6)]
     assert lib.rsx_fused_all_reduce(_arr(s), _arr(r), None, 3, 2, 0, 0, 0, None) == 1   # counts
     assert _far(lib, s, r, c, 0) == 1 and _far(lib, s, r, c, 17) == 1
-    assert _far(lib, s, r, c, 2, dt=3) == 2
+    assert _far(lib, s, r, c, 2, dt=8) == 2
     assert _far(lib, s, r, c, 2, op=7) == 3
     assert _far(lib, s, r, c, 2, algo=9) == 1
     assert _far(lib, s, r, [0, 0, 0], 2) == 0                      # nothing to do, no launch
@@ -295,14 +298,14 @@ def test_fusion_plan_matches_oracle(lib):
     import numpy as np
 
     import oracle
-    es = {0: 4, 1: 2, 2: 4}
+    es = {0: 4, 1: 2, 2: 4, 3: 8, 4: 2, 5: 8, 6: 8, 7: 1}
     rng = np.random.default_rng(8)
     for trial in range(400):
         n = int(rng.integers(0, 40))
         counts = [int(c) for c in rng.integers(0, 5000, n)]
         if trial % 5 == 0:
             counts = [int(c) for c in rng.integers(0, 3, n)]
-        dts = [int(d) for d in rng.choice([0, 0, 0, 1, 2], n)]
+        dts = [int(d) for d in rng.choice([0, 0, 0, 1, 2, 3, 7], n)]
         th = int(rng.choice([0, 1, 100, 4000, 16000, 64 * 2 ** 20]))
         got = _plan(lib, counts, dts, th)
         want = oracle.fusion_groups([c * es[d] for c, d in zip(counts, dts)], dts, th)
@@ -313,7 +316,7 @@ def test_fusion_plan_validation(lib):
     assert lib.rsx_fusion_plan(None, None, 0, 10, None) == 0
     assert lib.rsx_fusion_plan(None, None, -1, 10, None) == -1
     ends = (ctypes.c_int * 2)()
-    assert lib.rsx_fusion_plan(L.size_array([1, 2]), (ctypes.c_int * 2)(0, 7), 2, 10, ends) == -1
+    assert lib.rsx_fusion_plan(L.size_array([1, 2]), (ctypes.c_int * 2)(0, 9), 2, 10, ends) == -1
     assert lib.rsx_fusion_plan(L.size_array([1, 2]), None, 2, 10, ends) == -1
     # a tensor whose byte count overflows is a group of its own
     assert _plan(lib, [2 ** 63, 1, 1], [0, 0, 0], 2 ** 40) == [(0, 1), (1, 3)]

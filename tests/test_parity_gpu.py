@@ -16,8 +16,10 @@ from parity_util import assert_parity, empty, say, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
-DIST = {"f32": "normal", "bf16": "normal_bf16", "i32": "int_full"}
-VL = {"f32": 4, "bf16": 8, "i32": 4}
+DIST = {"f32": "normal", "bf16": "normal_bf16", "i32": "int_full", "f64": "normal_f64",
+        "f16": "normal_f16", "i64": "int64_full", "u64": "uint64_full", "i8": "int8_full"}
+VL = {"f32": 4, "bf16": 8, "i32": 4, "f64": 2, "f16": 8, "i64": 2, "u64": 2, "i8": 16}
+ALL_DTYPES = list(DIST)
 
 
 def units(w):  # dwordx4 per lane per source in the fold kernels
@@ -48,13 +50,13 @@ def run_ar(xs, dtype, op, algo="ring", in_place=False):
     return [to_host(o, dtype) for o in (dev if in_place else out)]
 
 
-OPS = ["sum", "max", "min", "avg"]
+OPS = ["sum", "max", "min", "avg", "prod"]
 WORLDS = [1, 2, 3, 4, 5, 8, 13, 16]
 
 
 # ------------------------------------------------------- reduce-scatter ----
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("dtype", ALL_DTYPES)
 @pytest.mark.parametrize("op", OPS)
 @pytest.mark.parametrize("w", WORLDS)
 @pytest.mark.parametrize("aligned", [True, False])
@@ -69,7 +71,7 @@ def test_reduce_scatter(w, op, dtype, aligned):
         assert_parity(got[k], want[k], dtype, f"block {k}")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("dtype", ALL_DTYPES)
 @pytest.mark.parametrize("op", OPS)
 @pytest.mark.parametrize("w", WORLDS)
 @pytest.mark.parametrize("algo", ["ring", "naive"])
@@ -147,7 +149,7 @@ def test_bf16_specials_and_rounding_ties():
 
 # ----------------------------------------------------------- in place -------
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("dtype", ALL_DTYPES)
 @pytest.mark.parametrize("w", [1, 2, 4, 8])
 def test_in_place(w, dtype):
     te = tile_elems(w, dtype)
@@ -241,7 +243,7 @@ def test_graph_capture_replays():
 
 # ---------------------------------------------------------- all-gather ------
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f64", "i8"])
 @pytest.mark.parametrize("w", [1, 2, 3, 8, 16])
 @pytest.mark.parametrize("n", [1, 5, 8, 4096 + 8, 4096 + 3])
 def test_all_gather(w, n, dtype):
@@ -271,7 +273,7 @@ def test_all_gather_in_place_and_composition():
 
 # --------------------------------------------------------------- fusion -----
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f64", "i8", "f16"])
 def test_fused_pack_allreduce_unpack(dtype):
     w = 4
     sizes = wl.fused_sizes(count=70, lo=1, hi=70_000)
@@ -303,7 +305,7 @@ def _list_case(seed, w, sizes, dtype):
 LIST_SIZES = [0, 1, 3, 4096 + 5, 7, 0, 20_000, 1, 1024, 33, 65_536 + 3, 2, 9_999]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("dtype", ALL_DTYPES)
 @pytest.mark.parametrize("op", OPS)
 @pytest.mark.parametrize("w", [1, 2, 3, 4, 8, 16])
 @pytest.mark.parametrize("algo", ["ring", "naive"])
@@ -436,9 +438,9 @@ def test_errors_with_real_tensors():
     with pytest.raises(ValueError):
         rsx.reduce_scatter(x, [torch.zeros(15, device="cuda:0")] * 4)
     with pytest.raises(ValueError):
-        rsx.all_reduce([torch.zeros(8, dtype=torch.float64, device="cuda:0")] * 2)
+        rsx.all_reduce([torch.zeros(8, dtype=torch.int16, device="cuda:0")] * 2)
     with pytest.raises(ValueError):
-        rsx.all_reduce(x, op="prod")
+        rsx.all_reduce(x, op="xor")
     with pytest.raises(ValueError):
         rsx.all_reduce([torch.zeros(8, device="cuda:0")] * 17)
     with pytest.raises(ValueError):
