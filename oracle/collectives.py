@@ -27,6 +27,10 @@ Sources (web pages this follows):
   fused buffer.
 * [MX] "Add scatter reduce for JACCL#3901": a naive all-reduce is kept for
   messages of at most 32 KB.
+* [SG] ``synchHalf`` / ``fusedSynchHalf``: fp32 gradients are converted to
+  half (``float2half``), all-reduced as ``ncclHalf``, and converted back
+  (``half2float``) into the fp32 tensors: fp16 as the wire format of an fp32
+  all-reduce (dtype ``"f32h"`` here).
 
 Precision.  The pages fix it: the NCCL kernel reduces in the element type
 (``FuncSum<float>`` on ``float`` data), so fp32 and fp64 are folded with IEEE
@@ -50,6 +54,9 @@ Readings where the pages are silent (each listed again in the design doc):
 * ``prod`` multiplies in the accumulation type (integers wrap);
 * fp16 (the page's ``half``, whose functor is off-page) folds in fp32 and is
   rounded once, like bf16;
+* ``"f32h"`` (fp32 data, half on the wire): each fp32 input is rounded to
+  half and widened back, the half values are folded as fp16 is, and the half
+  result is widened to fp32 for the output;
 * bf16 rounding: round-to-nearest-even on the fp32 bits, NaN -> quiet NaN
   with the sign kept (``sign | 0x7FC0``), overflow to +-inf as RNE gives;
 * the naive all-reduce folds in rank order 0..W-1;
@@ -60,11 +67,12 @@ from __future__ import annotations
 import numpy as np
 
 OPS = ("sum", "prod", "max", "min", "avg")
-DTYPES = ("f32", "bf16", "i32", "f64", "f16", "i64", "u64", "i8")
+DTYPES = ("f32", "bf16", "i32", "f64", "f16", "i64", "u64", "i8", "f32h")
 
 # storage type of each dtype (bf16 and f16 as their 16-bit patterns)
 STORAGE = {"f32": np.float32, "bf16": np.uint16, "i32": np.int32, "f64": np.float64,
-           "f16": np.uint16, "i64": np.int64, "u64": np.uint64, "i8": np.int8}
+           "f16": np.uint16, "i64": np.int64, "u64": np.uint64, "i8": np.int8,
+           "f32h": np.float32}
 # integer types and the unsigned type of the same width (wrap-around arithmetic)
 _UNSIGNED = {np.dtype(np.int8): np.uint8, np.dtype(np.int32): np.uint32,
              np.dtype(np.int64): np.uint64, np.dtype(np.uint64): np.uint64}
@@ -150,11 +158,14 @@ def f32_to_f16(x: np.ndarray) -> np.ndarray:
 
 
 def _widen(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Storage -> accumulation type: bf16 and f16 bits -> fp32; every other type as is."""
+    """Storage -> accumulation type: bf16 and f16 bits -> fp32; fp32 through half
+    (``"f32h"``: ``float2half`` on the sender) -> fp32; every other type as is."""
     if dtype == "bf16":
         return bf16_to_f32(x)
     if dtype == "f16":
         return f16_to_f32(x)
+    if dtype == "f32h":
+        return f16_to_f32(f32_to_f16(x))
     if dtype in STORAGE:
         return np.asarray(x, dtype=STORAGE[dtype])
     raise ValueError(dtype)
@@ -195,6 +206,8 @@ def _finish(op: str, acc: np.ndarray, world: int, dtype: str) -> np.ndarray:
         return f32_to_bf16(acc)
     if dtype == "f16":
         return f32_to_f16(acc)
+    if dtype == "f32h":                     # the half result, then half2float
+        return f16_to_f32(f32_to_f16(acc))
     return acc
 
 
@@ -270,6 +283,17 @@ def bucketed_all_reduce(inputs, bucket: int, op: str = "sum", dtype: str = "f32"
             outs[r][start:stop] = part[r]
         start = stop
     return outs
+
+
+def half_wire_all_reduce(inputs, op: str = "sum", algo: str = "ring") -> list[np.ndarray]:
+    """fp32 all-reduce with half on the wire [SG ``synchHalf``].
+
+    Each rank converts its fp32 data to half, the half buffers are all-reduced
+    as fp16, and each rank converts the half result back to fp32.
+    """
+    halves = [f32_to_f16(x) for x in inputs]
+    red = all_reduce(halves, op, "f16") if algo == "ring" else naive_all_reduce(halves, op, "f16")
+    return [f16_to_f32(h) for h in red]
 
 
 # ------------------------------------------------------------------ fusion ---

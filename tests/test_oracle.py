@@ -476,3 +476,44 @@ def test_f16_accumulates_in_fp32():
     xs = [np.array([0x3C00], np.uint16), np.array([0x1000], np.uint16), np.array([0x1000], np.uint16)]
     assert oracle.f16_to_f32(np.array([0x1000], np.uint16))[0] == 2.0 ** -11
     assert oracle.naive_all_reduce(xs, "sum", "f16")[0][0] == 0x3C01
+
+
+def test_half_wire_rounds_inputs_and_result_to_half():
+    f = np.float32
+    # inputs: 1 + 2^-11 is a half tie and goes to 1.0 before the fold; 2^-11 and
+    # 3 are exact halves.  fp32 fold in rank order: 1 + 2^-11 + 3 = 4 + 2^-11,
+    # which rounds to 4.0 in half (spacing 2^-8 near 4); the output is fp32 4.0.
+    xs = [np.array([1 + 2 ** -11], f), np.array([2 ** -11], f), np.array([3.0], f)]
+    out = oracle.naive_all_reduce(xs, "sum", "f32h")
+    assert out[0].dtype == np.float32 and out[0][0] == f(4.0)
+    # without the wire rounding the fp32 sum would be 4 + 2^-10
+    assert oracle.naive_all_reduce(xs, "sum", "f32")[0][0] == f(4 + 2 ** -10)
+    # beyond half's range: 70000 is inf on the wire
+    big = [np.array([70000.0, -70000.0], f), np.zeros(2, f)]
+    assert list(oracle.naive_all_reduce(big, "sum", "f32h")[0]) == [np.inf, -np.inf]
+    # every output is a half value widened: it survives another round trip unchanged
+    rng = np.random.default_rng(14)
+    ys = [rng.standard_normal(96).astype(f) for _ in range(4)]
+    for o in oracle.all_reduce(ys, "sum", "f32h"):
+        assert np.array_equal(oracle.f16_to_f32(oracle.f32_to_f16(o)), o)
+
+
+@pytest.mark.parametrize("op", ["sum", "max", "avg"])
+def test_half_wire_small_integers_exact(op):
+    # small integers are exact in half and in the fp32 fold
+    rng = np.random.default_rng(15)
+    xi = [rng.integers(-200, 200, 48) for _ in range(4)]
+    got = oracle.all_reduce([x.astype(np.float32) for x in xi], op, "f32h")[0]
+    st = np.stack(xi).astype(np.float64)
+    want = {"sum": st.sum(0), "max": st.max(0), "avg": st.sum(0) / 4}[op]
+    want = want.astype(np.float16).astype(np.float32)   # avg: a quarter step may round
+    assert np.array_equal(got, want)
+
+
+def test_half_wire_is_singa_float2half_allreduce_half2float():
+    rng = np.random.default_rng(16)
+    xs = [(rng.standard_normal(77) * 10).astype(np.float32) for _ in range(5)]
+    lit = oracle.half_wire_all_reduce(xs, "sum")
+    assert all(np.array_equal(a, b) for a, b in zip(lit, oracle.all_reduce(xs, "sum", "f32h")))
+    lit = oracle.half_wire_all_reduce(xs, "max", "naive")
+    assert all(np.array_equal(a, b) for a, b in zip(lit, oracle.naive_all_reduce(xs, "max", "f32h")))
