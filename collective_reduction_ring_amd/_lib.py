@@ -15,6 +15,7 @@ LIB_PATH = os.environ.get("RSX_LIB", os.path.join(PKG, "librsx.so"))
 
 RSX_FLOAT32, RSX_BFLOAT16, RSX_INT32 = 0, 1, 2
 RSX_FLOAT64, RSX_FLOAT16, RSX_INT64, RSX_UINT64, RSX_INT8 = 3, 4, 5, 6, 7
+RSX_FLOAT32_HALF_WIRE = 8
 RSX_SUM, RSX_MAX, RSX_MIN, RSX_AVG, RSX_PROD = 0, 1, 2, 3, 4
 RSX_ALGO_RING, RSX_ALGO_NAIVE, RSX_ALGO_AUTO = 0, 1, 2
 RSX_MAX_RANKS = 16

@@ -61,7 +61,18 @@ def _check(ts: Sequence[torch.Tensor], numel: int, what: str, dtype=None, device
             raise ValueError(f"{what}[{i}] has {t.numel()} elements, expected {numel}")
 
 
-def _dtype_code(t: torch.Tensor) -> int:
+WIRES = ("f16",)
+
+
+def _dtype_code(t: torch.Tensor, wire: str | None = None) -> int:
+    """Library dtype of ``t``; ``wire="f16"`` selects fp32 data with half on the
+    wire (SINGA synchHalf: float2half, half all-reduce, half2float)."""
+    if wire is not None:
+        if wire not in WIRES:
+            raise ValueError(f"unknown wire format {wire!r}; one of {WIRES}")
+        if t.dtype != torch.float32:
+            raise ValueError(f"the f16 wire format is for float32 tensors, got {t.dtype}")
+        return L.RSX_FLOAT32_HALF_WIRE
     try:
         return DTYPES[t.dtype]
     except KeyError:
@@ -88,7 +99,7 @@ class ReduceScatter:
     ``inputs[r]`` has W*recvcount elements, ``outputs[k]`` recvcount.
     """
 
-    def __init__(self, inputs, outputs, op: str = "sum"):
+    def __init__(self, inputs, outputs, op: str = "sum", wire: str | None = None):
         w = _ranks(inputs)
         if len(outputs) != w:
             raise ValueError("need one output per rank")
@@ -99,7 +110,7 @@ class ReduceScatter:
         self.device = dev
         self.args = (L.ptr_array([t.data_ptr() for t in inputs]),
                      L.ptr_array([t.data_ptr() for t in outputs]),
-                     w, recvcount, _dtype_code(inputs[0]), _op_code(op))
+                     w, recvcount, _dtype_code(inputs[0], wire), _op_code(op))
         self.fn = L.lib().rsx_reduce_scatter
         self.keep = (list(inputs), list(outputs))
 
@@ -110,7 +121,8 @@ class ReduceScatter:
 class AllReduce:
     """A prepared all-reduce (``algo`` ring / naive / auto); every tensor has ``count`` elements."""
 
-    def __init__(self, inputs, outputs=None, op: str = "sum", algo: str = "ring"):
+    def __init__(self, inputs, outputs=None, op: str = "sum", algo: str = "ring",
+                 wire: str | None = None):
         w = _ranks(inputs)
         outputs = inputs if outputs is None else outputs
         if len(outputs) != w:
@@ -124,7 +136,7 @@ class AllReduce:
         self.device = dev
         self.args = (L.ptr_array([t.data_ptr() for t in inputs]),
                      L.ptr_array([t.data_ptr() for t in outputs]),
-                     w, count, _dtype_code(inputs[0]), _op_code(op), ALGOS[algo])
+                     w, count, _dtype_code(inputs[0], wire), _op_code(op), ALGOS[algo])
         self.fn = L.lib().rsx_all_reduce
         self.keep = (list(inputs), list(outputs))
 
@@ -132,9 +144,9 @@ class AllReduce:
         _launch(self, "rsx_all_reduce", stream)
 
 
-def reduce_scatter(inputs, outputs, op: str = "sum", stream=None) -> None:
+def reduce_scatter(inputs, outputs, op: str = "sum", stream=None, wire: str | None = None) -> None:
     """Reduce-scatter ``inputs`` (W tensors of W*n) into ``outputs`` (W tensors of n)."""
-    ReduceScatter(inputs, outputs, op)(stream)
+    ReduceScatter(inputs, outputs, op, wire)(stream)
 
 
 def all_gather(inputs, outputs, stream=None) -> None:
@@ -153,13 +165,15 @@ def all_gather(inputs, outputs, stream=None) -> None:
     L.check("rsx_all_gather", st)
 
 
-def all_reduce(inputs, outputs=None, op: str = "sum", algo: str = "ring", stream=None) -> None:
-    """All-reduce; ``outputs=None`` reduces in place."""
-    AllReduce(inputs, outputs, op, algo)(stream)
+def all_reduce(inputs, outputs=None, op: str = "sum", algo: str = "ring", stream=None,
+               wire: str | None = None) -> None:
+    """All-reduce; ``outputs=None`` reduces in place.  ``wire="f16"``: float32
+    tensors reduced with half as the wire format (SINGA synchHalf)."""
+    AllReduce(inputs, outputs, op, algo, wire)(stream)
 
 
 def all_reduce_bucketed(inputs, outputs=None, bucket_elems: int = 13_107_200, op: str = "sum",
-                        algo: str = "ring", stream=None) -> None:
+                        algo: str = "ring", stream=None, wire: str | None = None) -> None:
     """All-reduce consecutive buckets of ``bucket_elems`` elements, one launch per bucket,
     in order on one stream ("Distributed primitives", bucketed ring all-reduce).
 
@@ -171,7 +185,8 @@ def all_reduce_bucketed(inputs, outputs=None, bucket_elems: int = 13_107_200, op
         raise ValueError("bucket_elems must be positive")
     for start in range(0, n, bucket_elems):
         stop = min(start + bucket_elems, n)
-        AllReduce([t[start:stop] for t in inputs], [t[start:stop] for t in outputs], op, algo)(stream)
+        AllReduce([t[start:stop] for t in inputs], [t[start:stop] for t in outputs], op, algo,
+                  wire)(stream)
 
 
 class _FuseCopy:
@@ -221,10 +236,10 @@ class FusedAllReduce:
     back into the input tensors."""
 
     def __init__(self, tensors_per_rank, fused_per_rank, outputs_per_rank=None, op: str = "sum",
-                 algo: str = "ring"):
+                 algo: str = "ring", wire: str | None = None):
         outputs_per_rank = tensors_per_rank if outputs_per_rank is None else outputs_per_rank
         self.packs = [FusePack(ts, f) for ts, f in zip(tensors_per_rank, fused_per_rank)]
-        self.reduce = AllReduce(list(fused_per_rank), None, op, algo)
+        self.reduce = AllReduce(list(fused_per_rank), None, op, algo, wire)
         self.unpacks = [FuseUnpack(f, ts) for f, ts in zip(fused_per_rank, outputs_per_rank)]
 
     def __call__(self, stream=None) -> None:
@@ -246,7 +261,8 @@ class TensorFusionAllReduce:
     themselves are read and written.  ``outputs_per_rank=None`` is in place.
     """
 
-    def __init__(self, tensors_per_rank, outputs_per_rank=None, op: str = "sum", algo: str = "ring"):
+    def __init__(self, tensors_per_rank, outputs_per_rank=None, op: str = "sum", algo: str = "ring",
+                 wire: str | None = None):
         w = _ranks(tensors_per_rank)
         outputs_per_rank = tensors_per_rank if outputs_per_rank is None else outputs_per_rank
         if len(outputs_per_rank) != w:
@@ -267,7 +283,7 @@ class TensorFusionAllReduce:
         self.device = dev
         self.args = (L.ptr_array([t.data_ptr() for ts in tensors_per_rank for t in ts]),
                      L.ptr_array([t.data_ptr() for ts in outputs_per_rank for t in ts]),
-                     L.size_array(counts), len(counts), w, _dtype_code(first), _op_code(op),
+                     L.size_array(counts), len(counts), w, _dtype_code(first, wire), _op_code(op),
                      ALGOS[algo])
         self.fn = L.lib().rsx_fused_all_reduce
         self.keep = (tensors_per_rank, outputs_per_rank)
@@ -306,11 +322,11 @@ class GroupedAllReduce:
     fusion buffer would be (one ``rsx_fused_all_reduce`` per group)."""
 
     def __init__(self, tensors_per_rank, outputs_per_rank=None, op: str = "sum", algo: str = "ring",
-                 threshold: int | None = None):
+                 threshold: int | None = None, wire: str | None = None):
         outputs_per_rank = tensors_per_rank if outputs_per_rank is None else outputs_per_rank
         self.groups = fusion_groups(tensors_per_rank[0], threshold)
         self.plans = [TensorFusionAllReduce([ts[lo:hi] for ts in tensors_per_rank],
-                                            [os_[lo:hi] for os_ in outputs_per_rank], op, algo)
+                                            [os_[lo:hi] for os_ in outputs_per_rank], op, algo, wire)
                       for lo, hi in self.groups]
 
     def __call__(self, stream=None) -> None:
@@ -329,9 +345,10 @@ def fuse_unpack(fused: torch.Tensor, tensors, stream=None) -> None:
 
 
 def fused_all_reduce(tensors_per_rank, fused_per_rank, outputs_per_rank=None, op: str = "sum",
-                     algo: str = "ring", stream=None) -> None:
-    """pack -> in-place all-reduce of the fusion buffers -> unpack."""
-    FusedAllReduce(tensors_per_rank, fused_per_rank, outputs_per_rank, op, algo)(stream)
+                     algo: str = "ring", stream=None, wire: str | None = None) -> None:
+    """pack -> in-place all-reduce of the fusion buffers -> unpack (SINGA fusedSynch;
+    with ``wire="f16"``, fusedSynchHalf)."""
+    FusedAllReduce(tensors_per_rank, fused_per_rank, outputs_per_rank, op, algo, wire)(stream)
 
 
 def segment_begin(count: int, nranks: int, k: int) -> int:

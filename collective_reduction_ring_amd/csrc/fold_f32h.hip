@@ -1,0 +1,15 @@
+// Fold kernels instantiated for one element type (see fold_impl.h).
+#include "fold_impl.h"
+
+namespace rsx {
+
+hipError_t launch_fold_f32h(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid,
+                           hipStream_t s) {
+  return launch_fold<F32HT>(op, world, rs, vec, a, grid, s);
+}
+
+hipError_t launch_list_f32h(int op, int world, const ListArgs& a, dim3 grid, hipStream_t s) {
+  return launch_list<F32HT>(op, world, a, grid, s);
+}
+
+}  // namespace rsx

@@ -68,6 +68,13 @@ struct I8T {
   using A = int8_t;
   static constexpr int kVL = 16;
 };
+// fp32 data with IEEE half as the wire format (Apache SINGA communicator.cc,
+// synchHalf / fusedSynchHalf: float2half, a half all-reduce, half2float).
+struct F32HT {
+  using S = float;
+  using A = float;
+  static constexpr int kVL = 4;
+};
 
 // bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 bits.
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -190,6 +197,31 @@ struct Elem<F16T> {
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = narrow(a[2 * i]) | (static_cast<uint32_t>(narrow(a[2 * i + 1])) << 16);
     return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+
+// fp32 through half: every input is rounded to half (round to nearest even)
+// and widened back before it enters the fold, as the sender's float2half
+// does; the fold is the fp16 one (fp32 arithmetic, rounded once); the result
+// is rounded to half and widened for the fp32 output, as half2float does.
+template <>
+struct Elem<F32HT> {
+  __device__ static float widen(float x) { return static_cast<float>(static_cast<_Float16>(x)); }
+  // The same barrier as the fp16 narrow: the fp32 fold result is rounded on
+  // its own, never merged with the last add or multiply into a mixed FMA.
+  __device__ static float narrow(float a) {
+    asm volatile("" : "+v"(a));
+    return static_cast<float>(static_cast<_Float16>(a));
+  }
+  __device__ static void unpack(const uint4& v, float (&a)[4]) {
+    a[0] = widen(__uint_as_float(v.x));
+    a[1] = widen(__uint_as_float(v.y));
+    a[2] = widen(__uint_as_float(v.z));
+    a[3] = widen(__uint_as_float(v.w));
+  }
+  __device__ static uint4 pack(const float (&a)[4]) {
+    return make_uint4(__float_as_uint(narrow(a[0])), __float_as_uint(narrow(a[1])),
+                      __float_as_uint(narrow(a[2])), __float_as_uint(narrow(a[3])));
   }
 };
 

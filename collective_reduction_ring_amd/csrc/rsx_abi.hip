@@ -27,6 +27,7 @@ size_t esize_of(int dtype) {
   switch (dtype) {
     case RSX_FLOAT32:
     case RSX_INT32:
+    case RSX_FLOAT32_HALF_WIRE:
       return 4;
     case RSX_BFLOAT16:
     case RSX_FLOAT16:
@@ -64,6 +65,8 @@ hipError_t launch_fold_by_type(int dtype, int op, int world, bool rs, bool vec, 
       return launch_fold_u64(op, world, rs, vec, a, grid, s);
     case RSX_INT8:
       return launch_fold_i8(op, world, rs, vec, a, grid, s);
+    case RSX_FLOAT32_HALF_WIRE:
+      return launch_fold_f32h(op, world, rs, vec, a, grid, s);
     default:
       return hipErrorInvalidValue;
   }
@@ -88,6 +91,8 @@ hipError_t launch_list_by_type(int dtype, int op, int world, const ListArgs& a, 
       return launch_list_u64(op, world, a, grid, s);
     case RSX_INT8:
       return launch_list_i8(op, world, a, grid, s);
+    case RSX_FLOAT32_HALF_WIRE:
+      return launch_list_f32h(op, world, a, grid, s);
     default:
       return hipErrorInvalidValue;
   }
@@ -296,7 +301,8 @@ rsx_status_t rsx_reduce_scatter(const void* const* sendbufs, void* const* recvbu
     for (int r = 0; r < nranks; ++r)
       if (overlap(out[k], in[r])) return RSX_ERR_ALIASING;
   }
-  if (nranks == 1 && in_place_all) return RSX_SUCCESS;
+  // One rank in place: nothing to do, except that a half wire still rounds.
+  if (nranks == 1 && in_place_all && dtype != RSX_FLOAT32_HALF_WIRE) return RSX_SUCCESS;
 
   bool vec = (seg_bytes % kVecBytes) == 0;
   for (int r = 0; r < nranks; ++r) vec = vec && aligned16(sendbufs[r]) && aligned16(recvbufs[r]);
@@ -320,6 +326,8 @@ rsx_status_t rsx_all_gather(const void* const* sendbufs, void* const* recvbufs, 
                             size_t sendcount, rsx_dtype_t dtype, hipStream_t stream) {
   rsx_status_t st = check_common(sendbufs, recvbufs, nranks, dtype);
   if (st != RSX_SUCCESS) return st;
+  // A gather reduces nothing: the half wire format applies to reductions only.
+  if (dtype == RSX_FLOAT32_HALF_WIRE) return RSX_ERR_INVALID_TYPE;
   if (sendcount == 0) return RSX_SUCCESS;
   if ((st = check_device_ptrs(sendbufs, recvbufs, nranks)) != RSX_SUCCESS) return st;
   const size_t es = esize_of(dtype);
@@ -392,7 +400,8 @@ rsx_status_t rsx_all_reduce(const void* const* sendbufs, void* const* recvbufs, 
     for (int j = 0; j < nranks; ++j)
       if (overlap(out[r], in[j]) && !same(out[r], in[j])) return RSX_ERR_ALIASING;
   }
-  if (nranks == 1 && in_place_all) return RSX_SUCCESS;
+  // One rank in place: nothing to do, except that a half wire still rounds.
+  if (nranks == 1 && in_place_all && dtype != RSX_FLOAT32_HALF_WIRE) return RSX_SUCCESS;
 
   const bool naive = algo == RSX_ALGO_NAIVE || (algo == RSX_ALGO_AUTO && bytes <= RSX_NAIVE_MAX_BYTES);
   bool vec = true;
@@ -464,7 +473,7 @@ rsx_status_t rsx_fused_all_reduce(const void* const* sendtensors, void* const* r
     }
   }
   if (!list_aliasing_ok(sends, recvs)) return RSX_ERR_ALIASING;
-  if (w == 1 && in_place_all) return RSX_SUCCESS;
+  if (w == 1 && in_place_all && dtype != RSX_FLOAT32_HALF_WIRE) return RSX_SUCCESS;
 
   const bool naive = algo == RSX_ALGO_NAIVE || (algo == RSX_ALGO_AUTO && total_bytes <= RSX_NAIVE_MAX_BYTES);
   const uint64_t seg = naive ? total : (total + w - 1) / w;

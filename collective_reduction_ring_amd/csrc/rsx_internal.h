@@ -151,6 +151,8 @@ hipError_t launch_fold_u64(int op, int world, bool rs, bool vec, const FoldArgs&
                            hipStream_t s);
 hipError_t launch_fold_i8(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid,
                            hipStream_t s);
+hipError_t launch_fold_f32h(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid,
+                            hipStream_t s);
 hipError_t launch_list_f32(int op, int world, const ListArgs& a, dim3 grid, hipStream_t s);
 hipError_t launch_list_bf16(int op, int world, const ListArgs& a, dim3 grid, hipStream_t s);
 hipError_t launch_list_i32(int op, int world, const ListArgs& a, dim3 grid, hipStream_t s);
@@ -159,6 +161,7 @@ hipError_t launch_list_f16(int op, int world, const ListArgs& a, dim3 grid, hipS
 hipError_t launch_list_i64(int op, int world, const ListArgs& a, dim3 grid, hipStream_t s);
 hipError_t launch_list_u64(int op, int world, const ListArgs& a, dim3 grid, hipStream_t s);
 hipError_t launch_list_i8(int op, int world, const ListArgs& a, dim3 grid, hipStream_t s);
+hipError_t launch_list_f32h(int op, int world, const ListArgs& a, dim3 grid, hipStream_t s);
 
 hipError_t launch_gather(int esize, bool vec, const GatherArgs& a, dim3 grid, hipStream_t s);
 hipError_t launch_multicopy(int esize, const MultiCopyArgs& a, hipStream_t s);

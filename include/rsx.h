@@ -61,7 +61,14 @@ typedef enum {
   RSX_FLOAT16 = 4,   /* IEEE half in, widened exactly to fp32, fp32 fold, one RNE rounding out */
   RSX_INT64 = 5,     /* int64, wrapping */
   RSX_UINT64 = 6,    /* uint64, wrapping */
-  RSX_INT8 = 7       /* int8 (the page's char), wrapping */
+  RSX_INT8 = 7,      /* int8 (the page's char), wrapping */
+  RSX_FLOAT32_HALF_WIRE = 8 /* fp32 in and out with IEEE half as the wire format
+                               [Apache SINGA communicator.cc, synchHalf / fusedSynchHalf]:
+                               each input is rounded (RNE) to half and widened back, the
+                               halves are folded as RSX_FLOAT16 is (fp32, one rounding), and
+                               the half result is widened to fp32.  Reductions only:
+                               rsx_all_gather rejects it with RSX_ERR_INVALID_TYPE; pack and
+                               unpack treat it as fp32.  W = 1 still rounds through half. */
 } rsx_dtype_t;
 
 typedef enum {

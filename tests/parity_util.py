@@ -12,9 +12,10 @@ import torch
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32,
                "f64": torch.float64, "f16": torch.float16, "i64": torch.int64,
-               "u64": torch.uint64, "i8": torch.int8}
+               "u64": torch.uint64, "i8": torch.int8, "f32h": torch.float32}
 NP_DTYPE = {"f32": np.float32, "bf16": np.uint16, "i32": np.int32, "f64": np.float64,
-            "f16": np.uint16, "i64": np.int64, "u64": np.uint64, "i8": np.int8}
+            "f16": np.uint16, "i64": np.int64, "u64": np.uint64, "i8": np.int8,
+            "f32h": np.float32}
 # a signed integer type of the same width, for filling and viewing raw bits
 _BITS_T = {1: torch.int8, 2: torch.int16, 4: torch.int32, 8: torch.int64}
 _BITS_NP = {1: np.uint8, 2: np.uint16, 4: np.uint32, 8: np.uint64}
@@ -68,7 +69,7 @@ def assert_parity(got: np.ndarray, want: np.ndarray, dtype: str, what: str = "")
         g = got.view(bits)
         w = want.view(bits)
         bad = np.flatnonzero(g != w)
-        if dtype in ("f32", "f64", "f16"):  # NaN payloads are not pinned: any NaN matches any NaN
+        if dtype in ("f32", "f64", "f16", "f32h"):  # NaN payloads are not pinned: any NaN matches any NaN
             gf = got.view(np.float16) if dtype == "f16" else got
             wf = want.view(np.float16) if dtype == "f16" else want
             bad = bad[~(np.isnan(gf[bad]) & np.isnan(wf[bad]))]

@@ -60,6 +60,7 @@ def test_enum_and_macro_values_match_binding(lib):
                       ("RSX_INT32", L.RSX_INT32), ("RSX_FLOAT64", L.RSX_FLOAT64),
                       ("RSX_FLOAT16", L.RSX_FLOAT16), ("RSX_INT64", L.RSX_INT64),
                       ("RSX_UINT64", L.RSX_UINT64), ("RSX_INT8", L.RSX_INT8),
+                      ("RSX_FLOAT32_HALF_WIRE", L.RSX_FLOAT32_HALF_WIRE),
                       ("RSX_SUM", L.RSX_SUM), ("RSX_MAX", L.RSX_MAX),
                       ("RSX_MIN", L.RSX_MIN), ("RSX_AVG", L.RSX_AVG), ("RSX_PROD", L.RSX_PROD),
                       ("RSX_ALGO_RING", L.RSX_ALGO_RING), ("RSX_ALGO_NAIVE", L.RSX_ALGO_NAIVE),
@@ -74,7 +75,7 @@ def test_enum_and_macro_values_match_binding(lib):
 
 
 def test_dtype_size_and_status_strings(lib):
-    assert [lib.rsx_dtype_size(d) for d in (0, 1, 2, 3, 4, 5, 6, 7, 8, -1)] == [4, 2, 4, 8, 2, 8, 8, 1, 0, 0]
+    assert [lib.rsx_dtype_size(d) for d in (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, -1)] == [4, 2, 4, 8, 2, 8, 8, 1, 4, 0, 0]
     for code in range(7):
         assert lib.rsx_status_string(code)
     assert lib.rsx_status_string(99) == b"unknown status"
@@ -133,7 +134,7 @@ def test_null_arrays_and_rank_range(lib):
 @fake_ptrs
 def test_bad_enums(lib):
     s, r = [A, A + MB], [A + 2 * MB, A + 3 * MB]
-    assert _rs(lib, s, r, 2, 4, dt=8) == 2
+    assert _rs(lib, s, r, 2, 4, dt=9) == 2
     assert _rs(lib, s, r, 2, 4, dt=-1) == 2
     assert _rs(lib, s, r, 2, 4, op=5) == 3
     assert _ar(lib, s, r, 2, 4, op=-1) == 3
@@ -161,6 +162,12 @@ def test_single_rank_in_place_is_a_no_op(lib):
     assert _rs(lib, [A], [A], 1, 100) == 0
     assert _ar(lib, [A], [A], 1, 100) == 0
     assert _ag(lib, [A], [A], 1, 100) == 0
+
+
+@fake_ptrs
+def test_half_wire_is_for_reductions_only(lib):
+    # a gather reduces nothing, so the half wire type is refused before any HIP call
+    assert _ag(lib, [A, A + MB], [A + 2 * MB, A + 3 * MB], 2, 4, dt=L.RSX_FLOAT32_HALF_WIRE) == 2
 
 
 @fake_ptrs
@@ -245,7 +252,7 @@ def test_fused_all_reduce_validation(lib):
     r = [A + 16 * MB + i * MB for i in range(6)]
     assert lib.rsx_fused_all_reduce(_arr(s), _arr(r), None, 3, 2, 0, 0, 0, None) == 1   # counts
     assert _far(lib, s, r, c, 0) == 1 and _far(lib, s, r, c, 17) == 1
-    assert _far(lib, s, r, c, 2, dt=8) == 2
+    assert _far(lib, s, r, c, 2, dt=9) == 2
     assert _far(lib, s, r, c, 2, op=7) == 3
     assert _far(lib, s, r, c, 2, algo=9) == 1
     assert _far(lib, s, r, [0, 0, 0], 2) == 0                      # nothing to do, no launch

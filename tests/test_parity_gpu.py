@@ -17,9 +17,15 @@ from parity_util import assert_parity, empty, say, to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 DIST = {"f32": "normal", "bf16": "normal_bf16", "i32": "int_full", "f64": "normal_f64",
-        "f16": "normal_f16", "i64": "int64_full", "u64": "uint64_full", "i8": "int8_full"}
-VL = {"f32": 4, "bf16": 8, "i32": 4, "f64": 2, "f16": 8, "i64": 2, "u64": 2, "i8": 16}
+        "f16": "normal_f16", "i64": "int64_full", "u64": "uint64_full", "i8": "int8_full",
+        "f32h": "normal"}
+VL = {"f32": 4, "bf16": 8, "i32": 4, "f64": 2, "f16": 8, "i64": 2, "u64": 2, "i8": 16, "f32h": 4}
 ALL_DTYPES = list(DIST)
+
+
+def wire(dtype):
+    """"f32h" = float32 tensors reduced with half as the wire format."""
+    return "f16" if dtype == "f32h" else None
 
 
 def units(w):  # dwordx4 per lane per source in the fold kernels
@@ -37,7 +43,7 @@ def inputs(seed, w, n, dtype, dist=None):
 def run_rs(xs, dtype, op, recvcount):
     dev = [to_dev(x, dtype) for x in xs]
     out = [empty(recvcount, dtype, fill=0x55) for _ in xs]
-    rsx.reduce_scatter(dev, out, op)
+    rsx.reduce_scatter(dev, out, op, wire=wire(dtype))
     torch.cuda.synchronize()
     return [to_host(o, dtype) for o in out]
 
@@ -45,7 +51,7 @@ def run_rs(xs, dtype, op, recvcount):
 def run_ar(xs, dtype, op, algo="ring", in_place=False):
     dev = [to_dev(x, dtype) for x in xs]
     out = None if in_place else [empty(len(xs[0]), dtype, fill=0x55) for _ in xs]
-    rsx.all_reduce(dev, out, op, algo)
+    rsx.all_reduce(dev, out, op, algo, wire=wire(dtype))
     torch.cuda.synchronize()
     return [to_host(o, dtype) for o in (dev if in_place else out)]
 
@@ -149,6 +155,29 @@ def test_bf16_specials_and_rounding_ties():
 
 # ----------------------------------------------------------- in place -------
 
+@pytest.mark.parametrize("algo", ["ring", "naive"])
+def test_half_wire_ties_ranges_and_one_rank(algo):
+    # half ties, values beyond half's range, half subnormals and fp32 values
+    # below them, in fp32 tensors; W = 1 (also in place) still rounds.
+    f = np.float32
+    special = np.array([1 + 2 ** -11, 1 + 3 * 2 ** -11, 65519.0, 65520.0, 1e5, -1e5, 2.0 ** -25,
+                        3 * 2.0 ** -25, 1e-9, -0.0, np.inf, np.nan, 4 + 2 ** -11, 2.0 ** -14], f)
+    rng = np.random.default_rng(31)
+    for w in (1, 3, 4):
+        xs = [np.concatenate([np.tile(special, 40), (rng.standard_normal(3000) * 3e4).astype(f),
+                              (rng.standard_normal(3000) * 1e-6).astype(f)]) for _ in range(w)]
+        say(f"half wire specials w={w} algo={algo}")
+        got = run_ar(xs, "f32h", "sum", algo)
+        want = (oracle.all_reduce if algo == "ring" else oracle.naive_all_reduce)(xs, "sum", "f32h")
+        lit = oracle.half_wire_all_reduce(xs, "sum", algo)
+        for r in range(w):
+            assert_parity(got[r], want[r], "f32h", f"rank {r}")
+            assert_parity(got[r], lit[r], "f32h", f"rank {r} vs float2half-allreduce-half2float")
+    say("half wire W=1 in place")
+    got = run_ar([xs[0][:1000]], "f32h", "avg", algo, in_place=True)
+    assert_parity(got[0], oracle.f16_to_f32(oracle.f32_to_f16(xs[0][:1000])), "f32h", "W=1")
+
+
 @pytest.mark.parametrize("dtype", ALL_DTYPES)
 @pytest.mark.parametrize("w", [1, 2, 4, 8])
 def test_in_place(w, dtype):
@@ -157,7 +186,7 @@ def test_in_place(w, dtype):
     xs = inputs(4, w, w * s, dtype)
     dev = [to_dev(x, dtype) for x in xs]
     say(f"in-place rs w={w} dtype={dtype}")
-    rsx.reduce_scatter(dev, [dev[k][k * s:(k + 1) * s] for k in range(w)], "sum")
+    rsx.reduce_scatter(dev, [dev[k][k * s:(k + 1) * s] for k in range(w)], "sum", wire=wire(dtype))
     torch.cuda.synchronize()
     want = oracle.reduce_scatter(xs, "sum", dtype)
     for k in range(w):
@@ -273,7 +302,7 @@ def test_all_gather_in_place_and_composition():
 
 # --------------------------------------------------------------- fusion -----
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "f64", "i8", "f16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f64", "i8", "f16", "f32h"])
 def test_fused_pack_allreduce_unpack(dtype):
     w = 4
     sizes = wl.fused_sizes(count=70, lo=1, hi=70_000)
@@ -289,7 +318,7 @@ def test_fused_pack_allreduce_unpack(dtype):
     for r in range(w):
         assert_parity(to_host(fused[r], dtype), oracle.fuse_pack(per_rank[r]), dtype, "pack")
     outs = [[empty(int(s), dtype) for s in sizes] for _ in range(w)]
-    rsx.fused_all_reduce(tens, fused, outs, "sum")
+    rsx.fused_all_reduce(tens, fused, outs, "sum", wire=wire(dtype))
     torch.cuda.synchronize()
     want = oracle.fused_all_reduce(per_rank, "sum", dtype)
     for r in range(w):
@@ -315,7 +344,7 @@ def test_tensor_fusion_all_reduce(w, op, dtype, algo):
     tens = [[to_dev(t, dtype) for t in ts] for ts in per_rank]
     outs = [[empty(len(t), dtype, fill=0x33) for t in ts] for ts in per_rank]
     say(f"tensor-fusion ar w={w} op={op} dtype={dtype} algo={algo}")
-    rsx.TensorFusionAllReduce(tens, outs, op, algo)()
+    rsx.TensorFusionAllReduce(tens, outs, op, algo, wire=wire(dtype))()
     torch.cuda.synchronize()
     want = oracle.fused_all_reduce(per_rank, op, dtype) if algo == "ring" else [
         oracle.fuse_unpack(f, LIST_SIZES) for f in oracle.naive_all_reduce(
