@@ -6,3 +6,6 @@ from .collectives import (  # noqa: F401
     fused_all_reduce, fusion_groups, grouped_all_reduce, half_wire_all_reduce, naive_all_reduce, naive_fold_order, reduce_scatter,
     ring_fold_order, segment_bounds,
 )
+from .sparse import (  # noqa: F401,E402
+    sparse_all_reduce, sparse_combine, sparsify_threshold, sparsify_topk, topk_count,
+)
