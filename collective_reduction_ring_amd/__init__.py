@@ -9,6 +9,6 @@ from .api import (  # noqa: F401
     GroupedAllReduce, TensorFusionAllReduce, fusion_groups, fusion_threshold,
     all_gather, all_reduce,
     all_reduce_bucketed, fuse_pack, fuse_unpack, fused_all_reduce, reduce_scatter,
-    segment_begin, version,
+    segment_begin, version, SparseAllReduce, sparse_all_reduce, topk_count, SPARSE_MODES,
 )
 from ._lib import RsxError  # noqa: F401

@@ -18,6 +18,7 @@ RSX_FLOAT64, RSX_FLOAT16, RSX_INT64, RSX_UINT64, RSX_INT8 = 3, 4, 5, 6, 7
 RSX_FLOAT32_HALF_WIRE = 8
 RSX_SUM, RSX_MAX, RSX_MIN, RSX_AVG, RSX_PROD = 0, 1, 2, 3, 4
 RSX_ALGO_RING, RSX_ALGO_NAIVE, RSX_ALGO_AUTO = 0, 1, 2
+RSX_SPARSE_THRESHOLD, RSX_SPARSE_TOPK = 0, 1
 RSX_MAX_RANKS = 16
 RSX_NAIVE_MAX_BYTES = 32768
 RSX_FUSE_BATCH = 64
@@ -46,6 +47,10 @@ SIGNATURES = {
     "rsx_fuse_unpack": (_I, [_P, _PP, ctypes.POINTER(_SZ), _I, _I, _P]),
     "rsx_fused_all_reduce": (_I, [_PP, _PP, ctypes.POINTER(_SZ), _I, _I, _I, _I, _I, _P]),
     "rsx_fusion_plan": (_I, [ctypes.POINTER(_SZ), ctypes.POINTER(_I), _I, _SZ, ctypes.POINTER(_I)]),
+    "rsx_sparse_topk_count": (_SZ, [_SZ, ctypes.c_float]),
+    "rsx_sparse_workspace_size": (_SZ, [_I, _SZ, _I, _I]),
+    "rsx_sparse_all_reduce": (_I, [_PP, _PP, _PP, _I, _SZ, _I, ctypes.c_float, _SZ, _PP, _PP, _SZ,
+                                   _P, _P, _SZ, _P]),
     "rsx_segment_begin": (_SZ, [_SZ, _I, _I]),
     "rsx_dtype_size": (_SZ, [_I]),
     "rsx_status_string": (ctypes.c_char_p, [_I]),

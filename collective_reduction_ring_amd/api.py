@@ -351,6 +351,97 @@ def fused_all_reduce(tensors_per_rank, fused_per_rank, outputs_per_rank=None, op
     FusedAllReduce(tensors_per_rank, fused_per_rank, outputs_per_rank, op, algo, wire)(stream)
 
 
+SPARSE_MODES = {"threshold": L.RSX_SPARSE_THRESHOLD, "topk": L.RSX_SPARSE_TOPK}
+
+
+def topk_count(count: int, fraction: float) -> int:
+    """K of the top-K mode: ceil(fraction * count) in fp32 arithmetic (SINGA topKSparsAllReduce)."""
+    return int(L.lib().rsx_sparse_topk_count(count, fraction))
+
+
+class SparseAllReduce:
+    """Prepared sparsified all-reduce with error feedback (SINGA communicator.cc,
+    sparsification -> valSparsAllReduce / topKSparsAllReduce).
+
+    ``grads``: W float32 tensors of ``count`` elements.  ``accums``: None, or W
+    float32 tensors that are added to the gradients first and receive what was
+    not sent.  ``outs``: None writes the result into ``grads`` (as the page
+    does); otherwise W tensors.  ``mode="threshold"`` sends entries with
+    ``|g| >= threshold``; ``mode="topk"`` sends the ``k`` largest values (or
+    ``topk_count(count, fraction)``).  After a call, rank r's message is
+    ``msg_idx[r][:n]`` / ``msg_val[r][:n]`` with ``n = nnz_host()[r]``.
+    The message buffers, the lengths and the workspace are allocated here,
+    once, by PyTorch; calls allocate nothing.
+    """
+
+    def __init__(self, grads, accums=None, outs=None, mode: str = "threshold",
+                 threshold: float = 0.0, k: int | None = None, fraction: float | None = None):
+        w = _ranks(grads)
+        count = grads[0].numel()
+        dev = grads[0].device
+        _check(grads, count, "grads", torch.float32, dev)
+        outs = grads if outs is None else outs
+        if len(outs) != w or (accums is not None and len(accums) != w):
+            raise ValueError("need one output and one accumulation buffer per rank")
+        _check(outs, count, "outs", torch.float32, dev)
+        if accums is not None:
+            _check(accums, count, "accums", torch.float32, dev)
+        for t in list(grads) + list(outs) + list(accums or []):
+            if t.data_ptr() % 16:
+                raise ValueError("sparse all-reduce buffers must be 16-byte aligned")
+        if mode not in SPARSE_MODES:
+            raise ValueError(f"unknown mode {mode!r}; one of {sorted(SPARSE_MODES)}")
+        if mode == "topk":
+            if k is None:
+                if fraction is None:
+                    raise ValueError("top-K needs k or fraction")
+                k = topk_count(count, fraction)
+            if not 0 <= k <= count:
+                raise ValueError(f"k={k} outside [0, {count}]")
+            cap = k
+        else:
+            k, cap = 0, count
+        lib = L.lib()
+        self.device, self.count, self.world, self.k = dev, count, w, k
+        self.msg_idx = [torch.empty(max(cap, 1), dtype=torch.int32, device=dev) for _ in range(w)]
+        self.msg_val = [torch.empty(max(cap, 1), dtype=torch.float32, device=dev) for _ in range(w)]
+        self.nnz = torch.zeros(w, dtype=torch.int32, device=dev)
+        ws = lib.rsx_sparse_workspace_size(w, count, SPARSE_MODES[mode], int(accums is not None))
+        if ws == 0:
+            raise ValueError("rsx_sparse_workspace_size rejected the sizes")
+        self._ws = torch.empty(ws + 256, dtype=torch.uint8, device=dev)
+        ws_ptr = self._ws.data_ptr() + (-self._ws.data_ptr()) % 256
+        self.args = (L.ptr_array([t.data_ptr() for t in grads]),
+                     L.ptr_array([t.data_ptr() for t in accums]) if accums is not None else None,
+                     L.ptr_array([t.data_ptr() for t in outs]),
+                     w, count, SPARSE_MODES[mode], float(threshold), k,
+                     L.ptr_array([t.data_ptr() for t in self.msg_idx]),
+                     L.ptr_array([t.data_ptr() for t in self.msg_val]),
+                     cap, self.nnz.data_ptr(), ws_ptr, ws)
+        self.fn = lib.rsx_sparse_all_reduce
+        self.keep = (list(grads), accums, list(outs))
+
+    def __call__(self, stream=None) -> None:
+        _launch(self, "rsx_sparse_all_reduce", stream)
+
+    def nnz_host(self) -> list[int]:
+        """Message lengths (synchronises with the device)."""
+        return [int(v) & 0xFFFFFFFF for v in self.nnz.cpu().tolist()]
+
+    def message(self, r: int):
+        """Rank r's (indices, values) message as device tensors (synchronises)."""
+        n = self.nnz_host()[r]
+        return self.msg_idx[r][:n], self.msg_val[r][:n]
+
+
+def sparse_all_reduce(grads, accums=None, outs=None, mode: str = "threshold", threshold: float = 0.0,
+                      k: int | None = None, fraction: float | None = None, stream=None) -> SparseAllReduce:
+    """One sparsified all-reduce; returns the plan, whose buffers hold the messages."""
+    p = SparseAllReduce(grads, accums, outs, mode, threshold, k, fraction)
+    p(stream)
+    return p
+
+
 def segment_begin(count: int, nranks: int, k: int) -> int:
     """First element of segment k of a ring all-reduce of ``count`` elements."""
     return int(L.lib().rsx_segment_begin(count, nranks, k))

@@ -3,6 +3,7 @@
 //
 // Every check runs before the first HIP call, so a rejected call has no side
 // effect and the error paths can be exercised on a machine without a GPU.
+#include <math.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -262,6 +263,40 @@ bool list_aliasing_ok(std::vector<Span>& sends, std::vector<Span>& recvs) {
       if (u.lo != r.lo || u.hi != r.hi || u.tensor != r.tensor) return false;
     }
   }
+  return true;
+}
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Workspace of the sparsified all-reduce: per-tile counts/offsets and ties,
+// radix histograms, selection state, and (top-K with an accumulation) the
+// values grad + accum that the selection passes read again.  Each region
+// starts on a 256-byte boundary.
+constexpr size_t kWsAlign = 256;
+size_t ws_align(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
+struct SparseLayout {
+  size_t tile_off, tile_eq, hist, state, keys, total;
+  uint32_t tiles;
+};
+bool sparse_layout(int w, size_t count, int mode, bool accum, SparseLayout* l) {
+  if (w < 1 || w > RSX_MAX_RANKS) return false;
+  if (mode != RSX_SPARSE_THRESHOLD && mode != RSX_SPARSE_TOPK) return false;
+  if (count > UINT32_MAX) return false;
+  const size_t ws = static_cast<size_t>(w);
+  l->tiles = static_cast<uint32_t>((count + kSpTile - 1) / kSpTile);
+  const size_t tile_bytes = ws_align(ws * (l->tiles + 1) * 4);
+  size_t off = 0;
+  l->tile_off = off;
+  off += tile_bytes;
+  l->tile_eq = off;
+  off += tile_bytes;
+  l->hist = off;
+  off += ws_align(ws * kSpBins * 4);
+  l->state = off;
+  off += ws_align(ws * 16);
+  l->keys = off;
+  if (mode == RSX_SPARSE_TOPK && accum) off += ws_align(ws * count * 4);
+  l->total = off;
   return true;
 }
 
@@ -570,6 +605,115 @@ int rsx_fusion_plan(const size_t* counts, const rsx_dtype_t* dtypes, int ntensor
     i = j;
   }
   return ngroups;
+}
+
+size_t rsx_sparse_topk_count(size_t count, float fraction) {
+  const float p = fraction * static_cast<float>(count);  // fp32 product, as on the page
+  if (!(p > 0.0f)) return 0;
+  const float c = ceilf(p);
+  if (c >= 18446744073709551616.0f) return SIZE_MAX;
+  return static_cast<size_t>(c);
+}
+
+size_t rsx_sparse_workspace_size(int nranks, size_t count, rsx_sparse_mode_t mode, int has_accum) {
+  SparseLayout l;
+  return sparse_layout(nranks, count, mode, has_accum != 0, &l) ? l.total : 0;
+}
+
+rsx_status_t rsx_sparse_all_reduce(const float* const* grads, float* const* accums,
+                                   float* const* outs, int nranks, size_t count,
+                                   rsx_sparse_mode_t mode, float threshold, size_t k,
+                                   uint32_t* const* msg_idx, float* const* msg_val,
+                                   size_t msg_capacity, uint32_t* nnz, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  if (grads == nullptr || outs == nullptr || msg_idx == nullptr || msg_val == nullptr)
+    return RSX_ERR_INVALID_ARGUMENT;
+  if (nranks < 1 || nranks > RSX_MAX_RANKS) return RSX_ERR_INVALID_ARGUMENT;
+  if (mode != RSX_SPARSE_THRESHOLD && mode != RSX_SPARSE_TOPK) return RSX_ERR_INVALID_ARGUMENT;
+  if (count > UINT32_MAX) return RSX_ERR_UNSUPPORTED;
+  if (mode == RSX_SPARSE_TOPK && k > count) return RSX_ERR_INVALID_ARGUMENT;
+  if (nnz == nullptr || !aligned4(nnz)) return RSX_ERR_INVALID_ARGUMENT;
+  const Range nr = range_of(nnz, static_cast<size_t>(nranks) * 4);
+  if (wraps(nr)) return RSX_ERR_INVALID_ARGUMENT;
+  if (count == 0) return hip_status(launch_sparse_zero_nnz(nnz, nranks, stream));
+
+  const bool has_acc = accums != nullptr;
+  const size_t sent_max = mode == RSX_SPARSE_THRESHOLD ? count : k;
+  if (msg_capacity < sent_max) return RSX_ERR_INVALID_ARGUMENT;
+  SparseLayout l;
+  sparse_layout(nranks, count, mode, has_acc, &l);
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & (kWsAlign - 1)) != 0 ||
+      workspace_bytes < l.total)
+    return RSX_ERR_INVALID_ARGUMENT;
+  const size_t bytes = count * 4;
+  for (int r = 0; r < nranks; ++r) {
+    if (grads[r] == nullptr || outs[r] == nullptr || msg_idx[r] == nullptr || msg_val[r] == nullptr ||
+        (has_acc && accums[r] == nullptr))
+      return RSX_ERR_INVALID_ARGUMENT;
+    if (!aligned16(grads[r]) || !aligned16(outs[r]) || (has_acc && !aligned16(accums[r])) ||
+        !aligned4(msg_idx[r]) || !aligned4(msg_val[r]))
+      return RSX_ERR_INVALID_ARGUMENT;
+  }
+  // Everything written must be pairwise disjoint and apart from the
+  // gradients, except the outputs: they are written after every read of the
+  // gradients, so they may overlap them (in place: outs[r] == grads[r]).
+  std::vector<Range> writes, outs_r;
+  Range grads_r[RSX_MAX_RANKS];
+  for (int r = 0; r < nranks; ++r) {
+    grads_r[r] = range_of(grads[r], bytes);
+    outs_r.push_back(range_of(outs[r], bytes));
+    writes.push_back(outs_r.back());
+    if (has_acc) writes.push_back(range_of(accums[r], bytes));
+    writes.push_back(range_of(msg_idx[r], sent_max * 4));
+    writes.push_back(range_of(msg_val[r], sent_max * 4));
+    if (wraps(grads_r[r])) return RSX_ERR_INVALID_ARGUMENT;
+  }
+  writes.push_back(nr);
+  writes.push_back(range_of(workspace, l.total));
+  for (const Range& w : writes)
+    if (wraps(w)) return RSX_ERR_INVALID_ARGUMENT;
+  if (!pairwise_disjoint(writes.data(), static_cast<int>(writes.size()))) return RSX_ERR_ALIASING;
+  for (const Range& w : writes) {
+    bool is_out = false;
+    for (const Range& o : outs_r) is_out = is_out || same(o, w);
+    if (is_out) continue;
+    for (int r = 0; r < nranks; ++r)
+      if (overlap(w, grads_r[r])) return RSX_ERR_ALIASING;
+  }
+
+  SparseArgs a;
+  memset(&a, 0, sizeof(a));
+  char* ws = static_cast<char*>(workspace);
+  for (int r = 0; r < nranks; ++r) {
+    a.grad[r] = grads[r];
+    a.accum[r] = has_acc ? accums[r] : nullptr;
+    a.out[r] = outs[r];
+    a.msg_idx[r] = msg_idx[r];
+    a.msg_val[r] = msg_val[r];
+    if (mode == RSX_SPARSE_TOPK && has_acc) {
+      a.key_store[r] = reinterpret_cast<float*>(ws + l.keys) + static_cast<size_t>(r) * count;
+      a.key[r] = a.key_store[r];
+    } else {
+      a.key[r] = grads[r];
+    }
+  }
+  a.nnz = nnz;
+  a.tile_off = reinterpret_cast<uint32_t*>(ws + l.tile_off);
+  a.tile_eq = reinterpret_cast<uint32_t*>(ws + l.tile_eq);
+  a.hist = reinterpret_cast<uint32_t*>(ws + l.hist);
+  a.state = reinterpret_cast<uint32_t*>(ws + l.state);
+  a.count = count;
+  a.tiles = l.tiles;
+  a.world = static_cast<uint32_t>(nranks);
+  a.k = mode == RSX_SPARSE_TOPK ? static_cast<uint32_t>(k) : 0u;
+  a.cap = static_cast<uint32_t>(sent_max);
+  a.threshold = threshold;
+  // About 2048 histogram workgroups in all (8 per CU), each over whole tiles.
+  uint32_t groups = std::max<uint32_t>(1, 2048u / static_cast<uint32_t>(nranks));
+  groups = std::min<uint32_t>(groups, l.tiles);
+  a.hist_chunk = (l.tiles + groups - 1) / groups;
+  a.hist_groups = (l.tiles + a.hist_chunk - 1) / a.hist_chunk;
+  return hip_status(launch_sparse(a, mode, has_acc, stream));
 }
 
 size_t rsx_segment_begin(size_t count, int nranks, int k) {

@@ -42,6 +42,7 @@
 #define RSX_H
 
 #include <stddef.h>
+#include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -187,6 +188,69 @@ rsx_status_t rsx_fused_all_reduce(const void* const* sendtensors, void* const* r
                                   const size_t* counts, int ntensors, int nranks,
                                   rsx_dtype_t dtype, rsx_op_t op, rsx_algo_t algo,
                                   hipStream_t stream);
+
+/* Sparsification of rsx_sparse_all_reduce [SG valSparsAllReduce / topKSparsAllReduce]. */
+typedef enum {
+  RSX_SPARSE_THRESHOLD = 0, /* send the entries with |x| >= threshold (never a zero) */
+  RSX_SPARSE_TOPK = 1       /* send the k largest values (not magnitudes); ties by lower index */
+} rsx_sparse_mode_t;
+
+/*
+ * K of the top-K mode as the page computes it: ceil(fraction * count) with
+ * `fraction` a float and `count` converted to float, the product rounded to
+ * float [SG topKSparsAllReduce].  Returns 0 when the product is not positive
+ * (or NaN).  Host arithmetic only.
+ */
+size_t rsx_sparse_topk_count(size_t count, float fraction);
+
+/*
+ * Bytes of device workspace rsx_sparse_all_reduce needs for these sizes
+ * (per-tile offsets, radix histograms and, for RSX_SPARSE_TOPK with an
+ * accumulation, a copy of grad + accum).  0 for invalid arguments.
+ */
+size_t rsx_sparse_workspace_size(int nranks, size_t count, rsx_sparse_mode_t mode, int has_accum);
+
+/*
+ * Sparsified all-reduce with error feedback [SG valSparsAllReduce,
+ * topKSparsAllReduce, via sparsification / fusedSparsification].
+ *
+ * For each rank r, with g = grads[r] + accums[r] (one fp32 add; g = grads[r]
+ * when accums is NULL):
+ *   RSX_SPARSE_THRESHOLD: entry i is sent when |g[i]| >= threshold and
+ *     g[i] != 0;
+ *   RSX_SPARSE_TOPK: the k largest g[i] are sent (a NaN ranks below every
+ *     number, -0 equals +0, equal values are taken by increasing index);
+ *   with accums: accums[r][i] = g[i] - (0 + g[i]) where sent, g[i] - 0 where
+ *     not (what was not sent; a sent inf leaves NaN);
+ *   msg_idx[r][0..nnz[r]), msg_val[r][0..nnz[r]): the sent (zero-based
+ *     index, g value) pairs in increasing index order (the page's wire
+ *     message; its top-K message holds the same pairs sorted by value).
+ * Then every outs[r][i] = the fp32 sum, starting from +0 and taking ranks
+ * 0, 1, ..., W-1 in order, of the values sent for index i (+0 if none).
+ *
+ * grads[r], outs[r], accums[r]: device arrays of `count` fp32, 16-byte
+ *   aligned.  accums may be NULL (no error feedback); if not, every entry
+ *   must be set.  outs[r] == grads[r] is allowed (in place, as the page
+ *   writes the result into the gradient).
+ * msg_idx[r], msg_val[r]: device arrays of msg_capacity entries, 4-byte
+ *   aligned; msg_capacity >= count (threshold) or >= k (top-K).
+ * nnz: device array of nranks uint32, the message lengths (k for top-K).
+ * workspace: device memory, 256-byte aligned, of at least
+ *   rsx_sparse_workspace_size(...) bytes; its contents are scratch.
+ * count <= UINT32_MAX (indices are uint32); k <= count.
+ * count 0: nnz is zeroed and nothing else is touched.
+ * Buffers other than outs[r] == grads[r] must not overlap (grads may overlap
+ * each other): RSX_ERR_ALIASING.  Invalid sizes, pointers, alignment, mode or
+ * capacity: RSX_ERR_INVALID_ARGUMENT; count > UINT32_MAX: RSX_ERR_UNSUPPORTED.
+ * Validation precedes every HIP call.  Enqueues about 6 kernels (threshold)
+ * or 12 (top-K) on `stream`; allocates nothing and does not synchronise.
+ */
+rsx_status_t rsx_sparse_all_reduce(const float* const* grads, float* const* accums,
+                                   float* const* outs, int nranks, size_t count,
+                                   rsx_sparse_mode_t mode, float threshold, size_t k,
+                                   uint32_t* const* msg_idx, float* const* msg_val,
+                                   size_t msg_capacity, uint32_t* nnz, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Tensor-fusion planner [HV BackgroundThreadLoop, fusion of consecutive

@@ -327,3 +327,73 @@ def test_fusion_plan_validation(lib):
     assert lib.rsx_fusion_plan(L.size_array([1, 2]), None, 2, 10, ends) == -1
     # a tensor whose byte count overflows is a group of its own
     assert _plan(lib, [2 ** 63, 1, 1], [0, 0, 0], 2 ** 40) == [(0, 1), (1, 3)]
+
+
+# ------------------------------------------------ sparsified all-reduce --
+
+def test_sparse_topk_count_fp32_arithmetic(lib):
+    import oracle
+    for n, frac in [(10, 0.1), (2 ** 24 + 1, 1.0), (10, 0.3), (7, 0.0), (1000, 0.5),
+                    (67_108_864, 0.01), (12345, 0.123)]:
+        assert lib.rsx_sparse_topk_count(n, frac) == oracle.topk_count(n, frac), (n, frac)
+    assert lib.rsx_sparse_topk_count(10, -0.5) == 0
+    assert lib.rsx_sparse_topk_count(10, float("nan")) == 0
+
+
+def test_sparse_workspace_size(lib):
+    T, K = L.RSX_SPARSE_THRESHOLD, L.RSX_SPARSE_TOPK
+    assert lib.rsx_sparse_workspace_size(0, 100, T, 0) == 0
+    assert lib.rsx_sparse_workspace_size(17, 100, T, 0) == 0
+    assert lib.rsx_sparse_workspace_size(2, 100, 2, 0) == 0
+    assert lib.rsx_sparse_workspace_size(2, 2 ** 32, T, 0) == 0
+    small = lib.rsx_sparse_workspace_size(4, 10_000, K, 0)
+    assert small > 0 and small % 256 == 0
+    # top-K with an accumulation keeps grad + accum: 4 bytes per element per rank more
+    assert lib.rsx_sparse_workspace_size(4, 10_000, K, 1) >= small + 4 * 10_000 * 4
+    assert lib.rsx_sparse_workspace_size(4, 10_000, T, 1) == lib.rsx_sparse_workspace_size(4, 10_000, T, 0)
+
+
+def _sp(lib, grads, accs, outs, w, n, mode=0, thr=0.5, k=0, mi=None, mv=None, cap=None, nnz=None,
+        ws=None, wsb=None):
+    cap = n if cap is None else cap
+    mi = mi if mi is not None else [A + (40 + 2 * r) * MB for r in range(w)]
+    mv = mv if mv is not None else [A + (41 + 2 * r) * MB for r in range(w)]
+    nnz = A + 90 * MB if nnz is None else nnz
+    ws = A + 100 * MB if ws is None else ws
+    wsb = lib.rsx_sparse_workspace_size(w, n, mode, int(accs is not None)) if wsb is None else wsb
+    return lib.rsx_sparse_all_reduce(_arr(grads), _arr(accs) if accs is not None else None, _arr(outs),
+                                     w, n, mode, thr, k, _arr(mi), _arr(mv), cap, nnz, ws, wsb, None)
+
+
+@fake_ptrs
+def test_sparse_validation(lib):
+    g, o, a = [A, A + MB], [A + 2 * MB, A + 3 * MB], [A + 4 * MB, A + 5 * MB]
+    n = 1000
+    assert lib.rsx_sparse_all_reduce(None, None, _arr(o), 2, n, 0, 0.5, 0, _arr([A] * 2), _arr([A] * 2),
+                                     n, A, A, 1 << 20, None) == 1
+    assert _sp(lib, g, a, o, 0, n) == 1                       # no ranks
+    assert _sp(lib, g * 9, a * 9, o * 9, 17, n) == 1          # too many ranks
+    assert _sp(lib, g, a, o, 2, n, mode=2) == 1               # unknown mode
+    assert _sp(lib, g, a, o, 2, 2 ** 32, wsb=1 << 40) == 4    # indices are uint32
+    assert _sp(lib, g, a, o, 2, n, mode=1, k=n + 1) == 1      # k > count
+    assert _sp(lib, g, a, o, 2, n, cap=n - 1) == 1            # threshold needs room for count
+    assert _sp(lib, g, a, o, 2, n, mode=1, k=10, cap=9) == 1  # top-K needs room for k
+    assert _sp(lib, [A + 4, A + MB], a, o, 2, n) == 1         # gradient not 16-byte aligned
+    assert _sp(lib, g, [A + 4 * MB, A + 5 * MB + 8], o, 2, n) == 1
+    assert _sp(lib, g, a, o, 2, n, nnz=A + 90 * MB + 2) == 1  # nnz not 4-byte aligned
+    assert _sp(lib, g, a, o, 2, n, ws=A + 100 * MB + 64) == 1  # workspace not 256-byte aligned
+    assert _sp(lib, g, a, o, 2, n, mode=1, k=5,
+               wsb=lib.rsx_sparse_workspace_size(2, n, 1, 1) - 1) == 1   # workspace too small
+    assert _sp(lib, g, a, [A + 2 * MB, None], 2, n) == 1      # null output
+
+
+@fake_ptrs
+def test_sparse_aliasing(lib):
+    g, o, a = [A, A + MB], [A + 2 * MB, A + 3 * MB], [A + 4 * MB, A + 5 * MB]
+    n = 1000
+    assert _sp(lib, g, [A + MB, A + 5 * MB], o, 2, n) == 5                 # accumulation = a gradient
+    assert _sp(lib, g, a, [A + 2 * MB, A + 2 * MB + 16], 2, n) == 5       # outputs overlap
+    assert _sp(lib, g, a, [A + 4 * MB, A + 3 * MB], 2, n) == 5            # output = accumulation
+    assert _sp(lib, g, a, o, 2, n, mi=[A + 3 * MB, A + 42 * MB]) == 5     # message over an output
+    assert _sp(lib, g, a, o, 2, n, ws=A + 41 * MB) == 5                   # workspace over a message
+    assert _sp(lib, g, a, o, 2, n, nnz=A + 8) == 5                        # nnz inside a gradient

@@ -1,0 +1,174 @@
+"""Parity of the sparsified all-reduce (HIP, through the C ABI) with the CPU oracle.
+
+Bit-exact on everything: the results on every rank, the residual in every
+accumulation buffer, the message lengths, and every message entry.  The
+oracle's top-K message is in the page's order (by value); the library sends
+the same pairs in index order, so the oracle's pairs are compared sorted by
+index (indices are unique within a message).  Sizes span several 4096-element
+tiles with a ragged tail; W from 1 to 16; both modes, with and without error
+feedback; ties at the cut, signed zeros, infinities and NaNs; K = 0 and K =
+count; in place.
+"""
+import numpy as np
+import pytest
+import torch
+
+import collective_reduction_ring_amd as rsx
+import oracle
+from parity_util import say
+
+pytestmark = pytest.mark.gpu
+
+f32 = np.float32
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x, f32)).to("cuda:0")
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def same_bits(got, want, what):
+    got, want = np.asarray(got, f32), np.asarray(want, f32)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    bad = np.flatnonzero(got.view(np.uint32) != want.view(np.uint32))
+    bad = bad[~(np.isnan(got[bad]) & np.isnan(want[bad]))]
+    assert bad.size == 0, (f"{what}: {bad.size} of {got.size} differ; first at {bad[:5].tolist()}: "
+                           f"got {got[bad[:5]].tolist()} want {want[bad[:5]].tolist()}")
+
+
+def run_case(grads, accs, mode, threshold=0.0, k=None, in_place=False):
+    w = len(grads)
+    g = [dev(x) for x in grads]
+    a = [dev(x) for x in accs] if accs is not None else None
+    outs = None if in_place else [torch.full((len(grads[0]),), 7.0, device="cuda:0") for _ in range(w)]
+    plan = rsx.SparseAllReduce(g, a, outs, mode, threshold, k)
+    plan()
+    torch.cuda.synchronize()
+    res = [host(t) for t in (g if in_place else outs)]
+    acc_out = [host(t) for t in a] if a is not None else None
+    nnz = plan.nnz_host()
+    msgs = [(host(plan.msg_idx[r][:nnz[r]]).view(np.uint32).astype(np.int64),
+             host(plan.msg_val[r][:nnz[r]])) for r in range(w)]
+    return res, acc_out, nnz, msgs
+
+
+def check(grads, accs, mode, threshold=0.0, k=None, in_place=False, what=""):
+    say(f"sparse {what} mode={mode} w={len(grads)} n={len(grads[0])} thr={threshold} k={k}")
+    res, acc_out, nnz, msgs = run_case(grads, accs, mode, threshold, k, in_place)
+    want_res, want_acc, want_msgs = oracle.sparse_all_reduce(grads, accs, mode, threshold, k)
+    for r in range(len(grads)):
+        wi, wv = want_msgs[r]
+        order = np.argsort(wi, kind="stable")
+        assert nnz[r] == len(wi), (what, r, nnz[r], len(wi))
+        assert np.array_equal(msgs[r][0], wi[order]), f"{what}: rank {r} message indices"
+        same_bits(msgs[r][1], wv[order], f"{what}: rank {r} message values")
+        same_bits(res[r], want_res[r], f"{what}: rank {r} result")
+        if accs is not None:
+            same_bits(acc_out[r], want_acc[r], f"{what}: rank {r} residual")
+
+
+def normal_case(seed, w, n, scale=1e-3):
+    rng = np.random.default_rng(seed)
+    grads = [(rng.standard_normal(n) * scale).astype(f32) for _ in range(w)]
+    accs = [(rng.standard_normal(n) * scale).astype(f32) for _ in range(w)]
+    return grads, accs
+
+
+SIZES = [1, 5, 4096, 3 * 4096 + 777]
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("w", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("feedback", [True, False])
+def test_threshold(w, n, feedback):
+    grads, accs = normal_case((60, w, n), w, n)
+    check(grads, accs if feedback else None, "threshold", threshold=2e-3, what="threshold")
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("w", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("feedback", [True, False])
+def test_topk(w, n, feedback):
+    grads, accs = normal_case((61, w, n), w, n)
+    k = rsx.topk_count(n, 0.05)
+    assert k == oracle.topk_count(n, 0.05)
+    check(grads, accs if feedback else None, "topk", k=k, what="topk")
+
+
+@pytest.mark.parametrize("mode", ["threshold", "topk"])
+def test_ties_at_the_cut_and_specials(mode):
+    # values on a coarse grid, so the cut falls inside long runs of equal values
+    rng = np.random.default_rng(62)
+    w, n = 4, 5 * 4096 + 100
+    grads = [(rng.integers(-4, 5, n) * 0.5).astype(f32) for _ in range(w)]
+    accs = [(rng.integers(-1, 2, n) * 0.25).astype(f32) for _ in range(w)]
+    special = np.array([np.nan, np.inf, -np.inf, -0.0, 0.0, 2.0 ** -149, -(2.0 ** -149)], f32)
+    for r in range(w):
+        pos = rng.choice(n, 300, replace=False)
+        grads[r][pos] = special[rng.integers(0, len(special), 300)]
+        accs[r][pos[:40]] = -0.0
+    if mode == "threshold":
+        for thr in (1.0, 0.0, 2.0 ** -149, np.inf):
+            check(grads, accs, mode, threshold=thr, what=f"ties thr={thr}")
+    else:
+        for k in (1, 7, 1000, 4096, n // 2, n - 1):
+            check(grads, accs, mode, k=k, what=f"ties k={k}")
+
+
+def test_topk_k_zero_and_all_in_place():
+    grads, accs = normal_case(63, 3, 2 * 4096 + 9)
+    check(grads, accs, "topk", k=0, what="k=0")
+    check(grads, accs, "topk", k=len(grads[0]), what="k=n")
+    check(grads, None, "topk", k=321, in_place=True, what="in place")
+    check(grads, accs, "threshold", threshold=1e-3, in_place=True, what="in place")
+
+
+def test_error_feedback_over_steps():
+    # three steps on fixed gradients: each step's residual feeds the next
+    w, n = 4, 4096 + 3
+    rng = np.random.default_rng(64)
+    grads = [(rng.standard_normal(n) * 1e-3).astype(f32) for _ in range(w)]
+    acc_host = [np.zeros(n, f32) for _ in range(w)]
+    acc_dev = [dev(a) for a in acc_host]
+    g_dev = [dev(g) for g in grads]
+    outs = [torch.empty(n, device="cuda:0") for _ in range(w)]
+    plan = rsx.SparseAllReduce(g_dev, acc_dev, outs, "topk", fraction=0.01)
+    for step in range(3):
+        say(f"error feedback step {step}")
+        plan()
+        torch.cuda.synchronize()
+        want_res, acc_host, _ = oracle.sparse_all_reduce(grads, acc_host, "topk", k=plan.k)
+        for r in range(w):
+            same_bits(host(outs[r]), want_res[r], f"step {step} rank {r}")
+            same_bits(host(acc_dev[r]), acc_host[r], f"step {step} rank {r} residual")
+
+
+def test_count_zero_zeroes_nnz():
+    g = [torch.empty(0, device="cuda:0") for _ in range(2)]
+    plan = rsx.SparseAllReduce(g, None, None, "topk", k=0)
+    plan.nnz.fill_(5)
+    plan()
+    assert plan.nnz_host() == [0, 0]
+
+
+def test_errors_with_real_tensors():
+    x = [torch.zeros(64, device="cuda:0") for _ in range(2)]
+    with pytest.raises(ValueError):
+        rsx.SparseAllReduce(x, None, None, "topk", k=65)
+    with pytest.raises(ValueError):
+        rsx.SparseAllReduce(x, None, None, "bogus")
+    with pytest.raises(ValueError):
+        rsx.SparseAllReduce([t[1:] for t in x], None, None, "threshold")   # misaligned
+    with pytest.raises(rsx.RsxError) as e:   # accumulation = gradient of another rank
+        rsx.SparseAllReduce(x, [x[1], torch.zeros(64, device="cuda:0")], None, "threshold")()
+    assert e.value.status == 5
+
+
+def test_mid_size_w8():
+    # the bench's shape scaled down: W = 8, N(0, 1e-3) gradients and residuals
+    grads, accs = normal_case(65, 8, 1 << 20)
+    check(grads, accs, "topk", k=rsx.topk_count(1 << 20, 0.01), what="w8 topk 1%")
+    check(grads, accs, "threshold", threshold=3.6e-3, what="w8 threshold")
