@@ -102,6 +102,24 @@ def time_launches(fn, reps: int, warmup: int, torch) -> list:
     return [a.elapsed_time(b) for a, b in zip(st, en)]
 
 
+def time_from_state(fn, reset, reps: int, warmup: int, torch) -> list:
+    """Per-call durations (ms) of `fn`, each call started from the same state:
+    `reset()` runs before every call, outside the events."""
+    for _ in range(warmup):
+        reset()
+        fn()
+    torch.cuda.synchronize()
+    st = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    en = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        reset()
+        st[i].record()
+        fn()
+        en[i].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in zip(st, en)]
+
+
 def graph_us_per_call(fn, inner: int, reps: int, torch) -> float:
     """Device time per call: `inner` calls captured in one HIP graph, replayed
     `reps` times; the median replay divided by `inner`."""
@@ -256,6 +274,62 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
                 row[algo]["graph_us_per_call"] = graph_us_per_call(p, 100, 20, torch)
             res[f"{kib}KiB"] = row
         return res
+    if name == "sparse":
+        world, n = wl.SPARSE_WORLD, wl.SPARSE_N
+        log("generating sparse inputs")
+        grads, accs = wl.sparse_inputs()
+        _, g = _arena(torch, torch.float32, world, n)
+        a0_all, a0 = _arena(torch, torch.float32, world, n)
+        for d, x in zip(g, grads):
+            d.copy_(torch.from_numpy(x))
+        for d, x in zip(a0, accs):
+            d.copy_(torch.from_numpy(x))
+        del grads, accs
+        a_all, a = _arena(torch, torch.float32, world, n)
+        _, out = _arena(torch, torch.float32, world, n)
+        res = {"workload": f"sparsified all-reduce with error feedback, W={world}, {n} fp32/rank, "
+                           "N(0,1e-3) gradients and residuals",
+               "algorithmic_bytes": "W*n*16 (read grad and accum, write accum and output) "
+                                    "+ 16 per message entry (written once, read once)"}
+        modes = (("topk", {"fraction": wl.SPARSE_TOPK_FRACTION}),
+                 ("threshold", {"threshold": wl.SPARSE_THRESHOLD}))
+
+        def reset():   # every call starts from the same residual, as one training step would
+            a_all.copy_(a0_all)
+        for mode, kw in modes:
+            plan = rsx.SparseAllReduce(g, a, out, mode, **kw)
+            ms = time_from_state(plan, reset, reps, warm, torch)
+            nnz = plan.nnz_host()
+            st = _stat(ms, world * n * 16 + 16 * sum(nnz))
+            st.update(k=plan.k, nnz_rank0=nnz[0], nnz_total=sum(nnz), params=kw)
+            res[mode] = st
+        return res
+    if name == "dtypes":
+        world, rank_bytes = 8, 256 * 2 ** 20
+        arena_in = torch.empty(world * rank_bytes, dtype=torch.uint8, device="cuda:0")
+        arena_out = torch.empty(rank_bytes, dtype=torch.uint8, device="cuda:0")
+        gen = torch.Generator(device="cuda:0")
+        gen.manual_seed(7)
+        res = {"workload": "reduce-scatter sum, W=8, 256 MiB per rank, every element type "
+                           "(inputs: seeded N(0,1) for floats, uniform bits for integers)"}
+        cases = (("f32", torch.float32, None), ("bf16", torch.bfloat16, None), ("f16", torch.float16, None),
+                 ("f64", torch.float64, None), ("i32", torch.int32, None), ("i64", torch.int64, None),
+                 ("u64", torch.uint64, None), ("i8", torch.int8, None), ("f32_half_wire", torch.float32, "f16"))
+        for name_, dt, wire in cases:
+            flat = arena_in.view(dt)
+            if dt.is_floating_point:
+                flat.copy_(torch.randn(flat.numel(), generator=gen, device="cuda:0").to(dt))
+            else:
+                arena_in.copy_(torch.randint(0, 256, (arena_in.numel(),), generator=gen, device="cuda:0",
+                                             dtype=torch.int32).to(torch.uint8))
+            n = flat.numel() // world
+            ins = [flat[r * n:(r + 1) * n] for r in range(world)]
+            seg = n // world
+            outs = [arena_out.view(dt)[k * seg:(k + 1) * seg] for k in range(world)]
+            p = rsx.ReduceScatter(ins, outs, "sum", wire)
+            es = flat.element_size()
+            res[name_] = _stat(time_launches(p, reps, warm, torch), world * n * es + world * seg * es)
+        return res
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -271,7 +345,7 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--workload", default="rs_w8_f32",
                     choices=("rs_w8_f32", "small", "bf16_bucketed", "int32_w16", "fused", "sweep",
-                             "ceilings"),
+                             "sparse", "dtypes", "ceilings"),
                     help="rs_w8_f32 (default) is the headline line; the others print timings only")
     args = ap.parse_args()
 

@@ -268,14 +268,15 @@ bool list_aliasing_ok(std::vector<Span>& sends, std::vector<Span>& recvs) {
 
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-// Workspace of the sparsified all-reduce: per-tile counts/offsets and ties,
-// radix histograms, selection state, and (top-K with an accumulation) the
-// values grad + accum that the selection passes read again.  Each region
-// starts on a 256-byte boundary.
+// Workspace of the sparsified all-reduce: per-tile counts and offsets,
+// radix histograms, selection state, one slot of kSpTile candidate entries
+// per tile, and (top-K with an accumulation) the values grad + accum that
+// the selection passes read again.  Each region starts on a 256-byte
+// boundary.
 constexpr size_t kWsAlign = 256;
 size_t ws_align(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 struct SparseLayout {
-  size_t tile_off, tile_eq, hist, state, keys, total;
+  size_t tile_cnt, tile_eqc, tile_off, tile_eqb, hist, state, gap_idx, gap_val, keys, total;
   uint32_t tiles;
 };
 bool sparse_layout(int w, size_t count, int mode, bool accum, SparseLayout* l) {
@@ -285,11 +286,20 @@ bool sparse_layout(int w, size_t count, int mode, bool accum, SparseLayout* l) {
   const size_t ws = static_cast<size_t>(w);
   l->tiles = static_cast<uint32_t>((count + kSpTile - 1) / kSpTile);
   const size_t tile_bytes = ws_align(ws * (l->tiles + 1) * 4);
+  const size_t slot_bytes = ws_align(ws * l->tiles * kSpTile * 4);
   size_t off = 0;
+  l->tile_cnt = off;
+  off += tile_bytes;
+  l->tile_eqc = off;
+  off += tile_bytes;
   l->tile_off = off;
   off += tile_bytes;
-  l->tile_eq = off;
+  l->tile_eqb = off;
   off += tile_bytes;
+  l->gap_idx = off;
+  off += slot_bytes;
+  l->gap_val = off;
+  off += slot_bytes;
   l->hist = off;
   off += ws_align(ws * kSpBins * 4);
   l->state = off;
@@ -698,8 +708,12 @@ rsx_status_t rsx_sparse_all_reduce(const float* const* grads, float* const* accu
     }
   }
   a.nnz = nnz;
+  a.tile_cnt = reinterpret_cast<uint32_t*>(ws + l.tile_cnt);
+  a.tile_eqc = reinterpret_cast<uint32_t*>(ws + l.tile_eqc);
   a.tile_off = reinterpret_cast<uint32_t*>(ws + l.tile_off);
-  a.tile_eq = reinterpret_cast<uint32_t*>(ws + l.tile_eq);
+  a.tile_eqb = reinterpret_cast<uint32_t*>(ws + l.tile_eqb);
+  a.gap_idx = reinterpret_cast<uint32_t*>(ws + l.gap_idx);
+  a.gap_val = reinterpret_cast<float*>(ws + l.gap_val);
   a.hist = reinterpret_cast<uint32_t*>(ws + l.hist);
   a.state = reinterpret_cast<uint32_t*>(ws + l.state);
   a.count = count;

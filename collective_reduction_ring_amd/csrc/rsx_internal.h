@@ -171,8 +171,9 @@ hipError_t launch_list_f32h(int op, int world, const ListArgs& a, dim3 grid, hip
 // messages, rank 0 first, into a zeroed buffer.  Every kernel below covers
 // the W ranks of one call in one launch.  Ranks are cut into tiles of
 // kSpTile elements; the compaction writes a tile's selected entries in index
-// order starting at that tile's offset, so the combine finds the entries of
-// an output tile in every message from the same offsets, without a search.
+// order into a slot of its own, so the combine finds the entries of an output
+// tile in every rank's slot, without a search, and places them in the
+// message at offsets scanned in between.
 constexpr uint32_t kSpTile = 4096;      // elements per tile: 256 lanes x 4 dwordx4
 constexpr uint32_t kSpUnits = 4;        // dwordx4 per lane per tile
 constexpr uint32_t kSpBins = 2048;      // radix-select histogram bins (11-bit digits)
@@ -187,8 +188,12 @@ struct SparseArgs {
   const float* key[RSX_MAX_RANKS];   // top-K: the values selected on (grad, or grad + accum)
   float* key_store[RSX_MAX_RANKS];   // top-K with accumulation: where grad + accum is kept
   uint32_t* nnz;                     // [W] message lengths
-  uint32_t* tile_off;                // [W][tiles + 1] per-tile counts, then offsets
-  uint32_t* tile_eq;                 // [W][tiles + 1] top-K: ties with the cut key, then their prefix
+  uint32_t* tile_cnt;                // [W][tiles + 1] per tile: entries sent for sure
+  uint32_t* tile_eqc;                // [W][tiles + 1] per tile: ties with the cut (top-K)
+  uint32_t* tile_off;                // [W][tiles + 1] per tile: offset in the message
+  uint32_t* tile_eqb;                // [W][tiles + 1] per tile: ties in earlier tiles
+  uint32_t* gap_idx;                 // [W][tiles][kSpTile] candidate entries, one slot per tile
+  float* gap_val;                    //   (tile-local index, value)
   uint32_t* hist;                    // [W][kSpBins]
   uint32_t* state;                   // [W][4]: cut key, ties still to take
   uint64_t count;                    // elements per rank

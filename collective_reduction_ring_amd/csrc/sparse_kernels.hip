@@ -19,15 +19,19 @@
 //             a histogram of the next digit among the keys that match the
 //             digits chosen so far, then the digit at which the K-th largest
 //             key lies (top-K only)
-//   count     per tile: entries to send (threshold), or keys above the cut
-//             and keys equal to it (top-K)
-//   scan      per rank: tile offsets in the message, its length
-//   compact   per tile: the message entries in index order, the residual
-//   combine   per output tile: zero an LDS tile, add each rank's entries of
-//             the tile in rank order, store the tile to all W outputs
+//   compact   per tile: the candidate entries (to send: threshold; above
+//             or equal to the cut: top-K) in index order into the tile's own
+//             slot of the workspace, their counts, and the residual
+//   scan      per rank: each tile's offset in the message, its length
+//   combine   per output tile: zero an LDS tile; for each rank in order,
+//             place the tile's sent entries in the message and add them into
+//             the tile; store the tile to all W outputs
 //
 // Ties at the cut are taken in index order, as a stable sort from large to
-// small values would take them.  No kernel waits on another workgroup.
+// small values would take them.  Writing each tile's entries into a slot of
+// its own lets the compaction run before the offsets are known, so every
+// element is read once after the selection passes.  No kernel waits on
+// another workgroup.
 #include "mem.h"
 #include "rsx_internal.h"
 
@@ -262,9 +266,16 @@ __device__ __forceinline__ void load_selected_on(const SparseArgs& a, uint32_t r
     load_tile<ACC>(a.grad[r], ACC ? a.accum[r] : nullptr, base, n, x);
 }
 
-// Per tile: entries sent for sure, and ties with the cut.
+// Per tile: the candidate entries (sent for sure, or tied with the cut) in
+// index order, into the tile's own slot of kSpTile entries in the workspace,
+// their two counts, and, with an accumulation, the residual.  A tie's
+// residual is written as if it were not sent; the combine rewrites the ties
+// that are taken.  Residuals follow the page's arithmetic: the threshold
+// mode subtracts the thresholded array (which keeps a +-0 reaching the
+// threshold), the top-K mode subtracts the sent values added to zeros (so a
+// sent -0 leaves -0); a sent inf leaves NaN in both.
 template <int MODE, bool ACC>
-__global__ __launch_bounds__(kBlock) void sp_count_kernel(const SparseArgs a) {
+__global__ __launch_bounds__(kBlock) void sp_compact_kernel(const SparseArgs a) {
   __shared__ uint32_t scratch[kBlock / 64];
   uint32_t r, t;
   if (!rank_tile(a, r, t)) return;
@@ -273,23 +284,53 @@ __global__ __launch_bounds__(kBlock) void sp_count_kernel(const SparseArgs a) {
   float x[kSpUnits][4];
   load_selected_on<MODE, ACC>(a, r, base, n, x);
   const uint32_t cut = MODE == RSX_SPARSE_TOPK ? a.state[4 * r] : 0u;
-  uint32_t c = 0;
+  const uint64_t slot = (static_cast<uint64_t>(r) * a.tiles + t) * kSpTile;
+  uint32_t* gi = a.gap_idx + slot;
+  float* gv = a.gap_val + slot;
+  float res[kSpUnits][4];
+  uint32_t run = 0;  // packed counts of the earlier units of the tile
 #pragma unroll
-  for (int u = 0; u < static_cast<int>(kSpUnits); ++u)
+  for (int u = 0; u < static_cast<int>(kSpUnits); ++u) {
+    uint32_t f[4];
+    uint32_t c = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) c += flags<MODE>(x[u][j], in_tile(u, j, n), a.threshold, cut);
-  uint32_t total;
-  block_excl<kBlock / 64>(c, scratch, total);
+    for (int j = 0; j < 4; ++j) {
+      f[j] = flags<MODE>(x[u][j], in_tile(u, j, n), a.threshold, cut);
+      c += f[j];
+    }
+    uint32_t tot;
+    uint32_t pre = block_excl<kBlock / 64>(c, scratch, tot) + run;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t local = static_cast<uint32_t>(u) * kBlock * 4 + threadIdx.x * 4 + j;
+      if (f[j] != 0) {
+        const uint32_t at = (pre & 0xFFFFu) + (pre >> 16);  // entries before it in the tile
+        gi[at] = local;
+        gv[at] = x[u][j];
+      }
+      if constexpr (ACC) {
+        const float v = x[u][j];
+        if constexpr (MODE == RSX_SPARSE_THRESHOLD)
+          res[u][j] = fabsf(v) >= a.threshold ? v - v : v - 0.0f;
+        else
+          res[u][j] = (f[j] & 1u) ? v - (0.0f + v) : v - 0.0f;
+      }
+      pre += f[j];
+    }
+    run += tot;
+  }
+  if constexpr (ACC) store_tile(a.accum[r], base, n, res);
   if (threadIdx.x == 0) {
     const uint32_t i = r * (a.tiles + 1) + t;
-    a.tile_off[i] = total & 0xFFFFu;
-    a.tile_eq[i] = total >> 16;
+    a.tile_cnt[i] = run & 0xFFFFu;
+    a.tile_eqc[i] = run >> 16;
   }
 }
 
-// Per rank: exclusive prefix of the tile counts.  A tile's message offset is
-// the entries sent for sure before it plus the ties before it, up to the
-// number of ties to take.  The last slot and nnz[r] get the message length.
+// Per rank: exclusive prefixes of the tile counts.  A tile's message offset
+// is the entries sent for sure before it plus the ties before it, up to the
+// number of ties to take; tile_eqb holds the ties before it.  The last slot
+// and nnz[r] get the message length.
 template <int MODE>
 __global__ __launch_bounds__(kSpScanBlock) void sp_scan_kernel(const SparseArgs a) {
   constexpr uint32_t kPer = 4;
@@ -297,8 +338,10 @@ __global__ __launch_bounds__(kSpScanBlock) void sp_scan_kernel(const SparseArgs 
   __shared__ uint32_t scratch[kWaves];
   const uint32_t r = blockIdx.x;
   const uint32_t n = a.tiles;
-  uint32_t* cnt = a.tile_off + r * (n + 1);
-  uint32_t* eqc = a.tile_eq + r * (n + 1);
+  const uint32_t* cnt = a.tile_cnt + r * (n + 1);
+  const uint32_t* eqc = a.tile_eqc + r * (n + 1);
+  uint32_t* off = a.tile_off + r * (n + 1);
+  uint32_t* eqb = a.tile_eqb + r * (n + 1);
   const uint32_t need = MODE == RSX_SPARSE_TOPK ? a.state[4 * r + 1] : 0u;
   uint32_t carry_s = 0, carry_e = 0;
   for (uint32_t c0 = 0; c0 < n; c0 += kSpScanBlock * kPer) {
@@ -320,8 +363,8 @@ __global__ __launch_bounds__(kSpScanBlock) void sp_scan_kernel(const SparseArgs 
     for (uint32_t i = 0; i < kPer; ++i) {
       const uint32_t idx = c0 + threadIdx.x * kPer + i;
       if (idx < n) {
-        cnt[idx] = bs + min(be, need);
-        if constexpr (MODE == RSX_SPARSE_TOPK) eqc[idx] = be;
+        off[idx] = bs + min(be, need);
+        eqb[idx] = be;
       }
       bs += s[i];
       be += e[i];
@@ -331,80 +374,22 @@ __global__ __launch_bounds__(kSpScanBlock) void sp_scan_kernel(const SparseArgs 
   }
   if (threadIdx.x == 0) {
     const uint32_t len = carry_s + min(carry_e, need);
-    cnt[n] = len;
-    eqc[n] = carry_e;
+    off[n] = len;
+    eqb[n] = carry_e;
     a.nnz[r] = len;
   }
 }
 
-// Per tile: write the sent entries (zero-based index, value) in index order
-// from the tile's offset, and, with an accumulation, the residual: what was
-// not sent, in the page's arithmetic (so a sent inf leaves NaN).
+// Per output tile: a zeroed LDS tile; for each rank in order, the entries of
+// the tile's slot that are sent (all of them, except ties beyond the number
+// to take, taken in index order) are added into it, written to their place
+// in the rank's message, and, for a taken tie, its residual is rewritten as
+// sent; then the tile is stored to every rank's output.  One barrier per rank
+// keeps the adds in rank order; entries of one rank have distinct indices.
 template <int MODE, bool ACC>
-__global__ __launch_bounds__(kBlock) void sp_compact_kernel(const SparseArgs a) {
-  __shared__ uint32_t scratch[kBlock / 64];
-  uint32_t r, t;
-  if (!rank_tile(a, r, t)) return;
-  const uint64_t base = static_cast<uint64_t>(t) * kSpTile;
-  const uint32_t n = static_cast<uint32_t>(min<uint64_t>(kSpTile, a.count - base));
-  float x[kSpUnits][4];
-  load_selected_on<MODE, ACC>(a, r, base, n, x);
-  const uint32_t slot = r * (a.tiles + 1) + t;
-  const uint32_t off = a.tile_off[slot];
-  uint32_t cut = 0, ties = 0;  // ties this tile may still take
-  if constexpr (MODE == RSX_SPARSE_TOPK) {
-    cut = a.state[4 * r];
-    const uint32_t need = a.state[4 * r + 1];
-    const uint32_t before = a.tile_eq[slot];
-    ties = need > before ? need - before : 0u;
-  }
-  uint32_t* mi = a.msg_idx[r];
-  float* mv = a.msg_val[r];
-  float res[kSpUnits][4];
-  uint32_t run = 0;  // packed counts of the earlier units of the tile
-#pragma unroll
-  for (int u = 0; u < static_cast<int>(kSpUnits); ++u) {
-    uint32_t f[4];
-    uint32_t c = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f[j] = flags<MODE>(x[u][j], in_tile(u, j, n), a.threshold, cut);
-      c += f[j];
-    }
-    uint32_t tot;
-    uint32_t pre = block_excl<kBlock / 64>(c, scratch, tot) + run;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t sure_before = pre & 0xFFFFu, ties_before = pre >> 16;
-      const bool sent = (f[j] & 1u) || ((f[j] >> 16) && ties_before < ties);
-      const uint32_t pos = off + sure_before + min(ties_before, ties);
-      if (sent && pos < a.cap) {  // always below: the counts bound every position
-        mi[pos] = static_cast<uint32_t>(base) + static_cast<uint32_t>(u) * kBlock * 4 + threadIdx.x * 4 + j;
-        mv[pos] = x[u][j];
-      }
-      if constexpr (ACC) {
-        const float v = x[u][j];
-        if constexpr (MODE == RSX_SPARSE_THRESHOLD) {
-          // backup minus the thresholded array, which keeps a +-0 that
-          // reaches the threshold (it is only left out of the message)
-          res[u][j] = fabsf(v) >= a.threshold ? v - v : v - 0.0f;
-        } else {
-          // backup minus the sent values scatter-added into zeros
-          res[u][j] = sent ? v - (0.0f + v) : v - 0.0f;
-        }
-      }
-      pre += f[j];
-    }
-    run += tot;
-  }
-  if constexpr (ACC) store_tile(a.accum[r], base, n, res);
-}
-
-// Per output tile: zeroed LDS tile, then each rank's message entries of the
-// tile added in rank order (one barrier per rank; entries of one rank have
-// distinct indices), then the tile stored to every rank's output.
 __global__ __launch_bounds__(kBlock) void sp_combine_kernel(const SparseArgs a) {
   __shared__ float4 acc4[kSpTile / 4];
+  __shared__ uint32_t scratch[kBlock / 64];
   float* acc = reinterpret_cast<float*>(acc4);
   const uint32_t t = xcd_tile(blockIdx.x, gridDim.x);
   if (t >= a.tiles) return;
@@ -414,13 +399,47 @@ __global__ __launch_bounds__(kBlock) void sp_combine_kernel(const SparseArgs a) 
   for (int u = 0; u < static_cast<int>(kSpUnits); ++u) acc4[u * kBlock + threadIdx.x] = make_float4(0.f, 0.f, 0.f, 0.f);
   __syncthreads();
   for (uint32_t r = 0; r < a.world; ++r) {
-    const uint32_t* off = a.tile_off + r * (a.tiles + 1);
-    const uint32_t lo = off[t], hi = min(off[t + 1], a.cap);
-    const uint32_t* mi = a.msg_idx[r];
-    const float* mv = a.msg_val[r];
-    for (uint32_t e = lo + threadIdx.x; e < hi; e += kBlock) {
-      const uint32_t i = mi[e] - static_cast<uint32_t>(base);
-      if (i < kSpTile) acc[i] = acc[i] + mv[e];
+    const uint32_t i = r * (a.tiles + 1) + t;
+    const uint32_t c = min(a.tile_cnt[i] + a.tile_eqc[i], n);
+    const uint32_t off = a.tile_off[i];
+    uint32_t cut = 0, ties = 0;
+    if constexpr (MODE == RSX_SPARSE_TOPK) {
+      cut = a.state[4 * r];
+      const uint32_t need = a.state[4 * r + 1];
+      const uint32_t before = a.tile_eqb[i];
+      ties = need > before ? need - before : 0u;
+    }
+    const uint64_t slot = (static_cast<uint64_t>(r) * a.tiles + t) * kSpTile;
+    const uint32_t* gi = a.gap_idx + slot;
+    const float* gv = a.gap_val + slot;
+    uint32_t* mi = a.msg_idx[r];
+    float* mv = a.msg_val[r];
+    uint32_t run = 0;
+    for (uint32_t c0 = 0; c0 < c; c0 += kBlock) {
+      const uint32_t e = c0 + threadIdx.x;
+      const bool valid = e < c;
+      const uint32_t local = valid ? min(gi[e], kSpTile - 1) : 0u;
+      const float v = valid ? gv[e] : 0.0f;
+      uint32_t f = 0;
+      if (valid) {
+        if constexpr (MODE == RSX_SPARSE_TOPK)
+          f = order_key(v) == cut ? 0x10000u : 1u;
+        else
+          f = 1u;
+      }
+      uint32_t tot;
+      const uint32_t pre = block_excl<kBlock / 64>(f, scratch, tot) + run;
+      const uint32_t sure_before = pre & 0xFFFFu, ties_before = pre >> 16;
+      const bool sent = (f & 1u) || ((f >> 16) && ties_before < ties);
+      const uint32_t pos = off + sure_before + min(ties_before, ties);
+      if (sent && pos < a.cap) {  // always below: the counts bound every position
+        mi[pos] = static_cast<uint32_t>(base) + local;
+        mv[pos] = v;
+        acc[local] = acc[local] + v;
+        if constexpr (MODE == RSX_SPARSE_TOPK && ACC)
+          if (f >> 16) a.accum[r][base + local] = v - (0.0f + v);
+      }
+      run += tot;
     }
     __syncthreads();
   }
@@ -460,10 +479,9 @@ hipError_t launch_mode(const SparseArgs& a, hipStream_t s) {
     if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_pick_kernel<2>), a.world, kBlock);
   }
   const uint64_t rt = xcd_grid(static_cast<uint64_t>(a.world) * a.tiles);
-  if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_count_kernel<MODE, ACC>), rt, kBlock);
-  if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_scan_kernel<MODE>), a.world, kSpScanBlock);
   if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_compact_kernel<MODE, ACC>), rt, kBlock);
-  if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_combine_kernel), xcd_grid(a.tiles), kBlock);
+  if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_scan_kernel<MODE>), a.world, kSpScanBlock);
+  if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_combine_kernel<MODE, ACC>), xcd_grid(a.tiles), kBlock);
   return e;
 }
 

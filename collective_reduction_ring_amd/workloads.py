@@ -161,6 +161,29 @@ def fused_tensors(world: int = 4, sizes: np.ndarray | None = None) -> list[list[
     return out
 
 
+# ------------------------------------------------ sparsified all-reduce --
+# Gradients of the reduce-scatter headline's shape (W = 8, 64 Mi fp32 per
+# rank, N(0, 1e-3)) with an error-feedback residual of the same spread; top-K
+# keeps 1 % of the entries, the threshold about 1 % (|g + acc| >= 3.6e-3 for
+# g + acc ~ N(0, 1.41e-3)).  The pages give no sizes for this path.
+SPARSE_CFG = 6
+SPARSE_WORLD = 8
+SPARSE_N = 67_108_864
+SPARSE_TOPK_FRACTION = 0.01
+SPARSE_THRESHOLD = 3.6e-3
+
+
+def sparse_inputs(n: int = SPARSE_N, world: int = SPARSE_WORLD):
+    """(grads, accums): per rank N(0, 1e-3) fp32 from (6, r) and (6, 100 + r)."""
+    def one(seed):
+        return rng_for(SPARSE_CFG, seed).standard_normal(n, dtype=np.float32) * np.float32(1e-3)
+    workers = max(1, min(2 * world, 16, os.cpu_count() or 1))
+    with ThreadPoolExecutor(workers) as ex:
+        grads = list(ex.map(one, range(world)))
+        accums = list(ex.map(one, range(100, 100 + world)))
+    return grads, accums
+
+
 def sweep_inputs(kib: int, world: int = 4) -> list[np.ndarray]:
     """Sweep point of ``kib`` KiB of fp32 per rank, N(0,1)."""
     n = kib * 1024 // 4

@@ -204,9 +204,10 @@ typedef enum {
 size_t rsx_sparse_topk_count(size_t count, float fraction);
 
 /*
- * Bytes of device workspace rsx_sparse_all_reduce needs for these sizes
- * (per-tile offsets, radix histograms and, for RSX_SPARSE_TOPK with an
- * accumulation, a copy of grad + accum).  0 for invalid arguments.
+ * Bytes of device workspace rsx_sparse_all_reduce needs for these sizes:
+ * per-tile counts and offsets, radix histograms, 8 bytes per element per
+ * rank of per-tile candidate slots and, for RSX_SPARSE_TOPK with an
+ * accumulation, 4 more (a copy of grad + accum).  0 for invalid arguments.
  */
 size_t rsx_sparse_workspace_size(int nranks, size_t count, rsx_sparse_mode_t mode, int has_accum);
 
@@ -242,8 +243,8 @@ size_t rsx_sparse_workspace_size(int nranks, size_t count, rsx_sparse_mode_t mod
  * Buffers other than outs[r] == grads[r] must not overlap (grads may overlap
  * each other): RSX_ERR_ALIASING.  Invalid sizes, pointers, alignment, mode or
  * capacity: RSX_ERR_INVALID_ARGUMENT; count > UINT32_MAX: RSX_ERR_UNSUPPORTED.
- * Validation precedes every HIP call.  Enqueues about 6 kernels (threshold)
- * or 12 (top-K) on `stream`; allocates nothing and does not synchronise.
+ * Validation precedes every HIP call.  Enqueues 4 kernels (threshold) or 10
+ * (top-K) on `stream`; allocates nothing and does not synchronise.
  */
 rsx_status_t rsx_sparse_all_reduce(const float* const* grads, float* const* accums,
                                    float* const* outs, int nranks, size_t count,
