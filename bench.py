@@ -304,6 +304,53 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
             st.update(k=plan.k, nnz_rank0=nnz[0], nnz_total=sum(nnz), params=kw)
             res[mode] = st
         return res
+    if name == "overlap":
+        # bucketed all-reduce beside a stand-in backward pass: per bucket, one
+        # fp32 matmul on the main stream, then that bucket's all-reduce
+        w = wl.WORKLOADS[3]
+        world, n, bucket = w.world, w.n, w.extra["bucket_elems"]
+        log("generating bf16 inputs")
+        xs = wl.rank_inputs(3)
+        _, dev = _arena(torch, torch.bfloat16, world, n)
+        for d, x in zip(dev, xs):
+            d.copy_(torch.from_numpy(x.view(np.int16)).view(torch.bfloat16))
+        del xs
+        _, out = _arena(torch, torch.bfloat16, world, n)
+        plan = rsx.BucketedAllReduce(dev, out, bucket, "avg")
+        gen = torch.Generator(device="cuda:0")
+        gen.manual_seed(3)
+        m = 1536
+        a = torch.randn(m, m, device="cuda:0", generator=gen)
+        c = torch.empty(m, m, device="cuda:0")
+
+        def compute(b):
+            torch.mm(a, a, out=c)
+
+        def serial():
+            for b in range(len(plan)):
+                compute(b)
+                plan.plans[b]()
+
+        def overlapped():
+            for b in range(len(plan)):
+                compute(b)
+                plan.ready(b)
+            plan.wait()
+
+        def compute_only():
+            for b in range(len(plan)):
+                compute(b)
+        nb = 2 * world * n * 2
+        res = {"workload": f"bucketed all-reduce avg bf16, W=8, 134,217,728/rank, {len(plan)} buckets; "
+                           f"per bucket one {m}x{m}x{m} fp32 matmul on the main stream first",
+               "compute_only": _stat(time_launches(compute_only, reps // 4 or 1, warm, torch), 0),
+               "all_reduce_only": _stat(time_launches(plan, reps // 4 or 1, warm, torch), nb),
+               "serial_one_stream": _stat(time_launches(serial, reps // 4 or 1, warm, torch), nb),
+               "overlapped_side_stream": _stat(time_launches(overlapped, reps // 4 or 1, warm, torch), nb)}
+        for k in ("compute_only",):
+            for f in ("GBps", "pct_of_peak_hbm", "bytes"):
+                res[k].pop(f)
+        return res
     if name == "dtypes":
         world, rank_bytes = 8, 256 * 2 ** 20
         arena_in = torch.empty(world * rank_bytes, dtype=torch.uint8, device="cuda:0")
@@ -345,7 +392,7 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--workload", default="rs_w8_f32",
                     choices=("rs_w8_f32", "small", "bf16_bucketed", "int32_w16", "fused", "sweep",
-                             "sparse", "dtypes", "ceilings"),
+                             "sparse", "dtypes", "overlap", "ceilings"),
                     help="rs_w8_f32 (default) is the headline line; the others print timings only")
     args = ap.parse_args()
 

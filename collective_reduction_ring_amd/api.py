@@ -189,6 +189,55 @@ def all_reduce_bucketed(inputs, outputs=None, bucket_elems: int = 13_107_200, op
                   wire)(stream)
 
 
+class BucketedAllReduce:
+    """Bucketed all-reduce that overlaps with whatever produces the gradients
+    ("Distributed primitives", In practice: the gradient is all-reduced in
+    buckets on a separate stream while the backward pass goes on).
+
+    Consecutive buckets of ``bucket_elems`` elements, each its own all-reduce
+    (its own segments), as ``all_reduce_bucketed``.  ``ready(b)`` is called
+    by the producer once bucket b's inputs are enqueued on its stream: it
+    records an event there, makes the reduction stream wait for it and
+    enqueues bucket b's all-reduce on the reduction stream, so the producer's
+    later work and the reduction run side by side.  ``wait()`` makes a stream
+    wait for every enqueued reduction.  The reduction stream is created here
+    with the default priority unless one is given.
+    """
+
+    def __init__(self, inputs, outputs=None, bucket_elems: int = 13_107_200, op: str = "sum",
+                 algo: str = "ring", wire: str | None = None, stream=None):
+        if bucket_elems <= 0:
+            raise ValueError("bucket_elems must be positive")
+        outputs = inputs if outputs is None else outputs
+        n = inputs[0].numel()
+        self.bounds = [(b0, min(b0 + bucket_elems, n)) for b0 in range(0, n, bucket_elems)]
+        self.plans = [AllReduce([t[b0:b1] for t in inputs], [t[b0:b1] for t in outputs], op, algo, wire)
+                      for b0, b1 in self.bounds]
+        self.device = inputs[0].device
+        self.stream = stream if stream is not None else torch.cuda.Stream(device=self.device)
+        self.events = [torch.cuda.Event() for _ in self.plans]
+
+    def __len__(self) -> int:
+        return len(self.plans)
+
+    def ready(self, b: int, stream=None) -> None:
+        """Bucket b's inputs are enqueued on `stream` (default: current): reduce it on the side."""
+        src = torch.cuda.current_stream(self.device) if stream is None else stream
+        self.events[b].record(src)
+        self.stream.wait_event(self.events[b])
+        self.plans[b](self.stream)
+
+    def wait(self, stream=None) -> None:
+        """Make `stream` (default: current) wait for every reduction enqueued so far."""
+        dst = torch.cuda.current_stream(self.device) if stream is None else stream
+        dst.wait_stream(self.stream)
+
+    def __call__(self, stream=None) -> None:
+        """Every bucket at once, on `stream` (no overlap): the serial reference."""
+        for p in self.plans:
+            p(stream)
+
+
 class _FuseCopy:
     """A prepared pack (tensors -> fused) or unpack (fused -> tensors)."""
 

@@ -540,6 +540,34 @@ def test_full_c3_bf16_bucketed_avg():
     say(f"bf16 exact fraction {stats[0]['exact'] / stats[0]['n']:.6f}")
 
 
+@pytest.mark.parametrize("dtype,op", [("bf16", "avg"), ("f32", "sum")])
+def test_bucket_overlap_on_a_side_stream(dtype, op):
+    # The producer writes bucket b only after some unrelated work on its
+    # stream and then calls ready(b); the inputs hold junk before that, so a
+    # reduction that did not wait for the producer's event would show.
+    w, bucket = 4, 3 * 4096 + 40
+    n = 3 * bucket + 1000
+    xs = inputs(40, w, n, dtype)
+    staged = [to_dev(x, dtype) for x in xs]
+    ins = [empty(n, dtype, fill=0x7F7F) for _ in range(w)]
+    outs = [empty(n, dtype, fill=0x55) for _ in range(w)]
+    plan = rsx.BucketedAllReduce(ins, outs, bucket, op)
+    assert plan.stream != torch.cuda.current_stream() and len(plan) == 4
+    a = torch.randn(1024, 1024, device="cuda:0")
+    say(f"bucket overlap dtype={dtype} op={op} buckets={len(plan)}")
+    for b, (b0, b1) in enumerate(plan.bounds):
+        for _ in range(4):
+            a = torch.mm(a, a) * 1e-3         # producer busy before bucket b exists
+        for r in range(w):
+            ins[r][b0:b1].copy_(staged[r][b0:b1])
+        plan.ready(b)
+    plan.wait()
+    torch.cuda.synchronize()
+    want = oracle.bucketed_all_reduce(xs, bucket, op, dtype)
+    for r in range(w):
+        assert_parity(to_host(outs[r], dtype), want[r], dtype, f"rank {r}")
+
+
 def test_full_c5_fused_200_tensors():
     w = 4
     sizes = wl.fused_sizes()
