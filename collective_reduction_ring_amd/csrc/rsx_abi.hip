@@ -269,14 +269,12 @@ bool list_aliasing_ok(std::vector<Span>& sends, std::vector<Span>& recvs) {
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // Workspace of the sparsified all-reduce: per-tile counts and offsets,
-// radix histograms, selection state, one slot of kSpTile candidate entries
-// per tile, and (top-K with an accumulation) the values grad + accum that
-// the selection passes read again.  Each region starts on a 256-byte
-// boundary.
+// radix histograms, selection state, and one slot of kSpTile entries per
+// tile.  Each region starts on a 256-byte boundary.
 constexpr size_t kWsAlign = 256;
 size_t ws_align(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 struct SparseLayout {
-  size_t tile_cnt, tile_eqc, tile_off, tile_eqb, hist, state, gap_idx, gap_val, keys, total;
+  size_t tile_slot, tile_cnt, tile_eqc, tile_off, tile_eqb, hist, state, gap_idx, gap_val, total;
   uint32_t tiles;
 };
 bool sparse_layout(int w, size_t count, int mode, bool accum, SparseLayout* l) {
@@ -288,6 +286,8 @@ bool sparse_layout(int w, size_t count, int mode, bool accum, SparseLayout* l) {
   const size_t tile_bytes = ws_align(ws * (l->tiles + 1) * 4);
   const size_t slot_bytes = ws_align(ws * l->tiles * kSpTile * 4);
   size_t off = 0;
+  l->tile_slot = off;
+  off += tile_bytes;
   l->tile_cnt = off;
   off += tile_bytes;
   l->tile_eqc = off;
@@ -304,8 +304,7 @@ bool sparse_layout(int w, size_t count, int mode, bool accum, SparseLayout* l) {
   off += ws_align(ws * kSpBins * 4);
   l->state = off;
   off += ws_align(ws * 16);
-  l->keys = off;
-  if (mode == RSX_SPARSE_TOPK && accum) off += ws_align(ws * count * 4);
+  (void)accum;  // the slots hold everything either mode keeps
   l->total = off;
   return true;
 }
@@ -700,14 +699,9 @@ rsx_status_t rsx_sparse_all_reduce(const float* const* grads, float* const* accu
     a.out[r] = outs[r];
     a.msg_idx[r] = msg_idx[r];
     a.msg_val[r] = msg_val[r];
-    if (mode == RSX_SPARSE_TOPK && has_acc) {
-      a.key_store[r] = reinterpret_cast<float*>(ws + l.keys) + static_cast<size_t>(r) * count;
-      a.key[r] = a.key_store[r];
-    } else {
-      a.key[r] = grads[r];
-    }
   }
   a.nnz = nnz;
+  a.tile_slot = reinterpret_cast<uint32_t*>(ws + l.tile_slot);
   a.tile_cnt = reinterpret_cast<uint32_t*>(ws + l.tile_cnt);
   a.tile_eqc = reinterpret_cast<uint32_t*>(ws + l.tile_eqc);
   a.tile_off = reinterpret_cast<uint32_t*>(ws + l.tile_off);
@@ -722,11 +716,6 @@ rsx_status_t rsx_sparse_all_reduce(const float* const* grads, float* const* accu
   a.k = mode == RSX_SPARSE_TOPK ? static_cast<uint32_t>(k) : 0u;
   a.cap = static_cast<uint32_t>(sent_max);
   a.threshold = threshold;
-  // About 2048 histogram workgroups in all (8 per CU), each over whole tiles.
-  uint32_t groups = std::max<uint32_t>(1, 2048u / static_cast<uint32_t>(nranks));
-  groups = std::min<uint32_t>(groups, l.tiles);
-  a.hist_chunk = (l.tiles + groups - 1) / groups;
-  a.hist_groups = (l.tiles + a.hist_chunk - 1) / a.hist_chunk;
   return hip_status(launch_sparse(a, mode, has_acc, stream));
 }
 

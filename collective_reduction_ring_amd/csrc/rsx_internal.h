@@ -185,15 +185,14 @@ struct SparseArgs {
   float* out[RSX_MAX_RANKS];
   uint32_t* msg_idx[RSX_MAX_RANKS];
   float* msg_val[RSX_MAX_RANKS];
-  const float* key[RSX_MAX_RANKS];   // top-K: the values selected on (grad, or grad + accum)
-  float* key_store[RSX_MAX_RANKS];   // top-K with accumulation: where grad + accum is kept
   uint32_t* nnz;                     // [W] message lengths
+  uint32_t* tile_slot;               // [W][tiles + 1] per tile: entries in its slot
   uint32_t* tile_cnt;                // [W][tiles + 1] per tile: entries sent for sure
   uint32_t* tile_eqc;                // [W][tiles + 1] per tile: ties with the cut (top-K)
   uint32_t* tile_off;                // [W][tiles + 1] per tile: offset in the message
   uint32_t* tile_eqb;                // [W][tiles + 1] per tile: ties in earlier tiles
-  uint32_t* gap_idx;                 // [W][tiles][kSpTile] candidate entries, one slot per tile
-  float* gap_val;                    //   (tile-local index, value)
+  uint32_t* gap_idx;                 // [W][tiles][kSpTile] one slot of entries per tile:
+  float* gap_val;                    //   (tile-local index, g value)
   uint32_t* hist;                    // [W][kSpBins]
   uint32_t* state;                   // [W][4]: cut key, ties still to take
   uint64_t count;                    // elements per rank

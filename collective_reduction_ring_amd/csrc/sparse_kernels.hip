@@ -12,26 +12,32 @@
 // combine kernel reading them.  The page sorts all values to find the top K;
 // only the set matters to the result (message entries of one rank have
 // distinct indices, so their order does not change any sum), so the K-th
-// largest value is found by a radix select instead:
+// largest value is found by a radix select on an order-preserving key
+// (digits of 11, 11 and 10 bits) instead.  Ranks are cut into tiles of 4096
+// elements, and each tile owns a slot of 4096 entries in the workspace.
 //
-//   init      zero the histograms; the selection state of every rank
-//   hist/pick three passes (11, 11 and 10 bits of an order-preserving key):
-//             a histogram of the next digit among the keys that match the
-//             digits chosen so far, then the digit at which the K-th largest
-//             key lies (top-K only)
-//   compact   per tile: the candidate entries (to send: threshold; above
-//             or equal to the cut: top-K) in index order into the tile's own
-//             slot of the workspace, their counts, and the residual
-//   scan      per rank: each tile's offset in the message, its length
-//   combine   per output tile: zero an LDS tile; for each rank in order,
-//             place the tile's sent entries in the message and add them into
-//             the tile; store the tile to all W outputs
+//   threshold:  compact  (every element) entries to send, in index order,
+//                        into the tile's slot; the residual
+//   top-K:      hist0    (every element) top-digit histogram; g = grad + acc
+//                        into the accumulation buffer
+//               select1  (every element) every element at or above the
+//                        top digit's cut bin into the tile's slot, in index
+//                        order
+//               hist1/2  (slots) middle- and low-digit histograms
+//               pick     after each histogram: the digit of the K-th key
+//               count    (slots) per tile, candidates above / equal to the cut
+//   both:       scan     per rank: each tile's offset in the message
+//               combine  per output tile: for each rank in order, its sent
+//                        entries into the message and into an LDS tile (top-K
+//                        also rewrites their residuals); the tile to all W
+//                        outputs
 //
 // Ties at the cut are taken in index order, as a stable sort from large to
-// small values would take them.  Writing each tile's entries into a slot of
-// its own lets the compaction run before the offsets are known, so every
-// element is read once after the selection passes.  No kernel waits on
-// another workgroup.
+// small values would take them.  A slot per tile lets a tile write its
+// entries before any offset is known; after the selection only slots are
+// read.  No kernel waits on another workgroup.
+#include <algorithm>
+
 #include "mem.h"
 #include "rsx_internal.h"
 
@@ -39,6 +45,7 @@ namespace rsx {
 namespace {
 
 constexpr uint32_t kSpLaneElems = kSpUnits * 4;  // 16 elements per lane per tile
+constexpr uint32_t kSpWalkGroups = 2048;          // workgroups of the tile-walking kernels
 static_assert(kSpLaneElems * kBlock == kSpTile, "tile = 256 lanes x 16 elements");
 
 // Order-preserving key of an fp32 value for the top-K cut: a larger value has
@@ -81,6 +88,36 @@ __device__ __forceinline__ uint32_t block_excl(uint32_t v, uint32_t* scratch, ui
   return before + inc - v;
 }
 
+// 64-bit versions, for four 16-bit counts scanned at once.
+__device__ __forceinline__ uint64_t wave_incl64(uint64_t v) {
+  const uint32_t lane = threadIdx.x & 63u;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t lo = __shfl_up(static_cast<uint32_t>(v), d, 64);
+    const uint32_t hi = __shfl_up(static_cast<uint32_t>(v >> 32), d, 64);
+    if (lane >= static_cast<uint32_t>(d)) v += (static_cast<uint64_t>(hi) << 32) | lo;
+  }
+  return v;
+}
+
+template <int NW>
+__device__ __forceinline__ uint64_t block_excl64(uint64_t v, uint64_t* scratch, uint64_t& total) {
+  const uint64_t inc = wave_incl64(v);
+  const uint32_t w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63u) == 63u) scratch[w] = inc;
+  __syncthreads();
+  uint64_t before = 0, sum = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const uint64_t s = scratch[i];
+    before += (static_cast<uint32_t>(i) < w) ? s : 0u;
+    sum += s;
+  }
+  __syncthreads();
+  total = sum;
+  return before + inc - v;
+}
+
 // The 16 values of this lane in tile `base` of a rank: x[u][j] is element
 // u*1024 + 4*lane + j of the tile.  With ACC, x = g + acc (one fp32 add, the
 // page's error feedback); lanes past the rank's end read zeros.
@@ -115,6 +152,42 @@ __device__ __forceinline__ void load_tile(const float* g, const float* acc, uint
   }
 }
 
+// The loads of one tile, issued ahead of their use: a workgroup that walks
+// several tiles issues tile t+1's loads before it works on tile t, so its
+// barriers do not leave the memory pipeline empty.
+template <bool ACC>
+struct TileLoad {
+  uint4 vg[kSpUnits], va[kSpUnits];
+  __device__ __forceinline__ void issue(const float* g, const float* acc, uint64_t base, uint32_t n) {
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(g + base, n * 4);
+#pragma unroll
+    for (int u = 0; u < static_cast<int>(kSpUnits); ++u)
+      vg[u] = load_stream(rg, threadIdx.x * 16, u * kBlock * 16);
+    if constexpr (ACC) {
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(acc + base, n * 4);
+#pragma unroll
+      for (int u = 0; u < static_cast<int>(kSpUnits); ++u)
+        va[u] = load_stream(ra, threadIdx.x * 16, u * kBlock * 16);
+    }
+  }
+  // x = g (+ acc), as load_tile gives it
+  __device__ __forceinline__ void values(float (&x)[kSpUnits][4]) const {
+#pragma unroll
+    for (int u = 0; u < static_cast<int>(kSpUnits); ++u) {
+      const uint32_t g4[4] = {vg[u].x, vg[u].y, vg[u].z, vg[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (ACC) {
+          const uint32_t a4[4] = {va[u].x, va[u].y, va[u].z, va[u].w};
+          x[u][j] = __uint_as_float(g4[j]) + __uint_as_float(a4[j]);
+        } else {
+          x[u][j] = __uint_as_float(g4[j]);
+        }
+      }
+    }
+  }
+};
+
 __device__ __forceinline__ void store_tile(float* dst, uint64_t base, uint32_t n,
                                            const float (&x)[kSpUnits][4]) {
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(dst + base, n * 4);
@@ -123,6 +196,11 @@ __device__ __forceinline__ void store_tile(float* dst, uint64_t base, uint32_t n
     store_b128<kStoreStream>(rd, threadIdx.x * 16, u * kBlock * 16,
                              make_uint4(__float_as_uint(x[u][0]), __float_as_uint(x[u][1]),
                                         __float_as_uint(x[u][2]), __float_as_uint(x[u][3])));
+}
+
+// Elements of tile t of a rank (kSpTile except in the last tile).
+__device__ __forceinline__ uint32_t tile_len(const SparseArgs& a, uint32_t t) {
+  return static_cast<uint32_t>(min<uint64_t>(kSpTile, a.count - static_cast<uint64_t>(t) * kSpTile));
 }
 
 // Element u*1024 + 4*lane + j of a tile lies inside the rank when below n.
@@ -140,11 +218,18 @@ struct Digit {
 
 // ----------------------------------------------------------------- kernels
 
-// Zero every rank's histogram; selection state = (cut key 0, K ties to
-// find).  K = 0 selects nothing: the cut key is above every key.
+// Per rank: zero the histogram and the per-tile counts; selection state =
+// (cut key 0, K still to find).  K = 0 selects nothing: the cut key is then
+// above every key.
 __global__ __launch_bounds__(kBlock) void sp_init_kernel(const SparseArgs a) {
   const uint32_t r = blockIdx.x;
   for (uint32_t i = threadIdx.x; i < kSpBins; i += kBlock) a.hist[r * kSpBins + i] = 0;
+  const uint32_t nt = a.tiles + 1;
+  for (uint32_t i = threadIdx.x; i < nt; i += kBlock) {
+    a.tile_slot[r * nt + i] = 0;
+    a.tile_cnt[r * nt + i] = 0;
+    a.tile_eqc[r * nt + i] = 0;
+  }
   if (threadIdx.x == 0) {
     uint32_t* st = a.state + 4 * r;
     st[0] = a.k == 0 ? 0xFFFFFFFFu : 0u;
@@ -154,44 +239,136 @@ __global__ __launch_bounds__(kBlock) void sp_init_kernel(const SparseArgs a) {
   }
 }
 
-// Histogram of digit PASS among the keys whose higher digits equal the cut
-// chosen so far.  hist_groups workgroups per rank, each over hist_chunk
-// consecutive tiles.  Pass 0 with an accumulation also stores g + acc, the
-// values every later pass selects on.
-template <int PASS, bool ACC>
-__global__ __launch_bounds__(kBlock) void sp_hist_kernel(const SparseArgs a) {
+// Workgroup-local histogram -> the rank's histogram in HBM.
+template <uint32_t BINS>
+__device__ __forceinline__ void merge_hist(const uint32_t* h, uint32_t* gh) {
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < BINS; i += kBlock)
+    if (h[i] != 0) atomicAdd(&gh[i], h[i]);
+}
+
+__device__ __forceinline__ void zero_hist(uint32_t* h) {
+  for (uint32_t i = threadIdx.x; i < kSpBins; i += kBlock) h[i] = 0;
+  __syncthreads();
+}
+
+// Top-K pass 0, over every element: histogram of the top digit.  With an
+// accumulation it also forms g = grad + acc and stores it in the
+// accumulation buffer, where it is at once the value every later kernel
+// selects on and the residual of every entry that is not sent (g - 0 = g);
+// the combine rewrites the residual of the entries that are.
+template <bool ACC>
+__global__ __launch_bounds__(kBlock) void sp_hist0_kernel(const SparseArgs a) {
+  using Dg = Digit<0>;
+  __shared__ uint32_t h[kSpBins];
+  const uint32_t r = blockIdx.x / a.hist_groups;
+  const uint32_t grp = blockIdx.x - r * a.hist_groups;
+  zero_hist(h);
+  const uint32_t t0 = grp * a.hist_chunk;
+  const uint32_t t1 = min(a.tiles, t0 + a.hist_chunk);
+  TileLoad<ACC> ld;
+  if (t0 < t1) ld.issue(a.grad[r], a.accum[r], static_cast<uint64_t>(t0) * kSpTile, tile_len(a, t0));
+  for (uint32_t t = t0; t < t1; ++t) {
+    const uint64_t base = static_cast<uint64_t>(t) * kSpTile;
+    const uint32_t n = tile_len(a, t);
+    float x[kSpUnits][4];
+    ld.values(x);
+    if (t + 1 < t1) ld.issue(a.grad[r], a.accum[r], base + kSpTile, tile_len(a, t + 1));
+    if constexpr (ACC) store_tile(a.accum[r], base, n, x);
+    if (a.k == 0) continue;  // only the residual is needed
+#pragma unroll
+    for (int u = 0; u < static_cast<int>(kSpUnits); ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (in_tile(u, j, n)) atomicAdd(&h[order_key(x[u][j]) >> Dg::kShift], 1u);
+  }
+  if (a.k != 0) merge_hist<Dg::kBins>(h, a.hist + r * kSpBins);
+}
+
+// Copy this tile's flagged elements, in index order, to its slot; returns
+// how many there are.  Element u*1024 + 4*lane + j comes after every element
+// of units < u, so the four units' counts (at most 1024 each) are scanned at
+// once as 16-bit fields of one 64-bit value.
+__device__ __forceinline__ uint32_t compact_to_slot(const SparseArgs& a, uint64_t slot,
+                                                    const uint32_t (&f)[kSpUnits][4],
+                                                    const float (&x)[kSpUnits][4], uint64_t* scratch) {
+  uint64_t c = 0;
+#pragma unroll
+  for (int u = 0; u < static_cast<int>(kSpUnits); ++u)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c += static_cast<uint64_t>(f[u][j]) << (16 * u);
+  uint64_t tot;
+  const uint64_t pre = block_excl64<kBlock / 64>(c, scratch, tot);
+  uint32_t before = 0;  // entries of the earlier units
+#pragma unroll
+  for (int u = 0; u < static_cast<int>(kSpUnits); ++u) {
+    uint32_t at = before + static_cast<uint32_t>((pre >> (16 * u)) & 0xFFFFu);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (f[u][j]) {
+        a.gap_idx[slot + at] = static_cast<uint32_t>(u) * kBlock * 4 + threadIdx.x * 4 + j;
+        a.gap_val[slot + at] = x[u][j];
+      }
+      at += f[u][j];
+    }
+    before += static_cast<uint32_t>((tot >> (16 * u)) & 0xFFFFu);
+  }
+  return before;
+}
+
+// Rank and tile of workgroup b in a (rank, tile) grid; false past the end.
+__device__ __forceinline__ bool rank_tile(const SparseArgs& a, uint32_t& r, uint32_t& t) {
+  const uint32_t lin = xcd_tile(blockIdx.x, gridDim.x);
+  if (lin >= a.world * a.tiles) return false;
+  r = lin / a.tiles;
+  t = lin - r * a.tiles;
+  return true;
+}
+
+// Top-K, one workgroup per tile: every element whose top digit is at or
+// above the cut's top digit (all that can still be sent) copied in index
+// order into the tile's slot.  Later kernels read the slots only.
+template <bool ACC>
+__global__ __launch_bounds__(kBlock) void sp_select1_kernel(const SparseArgs a) {
+  __shared__ uint64_t scratch[kBlock / 64];
+  uint32_t r, t;
+  if (!rank_tile(a, r, t)) return;
+  const uint32_t prefix = a.state[4 * r];   // top digit of the cut, lower bits 0
+  const uint64_t base = static_cast<uint64_t>(t) * kSpTile;
+  const uint32_t n = tile_len(a, t);
+  float x[kSpUnits][4];
+  load_tile<false>(ACC ? a.accum[r] : a.grad[r], nullptr, base, n, x);
+  uint32_t f[kSpUnits][4];
+#pragma unroll
+  for (int u = 0; u < static_cast<int>(kSpUnits); ++u)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f[u][j] = (in_tile(u, j, n) && order_key(x[u][j]) >= prefix) ? 1u : 0u;
+  const uint64_t slot = (static_cast<uint64_t>(r) * a.tiles + t) * kSpTile;
+  const uint32_t cnt = compact_to_slot(a, slot, f, x, scratch);
+  if (threadIdx.x == 0) a.tile_slot[r * (a.tiles + 1) + t] = cnt;
+}
+
+// Top-K passes 1 and 2, over the slots: histogram of digit PASS among the
+// keys matching the cut's higher digits.
+template <int PASS>
+__global__ __launch_bounds__(kBlock) void sp_hist_slots_kernel(const SparseArgs a) {
   using Dg = Digit<PASS>;
   __shared__ uint32_t h[kSpBins];
   const uint32_t r = blockIdx.x / a.hist_groups;
   const uint32_t grp = blockIdx.x - r * a.hist_groups;
-  for (uint32_t i = threadIdx.x; i < kSpBins; i += kBlock) h[i] = 0;
-  __syncthreads();
-  const uint32_t prefix = PASS == 0 ? 0u : a.state[4 * r];
+  zero_hist(h);
+  const uint32_t prefix = a.state[4 * r];
   const uint32_t t0 = grp * a.hist_chunk;
   const uint32_t t1 = min(a.tiles, t0 + a.hist_chunk);
   for (uint32_t t = t0; t < t1; ++t) {
-    const uint64_t base = static_cast<uint64_t>(t) * kSpTile;
-    const uint32_t n = static_cast<uint32_t>(min<uint64_t>(kSpTile, a.count - base));
-    float x[kSpUnits][4];
-    if constexpr (PASS == 0 && ACC) {
-      load_tile<true>(a.grad[r], a.accum[r], base, n, x);
-      store_tile(a.key_store[r], base, n, x);
-    } else {
-      load_tile<false>(a.key[r], nullptr, base, n, x);
+    const uint32_t c = min(a.tile_slot[r * (a.tiles + 1) + t], kSpTile);
+    const float* gv = a.gap_val + (static_cast<uint64_t>(r) * a.tiles + t) * kSpTile;
+    for (uint32_t e = threadIdx.x; e < c; e += kBlock) {
+      const uint32_t k = order_key(gv[e]);
+      if ((k & Dg::kHigh) == prefix) atomicAdd(&h[(k >> Dg::kShift) & (Dg::kBins - 1)], 1u);
     }
-#pragma unroll
-    for (int u = 0; u < static_cast<int>(kSpUnits); ++u)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t k = order_key(x[u][j]);
-        if (in_tile(u, j, n) && (k & Dg::kHigh) == prefix)
-          atomicAdd(&h[(k >> Dg::kShift) & (Dg::kBins - 1)], 1u);
-      }
   }
-  __syncthreads();
-  uint32_t* gh = a.hist + r * kSpBins;
-  for (uint32_t i = threadIdx.x; i < Dg::kBins; i += kBlock)
-    if (h[i] != 0) atomicAdd(&gh[i], h[i]);
+  merge_hist<Dg::kBins>(h, a.hist + r * kSpBins);
 }
 
 // The digit at which the K-th largest key lies: walking the bins from the
@@ -234,96 +411,68 @@ __global__ __launch_bounds__(kBlock) void sp_pick_kernel(const SparseArgs a) {
   for (uint32_t i = 0; i < kPer; ++i) gh[top - i] = 0;
 }
 
-// Rank and tile of workgroup b in a (rank, tile) grid; false past the end.
-__device__ __forceinline__ bool rank_tile(const SparseArgs& a, uint32_t& r, uint32_t& t) {
-  const uint32_t lin = xcd_tile(blockIdx.x, gridDim.x);
-  if (lin >= a.world * a.tiles) return false;
-  r = lin / a.tiles;
-  t = lin - r * a.tiles;
-  return true;
+// Flags of a top-K candidate against the cut: 1 = above it (sent), 0x10000 =
+// equal to it (sent while ties are left, in index order), 0 = below.
+__device__ __forceinline__ uint32_t cut_flags(float v, uint32_t cut) {
+  const uint32_t k = order_key(v);
+  return k > cut ? 1u : (k == cut ? 0x10000u : 0u);
 }
 
-// Selection flags of one element: bit 0 = sent for sure (threshold mode:
-// |x| >= threshold and x != 0; top-K: key above the cut), bit 16 = key equal
-// to the cut (top-K; sent while ties are left, in index order).
-template <int MODE>
-__device__ __forceinline__ uint32_t flags(float x, bool valid, float thr, uint32_t cut) {
-  if (!valid) return 0;
-  if constexpr (MODE == RSX_SPARSE_THRESHOLD) {
-    return (fabsf(x) >= thr && x != 0.0f) ? 1u : 0u;
-  } else {
-    const uint32_t k = order_key(x);
-    return (k > cut ? 1u : 0u) | (k == cut ? 0x10000u : 0u);
+// Top-K, over the slots: per tile, the candidates above the cut and those
+// equal to it.
+__global__ __launch_bounds__(kBlock) void sp_slot_count_kernel(const SparseArgs a) {
+  __shared__ uint32_t scratch[kBlock / 64];
+  const uint32_t r = blockIdx.x / a.hist_groups;
+  const uint32_t grp = blockIdx.x - r * a.hist_groups;
+  const uint32_t cut = a.state[4 * r];
+  const uint32_t t0 = grp * a.hist_chunk;
+  const uint32_t t1 = min(a.tiles, t0 + a.hist_chunk);
+  for (uint32_t t = t0; t < t1; ++t) {
+    const uint32_t i = r * (a.tiles + 1) + t;
+    const uint32_t c = min(a.tile_slot[i], kSpTile);
+    const float* gv = a.gap_val + (static_cast<uint64_t>(r) * a.tiles + t) * kSpTile;
+    uint32_t f = 0;
+    for (uint32_t e = threadIdx.x; e < c; e += kBlock) f += cut_flags(gv[e], cut);
+    uint32_t tot;
+    block_excl<kBlock / 64>(f, scratch, tot);
+    if (threadIdx.x == 0) {
+      a.tile_cnt[i] = tot & 0xFFFFu;
+      a.tile_eqc[i] = tot >> 16;
+    }
   }
 }
 
-template <int MODE, bool ACC>
-__device__ __forceinline__ void load_selected_on(const SparseArgs& a, uint32_t r, uint64_t base, uint32_t n,
-                                                 float (&x)[kSpUnits][4]) {
-  if constexpr (MODE == RSX_SPARSE_TOPK)
-    load_tile<false>(a.key[r], nullptr, base, n, x);  // grad, or the stored grad + acc
-  else
-    load_tile<ACC>(a.grad[r], ACC ? a.accum[r] : nullptr, base, n, x);
-}
-
-// Per tile: the candidate entries (sent for sure, or tied with the cut) in
-// index order, into the tile's own slot of kSpTile entries in the workspace,
-// their two counts, and, with an accumulation, the residual.  A tie's
-// residual is written as if it were not sent; the combine rewrites the ties
-// that are taken.  Residuals follow the page's arithmetic: the threshold
-// mode subtracts the thresholded array (which keeps a +-0 reaching the
-// threshold), the top-K mode subtracts the sent values added to zeros (so a
-// sent -0 leaves -0); a sent inf leaves NaN in both.
-template <int MODE, bool ACC>
+// Threshold mode, over every element: per tile, the entries to send
+// (|g| >= threshold, g != 0) in index order into the tile's slot, their
+// count, and with an accumulation the final residual: g minus the
+// thresholded array, which keeps a +-0 reaching the threshold (a sent inf
+// leaves NaN).
+template <bool ACC>
 __global__ __launch_bounds__(kBlock) void sp_compact_kernel(const SparseArgs a) {
-  __shared__ uint32_t scratch[kBlock / 64];
+  __shared__ uint64_t scratch[kBlock / 64];
   uint32_t r, t;
   if (!rank_tile(a, r, t)) return;
   const uint64_t base = static_cast<uint64_t>(t) * kSpTile;
   const uint32_t n = static_cast<uint32_t>(min<uint64_t>(kSpTile, a.count - base));
   float x[kSpUnits][4];
-  load_selected_on<MODE, ACC>(a, r, base, n, x);
-  const uint32_t cut = MODE == RSX_SPARSE_TOPK ? a.state[4 * r] : 0u;
+  load_tile<ACC>(a.grad[r], ACC ? a.accum[r] : nullptr, base, n, x);
   const uint64_t slot = (static_cast<uint64_t>(r) * a.tiles + t) * kSpTile;
-  uint32_t* gi = a.gap_idx + slot;
-  float* gv = a.gap_val + slot;
+  uint32_t f[kSpUnits][4];
   float res[kSpUnits][4];
-  uint32_t run = 0;  // packed counts of the earlier units of the tile
 #pragma unroll
-  for (int u = 0; u < static_cast<int>(kSpUnits); ++u) {
-    uint32_t f[4];
-    uint32_t c = 0;
+  for (int u = 0; u < static_cast<int>(kSpUnits); ++u)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      f[j] = flags<MODE>(x[u][j], in_tile(u, j, n), a.threshold, cut);
-      c += f[j];
+      const float v = x[u][j];
+      f[u][j] = (in_tile(u, j, n) && fabsf(v) >= a.threshold && v != 0.0f) ? 1u : 0u;
+      if constexpr (ACC) res[u][j] = fabsf(v) >= a.threshold ? v - v : v - 0.0f;
     }
-    uint32_t tot;
-    uint32_t pre = block_excl<kBlock / 64>(c, scratch, tot) + run;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t local = static_cast<uint32_t>(u) * kBlock * 4 + threadIdx.x * 4 + j;
-      if (f[j] != 0) {
-        const uint32_t at = (pre & 0xFFFFu) + (pre >> 16);  // entries before it in the tile
-        gi[at] = local;
-        gv[at] = x[u][j];
-      }
-      if constexpr (ACC) {
-        const float v = x[u][j];
-        if constexpr (MODE == RSX_SPARSE_THRESHOLD)
-          res[u][j] = fabsf(v) >= a.threshold ? v - v : v - 0.0f;
-        else
-          res[u][j] = (f[j] & 1u) ? v - (0.0f + v) : v - 0.0f;
-      }
-      pre += f[j];
-    }
-    run += tot;
-  }
   if constexpr (ACC) store_tile(a.accum[r], base, n, res);
+  const uint32_t cnt = compact_to_slot(a, slot, f, x, scratch);
   if (threadIdx.x == 0) {
     const uint32_t i = r * (a.tiles + 1) + t;
-    a.tile_cnt[i] = run & 0xFFFFu;
-    a.tile_eqc[i] = run >> 16;
+    a.tile_slot[i] = cnt;
+    a.tile_cnt[i] = cnt;
   }
 }
 
@@ -381,78 +530,100 @@ __global__ __launch_bounds__(kSpScanBlock) void sp_scan_kernel(const SparseArgs 
 }
 
 // Per output tile: a zeroed LDS tile; for each rank in order, the entries of
-// the tile's slot that are sent (all of them, except ties beyond the number
-// to take, taken in index order) are added into it, written to their place
-// in the rank's message, and, for a taken tie, its residual is rewritten as
-// sent; then the tile is stored to every rank's output.  One barrier per rank
-// keeps the adds in rank order; entries of one rank have distinct indices.
+// the tile's slot that are sent (threshold: all of them; top-K: those above
+// the cut, and ties in index order while ties are left) are written to
+// their place in the rank's message and added into the tile, and with an
+// accumulation a sent top-K entry's residual becomes g - (0 + g); then the
+// tile is stored to every rank's output.  One barrier per rank keeps the
+// adds in rank order; entries of one rank have distinct indices.  Every
+// rank's counts are read at once, and the next rank's first entries are
+// loaded while this rank's are placed.
 template <int MODE, bool ACC>
 __global__ __launch_bounds__(kBlock) void sp_combine_kernel(const SparseArgs a) {
   __shared__ float4 acc4[kSpTile / 4];
+  __shared__ uint32_t meta[RSX_MAX_RANKS][4];  // entries, message offset, cut, ties to take
   __shared__ uint32_t scratch[kBlock / 64];
   float* acc = reinterpret_cast<float*>(acc4);
   const uint32_t t = xcd_tile(blockIdx.x, gridDim.x);
   if (t >= a.tiles) return;
   const uint64_t base = static_cast<uint64_t>(t) * kSpTile;
-  const uint32_t n = static_cast<uint32_t>(min<uint64_t>(kSpTile, a.count - base));
+  const uint32_t n = tile_len(a, t);
+  const uint32_t world = a.world;
+  const uint32_t tid = threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < static_cast<int>(kSpUnits); ++u) acc4[u * kBlock + threadIdx.x] = make_float4(0.f, 0.f, 0.f, 0.f);
-  __syncthreads();
-  for (uint32_t r = 0; r < a.world; ++r) {
-    const uint32_t i = r * (a.tiles + 1) + t;
-    const uint32_t c = min(a.tile_cnt[i] + a.tile_eqc[i], n);
-    const uint32_t off = a.tile_off[i];
-    uint32_t cut = 0, ties = 0;
+  for (int u = 0; u < static_cast<int>(kSpUnits); ++u) acc4[u * kBlock + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (tid < world) {
+    const uint32_t i = tid * (a.tiles + 1) + t;
+    meta[tid][0] = min(a.tile_slot[i], n);
+    meta[tid][1] = a.tile_off[i];
     if constexpr (MODE == RSX_SPARSE_TOPK) {
-      cut = a.state[4 * r];
-      const uint32_t need = a.state[4 * r + 1];
+      const uint32_t need = a.state[4 * tid + 1];
       const uint32_t before = a.tile_eqb[i];
-      ties = need > before ? need - before : 0u;
+      meta[tid][2] = a.state[4 * tid];
+      meta[tid][3] = need > before ? need - before : 0u;
+    } else {
+      meta[tid][2] = 0;
+      meta[tid][3] = 0;
     }
-    const uint64_t slot = (static_cast<uint64_t>(r) * a.tiles + t) * kSpTile;
-    const uint32_t* gi = a.gap_idx + slot;
-    const float* gv = a.gap_val + slot;
+  }
+  __syncthreads();
+
+  // Entry c0 + tid of rank r's slot (index clamped into the tile).
+  auto fetch = [&](uint32_t r, uint32_t c0, uint32_t& local, float& v) {
+    const uint32_t e = c0 + tid;
+    local = 0;
+    v = 0.0f;
+    if (e < meta[r][0]) {
+      const uint64_t slot = (static_cast<uint64_t>(r) * a.tiles + t) * kSpTile;
+      local = min(a.gap_idx[slot + e], kSpTile - 1);
+      v = a.gap_val[slot + e];
+    }
+  };
+  uint32_t nlocal;
+  float nv;
+  fetch(0, 0, nlocal, nv);
+  for (uint32_t r = 0; r < world; ++r) {
+    const uint32_t c = meta[r][0], off = meta[r][1], cut = meta[r][2], ties = meta[r][3];
+    uint32_t local = nlocal;
+    float v = nv;
+    if (r + 1 < world) fetch(r + 1, 0, nlocal, nv);
     uint32_t* mi = a.msg_idx[r];
     float* mv = a.msg_val[r];
-    uint32_t run = 0;
+    uint32_t run = 0;  // packed counts of the chunks before this one
     for (uint32_t c0 = 0; c0 < c; c0 += kBlock) {
-      const uint32_t e = c0 + threadIdx.x;
-      const bool valid = e < c;
-      const uint32_t local = valid ? min(gi[e], kSpTile - 1) : 0u;
-      const float v = valid ? gv[e] : 0.0f;
+      if (c0 != 0) fetch(r, c0, local, v);  // a slot with more than kBlock entries
       uint32_t f = 0;
-      if (valid) {
+      if (c0 + tid < c) {
         if constexpr (MODE == RSX_SPARSE_TOPK)
-          f = order_key(v) == cut ? 0x10000u : 1u;
+          f = cut_flags(v, cut);
         else
           f = 1u;
       }
       uint32_t tot;
-      const uint32_t pre = block_excl<kBlock / 64>(f, scratch, tot) + run;
-      const uint32_t sure_before = pre & 0xFFFFu, ties_before = pre >> 16;
+      const uint32_t p = block_excl<kBlock / 64>(f, scratch, tot) + run;
+      run += tot;
+      const uint32_t sure_before = p & 0xFFFFu, ties_before = p >> 16;
       const bool sent = (f & 1u) || ((f >> 16) && ties_before < ties);
       const uint32_t pos = off + sure_before + min(ties_before, ties);
       if (sent && pos < a.cap) {  // always below: the counts bound every position
         mi[pos] = static_cast<uint32_t>(base) + local;
         mv[pos] = v;
         acc[local] = acc[local] + v;
-        if constexpr (MODE == RSX_SPARSE_TOPK && ACC)
-          if (f >> 16) a.accum[r][base + local] = v - (0.0f + v);
+        if constexpr (MODE == RSX_SPARSE_TOPK && ACC) a.accum[r][base + local] = v - (0.0f + v);
       }
-      run += tot;
     }
     __syncthreads();
   }
   float x[kSpUnits][4];
 #pragma unroll
   for (int u = 0; u < static_cast<int>(kSpUnits); ++u) {
-    const float4 v = acc4[u * kBlock + threadIdx.x];
-    x[u][0] = v.x;
-    x[u][1] = v.y;
-    x[u][2] = v.z;
-    x[u][3] = v.w;
+    const float4 q = acc4[u * kBlock + tid];
+    x[u][0] = q.x;
+    x[u][1] = q.y;
+    x[u][2] = q.z;
+    x[u][3] = q.w;
   }
-  for (uint32_t r = 0; r < a.world; ++r) store_tile(a.out[r], base, n, x);
+  for (uint32_t r = 0; r < world; ++r) store_tile(a.out[r], base, n, x);
 }
 
 __global__ void sp_zero_nnz_kernel(uint32_t* nnz, int world) {
@@ -460,26 +631,36 @@ __global__ void sp_zero_nnz_kernel(uint32_t* nnz, int world) {
 }
 
 template <int MODE, bool ACC>
-hipError_t launch_mode(const SparseArgs& a, hipStream_t s) {
-  void* args[] = {const_cast<SparseArgs*>(&a)};
+hipError_t launch_mode(SparseArgs a, hipStream_t s) {
+  // Kernels that walk tiles: about 2048 workgroups in all (8 per CU), each
+  // over whole tiles of one rank.  Measured faster than a grid that fits
+  // the device in one resident round.
+  const uint32_t groups = std::max<uint32_t>(1, std::min<uint32_t>(kSpWalkGroups / a.world, a.tiles));
+  a.hist_chunk = (a.tiles + groups - 1) / groups;
+  a.hist_groups = (a.tiles + a.hist_chunk - 1) / a.hist_chunk;
+  void* args[] = {&a};
   auto go = [&](const void* fn, uint64_t grid, uint32_t block) {
     return hipLaunchKernel(fn, dim3(static_cast<uint32_t>(grid)), dim3(block), args, 0, s);
   };
-  hipError_t e = go(reinterpret_cast<const void*>(&sp_init_kernel), a.world, kBlock);
   const uint64_t hg = static_cast<uint64_t>(a.world) * a.hist_groups;
-  // Pass 0 also stores grad + accum for the later kernels, so it runs even
-  // when K = 0 leaves nothing to select.
-  if (MODE == RSX_SPARSE_TOPK && (a.k > 0 || ACC) && e == hipSuccess)
-    e = go(reinterpret_cast<const void*>(&sp_hist_kernel<0, ACC>), hg, kBlock);
-  if (MODE == RSX_SPARSE_TOPK && a.k > 0 && e == hipSuccess) {
-    if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_pick_kernel<0>), a.world, kBlock);
-    if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_hist_kernel<1, ACC>), hg, kBlock);
-    if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_pick_kernel<1>), a.world, kBlock);
-    if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_hist_kernel<2, ACC>), hg, kBlock);
-    if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_pick_kernel<2>), a.world, kBlock);
-  }
   const uint64_t rt = xcd_grid(static_cast<uint64_t>(a.world) * a.tiles);
-  if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_compact_kernel<MODE, ACC>), rt, kBlock);
+  hipError_t e = go(reinterpret_cast<const void*>(&sp_init_kernel), a.world, kBlock);
+  if constexpr (MODE == RSX_SPARSE_TOPK) {
+    // Pass 0 also leaves g in the accumulation buffer, so it runs even when
+    // K = 0 has nothing to select.
+    if ((a.k > 0 || ACC) && e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_hist0_kernel<ACC>), hg, kBlock);
+    if (a.k > 0) {
+      if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_pick_kernel<0>), a.world, kBlock);
+      if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_select1_kernel<ACC>), rt, kBlock);
+      if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_hist_slots_kernel<1>), hg, kBlock);
+      if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_pick_kernel<1>), a.world, kBlock);
+      if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_hist_slots_kernel<2>), hg, kBlock);
+      if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_pick_kernel<2>), a.world, kBlock);
+      if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_slot_count_kernel), hg, kBlock);
+    }
+  } else {
+    if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_compact_kernel<ACC>), rt, kBlock);
+  }
   if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_scan_kernel<MODE>), a.world, kSpScanBlock);
   if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_combine_kernel<MODE, ACC>), xcd_grid(a.tiles), kBlock);
   return e;
