@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "rsx_internal.h"
+#include "sparse_internal.h"
 
 namespace rsx {
 namespace {

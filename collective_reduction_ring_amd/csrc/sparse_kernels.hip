@@ -40,6 +40,7 @@
 
 #include "mem.h"
 #include "rsx_internal.h"
+#include "sparse_internal.h"
 
 namespace rsx {
 namespace {

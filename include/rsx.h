@@ -205,9 +205,10 @@ size_t rsx_sparse_topk_count(size_t count, float fraction);
 
 /*
  * Bytes of device workspace rsx_sparse_all_reduce needs for these sizes:
- * per-tile counts and offsets, radix histograms, 8 bytes per element per
- * rank of per-tile candidate slots and, for RSX_SPARSE_TOPK with an
- * accumulation, 4 more (a copy of grad + accum).  0 for invalid arguments.
+ * per-tile counts and offsets, radix histograms and 8 bytes per element per
+ * rank (rounded up to whole 4096-element tiles) of per-tile entry slots.
+ * The same for both modes and with or without an accumulation.  0 for
+ * invalid arguments.
  */
 size_t rsx_sparse_workspace_size(int nranks, size_t count, rsx_sparse_mode_t mode, int has_accum);
 
@@ -240,10 +241,14 @@ size_t rsx_sparse_workspace_size(int nranks, size_t count, rsx_sparse_mode_t mod
  *   rsx_sparse_workspace_size(...) bytes; its contents are scratch.
  * count <= UINT32_MAX (indices are uint32); k <= count.
  * count 0: nnz is zeroed and nothing else is touched.
- * Buffers other than outs[r] == grads[r] must not overlap (grads may overlap
- * each other): RSX_ERR_ALIASING.  Invalid sizes, pointers, alignment, mode or
+ * The outputs may overlap the gradients (they are written after every read
+ * of the gradients; e.g. outs[r] == grads[r]) and gradients may overlap each
+ * other; any other overlap among grads, accums, outs, messages, nnz and the
+ * workspace is RSX_ERR_ALIASING.  Invalid sizes, pointers, alignment, mode or
  * capacity: RSX_ERR_INVALID_ARGUMENT; count > UINT32_MAX: RSX_ERR_UNSUPPORTED.
- * Validation precedes every HIP call.  Enqueues 4 kernels (threshold) or 10
+ * With an accumulation, top-K first stores g in accums[r] and then rewrites
+ * the sent entries, so accums[r] must not be read by other work meanwhile.
+ * Validation precedes every HIP call.  Enqueues 4 kernels (threshold) or 11
  * (top-K) on `stream`; allocates nothing and does not synchronise.
  */
 rsx_status_t rsx_sparse_all_reduce(const float* const* grads, float* const* accums,
