@@ -351,6 +351,36 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
             for f in ("GBps", "pct_of_peak_hbm", "bytes"):
                 res[k].pop(f)
         return res
+    if name == "size_sweep":
+        # reduce-scatter and ring all-reduce, W = 8 fp32, 4 KiB .. 1 GiB per rank
+        world = 8
+        top = 2 ** 30 // 4
+        gen = torch.Generator(device="cuda:0")
+        gen.manual_seed(11)
+        ins_all = torch.randn(world * top, device="cuda:0", generator=gen) * 1e-3
+        outs_all = torch.empty(world * top, device="cuda:0")
+        res = {"workload": "reduce-scatter and ring all-reduce sum fp32, W=8, per-rank size sweep; "
+                           "below 64 MiB graph-timed device time (50 calls per graph), above HIP events per call"}
+        kib = 4
+        while kib * 1024 <= 2 ** 30:
+            n = kib * 1024 // 4
+            ins = [ins_all[r * n:(r + 1) * n] for r in range(world)]
+            seg = n // world
+            rs_out = [outs_all[k * seg:(k + 1) * seg] for k in range(world)]
+            ar_out = [outs_all[r * n:(r + 1) * n] for r in range(world)]
+            rs = rsx.ReduceScatter(ins, rs_out, "sum")
+            ar = rsx.AllReduce(ins, ar_out, "sum", "ring")
+            row = {}
+            for what, fn, nbytes in (("reduce_scatter", rs, world * n * 4 + world * seg * 4),
+                                     ("all_reduce", ar, 2 * world * n * 4)):
+                if kib * 1024 < 64 * 2 ** 20:
+                    us = graph_us_per_call(fn, 50, 20, torch)
+                else:
+                    us = statistics.median(time_launches(fn, max(5, reps // 4), warm, torch)) * 1e3
+                row[what] = {"us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+            res[f"{kib}KiB"] = row
+            kib *= 4
+        return res
     if name == "dtypes":
         world, rank_bytes = 8, 256 * 2 ** 20
         arena_in = torch.empty(world * rank_bytes, dtype=torch.uint8, device="cuda:0")
@@ -392,7 +422,7 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--workload", default="rs_w8_f32",
                     choices=("rs_w8_f32", "small", "bf16_bucketed", "int32_w16", "fused", "sweep",
-                             "sparse", "dtypes", "overlap", "ceilings"),
+                             "sparse", "dtypes", "overlap", "size_sweep", "ceilings"),
                     help="rs_w8_f32 (default) is the headline line; the others print timings only")
     args = ap.parse_args()
 
