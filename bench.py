@@ -510,7 +510,7 @@ def main() -> int:
     del dev, out
 
     result = {
-        "metric": "reduce-scatter effective HBM GB/s (W=8, 64Mi fp32/rank)",
+        "metric": "reduce-scatter effective HBM GB/s and % of peak, W=8, 64Mi fp32/rank",
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
