@@ -377,7 +377,9 @@ __device__ __forceinline__ void fold_tile(const typename D::S* const (&src)[W],
     const uint64_t be = WHOLE ? e : max(hb, e / VL * VL);
     const uint64_t nv = (be - hb) / VL;
     const uint64_t v0 = static_cast<uint64_t>(tile) * (U * kBlock);
-    if (v0 < nv) {
+    // A whole segment's tiles all hold vectors: the grid has ceil(nv / tile)
+    // tiles per segment.
+    if (WHOLE || v0 < nv) {
       // This tile's vectors, [v0, v0 + nvt), as a byte range per buffer;
       // lanes past the range read zeros and their stores are dropped.
       const uint32_t nvt = static_cast<uint32_t>(min<uint64_t>(U * kBlock, nv - v0));
@@ -438,24 +440,33 @@ template <class D, int OP, int W, bool RS, bool VEC>
 __global__ __launch_bounds__(kBlock) void fold_kernel(const FoldArgs a) {
   using S = typename D::S;
 
-  // Read every scalar argument up front: one round of kernarg loads.
+  // Every scalar argument in one round of kernarg loads.  A workgroup runs a
+  // single tile, so each dependent round before its first HBM load costs a
+  // few percent of the kernel; the empty asm keeps the compiler from sinking
+  // these loads below the exit test, one round at a time.  A reduce-scatter
+  // always folds in ring order (rotation 1).
   const uint32_t tiles_total = a.tiles_total, magic = a.tps_magic, shift = a.tps_shift;
-  const uint32_t tps = a.tiles_per_seg, rot = a.rot;
+  const uint32_t tps = a.tiles_per_seg;
+  const uint32_t rot = RS ? 1u : a.rot;
+  const uint64_t seg = a.seg, count = a.count;
   const uint32_t t = xcd_tile(blockIdx.x, gridDim.x);
+  asm volatile("" ::"s"(magic), "s"(shift), "s"(tps), "s"(rot), "s"(seg), "s"(count), "s"(t));
   if (t >= tiles_total) return;
   const uint32_t k = static_cast<uint32_t>((static_cast<uint64_t>(t) * magic) >> shift);
   const uint32_t tile = t - k * tps;
   // Reduce-scatter segments are whole (count = W * seg, seg % VL == 0 for
   // the dwordx4 kernel); all-reduce ones are clipped to count.
-  const uint64_t b = RS ? static_cast<uint64_t>(k) * a.seg : min(static_cast<uint64_t>(k) * a.seg, a.count);
-  const uint64_t e = RS ? b + a.seg : min(b + a.seg, a.count);
+  const uint64_t b = RS ? static_cast<uint64_t>(k) * seg : min(static_cast<uint64_t>(k) * seg, count);
+  const uint64_t e = RS ? b + seg : min(b + seg, count);
 
-  // Ring rotation: source j of segment k is rank (k + rot + j) mod W, entry
-  // first + j of the doubled pointer table.
+  // Ring rotation: source j of segment k is rank (k + rot + j) mod W.  Each
+  // pointer is fetched on its own, just before its load is issued, so the
+  // first HBM load leaves as early as it can (measured faster than fetching
+  // the whole pointer table first and issuing the W loads back to back).
   const uint32_t first = (k + rot) % W;
   const S* src[W];
 #pragma unroll
-  for (int j = 0; j < W; ++j) src[j] = static_cast<const S*>(a.src[first + j]);
+  for (int j = 0; j < W; ++j) src[j] = static_cast<const S*>(a.src[(first + j) % W]);
 
   if constexpr (RS) {
     S* const dst[1] = {static_cast<S*>(a.dst[k])};

@@ -356,7 +356,6 @@ rsx_status_t rsx_reduce_scatter(const void* const* sendbufs, void* const* recvbu
   memset(&a, 0, sizeof(a));
   for (int r = 0; r < nranks; ++r) {
     a.src[r] = sendbufs[r];
-    a.src[r + nranks] = sendbufs[r];
     a.dst[r] = recvbufs[r];
   }
   a.count = n;
@@ -456,7 +455,6 @@ rsx_status_t rsx_all_reduce(const void* const* sendbufs, void* const* recvbufs, 
   memset(&a, 0, sizeof(a));
   for (int r = 0; r < nranks; ++r) {
     a.src[r] = sendbufs[r];
-    a.src[r + nranks] = sendbufs[r];
     a.dst[r] = recvbufs[r];
   }
   a.count = count;

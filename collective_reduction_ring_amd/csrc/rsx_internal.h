@@ -35,9 +35,7 @@ struct FoldArgs {
   uint32_t tps_magic;
   uint32_t tps_shift;
   uint32_t pad_;
-  // src[r] and src[r + W] both hold rank r's buffer, so the W sources of a
-  // segment are the W consecutive entries from its first rank on.
-  const void* src[2 * RSX_MAX_RANKS];
+  const void* src[RSX_MAX_RANKS];
   void* dst[RSX_MAX_RANKS];
 };
 
