@@ -174,6 +174,51 @@ def test_mid_size_w8():
     check(grads, accs, "threshold", threshold=3.6e-3, what="w8 threshold")
 
 
+@pytest.mark.parametrize("mode", ["topk", "threshold"])
+def test_graph_capture_replays(mode):
+    # The whole sparse call (all its kernels) captured in a HIP graph: every
+    # replay starts from the same residual (restored eagerly between
+    # replays, with synchronisation) and must equal the oracle bit for bit.
+    w, n = 4, 3 * 4096 + 500
+    grads, accs = normal_case(66, w, n)
+    g = [dev(x) for x in grads]
+    a = [dev(x) for x in accs]
+    a0 = [t.clone() for t in a]
+    outs = [torch.empty(n, device="cuda:0") for _ in range(w)]
+    kw = {"k": 150} if mode == "topk" else {"threshold": 2e-3}
+    plan = rsx.SparseAllReduce(g, a, outs, mode, **kw)
+    want_res, want_acc, want_msgs = oracle.sparse_all_reduce(
+        grads, accs, mode, kw.get("threshold", 0.0), kw.get("k"))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan()                                 # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    say(f"sparse graph capture mode={mode}")
+    with torch.cuda.graph(graph):
+        plan()
+    for rep in range(4):
+        for d, s0 in zip(a, a0):
+            d.copy_(s0)                        # eager work between replays
+        for o in outs:
+            o.fill_(-7.0)
+        plan.nnz.fill_(12345)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        nnz = plan.nnz_host()
+        for r in range(w):
+            wi, wv = want_msgs[r]
+            order = np.argsort(wi, kind="stable")
+            assert nnz[r] == len(wi), (rep, r)
+            assert np.array_equal(host(plan.msg_idx[r][:nnz[r]]).view(np.uint32), wi[order].astype(np.uint32))
+            same_bits(host(plan.msg_val[r][:nnz[r]]), wv[order], f"replay {rep} rank {r} message")
+            same_bits(host(outs[r]), want_res[r], f"replay {rep} rank {r} result")
+            same_bits(host(a[r]), want_acc[r], f"replay {rep} rank {r} residual")
+
+
 @pytest.mark.timeout(600)
 def test_full_size_bench_shape_properties():
     # W = 8, 64 Mi fp32 per rank, the timed configuration.  The oracle's
