@@ -21,7 +21,7 @@ RSX_ALGO_RING, RSX_ALGO_NAIVE, RSX_ALGO_AUTO = 0, 1, 2
 RSX_SPARSE_THRESHOLD, RSX_SPARSE_TOPK = 0, 1
 RSX_MAX_RANKS = 16
 RSX_NAIVE_MAX_BYTES = 32768
-RSX_FUSE_BATCH = 64
+RSX_FUSE_BATCH = 128
 RSX_FUSION_THRESHOLD_DEFAULT = 64 * 1024 * 1024   # Horovod's default tensor_fusion_threshold
 
 STATUS = {

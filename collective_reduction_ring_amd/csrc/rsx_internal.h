@@ -77,6 +77,8 @@ struct MultiCopyArgs {
   uint32_t tile_start[RSX_FUSE_BATCH + 1];
   int n;
 };
+// Kernel arguments are limited to 4 KiB.
+static_assert(sizeof(MultiCopyArgs) <= 4096, "pack/unpack batch must fit the kernel arguments");
 
 // MI355X: 256 CUs in 8 XCDs, each XCD with its own L2.  Workgroups of one
 // launch are handed to the XCDs round-robin by workgroup id.

@@ -52,7 +52,7 @@ extern "C" {
 #define RSX_VERSION 100          /* 1.0.0 */
 #define RSX_MAX_RANKS 16         /* largest W a call accepts */
 #define RSX_NAIVE_MAX_BYTES 32768 /* RSX_ALGO_AUTO picks naive at or below this, per rank [MX] */
-#define RSX_FUSE_BATCH 64        /* tensors per pack/unpack launch */
+#define RSX_FUSE_BATCH 128       /* tensors per pack/unpack launch */
 
 typedef enum {
   RSX_FLOAT32 = 0,   /* fp32 in, fp32 fold, fp32 out */
