@@ -47,6 +47,7 @@ namespace {
 
 constexpr uint32_t kSpLaneElems = kSpUnits * 4;  // 16 elements per lane per tile
 constexpr uint32_t kSpWalkGroups = 2048;          // workgroups of the tile-walking kernels
+constexpr uint32_t kSelTiles = 1;                 // tiles per workgroup of the top-K select
 static_assert(kSpLaneElems * kBlock == kSpTile, "tile = 256 lanes x 16 elements");
 
 // Order-preserving key of an fp32 value for the top-K cut: a larger value has
@@ -329,27 +330,39 @@ __device__ __forceinline__ bool rank_tile(const SparseArgs& a, uint32_t& r, uint
   return true;
 }
 
-// Top-K, one workgroup per tile: every element whose top digit is at or
-// above the cut's top digit (all that can still be sent) copied in index
-// order into the tile's slot.  Later kernels read the slots only.
+// Top-K: every element whose top digit is at or above the cut's top digit
+// (all that can still be sent) copied in index order into its tile's slot.
+// A workgroup takes kSelTiles consecutive tiles of one rank, issuing each
+// next tile's loads before it compacts the current one; one tile per
+// workgroup measured fastest (W = 8 x 64 Mi: 452 us, against 469 us with 4).
+// Later kernels read the slots only.
 template <bool ACC>
 __global__ __launch_bounds__(kBlock) void sp_select1_kernel(const SparseArgs a) {
   __shared__ uint64_t scratch[kBlock / 64];
-  uint32_t r, t;
-  if (!rank_tile(a, r, t)) return;
+  const uint32_t per_rank = (a.tiles + kSelTiles - 1) / kSelTiles;
+  const uint32_t lin = xcd_tile(blockIdx.x, gridDim.x);
+  if (lin >= a.world * per_rank) return;
+  const uint32_t r = lin / per_rank;
+  const uint32_t t0 = (lin - r * per_rank) * kSelTiles;
+  const uint32_t t1 = min(a.tiles, t0 + kSelTiles);
   const uint32_t prefix = a.state[4 * r];   // top digit of the cut, lower bits 0
-  const uint64_t base = static_cast<uint64_t>(t) * kSpTile;
-  const uint32_t n = tile_len(a, t);
-  float x[kSpUnits][4];
-  load_tile<false>(ACC ? a.accum[r] : a.grad[r], nullptr, base, n, x);
-  uint32_t f[kSpUnits][4];
+  const float* key = ACC ? a.accum[r] : a.grad[r];
+  TileLoad<false> ld;
+  ld.issue(key, nullptr, static_cast<uint64_t>(t0) * kSpTile, tile_len(a, t0));
+  for (uint32_t t = t0; t < t1; ++t) {
+    const uint32_t n = tile_len(a, t);
+    float x[kSpUnits][4];
+    ld.values(x);
+    if (t + 1 < t1) ld.issue(key, nullptr, static_cast<uint64_t>(t + 1) * kSpTile, tile_len(a, t + 1));
+    uint32_t f[kSpUnits][4];
 #pragma unroll
-  for (int u = 0; u < static_cast<int>(kSpUnits); ++u)
+    for (int u = 0; u < static_cast<int>(kSpUnits); ++u)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) f[u][j] = (in_tile(u, j, n) && order_key(x[u][j]) >= prefix) ? 1u : 0u;
-  const uint64_t slot = (static_cast<uint64_t>(r) * a.tiles + t) * kSpTile;
-  const uint32_t cnt = compact_to_slot(a, slot, f, x, scratch);
-  if (threadIdx.x == 0) a.tile_slot[r * (a.tiles + 1) + t] = cnt;
+      for (int j = 0; j < 4; ++j) f[u][j] = (in_tile(u, j, n) && order_key(x[u][j]) >= prefix) ? 1u : 0u;
+    const uint64_t slot = (static_cast<uint64_t>(r) * a.tiles + t) * kSpTile;
+    const uint32_t cnt = compact_to_slot(a, slot, f, x, scratch);
+    if (threadIdx.x == 0) a.tile_slot[r * (a.tiles + 1) + t] = cnt;
+  }
 }
 
 // Top-K passes 1 and 2, over the slots: histogram of digit PASS among the
@@ -655,7 +668,8 @@ hipError_t launch_mode(SparseArgs a, hipStream_t s) {
     if ((a.k > 0 || ACC) && e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_hist0_kernel<ACC>), hg, kBlock);
     if (a.k > 0) {
       if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_pick_kernel<0>), a.world, kBlock);
-      if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_select1_kernel<ACC>), rt, kBlock);
+      const uint64_t sel = xcd_grid(static_cast<uint64_t>(a.world) * ((a.tiles + kSelTiles - 1) / kSelTiles));
+      if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_select1_kernel<ACC>), sel, kBlock);
       if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_hist_slots_kernel<1>), hg, kBlock);
       if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_pick_kernel<1>), a.world, kBlock);
       if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_hist_slots_kernel<2>), hg, kBlock);
