@@ -18,12 +18,16 @@
 //
 //   threshold:  compact  (every element) entries to send, in index order,
 //                        into the tile's slot; the residual
-//   top-K:      hist0    (every element) top-digit histogram; g = grad + acc
+//   top-K:      sample   per rank: a lower bound for the K-th largest key
+//                        from a strided sample of 16384 keys (two kernels:
+//                        the keys, then the pick)
+//               gather   (every element) every key at or above the bound
+//                        into the tile's slot, in index order; g = grad + acc
 //                        into the accumulation buffer
-//               select1  (every element) every element at or above the
-//                        top digit's cut bin into the tile's slot, in index
-//                        order
-//               hist1/2  (slots) middle- and low-digit histograms
+//               check    per rank: fewer than K keys gathered?  Then an exact
+//                        fallback for that rank alone: a top-digit histogram
+//                        over every element, its bound, and the gather again
+//               hist0-2  (slots) top-, middle- and low-digit histograms
 //               pick     after each histogram: the digit of the K-th key
 //               count    (slots) per tile, candidates above / equal to the cut
 //   both:       scan     per rank: each tile's offset in the message
@@ -35,7 +39,8 @@
 // Ties at the cut are taken in index order, as a stable sort from large to
 // small values would take them.  A slot per tile lets a tile write its
 // entries before any offset is known; after the selection only slots are
-// read.  No kernel waits on another workgroup.
+// read.  The sample only decides how many candidates are gathered; the
+// result never depends on it.  No kernel waits on another workgroup.
 #include <algorithm>
 
 #include "mem.h"
@@ -47,8 +52,11 @@ namespace {
 
 constexpr uint32_t kSpLaneElems = kSpUnits * 4;  // 16 elements per lane per tile
 constexpr uint32_t kSpWalkGroups = 2048;          // workgroups of the tile-walking kernels
-constexpr uint32_t kSelTiles = 1;                 // tiles per workgroup of the top-K select
+constexpr uint32_t kSampleMax = 16384;            // top-K: keys sampled per rank for the gather bound
+constexpr int kSampleBlock = 1024;                // lanes of the sampling workgroup
 static_assert(kSpLaneElems * kBlock == kSpTile, "tile = 256 lanes x 16 elements");
+static_assert(kSampleMax % kBlock == 0 && kSampleMax % kSampleBlock == 0, "whole sample groups");
+static_assert(2 * kSampleBlock == kSpBins, "the sample pick holds two bins per lane");
 
 // Order-preserving key of an fp32 value for the top-K cut: a larger value has
 // a larger key; -0 and +0 share one key; every NaN has key 0, below -inf.
@@ -224,8 +232,8 @@ struct Digit {
 // ----------------------------------------------------------------- kernels
 
 // Per rank: zero the histogram and the per-tile counts; selection state =
-// (cut key 0, K still to find).  K = 0 selects nothing: the cut key is then
-// above every key.
+// (cut key 0, K still to find, gather bound, fallback flag).  K = 0 selects
+// nothing: the cut key and the gather bound are then above every key.
 __global__ __launch_bounds__(kBlock) void sp_init_kernel(const SparseArgs a) {
   const uint32_t r = blockIdx.x;
   for (uint32_t i = threadIdx.x; i < kSpBins; i += kBlock) a.hist[r * kSpBins + i] = 0;
@@ -239,8 +247,8 @@ __global__ __launch_bounds__(kBlock) void sp_init_kernel(const SparseArgs a) {
     uint32_t* st = a.state + 4 * r;
     st[0] = a.k == 0 ? 0xFFFFFFFFu : 0u;
     st[1] = a.k;
-    st[2] = 0;
-    st[3] = 0;
+    st[2] = a.k == 0 ? 0xFFFFFFFFu : 0u;  // keys gathered into the slots: >= st[2]
+    st[3] = 0;                              // 1: the sampled bound missed, gather again
   }
 }
 
@@ -257,37 +265,126 @@ __device__ __forceinline__ void zero_hist(uint32_t* h) {
   __syncthreads();
 }
 
-// Top-K pass 0, over every element: histogram of the top digit.  With an
-// accumulation it also forms g = grad + acc and stores it in the
-// accumulation buffer, where it is at once the value every later kernel
-// selects on and the residual of every entry that is not sent (g - 0 = g);
-// the combine rewrites the residual of the entries that are.
+// Top-K fallback, over every element of a rank whose sampled bound missed:
+// histogram of the top digit of the stored values g.  Ranks that need no
+// fallback leave at once.
 template <bool ACC>
-__global__ __launch_bounds__(kBlock) void sp_hist0_kernel(const SparseArgs a) {
+__global__ __launch_bounds__(kBlock) void sp_hist0_fb_kernel(const SparseArgs a) {
   using Dg = Digit<0>;
   __shared__ uint32_t h[kSpBins];
   const uint32_t r = blockIdx.x / a.hist_groups;
+  if (a.state[4 * r + 3] == 0) return;
   const uint32_t grp = blockIdx.x - r * a.hist_groups;
   zero_hist(h);
+  const float* key = ACC ? a.accum[r] : a.grad[r];
   const uint32_t t0 = grp * a.hist_chunk;
   const uint32_t t1 = min(a.tiles, t0 + a.hist_chunk);
-  TileLoad<ACC> ld;
-  if (t0 < t1) ld.issue(a.grad[r], a.accum[r], static_cast<uint64_t>(t0) * kSpTile, tile_len(a, t0));
+  TileLoad<false> ld;
+  if (t0 < t1) ld.issue(key, nullptr, static_cast<uint64_t>(t0) * kSpTile, tile_len(a, t0));
   for (uint32_t t = t0; t < t1; ++t) {
-    const uint64_t base = static_cast<uint64_t>(t) * kSpTile;
     const uint32_t n = tile_len(a, t);
     float x[kSpUnits][4];
     ld.values(x);
-    if (t + 1 < t1) ld.issue(a.grad[r], a.accum[r], base + kSpTile, tile_len(a, t + 1));
-    if constexpr (ACC) store_tile(a.accum[r], base, n, x);
-    if (a.k == 0) continue;  // only the residual is needed
+    if (t + 1 < t1) ld.issue(key, nullptr, static_cast<uint64_t>(t + 1) * kSpTile, tile_len(a, t + 1));
 #pragma unroll
     for (int u = 0; u < static_cast<int>(kSpUnits); ++u)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (in_tile(u, j, n)) atomicAdd(&h[order_key(x[u][j]) >> Dg::kShift], 1u);
   }
-  if (a.k != 0) merge_hist<Dg::kBins>(h, a.hist + r * kSpBins);
+  merge_hist<Dg::kBins>(h, a.hist + r * kSpBins);
+}
+
+// Top-K sample of a rank of n keys: m = min(n, kSampleMax) keys, every
+// (n / m)-th, and the rank j (from the top) of the sample key taken as the
+// gather bound: ceil(K m / n) + 4 sqrt(ceil(K m / n)) + 4.  That key is
+// expected to have about j n / m keys at or above it, comfortably more than
+// K.  j > m means the bound is 0: everything is gathered.
+struct SamplePlan {
+  uint32_t m, j;
+  uint64_t stride;
+  __device__ explicit SamplePlan(const SparseArgs& a) {
+    const uint64_t n = a.count;
+    m = static_cast<uint32_t>(min<uint64_t>(n, kSampleMax));
+    stride = n / m;
+    const uint64_t kk = (static_cast<uint64_t>(a.k) * m + n - 1) / n;
+    uint64_t root = 0;
+    while ((root + 1) * (root + 1) <= kk) ++root;  // isqrt, kk <= kSampleMax
+    j = static_cast<uint32_t>(min<uint64_t>(kk + 4 * root + 4, 0xFFFFFFFFull));
+  }
+  // The sampled keys of rank r sit at the start of the rank's slot area,
+  // which the gather fills only after they have been used.
+  __device__ static uint32_t* keys(const SparseArgs& a, uint32_t r) {
+    return a.gap_idx + static_cast<uint64_t>(r) * a.tiles * kSpTile;
+  }
+};
+
+// Top-K, kSampleMax / kBlock workgroups per rank: the sampled keys (of
+// g = grad + acc, as the gather forms it).
+template <bool ACC>
+__global__ __launch_bounds__(kBlock) void sp_sample_keys_kernel(const SparseArgs a) {
+  constexpr uint32_t kGroups = kSampleMax / kBlock;
+  const uint32_t r = blockIdx.x / kGroups;
+  const uint32_t smp = (blockIdx.x - r * kGroups) * kBlock + threadIdx.x;
+  const SamplePlan p(a);
+  if (p.j > p.m || smp >= p.m) return;
+  const uint64_t idx = smp * p.stride;
+  float v = __builtin_nontemporal_load(a.grad[r] + idx);
+  if constexpr (ACC) v = v + __builtin_nontemporal_load(a.accum[r] + idx);
+  SamplePlan::keys(a, r)[smp] = order_key(v);
+}
+
+// Top-K, one workgroup of kSampleBlock lanes per rank: the gather bound
+// (state[2]) from the rank's sampled keys, the lower edge of the 22-bit key
+// prefix of the j-th largest sampled key.  Everything at or above it is
+// gathered; if that is fewer than K keys the sample misled, and the exact
+// fallback takes over.  The result never depends on the sample.
+__global__ __launch_bounds__(kSampleBlock) void sp_sample_pick_kernel(const SparseArgs a) {
+  constexpr int kWaves = kSampleBlock / 64;
+  constexpr uint32_t kPer = kSampleMax / kSampleBlock;
+  __shared__ uint32_t h[kSpBins];
+  __shared__ uint32_t scratch[kWaves];
+  __shared__ uint32_t sel[2];
+  const uint32_t r = blockIdx.x;
+  const SamplePlan p(a);
+  uint32_t lo = 0;
+  if (p.j <= p.m) {
+    const uint32_t* keys = SamplePlan::keys(a, r);
+    uint32_t key[kPer];
+#pragma unroll
+    for (uint32_t q = 0; q < kPer; ++q) key[q] = keys[min(threadIdx.x + q * kSampleBlock, p.m - 1)];
+    uint32_t prefix = 0, need = p.j;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const uint32_t shift = pass == 0 ? 21u : 10u;
+      const uint32_t high = pass == 0 ? 0u : 0xFFE00000u;
+      for (uint32_t i = threadIdx.x; i < kSpBins; i += kSampleBlock) h[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (uint32_t q = 0; q < kPer; ++q)
+        if (threadIdx.x + q * kSampleBlock < p.m && (key[q] & high) == prefix)
+          atomicAdd(&h[(key[q] >> shift) & (kSpBins - 1)], 1u);
+      __syncthreads();
+      // thread i holds bins 2047 - 2i and 2046 - 2i (thread 0 the highest)
+      const uint32_t b0 = kSpBins - 1 - 2 * threadIdx.x, b1 = b0 - 1;
+      const uint32_t c0 = h[b0], c1 = h[b1];
+      uint32_t total;
+      const uint32_t above = block_excl<kWaves>(c0 + c1, scratch, total);
+      if (above < need && need <= above + c0 + c1) {
+        const bool first = above + c0 >= need;
+        sel[0] = prefix | ((first ? b0 : b1) << shift);
+        sel[1] = need - (first ? above : above + c0);
+      }
+      __syncthreads();
+      prefix = sel[0];
+      need = sel[1];
+    }
+    lo = prefix;
+  }
+  if (threadIdx.x == 0) {
+    a.state[4 * r + 2] = lo;
+    a.state[4 * r + 3] = 0;
+  }
 }
 
 // Copy this tile's flagged elements, in index order, to its slot; returns
@@ -330,43 +427,107 @@ __device__ __forceinline__ bool rank_tile(const SparseArgs& a, uint32_t& r, uint
   return true;
 }
 
-// Top-K: every element whose top digit is at or above the cut's top digit
-// (all that can still be sent) copied in index order into its tile's slot.
-// A workgroup takes kSelTiles consecutive tiles of one rank, issuing each
-// next tile's loads before it compacts the current one; one tile per
-// workgroup measured fastest (W = 8 x 64 Mi: 452 us, against 469 us with 4).
-// Later kernels read the slots only.
+// Every key of tile t of rank r at or above `lo` into the tile's slot, in
+// index order.
+__device__ __forceinline__ void gather_tile(const SparseArgs& a, uint32_t r, uint32_t t, uint32_t lo,
+                                            const float (&x)[kSpUnits][4], uint32_t n, uint64_t* scratch) {
+  uint32_t f[kSpUnits][4];
+#pragma unroll
+  for (int u = 0; u < static_cast<int>(kSpUnits); ++u)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f[u][j] = (in_tile(u, j, n) && order_key(x[u][j]) >= lo) ? 1u : 0u;
+  const uint64_t slot = (static_cast<uint64_t>(r) * a.tiles + t) * kSpTile;
+  const uint32_t cnt = compact_to_slot(a, slot, f, x, scratch);
+  if (threadIdx.x == 0) a.tile_slot[r * (a.tiles + 1) + t] = cnt;
+}
+
+// Top-K gather, one workgroup per tile, against the sampled bound
+// (state[2]).  It also forms g = grad + acc and stores it in the
+// accumulation buffer, where it is at once the value the later kernels
+// select on and the residual of every entry that is not sent (g - 0 = g;
+// the combine rewrites the residual of the entries that are).  Later
+// kernels read the slots only.
 template <bool ACC>
-__global__ __launch_bounds__(kBlock) void sp_select1_kernel(const SparseArgs a) {
+__global__ __launch_bounds__(kBlock) void sp_gather_kernel(const SparseArgs a) {
   __shared__ uint64_t scratch[kBlock / 64];
-  const uint32_t per_rank = (a.tiles + kSelTiles - 1) / kSelTiles;
-  const uint32_t lin = xcd_tile(blockIdx.x, gridDim.x);
-  if (lin >= a.world * per_rank) return;
-  const uint32_t r = lin / per_rank;
-  const uint32_t t0 = (lin - r * per_rank) * kSelTiles;
-  const uint32_t t1 = min(a.tiles, t0 + kSelTiles);
-  const uint32_t prefix = a.state[4 * r];   // top digit of the cut, lower bits 0
+  uint32_t r, t;
+  if (!rank_tile(a, r, t)) return;
+  const uint64_t base = static_cast<uint64_t>(t) * kSpTile;
+  const uint32_t n = tile_len(a, t);
+  float x[kSpUnits][4];
+  load_tile<ACC>(a.grad[r], ACC ? a.accum[r] : nullptr, base, n, x);
+  if constexpr (ACC) store_tile(a.accum[r], base, n, x);
+  gather_tile(a, r, t, a.state[4 * r + 2], x, n, scratch);
+}
+
+// The fallback's gather, from the stored values g, for a rank whose sampled
+// bound missed (its groups walk the rank's tiles; other ranks leave at once).
+template <bool ACC>
+__global__ __launch_bounds__(kBlock) void sp_gather_fb_kernel(const SparseArgs a) {
+  __shared__ uint64_t scratch[kBlock / 64];
+  const uint32_t r = blockIdx.x / a.hist_groups;
+  if (a.state[4 * r + 3] == 0) return;
+  const uint32_t grp = blockIdx.x - r * a.hist_groups;
+  const uint32_t lo = a.state[4 * r + 2];
   const float* key = ACC ? a.accum[r] : a.grad[r];
-  TileLoad<false> ld;
-  ld.issue(key, nullptr, static_cast<uint64_t>(t0) * kSpTile, tile_len(a, t0));
-  for (uint32_t t = t0; t < t1; ++t) {
+  const uint32_t t1 = min(a.tiles, (grp + 1) * a.hist_chunk);
+  for (uint32_t t = grp * a.hist_chunk; t < t1; ++t) {
     const uint32_t n = tile_len(a, t);
     float x[kSpUnits][4];
-    ld.values(x);
-    if (t + 1 < t1) ld.issue(key, nullptr, static_cast<uint64_t>(t + 1) * kSpTile, tile_len(a, t + 1));
-    uint32_t f[kSpUnits][4];
-#pragma unroll
-    for (int u = 0; u < static_cast<int>(kSpUnits); ++u)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) f[u][j] = (in_tile(u, j, n) && order_key(x[u][j]) >= prefix) ? 1u : 0u;
-    const uint64_t slot = (static_cast<uint64_t>(r) * a.tiles + t) * kSpTile;
-    const uint32_t cnt = compact_to_slot(a, slot, f, x, scratch);
-    if (threadIdx.x == 0) a.tile_slot[r * (a.tiles + 1) + t] = cnt;
+    load_tile<false>(key, nullptr, static_cast<uint64_t>(t) * kSpTile, n, x);
+    gather_tile(a, r, t, lo, x, n, scratch);
   }
 }
 
-// Top-K passes 1 and 2, over the slots: histogram of digit PASS among the
-// keys matching the cut's higher digits.
+// Top-K, one workgroup per rank: did the first gather hold at least K keys?
+// If not, flag the rank for the exact fallback.
+__global__ __launch_bounds__(kSpScanBlock) void sp_check_kernel(const SparseArgs a) {
+  __shared__ uint32_t scratch[kSpScanBlock / 64];
+  const uint32_t r = blockIdx.x;
+  const uint32_t* cnt = a.tile_slot + r * (a.tiles + 1);
+  uint32_t sum = 0;
+  for (uint32_t i = threadIdx.x; i < a.tiles; i += kSpScanBlock) sum += cnt[i];
+  uint32_t total;
+  block_excl<kSpScanBlock / 64>(sum, scratch, total);
+  if (threadIdx.x == 0) a.state[4 * r + 3] = total < a.k ? 1u : 0u;
+}
+
+// Sum over the 64 lanes of a wave, in every lane.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
+// Walks the slots of tiles [t0, t1) of rank r: each wave of the workgroup
+// takes every (kBlock / 64)-th tile, its lanes the tile's entries.  The
+// lanes first load the entry counts of the wave's next 64 tiles at once, so
+// a tile costs one dependent load, not two.  fn(tile, value, lane, count)
+// runs for every entry and once more per tile with lane >= count (so that
+// per-tile reductions see every lane).
+template <class F>
+__device__ __forceinline__ void walk_slots(const SparseArgs& a, uint32_t r, uint32_t t0, uint32_t t1, F&& fn) {
+  constexpr uint32_t kWaves = kBlock / 64;
+  const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63u;
+  const uint32_t* cnt = a.tile_slot + r * (a.tiles + 1);
+  for (uint32_t tb = t0 + wave; tb < t1; tb += 64 * kWaves) {
+    const uint32_t mine = tb + lane * kWaves;
+    const uint32_t c_l = mine < t1 ? min(cnt[mine], kSpTile) : 0u;
+    const uint32_t nt = min(64u, (t1 - tb + kWaves - 1) / kWaves);
+    for (uint32_t i = 0; i < nt; ++i) {
+      const uint32_t t = tb + i * kWaves;
+      const uint32_t c = __shfl(c_l, i, 64);
+      const float* gv = a.gap_val + (static_cast<uint64_t>(r) * a.tiles + t) * kSpTile;
+      for (uint32_t e0 = 0; e0 < max(c, 1u); e0 += 64) {
+        const uint32_t e = e0 + lane;
+        fn(t, e < c ? gv[e] : 0.0f, e < c, e0 + 64 >= c);
+      }
+    }
+  }
+}
+
+// Top-K, over the slots: histogram of digit PASS among the keys matching
+// the cut's higher digits.
 template <int PASS>
 __global__ __launch_bounds__(kBlock) void sp_hist_slots_kernel(const SparseArgs a) {
   using Dg = Digit<PASS>;
@@ -376,15 +537,10 @@ __global__ __launch_bounds__(kBlock) void sp_hist_slots_kernel(const SparseArgs 
   zero_hist(h);
   const uint32_t prefix = a.state[4 * r];
   const uint32_t t0 = grp * a.hist_chunk;
-  const uint32_t t1 = min(a.tiles, t0 + a.hist_chunk);
-  for (uint32_t t = t0; t < t1; ++t) {
-    const uint32_t c = min(a.tile_slot[r * (a.tiles + 1) + t], kSpTile);
-    const float* gv = a.gap_val + (static_cast<uint64_t>(r) * a.tiles + t) * kSpTile;
-    for (uint32_t e = threadIdx.x; e < c; e += kBlock) {
-      const uint32_t k = order_key(gv[e]);
-      if ((k & Dg::kHigh) == prefix) atomicAdd(&h[(k >> Dg::kShift) & (Dg::kBins - 1)], 1u);
-    }
-  }
+  walk_slots(a, r, t0, min(a.tiles, t0 + a.hist_chunk), [&](uint32_t, float v, bool valid, bool) {
+    const uint32_t k = order_key(v);
+    if (valid && (k & Dg::kHigh) == prefix) atomicAdd(&h[(k >> Dg::kShift) & (Dg::kBins - 1)], 1u);
+  });
   merge_hist<Dg::kBins>(h, a.hist + r * kSpBins);
 }
 
@@ -392,7 +548,10 @@ __global__ __launch_bounds__(kBlock) void sp_hist_slots_kernel(const SparseArgs 
 // top, the first bin at which the running count reaches the number still to
 // find.  The keys of the bins above it are all selected; the search goes on
 // inside that bin.  One workgroup per rank; clears the histogram afterwards.
-template <int PASS>
+// BOUND: the fallback's pick of the top digit, for a rank whose sampled
+// bound missed: the lower edge of the K-th largest key's top-digit bin
+// becomes the gather bound (state[2]); the cut itself is still found later.
+template <int PASS, bool BOUND = false>
 __global__ __launch_bounds__(kBlock) void sp_pick_kernel(const SparseArgs a) {
   using Dg = Digit<PASS>;
   constexpr uint32_t kPer = Dg::kBins / kBlock;
@@ -400,8 +559,9 @@ __global__ __launch_bounds__(kBlock) void sp_pick_kernel(const SparseArgs a) {
   const uint32_t r = blockIdx.x;
   uint32_t* gh = a.hist + r * kSpBins;
   uint32_t* st = a.state + 4 * r;
-  const uint32_t prefix = st[0];
-  const uint32_t need = st[1];
+  if (BOUND && st[3] == 0) return;
+  const uint32_t prefix = BOUND ? 0u : st[0];
+  const uint32_t need = BOUND ? a.k : st[1];
   // thread i holds bins top, top-1, ..., top-kPer+1 (thread 0 the highest)
   const uint32_t top = Dg::kBins - 1 - threadIdx.x * kPer;
   uint32_t c[kPer];
@@ -417,8 +577,12 @@ __global__ __launch_bounds__(kBlock) void sp_pick_kernel(const SparseArgs a) {
     uint32_t run = above;
     for (uint32_t i = 0; i < kPer; ++i) {
       if (run + c[i] >= need) {
-        st[0] = prefix | ((top - i) << Dg::kShift);
-        st[1] = need - run;
+        if (BOUND) {
+          st[2] = (top - i) << Dg::kShift;
+        } else {
+          st[0] = prefix | ((top - i) << Dg::kShift);
+          st[1] = need - run;
+        }
         break;
       }
       run += c[i];
@@ -438,25 +602,23 @@ __device__ __forceinline__ uint32_t cut_flags(float v, uint32_t cut) {
 // Top-K, over the slots: per tile, the candidates above the cut and those
 // equal to it.
 __global__ __launch_bounds__(kBlock) void sp_slot_count_kernel(const SparseArgs a) {
-  __shared__ uint32_t scratch[kBlock / 64];
   const uint32_t r = blockIdx.x / a.hist_groups;
   const uint32_t grp = blockIdx.x - r * a.hist_groups;
   const uint32_t cut = a.state[4 * r];
   const uint32_t t0 = grp * a.hist_chunk;
-  const uint32_t t1 = min(a.tiles, t0 + a.hist_chunk);
-  for (uint32_t t = t0; t < t1; ++t) {
-    const uint32_t i = r * (a.tiles + 1) + t;
-    const uint32_t c = min(a.tile_slot[i], kSpTile);
-    const float* gv = a.gap_val + (static_cast<uint64_t>(r) * a.tiles + t) * kSpTile;
-    uint32_t f = 0;
-    for (uint32_t e = threadIdx.x; e < c; e += kBlock) f += cut_flags(gv[e], cut);
-    uint32_t tot;
-    block_excl<kBlock / 64>(f, scratch, tot);
-    if (threadIdx.x == 0) {
-      a.tile_cnt[i] = tot & 0xFFFFu;
-      a.tile_eqc[i] = tot >> 16;
+  uint32_t f = 0;  // this lane's flags in the current tile
+  walk_slots(a, r, t0, min(a.tiles, t0 + a.hist_chunk), [&](uint32_t t, float v, bool valid, bool last) {
+    if (valid) f += cut_flags(v, cut);
+    if (last) {
+      const uint32_t tot = wave_sum(f);
+      f = 0;
+      if ((threadIdx.x & 63u) == 0) {
+        const uint32_t i = r * (a.tiles + 1) + t;
+        a.tile_cnt[i] = tot & 0xFFFFu;
+        a.tile_eqc[i] = tot >> 16;
+      }
     }
-  }
+  });
 }
 
 // Threshold mode, over every element: per tile, the entries to send
@@ -663,18 +825,25 @@ hipError_t launch_mode(SparseArgs a, hipStream_t s) {
   const uint64_t rt = xcd_grid(static_cast<uint64_t>(a.world) * a.tiles);
   hipError_t e = go(reinterpret_cast<const void*>(&sp_init_kernel), a.world, kBlock);
   if constexpr (MODE == RSX_SPARSE_TOPK) {
-    // Pass 0 also leaves g in the accumulation buffer, so it runs even when
-    // K = 0 has nothing to select.
-    if ((a.k > 0 || ACC) && e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_hist0_kernel<ACC>), hg, kBlock);
+    auto fn = [](auto k) { return reinterpret_cast<const void*>(k); };
+    if (a.k > 0 && e == hipSuccess)
+      e = go(fn(&sp_sample_keys_kernel<ACC>), static_cast<uint64_t>(a.world) * (kSampleMax / kBlock), kBlock);
+    if (a.k > 0 && e == hipSuccess) e = go(fn(&sp_sample_pick_kernel), a.world, kSampleBlock);
+    // The first gather also leaves g in the accumulation buffer, so it runs
+    // even when K = 0 has nothing to select.
+    if ((a.k > 0 || ACC) && e == hipSuccess) e = go(fn(&sp_gather_kernel<ACC>), rt, kBlock);
     if (a.k > 0) {
-      if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_pick_kernel<0>), a.world, kBlock);
-      const uint64_t sel = xcd_grid(static_cast<uint64_t>(a.world) * ((a.tiles + kSelTiles - 1) / kSelTiles));
-      if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_select1_kernel<ACC>), sel, kBlock);
-      if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_hist_slots_kernel<1>), hg, kBlock);
-      if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_pick_kernel<1>), a.world, kBlock);
-      if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_hist_slots_kernel<2>), hg, kBlock);
-      if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_pick_kernel<2>), a.world, kBlock);
-      if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_slot_count_kernel), hg, kBlock);
+      if (e == hipSuccess) e = go(fn(&sp_check_kernel), a.world, kSpScanBlock);
+      if (e == hipSuccess) e = go(fn(&sp_hist0_fb_kernel<ACC>), hg, kBlock);
+      if (e == hipSuccess) e = go(fn(&sp_pick_kernel<0, true>), a.world, kBlock);
+      if (e == hipSuccess) e = go(fn(&sp_gather_fb_kernel<ACC>), hg, kBlock);
+      if (e == hipSuccess) e = go(fn(&sp_hist_slots_kernel<0>), hg, kBlock);
+      if (e == hipSuccess) e = go(fn(&sp_pick_kernel<0>), a.world, kBlock);
+      if (e == hipSuccess) e = go(fn(&sp_hist_slots_kernel<1>), hg, kBlock);
+      if (e == hipSuccess) e = go(fn(&sp_pick_kernel<1>), a.world, kBlock);
+      if (e == hipSuccess) e = go(fn(&sp_hist_slots_kernel<2>), hg, kBlock);
+      if (e == hipSuccess) e = go(fn(&sp_pick_kernel<2>), a.world, kBlock);
+      if (e == hipSuccess) e = go(fn(&sp_slot_count_kernel), hg, kBlock);
     }
   } else {
     if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_compact_kernel<ACC>), rt, kBlock);

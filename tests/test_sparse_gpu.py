@@ -174,6 +174,34 @@ def test_mid_size_w8():
     check(grads, accs, "threshold", threshold=3.6e-3, what="w8 threshold")
 
 
+@pytest.mark.parametrize("fraction", [0.001, 0.01, 0.3, 0.97, 1.0])
+def test_topk_past_the_sample_size(fraction):
+    # more elements than the 16384 keys the top-K bound is sampled from; a
+    # large K makes the sampled rank exceed the sample (the bound is then 0)
+    n = 3 * 16384 + 4096 + 5
+    grads, accs = normal_case((66, int(fraction * 1000)), 3, n)
+    check(grads, accs, "topk", k=rsx.topk_count(n, fraction), what=f"topk {fraction}")
+
+
+@pytest.mark.parametrize("feedback", [True, False])
+@pytest.mark.parametrize("fraction", [0.05, 0.5])
+def test_topk_sample_misled(feedback, fraction):
+    # White-box: the top-K bound is drawn from every (n // 16384)-th key.
+    # Large values at exactly those positions make the sample claim that
+    # few keys reach the bound's level, so the gather holds fewer than K
+    # keys and the exact fallback must take over.  Rank 1 keeps ordinary
+    # values, so one call mixes ranks with and without the fallback.
+    n = 5 * 16384 + 777
+    w = 3
+    grads, accs = normal_case((67, int(fraction * 1000)), w, n)
+    rng = np.random.default_rng(68)
+    sampled = np.arange(16384) * (n // 16384)
+    for r in (0, 2):
+        grads[r][sampled] = (1.0 + rng.random(16384)).astype(f32)
+    check(grads, accs if feedback else None, "topk", k=rsx.topk_count(n, fraction),
+          what=f"misled sample {fraction}")
+
+
 @pytest.mark.parametrize("mode", ["topk", "threshold"])
 def test_graph_capture_replays(mode):
     # The whole sparse call (all its kernels) captured in a HIP graph: every
