@@ -22,8 +22,9 @@
 //                        from a strided sample of 16384 keys (two kernels:
 //                        the keys, then the pick)
 //               gather   (every element) every key at or above the bound
-//                        into the tile's slot, in index order; g = grad + acc
-//                        into the accumulation buffer
+//                        into the tile's slot, in index order; into the
+//                        accumulation buffer g = grad + acc, or at a
+//                        candidate the residual it has if sent
 //               check    per rank: fewer than K keys gathered?  Then an exact
 //                        fallback for that rank alone: a top-digit histogram
 //                        over every element, its bound, and the gather again
@@ -33,8 +34,8 @@
 //   both:       scan     per rank: each tile's offset in the message
 //               combine  per output tile: for each rank in order, its sent
 //                        entries into the message and into an LDS tile (top-K
-//                        also rewrites their residuals); the tile to all W
-//                        outputs
+//                        puts g back as the residual of candidates not sent);
+//                        the tile to all W outputs
 //
 // Ties at the cut are taken in index order, as a stable sort from large to
 // small values would take them.  A slot per tile lets a tile write its
@@ -266,12 +267,16 @@ __device__ __forceinline__ void zero_hist(uint32_t* h) {
 }
 
 // Top-K fallback, over every element of a rank whose sampled bound missed:
-// histogram of the top digit of the stored values g.  Ranks that need no
-// fallback leave at once.
+// histogram of the top digit of g.  With an accumulation the first gather
+// left, at each of its candidates, the residual of a sent entry in the
+// accumulation buffer, and g in the tile's slot: those g are counted from
+// the slot and put back, so that the buffer holds g everywhere again for
+// the fallback's gather.  Ranks that need no fallback leave at once.
 template <bool ACC>
 __global__ __launch_bounds__(kBlock) void sp_hist0_fb_kernel(const SparseArgs a) {
   using Dg = Digit<0>;
   __shared__ uint32_t h[kSpBins];
+  __shared__ uint32_t cand[kSpTile / 32];  // the tile's first-gather candidates
   const uint32_t r = blockIdx.x / a.hist_groups;
   if (a.state[4 * r + 3] == 0) return;
   const uint32_t grp = blockIdx.x - r * a.hist_groups;
@@ -279,18 +284,34 @@ __global__ __launch_bounds__(kBlock) void sp_hist0_fb_kernel(const SparseArgs a)
   const float* key = ACC ? a.accum[r] : a.grad[r];
   const uint32_t t0 = grp * a.hist_chunk;
   const uint32_t t1 = min(a.tiles, t0 + a.hist_chunk);
-  TileLoad<false> ld;
-  if (t0 < t1) ld.issue(key, nullptr, static_cast<uint64_t>(t0) * kSpTile, tile_len(a, t0));
   for (uint32_t t = t0; t < t1; ++t) {
     const uint32_t n = tile_len(a, t);
+    const uint64_t base = static_cast<uint64_t>(t) * kSpTile;
+    if constexpr (ACC) {
+      for (uint32_t i = threadIdx.x; i < kSpTile / 32; i += kBlock) cand[i] = 0;
+      __syncthreads();
+      const uint32_t c = min(a.tile_slot[r * (a.tiles + 1) + t], n);
+      const uint64_t slot = (static_cast<uint64_t>(r) * a.tiles + t) * kSpTile;
+      for (uint32_t e = threadIdx.x; e < c; e += kBlock) {
+        const uint32_t local = min(a.gap_idx[slot + e], n - 1);
+        const float v = a.gap_val[slot + e];
+        atomicOr(&cand[local >> 5], 1u << (local & 31u));
+        atomicAdd(&h[order_key(v) >> Dg::kShift], 1u);
+        a.accum[r][base + local] = v;
+      }
+      __syncthreads();
+    }
     float x[kSpUnits][4];
-    ld.values(x);
-    if (t + 1 < t1) ld.issue(key, nullptr, static_cast<uint64_t>(t + 1) * kSpTile, tile_len(a, t + 1));
+    load_tile<false>(key, nullptr, base, n, x);
 #pragma unroll
     for (int u = 0; u < static_cast<int>(kSpUnits); ++u)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (in_tile(u, j, n)) atomicAdd(&h[order_key(x[u][j]) >> Dg::kShift], 1u);
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t local = static_cast<uint32_t>(u) * kBlock * 4 + threadIdx.x * 4 + j;
+        const bool counted = ACC && ((cand[local >> 5] >> (local & 31u)) & 1u);
+        if (in_tile(u, j, n) && !counted) atomicAdd(&h[order_key(x[u][j]) >> Dg::kShift], 1u);
+      }
+    if constexpr (ACC) __syncthreads();  // the bitmap is reused by the next tile
   }
   merge_hist<Dg::kBins>(h, a.hist + r * kSpBins);
 }
@@ -441,27 +462,41 @@ __device__ __forceinline__ void gather_tile(const SparseArgs& a, uint32_t r, uin
   if (threadIdx.x == 0) a.tile_slot[r * (a.tiles + 1) + t] = cnt;
 }
 
+// The residual of a gathered candidate as if it were sent, g - (0 + g),
+// and g itself elsewhere: what the accumulation buffer holds after a
+// gather.  Most candidates are sent; the combine puts g back at the others.
+__device__ __forceinline__ void store_residual(float* acc, uint64_t base, uint32_t n, uint32_t lo,
+                                               const float (&x)[kSpUnits][4]) {
+  float y[kSpUnits][4];
+#pragma unroll
+  for (int u = 0; u < static_cast<int>(kSpUnits); ++u)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[u][j] = order_key(x[u][j]) >= lo ? x[u][j] - (0.0f + x[u][j]) : x[u][j];
+  store_tile(acc, base, n, y);
+}
+
 // Top-K gather, one workgroup per tile, against the sampled bound
-// (state[2]).  It also forms g = grad + acc and stores it in the
-// accumulation buffer, where it is at once the value the later kernels
-// select on and the residual of every entry that is not sent (g - 0 = g;
-// the combine rewrites the residual of the entries that are).  Later
-// kernels read the slots only.
+// (state[2]).  It forms g = grad + acc, and with an accumulation stores the
+// residual each entry has if the candidates are exactly the entries sent
+// (g - 0 = g for the rest).  Later kernels read the slots only.
 template <bool ACC>
 __global__ __launch_bounds__(kBlock) void sp_gather_kernel(const SparseArgs a) {
   __shared__ uint64_t scratch[kBlock / 64];
   uint32_t r, t;
   if (!rank_tile(a, r, t)) return;
+  const uint32_t lo = a.state[4 * r + 2];
   const uint64_t base = static_cast<uint64_t>(t) * kSpTile;
   const uint32_t n = tile_len(a, t);
   float x[kSpUnits][4];
   load_tile<ACC>(a.grad[r], ACC ? a.accum[r] : nullptr, base, n, x);
-  if constexpr (ACC) store_tile(a.accum[r], base, n, x);
-  gather_tile(a, r, t, a.state[4 * r + 2], x, n, scratch);
+  if constexpr (ACC) store_residual(a.accum[r], base, n, lo, x);
+  gather_tile(a, r, t, lo, x, n, scratch);
 }
 
-// The fallback's gather, from the stored values g, for a rank whose sampled
-// bound missed (its groups walk the rank's tiles; other ranks leave at once).
+// The fallback's gather, for a rank whose sampled bound missed (its groups
+// walk the rank's tiles; other ranks leave at once), from g: the gradient,
+// or the accumulation buffer as the fallback's histogram restored it, which
+// then gets the candidates' residuals as the first gather would store them.
 template <bool ACC>
 __global__ __launch_bounds__(kBlock) void sp_gather_fb_kernel(const SparseArgs a) {
   __shared__ uint64_t scratch[kBlock / 64];
@@ -475,6 +510,7 @@ __global__ __launch_bounds__(kBlock) void sp_gather_fb_kernel(const SparseArgs a
     const uint32_t n = tile_len(a, t);
     float x[kSpUnits][4];
     load_tile<false>(key, nullptr, static_cast<uint64_t>(t) * kSpTile, n, x);
+    if constexpr (ACC) store_residual(a.accum[r], static_cast<uint64_t>(t) * kSpTile, n, lo, x);
     gather_tile(a, r, t, lo, x, n, scratch);
   }
 }
@@ -712,8 +748,8 @@ __global__ __launch_bounds__(kSpScanBlock) void sp_scan_kernel(const SparseArgs 
 // the tile's slot that are sent (threshold: all of them; top-K: those above
 // the cut, and ties in index order while ties are left) are written to
 // their place in the rank's message and added into the tile, and with an
-// accumulation a sent top-K entry's residual becomes g - (0 + g); then the
-// tile is stored to every rank's output.  One barrier per rank keeps the
+// accumulation a top-K candidate that is not sent gets g back as its
+// residual; then the tile is stored to every rank's output.  One barrier per rank keeps the
 // adds in rank order; entries of one rank have distinct indices.  Every
 // rank's counts are read at once, and the next rank's first entries are
 // loaded while this rank's are placed.
@@ -788,8 +824,10 @@ __global__ __launch_bounds__(kBlock) void sp_combine_kernel(const SparseArgs a) 
         mi[pos] = static_cast<uint32_t>(base) + local;
         mv[pos] = v;
         acc[local] = acc[local] + v;
-        if constexpr (MODE == RSX_SPARSE_TOPK && ACC) a.accum[r][base + local] = v - (0.0f + v);
       }
+      // a candidate not sent keeps g as its residual
+      if constexpr (MODE == RSX_SPARSE_TOPK && ACC)
+        if (c0 + tid < c && !sent) a.accum[r][base + local] = v;
     }
     __syncthreads();
   }
