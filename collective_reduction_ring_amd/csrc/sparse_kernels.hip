@@ -19,8 +19,8 @@
 //   threshold:  compact  (every element) entries to send, in index order,
 //                        into the tile's slot; the residual
 //   top-K:      sample   per rank: a lower bound for the K-th largest key
-//                        from a strided sample of 16384 keys (two kernels:
-//                        the keys, then the pick)
+//                        from a sample of 65536 keys (runs of 16 spread
+//                        over the rank)
 //               gather   (every element) every key at or above the bound
 //                        into the tile's slot, in index order; into the
 //                        accumulation buffer g = grad + acc, or at a
@@ -53,11 +53,10 @@ namespace {
 
 constexpr uint32_t kSpLaneElems = kSpUnits * 4;  // 16 elements per lane per tile
 constexpr uint32_t kSpWalkGroups = 2048;          // workgroups of the tile-walking kernels
-constexpr uint32_t kSampleMax = 16384;            // top-K: keys sampled per rank for the gather bound
+constexpr uint32_t kSampleMax = 65536;            // top-K: keys sampled per rank for the gather bound
 constexpr int kSampleBlock = 1024;                // lanes of the sampling workgroup
 static_assert(kSpLaneElems * kBlock == kSpTile, "tile = 256 lanes x 16 elements");
-static_assert(kSampleMax % kBlock == 0 && kSampleMax % kSampleBlock == 0, "whole sample groups");
-static_assert(2 * kSampleBlock == kSpBins, "the sample pick holds two bins per lane");
+static_assert(kSampleMax % (16 * kSampleBlock) == 0, "whole sample batches");
 
 // Order-preserving key of an fp32 value for the top-K cut: a larger value has
 // a larger key; -0 and +0 share one key; every NaN has key 0, below -inf.
@@ -316,94 +315,92 @@ __global__ __launch_bounds__(kBlock) void sp_hist0_fb_kernel(const SparseArgs a)
   merge_hist<Dg::kBins>(h, a.hist + r * kSpBins);
 }
 
-// Top-K sample of a rank of n keys: m = min(n, kSampleMax) keys, every
-// (n / m)-th, and the rank j (from the top) of the sample key taken as the
-// gather bound: ceil(K m / n) + 4 sqrt(ceil(K m / n)) + 4.  That key is
-// expected to have about j n / m keys at or above it, comfortably more than
-// K.  j > m means the bound is 0: everything is gathered.
+// Top-K sample of a rank of n keys: m = min(n, kSampleMax) keys, in runs
+// of 16 consecutive elements (one 64-byte line) spread evenly over the rank,
+// and the rank j (from the top) of the sample key taken as the gather
+// bound: ceil(K m / n) + 4 sqrt(ceil(K m / n)) + 4.  That key is expected to
+// have about j n / m keys at or above it, comfortably more than K.  j > m
+// means the bound is 0: everything is gathered.
 struct SamplePlan {
   uint32_t m, j;
-  uint64_t stride;
+  uint64_t run_stride;  // elements from one sampled run of 16 to the next
   __device__ explicit SamplePlan(const SparseArgs& a) {
     const uint64_t n = a.count;
     m = static_cast<uint32_t>(min<uint64_t>(n, kSampleMax));
-    stride = n / m;
+    run_stride = 16 * max<uint64_t>(1, n / kSampleMax);
     const uint64_t kk = (static_cast<uint64_t>(a.k) * m + n - 1) / n;
     uint64_t root = 0;
     while ((root + 1) * (root + 1) <= kk) ++root;  // isqrt, kk <= kSampleMax
     j = static_cast<uint32_t>(min<uint64_t>(kk + 4 * root + 4, 0xFFFFFFFFull));
   }
-  // The sampled keys of rank r sit at the start of the rank's slot area,
-  // which the gather fills only after they have been used.
-  __device__ static uint32_t* keys(const SparseArgs& a, uint32_t r) {
-    return a.gap_idx + static_cast<uint64_t>(r) * a.tiles * kSpTile;
-  }
+  // Element of sample key s < m: run s / 16, position s % 16 in it.  With
+  // n <= kSampleMax the sample is every element.
+  __device__ uint64_t index(uint32_t s) const { return (s >> 4) * run_stride + (s & 15u); }
 };
 
-// Top-K, kSampleMax / kBlock workgroups per rank: the sampled keys (of
-// g = grad + acc, as the gather forms it).
-template <bool ACC>
-__global__ __launch_bounds__(kBlock) void sp_sample_keys_kernel(const SparseArgs a) {
-  constexpr uint32_t kGroups = kSampleMax / kBlock;
-  const uint32_t r = blockIdx.x / kGroups;
-  const uint32_t smp = (blockIdx.x - r * kGroups) * kBlock + threadIdx.x;
-  const SamplePlan p(a);
-  if (p.j > p.m || smp >= p.m) return;
-  const uint64_t idx = smp * p.stride;
-  float v = __builtin_nontemporal_load(a.grad[r] + idx);
-  if constexpr (ACC) v = v + __builtin_nontemporal_load(a.accum[r] + idx);
-  SamplePlan::keys(a, r)[smp] = order_key(v);
-}
-
 // Top-K, one workgroup of kSampleBlock lanes per rank: the gather bound
-// (state[2]) from the rank's sampled keys, the lower edge of the 22-bit key
-// prefix of the j-th largest sampled key.  Everything at or above it is
-// gathered; if that is fewer than K keys the sample misled, and the exact
-// fallback takes over.  The result never depends on the sample.
-__global__ __launch_bounds__(kSampleBlock) void sp_sample_pick_kernel(const SparseArgs a) {
+// (state[2]), the lower edge of the 14-bit key prefix (about 2% of the
+// value) of the j-th largest sampled key of g = grad + acc, from one
+// histogram of the sample.  Everything at or above the bound is gathered;
+// if that is fewer than K keys the sample misled, and the exact fallback
+// takes over.  The result never depends on the sample.
+template <bool ACC>
+__global__ __launch_bounds__(kSampleBlock) void sp_sample_kernel(const SparseArgs a) {
   constexpr int kWaves = kSampleBlock / 64;
   constexpr uint32_t kPer = kSampleMax / kSampleBlock;
-  __shared__ uint32_t h[kSpBins];
+  constexpr uint32_t kBatch = 16;
+  constexpr uint32_t kBins = 16384, kShift = 18;
+  constexpr uint32_t kLaneBins = kBins / kSampleBlock;
+  __shared__ uint32_t h[kBins];
   __shared__ uint32_t scratch[kWaves];
-  __shared__ uint32_t sel[2];
   const uint32_t r = blockIdx.x;
   const SamplePlan p(a);
-  uint32_t lo = 0;
-  if (p.j <= p.m) {
-    const uint32_t* keys = SamplePlan::keys(a, r);
-    uint32_t key[kPer];
-#pragma unroll
-    for (uint32_t q = 0; q < kPer; ++q) key[q] = keys[min(threadIdx.x + q * kSampleBlock, p.m - 1)];
-    uint32_t prefix = 0, need = p.j;
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const uint32_t shift = pass == 0 ? 21u : 10u;
-      const uint32_t high = pass == 0 ? 0u : 0xFFE00000u;
-      for (uint32_t i = threadIdx.x; i < kSpBins; i += kSampleBlock) h[i] = 0;
-      __syncthreads();
-#pragma unroll
-      for (uint32_t q = 0; q < kPer; ++q)
-        if (threadIdx.x + q * kSampleBlock < p.m && (key[q] & high) == prefix)
-          atomicAdd(&h[(key[q] >> shift) & (kSpBins - 1)], 1u);
-      __syncthreads();
-      // thread i holds bins 2047 - 2i and 2046 - 2i (thread 0 the highest)
-      const uint32_t b0 = kSpBins - 1 - 2 * threadIdx.x, b1 = b0 - 1;
-      const uint32_t c0 = h[b0], c1 = h[b1];
-      uint32_t total;
-      const uint32_t above = block_excl<kWaves>(c0 + c1, scratch, total);
-      if (above < need && need <= above + c0 + c1) {
-        const bool first = above + c0 >= need;
-        sel[0] = prefix | ((first ? b0 : b1) << shift);
-        sel[1] = need - (first ? above : above + c0);
-      }
-      __syncthreads();
-      prefix = sel[0];
-      need = sel[1];
+  if (p.j > p.m) {
+    if (threadIdx.x == 0) {
+      a.state[4 * r + 2] = 0;
+      a.state[4 * r + 3] = 0;
     }
-    lo = prefix;
+    return;
   }
-  if (threadIdx.x == 0) {
-    a.state[4 * r + 2] = lo;
+  const float* g = a.grad[r];
+  const float* acc = ACC ? a.accum[r] : nullptr;
+  for (uint32_t i = threadIdx.x; i < kBins; i += kSampleBlock) h[i] = 0;
+  __syncthreads();
+#pragma unroll 1
+  for (uint32_t q0 = 0; q0 < kPer; q0 += kBatch) {
+    // consecutive lanes take consecutive sample keys: 16 lanes per run
+    float gv[kBatch], av[kBatch];
+#pragma unroll
+    for (uint32_t q = 0; q < kBatch; ++q) {
+      const uint64_t idx = p.index(min(threadIdx.x + (q0 + q) * kSampleBlock, p.m - 1));
+      gv[q] = g[idx];
+      if constexpr (ACC) av[q] = acc[idx];
+    }
+#pragma unroll
+    for (uint32_t q = 0; q < kBatch; ++q)
+      if (threadIdx.x + (q0 + q) * kSampleBlock < p.m)
+        atomicAdd(&h[order_key(ACC ? gv[q] + av[q] : gv[q]) >> kShift], 1u);
+  }
+  __syncthreads();
+  // thread i holds bins top, top-1, ..., top-kLaneBins+1 (thread 0 the highest)
+  const uint32_t top = kBins - 1 - threadIdx.x * kLaneBins;
+  uint32_t c[kLaneBins];
+  uint32_t sum = 0;
+#pragma unroll
+  for (uint32_t i = 0; i < kLaneBins; ++i) {
+    c[i] = h[top - i];
+    sum += c[i];
+  }
+  uint32_t total;
+  const uint32_t above = block_excl<kWaves>(sum, scratch, total);
+  if (above < p.j && p.j <= above + sum) {  // exactly one lane: p.j <= m = total
+    uint32_t run = above, bin = top;
+#pragma unroll
+    for (uint32_t i = 0; i < kLaneBins; ++i) {
+      if (run < p.j) bin = top - i;
+      run += c[i];
+    }
+    a.state[4 * r + 2] = bin << kShift;
     a.state[4 * r + 3] = 0;
   }
 }
@@ -864,9 +861,7 @@ hipError_t launch_mode(SparseArgs a, hipStream_t s) {
   hipError_t e = go(reinterpret_cast<const void*>(&sp_init_kernel), a.world, kBlock);
   if constexpr (MODE == RSX_SPARSE_TOPK) {
     auto fn = [](auto k) { return reinterpret_cast<const void*>(k); };
-    if (a.k > 0 && e == hipSuccess)
-      e = go(fn(&sp_sample_keys_kernel<ACC>), static_cast<uint64_t>(a.world) * (kSampleMax / kBlock), kBlock);
-    if (a.k > 0 && e == hipSuccess) e = go(fn(&sp_sample_pick_kernel), a.world, kSampleBlock);
+    if (a.k > 0 && e == hipSuccess) e = go(fn(&sp_sample_kernel<ACC>), a.world, kSampleBlock);
     // The first gather also leaves g in the accumulation buffer, so it runs
     // even when K = 0 has nothing to select.
     if ((a.k > 0 || ACC) && e == hipSuccess) e = go(fn(&sp_gather_kernel<ACC>), rt, kBlock);

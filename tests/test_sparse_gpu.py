@@ -174,30 +174,41 @@ def test_mid_size_w8():
     check(grads, accs, "threshold", threshold=3.6e-3, what="w8 threshold")
 
 
+# keys per rank the top-K gather bound is sampled from: runs of 16
+# consecutive elements, one every 16 * (n // SAMPLE) elements
+SAMPLE = 65536
+
+
+def sampled_positions(n):
+    s = np.arange(min(n, SAMPLE))
+    return (s >> 4) * (16 * max(1, n // SAMPLE)) + (s & 15)
+
+
+@pytest.mark.parametrize("n", [SAMPLE + 3 * 4096 + 5, 2 * SAMPLE + 4096 + 3])
 @pytest.mark.parametrize("fraction", [0.001, 0.01, 0.3, 0.97, 1.0])
-def test_topk_past_the_sample_size(fraction):
-    # more elements than the 16384 keys the top-K bound is sampled from; a
-    # large K makes the sampled rank exceed the sample (the bound is then 0)
-    n = 3 * 16384 + 4096 + 5
-    grads, accs = normal_case((66, int(fraction * 1000)), 3, n)
+def test_topk_past_the_sample_size(fraction, n):
+    # more elements than the keys the top-K bound is sampled from; a large K
+    # makes the sampled rank exceed the sample (the bound is then 0)
+    grads, accs = normal_case((66, int(fraction * 1000), n), 3, n)
     check(grads, accs, "topk", k=rsx.topk_count(n, fraction), what=f"topk {fraction}")
 
 
 @pytest.mark.parametrize("feedback", [True, False])
 @pytest.mark.parametrize("fraction", [0.05, 0.5])
 def test_topk_sample_misled(feedback, fraction):
-    # White-box: the top-K bound is drawn from every (n // 16384)-th key.
+    # White-box: the top-K bound is drawn from the keys at sampled_positions.
     # Large values at exactly those positions make the sample claim that
     # few keys reach the bound's level, so the gather holds fewer than K
     # keys and the exact fallback must take over.  Rank 1 keeps ordinary
     # values, so one call mixes ranks with and without the fallback.
-    n = 5 * 16384 + 777
+    n = 3 * SAMPLE + 777
     w = 3
     grads, accs = normal_case((67, int(fraction * 1000)), w, n)
     rng = np.random.default_rng(68)
-    sampled = np.arange(16384) * (n // 16384)
+    sampled = sampled_positions(n)
+    assert sampled[-1] < n and len(np.unique(sampled)) == SAMPLE
     for r in (0, 2):
-        grads[r][sampled] = (1.0 + rng.random(16384)).astype(f32)
+        grads[r][sampled] = (1.0 + rng.random(SAMPLE)).astype(f32)
     check(grads, accs if feedback else None, "topk", k=rsx.topk_count(n, fraction),
           what=f"misled sample {fraction}")
 
