@@ -162,42 +162,6 @@ __device__ __forceinline__ void load_tile(const float* g, const float* acc, uint
   }
 }
 
-// The loads of one tile, issued ahead of their use: a workgroup that walks
-// several tiles issues tile t+1's loads before it works on tile t, so its
-// barriers do not leave the memory pipeline empty.
-template <bool ACC>
-struct TileLoad {
-  uint4 vg[kSpUnits], va[kSpUnits];
-  __device__ __forceinline__ void issue(const float* g, const float* acc, uint64_t base, uint32_t n) {
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(g + base, n * 4);
-#pragma unroll
-    for (int u = 0; u < static_cast<int>(kSpUnits); ++u)
-      vg[u] = load_stream(rg, threadIdx.x * 16, u * kBlock * 16);
-    if constexpr (ACC) {
-      const __amdgpu_buffer_rsrc_t ra = make_rsrc(acc + base, n * 4);
-#pragma unroll
-      for (int u = 0; u < static_cast<int>(kSpUnits); ++u)
-        va[u] = load_stream(ra, threadIdx.x * 16, u * kBlock * 16);
-    }
-  }
-  // x = g (+ acc), as load_tile gives it
-  __device__ __forceinline__ void values(float (&x)[kSpUnits][4]) const {
-#pragma unroll
-    for (int u = 0; u < static_cast<int>(kSpUnits); ++u) {
-      const uint32_t g4[4] = {vg[u].x, vg[u].y, vg[u].z, vg[u].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if constexpr (ACC) {
-          const uint32_t a4[4] = {va[u].x, va[u].y, va[u].z, va[u].w};
-          x[u][j] = __uint_as_float(g4[j]) + __uint_as_float(a4[j]);
-        } else {
-          x[u][j] = __uint_as_float(g4[j]);
-        }
-      }
-    }
-  }
-};
-
 // Dense tile stores are non-temporal.  Plain stores win a write-only test
 // (2 GiB over 8 buffers: 387 vs 407 us) but lose in these kernels, which
 // also read (compaction 1134 -> 1216 us, top-K combine 612 -> 791 us).
@@ -534,26 +498,41 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
 
 // Walks the slots of tiles [t0, t1) of rank r: each wave of the workgroup
 // takes every (kBlock / 64)-th tile, its lanes the tile's entries.  The
-// lanes first load the entry counts of the wave's next 64 tiles at once, so
-// a tile costs one dependent load, not two.  fn(tile, value, lane, count)
-// runs for every entry and once more per tile with lane >= count (so that
-// per-tile reductions see every lane).
+// lanes first load the entry counts of the wave's next 64 tiles at once,
+// then the first 64 entries of 4 tiles at a time (measured against 16), so
+// that few loads wait on each other.  fn(tile, value, valid, last) runs for
+// every entry of a tile
+// (valid), in tile order, and with last set on the tile's final call, once
+// per 64 entries (a tile with no entry gets one call with none valid).
 template <class F>
 __device__ __forceinline__ void walk_slots(const SparseArgs& a, uint32_t r, uint32_t t0, uint32_t t1, F&& fn) {
   constexpr uint32_t kWaves = kBlock / 64;
+  constexpr uint32_t kAhead = 4;
   const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63u;
   const uint32_t* cnt = a.tile_slot + r * (a.tiles + 1);
+  const float* slots = a.gap_val + static_cast<uint64_t>(r) * a.tiles * kSpTile;
   for (uint32_t tb = t0 + wave; tb < t1; tb += 64 * kWaves) {
     const uint32_t mine = tb + lane * kWaves;
     const uint32_t c_l = mine < t1 ? min(cnt[mine], kSpTile) : 0u;
     const uint32_t nt = min(64u, (t1 - tb + kWaves - 1) / kWaves);
-    for (uint32_t i = 0; i < nt; ++i) {
-      const uint32_t t = tb + i * kWaves;
-      const uint32_t c = __shfl(c_l, i, 64);
-      const float* gv = a.gap_val + (static_cast<uint64_t>(r) * a.tiles + t) * kSpTile;
-      for (uint32_t e0 = 0; e0 < max(c, 1u); e0 += 64) {
-        const uint32_t e = e0 + lane;
-        fn(t, e < c ? gv[e] : 0.0f, e < c, e0 + 64 >= c);
+    for (uint32_t i = 0; i < nt; i += kAhead) {
+      uint32_t c[kAhead];
+      float v[kAhead];
+#pragma unroll
+      for (uint32_t k = 0; k < kAhead; ++k) {
+        const uint32_t t = tb + (i + k) * kWaves;
+        c[k] = i + k < nt ? __shfl(c_l, i + k, 64) : 0u;
+        v[k] = lane < c[k] ? slots[static_cast<uint64_t>(t) * kSpTile + lane] : 0.0f;
+      }
+#pragma unroll
+      for (uint32_t k = 0; k < kAhead; ++k) {
+        if (i + k >= nt) break;
+        const uint32_t t = tb + (i + k) * kWaves;
+        fn(t, v[k], lane < c[k], c[k] <= 64);
+        for (uint32_t e0 = 64; e0 < c[k]; e0 += 64) {  // a tile with more than 64 entries
+          const uint32_t e = e0 + lane;
+          fn(t, e < c[k] ? slots[static_cast<uint64_t>(t) * kSpTile + e] : 0.0f, e < c[k], e0 + 64 >= c[k]);
+        }
       }
     }
   }
@@ -705,17 +684,28 @@ __global__ __launch_bounds__(kSpScanBlock) void sp_scan_kernel(const SparseArgs 
   uint32_t* eqb = a.tile_eqb + r * (n + 1);
   const uint32_t need = MODE == RSX_SPARSE_TOPK ? a.state[4 * r + 1] : 0u;
   uint32_t carry_s = 0, carry_e = 0;
+  // chunk c0's counts; the next chunk's are loaded before this one is scanned
+  uint32_t ns[kPer], ne[kPer];
+  auto load = [&](uint32_t c0) {
+#pragma unroll
+    for (uint32_t i = 0; i < kPer; ++i) {
+      const uint32_t idx = c0 + threadIdx.x * kPer + i;
+      ns[i] = idx < n ? cnt[idx] : 0u;
+      ne[i] = (MODE == RSX_SPARSE_TOPK && idx < n) ? eqc[idx] : 0u;
+    }
+  };
+  load(0);
   for (uint32_t c0 = 0; c0 < n; c0 += kSpScanBlock * kPer) {
     uint32_t s[kPer], e[kPer];
     uint32_t ss = 0, se = 0;
 #pragma unroll
     for (uint32_t i = 0; i < kPer; ++i) {
-      const uint32_t idx = c0 + threadIdx.x * kPer + i;
-      s[i] = idx < n ? cnt[idx] : 0u;
-      e[i] = (MODE == RSX_SPARSE_TOPK && idx < n) ? eqc[idx] : 0u;
+      s[i] = ns[i];
+      e[i] = ne[i];
       ss += s[i];
       se += e[i];
     }
+    if (c0 + kSpScanBlock * kPer < n) load(c0 + kSpScanBlock * kPer);
     uint32_t ts, te = 0;
     uint32_t bs = block_excl<kWaves>(ss, scratch, ts) + carry_s;
     uint32_t be = 0;
