@@ -501,9 +501,9 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
 // lanes first load the entry counts of the wave's next 64 tiles at once,
 // then the first 64 entries of 4 tiles at a time (measured against 16), so
 // that few loads wait on each other.  fn(tile, value, valid, last) runs for
-// every entry of a tile
-// (valid), in tile order, and with last set on the tile's final call, once
-// per 64 entries (a tile with no entry gets one call with none valid).
+// every entry of a tile (valid), in tile order, and with last set on the
+// tile's final call, once per 64 entries (a tile with no entry gets one call
+// with none valid).
 template <class F>
 __device__ __forceinline__ void walk_slots(const SparseArgs& a, uint32_t r, uint32_t t0, uint32_t t1, F&& fn) {
   constexpr uint32_t kWaves = kBlock / 64;
