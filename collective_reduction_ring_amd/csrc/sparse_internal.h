@@ -37,7 +37,8 @@ struct SparseArgs {
   uint32_t* gap_idx;                 // [W][tiles][kSpTile] one slot of entries per tile:
   float* gap_val;                    //   (tile-local index, g value)
   uint32_t* hist;                    // [W][kSpBins]
-  uint32_t* state;                   // [W][4]: cut key, ties still to take
+  uint32_t* state;                   // [W][4]: cut key, entries still to take, top-K gather
+                                     //   bound, fallback flag (1: the bound missed)
   uint64_t count;                    // elements per rank
   uint32_t tiles;                    // tiles per rank
   uint32_t world;
