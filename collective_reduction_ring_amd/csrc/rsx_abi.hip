@@ -304,7 +304,7 @@ bool sparse_layout(int w, size_t count, int mode, bool accum, SparseLayout* l) {
   l->hist = off;
   off += ws_align(ws * kSpBins * 4);
   l->state = off;
-  off += ws_align(ws * 16);
+  off += ws_align(ws * kSpState * 4);
   (void)accum;  // the slots hold everything either mode keeps
   l->total = off;
   return true;

@@ -22,6 +22,16 @@ constexpr uint32_t kSpUnits = 4;        // dwordx4 per lane per tile
 constexpr uint32_t kSpBins = 2048;      // radix-select histogram bins (11-bit digits)
 constexpr uint32_t kSpScanBlock = 1024; // threads of the per-rank offset scan
 
+// Per-rank selection state, kSpState words per rank.
+enum : uint32_t {
+  kStCut = 0,       // top-K: the K-th largest key (its prefix while the search runs)
+  kStNeed = 1,      // top-K: entries still to take at the cut
+  kStBound = 2,     // top-K: every key at or above it is gathered into the slots
+  kStFallback = 3,  // top-K: 1 if the sampled bound missed and the exact fallback runs
+  kStGuess = 4,     // top-K: keys at or above it get the sent-entry residual at the gather
+  kSpState = 8
+};
+
 struct SparseArgs {
   const float* grad[RSX_MAX_RANKS];
   float* accum[RSX_MAX_RANKS];       // error-feedback buffers (read, then the residual)
@@ -37,8 +47,7 @@ struct SparseArgs {
   uint32_t* gap_idx;                 // [W][tiles][kSpTile] one slot of entries per tile:
   float* gap_val;                    //   (tile-local index, g value)
   uint32_t* hist;                    // [W][kSpBins]
-  uint32_t* state;                   // [W][4]: cut key, entries still to take, top-K gather
-                                     //   bound, fallback flag (1: the bound missed)
+  uint32_t* state;                   // [W][kSpState]: kSt* fields
   uint64_t count;                    // elements per rank
   uint32_t tiles;                    // tiles per rank
   uint32_t world;

@@ -23,8 +23,8 @@
 //                        over the rank)
 //               gather   (every element) every key at or above the bound
 //                        into the tile's slot, in index order; into the
-//                        accumulation buffer g = grad + acc, or at a
-//                        candidate the residual it has if sent
+//                        accumulation buffer g = grad + acc, or from a
+//                        guessed cut up the residual of a sent entry
 //               check    per rank: fewer than K keys gathered?  Then an exact
 //                        fallback for that rank alone: a top-digit histogram
 //                        over every element, its bound, and the gather again
@@ -34,8 +34,8 @@
 //   both:       scan     per rank: each tile's offset in the message
 //               combine  per output tile: for each rank in order, its sent
 //                        entries into the message and into an LDS tile (top-K
-//                        puts g back as the residual of candidates not sent);
-//                        the tile to all W outputs
+//                        corrects the residuals the guess got wrong); the
+//                        tile to all W outputs
 //
 // Ties at the cut are taken in index order, as a stable sort from large to
 // small values would take them.  A slot per tile lets a tile write its
@@ -195,9 +195,10 @@ struct Digit {
 
 // ----------------------------------------------------------------- kernels
 
-// Per rank: zero the histogram and the per-tile counts; selection state =
-// (cut key 0, K still to find, gather bound, fallback flag).  K = 0 selects
-// nothing: the cut key and the gather bound are then above every key.
+// Per rank: zero the histogram and the per-tile counts, and set the
+// selection state: cut key 0 with K still to find, no fallback.  K = 0
+// selects nothing: the cut key, the gather bound and the guess are then
+// above every key.
 __global__ __launch_bounds__(kBlock) void sp_init_kernel(const SparseArgs a) {
   const uint32_t r = blockIdx.x;
   for (uint32_t i = threadIdx.x; i < kSpBins; i += kBlock) a.hist[r * kSpBins + i] = 0;
@@ -208,11 +209,13 @@ __global__ __launch_bounds__(kBlock) void sp_init_kernel(const SparseArgs a) {
     a.tile_eqc[r * nt + i] = 0;
   }
   if (threadIdx.x == 0) {
-    uint32_t* st = a.state + 4 * r;
-    st[0] = a.k == 0 ? 0xFFFFFFFFu : 0u;
-    st[1] = a.k;
-    st[2] = a.k == 0 ? 0xFFFFFFFFu : 0u;  // keys gathered into the slots: >= st[2]
-    st[3] = 0;                              // 1: the sampled bound missed, gather again
+    uint32_t* st = a.state + kSpState * r;
+    const uint32_t none = a.k == 0 ? 0xFFFFFFFFu : 0u;  // K = 0: above every key
+    st[kStCut] = none;
+    st[kStNeed] = a.k;
+    st[kStBound] = none;
+    st[kStFallback] = 0;
+    st[kStGuess] = none;
   }
 }
 
@@ -241,7 +244,7 @@ __global__ __launch_bounds__(kBlock) void sp_hist0_fb_kernel(const SparseArgs a)
   __shared__ uint32_t h[kSpBins];
   __shared__ uint32_t cand[kSpTile / 32];  // the tile's first-gather candidates
   const uint32_t r = blockIdx.x / a.hist_groups;
-  if (a.state[4 * r + 3] == 0) return;
+  if (a.state[kSpState * r + kStFallback] == 0) return;
   const uint32_t grp = blockIdx.x - r * a.hist_groups;
   zero_hist(h);
   const float* key = ACC ? a.accum[r] : a.grad[r];
@@ -286,28 +289,33 @@ __global__ __launch_bounds__(kBlock) void sp_hist0_fb_kernel(const SparseArgs a)
 // have about j n / m keys at or above it, comfortably more than K.  j > m
 // means the bound is 0: everything is gathered.
 struct SamplePlan {
-  uint32_t m, j;
+  uint32_t m, kk, j;    // sample size, K scaled to it, the bound's rank
   uint64_t run_stride;  // elements from one sampled run of 16 to the next
   __device__ explicit SamplePlan(const SparseArgs& a) {
     const uint64_t n = a.count;
     m = static_cast<uint32_t>(min<uint64_t>(n, kSampleMax));
     run_stride = 16 * max<uint64_t>(1, n / kSampleMax);
-    const uint64_t kk = (static_cast<uint64_t>(a.k) * m + n - 1) / n;
+    kk = static_cast<uint32_t>((static_cast<uint64_t>(a.k) * m + n - 1) / n);
     uint64_t root = 0;
     while ((root + 1) * (root + 1) <= kk) ++root;  // isqrt, kk <= kSampleMax
-    j = static_cast<uint32_t>(min<uint64_t>(kk + 4 * root + 4, 0xFFFFFFFFull));
+    j = static_cast<uint32_t>(kk + 4 * root + 4);
   }
   // Element of sample key s < m: run s / 16, position s % 16 in it.  With
   // n <= kSampleMax the sample is every element.
   __device__ uint64_t index(uint32_t s) const { return (s >> 4) * run_stride + (s & 15u); }
 };
 
-// Top-K, one workgroup of kSampleBlock lanes per rank: the gather bound
-// (state[2]), the lower edge of the 14-bit key prefix (about 2% of the
-// value) of the j-th largest sampled key of g = grad + acc, from one
-// histogram of the sample.  Everything at or above the bound is gathered;
-// if that is fewer than K keys the sample misled, and the exact fallback
-// takes over.  The result never depends on the sample.
+// Top-K, one workgroup of kSampleBlock lanes per rank, from one histogram
+// of the 14-bit key prefixes (about 2% of the value) of the sampled keys of
+// g = grad + acc:
+// - the gather bound, the lower edge of the j-th largest sampled key's
+//   prefix.  Everything at or above it is gathered; if that is fewer than K
+//   keys the sample misled, and the exact fallback takes over;
+// - the guess, the same for the ceil(K m / n)-th largest sampled key: an
+//   estimate of the cut.  At keys from the guess up, the gather stores the
+//   residual of a sent entry, below it g; the combine corrects the
+//   candidates on the wrong side, which are few when the guess is good.
+// The result never depends on the sample.
 template <bool ACC>
 __global__ __launch_bounds__(kSampleBlock) void sp_sample_kernel(const SparseArgs a) {
   constexpr int kWaves = kSampleBlock / 64;
@@ -319,10 +327,11 @@ __global__ __launch_bounds__(kSampleBlock) void sp_sample_kernel(const SparseArg
   __shared__ uint32_t scratch[kWaves];
   const uint32_t r = blockIdx.x;
   const SamplePlan p(a);
-  if (p.j > p.m) {
+  if (p.j > p.m) {  // everything is gathered, and guessed sent
     if (threadIdx.x == 0) {
-      a.state[4 * r + 2] = 0;
-      a.state[4 * r + 3] = 0;
+      a.state[kSpState * r + kStBound] = 0;
+      a.state[kSpState * r + kStGuess] = 0;
+      a.state[kSpState * r + kStFallback] = 0;
     }
     return;
   }
@@ -357,16 +366,22 @@ __global__ __launch_bounds__(kSampleBlock) void sp_sample_kernel(const SparseArg
   }
   uint32_t total;
   const uint32_t above = block_excl<kWaves>(sum, scratch, total);
-  if (above < p.j && p.j <= above + sum) {  // exactly one lane: p.j <= m = total
+  // the bin of the rank-th largest sampled key, in the one lane that holds it
+  // (1 <= rank <= m = total)
+  auto bin_of = [&](uint32_t rank) {
     uint32_t run = above, bin = top;
 #pragma unroll
     for (uint32_t i = 0; i < kLaneBins; ++i) {
-      if (run < p.j) bin = top - i;
+      if (run < rank) bin = top - i;
       run += c[i];
     }
-    a.state[4 * r + 2] = bin << kShift;
-    a.state[4 * r + 3] = 0;
+    return bin << kShift;
+  };
+  if (above < p.j && p.j <= above + sum) {
+    a.state[kSpState * r + kStBound] = bin_of(p.j);
+    a.state[kSpState * r + kStFallback] = 0;
   }
+  if (above < p.kk && p.kk <= above + sum) a.state[kSpState * r + kStGuess] = bin_of(p.kk);
 }
 
 // Copy this tile's flagged elements, in index order, to its slot; returns
@@ -423,16 +438,17 @@ __device__ __forceinline__ void gather_tile(const SparseArgs& a, uint32_t r, uin
   if (threadIdx.x == 0) a.tile_slot[r * (a.tiles + 1) + t] = cnt;
 }
 
-// The residual of a gathered candidate as if it were sent, g - (0 + g),
-// and g itself elsewhere: what the accumulation buffer holds after a
-// gather.  Most candidates are sent; the combine puts g back at the others.
-__device__ __forceinline__ void store_residual(float* acc, uint64_t base, uint32_t n, uint32_t lo,
+// What the accumulation buffer holds after a gather: at keys from the guess
+// up (all of them candidates) the residual of a sent entry, g - (0 + g),
+// elsewhere g itself, the residual of an entry not sent.  The combine
+// corrects the candidates that the guess put on the wrong side of the cut.
+__device__ __forceinline__ void store_residual(float* acc, uint64_t base, uint32_t n, uint32_t guess,
                                                const float (&x)[kSpUnits][4]) {
   float y[kSpUnits][4];
 #pragma unroll
   for (int u = 0; u < static_cast<int>(kSpUnits); ++u)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) y[u][j] = order_key(x[u][j]) >= lo ? x[u][j] - (0.0f + x[u][j]) : x[u][j];
+    for (int j = 0; j < 4; ++j) y[u][j] = order_key(x[u][j]) >= guess ? x[u][j] - (0.0f + x[u][j]) : x[u][j];
   store_tile(acc, base, n, y);
 }
 
@@ -445,33 +461,34 @@ __global__ __launch_bounds__(kBlock) void sp_gather_kernel(const SparseArgs a) {
   __shared__ uint64_t scratch[kBlock / 64];
   uint32_t r, t;
   if (!rank_tile(a, r, t)) return;
-  const uint32_t lo = a.state[4 * r + 2];
+  const uint32_t lo = a.state[kSpState * r + kStBound];
   const uint64_t base = static_cast<uint64_t>(t) * kSpTile;
   const uint32_t n = tile_len(a, t);
   float x[kSpUnits][4];
   load_tile<ACC>(a.grad[r], ACC ? a.accum[r] : nullptr, base, n, x);
-  if constexpr (ACC) store_residual(a.accum[r], base, n, lo, x);
+  if constexpr (ACC) store_residual(a.accum[r], base, n, a.state[kSpState * r + kStGuess], x);
   gather_tile(a, r, t, lo, x, n, scratch);
 }
 
 // The fallback's gather, for a rank whose sampled bound missed (its groups
 // walk the rank's tiles; other ranks leave at once), from g: the gradient,
 // or the accumulation buffer as the fallback's histogram restored it, which
-// then gets the candidates' residuals as the first gather would store them.
+// then gets the guessed residuals as the first gather would store them.
 template <bool ACC>
 __global__ __launch_bounds__(kBlock) void sp_gather_fb_kernel(const SparseArgs a) {
   __shared__ uint64_t scratch[kBlock / 64];
   const uint32_t r = blockIdx.x / a.hist_groups;
-  if (a.state[4 * r + 3] == 0) return;
+  if (a.state[kSpState * r + kStFallback] == 0) return;
   const uint32_t grp = blockIdx.x - r * a.hist_groups;
-  const uint32_t lo = a.state[4 * r + 2];
+  const uint32_t lo = a.state[kSpState * r + kStBound];
+  const uint32_t guess = a.state[kSpState * r + kStGuess];  // at least lo
   const float* key = ACC ? a.accum[r] : a.grad[r];
   const uint32_t t1 = min(a.tiles, (grp + 1) * a.hist_chunk);
   for (uint32_t t = grp * a.hist_chunk; t < t1; ++t) {
     const uint32_t n = tile_len(a, t);
     float x[kSpUnits][4];
     load_tile<false>(key, nullptr, static_cast<uint64_t>(t) * kSpTile, n, x);
-    if constexpr (ACC) store_residual(a.accum[r], static_cast<uint64_t>(t) * kSpTile, n, lo, x);
+    if constexpr (ACC) store_residual(a.accum[r], static_cast<uint64_t>(t) * kSpTile, n, guess, x);
     gather_tile(a, r, t, lo, x, n, scratch);
   }
 }
@@ -486,7 +503,7 @@ __global__ __launch_bounds__(kSpScanBlock) void sp_check_kernel(const SparseArgs
   for (uint32_t i = threadIdx.x; i < a.tiles; i += kSpScanBlock) sum += cnt[i];
   uint32_t total;
   block_excl<kSpScanBlock / 64>(sum, scratch, total);
-  if (threadIdx.x == 0) a.state[4 * r + 3] = total < a.k ? 1u : 0u;
+  if (threadIdx.x == 0) a.state[kSpState * r + kStFallback] = total < a.k ? 1u : 0u;
 }
 
 // Sum over the 64 lanes of a wave, in every lane.
@@ -547,7 +564,7 @@ __global__ __launch_bounds__(kBlock) void sp_hist_slots_kernel(const SparseArgs 
   const uint32_t r = blockIdx.x / a.hist_groups;
   const uint32_t grp = blockIdx.x - r * a.hist_groups;
   zero_hist(h);
-  const uint32_t prefix = a.state[4 * r];
+  const uint32_t prefix = a.state[kSpState * r + kStCut];
   const uint32_t t0 = grp * a.hist_chunk;
   walk_slots(a, r, t0, min(a.tiles, t0 + a.hist_chunk), [&](uint32_t, float v, bool valid, bool) {
     const uint32_t k = order_key(v);
@@ -562,7 +579,8 @@ __global__ __launch_bounds__(kBlock) void sp_hist_slots_kernel(const SparseArgs 
 // inside that bin.  One workgroup per rank; clears the histogram afterwards.
 // BOUND: the fallback's pick of the top digit, for a rank whose sampled
 // bound missed: the lower edge of the K-th largest key's top-digit bin
-// becomes the gather bound (state[2]); the cut itself is still found later.
+// becomes the gather bound (and the least guess); the cut itself is still
+// found later.
 template <int PASS, bool BOUND = false>
 __global__ __launch_bounds__(kBlock) void sp_pick_kernel(const SparseArgs a) {
   using Dg = Digit<PASS>;
@@ -570,10 +588,10 @@ __global__ __launch_bounds__(kBlock) void sp_pick_kernel(const SparseArgs a) {
   __shared__ uint32_t scratch[kBlock / 64];
   const uint32_t r = blockIdx.x;
   uint32_t* gh = a.hist + r * kSpBins;
-  uint32_t* st = a.state + 4 * r;
-  if (BOUND && st[3] == 0) return;
-  const uint32_t prefix = BOUND ? 0u : st[0];
-  const uint32_t need = BOUND ? a.k : st[1];
+  uint32_t* st = a.state + kSpState * r;
+  if (BOUND && st[kStFallback] == 0) return;
+  const uint32_t prefix = BOUND ? 0u : st[kStCut];
+  const uint32_t need = BOUND ? a.k : st[kStNeed];
   // thread i holds bins top, top-1, ..., top-kPer+1 (thread 0 the highest)
   const uint32_t top = Dg::kBins - 1 - threadIdx.x * kPer;
   uint32_t c[kPer];
@@ -590,10 +608,12 @@ __global__ __launch_bounds__(kBlock) void sp_pick_kernel(const SparseArgs a) {
     for (uint32_t i = 0; i < kPer; ++i) {
       if (run + c[i] >= need) {
         if (BOUND) {
-          st[2] = (top - i) << Dg::kShift;
+          const uint32_t bound = (top - i) << Dg::kShift;
+          st[kStBound] = bound;
+          st[kStGuess] = max(st[kStGuess], bound);  // every key given the residual is gathered
         } else {
-          st[0] = prefix | ((top - i) << Dg::kShift);
-          st[1] = need - run;
+          st[kStCut] = prefix | ((top - i) << Dg::kShift);
+          st[kStNeed] = need - run;
         }
         break;
       }
@@ -616,7 +636,7 @@ __device__ __forceinline__ uint32_t cut_flags(float v, uint32_t cut) {
 __global__ __launch_bounds__(kBlock) void sp_slot_count_kernel(const SparseArgs a) {
   const uint32_t r = blockIdx.x / a.hist_groups;
   const uint32_t grp = blockIdx.x - r * a.hist_groups;
-  const uint32_t cut = a.state[4 * r];
+  const uint32_t cut = a.state[kSpState * r + kStCut];
   const uint32_t t0 = grp * a.hist_chunk;
   uint32_t f = 0;  // this lane's flags in the current tile
   walk_slots(a, r, t0, min(a.tiles, t0 + a.hist_chunk), [&](uint32_t t, float v, bool valid, bool last) {
@@ -682,7 +702,7 @@ __global__ __launch_bounds__(kSpScanBlock) void sp_scan_kernel(const SparseArgs 
   const uint32_t* eqc = a.tile_eqc + r * (n + 1);
   uint32_t* off = a.tile_off + r * (n + 1);
   uint32_t* eqb = a.tile_eqb + r * (n + 1);
-  const uint32_t need = MODE == RSX_SPARSE_TOPK ? a.state[4 * r + 1] : 0u;
+  const uint32_t need = MODE == RSX_SPARSE_TOPK ? a.state[kSpState * r + kStNeed] : 0u;
   uint32_t carry_s = 0, carry_e = 0;
   // chunk c0's counts; the next chunk's are loaded before this one is scanned
   uint32_t ns[kPer], ne[kPer];
@@ -735,15 +755,15 @@ __global__ __launch_bounds__(kSpScanBlock) void sp_scan_kernel(const SparseArgs 
 // the tile's slot that are sent (threshold: all of them; top-K: those above
 // the cut, and ties in index order while ties are left) are written to
 // their place in the rank's message and added into the tile, and with an
-// accumulation a top-K candidate that is not sent gets g back as its
-// residual; then the tile is stored to every rank's output.  One barrier per rank keeps the
+// accumulation the residual of a top-K candidate that the gather guessed
+// wrong is corrected; then the tile is stored to every rank's output.  One barrier per rank keeps the
 // adds in rank order; entries of one rank have distinct indices.  Every
 // rank's counts are read at once, and the next rank's first entries are
 // loaded while this rank's are placed.
 template <int MODE, bool ACC>
 __global__ __launch_bounds__(kBlock) void sp_combine_kernel(const SparseArgs a) {
   __shared__ float4 acc4[kSpTile / 4];
-  __shared__ uint32_t meta[RSX_MAX_RANKS][4];  // entries, message offset, cut, ties to take
+  __shared__ uint32_t meta[RSX_MAX_RANKS][5];  // entries, message offset, cut, ties to take, guess
   __shared__ uint32_t scratch[kBlock / 64];
   float* acc = reinterpret_cast<float*>(acc4);
   const uint32_t t = xcd_tile(blockIdx.x, gridDim.x);
@@ -759,13 +779,15 @@ __global__ __launch_bounds__(kBlock) void sp_combine_kernel(const SparseArgs a) 
     meta[tid][0] = min(a.tile_slot[i], n);
     meta[tid][1] = a.tile_off[i];
     if constexpr (MODE == RSX_SPARSE_TOPK) {
-      const uint32_t need = a.state[4 * tid + 1];
+      const uint32_t need = a.state[kSpState * tid + kStNeed];
       const uint32_t before = a.tile_eqb[i];
-      meta[tid][2] = a.state[4 * tid];
+      meta[tid][2] = a.state[kSpState * tid + kStCut];
       meta[tid][3] = need > before ? need - before : 0u;
+      meta[tid][4] = a.state[kSpState * tid + kStGuess];
     } else {
       meta[tid][2] = 0;
       meta[tid][3] = 0;
+      meta[tid][4] = 0;
     }
   }
   __syncthreads();
@@ -785,7 +807,7 @@ __global__ __launch_bounds__(kBlock) void sp_combine_kernel(const SparseArgs a) 
   float nv;
   fetch(0, 0, nlocal, nv);
   for (uint32_t r = 0; r < world; ++r) {
-    const uint32_t c = meta[r][0], off = meta[r][1], cut = meta[r][2], ties = meta[r][3];
+    const uint32_t c = meta[r][0], off = meta[r][1], cut = meta[r][2], ties = meta[r][3], guess = meta[r][4];
     uint32_t local = nlocal;
     float v = nv;
     if (r + 1 < world) fetch(r + 1, 0, nlocal, nv);
@@ -812,9 +834,14 @@ __global__ __launch_bounds__(kBlock) void sp_combine_kernel(const SparseArgs a) 
         mv[pos] = v;
         acc[local] = acc[local] + v;
       }
-      // a candidate not sent keeps g as its residual
-      if constexpr (MODE == RSX_SPARSE_TOPK && ACC)
-        if (c0 + tid < c && !sent) a.accum[r][base + local] = v;
+      // the candidates the gather's guess put on the wrong side of the cut
+      if constexpr (MODE == RSX_SPARSE_TOPK && ACC) {
+        if (c0 + tid < c) {
+          const bool guessed_sent = order_key(v) >= guess;
+          if (sent && !guessed_sent) a.accum[r][base + local] = v - (0.0f + v);
+          if (!sent && guessed_sent) a.accum[r][base + local] = v;
+        }
+      }
     }
     __syncthreads();
   }
