@@ -213,6 +213,22 @@ def test_topk_sample_misled(feedback, fraction):
           what=f"misled sample {fraction}")
 
 
+@pytest.mark.parametrize("feedback", [True, False])
+def test_topk_sample_misled_low(feedback):
+    # The other direction: the sampled positions hold tiny values, so the
+    # bound and the guessed cut are far too low.  Most elements are then
+    # gathered, most guessed sent, and the combine corrects the residual of
+    # every candidate that is not.
+    n = 2 * SAMPLE + 4096 + 3
+    grads, accs = normal_case(69, 3, n)
+    sampled = sampled_positions(n)
+    for r in (0, 1):
+        grads[r][sampled] = f32(1e-9)
+        accs[r][sampled] = f32(0.0)
+    check(grads, accs if feedback else None, "topk", k=rsx.topk_count(n, 0.01),
+          what="sample misled low")
+
+
 @pytest.mark.parametrize("mode", ["topk", "threshold"])
 def test_graph_capture_replays(mode):
     # The whole sparse call (all its kernels) captured in a HIP graph: every
