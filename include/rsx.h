@@ -246,10 +246,11 @@ size_t rsx_sparse_workspace_size(int nranks, size_t count, rsx_sparse_mode_t mod
  * other; any other overlap among grads, accums, outs, messages, nnz and the
  * workspace is RSX_ERR_ALIASING.  Invalid sizes, pointers, alignment, mode or
  * capacity: RSX_ERR_INVALID_ARGUMENT; count > UINT32_MAX: RSX_ERR_UNSUPPORTED.
- * With an accumulation, top-K first stores g in accums[r] and then rewrites
- * the sent entries, so accums[r] must not be read by other work meanwhile.
- * Validation precedes every HIP call.  Enqueues 4 kernels (threshold) or 11
- * (top-K) on `stream`; allocates nothing and does not synchronise.
+ * With an accumulation, top-K writes accums[r] twice (a guess of the
+ * residual, then its corrections), so accums[r] must not be read by other
+ * work meanwhile.  Validation precedes every HIP call.  Enqueues 4 kernels
+ * (threshold) or up to 16 (top-K) on `stream`; allocates nothing and does
+ * not synchronise.
  */
 rsx_status_t rsx_sparse_all_reduce(const float* const* grads, float* const* accums,
                                    float* const* outs, int nranks, size_t count,
