@@ -229,6 +229,17 @@ def test_topk_sample_misled_low(feedback):
           what="sample misled low")
 
 
+@pytest.mark.timeout(600)
+def test_more_tiles_than_the_bench_shape():
+    # 16386 tiles per rank with a ragged tail: more than the bench shape's
+    # 16384, so the per-rank offset scan's last pass is a partial one; the
+    # top-K sample's runs are 1024 runs of 16 apart
+    n = 16384 * 4096 + 4096 + 5
+    grads, accs = normal_case(70, 2, n)
+    check(grads, accs, "threshold", threshold=3.6e-3, what="16386 tiles, threshold")
+    check(grads, accs, "topk", k=rsx.topk_count(n, 0.001), what="16386 tiles, top-K")
+
+
 @pytest.mark.parametrize("mode", ["topk", "threshold"])
 def test_graph_capture_replays(mode):
     # The whole sparse call (all its kernels) captured in a HIP graph: every
