@@ -304,6 +304,45 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
             st.update(k=plan.k, nnz_rank0=nnz[0], nnz_total=sum(nnz), params=kw)
             res[mode] = st
         return res
+    if name == "sparse_sweep":
+        # The sparsified all-reduce across selection sizes and rank counts, at
+        # the same total bytes as the sparse workload (W * n = 8 * 64 Mi):
+        # N(0, 1e-3) gradients and residuals drawn on the GPU with
+        # torch.Generator(8).
+        gen = torch.Generator(device="cuda:0")
+        gen.manual_seed(8)
+        points = [(8, "topk", {"fraction": f}) for f in (0.001, 0.01, 0.05, 0.1)]
+        points += [(8, "threshold", {"threshold": t}) for t in (3.6e-3, 2.6e-3)]
+        points += [(w, "topk", {"fraction": 0.01}) for w in (2, 16)]
+        points += [(w, "threshold", {"threshold": 3.6e-3}) for w in (2, 16)]
+        rows = []
+        for world in (2, 8, 16):
+            n = 8 * (64 << 20) // world
+            g_all, g = _arena(torch, torch.float32, world, n)
+            a0_all, _ = _arena(torch, torch.float32, world, n)
+            g_all.normal_(0.0, 1e-3, generator=gen)
+            a0_all.normal_(0.0, 1e-3, generator=gen)
+            a_all, a = _arena(torch, torch.float32, world, n)
+            _, out = _arena(torch, torch.float32, world, n)
+
+            def reset():
+                a_all.copy_(a0_all)
+            for w, mode, kw in points:
+                if w != world:
+                    continue
+                log(f"sparse sweep: W={world} n={n} {mode} {kw}")
+                plan = rsx.SparseAllReduce(g, a, out, mode, **kw)
+                ms = time_from_state(plan, reset, reps, warm, torch)
+                nnz = plan.nnz_host()
+                st = _stat(ms, world * n * 16 + 16 * sum(nnz))
+                st.update(world=world, n=n, mode=mode, params=kw, k=plan.k, sent_fraction=sum(nnz) / (world * n))
+                rows.append(st)
+                del plan
+            del g_all, g, a0_all, a_all, a, out
+            torch.cuda.empty_cache()
+        return {"workload": "sparsified all-reduce with error feedback, W * n = 8 * 64 Mi fp32, "
+                            "N(0,1e-3) gradients and residuals",
+                "algorithmic_bytes": "W*n*16 + 16 per message entry", "points": rows}
     if name == "overlap":
         # bucketed all-reduce beside a stand-in backward pass: per bucket, one
         # fp32 matmul on the main stream, then that bucket's all-reduce
@@ -422,7 +461,7 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--workload", default="rs_w8_f32",
                     choices=("rs_w8_f32", "small", "bf16_bucketed", "int32_w16", "fused", "sweep",
-                             "sparse", "dtypes", "overlap", "size_sweep", "ceilings"),
+                             "sparse", "sparse_sweep", "dtypes", "overlap", "size_sweep", "ceilings"),
                     help="rs_w8_f32 (default) is the headline line; the others print timings only")
     args = ap.parse_args()
 

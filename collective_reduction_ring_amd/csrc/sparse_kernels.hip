@@ -31,7 +31,8 @@
 //               hist0-2  (slots) top-, middle- and low-digit histograms
 //               pick     after each histogram: the digit of the K-th key
 //               count    (slots) per tile, candidates above / equal to the cut
-//   both:       scan     per rank: each tile's offset in the message
+//   both:       scan     per rank: each tile's offset in the message (one
+//                        workgroup per 4096 tiles)
 //               combine  per output tile: for each rank in order, its sent
 //                        entries into the message and into an LDS tile (top-K
 //                        corrects the residuals the guess got wrong); the
@@ -55,6 +56,7 @@ constexpr uint32_t kSpLaneElems = kSpUnits * 4;  // 16 elements per lane per til
 constexpr uint32_t kSpWalkGroups = 2048;          // workgroups of the tile-walking kernels
 constexpr uint32_t kSampleMax = 65536;            // top-K: keys sampled per rank for the gather bound
 constexpr int kSampleBlock = 1024;                // lanes of the sampling workgroup
+constexpr uint32_t kScanChunk = 4 * kSpScanBlock;  // tiles per workgroup of the offset scan
 static_assert(kSpLaneElems * kBlock == kSpTile, "tile = 256 lanes x 16 elements");
 static_assert(kSampleMax % (16 * kSampleBlock) == 0, "whole sample batches");
 
@@ -500,6 +502,7 @@ __global__ __launch_bounds__(kSpScanBlock) void sp_check_kernel(const SparseArgs
   const uint32_t r = blockIdx.x;
   const uint32_t* cnt = a.tile_slot + r * (a.tiles + 1);
   uint32_t sum = 0;
+#pragma unroll 8
   for (uint32_t i = threadIdx.x; i < a.tiles; i += kSpScanBlock) sum += cnt[i];
   uint32_t total;
   block_excl<kSpScanBlock / 64>(sum, scratch, total);
@@ -687,66 +690,66 @@ __global__ __launch_bounds__(kBlock) void sp_compact_kernel(const SparseArgs a) 
   }
 }
 
-// Per rank: exclusive prefixes of the tile counts.  A tile's message offset
-// is the entries sent for sure before it plus the ties before it, up to the
-// number of ties to take; tile_eqb holds the ties before it.  The last slot
-// and nnz[r] get the message length.
+// Exclusive prefixes of a rank's tile counts, one workgroup per chunk of
+// kScanChunk tiles.  A workgroup first sums the counts of every tile before
+// its chunk itself (coalesced reads, many in flight), so no workgroup waits
+// for another.  A tile's message offset is the entries sent for sure before
+// it plus the ties before it, up to the number of ties to take; tile_eqb
+// holds the ties before it.  The last chunk's workgroup also writes the
+// message length into the last slot and nnz[r].
 template <int MODE>
 __global__ __launch_bounds__(kSpScanBlock) void sp_scan_kernel(const SparseArgs a) {
-  constexpr uint32_t kPer = 4;  // tiles per lane (16 measured slower: the lanes' loads spread over 4x the lines)
+  constexpr bool TOPK = MODE == RSX_SPARSE_TOPK;
+  constexpr uint32_t kPer = kScanChunk / kSpScanBlock;
   constexpr int kWaves = kSpScanBlock / 64;
   __shared__ uint32_t scratch[kWaves];
-  const uint32_t r = blockIdx.x;
   const uint32_t n = a.tiles;
+  const uint32_t groups = (n + kScanChunk - 1) / kScanChunk;
+  const uint32_t r = blockIdx.x / groups;
+  const uint32_t c0 = (blockIdx.x - r * groups) * kScanChunk;
   const uint32_t* cnt = a.tile_cnt + r * (n + 1);
   const uint32_t* eqc = a.tile_eqc + r * (n + 1);
   uint32_t* off = a.tile_off + r * (n + 1);
   uint32_t* eqb = a.tile_eqb + r * (n + 1);
-  const uint32_t need = MODE == RSX_SPARSE_TOPK ? a.state[kSpState * r + kStNeed] : 0u;
-  uint32_t carry_s = 0, carry_e = 0;
-  // chunk c0's counts; the next chunk's are loaded before this one is scanned
-  uint32_t ns[kPer], ne[kPer];
-  auto load = [&](uint32_t c0) {
+  const uint32_t need = TOPK ? a.state[kSpState * r + kStNeed] : 0u;
+  // this chunk's counts: 4 consecutive tiles per lane
+  uint32_t s[kPer], e[kPer];
+  uint32_t ss = 0, se = 0;
 #pragma unroll
-    for (uint32_t i = 0; i < kPer; ++i) {
-      const uint32_t idx = c0 + threadIdx.x * kPer + i;
-      ns[i] = idx < n ? cnt[idx] : 0u;
-      ne[i] = (MODE == RSX_SPARSE_TOPK && idx < n) ? eqc[idx] : 0u;
-    }
-  };
-  load(0);
-  for (uint32_t c0 = 0; c0 < n; c0 += kSpScanBlock * kPer) {
-    uint32_t s[kPer], e[kPer];
-    uint32_t ss = 0, se = 0;
-#pragma unroll
-    for (uint32_t i = 0; i < kPer; ++i) {
-      s[i] = ns[i];
-      e[i] = ne[i];
-      ss += s[i];
-      se += e[i];
-    }
-    if (c0 + kSpScanBlock * kPer < n) load(c0 + kSpScanBlock * kPer);
-    uint32_t ts, te = 0;
-    uint32_t bs = block_excl<kWaves>(ss, scratch, ts) + carry_s;
-    uint32_t be = 0;
-    if constexpr (MODE == RSX_SPARSE_TOPK) be = block_excl<kWaves>(se, scratch, te) + carry_e;
-#pragma unroll
-    for (uint32_t i = 0; i < kPer; ++i) {
-      const uint32_t idx = c0 + threadIdx.x * kPer + i;
-      if (idx < n) {
-        off[idx] = bs + min(be, need);
-        eqb[idx] = be;
-      }
-      bs += s[i];
-      be += e[i];
-    }
-    carry_s += ts;
-    carry_e += te;
+  for (uint32_t i = 0; i < kPer; ++i) {
+    const uint32_t idx = c0 + threadIdx.x * kPer + i;
+    s[i] = idx < n ? cnt[idx] : 0u;
+    e[i] = (TOPK && idx < n) ? eqc[idx] : 0u;
+    ss += s[i];
+    se += e[i];
   }
-  if (threadIdx.x == 0) {
-    const uint32_t len = carry_s + min(carry_e, need);
+  // every tile before the chunk
+  uint32_t ps = 0, pe = 0;
+#pragma unroll 8
+  for (uint32_t i = threadIdx.x; i < c0; i += kSpScanBlock) {
+    ps += cnt[i];
+    if constexpr (TOPK) pe += eqc[i];
+  }
+  uint32_t carry_s, carry_e = 0, ts, te = 0;
+  block_excl<kWaves>(ps, scratch, carry_s);
+  if constexpr (TOPK) block_excl<kWaves>(pe, scratch, carry_e);
+  uint32_t bs = block_excl<kWaves>(ss, scratch, ts) + carry_s;
+  uint32_t be = 0;
+  if constexpr (TOPK) be = block_excl<kWaves>(se, scratch, te) + carry_e;
+#pragma unroll
+  for (uint32_t i = 0; i < kPer; ++i) {
+    const uint32_t idx = c0 + threadIdx.x * kPer + i;
+    if (idx < n) {
+      off[idx] = bs + min(be, need);
+      eqb[idx] = be;
+    }
+    bs += s[i];
+    be += e[i];
+  }
+  if (c0 + kScanChunk >= n && threadIdx.x == 0) {
+    const uint32_t len = carry_s + ts + min(carry_e + te, need);
     off[n] = len;
-    eqb[n] = carry_e;
+    eqb[n] = carry_e + te;
     a.nnz[r] = len;
   }
 }
@@ -898,7 +901,9 @@ hipError_t launch_mode(SparseArgs a, hipStream_t s) {
   } else {
     if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_compact_kernel<ACC>), rt, kBlock);
   }
-  if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_scan_kernel<MODE>), a.world, kSpScanBlock);
+  const uint64_t scan_groups = (a.tiles + kScanChunk - 1) / kScanChunk;
+  if (e == hipSuccess)
+    e = go(reinterpret_cast<const void*>(&sp_scan_kernel<MODE>), a.world * scan_groups, kSpScanBlock);
   if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_combine_kernel<MODE, ACC>), xcd_grid(a.tiles), kBlock);
   return e;
 }
