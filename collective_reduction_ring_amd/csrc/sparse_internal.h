@@ -17,8 +17,9 @@ namespace rsx {
 // order into a slot of its own, so the combine finds the entries of an output
 // tile in every rank's slot, without a search, and places them in the
 // message at offsets scanned in between.
-constexpr uint32_t kSpTile = 4096;      // elements per tile: 256 lanes x 4 dwordx4
-constexpr uint32_t kSpUnits = 4;        // dwordx4 per lane per tile
+constexpr uint32_t kSpTile = 4096;      // elements per tile: 1024 lanes x 1 dwordx4
+constexpr uint32_t kSpUnits = 1;        // dwordx4 per lane per tile
+constexpr uint32_t kSpTileBlock = kSpTile / (4 * kSpUnits);  // lanes of the per-tile kernels
 constexpr uint32_t kSpBins = 2048;      // radix-select histogram bins (11-bit digits)
 constexpr uint32_t kSpScanBlock = 1024; // threads of the per-rank offset scan
 

@@ -52,12 +52,12 @@
 namespace rsx {
 namespace {
 
-constexpr uint32_t kSpLaneElems = kSpUnits * 4;  // 16 elements per lane per tile
+constexpr uint32_t kSpLaneElems = kSpUnits * 4;  // elements per lane per tile
 constexpr uint32_t kSpWalkGroups = 2048;          // workgroups of the tile-walking kernels
 constexpr uint32_t kSampleMax = 65536;            // top-K: keys sampled per rank for the gather bound
 constexpr int kSampleBlock = 1024;                // lanes of the sampling workgroup
 constexpr uint32_t kScanChunk = 4 * kSpScanBlock;  // tiles per workgroup of the offset scan
-static_assert(kSpLaneElems * kBlock == kSpTile, "tile = 256 lanes x 16 elements");
+static_assert(kSpLaneElems * kSpTileBlock == kSpTile, "a tile is one element group per lane");
 static_assert(kSampleMax % (16 * kSampleBlock) == 0, "whole sample batches");
 
 // Order-preserving key of an fp32 value for the top-K cut: a larger value has
@@ -100,39 +100,12 @@ __device__ __forceinline__ uint32_t block_excl(uint32_t v, uint32_t* scratch, ui
   return before + inc - v;
 }
 
-// 64-bit versions, for four 16-bit counts scanned at once.
-__device__ __forceinline__ uint64_t wave_incl64(uint64_t v) {
-  const uint32_t lane = threadIdx.x & 63u;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t lo = __shfl_up(static_cast<uint32_t>(v), d, 64);
-    const uint32_t hi = __shfl_up(static_cast<uint32_t>(v >> 32), d, 64);
-    if (lane >= static_cast<uint32_t>(d)) v += (static_cast<uint64_t>(hi) << 32) | lo;
-  }
-  return v;
-}
-
-template <int NW>
-__device__ __forceinline__ uint64_t block_excl64(uint64_t v, uint64_t* scratch, uint64_t& total) {
-  const uint64_t inc = wave_incl64(v);
-  const uint32_t w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63u) == 63u) scratch[w] = inc;
-  __syncthreads();
-  uint64_t before = 0, sum = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const uint64_t s = scratch[i];
-    before += (static_cast<uint32_t>(i) < w) ? s : 0u;
-    sum += s;
-  }
-  __syncthreads();
-  total = sum;
-  return before + inc - v;
-}
-
-// The 16 values of this lane in tile `base` of a rank: x[u][j] is element
-// u*1024 + 4*lane + j of the tile.  With ACC, x = g + acc (one fp32 add, the
-// page's error feedback); lanes past the rank's end read zeros.
+// This lane's values in tile `base` of a rank (kSpTileBlock lanes): x[u][j]
+// is element 4 (u kSpTileBlock + lane) + j of the tile.  One 16-byte vector
+// per lane and stream: on this GPU that streams faster than several per lane
+// (two reads and an in-place write of 2 GiB: 6.5 against 6.0 TB/s).  With
+// ACC, x = g + acc (one fp32 add, the page's error feedback); lanes past the
+// rank's end read zeros.
 template <bool ACC>
 __device__ __forceinline__ void load_tile(const float* g, const float* acc, uint64_t base, uint32_t n,
                                           float (&x)[kSpUnits][4]) {
@@ -140,12 +113,12 @@ __device__ __forceinline__ void load_tile(const float* g, const float* acc, uint
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(g + base, n * 4);
   uint4 vg[kSpUnits];
 #pragma unroll
-  for (int u = 0; u < static_cast<int>(kSpUnits); ++u) vg[u] = load_stream(rg, tid * 16, u * kBlock * 16);
+  for (int u = 0; u < static_cast<int>(kSpUnits); ++u) vg[u] = load_stream(rg, tid * 16, u * kSpTileBlock * 16);
   if constexpr (ACC) {
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(acc + base, n * 4);
     uint4 va[kSpUnits];
 #pragma unroll
-    for (int u = 0; u < static_cast<int>(kSpUnits); ++u) va[u] = load_stream(ra, tid * 16, u * kBlock * 16);
+    for (int u = 0; u < static_cast<int>(kSpUnits); ++u) va[u] = load_stream(ra, tid * 16, u * kSpTileBlock * 16);
 #pragma unroll
     for (int u = 0; u < static_cast<int>(kSpUnits); ++u) {
       x[u][0] = __uint_as_float(vg[u].x) + __uint_as_float(va[u].x);
@@ -172,7 +145,7 @@ __device__ __forceinline__ void store_tile(float* dst, uint64_t base, uint32_t n
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(dst + base, n * 4);
 #pragma unroll
   for (int u = 0; u < static_cast<int>(kSpUnits); ++u)
-    store_b128<kStoreStream>(rd, threadIdx.x * 16, u * kBlock * 16,
+    store_b128<kStoreStream>(rd, threadIdx.x * 16, u * kSpTileBlock * 16,
                              make_uint4(__float_as_uint(x[u][0]), __float_as_uint(x[u][1]),
                                         __float_as_uint(x[u][2]), __float_as_uint(x[u][3])));
 }
@@ -182,9 +155,10 @@ __device__ __forceinline__ uint32_t tile_len(const SparseArgs& a, uint32_t t) {
   return static_cast<uint32_t>(min<uint64_t>(kSpTile, a.count - static_cast<uint64_t>(t) * kSpTile));
 }
 
-// Element u*1024 + 4*lane + j of a tile lies inside the rank when below n.
+// Element 4 (u kSpTileBlock + lane) + j of a tile lies inside the rank when
+// below n.
 __device__ __forceinline__ bool in_tile(int u, int j, uint32_t n) {
-  return static_cast<uint32_t>(u) * kBlock * 4 + threadIdx.x * 4 + static_cast<uint32_t>(j) < n;
+  return (static_cast<uint32_t>(u) * kSpTileBlock + threadIdx.x) * 4 + static_cast<uint32_t>(j) < n;
 }
 
 // Radix digits of the top-K cut, most significant first.
@@ -221,16 +195,17 @@ __global__ __launch_bounds__(kBlock) void sp_init_kernel(const SparseArgs a) {
   }
 }
 
-// Workgroup-local histogram -> the rank's histogram in HBM.
-template <uint32_t BINS>
+// Workgroup-local histogram -> the rank's histogram in HBM (NT lanes).
+template <uint32_t BINS, uint32_t NT = kBlock>
 __device__ __forceinline__ void merge_hist(const uint32_t* h, uint32_t* gh) {
   __syncthreads();
-  for (uint32_t i = threadIdx.x; i < BINS; i += kBlock)
+  for (uint32_t i = threadIdx.x; i < BINS; i += NT)
     if (h[i] != 0) atomicAdd(&gh[i], h[i]);
 }
 
+template <uint32_t NT = kBlock>
 __device__ __forceinline__ void zero_hist(uint32_t* h) {
-  for (uint32_t i = threadIdx.x; i < kSpBins; i += kBlock) h[i] = 0;
+  for (uint32_t i = threadIdx.x; i < kSpBins; i += NT) h[i] = 0;
   __syncthreads();
 }
 
@@ -241,14 +216,14 @@ __device__ __forceinline__ void zero_hist(uint32_t* h) {
 // the slot and put back, so that the buffer holds g everywhere again for
 // the fallback's gather.  Ranks that need no fallback leave at once.
 template <bool ACC>
-__global__ __launch_bounds__(kBlock) void sp_hist0_fb_kernel(const SparseArgs a) {
+__global__ __launch_bounds__(kSpTileBlock) void sp_hist0_fb_kernel(const SparseArgs a) {
   using Dg = Digit<0>;
   __shared__ uint32_t h[kSpBins];
   __shared__ uint32_t cand[kSpTile / 32];  // the tile's first-gather candidates
   const uint32_t r = blockIdx.x / a.hist_groups;
   if (a.state[kSpState * r + kStFallback] == 0) return;
   const uint32_t grp = blockIdx.x - r * a.hist_groups;
-  zero_hist(h);
+  zero_hist<kSpTileBlock>(h);
   const float* key = ACC ? a.accum[r] : a.grad[r];
   const uint32_t t0 = grp * a.hist_chunk;
   const uint32_t t1 = min(a.tiles, t0 + a.hist_chunk);
@@ -256,11 +231,11 @@ __global__ __launch_bounds__(kBlock) void sp_hist0_fb_kernel(const SparseArgs a)
     const uint32_t n = tile_len(a, t);
     const uint64_t base = static_cast<uint64_t>(t) * kSpTile;
     if constexpr (ACC) {
-      for (uint32_t i = threadIdx.x; i < kSpTile / 32; i += kBlock) cand[i] = 0;
+      for (uint32_t i = threadIdx.x; i < kSpTile / 32; i += kSpTileBlock) cand[i] = 0;
       __syncthreads();
       const uint32_t c = min(a.tile_slot[r * (a.tiles + 1) + t], n);
       const uint64_t slot = (static_cast<uint64_t>(r) * a.tiles + t) * kSpTile;
-      for (uint32_t e = threadIdx.x; e < c; e += kBlock) {
+      for (uint32_t e = threadIdx.x; e < c; e += kSpTileBlock) {
         const uint32_t local = min(a.gap_idx[slot + e], n - 1);
         const float v = a.gap_val[slot + e];
         atomicOr(&cand[local >> 5], 1u << (local & 31u));
@@ -275,13 +250,13 @@ __global__ __launch_bounds__(kBlock) void sp_hist0_fb_kernel(const SparseArgs a)
     for (int u = 0; u < static_cast<int>(kSpUnits); ++u)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t local = static_cast<uint32_t>(u) * kBlock * 4 + threadIdx.x * 4 + j;
+        const uint32_t local = (static_cast<uint32_t>(u) * kSpTileBlock + threadIdx.x) * 4 + j;
         const bool counted = ACC && ((cand[local >> 5] >> (local & 31u)) & 1u);
         if (in_tile(u, j, n) && !counted) atomicAdd(&h[order_key(x[u][j]) >> Dg::kShift], 1u);
       }
     if constexpr (ACC) __syncthreads();  // the bitmap is reused by the next tile
   }
-  merge_hist<Dg::kBins>(h, a.hist + r * kSpBins);
+  merge_hist<Dg::kBins, kSpTileBlock>(h, a.hist + r * kSpBins);
 }
 
 // Top-K sample of a rank of n keys: m = min(n, kSampleMax) keys, in runs
@@ -387,34 +362,24 @@ __global__ __launch_bounds__(kSampleBlock) void sp_sample_kernel(const SparseArg
 }
 
 // Copy this tile's flagged elements, in index order, to its slot; returns
-// how many there are.  Element u*1024 + 4*lane + j comes after every element
-// of units < u, so the four units' counts (at most 1024 each) are scanned at
-// once as 16-bit fields of one 64-bit value.
+// how many there are.  Lane l holds elements 4l .. 4l + 3, so one block scan
+// of the lanes' counts places every entry.
+static_assert(kSpUnits == 1, "compact_to_slot takes one element group per lane");
 __device__ __forceinline__ uint32_t compact_to_slot(const SparseArgs& a, uint64_t slot,
                                                     const uint32_t (&f)[kSpUnits][4],
-                                                    const float (&x)[kSpUnits][4], uint64_t* scratch) {
-  uint64_t c = 0;
+                                                    const float (&x)[kSpUnits][4], uint32_t* scratch) {
+  const uint32_t c = f[0][0] + f[0][1] + f[0][2] + f[0][3];
+  uint32_t tot;
+  uint32_t at = block_excl<kSpTileBlock / 64>(c, scratch, tot);
 #pragma unroll
-  for (int u = 0; u < static_cast<int>(kSpUnits); ++u)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) c += static_cast<uint64_t>(f[u][j]) << (16 * u);
-  uint64_t tot;
-  const uint64_t pre = block_excl64<kBlock / 64>(c, scratch, tot);
-  uint32_t before = 0;  // entries of the earlier units
-#pragma unroll
-  for (int u = 0; u < static_cast<int>(kSpUnits); ++u) {
-    uint32_t at = before + static_cast<uint32_t>((pre >> (16 * u)) & 0xFFFFu);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (f[u][j]) {
-        a.gap_idx[slot + at] = static_cast<uint32_t>(u) * kBlock * 4 + threadIdx.x * 4 + j;
-        a.gap_val[slot + at] = x[u][j];
-      }
-      at += f[u][j];
+  for (int j = 0; j < 4; ++j) {
+    if (f[0][j]) {
+      a.gap_idx[slot + at] = threadIdx.x * 4 + j;
+      a.gap_val[slot + at] = x[0][j];
     }
-    before += static_cast<uint32_t>((tot >> (16 * u)) & 0xFFFFu);
+    at += f[0][j];
   }
-  return before;
+  return tot;
 }
 
 // Rank and tile of workgroup b in a (rank, tile) grid; false past the end.
@@ -429,7 +394,7 @@ __device__ __forceinline__ bool rank_tile(const SparseArgs& a, uint32_t& r, uint
 // Every key of tile t of rank r at or above `lo` into the tile's slot, in
 // index order.
 __device__ __forceinline__ void gather_tile(const SparseArgs& a, uint32_t r, uint32_t t, uint32_t lo,
-                                            const float (&x)[kSpUnits][4], uint32_t n, uint64_t* scratch) {
+                                            const float (&x)[kSpUnits][4], uint32_t n, uint32_t* scratch) {
   uint32_t f[kSpUnits][4];
 #pragma unroll
   for (int u = 0; u < static_cast<int>(kSpUnits); ++u)
@@ -459,8 +424,8 @@ __device__ __forceinline__ void store_residual(float* acc, uint64_t base, uint32
 // residual each entry has if the candidates are exactly the entries sent
 // (g - 0 = g for the rest).  Later kernels read the slots only.
 template <bool ACC>
-__global__ __launch_bounds__(kBlock) void sp_gather_kernel(const SparseArgs a) {
-  __shared__ uint64_t scratch[kBlock / 64];
+__global__ __launch_bounds__(kSpTileBlock) void sp_gather_kernel(const SparseArgs a) {
+  __shared__ uint32_t scratch[kSpTileBlock / 64];
   uint32_t r, t;
   if (!rank_tile(a, r, t)) return;
   const uint32_t lo = a.state[kSpState * r + kStBound];
@@ -477,8 +442,8 @@ __global__ __launch_bounds__(kBlock) void sp_gather_kernel(const SparseArgs a) {
 // or the accumulation buffer as the fallback's histogram restored it, which
 // then gets the guessed residuals as the first gather would store them.
 template <bool ACC>
-__global__ __launch_bounds__(kBlock) void sp_gather_fb_kernel(const SparseArgs a) {
-  __shared__ uint64_t scratch[kBlock / 64];
+__global__ __launch_bounds__(kSpTileBlock) void sp_gather_fb_kernel(const SparseArgs a) {
+  __shared__ uint32_t scratch[kSpTileBlock / 64];
   const uint32_t r = blockIdx.x / a.hist_groups;
   if (a.state[kSpState * r + kStFallback] == 0) return;
   const uint32_t grp = blockIdx.x - r * a.hist_groups;
@@ -662,8 +627,8 @@ __global__ __launch_bounds__(kBlock) void sp_slot_count_kernel(const SparseArgs 
 // thresholded array, which keeps a +-0 reaching the threshold (a sent inf
 // leaves NaN).
 template <bool ACC>
-__global__ __launch_bounds__(kBlock) void sp_compact_kernel(const SparseArgs a) {
-  __shared__ uint64_t scratch[kBlock / 64];
+__global__ __launch_bounds__(kSpTileBlock) void sp_compact_kernel(const SparseArgs a) {
+  __shared__ uint32_t scratch[kSpTileBlock / 64];
   uint32_t r, t;
   if (!rank_tile(a, r, t)) return;
   const uint64_t base = static_cast<uint64_t>(t) * kSpTile;
@@ -759,12 +724,16 @@ __global__ __launch_bounds__(kSpScanBlock) void sp_scan_kernel(const SparseArgs 
 // the cut, and ties in index order while ties are left) are written to
 // their place in the rank's message and added into the tile, and with an
 // accumulation the residual of a top-K candidate that the gather guessed
-// wrong is corrected; then the tile is stored to every rank's output.  One barrier per rank keeps the
-// adds in rank order; entries of one rank have distinct indices.  Every
-// rank's counts are read at once, and the next rank's first entries are
-// loaded while this rank's are placed.
+// wrong is corrected; then the tile is stored to every rank's output.  One
+// barrier per rank keeps the adds in rank order; entries of one rank have
+// distinct indices.  Every rank's counts are read at once, and the next
+// rank's first entries are loaded while this rank's are placed.  256 lanes,
+// 4 vectors each: a tile holds few entries per rank, and 1024 lanes with one
+// vector each spent the time in their per-rank scans and barriers (threshold
+// combine 434 -> 662 us).
 template <int MODE, bool ACC>
 __global__ __launch_bounds__(kBlock) void sp_combine_kernel(const SparseArgs a) {
+  constexpr uint32_t kVecs = kSpTile / 4 / kBlock;  // 16-byte vectors per lane of the output tile
   __shared__ float4 acc4[kSpTile / 4];
   __shared__ uint32_t meta[RSX_MAX_RANKS][5];  // entries, message offset, cut, ties to take, guess
   __shared__ uint32_t scratch[kBlock / 64];
@@ -776,7 +745,7 @@ __global__ __launch_bounds__(kBlock) void sp_combine_kernel(const SparseArgs a) 
   const uint32_t world = a.world;
   const uint32_t tid = threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < static_cast<int>(kSpUnits); ++u) acc4[u * kBlock + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (uint32_t u = 0; u < kVecs; ++u) acc4[u * kBlock + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
   if (tid < world) {
     const uint32_t i = tid * (a.tiles + 1) + t;
     meta[tid][0] = min(a.tile_slot[i], n);
@@ -848,16 +817,17 @@ __global__ __launch_bounds__(kBlock) void sp_combine_kernel(const SparseArgs a) 
     }
     __syncthreads();
   }
-  float x[kSpUnits][4];
+  uint4 q[kVecs];
 #pragma unroll
-  for (int u = 0; u < static_cast<int>(kSpUnits); ++u) {
-    const float4 q = acc4[u * kBlock + tid];
-    x[u][0] = q.x;
-    x[u][1] = q.y;
-    x[u][2] = q.z;
-    x[u][3] = q.w;
+  for (uint32_t u = 0; u < kVecs; ++u) {
+    const float4 v = acc4[u * kBlock + tid];
+    q[u] = make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w));
   }
-  for (uint32_t r = 0; r < world; ++r) store_tile(a.out[r], base, n, x);
+  for (uint32_t r = 0; r < world; ++r) {
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.out[r] + base, n * 4);
+#pragma unroll
+    for (uint32_t u = 0; u < kVecs; ++u) store_b128<kStoreStream>(rd, tid * 16, u * kBlock * 16, q[u]);
+  }
 }
 
 __global__ void sp_zero_nnz_kernel(uint32_t* nnz, int world) {
@@ -884,12 +854,12 @@ hipError_t launch_mode(SparseArgs a, hipStream_t s) {
     if (a.k > 0 && e == hipSuccess) e = go(fn(&sp_sample_kernel<ACC>), a.world, kSampleBlock);
     // The first gather also leaves g in the accumulation buffer, so it runs
     // even when K = 0 has nothing to select.
-    if ((a.k > 0 || ACC) && e == hipSuccess) e = go(fn(&sp_gather_kernel<ACC>), rt, kBlock);
+    if ((a.k > 0 || ACC) && e == hipSuccess) e = go(fn(&sp_gather_kernel<ACC>), rt, kSpTileBlock);
     if (a.k > 0) {
       if (e == hipSuccess) e = go(fn(&sp_check_kernel), a.world, kSpScanBlock);
-      if (e == hipSuccess) e = go(fn(&sp_hist0_fb_kernel<ACC>), hg, kBlock);
+      if (e == hipSuccess) e = go(fn(&sp_hist0_fb_kernel<ACC>), hg, kSpTileBlock);
       if (e == hipSuccess) e = go(fn(&sp_pick_kernel<0, true>), a.world, kBlock);
-      if (e == hipSuccess) e = go(fn(&sp_gather_fb_kernel<ACC>), hg, kBlock);
+      if (e == hipSuccess) e = go(fn(&sp_gather_fb_kernel<ACC>), hg, kSpTileBlock);
       if (e == hipSuccess) e = go(fn(&sp_hist_slots_kernel<0>), hg, kBlock);
       if (e == hipSuccess) e = go(fn(&sp_pick_kernel<0>), a.world, kBlock);
       if (e == hipSuccess) e = go(fn(&sp_hist_slots_kernel<1>), hg, kBlock);
@@ -899,7 +869,7 @@ hipError_t launch_mode(SparseArgs a, hipStream_t s) {
       if (e == hipSuccess) e = go(fn(&sp_slot_count_kernel), hg, kBlock);
     }
   } else {
-    if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_compact_kernel<ACC>), rt, kBlock);
+    if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_compact_kernel<ACC>), rt, kSpTileBlock);
   }
   const uint64_t scan_groups = (a.tiles + kScanChunk - 1) / kScanChunk;
   if (e == hipSuccess)
