@@ -2,9 +2,15 @@
 // write, 16-byte lanes, XCD-contiguous tiles, buffer descriptors and the
 // same cache hints as the library's kernels.  These bound what a
 // reduce-scatter (mostly reads) and an all-reduce (as many writes as reads)
-// can reach.  Two more patterns bound the sparsified all-reduce: reading two
+// can reach, and reading 8 buffers into a sum written to a ninth is the
+// reduce-scatter's own pattern at W = 8 without the ring order.  Two more
+// patterns bound the sparsified all-reduce: reading two
 // buffers and writing the second in place (its compaction and gather), and
-// writing each tile to 8 buffers (its combine).  Prints one JSON line.
+// writing each tile to 8 buffers (its combine).  Every pattern runs with
+// 256, 512 and 1024 lanes of one vector each and with 256 lanes of four;
+// the best is the ceiling.  Prints one JSON line: per pattern the best rate
+// and the configuration that reached it, and the rate with 256 lanes of one
+// vector.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -23,26 +29,28 @@
 
 namespace {
 
-constexpr int kBlock = 256;
-constexpr int kUnits = 4;                        // dwordx4 per lane per tile
-constexpr unsigned kTileBytes = kBlock * kUnits * 16;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ unsigned xcd_tile(unsigned b, unsigned n) { return (b % 8) * (n / 8) + b / 8; }
+template <unsigned BYTES>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, kTileBytes, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, BYTES, 0x00020000);
 }
 
 // MODE 0: read only; 1: copy; 2: write only; 3: dst += src (two reads, one
 // write in place); 4: write each tile to 8 buffers (dst cut in 8, the grid
-// covering one eighth).  The grid is a multiple of 8.
-template <int MODE, int LOAD_AUX, int STORE_AUX>
-__global__ __launch_bounds__(kBlock) void stream_kernel(const char* src, char* dst, float* sink) {
+// covering one eighth); 5: the sum of a tile of 8 buffers (src cut in 8, the
+// grid covering one eighth) written to dst.  B lanes of U vectors per tile;
+// the grid is a multiple of 8.
+template <int MODE, int LOAD_AUX, int STORE_AUX, int B, int U>
+__global__ __launch_bounds__(B) void stream_kernel(const char* src, char* dst, float* sink) {
+  constexpr int kUnits = U, kBlock = B;
+  constexpr unsigned kTileBytes = B * U * 16;
   const size_t off = size_t(xcd_tile(blockIdx.x, gridDim.x)) * kTileBytes;
   const unsigned voff = threadIdx.x * 16u;
   u32x4 v[kUnits];
   if (MODE == 0 || MODE == 1 || MODE == 3) {
-    const __amdgpu_buffer_rsrc_t r = rsrc(src + off);
+    const __amdgpu_buffer_rsrc_t r = rsrc<kTileBytes>(src + off);
 #pragma unroll
     for (int u = 0; u < kUnits; ++u) v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, voff, u * kBlock * 16, LOAD_AUX);
   } else {
@@ -50,15 +58,35 @@ __global__ __launch_bounds__(kBlock) void stream_kernel(const char* src, char* d
     for (int u = 0; u < kUnits; ++u) v[u] = u32x4{threadIdx.x, 1u, 2u, 3u};
   }
   if (MODE == 3) {
-    const __amdgpu_buffer_rsrc_t r = rsrc(dst + off);
+    const __amdgpu_buffer_rsrc_t r = rsrc<kTileBytes>(dst + off);
 #pragma unroll
     for (int u = 0; u < kUnits; ++u) v[u] += __builtin_amdgcn_raw_buffer_load_b128(r, voff, u * kBlock * 16, LOAD_AUX);
+  }
+  if (MODE == 5) {
+    const size_t part = size_t(gridDim.x) * kTileBytes;
+    u32x4 w[8][kUnits];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const __amdgpu_buffer_rsrc_t r = rsrc<kTileBytes>(src + b * part + off);
+#pragma unroll
+      for (int u = 0; u < kUnits; ++u) w[b][u] = __builtin_amdgcn_raw_buffer_load_b128(r, voff, u * kBlock * 16, LOAD_AUX);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+      v[u] = w[0][u];
+#pragma unroll
+      for (int b = 1; b < 8; ++b) v[u] += w[b][u];
+    }
+    const __amdgpu_buffer_rsrc_t d = rsrc<kTileBytes>(dst + off);
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], d, voff, u * kBlock * 16, STORE_AUX);
+    return;
   }
   if (MODE == 4) {
     const size_t part = size_t(gridDim.x) * kTileBytes;
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const __amdgpu_buffer_rsrc_t w = rsrc(dst + b * part + off);
+      const __amdgpu_buffer_rsrc_t w = rsrc<kTileBytes>(dst + b * part + off);
 #pragma unroll
       for (int u = 0; u < kUnits; ++u)
         __builtin_amdgcn_raw_buffer_store_b128(v[u], w, voff, u * kBlock * 16, STORE_AUX);
@@ -71,7 +99,7 @@ __global__ __launch_bounds__(kBlock) void stream_kernel(const char* src, char* d
     for (int u = 0; u < kUnits; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     if (acc == 0x9e3779b9u) sink[blockIdx.x] = float(acc);  // keeps the loads (sink has one slot per tile)
   } else {
-    const __amdgpu_buffer_rsrc_t w = rsrc(dst + off);
+    const __amdgpu_buffer_rsrc_t w = rsrc<kTileBytes>(dst + off);
 #pragma unroll
     for (int u = 0; u < kUnits; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], w, voff, u * kBlock * 16, STORE_AUX);
   }
@@ -110,45 +138,79 @@ float median_ms(F launch) {
   return t[t.size() / 2];
 }
 
+struct Best {
+  double gbs = 0, first = 0;
+  const char* cfg = "";
+};
+
+// Rate of one pattern in each lane configuration; the best and the first
+// (256 lanes of one vector).
+template <int MODE, int LA, int SA>
+Best measure(const char* src, char* dst, float* sink, size_t bytes, double moved) {
+  Best best;
+  auto one = [&](auto kernel, unsigned tile_bytes, unsigned block, const char* cfg) {
+    const unsigned tiles = unsigned(bytes / tile_bytes) / (MODE >= 4 ? 8 : 1);  // a multiple of 8
+    const float ms = median_ms([&] { hipLaunchKernelGGL(kernel, dim3(tiles), dim3(block), 0, 0, src, dst, sink); });
+    CHECK(hipGetLastError());
+    const double g = moved / (ms * 1e-3) / 1e9;
+    if (best.first == 0) best.first = g;
+    if (g > best.gbs) {
+      best.gbs = g;
+      best.cfg = cfg;
+    }
+  };
+  one(stream_kernel<MODE, LA, SA, 256, 1>, 256 * 16, 256, "256x1");
+  one(stream_kernel<MODE, LA, SA, 512, 1>, 512 * 16, 512, "512x1");
+  one(stream_kernel<MODE, LA, SA, 1024, 1>, 1024 * 16, 1024, "1024x1");
+  one(stream_kernel<MODE, LA, SA, 256, 4>, 256 * 64, 256, "256x4");
+  return best;
+}
+
 }  // namespace
 
 int main() {
-  const size_t bytes = size_t(2) << 30;           // 2 GiB per buffer
-  const unsigned tiles = unsigned(bytes / kTileBytes);  // 131072, a multiple of 8
+  const size_t bytes = size_t(2) << 30;  // 2 GiB per buffer
   char *src, *dst;
   float* sink;
   CHECK(hipMalloc(&src, bytes));
   CHECK(hipMalloc(&dst, bytes));
-  CHECK(hipMalloc(&sink, tiles * sizeof(float)));
-  const dim3 grid(tiles), block(kBlock);
-  auto gbs = [&](double moved, float ms) { return moved / (ms * 1e-3) / 1e9; };
+  CHECK(hipMalloc(&sink, bytes / (256 * 16) * sizeof(float)));  // one slot per tile of the smallest tiles
   // The same read on a zeroed buffer, for comparison only.
   CHECK(hipMemset(src, 0, bytes));
   CHECK(hipDeviceSynchronize());
-  const float r_nt_zero = median_ms([&] { hipLaunchKernelGGL((stream_kernel<0, 2, 0>), grid, block, 0, 0, src, dst, sink); });
+  const Best r_nt_zero = measure<0, 2, 0>(src, dst, sink, bytes, double(bytes));
   hipLaunchKernelGGL(fill_kernel, dim3(4096), dim3(256), 0, 0, reinterpret_cast<unsigned*>(src), bytes / 4);
   CHECK(hipGetLastError());
   CHECK(hipDeviceSynchronize());
-  const float r_plain = median_ms([&] { hipLaunchKernelGGL((stream_kernel<0, 0, 0>), grid, block, 0, 0, src, dst, sink); });
-  const float r_nt = median_ms([&] { hipLaunchKernelGGL((stream_kernel<0, 2, 0>), grid, block, 0, 0, src, dst, sink); });
-  const float c_plain = median_ms([&] { hipLaunchKernelGGL((stream_kernel<1, 0, 0>), grid, block, 0, 0, src, dst, sink); });
-  const float c_nt = median_ms([&] { hipLaunchKernelGGL((stream_kernel<1, 2, 2>), grid, block, 0, 0, src, dst, sink); });
-  const float w_plain = median_ms([&] { hipLaunchKernelGGL((stream_kernel<2, 0, 0>), grid, block, 0, 0, src, dst, sink); });
-  const float w_nt = median_ms([&] { hipLaunchKernelGGL((stream_kernel<2, 0, 2>), grid, block, 0, 0, src, dst, sink); });
+  const Best r_plain = measure<0, 0, 0>(src, dst, sink, bytes, double(bytes));
+  const Best r_nt = measure<0, 2, 0>(src, dst, sink, bytes, double(bytes));
+  const Best c_plain = measure<1, 0, 0>(src, dst, sink, bytes, 2.0 * bytes);
+  const Best c_nt = measure<1, 2, 2>(src, dst, sink, bytes, 2.0 * bytes);
+  const Best w_plain = measure<2, 0, 0>(src, dst, sink, bytes, double(bytes));
+  const Best w_nt = measure<2, 0, 2>(src, dst, sink, bytes, double(bytes));
   // dst += src needs dst to hold data too
   CHECK(hipMemcpy(dst, src, bytes, hipMemcpyDeviceToDevice));
-  const float rw_nt = median_ms([&] { hipLaunchKernelGGL((stream_kernel<3, 2, 2>), grid, block, 0, 0, src, dst, sink); });
-  const dim3 grid8(tiles / 8);  // a multiple of 8: each workgroup writes its tile to all 8 parts
-  const float w8_plain = median_ms([&] { hipLaunchKernelGGL((stream_kernel<4, 0, 0>), grid8, block, 0, 0, src, dst, sink); });
-  const float w8_nt = median_ms([&] { hipLaunchKernelGGL((stream_kernel<4, 0, 2>), grid8, block, 0, 0, src, dst, sink); });
-  CHECK(hipGetLastError());
-  printf("{\"ceilings\": \"HBM streaming, 2 GiB buffers\", \"unit\": \"GB/s\", "
-         "\"read\": %.1f, \"read_nt\": %.1f, \"copy\": %.1f, \"copy_nt\": %.1f, "
-         "\"write\": %.1f, \"write_nt\": %.1f, \"read2_write1_in_place_nt\": %.1f, "
-         "\"write_8_buffers\": %.1f, \"write_8_buffers_nt\": %.1f, \"read_nt_zeroed_buffer\": %.1f}\n",
-         gbs(bytes, r_plain), gbs(bytes, r_nt), gbs(2.0 * bytes, c_plain), gbs(2.0 * bytes, c_nt),
-         gbs(bytes, w_plain), gbs(bytes, w_nt), gbs(3.0 * bytes, rw_nt), gbs(bytes, w8_plain), gbs(bytes, w8_nt),
-         gbs(bytes, r_nt_zero));
+  const Best rw_nt = measure<3, 2, 2>(src, dst, sink, bytes, 3.0 * bytes);
+  const Best w8_plain = measure<4, 0, 0>(src, dst, sink, bytes, double(bytes));
+  const Best w8_nt = measure<4, 0, 2>(src, dst, sink, bytes, double(bytes));
+  const Best r8w1 = measure<5, 2, 16>(src, dst, sink, bytes, bytes + bytes / 8.0);
+  printf("{\"ceilings\": \"HBM streaming, 2 GiB buffers; per pattern the best of 256x1, 512x1, 1024x1 and "
+         "256x4 (lanes x 16-byte vectors per lane) and the rate at 256x1\", \"unit\": \"GB/s\"");
+  auto put = [](const char* name, const Best& b) {
+    printf(", \"%s\": {\"best\": %.1f, \"at\": \"%s\", \"256x1\": %.1f}", name, b.gbs, b.cfg, b.first);
+  };
+  put("read", r_plain);
+  put("read_nt", r_nt);
+  put("copy", c_plain);
+  put("copy_nt", c_nt);
+  put("write", w_plain);
+  put("write_nt", w_nt);
+  put("read2_write1_in_place_nt", rw_nt);
+  put("write_8_buffers", w8_plain);
+  put("write_8_buffers_nt", w8_nt);
+  put("read_8_sum_write_1", r8w1);
+  put("read_nt_zeroed_buffer", r_nt_zero);
+  printf("}\n");
   CHECK(hipFree(src));
   CHECK(hipFree(dst));
   CHECK(hipFree(sink));
