@@ -2,8 +2,9 @@
 // write, 16-byte lanes, XCD-contiguous tiles, buffer descriptors and the
 // same cache hints as the library's kernels.  These bound what a
 // reduce-scatter (mostly reads) and an all-reduce (as many writes as reads)
-// can reach, and reading 8 buffers into a sum written to a ninth is the
-// reduce-scatter's own pattern at W = 8 without the ring order.  Two more
+// can reach; reading 8 buffers into a sum written to a ninth, or to all 8
+// (in place), are the reduce-scatter's and the all-reduce's own patterns at
+// W = 8 without the ring order.  Two more
 // patterns bound the sparsified all-reduce: reading two
 // buffers and writing the second in place (its compaction and gather), and
 // writing each tile to 8 buffers (its combine).  Every pattern runs with
@@ -40,8 +41,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p) {
 // MODE 0: read only; 1: copy; 2: write only; 3: dst += src (two reads, one
 // write in place); 4: write each tile to 8 buffers (dst cut in 8, the grid
 // covering one eighth); 5: the sum of a tile of 8 buffers (src cut in 8, the
-// grid covering one eighth) written to dst.  B lanes of U vectors per tile;
-// the grid is a multiple of 8.
+// grid covering one eighth) written to dst; 6: the same sum written back to
+// all 8 (in place).  B lanes of U vectors per tile; the grid is a multiple
+// of 8.
 template <int MODE, int LOAD_AUX, int STORE_AUX, int B, int U>
 __global__ __launch_bounds__(B) void stream_kernel(const char* src, char* dst, float* sink) {
   constexpr int kUnits = U, kBlock = B;
@@ -62,7 +64,7 @@ __global__ __launch_bounds__(B) void stream_kernel(const char* src, char* dst, f
 #pragma unroll
     for (int u = 0; u < kUnits; ++u) v[u] += __builtin_amdgcn_raw_buffer_load_b128(r, voff, u * kBlock * 16, LOAD_AUX);
   }
-  if (MODE == 5) {
+  if (MODE == 5 || MODE == 6) {
     const size_t part = size_t(gridDim.x) * kTileBytes;
     u32x4 w[8][kUnits];
 #pragma unroll
@@ -77,9 +79,18 @@ __global__ __launch_bounds__(B) void stream_kernel(const char* src, char* dst, f
 #pragma unroll
       for (int b = 1; b < 8; ++b) v[u] += w[b][u];
     }
-    const __amdgpu_buffer_rsrc_t d = rsrc<kTileBytes>(dst + off);
+    if (MODE == 5) {
+      const __amdgpu_buffer_rsrc_t d = rsrc<kTileBytes>(dst + off);
 #pragma unroll
-    for (int u = 0; u < kUnits; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], d, voff, u * kBlock * 16, STORE_AUX);
+      for (int u = 0; u < kUnits; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], d, voff, u * kBlock * 16, STORE_AUX);
+    } else {
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const __amdgpu_buffer_rsrc_t d = rsrc<kTileBytes>(const_cast<char*>(src) + b * part + off);
+#pragma unroll
+        for (int u = 0; u < kUnits; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], d, voff, u * kBlock * 16, STORE_AUX);
+      }
+    }
     return;
   }
   if (MODE == 4) {
@@ -194,6 +205,7 @@ int main() {
   const Best w8_plain = measure<4, 0, 0>(src, dst, sink, bytes, double(bytes));
   const Best w8_nt = measure<4, 0, 2>(src, dst, sink, bytes, double(bytes));
   const Best r8w1 = measure<5, 2, 16>(src, dst, sink, bytes, bytes + bytes / 8.0);
+  const Best r8w8 = measure<6, 2, 2>(src, dst, sink, bytes, 2.0 * bytes);  // last: it rewrites src
   printf("{\"ceilings\": \"HBM streaming, 2 GiB buffers; per pattern the best of 256x1, 512x1, 1024x1 and "
          "256x4 (lanes x 16-byte vectors per lane) and the rate at 256x1\", \"unit\": \"GB/s\"");
   auto put = [](const char* name, const Best& b) {
@@ -209,6 +221,7 @@ int main() {
   put("write_8_buffers", w8_plain);
   put("write_8_buffers_nt", w8_nt);
   put("read_8_sum_write_1", r8w1);
+  put("read_8_sum_write_8_in_place", r8w8);
   put("read_nt_zeroed_buffer", r_nt_zero);
   printf("}\n");
   CHECK(hipFree(src));
