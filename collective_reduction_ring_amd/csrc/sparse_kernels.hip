@@ -57,6 +57,7 @@ constexpr uint32_t kSpWalkGroups = 2048;          // workgroups of the tile-walk
 constexpr uint32_t kSampleMax = 65536;            // top-K: keys sampled per rank for the gather bound
 constexpr int kSampleBlock = 1024;                // lanes of the sampling workgroup
 constexpr uint32_t kScanChunk = 4 * kSpScanBlock;  // tiles per workgroup of the offset scan
+constexpr uint32_t kCombBlock = 256;               // lanes of the combine (see the kernel)
 static_assert(kSpLaneElems * kSpTileBlock == kSpTile, "a tile is one element group per lane");
 static_assert(kSampleMax % (16 * kSampleBlock) == 0, "whole sample batches");
 
@@ -728,15 +729,15 @@ __global__ __launch_bounds__(kSpScanBlock) void sp_scan_kernel(const SparseArgs 
 // barrier per rank keeps the adds in rank order; entries of one rank have
 // distinct indices.  Every rank's counts are read at once, and the next
 // rank's first entries are loaded while this rank's are placed.  256 lanes,
-// 4 vectors each: a tile holds few entries per rank, and 1024 lanes with one
-// vector each spent the time in their per-rank scans and barriers (threshold
-// combine 434 -> 662 us).
+// 4 vectors each: a tile holds few entries per rank, and more lanes spend the
+// time in their per-rank scans and barriers (threshold combine 434 -> 481 us
+// with 512 lanes, 662 us with 1024).
 template <int MODE, bool ACC>
-__global__ __launch_bounds__(kBlock) void sp_combine_kernel(const SparseArgs a) {
-  constexpr uint32_t kVecs = kSpTile / 4 / kBlock;  // 16-byte vectors per lane of the output tile
+__global__ __launch_bounds__(kCombBlock) void sp_combine_kernel(const SparseArgs a) {
+  constexpr uint32_t kVecs = kSpTile / 4 / kCombBlock;  // 16-byte vectors per lane of the output tile
   __shared__ float4 acc4[kSpTile / 4];
   __shared__ uint32_t meta[RSX_MAX_RANKS][5];  // entries, message offset, cut, ties to take, guess
-  __shared__ uint32_t scratch[kBlock / 64];
+  __shared__ uint32_t scratch[kCombBlock / 64];
   float* acc = reinterpret_cast<float*>(acc4);
   const uint32_t t = xcd_tile(blockIdx.x, gridDim.x);
   if (t >= a.tiles) return;
@@ -745,7 +746,7 @@ __global__ __launch_bounds__(kBlock) void sp_combine_kernel(const SparseArgs a) 
   const uint32_t world = a.world;
   const uint32_t tid = threadIdx.x;
 #pragma unroll
-  for (uint32_t u = 0; u < kVecs; ++u) acc4[u * kBlock + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (uint32_t u = 0; u < kVecs; ++u) acc4[u * kCombBlock + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
   if (tid < world) {
     const uint32_t i = tid * (a.tiles + 1) + t;
     meta[tid][0] = min(a.tile_slot[i], n);
@@ -786,8 +787,8 @@ __global__ __launch_bounds__(kBlock) void sp_combine_kernel(const SparseArgs a) 
     uint32_t* mi = a.msg_idx[r];
     float* mv = a.msg_val[r];
     uint32_t run = 0;  // packed counts of the chunks before this one
-    for (uint32_t c0 = 0; c0 < c; c0 += kBlock) {
-      if (c0 != 0) fetch(r, c0, local, v);  // a slot with more than kBlock entries
+    for (uint32_t c0 = 0; c0 < c; c0 += kCombBlock) {
+      if (c0 != 0) fetch(r, c0, local, v);  // a slot with more than kCombBlock entries
       uint32_t f = 0;
       if (c0 + tid < c) {
         if constexpr (MODE == RSX_SPARSE_TOPK)
@@ -796,7 +797,7 @@ __global__ __launch_bounds__(kBlock) void sp_combine_kernel(const SparseArgs a) 
           f = 1u;
       }
       uint32_t tot;
-      const uint32_t p = block_excl<kBlock / 64>(f, scratch, tot) + run;
+      const uint32_t p = block_excl<kCombBlock / 64>(f, scratch, tot) + run;
       run += tot;
       const uint32_t sure_before = p & 0xFFFFu, ties_before = p >> 16;
       const bool sent = (f & 1u) || ((f >> 16) && ties_before < ties);
@@ -820,13 +821,13 @@ __global__ __launch_bounds__(kBlock) void sp_combine_kernel(const SparseArgs a) 
   uint4 q[kVecs];
 #pragma unroll
   for (uint32_t u = 0; u < kVecs; ++u) {
-    const float4 v = acc4[u * kBlock + tid];
+    const float4 v = acc4[u * kCombBlock + tid];
     q[u] = make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w));
   }
   for (uint32_t r = 0; r < world; ++r) {
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.out[r] + base, n * 4);
 #pragma unroll
-    for (uint32_t u = 0; u < kVecs; ++u) store_b128<kStoreStream>(rd, tid * 16, u * kBlock * 16, q[u]);
+    for (uint32_t u = 0; u < kVecs; ++u) store_b128<kStoreStream>(rd, tid * 16, u * kCombBlock * 16, q[u]);
   }
 }
 
@@ -874,7 +875,8 @@ hipError_t launch_mode(SparseArgs a, hipStream_t s) {
   const uint64_t scan_groups = (a.tiles + kScanChunk - 1) / kScanChunk;
   if (e == hipSuccess)
     e = go(reinterpret_cast<const void*>(&sp_scan_kernel<MODE>), a.world * scan_groups, kSpScanBlock);
-  if (e == hipSuccess) e = go(reinterpret_cast<const void*>(&sp_combine_kernel<MODE, ACC>), xcd_grid(a.tiles), kBlock);
+  if (e == hipSuccess)
+    e = go(reinterpret_cast<const void*>(&sp_combine_kernel<MODE, ACC>), xcd_grid(a.tiles), kCombBlock);
   return e;
 }
 
