@@ -796,8 +796,13 @@ __global__ __launch_bounds__(kCombBlock) void sp_combine_kernel(const SparseArgs
         else
           f = 1u;
       }
-      uint32_t tot;
-      const uint32_t p = block_excl<kCombBlock / 64>(f, scratch, tot) + run;
+      uint32_t p, tot;
+      if constexpr (MODE == RSX_SPARSE_TOPK) {
+        p = block_excl<kCombBlock / 64>(f, scratch, tot) + run;
+      } else {  // every slot entry is sent: its place is its index
+        p = run + tid;
+        tot = min(c - c0, kCombBlock);
+      }
       run += tot;
       const uint32_t sure_before = p & 0xFFFFu, ties_before = p >> 16;
       const bool sent = (f & 1u) || ((f >> 16) && ties_before < ties);
