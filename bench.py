@@ -398,7 +398,8 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
         gen.manual_seed(11)
         ins_all = torch.randn(world * top, device="cuda:0", generator=gen) * 1e-3
         outs_all = torch.empty(world * top, device="cuda:0")
-        res = {"workload": "reduce-scatter and ring all-reduce sum fp32, W=8, per-rank size sweep; "
+        res = {"workload": "reduce-scatter and ring all-reduce sum fp32 (and an in-place avg all-reduce), W=8, "
+                           "per-rank size sweep; "
                            "below 64 MiB graph-timed device time (50 calls per graph), above HIP events per call"}
         kib = 4
         while kib * 1024 <= 2 ** 30:
@@ -409,9 +410,12 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
             ar_out = [outs_all[r * n:(r + 1) * n] for r in range(world)]
             rs = rsx.ReduceScatter(ins, rs_out, "sum")
             ar = rsx.AllReduce(ins, ar_out, "sum", "ring")
+            # in place (8 buffers instead of 16); avg keeps repeated calls' values bounded
+            ar_in = rsx.AllReduce(ins, None, "avg", "ring")
             row = {}
             for what, fn, nbytes in (("reduce_scatter", rs, world * n * 4 + world * seg * 4),
-                                     ("all_reduce", ar, 2 * world * n * 4)):
+                                     ("all_reduce", ar, 2 * world * n * 4),
+                                     ("all_reduce_in_place_avg", ar_in, 2 * world * n * 4)):
                 if kib * 1024 < 64 * 2 ** 20:
                     us = graph_us_per_call(fn, 50, 20, torch)
                 else:
