@@ -219,7 +219,8 @@ size_t rsx_sparse_workspace_size(int nranks, size_t count, rsx_sparse_mode_t mod
  * For each rank r, with g = grads[r] + accums[r] (one fp32 add; g = grads[r]
  * when accums is NULL):
  *   RSX_SPARSE_THRESHOLD: entry i is sent when |g[i]| >= threshold and
- *     g[i] != 0;
+ *     g[i] != 0 (any threshold: a NaN threshold sends nothing, one <= 0
+ *     every nonzero entry);
  *   RSX_SPARSE_TOPK: the k largest g[i] are sent (a NaN ranks below every
  *     number, -0 equals +0, equal values are taken by increasing index);
  *   with accums: accums[r][i] = g[i] - (0 + g[i]) where sent, g[i] - 0 where

@@ -34,6 +34,24 @@ def test_threshold_hand_case():
     assert idx.tolist() == [2]
 
 
+def test_threshold_nan_and_negative():
+    # the comparison |g| >= threshold decides: a NaN threshold sends nothing, a
+    # negative one keeps everything but a NaN entry (|NaN| >= t is false) and
+    # sends what is nonzero
+    g = np.array([1.0, -2.0, 0.0, -0.0, np.nan, np.inf], f32)
+    acc = np.zeros(6, f32)
+    idx, val, res = oracle.sparsify_threshold(g, acc, float("nan"))
+    assert idx.tolist() == [] and val.tolist() == []
+    bits = res.view(np.uint32).tolist()
+    assert bits[:4] == [0x3F800000, 0xC0000000, 0, 0] and np.isnan(res[4]) and res[5] == np.inf
+    idx, val, res = oracle.sparsify_threshold(g, acc, -1.0)
+    assert idx.tolist() == [0, 1, 5] and val.tolist() == [1.0, -2.0, np.inf]
+    # sent entries leave x - x: 0 for finite, NaN for inf; the kept -0 leaves
+    # (-0 + 0) - (-0 + 0) = +0; the NaN entry stays
+    assert res[:4].view(np.uint32).tolist() == [0, 0, 0, 0]
+    assert np.isnan(res[4]) and np.isnan(res[5])
+
+
 def test_threshold_error_feedback_two_steps():
     # step 1: 1.0 is sent, 0.25 is kept back; step 2: 0.25 + 0.375 = 0.625 >= 0.5 is sent
     acc = np.zeros(2, f32)

@@ -111,7 +111,7 @@ def test_ties_at_the_cut_and_specials(mode):
         grads[r][pos] = special[rng.integers(0, len(special), 300)]
         accs[r][pos[:40]] = -0.0
     if mode == "threshold":
-        for thr in (1.0, 0.0, 2.0 ** -149, np.inf):
+        for thr in (1.0, 0.0, 2.0 ** -149, np.inf, -1.0, np.nan):  # NaN sends nothing; <= 0 every nonzero
             check(grads, accs, mode, threshold=thr, what=f"ties thr={thr}")
     else:
         for k in (1, 7, 1000, 4096, n // 2, n - 1):
