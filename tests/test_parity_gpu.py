@@ -92,6 +92,44 @@ def test_all_reduce(w, op, dtype, algo):
         assert_parity(got[r], want[r], dtype, f"rank {r}")
 
 
+def _with_ieee_specials(xs, dtype, seed):
+    """Normal data with IEEE specials planted: +-inf, NaN, +-0, the smallest
+    subnormal and values near the top of the range (sums and products then
+    overflow, tiny products underflow)."""
+    ft = np.float32 if dtype == "f32" else np.float64
+    fi = np.finfo(ft)
+    specials = np.array([np.inf, -np.inf, np.nan, 0.0, -0.0, fi.smallest_subnormal, -fi.smallest_subnormal,
+                         fi.max / 2, -fi.max / 2, fi.tiny, 1e-30 if dtype == "f32" else 1e-300], ft)
+    rng = np.random.default_rng(seed)
+    out = []
+    for x in xs:
+        x = x.astype(ft).copy()
+        pos = rng.choice(len(x), len(x) // 8, replace=False)
+        x[pos] = specials[rng.integers(0, len(specials), len(pos))]
+        out.append(x)
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("op", ["sum", "prod", "avg"])
+@pytest.mark.parametrize("w", [2, 3, 8])
+def test_ieee_specials_rs_and_ar(w, op, dtype):
+    # inf - inf and 0 * inf give NaN, overflow gives inf, subnormals are kept
+    # (no flush to zero), -0 + -0 stays -0: bit for bit against the oracle
+    te = tile_elems(w, dtype)
+    recvcount = te + 7
+    xs = _with_ieee_specials(inputs(4, w, w * recvcount, dtype), dtype, (40, w))
+    say(f"ieee specials rs/ar w={w} op={op} dtype={dtype}")
+    got = run_rs(xs, dtype, op, recvcount)
+    want = oracle.reduce_scatter(xs, op, dtype)
+    for k in range(w):
+        assert_parity(got[k], want[k], dtype, f"rs block {k}")
+    got = run_ar(xs, dtype, op, "ring")
+    want = oracle.all_reduce(xs, op, dtype)
+    for r in range(w):
+        assert_parity(got[r], want[r], dtype, f"ar rank {r}")
+
+
 @pytest.mark.parametrize("count", [1, 2, 3, 7, 8, 9, 15, 16, 17, 31, 33, 100, 1023])
 @pytest.mark.parametrize("w", [2, 4, 16])
 def test_all_reduce_small_and_ragged(w, count):
