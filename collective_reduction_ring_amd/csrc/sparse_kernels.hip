@@ -515,9 +515,17 @@ __device__ __forceinline__ void walk_slots(const SparseArgs& a, uint32_t r, uint
         if (i + k >= nt) break;
         const uint32_t t = tb + (i + k) * kWaves;
         fn(t, v[k], lane < c[k], c[k] <= 64);
-        for (uint32_t e0 = 64; e0 < c[k]; e0 += 64) {  // a tile with more than 64 entries
-          const uint32_t e = e0 + lane;
-          fn(t, e < c[k] ? slots[static_cast<uint64_t>(t) * kSpTile + e] : 0.0f, e < c[k], e0 + 64 >= c[k]);
+        // a tile with more than 64 entries: 4 chunks of 64 loaded at a time
+        for (uint32_t e0 = 64; e0 < c[k]; e0 += 4 * 64) {
+          float w4[4];
+#pragma unroll
+          for (uint32_t q = 0; q < 4; ++q) {
+            const uint32_t e = e0 + q * 64 + lane;
+            w4[q] = e < c[k] ? slots[static_cast<uint64_t>(t) * kSpTile + e] : 0.0f;
+          }
+#pragma unroll
+          for (uint32_t q = 0; q < 4; ++q)
+            if (e0 + q * 64 < c[k]) fn(t, w4[q], e0 + q * 64 + lane < c[k], e0 + (q + 1) * 64 >= c[k]);
         }
       }
     }
