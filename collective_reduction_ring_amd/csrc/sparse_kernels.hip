@@ -796,7 +796,11 @@ __global__ __launch_bounds__(kCombBlock) void sp_combine_kernel(const SparseArgs
     float* mv = a.msg_val[r];
     uint32_t run = 0;  // packed counts of the chunks before this one
     for (uint32_t c0 = 0; c0 < c; c0 += kCombBlock) {
-      if (c0 != 0) fetch(r, c0, local, v);  // a slot with more than kCombBlock entries
+      // a slot with more than kCombBlock entries: its next chunk loads while
+      // this one is placed
+      uint32_t local_next = 0;
+      float v_next = 0.0f;
+      if (c0 + kCombBlock < c) fetch(r, c0 + kCombBlock, local_next, v_next);
       uint32_t f = 0;
       if (c0 + tid < c) {
         if constexpr (MODE == RSX_SPARSE_TOPK)
@@ -828,6 +832,8 @@ __global__ __launch_bounds__(kCombBlock) void sp_combine_kernel(const SparseArgs
           if (!sent && guessed_sent) a.accum[r][base + local] = v;
         }
       }
+      local = local_next;
+      v = v_next;
     }
     __syncthreads();
   }
