@@ -240,6 +240,40 @@ def test_more_tiles_than_the_bench_shape():
     check(grads, accs, "topk", k=rsx.topk_count(n, 0.001), what="16386 tiles, top-K")
 
 
+@pytest.mark.parametrize("case", range(40))
+def test_random_configurations(case):
+    # Seeded random mixes: rank count, size (some past the sampled 65536
+    # keys), mode, K or threshold, error feedback, a coarse value grid (ties at
+    # the cut) and planted specials.
+    rng = np.random.default_rng((71, case))
+    w = int(rng.choice([1, 2, 3, 5, 8, 16]))
+    n = int(rng.choice([int(rng.integers(1, 3 * 4096)), int(rng.integers(SAMPLE, 2 * SAMPLE + 9000))]))
+    coarse = rng.random() < 0.3
+    grads, accs = [], []
+    for _ in range(w):
+        if coarse:
+            g = (rng.integers(-6, 7, n) * 0.125).astype(f32)
+            a = (rng.integers(-2, 3, n) * 0.0625).astype(f32)
+        else:
+            g = (rng.standard_normal(n) * 1e-3).astype(f32)
+            a = (rng.standard_normal(n) * 1e-3).astype(f32)
+        m = int(rng.integers(0, max(1, n // 50)))
+        if m:
+            pos = rng.choice(n, m, replace=False)
+            g[pos] = np.array([np.nan, np.inf, -np.inf, -0.0, 0.0, 2.0 ** -149], f32)[rng.integers(0, 6, m)]
+        grads.append(g)
+        accs.append(a)
+    feedback = rng.random() < 0.7
+    if rng.random() < 0.5:
+        frac = float(rng.choice([0.0, 0.0005, 0.01, 0.05, 0.3, 0.9, 1.0]))
+        check(grads, accs if feedback else None, "topk", k=rsx.topk_count(n, frac),
+              what=f"random {case} topk w={w} n={n} frac={frac} coarse={coarse}")
+    else:
+        thr = float(rng.choice([1e-3, 2e-3, 0.25, 0.0]))
+        check(grads, accs if feedback else None, "threshold", threshold=thr,
+              what=f"random {case} threshold w={w} n={n} thr={thr} coarse={coarse}")
+
+
 @pytest.mark.parametrize("mode", ["topk", "threshold"])
 def test_graph_capture_replays(mode):
     # The whole sparse call (all its kernels) captured in a HIP graph: every
