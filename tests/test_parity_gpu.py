@@ -21,6 +21,8 @@ DIST = {"f32": "normal", "bf16": "normal_bf16", "i32": "int_full", "f64": "norma
         "f32h": "normal"}
 VL = {"f32": 4, "bf16": 8, "i32": 4, "f64": 2, "f16": 8, "i64": 2, "u64": 2, "i8": 16, "f32h": 4}
 ALL_DTYPES = list(DIST)
+ES = {"f32": 4, "bf16": 2, "i32": 4, "f64": 8, "f16": 2, "i64": 8, "u64": 8, "i8": 1, "f32h": 4}
+RSX_NAIVE_MAX_BYTES = 32768
 
 
 def wire(dtype):
@@ -126,6 +128,34 @@ def test_ieee_specials_rs_and_ar(w, op, dtype):
         assert_parity(got[k], want[k], dtype, f"rs block {k}")
     got = run_ar(xs, dtype, op, "ring")
     want = oracle.all_reduce(xs, op, dtype)
+    for r in range(w):
+        assert_parity(got[r], want[r], dtype, f"ar rank {r}")
+
+
+@pytest.mark.parametrize("case", range(60))
+def test_random_configurations(case):
+    # Seeded random mixes of rank count, size, type, op, algorithm and
+    # in-place form, for both collectives.
+    rng = np.random.default_rng((72, case))
+    w = int(rng.integers(1, 17))
+    dtype = str(rng.choice(ALL_DTYPES))
+    op = str(rng.choice(OPS))
+    recvcount = int(rng.integers(1, 3 * tile_elems(w, dtype) // max(1, w // 4)))
+    xs = inputs(5 + case, w, w * recvcount, dtype)
+    say(f"random {case}: rs w={w} dtype={dtype} op={op} recvcount={recvcount}")
+    got = run_rs(xs, dtype, op, recvcount)
+    want = oracle.reduce_scatter(xs, op, dtype)
+    for k in range(w):
+        assert_parity(got[k], want[k], dtype, f"rs block {k}")
+    count = int(rng.integers(1, 3 * tile_elems(w, dtype)))
+    algo = str(rng.choice(["ring", "naive", "auto"]))
+    in_place = bool(rng.random() < 0.5)
+    xs = inputs(500 + case, w, count, dtype)
+    say(f"random {case}: ar w={w} dtype={dtype} op={op} count={count} algo={algo} in_place={in_place}")
+    got = run_ar(xs, dtype, op, algo, in_place)
+    # auto: naive at or below RSX_NAIVE_MAX_BYTES of elements per rank (rsx.h)
+    naive = algo == "naive" or (algo == "auto" and count * ES[dtype] <= RSX_NAIVE_MAX_BYTES)
+    want = (oracle.naive_all_reduce if naive else oracle.all_reduce)(xs, op, dtype)
     for r in range(w):
         assert_parity(got[r], want[r], dtype, f"ar rank {r}")
 
