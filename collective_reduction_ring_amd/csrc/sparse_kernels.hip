@@ -138,9 +138,9 @@ __device__ __forceinline__ void load_tile(const float* g, const float* acc, uint
   }
 }
 
-// Dense tile stores are non-temporal.  Plain stores win a write-only test
-// (2 GiB over 8 buffers: 387 vs 407 us) but lose in these kernels, which
-// also read (compaction 1134 -> 1216 us, top-K combine 612 -> 791 us).
+// Dense tile stores are non-temporal.  In these kernels, which also read,
+// plain stores lose (compaction 1068 -> 1198 us, and the combine that
+// follows slows too) and sc1 stores lose a little (1068 -> 1084 us).
 __device__ __forceinline__ void store_tile(float* dst, uint64_t base, uint32_t n,
                                            const float (&x)[kSpUnits][4]) {
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(dst + base, n * 4);
