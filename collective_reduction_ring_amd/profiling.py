@@ -9,6 +9,8 @@
   the same counter reads for a plain copy kernel of known size.  The record
   carries a digest of the kernel's sources so that ``bench.py`` reports it
   only while the kernel is unchanged.
+* ``traffic-table``: the same scaled bytes for several kernels of one run, as
+  a markdown table against each kernel's algorithmic bytes.
 
 Usage::
 
@@ -125,6 +127,32 @@ def traffic_record(fetch: str, write: str, cal_fetch: str, cal_write: str, kerne
     }
 
 
+def traffic_table(fetch: str, write: str, cal_fetch: str, cal_write: str, cal_kernel: str,
+                  cal_bytes: int, kernels: list[tuple[str, int]], commands: str) -> str:
+    """Markdown table of HBM bytes per dispatch for (kernel, algorithmic bytes) pairs."""
+    cf = counter_per_dispatch(cal_fetch, "FETCH_SIZE", cal_kernel)
+    cw = counter_per_dispatch(cal_write, "WRITE_SIZE", cal_kernel)
+    if not (cf and cw):
+        raise SystemExit("missing counter rows for the calibration kernel")
+    f_scale = cal_bytes / (statistics.mean(cf) * 1024.0)
+    w_scale = cal_bytes / (statistics.mean(cw) * 1024.0)
+    lines = ["# rocprofv3 HBM traffic per dispatch", "", "Commands:", "", "```", commands, "```", "",
+             f"Scale factors from the calibration kernel `{cal_kernel}` ({cal_bytes} bytes read and written "
+             f"per dispatch): FETCH_SIZE x {f_scale:.5f}, WRITE_SIZE x {w_scale:.5f}.", "",
+             "| kernel | dispatches | fetch bytes | write bytes | traffic | algorithmic | traffic / algorithmic |",
+             "|---|---|---|---|---|---|---|"]
+    for kernel, algo in kernels:
+        f = counter_per_dispatch(fetch, "FETCH_SIZE", kernel)
+        w = counter_per_dispatch(write, "WRITE_SIZE", kernel)
+        if not (f and w):
+            raise SystemExit(f"missing counter rows for {kernel}")
+        fb = statistics.mean(f) * 1024.0 * f_scale
+        wb = statistics.mean(w) * 1024.0 * w_scale
+        lines.append(f"| `{kernel}` | {len(f)} | {fb:,.0f} | {wb:,.0f} | {fb + wb:,.0f} | {algo:,} | "
+                     f"{(fb + wb) / algo:.4f} |")
+    return "\n".join(lines) + "\n"
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -141,8 +169,21 @@ def main() -> None:
         t.add_argument(f"--{name}", required=True)
     t.add_argument("--cal-bytes", type=int, required=True)
     t.add_argument("--algorithmic-bytes", type=int, required=True)
+    tt = sub.add_parser("traffic-table")
+    for name in ("fetch", "write", "cal-fetch", "cal-write", "cal-kernel", "commands", "out"):
+        tt.add_argument(f"--{name}", required=True)
+    tt.add_argument("--cal-bytes", type=int, required=True)
+    tt.add_argument("--kernel", action="append", required=True,
+                    help="NAME=ALGORITHMIC_BYTES (NAME matches a substring of the kernel name); repeatable")
     a = ap.parse_args()
-    if a.cmd == "ktrace":
+    if a.cmd == "traffic-table":
+        pairs = [(k.rsplit("=", 1)[0], int(k.rsplit("=", 1)[1])) for k in a.kernel]
+        text = traffic_table(a.fetch, a.write, a.cal_fetch, a.cal_write, a.cal_kernel, a.cal_bytes,
+                             pairs, a.commands)
+        with open(a.out, "w") as f:
+            f.write(text)
+        print(text)
+    elif a.cmd == "ktrace":
         text = ktrace_summary(a.trace, a.stats, a.kernel, a.skip, a.timed, a.command)
         with open(a.out, "w") as f:
             f.write(text)

@@ -82,3 +82,19 @@ def test_traffic_record_scales_by_the_copy_calibration(tmp_path):
     assert rec["write_bytes_per_launch"] == 256_000
     assert rec["traffic_over_algorithmic"] == 1.0
     assert rec["kernel_source_sha256"] == profiling.kernel_source_digest()
+
+
+def test_traffic_table_scales_each_kernel(tmp_path):
+    def counters(path, name, rows):
+        _write(path, [{"Counter_Name": name, "Kernel_Name": k, "Counter_Value": v} for k, v in rows])
+    counters(tmp_path / "f.csv", "FETCH_SIZE", [("gather<1>", 100.0), ("gather<1>", 300.0), ("combine", 10.0)])
+    counters(tmp_path / "w.csv", "WRITE_SIZE", [("gather<1>", 50.0), ("combine", 40.0)])
+    counters(tmp_path / "cf.csv", "FETCH_SIZE", [("copy", 512.0)])    # scale 2
+    counters(tmp_path / "cw.csv", "WRITE_SIZE", [("copy", 1024.0)])   # scale 1
+    text = profiling.traffic_table(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "cf.csv"),
+                                   str(tmp_path / "cw.csv"), "copy", 1 << 20,
+                                   [("gather", 460_800), ("combine", 61_440)], "cmds")
+    # gather: fetch mean 200 KiB x 2 = 409,600 B, write 51,200 B -> 460,800 = 1.0000
+    assert "| `gather` | 2 | 409,600 | 51,200 | 460,800 | 460,800 | 1.0000 |" in text
+    # combine: 10 KiB x 2 + 40 KiB = 20,480 + 40,960 = 61,440
+    assert "| `combine` | 1 | 20,480 | 40,960 | 61,440 | 61,440 | 1.0000 |" in text
