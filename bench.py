@@ -178,36 +178,28 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
             d.copy_(torch.from_numpy(x.view(np.int16)).view(torch.bfloat16))
         del xs
         _, out = _arena(torch, torch.bfloat16, world, n)
-        plans = []
-        for b0 in range(0, n, bucket):
-            b1 = min(b0 + bucket, n)
-            plans.append(rsx.AllReduce([d[b0:b1] for d in dev], [o[b0:b1] for o in out], "avg", "ring"))
-        step = lambda: [p() for p in plans]  # noqa: E731
+        bounds = [(b0, min(b0 + bucket, n)) for b0 in range(0, n, bucket)]
+
+        def bucketed(algo):
+            plans = [rsx.AllReduce([d[b0:b1] for d in dev], [o[b0:b1] for o in out], "avg", algo)
+                     for b0, b1 in bounds]
+            return lambda: [p() for p in plans]
+        nb = 2 * world * n * 2
+        step = bucketed("ring")
         res = {"workload": "all-reduce avg bf16 (fp32 accumulate), W=8, 134,217,728/rank, "
-                           f"{len(plans)} buckets of <= 25 MiB in sequence on one stream",
-               "ring_one_pass": _stat(time_launches(step, reps // 4 or 1, warm, torch), 2 * world * n * 2)}
-        res["ring_one_pass"]["graph_us_per_step"] = graph_us_per_call(step, 1, 10, torch)
+                           f"{len(bounds)} buckets of <= 25 MiB in sequence on one stream; "
+                           "ring = the library's choice by shape (two passes for these buckets)",
+               "ring": _stat(time_launches(step, reps // 4 or 1, warm, torch), nb)}
+        res["ring"]["graph_us_per_step"] = graph_us_per_call(step, 1, 10, torch)
+        # The two forms of the ring all-reduce, forced; the same bits.
+        res["ring_fused_one_pass"] = _stat(time_launches(bucketed("ring_fused"), reps // 4 or 1, warm, torch), nb)
+        st = _stat(time_launches(bucketed("ring_split"), reps // 4 or 1, warm, torch), nb)
+        # reduce-scatter W*n*2 in, n*2 out; all-gather n*2 in, (W-1)*n*2 out
+        st["actual_bytes"] = nb + n * 2
+        res["ring_split_two_pass"] = st
         # For comparison only: the same bytes as one all-reduce without buckets.
         whole = rsx.AllReduce(dev, out, "avg", "ring")
-        res["unbucketed_one_launch"] = _stat(time_launches(whole, reps // 4 or 1, warm, torch), 2 * world * n * 2)
-        # The same all-reduce composed of a reduce-scatter into a bf16 buffer of
-        # W segments, then an all-gather: more traffic, same bits.
-        _, seg_buf = _arena(torch, torch.bfloat16, world, bucket // world)
-        comp = []
-        for b0 in range(0, n, bucket):
-            b1 = min(b0 + bucket, n)
-            s = (b1 - b0) // world
-            segs = [t[:s] for t in seg_buf]
-            comp.append((rsx.ReduceScatter([d[b0:b1] for d in dev], segs, "avg"),
-                         segs, [o[b0:b1] for o in out]))
-
-        def step2():
-            for rs, segs, outs in comp:
-                rs()
-                rsx.all_gather(segs, outs)
-        st = _stat(time_launches(step2, reps // 4 or 1, warm, torch), 2 * world * n * 2)
-        st["actual_bytes"] = 2 * world * n * 2 + 2 * world * (n // world) * 2
-        res["rs_then_ag"] = st
+        res["unbucketed_one_call"] = _stat(time_launches(whole, reps // 4 or 1, warm, torch), nb)
         return res
     if name == "int32_w16":
         w = wl.WORKLOADS[4]
@@ -226,6 +218,8 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
                                                 world * n * 4 + world * seg * 4)
             res[f"all_reduce_{op}"] = _stat(time_launches(rsx.AllReduce(dev, ar, op, "ring"), reps, warm, torch),
                                             2 * world * n * 4)
+        res["all_reduce_sum_one_pass"] = _stat(time_launches(rsx.AllReduce(dev, ar, "sum", "ring_fused"), reps,
+                                                             warm, torch), 2 * world * n * 4)
         return res
     if name == "fused":
         world = 4
@@ -398,8 +392,8 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
         gen.manual_seed(11)
         ins_all = torch.randn(world * top, device="cuda:0", generator=gen) * 1e-3
         outs_all = torch.empty(world * top, device="cuda:0")
-        res = {"workload": "reduce-scatter and ring all-reduce sum fp32 (and an in-place avg all-reduce), W=8, "
-                           "per-rank size sweep; "
+        res = {"workload": "reduce-scatter and ring all-reduce sum fp32 (the library's choice of form, and "
+                           "one pass forced; and an in-place avg all-reduce), W=8, per-rank size sweep; "
                            "below 64 MiB graph-timed device time (50 calls per graph), above HIP events per call"}
         kib = 4
         while kib * 1024 <= 2 ** 30:
@@ -412,9 +406,12 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
             ar = rsx.AllReduce(ins, ar_out, "sum", "ring")
             # in place (8 buffers instead of 16); avg keeps repeated calls' values bounded
             ar_in = rsx.AllReduce(ins, None, "avg", "ring")
+            # the one-pass form forced, for comparison where "ring" takes two passes
+            ar_one = rsx.AllReduce(ins, ar_out, "sum", "ring_fused")
             row = {}
             for what, fn, nbytes in (("reduce_scatter", rs, world * n * 4 + world * seg * 4),
                                      ("all_reduce", ar, 2 * world * n * 4),
+                                     ("all_reduce_one_pass", ar_one, 2 * world * n * 4),
                                      ("all_reduce_in_place_avg", ar_in, 2 * world * n * 4)):
                 if kib * 1024 < 64 * 2 ** 20:
                     us = graph_us_per_call(fn, 50, 20, torch)

@@ -17,10 +17,13 @@ RSX_FLOAT32, RSX_BFLOAT16, RSX_INT32 = 0, 1, 2
 RSX_FLOAT64, RSX_FLOAT16, RSX_INT64, RSX_UINT64, RSX_INT8 = 3, 4, 5, 6, 7
 RSX_FLOAT32_HALF_WIRE = 8
 RSX_SUM, RSX_MAX, RSX_MIN, RSX_AVG, RSX_PROD = 0, 1, 2, 3, 4
-RSX_ALGO_RING, RSX_ALGO_NAIVE, RSX_ALGO_AUTO = 0, 1, 2
+RSX_ALGO_RING, RSX_ALGO_NAIVE, RSX_ALGO_AUTO, RSX_ALGO_RING_FUSED, RSX_ALGO_RING_SPLIT = 0, 1, 2, 3, 4
 RSX_SPARSE_THRESHOLD, RSX_SPARSE_TOPK = 0, 1
 RSX_MAX_RANKS = 16
 RSX_NAIVE_MAX_BYTES = 32768
+RSX_SPLIT_MIN_RANKS = 4
+RSX_SPLIT_MIN_BYTES = 4 * 1024 * 1024
+RSX_SPLIT_MAX_IN_PLACE_BYTES = 256 * 1024 * 1024
 RSX_FUSE_BATCH = 128
 RSX_FUSION_THRESHOLD_DEFAULT = 64 * 1024 * 1024   # Horovod's default tensor_fusion_threshold
 

@@ -25,7 +25,8 @@ DTYPES = {torch.float32: L.RSX_FLOAT32, torch.bfloat16: L.RSX_BFLOAT16, torch.in
           torch.float64: L.RSX_FLOAT64, torch.float16: L.RSX_FLOAT16, torch.int64: L.RSX_INT64,
           torch.uint64: L.RSX_UINT64, torch.int8: L.RSX_INT8}
 OPS = {"sum": L.RSX_SUM, "max": L.RSX_MAX, "min": L.RSX_MIN, "avg": L.RSX_AVG, "prod": L.RSX_PROD}
-ALGOS = {"ring": L.RSX_ALGO_RING, "naive": L.RSX_ALGO_NAIVE, "auto": L.RSX_ALGO_AUTO}
+ALGOS = {"ring": L.RSX_ALGO_RING, "naive": L.RSX_ALGO_NAIVE, "auto": L.RSX_ALGO_AUTO,
+         "ring_fused": L.RSX_ALGO_RING_FUSED, "ring_split": L.RSX_ALGO_RING_SPLIT}
 
 
 def _launch(plan, name: str, stream) -> None:
@@ -119,7 +120,12 @@ class ReduceScatter:
 
 
 class AllReduce:
-    """A prepared all-reduce (``algo`` ring / naive / auto); every tensor has ``count`` elements."""
+    """A prepared all-reduce; every tensor has ``count`` elements.
+
+    ``algo``: "ring" (ring order, one pass or reduce-scatter + all-gather
+    by shape), "ring_fused" (always one pass), "ring_split" (always two
+    passes; W must divide count), "naive" (rank order) or "auto" (naive up
+    to RSX_NAIVE_MAX_BYTES per rank, else ring)."""
 
     def __init__(self, inputs, outputs=None, op: str = "sum", algo: str = "ring",
                  wire: str | None = None):

@@ -154,6 +154,34 @@ rsx_status_t launch_fold_any(int dtype, int op, int world, bool rs, bool vec, Fo
   return hip_status(launch_fold_by_type(dtype, op, world, rs, vec, a, grid, s));
 }
 
+// All-gather launch over validated buffers: piece k = src[k] goes to
+// dst[r] + k * n elements for every r.  A piece already in place (src[k] ==
+// dst[k] + k * n) is read but not written back.
+rsx_status_t launch_gather_any(const void* const* src, void* const* dst, int nranks, size_t n,
+                               size_t es, hipStream_t stream) {
+  const size_t piece_bytes = n * es;
+  bool vec = (piece_bytes % kVecBytes) == 0;
+  for (int r = 0; r < nranks; ++r) vec = vec && aligned16(src[r]) && aligned16(dst[r]);
+  GatherArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int r = 0; r < nranks; ++r) {
+    a.src[r] = src[r];
+    a.dst[r] = dst[r];
+  }
+  a.n = n;
+  a.world = nranks;
+  const uint64_t units = vec ? piece_bytes / kVecBytes : n;
+  const uint64_t per = static_cast<uint64_t>(kCopyUnits) * kBlock;
+  const uint64_t tiles = std::max<uint64_t>(1, (units + per - 1) / per);
+  const uint64_t total = tiles * static_cast<uint64_t>(nranks);
+  if (total > 0x7ffffff0ull) return RSX_ERR_UNSUPPORTED;
+  a.tiles_per_piece = static_cast<uint32_t>(tiles);
+  a.tiles_total = static_cast<uint32_t>(total);
+  split_magic(a.tiles_per_piece, &a.tps_magic, &a.tps_shift);
+  return hip_status(launch_gather(static_cast<int>(es), vec, a,
+                                  dim3(static_cast<uint32_t>(xcd_grid(total))), stream));
+}
+
 // Shared validation of the pointer arrays and enums of the collectives.
 rsx_status_t check_common(const void* const* sendbufs, void* const* recvbufs, int nranks,
                           int dtype) {
@@ -396,26 +424,7 @@ rsx_status_t rsx_all_gather(const void* const* sendbufs, void* const* recvbufs, 
   }
   if (nranks == 1 && in_place_all) return RSX_SUCCESS;
 
-  bool vec = (piece_bytes % kVecBytes) == 0;
-  for (int r = 0; r < nranks; ++r) vec = vec && aligned16(sendbufs[r]) && aligned16(recvbufs[r]);
-  GatherArgs a;
-  memset(&a, 0, sizeof(a));
-  for (int r = 0; r < nranks; ++r) {
-    a.src[r] = sendbufs[r];
-    a.dst[r] = recvbufs[r];
-  }
-  a.n = sendcount;
-  a.world = nranks;
-  const uint64_t units = vec ? piece_bytes / kVecBytes : sendcount;
-  const uint64_t per = static_cast<uint64_t>(kCopyUnits) * kBlock;
-  const uint64_t tiles = std::max<uint64_t>(1, (units + per - 1) / per);
-  const uint64_t total = tiles * static_cast<uint64_t>(nranks);
-  if (total > 0x7ffffff0ull) return RSX_ERR_UNSUPPORTED;
-  a.tiles_per_piece = static_cast<uint32_t>(tiles);
-  a.tiles_total = static_cast<uint32_t>(total);
-  split_magic(a.tiles_per_piece, &a.tps_magic, &a.tps_shift);
-  return hip_status(launch_gather(static_cast<int>(es), vec, a,
-                                  dim3(static_cast<uint32_t>(xcd_grid(total))), stream));
+  return launch_gather_any(sendbufs, recvbufs, nranks, sendcount, es, stream);
 }
 
 rsx_status_t rsx_all_reduce(const void* const* sendbufs, void* const* recvbufs, int nranks,
@@ -424,13 +433,16 @@ rsx_status_t rsx_all_reduce(const void* const* sendbufs, void* const* recvbufs, 
   rsx_status_t st = check_common(sendbufs, recvbufs, nranks, dtype);
   if (st != RSX_SUCCESS) return st;
   if (!valid_op(op)) return RSX_ERR_INVALID_OP;
-  if (algo != RSX_ALGO_RING && algo != RSX_ALGO_NAIVE && algo != RSX_ALGO_AUTO)
+  if (algo != RSX_ALGO_RING && algo != RSX_ALGO_NAIVE && algo != RSX_ALGO_AUTO &&
+      algo != RSX_ALGO_RING_FUSED && algo != RSX_ALGO_RING_SPLIT)
     return RSX_ERR_INVALID_ARGUMENT;
   if (count == 0) return RSX_SUCCESS;
   if ((st = check_device_ptrs(sendbufs, recvbufs, nranks)) != RSX_SUCCESS) return st;
   const size_t es = esize_of(dtype);
   size_t bytes;
   if (!mul_ok(count, es, &bytes)) return RSX_ERR_UNSUPPORTED;
+  if (algo == RSX_ALGO_RING_SPLIT && count % static_cast<size_t>(nranks) != 0)
+    return RSX_ERR_UNSUPPORTED;
   Range in[RSX_MAX_RANKS], out[RSX_MAX_RANKS];
   bool in_place_all = true;
   for (int r = 0; r < nranks; ++r) {
@@ -450,6 +462,41 @@ rsx_status_t rsx_all_reduce(const void* const* sendbufs, void* const* recvbufs, 
   const bool naive = algo == RSX_ALGO_NAIVE || (algo == RSX_ALGO_AUTO && bytes <= RSX_NAIVE_MAX_BYTES);
   bool vec = true;
   for (int r = 0; r < nranks; ++r) vec = vec && aligned16(sendbufs[r]) && aligned16(recvbufs[r]);
+
+  // Two passes ("Distributed primitives": Ring AllReduce = ReduceScatter +
+  // AllGather): the reduce-scatter stores segment k into recvbufs[k] at its
+  // own offset, and the all-gather copies it from there to the other ranks.
+  // Each lane of the reduce-scatter reads its element of every input before
+  // it stores, and touches no other segment, so every alias the one-pass
+  // form accepts is still safe; the all-gather runs after the last read of
+  // the inputs, in stream order.
+  if (!naive && count % static_cast<size_t>(nranks) == 0) {
+    const size_t seg = count / static_cast<size_t>(nranks);
+    const bool split =
+        algo == RSX_ALGO_RING_SPLIT ||
+        (algo != RSX_ALGO_RING_FUSED && nranks >= RSX_SPLIT_MIN_RANKS && vec &&
+         (seg * es) % kVecBytes == 0 && bytes >= RSX_SPLIT_MIN_BYTES &&
+         !(in_place_all && bytes > RSX_SPLIT_MAX_IN_PLACE_BYTES));
+    if (split) {
+      const bool rs_vec = vec && (seg * es) % kVecBytes == 0;
+      FoldArgs a;
+      memset(&a, 0, sizeof(a));
+      const void* pieces[RSX_MAX_RANKS];
+      for (int r = 0; r < nranks; ++r) {
+        a.src[r] = sendbufs[r];
+        a.dst[r] = static_cast<char*>(recvbufs[r]) + static_cast<size_t>(r) * seg * es;
+        pieces[r] = a.dst[r];
+      }
+      a.count = count;
+      a.seg = seg;
+      a.rot = 1;
+      const int vl = static_cast<int>(kVecBytes / es);
+      st = launch_fold_any(dtype, op, nranks, true, rs_vec, a, fold_tiles(seg, nranks, rs_vec, vl),
+                           static_cast<uint32_t>(nranks), stream);
+      if (st != RSX_SUCCESS) return st;
+      return launch_gather_any(pieces, recvbufs, nranks, seg, es, stream);
+    }
+  }
 
   FoldArgs a;
   memset(&a, 0, sizeof(a));
@@ -485,8 +532,10 @@ rsx_status_t rsx_fused_all_reduce(const void* const* sendtensors, void* const* r
   const size_t es = esize_of(dtype);
   if (es == 0) return RSX_ERR_INVALID_TYPE;
   if (!valid_op(op)) return RSX_ERR_INVALID_OP;
-  if (algo != RSX_ALGO_RING && algo != RSX_ALGO_NAIVE && algo != RSX_ALGO_AUTO)
+  if (algo != RSX_ALGO_RING && algo != RSX_ALGO_NAIVE && algo != RSX_ALGO_AUTO &&
+      algo != RSX_ALGO_RING_FUSED && algo != RSX_ALGO_RING_SPLIT)
     return RSX_ERR_INVALID_ARGUMENT;
+  if (algo == RSX_ALGO_RING_SPLIT) return RSX_ERR_UNSUPPORTED;
   if (ntensors > 0 && counts == nullptr) return RSX_ERR_INVALID_ARGUMENT;
   size_t total = 0;
   for (int i = 0; i < ntensors; ++i) {

@@ -49,9 +49,15 @@
 extern "C" {
 #endif
 
-#define RSX_VERSION 100          /* 1.0.0 */
+#define RSX_VERSION 110          /* 1.1.0 */
 #define RSX_MAX_RANKS 16         /* largest W a call accepts */
 #define RSX_NAIVE_MAX_BYTES 32768 /* RSX_ALGO_AUTO picks naive at or below this, per rank [MX] */
+/* RSX_ALGO_RING runs the all-reduce as two passes (reduce-scatter, then
+ * all-gather) from this many ranks and bytes per rank on; in place, only up
+ * to RSX_SPLIT_MAX_IN_PLACE_BYTES per rank (see rsx_all_reduce). */
+#define RSX_SPLIT_MIN_RANKS 4
+#define RSX_SPLIT_MIN_BYTES 4194304
+#define RSX_SPLIT_MAX_IN_PLACE_BYTES 268435456
 #define RSX_FUSE_BATCH 128       /* tensors per pack/unpack launch */
 
 typedef enum {
@@ -81,9 +87,11 @@ typedef enum {
 } rsx_op_t;
 
 typedef enum {
-  RSX_ALGO_RING = 0,  /* segment k folded in ring order (k+1)%W, ..., k; then gathered */
-  RSX_ALGO_NAIVE = 1, /* every element folded in rank order 0..W-1 [MX] */
-  RSX_ALGO_AUTO = 2   /* NAIVE when count * element size <= RSX_NAIVE_MAX_BYTES, else RING */
+  RSX_ALGO_RING = 0,       /* segment k folded in ring order (k+1)%W, ..., k; then gathered */
+  RSX_ALGO_NAIVE = 1,      /* every element folded in rank order 0..W-1 [MX] */
+  RSX_ALGO_AUTO = 2,       /* NAIVE when count * element size <= RSX_NAIVE_MAX_BYTES, else RING */
+  RSX_ALGO_RING_FUSED = 3, /* RING, always as one pass (fold, then store to every rank) */
+  RSX_ALGO_RING_SPLIT = 4  /* RING, always as a reduce-scatter, then an all-gather [DP] */
 } rsx_algo_t;
 
 typedef enum {
@@ -137,8 +145,21 @@ rsx_status_t rsx_all_gather(const void* const* sendbufs, void* const* recvbufs,
  *   S = ceil(count/W): segment k = [min(kS,count), min((k+1)S,count)), see
  *   rsx_segment_begin.  Segment k is folded in ring order (k+1)%W, ..., k and
  *   written to every rank: the result equals rsx_all_gather applied to the
- *   reduce-scatter output whenever W divides count, in one pass that keeps
- *   the partials in registers.
+ *   reduce-scatter output whenever W divides count.  It runs in one of two
+ *   forms, with the same bits (the same folds in the same order):
+ *   - one pass (RSX_ALGO_RING_FUSED): each lane folds its element of all W
+ *     inputs in registers and stores the result to all W outputs;
+ *   - two passes (RSX_ALGO_RING_SPLIT): a reduce-scatter writes segment k
+ *     into recvbufs[k] at its own offset, then an all-gather copies it from
+ *     there to the other W-1 outputs.  That moves (2W+1)/(2W) of the bytes
+ *     of one pass, yet runs faster on large buffers: each pass has fewer
+ *     concurrent streams (W+1, then 1+(W-1)) than the single pass (2W).
+ *   RSX_ALGO_RING takes two passes when W >= RSX_SPLIT_MIN_RANKS, W divides
+ *   count, every buffer is 16-byte aligned, S * size is a multiple of 16,
+ *   count * size >= RSX_SPLIT_MIN_BYTES and, in place, count * size <=
+ *   RSX_SPLIT_MAX_IN_PLACE_BYTES; one pass otherwise.
+ *   RSX_ALGO_RING_SPLIT needs W to divide count (else RSX_ERR_UNSUPPORTED)
+ *   and takes any alignment.
  * RSX_ALGO_NAIVE: every element folded in rank order 0..W-1 [MX].
  * In place: recvbufs[r] == sendbufs[r] for every r (or a permutation of the
  * send buffers) is allowed; other overlaps return RSX_ERR_ALIASING.
@@ -179,6 +200,8 @@ rsx_status_t rsx_fuse_unpack(const void* fused, void* const* tensors, const size
  * folded in the order of the fused segment holding that offset.  No fusion
  * buffer is read or written, so HBM traffic is one all-reduce of the tensors.
  * RSX_ALGO_AUTO picks naive when F * element size <= RSX_NAIVE_MAX_BYTES.
+ * Ring order is always one pass here (RSX_ALGO_RING_FUSED and RSX_ALGO_RING
+ * alike); RSX_ALGO_RING_SPLIT returns RSX_ERR_UNSUPPORTED.
  * In place: recvtensors[r*n + i] == sendtensors[r2*n + i] (same tensor index)
  * is allowed; any other overlap of a destination returns RSX_ERR_ALIASING.
  * Zero-count tensors are skipped and may be null.  Launches about one kernel

@@ -64,12 +64,16 @@ def test_enum_and_macro_values_match_binding(lib):
                       ("RSX_SUM", L.RSX_SUM), ("RSX_MAX", L.RSX_MAX),
                       ("RSX_MIN", L.RSX_MIN), ("RSX_AVG", L.RSX_AVG), ("RSX_PROD", L.RSX_PROD),
                       ("RSX_ALGO_RING", L.RSX_ALGO_RING), ("RSX_ALGO_NAIVE", L.RSX_ALGO_NAIVE),
-                      ("RSX_ALGO_AUTO", L.RSX_ALGO_AUTO)]:
+                      ("RSX_ALGO_AUTO", L.RSX_ALGO_AUTO), ("RSX_ALGO_RING_FUSED", L.RSX_ALGO_RING_FUSED),
+                      ("RSX_ALGO_RING_SPLIT", L.RSX_ALGO_RING_SPLIT)]:
         assert re.search(rf"\b{name}\s*=\s*{val}\b", text), name
     for code, name in L.STATUS.items():
         assert re.search(rf"\b{name}\s*=\s*{code}\b", text), name
     assert _header_int("RSX_MAX_RANKS") == L.RSX_MAX_RANKS
     assert _header_int("RSX_NAIVE_MAX_BYTES") == L.RSX_NAIVE_MAX_BYTES
+    assert _header_int("RSX_SPLIT_MIN_RANKS") == L.RSX_SPLIT_MIN_RANKS
+    assert _header_int("RSX_SPLIT_MIN_BYTES") == L.RSX_SPLIT_MIN_BYTES
+    assert _header_int("RSX_SPLIT_MAX_IN_PLACE_BYTES") == L.RSX_SPLIT_MAX_IN_PLACE_BYTES
     assert _header_int("RSX_FUSE_BATCH") == L.RSX_FUSE_BATCH
     assert lib.rsx_version() == _header_int("RSX_VERSION")
 
@@ -138,10 +142,23 @@ def test_bad_enums(lib):
     assert _rs(lib, s, r, 2, 4, dt=-1) == 2
     assert _rs(lib, s, r, 2, 4, op=5) == 3
     assert _ar(lib, s, r, 2, 4, op=-1) == 3
-    assert _ar(lib, s, r, 2, 4, algo=3) == 1
+    assert _ar(lib, s, r, 2, 4, algo=5) == 1
+    assert _ar(lib, s, r, 2, 4, algo=-1) == 1
     assert _ag(lib, s, r, 2, 4, dt=9) == 2
     # type is checked before op, as the page's dispatch switches on type first
     assert _rs(lib, s, r, 2, 4, dt=9, op=9) == 2
+
+
+@fake_ptrs
+def test_ring_split_needs_rank_count_to_divide_count(lib):
+    s = [A + i * MB for i in range(3)]
+    r = [A + 8 * MB + i * MB for i in range(3)]
+    assert _ar(lib, s, r, 3, 4, algo=L.RSX_ALGO_RING_SPLIT) == 4
+    assert _ar(lib, s, r, 3, 7, algo=L.RSX_ALGO_RING_SPLIT) == 4
+    assert _ar(lib, s, r, 3, 0, algo=L.RSX_ALGO_RING_SPLIT) == 0   # nothing to do
+    # bad arguments are still reported as such
+    assert _ar(lib, s, r, 3, 4, op=9, algo=L.RSX_ALGO_RING_SPLIT) == 3
+    assert _ar(lib, s[:2] + [None], r, 3, 4, algo=L.RSX_ALGO_RING_SPLIT) == 1
 
 
 @fake_ptrs
@@ -255,6 +272,7 @@ def test_fused_all_reduce_validation(lib):
     assert _far(lib, s, r, c, 2, dt=9) == 2
     assert _far(lib, s, r, c, 2, op=7) == 3
     assert _far(lib, s, r, c, 2, algo=9) == 1
+    assert _far(lib, s, r, c, 2, algo=L.RSX_ALGO_RING_SPLIT) == 4   # the list kernel is one pass
     assert _far(lib, s, r, [0, 0, 0], 2) == 0                      # nothing to do, no launch
     assert lib.rsx_fused_all_reduce(None, None, L.size_array([0]), 1, 2, 0, 0, 0, None) == 0
     assert _far(lib, s, r, [2 ** 62, 1, 1], 2) == 4                 # bytes overflow

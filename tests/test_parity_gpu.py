@@ -94,6 +94,121 @@ def test_all_reduce(w, op, dtype, algo):
         assert_parity(got[r], want[r], dtype, f"rank {r}")
 
 
+@pytest.mark.parametrize("dtype", ALL_DTYPES)
+@pytest.mark.parametrize("w", WORLDS)
+@pytest.mark.parametrize("ragged", [False, True])
+def test_all_reduce_two_pass_form(w, dtype, ragged):
+    # Reduce-scatter into each output's own segment, then an in-place
+    # all-gather: the same bits as the one-pass form and the oracle.  A
+    # segment that is not a whole number of 16-byte vectors takes the
+    # element-wise kernels.  Op and in-place vary with the case.
+    te = tile_elems(w, dtype)
+    seg = 2 * te + te // 2 + 3 * VL[dtype] + (1 if ragged else 0)
+    i = WORLDS.index(w) + 3 * ALL_DTYPES.index(dtype) + int(ragged)
+    op, in_place = OPS[i % len(OPS)], bool(i % 2)
+    xs = inputs(21, w, w * seg, dtype)
+    say(f"ar two-pass w={w} dtype={dtype} seg={seg} op={op} in_place={in_place}")
+    got = run_ar(xs, dtype, op, "ring_split", in_place)
+    fused = run_ar(xs, dtype, op, "ring_fused", in_place)
+    want = oracle.all_reduce(xs, op, dtype)
+    for r in range(w):
+        assert_parity(got[r], want[r], dtype, f"two-pass rank {r}")
+        assert_parity(fused[r], want[r], dtype, f"one-pass rank {r}")
+
+
+@pytest.mark.parametrize("op", OPS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32", "f32h"])
+def test_all_reduce_two_pass_every_op(op, dtype):
+    w = 8
+    seg = 3 * tile_elems(w, dtype) + 5 * VL[dtype]
+    xs = inputs(22, w, w * seg, dtype)
+    say(f"ar two-pass w={w} dtype={dtype} op={op}")
+    got = run_ar(xs, dtype, op, "ring_split")
+    want = oracle.all_reduce(xs, op, dtype)
+    for r in range(w):
+        assert_parity(got[r], want[r], dtype, f"rank {r}")
+
+
+@pytest.mark.parametrize("w,dtype,count,in_place", [
+    (4, "f32", 1 << 20, False),          # exactly RSX_SPLIT_MIN_BYTES per rank: two passes
+    (4, "f32", (1 << 20) - 4, False),    # just below: one pass
+    (8, "bf16", 1 << 21, True),          # in place, 4 MiB: two passes
+    (16, "i32", (1 << 20) + 8, False),   # W does not divide count: one pass
+    (3, "f32", 3 << 20, False),          # fewer than RSX_SPLIT_MIN_RANKS: one pass
+    (8, "f32", (1 << 21) + 8, False),    # segments not whole vectors: one pass
+])
+def test_ring_around_the_two_pass_threshold(w, dtype, count, in_place):
+    # "ring" picks its form by shape; every choice gives the oracle's bits.
+    xs = inputs(23, w, count, dtype)
+    say(f"ar ring by shape w={w} dtype={dtype} count={count} in_place={in_place}")
+    got = run_ar(xs, dtype, "sum", "ring", in_place)
+    want = oracle.all_reduce(xs, "sum", dtype)
+    for r in range(w):
+        assert_parity(got[r], want[r], dtype, f"rank {r}")
+
+
+def test_two_pass_with_outputs_a_permutation_of_the_inputs():
+    # recvbufs[r] == sendbufs[(r + 1) % W]: the reduce-scatter overwrites a
+    # segment of another rank's input only in the lanes that already read it.
+    for w, algo in ((8, "ring_split"), (8, "ring"), (5, "ring_split")):
+        seg = (1 << 19) if algo == "ring" else 3000
+        xs = inputs(24, w, w * seg, "f32")
+        dev = [to_dev(x, "f32") for x in xs]
+        say(f"ar permuted outputs w={w} algo={algo}")
+        rsx.all_reduce(dev, [dev[(r + 1) % w] for r in range(w)], "sum", algo)
+        torch.cuda.synchronize()
+        want = oracle.all_reduce(xs, "sum", "f32")
+        for r in range(w):
+            assert_parity(to_host(dev[r], "f32"), want[r], "f32", f"rank {r}")
+
+
+def test_two_pass_unaligned_and_refusals():
+    w, s = 4, 3001
+    xs = inputs(25, w, w * s, "f32")
+    bases = [to_dev(np.concatenate([np.zeros(1, np.float32), x]), "f32") for x in xs]
+    dev = [b[1:] for b in bases]                      # 4-byte offset: not 16-byte aligned
+    outs = [empty(w * s + 3, "f32")[3:] for _ in range(w)]
+    say("unaligned two-pass ar")
+    rsx.all_reduce(dev, outs, "min", "ring_split")
+    torch.cuda.synchronize()
+    want = oracle.all_reduce(xs, "min", "f32")
+    for r in range(w):
+        assert_parity(to_host(outs[r], "f32"), want[r], "f32", f"rank {r}")
+    with pytest.raises(rsx.RsxError) as e:           # W does not divide count
+        rsx.all_reduce([d[:-1] for d in dev], None, "sum", "ring_split")
+    assert e.value.status == 4
+    tens = [[to_dev(x[:100], "f32")] for x in xs]
+    with pytest.raises(rsx.RsxError) as e:           # the tensor-list kernel is one pass only
+        rsx.TensorFusionAllReduce(tens, None, "sum", "ring_split")()
+    assert e.value.status == 4
+
+
+def test_two_pass_graph_capture_replays():
+    w, n = 8, 8 * 4096
+    xs = inputs(26, w, n, "bf16")
+    dev = [to_dev(x, "bf16") for x in xs]
+    out = [empty(n, "bf16") for _ in range(w)]
+    ar = rsx.AllReduce(dev, out, "avg", "ring_split")
+    want = oracle.all_reduce(xs, "avg", "bf16")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ar()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    say("graph capture two-pass ar")
+    with torch.cuda.graph(g):
+        ar()
+    for rep in range(4):
+        for o in out:
+            o.fill_(3.0)                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for r in range(w):
+            assert_parity(to_host(out[r], "bf16"), want[r], "bf16", f"replay {rep} rank {r}")
+
+
 def _with_ieee_specials(xs, dtype, seed):
     """Normal data with IEEE specials planted: +-inf, NaN, +-0, the smallest
     subnormal and values near the top of the range (sums and products then
