@@ -188,11 +188,10 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
         step = bucketed("ring")
         res = {"workload": "all-reduce avg bf16 (fp32 accumulate), W=8, 134,217,728/rank, "
                            f"{len(bounds)} buckets of <= 25 MiB in sequence on one stream; "
-                           "ring = the library's choice by shape (two passes for these buckets)",
+                           "ring = one pass per bucket",
                "ring": _stat(time_launches(step, reps // 4 or 1, warm, torch), nb)}
         res["ring"]["graph_us_per_step"] = graph_us_per_call(step, 1, 10, torch)
-        # The two forms of the ring all-reduce, forced; the same bits.
-        res["ring_fused_one_pass"] = _stat(time_launches(bucketed("ring_fused"), reps // 4 or 1, warm, torch), nb)
+        # The two-pass form (reduce-scatter, then all-gather); the same bits.
         st = _stat(time_launches(bucketed("ring_split"), reps // 4 or 1, warm, torch), nb)
         # reduce-scatter W*n*2 in, n*2 out; all-gather n*2 in, (W-1)*n*2 out
         st["actual_bytes"] = nb + n * 2
@@ -218,7 +217,7 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
                                                 world * n * 4 + world * seg * 4)
             res[f"all_reduce_{op}"] = _stat(time_launches(rsx.AllReduce(dev, ar, op, "ring"), reps, warm, torch),
                                             2 * world * n * 4)
-        res["all_reduce_sum_one_pass"] = _stat(time_launches(rsx.AllReduce(dev, ar, "sum", "ring_fused"), reps,
+        res["all_reduce_sum_two_pass"] = _stat(time_launches(rsx.AllReduce(dev, ar, "sum", "ring_split"), reps,
                                                              warm, torch), 2 * world * n * 4)
         return res
     if name == "fused":
@@ -375,11 +374,16 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
                 compute(b)
         nb = 2 * world * n * 2
         res = {"workload": f"bucketed all-reduce avg bf16, W=8, 134,217,728/rank, {len(plan)} buckets; "
-                           f"per bucket one {m}x{m}x{m} fp32 matmul on the main stream first",
+                           f"per bucket one {m}x{m}x{m} fp32 matmul on the main stream first; "
+                           "side-stream reductions without the occupancy caps unless named",
                "compute_only": _stat(time_launches(compute_only, reps // 4 or 1, warm, torch), 0),
                "all_reduce_only": _stat(time_launches(plan, reps // 4 or 1, warm, torch), nb),
                "serial_one_stream": _stat(time_launches(serial, reps // 4 or 1, warm, torch), nb),
                "overlapped_side_stream": _stat(time_launches(overlapped, reps // 4 or 1, warm, torch), nb)}
+        # the same with the library's occupancy caps left on for the side-stream launches
+        plan.occupancy_caps = True
+        res["overlapped_side_stream_caps_on"] = _stat(time_launches(overlapped, reps // 4 or 1, warm, torch), nb)
+        plan.occupancy_caps = False
         for k in ("compute_only",):
             for f in ("GBps", "pct_of_peak_hbm", "bytes"):
                 res[k].pop(f)
@@ -392,8 +396,8 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
         gen.manual_seed(11)
         ins_all = torch.randn(world * top, device="cuda:0", generator=gen) * 1e-3
         outs_all = torch.empty(world * top, device="cuda:0")
-        res = {"workload": "reduce-scatter and ring all-reduce sum fp32 (the library's choice of form, and "
-                           "one pass forced; and an in-place avg all-reduce), W=8, per-rank size sweep; "
+        res = {"workload": "reduce-scatter and ring all-reduce sum fp32 (one pass, and two passes for "
+                           "comparison; and an in-place avg all-reduce), W=8, per-rank size sweep; "
                            "below 64 MiB graph-timed device time (50 calls per graph), above HIP events per call"}
         kib = 4
         while kib * 1024 <= 2 ** 30:
@@ -406,12 +410,12 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
             ar = rsx.AllReduce(ins, ar_out, "sum", "ring")
             # in place (8 buffers instead of 16); avg keeps repeated calls' values bounded
             ar_in = rsx.AllReduce(ins, None, "avg", "ring")
-            # the one-pass form forced, for comparison where "ring" takes two passes
-            ar_one = rsx.AllReduce(ins, ar_out, "sum", "ring_fused")
+            # the two-pass form (reduce-scatter, then all-gather), for comparison
+            ar_two = rsx.AllReduce(ins, ar_out, "sum", "ring_split")
             row = {}
             for what, fn, nbytes in (("reduce_scatter", rs, world * n * 4 + world * seg * 4),
                                      ("all_reduce", ar, 2 * world * n * 4),
-                                     ("all_reduce_one_pass", ar_one, 2 * world * n * 4),
+                                     ("all_reduce_two_pass", ar_two, 2 * world * n * 4),
                                      ("all_reduce_in_place_avg", ar_in, 2 * world * n * 4)):
                 if kib * 1024 < 64 * 2 ** 20:
                     us = graph_us_per_call(fn, 50, 20, torch)

@@ -10,5 +10,6 @@ from .api import (  # noqa: F401
     all_gather, all_reduce,
     all_reduce_bucketed, fuse_pack, fuse_unpack, fused_all_reduce, reduce_scatter,
     segment_begin, version, SparseAllReduce, sparse_all_reduce, topk_count, SPARSE_MODES,
+    occupancy_caps,
 )
 from ._lib import RsxError  # noqa: F401

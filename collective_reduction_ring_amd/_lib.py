@@ -21,9 +21,6 @@ RSX_ALGO_RING, RSX_ALGO_NAIVE, RSX_ALGO_AUTO, RSX_ALGO_RING_FUSED, RSX_ALGO_RING
 RSX_SPARSE_THRESHOLD, RSX_SPARSE_TOPK = 0, 1
 RSX_MAX_RANKS = 16
 RSX_NAIVE_MAX_BYTES = 32768
-RSX_SPLIT_MIN_RANKS = 4
-RSX_SPLIT_MIN_BYTES = 4 * 1024 * 1024
-RSX_SPLIT_MAX_IN_PLACE_BYTES = 256 * 1024 * 1024
 RSX_FUSE_BATCH = 128
 RSX_FUSION_THRESHOLD_DEFAULT = 64 * 1024 * 1024   # Horovod's default tensor_fusion_threshold
 
@@ -58,6 +55,7 @@ SIGNATURES = {
     "rsx_dtype_size": (_SZ, [_I]),
     "rsx_status_string": (ctypes.c_char_p, [_I]),
     "rsx_version": (_I, []),
+    "rsx_set_occupancy_caps": (_I, [_I]),
 }
 
 

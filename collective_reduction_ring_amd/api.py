@@ -9,7 +9,8 @@ pointers and counts.
 Semantics (see include/rsx.h): W virtual ranks are W tensors on one GPU.
 ``reduce_scatter`` folds block k of every rank in ring order (k+1)%W, ..., k
 (NCCL 1.x ring reduce-scatter, GetBlock); ``all_reduce`` is reduce-scatter then
-all-gather ("Distributed primitives", Ring AllReduce) in one pass.
+all-gather ("Distributed primitives", Ring AllReduce), in one pass unless
+``algo="ring_split"``.
 """
 from __future__ import annotations
 
@@ -122,10 +123,10 @@ class ReduceScatter:
 class AllReduce:
     """A prepared all-reduce; every tensor has ``count`` elements.
 
-    ``algo``: "ring" (ring order, one pass or reduce-scatter + all-gather
-    by shape), "ring_fused" (always one pass), "ring_split" (always two
-    passes; W must divide count), "naive" (rank order) or "auto" (naive up
-    to RSX_NAIVE_MAX_BYTES per rank, else ring)."""
+    ``algo``: "ring" (ring order, one pass), "ring_fused" (the same, named
+    by its form), "ring_split" (ring order as a reduce-scatter, then an
+    all-gather; W must divide count), "naive" (rank order) or "auto" (naive
+    up to RSX_NAIVE_MAX_BYTES per rank, else ring)."""
 
     def __init__(self, inputs, outputs=None, op: str = "sum", algo: str = "ring",
                  wire: str | None = None):
@@ -195,6 +196,24 @@ def all_reduce_bucketed(inputs, outputs=None, bucket_elems: int = 13_107_200, op
                   wire)(stream)
 
 
+class occupancy_caps:
+    """Context manager: the library's occupancy caps on (True) or off (False)
+    for the launches this thread makes inside it (rsx_set_occupancy_caps);
+    the previous setting comes back on exit.  Off suits launches that overlap
+    other kernels; the results are the same either way."""
+
+    def __init__(self, enabled: bool):
+        self.enabled = bool(enabled)
+
+    def __enter__(self):
+        self.prev = L.lib().rsx_set_occupancy_caps(1 if self.enabled else 0)
+        return self
+
+    def __exit__(self, *exc):
+        L.lib().rsx_set_occupancy_caps(self.prev)
+        return False
+
+
 class BucketedAllReduce:
     """Bucketed all-reduce that overlaps with whatever produces the gradients
     ("Distributed primitives", In practice: the gradient is all-reduced in
@@ -208,10 +227,15 @@ class BucketedAllReduce:
     later work and the reduction run side by side.  ``wait()`` makes a stream
     wait for every enqueued reduction.  The reduction stream is created here
     with the default priority unless one is given.
+
+    ``occupancy_caps`` (default False): the reductions launched by ``ready``
+    and ``__call__`` run without the library's occupancy caps, so that the
+    producer's kernels still find LDS free on the CUs they share.
     """
 
     def __init__(self, inputs, outputs=None, bucket_elems: int = 13_107_200, op: str = "sum",
-                 algo: str = "ring", wire: str | None = None, stream=None):
+                 algo: str = "ring", wire: str | None = None, stream=None,
+                 occupancy_caps: bool = False):
         if bucket_elems <= 0:
             raise ValueError("bucket_elems must be positive")
         outputs = inputs if outputs is None else outputs
@@ -222,6 +246,7 @@ class BucketedAllReduce:
         self.device = inputs[0].device
         self.stream = stream if stream is not None else torch.cuda.Stream(device=self.device)
         self.events = [torch.cuda.Event() for _ in self.plans]
+        self.occupancy_caps = occupancy_caps
 
     def __len__(self) -> int:
         return len(self.plans)
@@ -231,7 +256,8 @@ class BucketedAllReduce:
         src = torch.cuda.current_stream(self.device) if stream is None else stream
         self.events[b].record(src)
         self.stream.wait_event(self.events[b])
-        self.plans[b](self.stream)
+        with occupancy_caps(self.occupancy_caps):
+            self.plans[b](self.stream)
 
     def wait(self, stream=None) -> None:
         """Make `stream` (default: current) wait for every reduction enqueued so far."""
@@ -240,8 +266,9 @@ class BucketedAllReduce:
 
     def __call__(self, stream=None) -> None:
         """Every bucket at once, on `stream` (no overlap): the serial reference."""
-        for p in self.plans:
-            p(stream)
+        with occupancy_caps(self.occupancy_caps):
+            for p in self.plans:
+                p(stream)
 
 
 class _FuseCopy:

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a) {
   }
 }
 
-hipError_t launch_gather(int esize, bool vec, const GatherArgs& a, dim3 grid, hipStream_t s) {
+hipError_t launch_gather(int esize, bool vec, const GatherArgs& a, dim3 grid, uint32_t lds, hipStream_t s) {
   void* args[] = {const_cast<GatherArgs*>(&a)};
   const void* fn;
   switch (esize) {
@@ -100,7 +100,7 @@ hipError_t launch_gather(int esize, bool vec, const GatherArgs& a, dim3 grid, hi
     default:
       return hipErrorInvalidValue;
   }
-  return hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, s);
+  return hipLaunchKernel(fn, grid, dim3(kBlock), args, lds, s);
 }
 
 // -------------------------------------------------------- pack / unpack
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(kBlock) void multicopy_kernel(const MultiCopyArgs a
   }
 }
 
-hipError_t launch_multicopy(int esize, const MultiCopyArgs& a, hipStream_t s) {
+hipError_t launch_multicopy(int esize, const MultiCopyArgs& a, uint32_t lds, hipStream_t s) {
   void* args[] = {const_cast<MultiCopyArgs*>(&a)};
   const void* fn;
   switch (esize) {
@@ -213,7 +213,7 @@ hipError_t launch_multicopy(int esize, const MultiCopyArgs& a, hipStream_t s) {
       return hipErrorInvalidValue;
   }
   const uint64_t tiles = a.tile_start[a.n];
-  return hipLaunchKernel(fn, dim3(static_cast<uint32_t>(xcd_grid(tiles))), dim3(kBlock), args, 0, s);
+  return hipLaunchKernel(fn, dim3(static_cast<uint32_t>(xcd_grid(tiles))), dim3(kBlock), args, lds, s);
 }
 
 }  // namespace rsx

@@ -3,13 +3,13 @@
 
 namespace rsx {
 
-hipError_t launch_fold_f64(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid,
+hipError_t launch_fold_f64(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid, uint32_t lds,
                            hipStream_t s) {
-  return launch_fold<F64T>(op, world, rs, vec, a, grid, s);
+  return launch_fold<F64T>(op, world, rs, vec, a, grid, lds, s);
 }
 
-hipError_t launch_list_f64(int op, int world, const ListArgs& a, dim3 grid, hipStream_t s) {
-  return launch_list<F64T>(op, world, a, grid, s);
+hipError_t launch_list_f64(int op, int world, const ListArgs& a, dim3 grid, uint32_t lds, hipStream_t s) {
+  return launch_list<F64T>(op, world, a, grid, lds, s);
 }
 
 }  // namespace rsx

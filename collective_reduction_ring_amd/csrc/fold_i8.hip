@@ -3,13 +3,13 @@
 
 namespace rsx {
 
-hipError_t launch_fold_i8(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid,
+hipError_t launch_fold_i8(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid, uint32_t lds,
                            hipStream_t s) {
-  return launch_fold<I8T>(op, world, rs, vec, a, grid, s);
+  return launch_fold<I8T>(op, world, rs, vec, a, grid, lds, s);
 }
 
-hipError_t launch_list_i8(int op, int world, const ListArgs& a, dim3 grid, hipStream_t s) {
-  return launch_list<I8T>(op, world, a, grid, s);
+hipError_t launch_list_i8(int op, int world, const ListArgs& a, dim3 grid, uint32_t lds, hipStream_t s) {
+  return launch_list<I8T>(op, world, a, grid, lds, s);
 }
 
 }  // namespace rsx

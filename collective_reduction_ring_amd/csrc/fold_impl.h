@@ -517,7 +517,7 @@ __global__ __launch_bounds__(kBlock) void list_fold_kernel(const ListArgs a) {
 // --------------------------------------------------------------- dispatch
 
 template <class D, int OP, int W>
-hipError_t launch_world(bool rs, bool vec, const FoldArgs& a, dim3 grid, hipStream_t s) {
+hipError_t launch_world(bool rs, bool vec, const FoldArgs& a, dim3 grid, uint32_t lds, hipStream_t s) {
   void* args[] = {const_cast<FoldArgs*>(&a)};
   const void* fn;
   if (rs) {
@@ -527,15 +527,15 @@ hipError_t launch_world(bool rs, bool vec, const FoldArgs& a, dim3 grid, hipStre
     fn = vec ? reinterpret_cast<const void*>(&fold_kernel<D, OP, W, false, true>)
              : reinterpret_cast<const void*>(&fold_kernel<D, OP, W, false, false>);
   }
-  return hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, s);
+  return hipLaunchKernel(fn, grid, dim3(kBlock), args, lds, s);
 }
 
 template <class D, int OP>
-hipError_t launch_op(int world, bool rs, bool vec, const FoldArgs& a, dim3 grid, hipStream_t s) {
+hipError_t launch_op(int world, bool rs, bool vec, const FoldArgs& a, dim3 grid, uint32_t lds, hipStream_t s) {
   switch (world) {
 #define RSX_W(n) \
   case n:        \
-    return launch_world<D, OP, n>(rs, vec, a, grid, s);
+    return launch_world<D, OP, n>(rs, vec, a, grid, lds, s);
     RSX_W(1) RSX_W(2) RSX_W(3) RSX_W(4) RSX_W(5) RSX_W(6) RSX_W(7) RSX_W(8)
     RSX_W(9) RSX_W(10) RSX_W(11) RSX_W(12) RSX_W(13) RSX_W(14) RSX_W(15) RSX_W(16)
 #undef RSX_W
@@ -545,7 +545,7 @@ hipError_t launch_op(int world, bool rs, bool vec, const FoldArgs& a, dim3 grid,
 }
 
 template <class D, int OP>
-hipError_t launch_list_op(int world, const ListArgs& a, dim3 grid, hipStream_t s) {
+hipError_t launch_list_op(int world, const ListArgs& a, dim3 grid, uint32_t lds, hipStream_t s) {
   void* args[] = {const_cast<ListArgs*>(&a)};
   const void* fn;
   switch (world) {
@@ -559,41 +559,41 @@ hipError_t launch_list_op(int world, const ListArgs& a, dim3 grid, hipStream_t s
     default:
       return hipErrorInvalidValue;
   }
-  return hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, s);
+  return hipLaunchKernel(fn, grid, dim3(kBlock), args, lds, s);
 }
 
 template <class D>
-hipError_t launch_list(int op, int world, const ListArgs& a, dim3 grid, hipStream_t s) {
+hipError_t launch_list(int op, int world, const ListArgs& a, dim3 grid, uint32_t lds, hipStream_t s) {
   switch (op) {
     case RSX_SUM:
-      return launch_list_op<D, RSX_SUM>(world, a, grid, s);
+      return launch_list_op<D, RSX_SUM>(world, a, grid, lds, s);
     case RSX_MAX:
-      return launch_list_op<D, RSX_MAX>(world, a, grid, s);
+      return launch_list_op<D, RSX_MAX>(world, a, grid, lds, s);
     case RSX_MIN:
-      return launch_list_op<D, RSX_MIN>(world, a, grid, s);
+      return launch_list_op<D, RSX_MIN>(world, a, grid, lds, s);
     case RSX_AVG:
-      return launch_list_op<D, RSX_AVG>(world, a, grid, s);
+      return launch_list_op<D, RSX_AVG>(world, a, grid, lds, s);
     case RSX_PROD:
-      return launch_list_op<D, RSX_PROD>(world, a, grid, s);
+      return launch_list_op<D, RSX_PROD>(world, a, grid, lds, s);
     default:
       return hipErrorInvalidValue;
   }
 }
 
 template <class D>
-hipError_t launch_fold(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid,
+hipError_t launch_fold(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid, uint32_t lds,
                        hipStream_t s) {
   switch (op) {
     case RSX_SUM:
-      return launch_op<D, RSX_SUM>(world, rs, vec, a, grid, s);
+      return launch_op<D, RSX_SUM>(world, rs, vec, a, grid, lds, s);
     case RSX_MAX:
-      return launch_op<D, RSX_MAX>(world, rs, vec, a, grid, s);
+      return launch_op<D, RSX_MAX>(world, rs, vec, a, grid, lds, s);
     case RSX_MIN:
-      return launch_op<D, RSX_MIN>(world, rs, vec, a, grid, s);
+      return launch_op<D, RSX_MIN>(world, rs, vec, a, grid, lds, s);
     case RSX_AVG:
-      return launch_op<D, RSX_AVG>(world, rs, vec, a, grid, s);
+      return launch_op<D, RSX_AVG>(world, rs, vec, a, grid, lds, s);
     case RSX_PROD:
-      return launch_op<D, RSX_PROD>(world, rs, vec, a, grid, s);
+      return launch_op<D, RSX_PROD>(world, rs, vec, a, grid, lds, s);
     default:
       return hipErrorInvalidValue;
   }

@@ -5,6 +5,7 @@
 // effect and the error paths can be exercised on a machine without a GPU.
 #include <math.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -47,54 +48,81 @@ size_t esize_of(int dtype) {
 
 bool valid_op(int op) { return op >= RSX_SUM && op <= RSX_PROD; }
 
+// Occupancy caps.  Every lane of the dwordx4 fold and copy kernels keeps one
+// 16-byte access per buffer in flight, so with all 8 workgroups per CU
+// resident the chip keeps more HBM streams open than the memory system serves
+// best.  Reserving LDS, which these kernels do not otherwise use, limits the
+// workgroups resident per CU.  Measured best caps (fp32, 256 MiB per rank,
+// W = 2..16; W = 8 reduce-scatter 381 -> 362-371 us, one-pass all-reduce
+// 805 -> 725-732 us, all-gather 426 -> 380-383 us):
+//   reduce-scatter (W+1 streams per workgroup): 8 at W <= 2, 5 up to W = 10, 3 above;
+//   all-reduce, one pass (2W streams): 8 at W = 1, 5 at W = 2, 3 from W = 3;
+//   all-gather (1 + W): 8 at W <= 2, 6 at W = 4, 6, 8, otherwise 5 up to W = 9, 3 above.
+// The element-wise kernels (unaligned buffers) run best uncapped: they keep
+// less in flight per lane.
+// The caps are per calling thread (rsx_set_occupancy_caps): launches meant to
+// overlap other kernels go without them.
+constexpr uint32_t kLdsPerCu = 160u * 1024u;
+thread_local bool t_caps = true;
+uint32_t lds_for_cap(uint32_t wg_per_cu) {
+  return (!t_caps || wg_per_cu >= 8) ? 0u : (kLdsPerCu / wg_per_cu) & ~1023u;
+}
+uint32_t rs_cap(int w) { return w <= 2 ? 8u : w <= 10 ? 5u : 3u; }
+uint32_t ar_cap(int w) { return w <= 1 ? 8u : w == 2 ? 5u : 3u; }
+uint32_t ag_cap(int w) {
+  if (w <= 2) return 8u;
+  if (w == 4 || w == 6 || w == 8) return 6u;
+  return w <= 9 ? 5u : 3u;
+}
+
 // Per element type launchers (one translation unit each).
 hipError_t launch_fold_by_type(int dtype, int op, int world, bool rs, bool vec, const FoldArgs& a,
-                               dim3 grid, hipStream_t s) {
+                               dim3 grid, uint32_t lds, hipStream_t s) {
   switch (dtype) {
     case RSX_FLOAT32:
-      return launch_fold_f32(op, world, rs, vec, a, grid, s);
+      return launch_fold_f32(op, world, rs, vec, a, grid, lds, s);
     case RSX_BFLOAT16:
-      return launch_fold_bf16(op, world, rs, vec, a, grid, s);
+      return launch_fold_bf16(op, world, rs, vec, a, grid, lds, s);
     case RSX_INT32:
-      return launch_fold_i32(op, world, rs, vec, a, grid, s);
+      return launch_fold_i32(op, world, rs, vec, a, grid, lds, s);
     case RSX_FLOAT64:
-      return launch_fold_f64(op, world, rs, vec, a, grid, s);
+      return launch_fold_f64(op, world, rs, vec, a, grid, lds, s);
     case RSX_FLOAT16:
-      return launch_fold_f16(op, world, rs, vec, a, grid, s);
+      return launch_fold_f16(op, world, rs, vec, a, grid, lds, s);
     case RSX_INT64:
-      return launch_fold_i64(op, world, rs, vec, a, grid, s);
+      return launch_fold_i64(op, world, rs, vec, a, grid, lds, s);
     case RSX_UINT64:
-      return launch_fold_u64(op, world, rs, vec, a, grid, s);
+      return launch_fold_u64(op, world, rs, vec, a, grid, lds, s);
     case RSX_INT8:
-      return launch_fold_i8(op, world, rs, vec, a, grid, s);
+      return launch_fold_i8(op, world, rs, vec, a, grid, lds, s);
     case RSX_FLOAT32_HALF_WIRE:
-      return launch_fold_f32h(op, world, rs, vec, a, grid, s);
+      return launch_fold_f32h(op, world, rs, vec, a, grid, lds, s);
     default:
       return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_list_by_type(int dtype, int op, int world, const ListArgs& a, dim3 grid,
+hipError_t launch_list_by_type(int dtype, int op, int world, const ListArgs& a, dim3 grid, uint32_t lds,
                                hipStream_t s) {
   switch (dtype) {
     case RSX_FLOAT32:
-      return launch_list_f32(op, world, a, grid, s);
+      return launch_list_f32(op, world, a, grid, lds, s);
     case RSX_BFLOAT16:
-      return launch_list_bf16(op, world, a, grid, s);
+      return launch_list_bf16(op, world, a, grid, lds, s);
     case RSX_INT32:
-      return launch_list_i32(op, world, a, grid, s);
+      return launch_list_i32(op, world, a, grid, lds, s);
     case RSX_FLOAT64:
-      return launch_list_f64(op, world, a, grid, s);
+      return launch_list_f64(op, world, a, grid, lds, s);
     case RSX_FLOAT16:
-      return launch_list_f16(op, world, a, grid, s);
+      return launch_list_f16(op, world, a, grid, lds, s);
     case RSX_INT64:
-      return launch_list_i64(op, world, a, grid, s);
+      return launch_list_i64(op, world, a, grid, lds, s);
     case RSX_UINT64:
-      return launch_list_u64(op, world, a, grid, s);
+      return launch_list_u64(op, world, a, grid, lds, s);
     case RSX_INT8:
-      return launch_list_i8(op, world, a, grid, s);
+      return launch_list_i8(op, world, a, grid, lds, s);
     case RSX_FLOAT32_HALF_WIRE:
-      return launch_list_f32h(op, world, a, grid, s);
+      return launch_list_f32h(op, world, a, grid, lds, s);
     default:
       return hipErrorInvalidValue;
   }
@@ -151,7 +179,8 @@ rsx_status_t launch_fold_any(int dtype, int op, int world, bool rs, bool vec, Fo
   a.tiles_total = static_cast<uint32_t>(total);
   split_magic(a.tiles_per_seg, &a.tps_magic, &a.tps_shift);
   const dim3 grid(static_cast<uint32_t>(xcd_grid(total)));
-  return hip_status(launch_fold_by_type(dtype, op, world, rs, vec, a, grid, s));
+  const uint32_t lds = vec ? lds_for_cap(rs ? rs_cap(world) : ar_cap(world)) : 0u;
+  return hip_status(launch_fold_by_type(dtype, op, world, rs, vec, a, grid, lds, s));
 }
 
 // All-gather launch over validated buffers: piece k = src[k] goes to
@@ -179,7 +208,8 @@ rsx_status_t launch_gather_any(const void* const* src, void* const* dst, int nra
   a.tiles_total = static_cast<uint32_t>(total);
   split_magic(a.tiles_per_piece, &a.tps_magic, &a.tps_shift);
   return hip_status(launch_gather(static_cast<int>(es), vec, a,
-                                  dim3(static_cast<uint32_t>(xcd_grid(total))), stream));
+                                  dim3(static_cast<uint32_t>(xcd_grid(total))),
+                                  vec ? lds_for_cap(ag_cap(nranks)) : 0u, stream));
 }
 
 // Shared validation of the pointer arrays and enums of the collectives.
@@ -251,7 +281,7 @@ rsx_status_t fuse_copy(const void* const* tens, const size_t* counts, int ntenso
     }
     if (a.n == 0) continue;
     a.tile_start[a.n] = static_cast<uint32_t>(tiles);
-    const rsx_status_t st = hip_status(launch_multicopy(static_cast<int>(es), a, stream));
+    const rsx_status_t st = hip_status(launch_multicopy(static_cast<int>(es), a, 0u, stream));
     if (st != RSX_SUCCESS) return st;
   }
   return RSX_SUCCESS;
@@ -463,39 +493,35 @@ rsx_status_t rsx_all_reduce(const void* const* sendbufs, void* const* recvbufs, 
   bool vec = true;
   for (int r = 0; r < nranks; ++r) vec = vec && aligned16(sendbufs[r]) && aligned16(recvbufs[r]);
 
-  // Two passes ("Distributed primitives": Ring AllReduce = ReduceScatter +
-  // AllGather): the reduce-scatter stores segment k into recvbufs[k] at its
-  // own offset, and the all-gather copies it from there to the other ranks.
-  // Each lane of the reduce-scatter reads its element of every input before
-  // it stores, and touches no other segment, so every alias the one-pass
-  // form accepts is still safe; the all-gather runs after the last read of
-  // the inputs, in stream order.
-  if (!naive && count % static_cast<size_t>(nranks) == 0) {
+  // Two passes on request ("Distributed primitives": Ring AllReduce =
+  // ReduceScatter + AllGather): the reduce-scatter stores segment k into
+  // recvbufs[k] at its own offset, and the all-gather copies it from there to
+  // the other ranks.  Each lane of the reduce-scatter reads its element of
+  // every input before it stores, and touches no other segment, so every
+  // alias the one-pass form accepts is still safe; the all-gather runs after
+  // the last read of the inputs, in stream order.  With the occupancy caps
+  // the one-pass form is as fast or faster at every measured W and size
+  // (W = 8, 256 MiB per rank: 725-732 against 745-754 us), so RSX_ALGO_RING
+  // takes it.
+  if (algo == RSX_ALGO_RING_SPLIT) {
     const size_t seg = count / static_cast<size_t>(nranks);
-    const bool split =
-        algo == RSX_ALGO_RING_SPLIT ||
-        (algo != RSX_ALGO_RING_FUSED && nranks >= RSX_SPLIT_MIN_RANKS && vec &&
-         (seg * es) % kVecBytes == 0 && bytes >= RSX_SPLIT_MIN_BYTES &&
-         !(in_place_all && bytes > RSX_SPLIT_MAX_IN_PLACE_BYTES));
-    if (split) {
-      const bool rs_vec = vec && (seg * es) % kVecBytes == 0;
-      FoldArgs a;
-      memset(&a, 0, sizeof(a));
-      const void* pieces[RSX_MAX_RANKS];
-      for (int r = 0; r < nranks; ++r) {
-        a.src[r] = sendbufs[r];
-        a.dst[r] = static_cast<char*>(recvbufs[r]) + static_cast<size_t>(r) * seg * es;
-        pieces[r] = a.dst[r];
-      }
-      a.count = count;
-      a.seg = seg;
-      a.rot = 1;
-      const int vl = static_cast<int>(kVecBytes / es);
-      st = launch_fold_any(dtype, op, nranks, true, rs_vec, a, fold_tiles(seg, nranks, rs_vec, vl),
-                           static_cast<uint32_t>(nranks), stream);
-      if (st != RSX_SUCCESS) return st;
-      return launch_gather_any(pieces, recvbufs, nranks, seg, es, stream);
+    const bool rs_vec = vec && (seg * es) % kVecBytes == 0;
+    FoldArgs a;
+    memset(&a, 0, sizeof(a));
+    const void* pieces[RSX_MAX_RANKS];
+    for (int r = 0; r < nranks; ++r) {
+      a.src[r] = sendbufs[r];
+      a.dst[r] = static_cast<char*>(recvbufs[r]) + static_cast<size_t>(r) * seg * es;
+      pieces[r] = a.dst[r];
     }
+    a.count = count;
+    a.seg = seg;
+    a.rot = 1;
+    const int vl = static_cast<int>(kVecBytes / es);
+    st = launch_fold_any(dtype, op, nranks, true, rs_vec, a, fold_tiles(seg, nranks, rs_vec, vl),
+                         static_cast<uint32_t>(nranks), stream);
+    if (st != RSX_SUCCESS) return st;
+    return launch_gather_any(pieces, recvbufs, nranks, seg, es, stream);
   }
 
   FoldArgs a;
@@ -576,19 +602,22 @@ rsx_status_t rsx_fused_all_reduce(const void* const* sendtensors, void* const* r
   const int slots = in_place_all ? w : 2 * w;
   ListArgs a;
   uint64_t tiles = 0;
-  int ntens = 0;  // tensors in the current launch
+  int ntens = 0;        // tensors in the current launch
+  bool all_vec = true;  // every piece of the current launch takes the dwordx4 path
   auto reset = [&]() {
     memset(&a, 0, sizeof(a));
     a.rot = naive ? 0 : 1;
     a.in_place = in_place_all ? 1 : 0;
     tiles = 0;
     ntens = 0;
+    all_vec = true;
   };
   auto flush = [&]() -> rsx_status_t {
     if (a.npieces == 0) return RSX_SUCCESS;
     a.tile_start[a.npieces] = static_cast<uint32_t>(tiles);
     const dim3 grid(static_cast<uint32_t>(xcd_grid(tiles)));
-    const rsx_status_t st = hip_status(launch_list_by_type(dtype, op, w, a, grid, stream));
+    const uint32_t lds = all_vec ? lds_for_cap(ar_cap(w)) : 0u;
+    const rsx_status_t st = hip_status(launch_list_by_type(dtype, op, w, a, grid, lds, stream));
     reset();
     return st;
   };
@@ -612,6 +641,7 @@ rsx_status_t rsx_fused_all_reduce(const void* const* sendtensors, void* const* r
       if (!in_place_all) a.ptr[ntens * slots + w + r] = rp;
       vec = vec && aligned16(sp) && aligned16(rp);
     }
+    all_vec = all_vec && vec;
     for (uint32_t k = k0; k <= k1; ++k) {
       ListPiece& pc = a.piece[a.npieces];
       const uint64_t slo = naive ? 0 : static_cast<uint64_t>(k) * seg;
@@ -799,5 +829,11 @@ const char* rsx_status_string(rsx_status_t status) {
 }
 
 int rsx_version(void) { return RSX_VERSION; }
+
+int rsx_set_occupancy_caps(int enable) {
+  const int prev = t_caps ? 1 : 0;
+  t_caps = enable != 0;
+  return prev;
+}
 
 }  // extern "C"

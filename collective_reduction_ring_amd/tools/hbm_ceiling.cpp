@@ -8,8 +8,9 @@
 // patterns bound the sparsified all-reduce: reading two
 // buffers and writing the second in place (its compaction and gather), and
 // writing each tile to 8 buffers (its combine).  Every pattern runs with
-// 256, 512 and 1024 lanes of one vector each and with 256 lanes of four;
-// the best is the ceiling.  Prints one JSON line: per pattern the best rate
+// 256, 512 and 1024 lanes of one vector each, with 256 lanes of four, and
+// with 256 lanes of one at 6, 5, 4, 3 and 2 workgroups per CU (LDS reserved
+// to cap them, as the library's launches do); the best is the ceiling.  Prints one JSON line: per pattern the best rate
 // and the configuration that reached it, and the rate with 256 lanes of one
 // vector.
 #include <hip/hip_runtime.h>
@@ -159,9 +160,10 @@ struct Best {
 template <int MODE, int LA, int SA>
 Best measure(const char* src, char* dst, float* sink, size_t bytes, double moved) {
   Best best;
-  auto one = [&](auto kernel, unsigned tile_bytes, unsigned block, const char* cfg) {
+  auto one = [&](auto kernel, unsigned tile_bytes, unsigned block, const char* cfg, unsigned wg_per_cu = 8) {
     const unsigned tiles = unsigned(bytes / tile_bytes) / (MODE >= 4 ? 8 : 1);  // a multiple of 8
-    const float ms = median_ms([&] { hipLaunchKernelGGL(kernel, dim3(tiles), dim3(block), 0, 0, src, dst, sink); });
+    const unsigned lds = wg_per_cu >= 8 ? 0u : (160u * 1024u / wg_per_cu) & ~1023u;
+    const float ms = median_ms([&] { hipLaunchKernelGGL(kernel, dim3(tiles), dim3(block), lds, 0, src, dst, sink); });
     CHECK(hipGetLastError());
     const double g = moved / (ms * 1e-3) / 1e9;
     if (best.first == 0) best.first = g;
@@ -174,6 +176,11 @@ Best measure(const char* src, char* dst, float* sink, size_t bytes, double moved
   one(stream_kernel<MODE, LA, SA, 512, 1>, 512 * 16, 512, "512x1");
   one(stream_kernel<MODE, LA, SA, 1024, 1>, 1024 * 16, 1024, "1024x1");
   one(stream_kernel<MODE, LA, SA, 256, 4>, 256 * 64, 256, "256x4");
+  one(stream_kernel<MODE, LA, SA, 256, 1>, 256 * 16, 256, "256x1, 6 WG/CU", 6);
+  one(stream_kernel<MODE, LA, SA, 256, 1>, 256 * 16, 256, "256x1, 5 WG/CU", 5);
+  one(stream_kernel<MODE, LA, SA, 256, 1>, 256 * 16, 256, "256x1, 4 WG/CU", 4);
+  one(stream_kernel<MODE, LA, SA, 256, 1>, 256 * 16, 256, "256x1, 3 WG/CU", 3);
+  one(stream_kernel<MODE, LA, SA, 256, 1>, 256 * 16, 256, "256x1, 2 WG/CU", 2);
   return best;
 }
 
@@ -206,8 +213,9 @@ int main() {
   const Best w8_nt = measure<4, 0, 2>(src, dst, sink, bytes, double(bytes));
   const Best r8w1 = measure<5, 2, 16>(src, dst, sink, bytes, bytes + bytes / 8.0);
   const Best r8w8 = measure<6, 2, 2>(src, dst, sink, bytes, 2.0 * bytes);  // last: it rewrites src
-  printf("{\"ceilings\": \"HBM streaming, 2 GiB buffers; per pattern the best of 256x1, 512x1, 1024x1 and "
-         "256x4 (lanes x 16-byte vectors per lane) and the rate at 256x1\", \"unit\": \"GB/s\"");
+  printf("{\"ceilings\": \"HBM streaming, 2 GiB buffers; per pattern the best of 256x1, 512x1, 1024x1, "
+         "256x4 (lanes x 16-byte vectors per lane) and 256x1 at 6..2 workgroups per CU, and the rate at "
+         "256x1 uncapped\", \"unit\": \"GB/s\"");
   auto put = [](const char* name, const Best& b) {
     printf(", \"%s\": {\"best\": %.1f, \"at\": \"%s\", \"256x1\": %.1f}", name, b.gbs, b.cfg, b.first);
   };

@@ -37,6 +37,10 @@
  *     without launching anything [NC host launcher].
  *   - Buffers of 16-byte-aligned address take the dwordx4 kernels; other
  *     alignments are correct but slower.
+ *   - The dwordx4 reduction and gather kernels reserve LDS they do not use
+ *     (up to 53 KiB per workgroup) to limit how many of their workgroups
+ *     share a CU, unless the calling thread turned that off with
+ *     rsx_set_occupancy_caps (for launches that overlap other kernels).
  */
 #ifndef RSX_H
 #define RSX_H
@@ -52,12 +56,6 @@ extern "C" {
 #define RSX_VERSION 110          /* 1.1.0 */
 #define RSX_MAX_RANKS 16         /* largest W a call accepts */
 #define RSX_NAIVE_MAX_BYTES 32768 /* RSX_ALGO_AUTO picks naive at or below this, per rank [MX] */
-/* RSX_ALGO_RING runs the all-reduce as two passes (reduce-scatter, then
- * all-gather) from this many ranks and bytes per rank on; in place, only up
- * to RSX_SPLIT_MAX_IN_PLACE_BYTES per rank (see rsx_all_reduce). */
-#define RSX_SPLIT_MIN_RANKS 4
-#define RSX_SPLIT_MIN_BYTES 4194304
-#define RSX_SPLIT_MAX_IN_PLACE_BYTES 268435456
 #define RSX_FUSE_BATCH 128       /* tensors per pack/unpack launch */
 
 typedef enum {
@@ -90,7 +88,7 @@ typedef enum {
   RSX_ALGO_RING = 0,       /* segment k folded in ring order (k+1)%W, ..., k; then gathered */
   RSX_ALGO_NAIVE = 1,      /* every element folded in rank order 0..W-1 [MX] */
   RSX_ALGO_AUTO = 2,       /* NAIVE when count * element size <= RSX_NAIVE_MAX_BYTES, else RING */
-  RSX_ALGO_RING_FUSED = 3, /* RING, always as one pass (fold, then store to every rank) */
+  RSX_ALGO_RING_FUSED = 3, /* RING as one pass (fold, then store to every rank); RING takes it too */
   RSX_ALGO_RING_SPLIT = 4  /* RING, always as a reduce-scatter, then an all-gather [DP] */
 } rsx_algo_t;
 
@@ -145,21 +143,15 @@ rsx_status_t rsx_all_gather(const void* const* sendbufs, void* const* recvbufs,
  *   S = ceil(count/W): segment k = [min(kS,count), min((k+1)S,count)), see
  *   rsx_segment_begin.  Segment k is folded in ring order (k+1)%W, ..., k and
  *   written to every rank: the result equals rsx_all_gather applied to the
- *   reduce-scatter output whenever W divides count.  It runs in one of two
- *   forms, with the same bits (the same folds in the same order):
- *   - one pass (RSX_ALGO_RING_FUSED): each lane folds its element of all W
- *     inputs in registers and stores the result to all W outputs;
+ *   reduce-scatter output whenever W divides count.  Two forms give the
+ *   same bits (the same folds in the same order):
+ *   - one pass (RSX_ALGO_RING, RSX_ALGO_RING_FUSED): each lane folds its
+ *     element of all W inputs in registers and stores the result to all W
+ *     outputs;
  *   - two passes (RSX_ALGO_RING_SPLIT): a reduce-scatter writes segment k
  *     into recvbufs[k] at its own offset, then an all-gather copies it from
- *     there to the other W-1 outputs.  That moves (2W+1)/(2W) of the bytes
- *     of one pass, yet runs faster on large buffers: each pass has fewer
- *     concurrent streams (W+1, then 1+(W-1)) than the single pass (2W).
- *   RSX_ALGO_RING takes two passes when W >= RSX_SPLIT_MIN_RANKS, W divides
- *   count, every buffer is 16-byte aligned, S * size is a multiple of 16,
- *   count * size >= RSX_SPLIT_MIN_BYTES and, in place, count * size <=
- *   RSX_SPLIT_MAX_IN_PLACE_BYTES; one pass otherwise.
- *   RSX_ALGO_RING_SPLIT needs W to divide count (else RSX_ERR_UNSUPPORTED)
- *   and takes any alignment.
+ *     there to the other W-1 outputs, (2W+1)/(2W) of the one-pass bytes.
+ *     W must divide count (else RSX_ERR_UNSUPPORTED); any alignment.
  * RSX_ALGO_NAIVE: every element folded in rank order 0..W-1 [MX].
  * In place: recvbufs[r] == sendbufs[r] for every r (or a permutation of the
  * send buffers) is allowed; other overlaps return RSX_ERR_ALIASING.
@@ -318,6 +310,19 @@ const char* rsx_status_string(rsx_status_t status);
 
 /* RSX_VERSION of the built library. */
 int rsx_version(void);
+
+/*
+ * Occupancy caps of the calling thread's launches; returns the previous
+ * setting (1 on, 0 off).  On by default: the dwordx4 reduction and gather
+ * kernels then reserve LDS they do not use, so that fewer of their
+ * workgroups share a CU, which keeps HBM busiest when a collective runs by
+ * itself (W = 8 reduce-scatter 378 -> 361 us, one-pass all-reduce
+ * 769 -> 735 us).  Reserved LDS also keeps other kernels off those CUs:
+ * turn the caps off for launches meant to overlap compute on another stream
+ * (bucketed all-reduce beside a matmul per bucket: 1,382 us with the caps,
+ * 1,132 us without).  Results are the same either way.  Host state only.
+ */
+int rsx_set_occupancy_caps(int enable);
 
 #ifdef __cplusplus
 }

@@ -71,9 +71,6 @@ def test_enum_and_macro_values_match_binding(lib):
         assert re.search(rf"\b{name}\s*=\s*{code}\b", text), name
     assert _header_int("RSX_MAX_RANKS") == L.RSX_MAX_RANKS
     assert _header_int("RSX_NAIVE_MAX_BYTES") == L.RSX_NAIVE_MAX_BYTES
-    assert _header_int("RSX_SPLIT_MIN_RANKS") == L.RSX_SPLIT_MIN_RANKS
-    assert _header_int("RSX_SPLIT_MIN_BYTES") == L.RSX_SPLIT_MIN_BYTES
-    assert _header_int("RSX_SPLIT_MAX_IN_PLACE_BYTES") == L.RSX_SPLIT_MAX_IN_PLACE_BYTES
     assert _header_int("RSX_FUSE_BATCH") == L.RSX_FUSE_BATCH
     assert lib.rsx_version() == _header_int("RSX_VERSION")
 
@@ -147,6 +144,19 @@ def test_bad_enums(lib):
     assert _ag(lib, s, r, 2, 4, dt=9) == 2
     # type is checked before op, as the page's dispatch switches on type first
     assert _rs(lib, s, r, 2, 4, dt=9, op=9) == 2
+
+
+def test_occupancy_caps_setting_is_per_thread(lib):
+    import threading
+    assert lib.rsx_set_occupancy_caps(0) == 1           # on by default
+    assert lib.rsx_set_occupancy_caps(5) == 0           # any nonzero value turns them on
+    assert lib.rsx_set_occupancy_caps(0) == 1
+    seen = []
+    th = threading.Thread(target=lambda: seen.append(lib.rsx_set_occupancy_caps(1)))
+    th.start()
+    th.join()
+    assert seen == [1]                                  # another thread still has its default
+    assert lib.rsx_set_occupancy_caps(1) == 0           # this thread's setting was kept
 
 
 @fake_ptrs

@@ -129,22 +129,36 @@ def test_all_reduce_two_pass_every_op(op, dtype):
         assert_parity(got[r], want[r], dtype, f"rank {r}")
 
 
-@pytest.mark.parametrize("w,dtype,count,in_place", [
-    (4, "f32", 1 << 20, False),          # exactly RSX_SPLIT_MIN_BYTES per rank: two passes
-    (4, "f32", (1 << 20) - 4, False),    # just below: one pass
-    (8, "bf16", 1 << 21, True),          # in place, 4 MiB: two passes
-    (16, "i32", (1 << 20) + 8, False),   # W does not divide count: one pass
-    (3, "f32", 3 << 20, False),          # fewer than RSX_SPLIT_MIN_RANKS: one pass
-    (8, "f32", (1 << 21) + 8, False),    # segments not whole vectors: one pass
+@pytest.mark.parametrize("w,dtype,count,in_place,algo", [
+    (4, "f32", 1 << 20, False, "ring"),
+    (4, "f32", 1 << 20, False, "ring_split"),
+    (8, "bf16", 1 << 21, True, "ring"),
+    (8, "bf16", 1 << 21, True, "ring_split"),
+    (16, "i32", (1 << 20) + 8, False, "ring"),    # W does not divide count
+    (3, "f32", 3 << 20, False, "ring_split"),
+    (11, "f32", 11 << 18, False, "ring_split"),
+    (2, "f32", 1 << 21, False, "ring_split"),
 ])
-def test_ring_around_the_two_pass_threshold(w, dtype, count, in_place):
-    # "ring" picks its form by shape; every choice gives the oracle's bits.
+@pytest.mark.parametrize("caps", [True, False])
+def test_large_grids_with_occupancy_caps(w, dtype, count, in_place, algo, caps):
+    # Grids of thousands of workgroups, far more than the capped number of
+    # resident workgroups per CU (the caps depend on W and the kernel), with
+    # the caps on and off: the all-reduce and, where W divides count, the
+    # reduce-scatter give the oracle's bits.
     xs = inputs(23, w, count, dtype)
-    say(f"ar ring by shape w={w} dtype={dtype} count={count} in_place={in_place}")
-    got = run_ar(xs, dtype, "sum", "ring", in_place)
+    say(f"large grid ar w={w} dtype={dtype} count={count} in_place={in_place} algo={algo} caps={caps}")
+    with rsx.occupancy_caps(caps):
+        got = run_ar(xs, dtype, "sum", algo, in_place)
     want = oracle.all_reduce(xs, "sum", dtype)
     for r in range(w):
         assert_parity(got[r], want[r], dtype, f"rank {r}")
+    if count % w == 0:
+        say(f"large grid rs w={w} dtype={dtype} recvcount={count // w} caps={caps}")
+        with rsx.occupancy_caps(caps):
+            got = run_rs(xs, dtype, "sum", count // w)
+        want = oracle.reduce_scatter(xs, "sum", dtype)
+        for k in range(w):
+            assert_parity(got[k], want[k], dtype, f"block {k}")
 
 
 def test_two_pass_with_outputs_a_permutation_of_the_inputs():
