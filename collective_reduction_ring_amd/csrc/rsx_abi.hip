@@ -5,7 +5,6 @@
 // effect and the error paths can be exercised on a machine without a GPU.
 #include <math.h>
 #include <stdio.h>
-#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -518,6 +517,9 @@ rsx_status_t rsx_all_reduce(const void* const* sendbufs, void* const* recvbufs, 
     a.seg = seg;
     a.rot = 1;
     const int vl = static_cast<int>(kVecBytes / es);
+    // The all-gather's grid has no more tiles than the reduce-scatter's (the
+    // same segments, in 16-byte units whenever the reduce-scatter's are), so
+    // its size check cannot fail after the reduce-scatter has launched.
     st = launch_fold_any(dtype, op, nranks, true, rs_vec, a, fold_tiles(seg, nranks, rs_vec, vl),
                          static_cast<uint32_t>(nranks), stream);
     if (st != RSX_SUCCESS) return st;
