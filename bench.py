@@ -397,7 +397,8 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
         ins_all = torch.randn(world * top, device="cuda:0", generator=gen) * 1e-3
         outs_all = torch.empty(world * top, device="cuda:0")
         res = {"workload": "reduce-scatter and ring all-reduce sum fp32 (one pass, and two passes for "
-                           "comparison; and an in-place avg all-reduce), W=8, per-rank size sweep; "
+                           "comparison; and an in-place avg all-reduce), all-gather of the W blocks, W=8, "
+                           "per-rank size sweep; "
                            "below 64 MiB graph-timed device time (50 calls per graph), above HIP events per call"}
         kib = 4
         while kib * 1024 <= 2 ** 30:
@@ -412,10 +413,15 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
             ar_in = rsx.AllReduce(ins, None, "avg", "ring")
             # the two-pass form (reduce-scatter, then all-gather), for comparison
             ar_two = rsx.AllReduce(ins, ar_out, "sum", "ring_split")
+            # all-gather of W blocks of n/W elements (taken from the input arena) into the
+            # W full-size outputs, out of place
+            ag_in = [ins_all[k * seg:(k + 1) * seg] for k in range(world)]
+            ag = lambda: rsx.all_gather(ag_in, ar_out)  # noqa: E731
             row = {}
             for what, fn, nbytes in (("reduce_scatter", rs, world * n * 4 + world * seg * 4),
                                      ("all_reduce", ar, 2 * world * n * 4),
                                      ("all_reduce_two_pass", ar_two, 2 * world * n * 4),
+                                     ("all_gather", ag, n * 4 + world * n * 4),
                                      ("all_reduce_in_place_avg", ar_in, 2 * world * n * 4)):
                 if kib * 1024 < 64 * 2 ** 20:
                     us = graph_us_per_call(fn, 50, 20, torch)

@@ -56,7 +56,11 @@ bool valid_op(int op) { return op >= RSX_SUM && op <= RSX_PROD; }
 // 805 -> 725-732 us, all-gather 426 -> 380-383 us):
 //   reduce-scatter (W+1 streams per workgroup): 8 at W <= 2, 5 up to W = 10, 3 above;
 //   all-reduce, one pass (2W streams): 8 at W = 1, 5 at W = 2, 3 from W = 3;
-//   all-gather (1 + W): 8 at W <= 2, 6 at W = 4, 6, 8, otherwise 5 up to W = 9, 3 above.
+//   all-gather, every piece in place (1 + (W-1)): 8 at W <= 2, 6 at W = 4, 6, 8,
+//     otherwise 5 up to W = 9, 3 above;
+//   all-gather, out of place (1 + W): 5 up to W = 5, 3 above (W = 2 164 -> 130 us,
+//     W = 8 498 -> 459 us);
+//   tensor-list all-reduce: 5 up to W = 4 (C5-like lists: 182 -> 177 us), 3 above.
 // The element-wise kernels (unaligned buffers) run best uncapped: they keep
 // less in flight per lane.
 // The caps are per calling thread (rsx_set_occupancy_caps): launches meant to
@@ -68,11 +72,13 @@ uint32_t lds_for_cap(uint32_t wg_per_cu) {
 }
 uint32_t rs_cap(int w) { return w <= 2 ? 8u : w <= 10 ? 5u : 3u; }
 uint32_t ar_cap(int w) { return w <= 1 ? 8u : w == 2 ? 5u : 3u; }
-uint32_t ag_cap(int w) {
+uint32_t ag_cap(int w, bool in_place) {
+  if (!in_place) return w <= 5 ? 5u : 3u;
   if (w <= 2) return 8u;
   if (w == 4 || w == 6 || w == 8) return 6u;
   return w <= 9 ? 5u : 3u;
 }
+uint32_t list_cap(int w) { return w <= 1 ? 8u : w <= 4 ? 5u : 3u; }
 
 // Per element type launchers (one translation unit each).
 hipError_t launch_fold_by_type(int dtype, int op, int world, bool rs, bool vec, const FoldArgs& a,
@@ -189,7 +195,11 @@ rsx_status_t launch_gather_any(const void* const* src, void* const* dst, int nra
                                size_t es, hipStream_t stream) {
   const size_t piece_bytes = n * es;
   bool vec = (piece_bytes % kVecBytes) == 0;
-  for (int r = 0; r < nranks; ++r) vec = vec && aligned16(src[r]) && aligned16(dst[r]);
+  bool in_place = true;
+  for (int r = 0; r < nranks; ++r) {
+    vec = vec && aligned16(src[r]) && aligned16(dst[r]);
+    in_place = in_place && src[r] == static_cast<const char*>(dst[r]) + static_cast<size_t>(r) * piece_bytes;
+  }
   GatherArgs a;
   memset(&a, 0, sizeof(a));
   for (int r = 0; r < nranks; ++r) {
@@ -208,7 +218,7 @@ rsx_status_t launch_gather_any(const void* const* src, void* const* dst, int nra
   split_magic(a.tiles_per_piece, &a.tps_magic, &a.tps_shift);
   return hip_status(launch_gather(static_cast<int>(es), vec, a,
                                   dim3(static_cast<uint32_t>(xcd_grid(total))),
-                                  vec ? lds_for_cap(ag_cap(nranks)) : 0u, stream));
+                                  vec ? lds_for_cap(ag_cap(nranks, in_place)) : 0u, stream));
 }
 
 // Shared validation of the pointer arrays and enums of the collectives.
@@ -618,7 +628,7 @@ rsx_status_t rsx_fused_all_reduce(const void* const* sendtensors, void* const* r
     if (a.npieces == 0) return RSX_SUCCESS;
     a.tile_start[a.npieces] = static_cast<uint32_t>(tiles);
     const dim3 grid(static_cast<uint32_t>(xcd_grid(tiles)));
-    const uint32_t lds = all_vec ? lds_for_cap(ar_cap(w)) : 0u;
+    const uint32_t lds = all_vec ? lds_for_cap(list_cap(w)) : 0u;
     const rsx_status_t st = hip_status(launch_list_by_type(dtype, op, w, a, grid, lds, stream));
     reset();
     return st;
