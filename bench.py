@@ -73,6 +73,50 @@ def cpu_baseline(xs, reps_budget_s: float):
     return out, statistics.median(times), len(times)
 
 
+def cpu_baseline_threaded(xs, reps_budget_s: float):
+    """The same oracle, with each segment's fold cut into per-thread ranges and
+    run in a thread pool (NumPy releases the GIL in its ufuncs).  Every element
+    is still the oracle's fold of that element, in ring order."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    w = len(xs)
+    s = len(xs[0]) // w
+    step = -(-s // threads)
+    tasks = [(k, lo, min(lo + step, (k + 1) * s)) for k in range(w) for lo in range(k * s, (k + 1) * s, step)]
+
+    def one(t):
+        k, lo, hi = t
+        return oracle.fold(xs, oracle.ring_fold_order(k, w), "sum", "f32", lo, hi)
+
+    times, out = [], None
+    t_start = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        while True:
+            t0 = time.perf_counter()
+            parts = list(ex.map(one, tasks))
+            out = [np.concatenate([p for (k, _, _), p in zip(tasks, parts) if k == kk]) for kk in range(w)]
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_start >= reps_budget_s or len(times) >= 500:
+                break
+    return out, statistics.median(times), len(times), threads
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def calibrate_copy(rsx, torch) -> int:
     """Plain copy of 1 GiB (one-rank all-gather), 20 launches: counter calibration."""
     nbytes = 1 << 30
@@ -608,7 +652,16 @@ def main() -> int:
             "kind": "oracle",
             "sample": f"the whole workload (one reduce-scatter of 8 x 67,108,864 fp32), "
                       f"{reps} passes, median {t_med:.2f} s; single-threaded NumPy",
+            "cpu_model": cpu_model(),
         }
+        log("oracle baseline on the host, threaded")
+        want_t, t_thr, reps_t, threads = cpu_baseline_threaded(xs, max(2.0, args.cpu_seconds / 3))
+        same_t = all(np.array_equal(a.view(np.uint32), b.view(np.uint32)) for a, b in zip(want_t, want))
+        result["cpu_baseline"]["threaded"] = {
+            "value": round(bytes_per_step / t_thr / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "sample": f"the same workload, each segment's fold split over {threads} threads, "
+                      f"{reps_t} passes, median {t_thr:.3f} s; bit-identical to the single-threaded "
+                      f"oracle: {same_t}"}
         bad = sum(int(np.count_nonzero(g.view(np.uint32) != o.view(np.uint32)))
                   for g, o in zip(got, want))
         result["parity"] = {"checked_elements": int(sum(g.size for g in got)),
