@@ -509,9 +509,10 @@ rsx_status_t rsx_all_reduce(const void* const* sendbufs, void* const* recvbufs, 
   // every input before it stores, and touches no other segment, so every
   // alias the one-pass form accepts is still safe; the all-gather runs after
   // the last read of the inputs, in stream order.  With the occupancy caps
-  // the one-pass form is as fast or faster at every measured W and size
-  // (W = 8, 256 MiB per rank: 725-732 against 745-754 us), so RSX_ALGO_RING
-  // takes it.
+  // the two forms are within a few percent of each other as whole calls
+  // (W = 8 fp32, 256 MiB per rank: 734 against 729 us; W = 4: one pass up
+  // to 9% ahead; W = 16 at 256 MiB: two passes 4% ahead), so RSX_ALGO_RING
+  // takes the one-pass form, which moves the fewest bytes.
   if (algo == RSX_ALGO_RING_SPLIT) {
     const size_t seg = count / static_cast<size_t>(nranks);
     const bool rs_vec = vec && (seg * es) % kVecBytes == 0;

@@ -319,8 +319,8 @@ int rsx_version(void);
  * itself (W = 8 reduce-scatter 378 -> 361 us, one-pass all-reduce
  * 769 -> 735 us).  Reserved LDS also keeps other kernels off those CUs:
  * turn the caps off for launches meant to overlap compute on another stream
- * (bucketed all-reduce beside a matmul per bucket: 1,382 us with the caps,
- * 1,132 us without).  Results are the same either way.  Host state only.
+ * (bucketed all-reduce beside a matmul per bucket: 1,371 us with the caps,
+ * 1,185 us without).  Results are the same either way.  Host state only.
  */
 int rsx_set_occupancy_caps(int enable);
 
