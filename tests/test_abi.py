@@ -425,3 +425,20 @@ def test_sparse_aliasing(lib):
     assert _sp(lib, g, a, o, 2, n, mi=[A + 3 * MB, A + 42 * MB]) == 5     # message over an output
     assert _sp(lib, g, a, o, 2, n, ws=A + 41 * MB) == 5                   # workspace over a message
     assert _sp(lib, g, a, o, 2, n, nnz=A + 8) == 5                        # nnz inside a gradient
+
+
+def test_occupancy_caps_context_manager_restores_the_setting(lib):
+    import collective_reduction_ring_amd as rsx
+    assert lib.rsx_set_occupancy_caps(1) in (0, 1)      # start from "on"
+    with rsx.occupancy_caps(False):
+        assert lib.rsx_set_occupancy_caps(0) == 0        # off inside
+        with rsx.occupancy_caps(True):
+            assert lib.rsx_set_occupancy_caps(1) == 1    # on in the nested block
+        assert lib.rsx_set_occupancy_caps(0) == 0        # off again after it
+    assert lib.rsx_set_occupancy_caps(1) == 1            # on after the outer block
+    try:
+        with rsx.occupancy_caps(False):
+            raise RuntimeError("inside")
+    except RuntimeError:
+        pass
+    assert lib.rsx_set_occupancy_caps(1) == 1            # restored on an exception too
