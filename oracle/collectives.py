@@ -40,7 +40,7 @@ widened exactly to fp32, folded in fp32 and rounded once to bf16 at the end
 (bf16 in, fp32 accumulate, bf16 out); fp16 (the page's ``half``) is read the
 same way.
 
-Readings where the pages are silent (each listed again in the design doc):
+Readings where the pages are silent:
 
 * ring = identity (``userFromRing[i] = i``): rank ``r`` is ring position ``r``;
 * the segment of a rank that does not divide evenly in an all-reduce is the
