@@ -164,6 +164,20 @@ def time_from_state(fn, reset, reps: int, warmup: int, torch) -> list:
     return [a.elapsed_time(b) for a, b in zip(st, en)]
 
 
+def capture(fn, torch):
+    """`fn` captured once in a HIP graph (after warm-up calls on a side stream)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
 def graph_us_per_call(fn, inner: int, reps: int, torch) -> float:
     """Device time per call: `inner` calls captured in one HIP graph, replayed
     `reps` times; the median replay divided by `inner`."""
@@ -339,6 +353,10 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
             nnz = plan.nnz_host()
             st = _stat(ms, world * n * 16 + 16 * sum(nnz))
             st.update(k=plan.k, nnz_rank0=nnz[0], nnz_total=sum(nnz), params=kw)
+            # the whole call captured in one HIP graph (its ~15 launches replayed at once)
+            graph = capture(plan, torch)
+            ms_g = time_from_state(graph.replay, reset, reps, warm, torch)
+            st["graph_replay_median_us"] = round(statistics.median(ms_g) * 1e3, 2)
             res[mode] = st
         return res
     if name == "sparse_sweep":
