@@ -3,8 +3,8 @@
 // same cache hints as the library's kernels.  These bound what a
 // reduce-scatter (mostly reads) and an all-reduce (as many writes as reads)
 // can reach; reading 8 buffers into a sum written to a ninth, or to all 8
-// (in place), are the reduce-scatter's and the all-reduce's own patterns at
-// W = 8 without the ring order.  Two more
+// (in place) or to 8 other buffers, are the reduce-scatter's and the
+// all-reduce's own patterns at W = 8 without the ring order.  Two more
 // patterns bound the sparsified all-reduce: reading two
 // buffers and writing the second in place (its compaction and gather), and
 // writing each tile to 8 buffers (its combine).  Every pattern runs with
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(B) void stream_kernel(const char* src, char* dst, f
 #pragma unroll
     for (int u = 0; u < kUnits; ++u) v[u] += __builtin_amdgcn_raw_buffer_load_b128(r, voff, u * kBlock * 16, LOAD_AUX);
   }
-  if (MODE == 5 || MODE == 6) {
+  if (MODE == 5 || MODE == 6 || MODE == 7) {
     const size_t part = size_t(gridDim.x) * kTileBytes;
     u32x4 w[8][kUnits];
 #pragma unroll
@@ -87,7 +87,9 @@ __global__ __launch_bounds__(B) void stream_kernel(const char* src, char* dst, f
     } else {
 #pragma unroll
       for (int b = 0; b < 8; ++b) {
-        const __amdgpu_buffer_rsrc_t d = rsrc<kTileBytes>(const_cast<char*>(src) + b * part + off);
+        // MODE 6 writes back over the 8 sources; MODE 7 to 8 separate buffers
+        char* const base = MODE == 6 ? const_cast<char*>(src) : dst;
+        const __amdgpu_buffer_rsrc_t d = rsrc<kTileBytes>(base + b * part + off);
 #pragma unroll
         for (int u = 0; u < kUnits; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], d, voff, u * kBlock * 16, STORE_AUX);
       }
@@ -212,6 +214,7 @@ int main() {
   const Best w8_plain = measure<4, 0, 0>(src, dst, sink, bytes, double(bytes));
   const Best w8_nt = measure<4, 0, 2>(src, dst, sink, bytes, double(bytes));
   const Best r8w1 = measure<5, 2, 16>(src, dst, sink, bytes, bytes + bytes / 8.0);
+  const Best r8w8o = measure<7, 2, 2>(src, dst, sink, bytes, 2.0 * bytes);
   const Best r8w8 = measure<6, 2, 2>(src, dst, sink, bytes, 2.0 * bytes);  // last: it rewrites src
   printf("{\"ceilings\": \"HBM streaming, 2 GiB buffers; per pattern the best of 256x1, 512x1, 1024x1, "
          "256x4 (lanes x 16-byte vectors per lane) and 256x1 at 6..2 workgroups per CU, and the rate at "
@@ -230,6 +233,7 @@ int main() {
   put("write_8_buffers_nt", w8_nt);
   put("read_8_sum_write_1", r8w1);
   put("read_8_sum_write_8_in_place", r8w8);
+  put("read_8_sum_write_8_other_buffers", r8w8o);
   put("read_nt_zeroed_buffer", r_nt_zero);
   printf("}\n");
   CHECK(hipFree(src));
