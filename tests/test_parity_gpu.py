@@ -497,6 +497,31 @@ def test_all_gather_in_place_and_composition():
         assert_parity(to_host(dev[r], "f32"), want[r], "f32", f"rank {r}")
 
 
+@pytest.mark.parametrize("w", [2, 3, 4, 5, 8, 12, 16])
+@pytest.mark.parametrize("in_place", [False, True])
+@pytest.mark.parametrize("caps", [True, False])
+def test_all_gather_large_grids(w, in_place, caps):
+    # Pieces of 512 Ki + 4 fp32 (a ragged last tile), thousands of workgroups:
+    # every occupancy cap the all-gather uses (in place and out of place,
+    # W = 2..16), and none.
+    n = (1 << 19) + 4
+    pieces = inputs(9, w, n, "f32")
+    out = [empty(w * n, "f32", fill=0x11) for _ in range(w)]
+    if in_place:
+        for k in range(w):
+            out[k][k * n:(k + 1) * n].copy_(to_dev(pieces[k], "f32"))
+        src = [out[k][k * n:(k + 1) * n] for k in range(w)]
+    else:
+        src = [to_dev(p, "f32") for p in pieces]
+    say(f"ag large grid w={w} in_place={in_place} caps={caps}")
+    with rsx.occupancy_caps(caps):
+        rsx.all_gather(src, out)
+    torch.cuda.synchronize()
+    want = oracle.all_gather(pieces)
+    for r in range(w):
+        assert_parity(to_host(out[r], "f32"), want[r], "f32", f"rank {r}")
+
+
 # --------------------------------------------------------------- fusion -----
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f64", "i8", "f16", "f32h"])
