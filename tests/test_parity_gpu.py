@@ -161,6 +161,24 @@ def test_large_grids_with_occupancy_caps(w, dtype, count, in_place, algo, caps):
             assert_parity(got[k], want[k], dtype, f"block {k}")
 
 
+@pytest.mark.parametrize("w,dtype,extra", [(3, "f32", 1), (8, "f32", 3), (16, "f32", 2), (8, "bf16", 5),
+                                           (5, "i8", 11), (8, "f64", 1), (2, "f16", 7), (8, "i32", 2)])
+@pytest.mark.parametrize("caps", [True, False])
+def test_reduce_scatter_blocks_of_partial_vectors(w, dtype, extra, caps):
+    # Block length a whole number of vectors plus `extra` elements, on
+    # 16-byte-aligned buffers: every block but the first starts mid-vector in
+    # the sources (the element-wise kernel), the last reaches the end of
+    # them; thousands of workgroups.
+    recvcount = (1 << 17) + extra
+    xs = inputs(27, w, w * recvcount, dtype)
+    say(f"rs partial-vector blocks w={w} dtype={dtype} recvcount={recvcount} caps={caps}")
+    with rsx.occupancy_caps(caps):
+        got = run_rs(xs, dtype, "sum", recvcount)
+    want = oracle.reduce_scatter(xs, "sum", dtype)
+    for k in range(w):
+        assert_parity(got[k], want[k], dtype, f"block {k}")
+
+
 def test_two_pass_with_outputs_a_permutation_of_the_inputs():
     # recvbufs[r] == sendbufs[(r + 1) % W]: the reduce-scatter overwrites a
     # segment of another rank's input only in the lanes that already read it.
