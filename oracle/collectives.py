@@ -32,13 +32,16 @@ Sources (web pages this follows):
   (``half2float``) into the fp32 tensors: fp16 as the wire format of an fp32
   all-reduce (dtype ``"f32h"`` here).
 
-Precision.  The pages fix it: the NCCL kernel reduces in the element type
-(``FuncSum<float>`` on ``float`` data), so fp32 and fp64 are folded with IEEE
-round-to-nearest-even operations in their own type, one per ring step, and
-int8 / int32 / int64 / uint64 with wrapping integer arithmetic.  bf16 data is
-widened exactly to fp32, folded in fp32 and rounded once to bf16 at the end
-(bf16 in, fp32 accumulate, bf16 out); fp16 (the page's ``half``) is read the
-same way.
+Precision.  The pages fix it: the NCCL kernel reduces in the element type.
+Its ring buffers (``ThisBuffer`` / ``NextBuffer`` of
+``ReduceScatterKernelArgs<T>``) hold ``T``, and every step from 1 on reduces
+the partial it received with its own input into one of them, so the partial
+is stored as ``T`` after every step.  Hence fp32, fp64 and fp16 (the page's
+``half``) are folded with IEEE round-to-nearest-even operations in their own
+type, one per ring step, and int8 / int32 / int64 / uint64 with wrapping
+integer arithmetic.  bf16 is not on the page's type list; its workload defines
+it as bf16 in, fp32 accumulate, bf16 out: widened exactly to fp32, folded in
+fp32 and rounded once to bf16 at the end.
 
 Readings where the pages are silent:
 
@@ -52,11 +55,14 @@ Readings where the pages are silent:
   (IEEE division for floats; signed integers truncate toward zero, uint64
   floors);
 * ``prod`` multiplies in the accumulation type (integers wrap);
-* fp16 (the page's ``half``, whose functor is off-page) folds in fp32 and is
-  rounded once, like bf16;
+* fp16 (the page's ``half``; its functors are off-page): each step's result
+  is the exact result of the operation rounded to nearest-even half (NumPy's
+  float16 arithmetic), so a half partial enters the next step; ``avg``
+  divides the half fold by W and rounds the quotient to half; the naive fold
+  rounds the same way, in rank order;
 * ``"f32h"`` (fp32 data, half on the wire): each fp32 input is rounded to
-  half and widened back, the half values are folded as fp16 is, and the half
-  result is widened to fp32 for the output;
+  half (``float2half``), the halves are folded as fp16 is, and the half
+  result is widened to fp32 for the output (``half2float``);
 * bf16 rounding: round-to-nearest-even on the fp32 bits, NaN -> quiet NaN
   with the sign kept (``sign | 0x7FC0``), overflow to +-inf as RNE gives;
 * the naive all-reduce folds in rank order 0..W-1;
@@ -154,18 +160,20 @@ def f16_to_f32(bits: np.ndarray) -> np.ndarray:
 
 def f32_to_f16(x: np.ndarray) -> np.ndarray:
     """Round fp32 to IEEE half bit patterns, to nearest, ties to even (NumPy's conversion)."""
-    return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+    with np.errstate(over="ignore"):    # beyond the half range is +-inf, as RNE gives
+        return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
 
 
 def _widen(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Storage -> accumulation type: bf16 and f16 bits -> fp32; fp32 through half
-    (``"f32h"``: ``float2half`` on the sender) -> fp32; every other type as is."""
+    """Storage -> accumulation type: bf16 bits -> fp32; f16 bits -> float16 values
+    (the ring partial stays half); fp32 -> half for ``"f32h"`` (``float2half`` on
+    the sender); every other type as is."""
     if dtype == "bf16":
         return bf16_to_f32(x)
     if dtype == "f16":
-        return f16_to_f32(x)
+        return np.asarray(x, dtype=np.uint16).view(np.float16)
     if dtype == "f32h":
-        return f16_to_f32(f32_to_f16(x))
+        return np.asarray(x, dtype=np.float32).astype(np.float16)
     if dtype in STORAGE:
         return np.asarray(x, dtype=STORAGE[dtype])
     raise ValueError(dtype)
@@ -204,10 +212,10 @@ def _finish(op: str, acc: np.ndarray, world: int, dtype: str) -> np.ndarray:
             acc = (acc / acc.dtype.type(world)).astype(acc.dtype)
     if dtype == "bf16":
         return f32_to_bf16(acc)
-    if dtype == "f16":
-        return f32_to_f16(acc)
+    if dtype == "f16":                      # the half result, as bits
+        return np.ascontiguousarray(acc, dtype=np.float16).view(np.uint16)
     if dtype == "f32h":                     # the half result, then half2float
-        return f16_to_f32(f32_to_f16(acc))
+        return np.asarray(acc, dtype=np.float16).astype(np.float32)
     return acc
 
 
@@ -216,10 +224,12 @@ def fold(inputs, order, op: str, dtype: str, lo: int = 0, hi: int | None = None)
     if op not in OPS:
         raise ValueError(f"op {op!r}")
     hi = len(inputs[0]) if hi is None else hi
-    acc = _widen(inputs[order[0]][lo:hi], dtype).copy()
-    for r in order[1:]:
-        acc = _combine(op, acc, _widen(inputs[r][lo:hi], dtype))
-    return _finish(op, acc, len(inputs), dtype)
+    # overflow to +-inf and inf - inf = NaN are the IEEE results, not errors
+    with np.errstate(over="ignore", invalid="ignore"):
+        acc = _widen(inputs[order[0]][lo:hi], dtype).copy()
+        for r in order[1:]:
+            acc = _combine(op, acc, _widen(inputs[r][lo:hi], dtype))
+        return _finish(op, acc, len(inputs), dtype)
 
 
 # ------------------------------------------------------------ collectives ----

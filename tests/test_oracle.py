@@ -470,19 +470,171 @@ def test_f16_rounding_hand_ties_and_torch_cast():
     assert np.array_equal(oracle.f16_to_f32(want), torch.from_numpy(want.view(np.int16)).view(torch.float16).float().numpy())
 
 
-def test_f16_accumulates_in_fp32():
-    # rank order: 1 + 2^-11 + 2^-11 = 1 + 2^-10 exactly in fp32 -> half 0x3C01;
-    # rounding each partial to half would give 1.0 (1 + 2^-11 ties to 1.0)
-    xs = [np.array([0x3C00], np.uint16), np.array([0x1000], np.uint16), np.array([0x1000], np.uint16)]
-    assert oracle.f16_to_f32(np.array([0x1000], np.uint16))[0] == 2.0 ** -11
-    assert oracle.naive_all_reduce(xs, "sum", "f16")[0][0] == 0x3C01
+H1, H_EPS = 0x3C00, 0x1000          # half 1.0 and 2^-11
+
+
+def _h(*bits):
+    return np.array(bits, dtype=np.uint16)
+
+
+def test_f16_partial_rounded_to_half_after_every_ring_step():
+    # W = 3, one element per block; block 0 is folded in ring order 1, 2, 0.
+    # x1 = 1, x2 = x0 = 2^-11: 1 + 2^-11 is a half tie and goes to the even 1.0
+    # at step 1 and again at step 2 -> 0x3C00.  An fp32 partial rounded once
+    # at the end would give 1 + 2^-10 = 0x3C01.
+    assert oracle.f16_to_f32(_h(H_EPS))[0] == 2.0 ** -11
+    xs = [_h(H_EPS, 0, 0), _h(H1, 0, 0), _h(H_EPS, 0, 0)]
+    assert oracle.reduce_scatter(xs, "sum", "f16")[0][0] == 0x3C00
+    assert oracle.all_reduce(xs, "sum", "f16")[1][0] == 0x3C00
+    # naive (rank order 0, 1, 2): 2^-11 + 1 -> 1.0, then + 2^-11 -> 1.0
+    assert oracle.naive_all_reduce(xs, "sum", "f16")[2][0] == 0x3C00
+
+
+def test_f16_ring_order_probe():
+    # W = 4, segment 0, (x0..x3) = (1, 2048, 1, -2048).  Half spacing at 2048
+    # is 2.  Ring order 1, 2, 3, 0: 2048 + 1 ties to 2048, - 2048 = 0, + 1 = 1.
+    # Rank order: 1 + 2048 -> 2048, + 1 -> 2048, - 2048 = 0.  (In exact or
+    # fp32 arithmetic both orders give 1.)
+    vals = [0x3C00, 0x6800, 0x3C00, 0xE800]       # 1, 2048, 1, -2048
+    xs = [_h(v, 0, 0, 0) for v in vals]
+    assert oracle.reduce_scatter(xs, "sum", "f16")[0][0] == 0x3C00
+    assert oracle.naive_all_reduce(xs, "sum", "f16")[0][0] == 0x0000
+
+
+def test_f16_overflow_inside_the_fold_sticks():
+    # 65504 + 16 = 65520 lies halfway between 65504 (odd significand) and 2^16,
+    # which is beyond the format: it rounds to +inf, and inf - 65504 stays inf.
+    # fp32 accumulation would give 16.
+    xs = [_h(0x7BFF), _h(0x4C00), _h(0xFBFF)]      # 65504, 16, -65504
+    assert oracle.naive_all_reduce(xs, "sum", "f16")[0][0] == 0x7C00
+    # prod: 256 * 256 = 65536 overflows to inf; inf * 2^-8 = inf (exact: 256)
+    xs = [_h(0x5C00), _h(0x5C00), _h(0x1C00)]      # 256, 256, 2^-8
+    assert oracle.naive_all_reduce(xs, "prod", "f16")[0][0] == 0x7C00
+
+
+def test_f16_avg_divides_the_half_fold():
+    # half fold of (1, 2^-11, 2^-11) in rank order is 1.0; 1/3 rounded to half:
+    # spacing 2^-12 in [1/4, 1/2), 4096/3 = 1365.33 -> 1365 * 2^-12 = 0x3555.
+    # The fp32 fold 1 + 2^-10 divided by 3 would round to 1367 * 2^-12 = 0x3557.
+    xs = [_h(H1), _h(H_EPS), _h(H_EPS)]
+    assert oracle.naive_all_reduce(xs, "avg", "f16")[0][0] == 0x3555
+
+
+def _half_exact(bits):
+    """Exact rational value of a finite IEEE half bit pattern."""
+    from fractions import Fraction
+    sign = -1 if bits & 0x8000 else 1
+    e, m = (bits >> 10) & 0x1F, bits & 0x3FF
+    mag = Fraction(m, 2 ** 24) if e == 0 else Fraction(1024 + m, 1024) * Fraction(2) ** (e - 15)
+    return sign * mag
+
+
+def _round_half(q):
+    """Round an exact rational to IEEE binary16 by the definition: nearest value
+    on the grid of the operand's binade (subnormal spacing 2^-24 below 2^-14),
+    ties to the even significand, +-inf once the rounded magnitude reaches 2^16.
+    Returns a float (every half is exactly a Python float)."""
+    from fractions import Fraction
+    if q == 0:
+        return 0.0
+    neg, a = q < 0, abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, -14)
+    ulp = Fraction(2) ** (e - 10)
+    n, rem = divmod(a, ulp)
+    n = int(n)
+    rem = rem / ulp
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    val = n * ulp
+    out = float("inf") if val >= 2 ** 16 else float(val)
+    return -out if neg else out
+
+
+def _random_finite_halves(rng, n):
+    """Finite, nonzero halves spread over the whole range, with many ties."""
+    mags = rng.choice([1e-6, 1e-3, 1.0, 30.0, 2000.0, 30000.0], n)
+    with np.errstate(over="ignore"):
+        x = (rng.standard_normal(n) * mags).astype(np.float16)
+    x[x == 0] = np.float16(1.0)
+    x[~np.isfinite(x)] = np.float16(-3.0)
+    return x.view(np.uint16)
+
+
+@pytest.mark.parametrize("w", [1, 2, 3, 4])
+@pytest.mark.parametrize("op", ["sum", "prod", "max", "min", "avg"])
+def test_f16_brute_force_exact_rationals(w, op):
+    # Every ring step in exact rational arithmetic, rounded to half by the
+    # definition above; block k is folded from rank (k+1) mod W round to k.
+    rng = np.random.default_rng(300 + 7 * w + len(op))
+    s = 16
+    xs = [_random_finite_halves(rng, w * s) for _ in range(w)]
+    got = np.concatenate(oracle.reduce_scatter(xs, op, "f16")).view(np.float16).astype(np.float64)
+    from fractions import Fraction
+    for k in range(w):
+        for i in range(s):
+            e = k * s + i
+            acc = None
+            for j in range(w):
+                v = float(_half_exact(int(xs[(k + 1 + j) % w][e])))
+                if acc is None:
+                    acc = v
+                elif op == "sum" or op == "avg":
+                    acc = acc + v if np.isinf(acc) else _round_half(Fraction(acc) + Fraction(v))
+                elif op == "prod":
+                    acc = acc * v if np.isinf(acc) else _round_half(Fraction(acc) * Fraction(v))
+                elif op == "max":
+                    acc = v if v > acc else acc
+                else:
+                    acc = v if v < acc else acc
+            if op == "avg" and np.isfinite(acc):
+                acc = _round_half(Fraction(acc) / w)
+            elif op == "avg":
+                acc = acc / w
+            g = got[e]
+            assert (np.isnan(g) and np.isnan(acc)) or g == acc, (op, w, k, i, g, acc)
+
+
+@pytest.mark.parametrize("op", ["sum", "prod"])
+def test_f16_fold_matches_torch_cpu_half_arithmetic(op):
+    # PyTorch's CPU half add / multiply (a library routine, correctly rounded to
+    # half per operation), applied in ring order segment by segment.
+    rng = np.random.default_rng(17)
+    w, s = 5, 4000
+    xs = [(rng.standard_normal(w * s) * (30 if op == "sum" else 1.5)).astype(np.float16).view(np.uint16)
+          for _ in range(w)]
+    got = np.concatenate(oracle.reduce_scatter(xs, op, "f16"))
+    th = [torch.from_numpy(x.view(np.int16)).view(torch.float16) for x in xs]
+    want = []
+    for k in range(w):
+        acc = th[(k + 1) % w][k * s:(k + 1) * s].clone()
+        for j in range(1, w):
+            x = th[(k + 1 + j) % w][k * s:(k + 1) * s]
+            acc = acc + x if op == "sum" else acc * x
+        want.append(acc.view(torch.int16).numpy().view(np.uint16))
+    want = np.concatenate(want)
+    same = (got == want) | (np.isnan(got.view(np.float16)) & np.isnan(want.view(np.float16)))
+    assert same.all()
+    # and it is not the fp32-accumulated result on this data
+    acc32 = [np.sum(np.stack([oracle.f16_to_f32(x[k * s:(k + 1) * s]) for x in xs]), 0) for k in range(w)]
+    assert op == "prod" or not np.array_equal(got, oracle.f32_to_f16(np.concatenate(acc32)))
+
+
+def test_half_wire_partial_is_half_at_every_step():
+    f = np.float32
+    # 1, 2^-11, 2^-11 are exact halves; the half fold in rank order gives 1.0
+    # (each 1 + 2^-11 ties to 1.0); an fp32 fold rounded once would give 1 + 2^-10.
+    xs = [np.array([1.0], f), np.array([2 ** -11], f), np.array([2 ** -11], f)]
+    assert oracle.naive_all_reduce(xs, "sum", "f32h")[0][0] == f(1.0)
 
 
 def test_half_wire_rounds_inputs_and_result_to_half():
     f = np.float32
     # inputs: 1 + 2^-11 is a half tie and goes to 1.0 before the fold; 2^-11 and
-    # 3 are exact halves.  fp32 fold in rank order: 1 + 2^-11 + 3 = 4 + 2^-11,
-    # which rounds to 4.0 in half (spacing 2^-8 near 4); the output is fp32 4.0.
+    # 3 are exact halves.  Half fold in rank order: 1 + 2^-11 ties to 1.0, and
+    # 1 + 3 = 4; the output is fp32 4.0.
     xs = [np.array([1 + 2 ** -11], f), np.array([2 ** -11], f), np.array([3.0], f)]
     out = oracle.naive_all_reduce(xs, "sum", "f32h")
     assert out[0].dtype == np.float32 and out[0][0] == f(4.0)
@@ -500,7 +652,7 @@ def test_half_wire_rounds_inputs_and_result_to_half():
 
 @pytest.mark.parametrize("op", ["sum", "max", "avg"])
 def test_half_wire_small_integers_exact(op):
-    # small integers are exact in half and in the fp32 fold
+    # small integers (|sum| <= 800) are exact in half at every step
     rng = np.random.default_rng(15)
     xi = [rng.integers(-200, 200, 48) for _ in range(4)]
     got = oracle.all_reduce([x.astype(np.float32) for x in xi], op, "f32h")[0]
