@@ -7,6 +7,7 @@ Run as ``python -m collective_reduction_ring_amd.build`` or call ``build()``.
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -33,7 +34,9 @@ CFLAGS = [
     "-Wno-unused-function",
     # correctly rounded fp32 division (the avg op divides by W once)
     "-fhip-fp32-correctly-rounded-divide-sqrt",
-    # no packed-fp32 instructions (v_pk_*_f32) in generated code
+    # Turns off packed-fp32 instructions (v_pk_add/mul/fma_f32) in the gfx950
+    # code.  The host pass prints "not a recognized feature" and ignores it;
+    # the device pass honours it.  check_no_packed_fp32 verifies the result.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
@@ -46,11 +49,25 @@ def sources() -> list[str]:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    # -save-temps=obj keeps the gfx950 assembly next to the object
+    cmd = [HIPCC, *CFLAGS, "-save-temps=obj", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
+
+
+PACKED_FP32 = re.compile(r"\bv_pk_(add|mul|fma)_f32\b")
+
+
+def check_no_packed_fp32(objs: list[str]) -> None:
+    """Raise if the gfx950 assembly of any object holds a packed-fp32 instruction."""
+    for obj in objs:
+        asm = obj[:-2] + f"-hip-amdgcn-amd-amdhsa-{ARCH}.s"
+        with open(asm) as f:
+            for n, line in enumerate(f, 1):
+                if PACKED_FP32.search(line.split(";")[0]):
+                    raise RuntimeError(f"packed-fp32 instruction in {asm}:{n}: {line.strip()}")
 
 
 def build(verbose: bool = True, jobs: int | None = None) -> str:
@@ -60,6 +77,7 @@ def build(verbose: bool = True, jobs: int | None = None) -> str:
     jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, srcs))
+    check_no_packed_fp32(objs)
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -50,7 +50,7 @@ struct F64T {
 };
 struct F16T {
   using S = uint16_t;  // IEEE half bit patterns
-  using A = float;
+  using A = _Float16;  // the ring partial stays half (the page's T-typed ring buffers)
   static constexpr int kVL = 8;
 };
 struct I64T {
@@ -72,7 +72,7 @@ struct I8T {
 // synchHalf / fusedSynchHalf: float2half, a half all-reduce, half2float).
 struct F32HT {
   using S = float;
-  using A = float;
+  using A = _Float16;
   static constexpr int kVL = 4;
 };
 
@@ -170,21 +170,16 @@ struct Elem<I64T> : Elem64<int64_t> {};
 template <>
 struct Elem<U64T> : Elem64<uint64_t> {};
 
-// IEEE half: widened exactly to fp32 and narrowed with round-to-nearest-even
-// (the hardware conversions, which implement both).
+// IEEE half, folded in half: every combine is one native half operation
+// (v_add_f16 / v_mul_f16, IEEE and correctly rounded, denormals kept), so the
+// partial is a half after every ring step, as it is in the NCCL ring, whose
+// buffers between steps hold the element type (ReduceScatterKernelArgs<T>,
+// ThisBuffer / NextBuffer).
 template <>
 struct Elem<F16T> {
-  __device__ static float widen(uint16_t h) { return static_cast<float>(__builtin_bit_cast(_Float16, h)); }
-  // The fold's fp32 result is rounded to half once, by itself.  The empty asm
-  // pins `a` as an fp32 register value: without it the compiler fuses the
-  // last fp32 add or multiply with this conversion into one mixed-precision
-  // FMA that rounds the exact result straight to half, which differs from
-  // fp32-then-half rounding whenever the fp32 value lands on a half tie.
-  __device__ static uint16_t narrow(float a) {
-    asm volatile("" : "+v"(a));
-    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(a));
-  }
-  __device__ static void unpack(const uint4& v, float (&a)[8]) {
+  __device__ static _Float16 widen(uint16_t h) { return __builtin_bit_cast(_Float16, h); }
+  __device__ static uint16_t narrow(_Float16 a) { return __builtin_bit_cast(uint16_t, a); }
+  __device__ static void unpack(const uint4& v, _Float16 (&a)[8]) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -192,7 +187,7 @@ struct Elem<F16T> {
       a[2 * i + 1] = widen(static_cast<uint16_t>(w[i] >> 16));
     }
   }
-  __device__ static uint4 pack(const float (&a)[8]) {
+  __device__ static uint4 pack(const _Float16 (&a)[8]) {
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = narrow(a[2 * i]) | (static_cast<uint32_t>(narrow(a[2 * i + 1])) << 16);
@@ -201,25 +196,20 @@ struct Elem<F16T> {
 };
 
 // fp32 through half: every input is rounded to half (round to nearest even)
-// and widened back before it enters the fold, as the sender's float2half
-// does; the fold is the fp16 one (fp32 arithmetic, rounded once); the result
-// is rounded to half and widened for the fp32 output, as half2float does.
+// as the sender's float2half does, the halves are folded in half as the fp16
+// type is, and the half result is widened exactly for the fp32 output, as
+// half2float does.
 template <>
 struct Elem<F32HT> {
-  __device__ static float widen(float x) { return static_cast<float>(static_cast<_Float16>(x)); }
-  // The same barrier as the fp16 narrow: the fp32 fold result is rounded on
-  // its own, never merged with the last add or multiply into a mixed FMA.
-  __device__ static float narrow(float a) {
-    asm volatile("" : "+v"(a));
-    return static_cast<float>(static_cast<_Float16>(a));
-  }
-  __device__ static void unpack(const uint4& v, float (&a)[4]) {
+  __device__ static _Float16 widen(float x) { return static_cast<_Float16>(x); }
+  __device__ static float narrow(_Float16 a) { return static_cast<float>(a); }
+  __device__ static void unpack(const uint4& v, _Float16 (&a)[4]) {
     a[0] = widen(__uint_as_float(v.x));
     a[1] = widen(__uint_as_float(v.y));
     a[2] = widen(__uint_as_float(v.z));
     a[3] = widen(__uint_as_float(v.w));
   }
-  __device__ static uint4 pack(const float (&a)[4]) {
+  __device__ static uint4 pack(const _Float16 (&a)[4]) {
     return make_uint4(__float_as_uint(narrow(a[0])), __float_as_uint(narrow(a[1])),
                       __float_as_uint(narrow(a[2])), __float_as_uint(narrow(a[3])));
   }
@@ -268,8 +258,11 @@ struct Unsigned<uint64_t> {
 };
 
 template <class A>
+inline constexpr bool kIsFloat = std::is_floating_point<A>::value || std::is_same<A, _Float16>::value;
+
+template <class A>
 __device__ __forceinline__ A add_op(A a, A b) {
-  if constexpr (std::is_floating_point<A>::value) {
+  if constexpr (kIsFloat<A>) {
     return a + b;
   } else {
     using U = typename Unsigned<A>::T;
@@ -279,7 +272,7 @@ __device__ __forceinline__ A add_op(A a, A b) {
 
 template <class A>
 __device__ __forceinline__ A mul_op(A a, A b) {
-  if constexpr (std::is_floating_point<A>::value) {
+  if constexpr (kIsFloat<A>) {
     return a * b;
   } else {
     using U = typename Unsigned<A>::T;
@@ -305,10 +298,18 @@ __device__ __forceinline__ A combine(A acc, A x) {
 }
 
 // avg: one division by W in the accumulation type (IEEE for floats; C
-// integer division: toward zero for signed types, floor for uint64).
+// integer division: toward zero for signed types, floor for uint64).  A half
+// fold is divided in fp32 (correctly rounded here) and converted: fp32 holds
+// 24 >= 2 * 11 + 2 significand bits, so the quotient rounded to fp32 and
+// then to half equals the correctly rounded half quotient.  The empty asm
+// keeps the quotient a plain fp32 value before the conversion.
 template <int OP, int W, class A>
 __device__ __forceinline__ A finish(A acc) {
-  if constexpr (OP == RSX_AVG) {
+  if constexpr (OP == RSX_AVG && std::is_same<A, _Float16>::value) {
+    float q = static_cast<float>(acc) / static_cast<float>(W);
+    asm volatile("" : "+v"(q));
+    return static_cast<_Float16>(q);
+  } else if constexpr (OP == RSX_AVG) {
     return static_cast<A>(acc / static_cast<A>(W));
   } else {
     return acc;

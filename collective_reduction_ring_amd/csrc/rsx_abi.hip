@@ -230,9 +230,16 @@ rsx_status_t check_common(const void* const* sendbufs, void* const* recvbufs, in
   return RSX_SUCCESS;
 }
 
-rsx_status_t check_device_ptrs(const void* const* sendbufs, void* const* recvbufs, int nranks) {
-  for (int r = 0; r < nranks; ++r)
+// Every element access of the kernels is naturally aligned: a buffer must
+// start at a multiple of its element size (es is a power of two).
+bool elem_aligned(const void* p, size_t es) { return (reinterpret_cast<uintptr_t>(p) & (es - 1)) == 0; }
+
+rsx_status_t check_device_ptrs(const void* const* sendbufs, void* const* recvbufs, int nranks,
+                               size_t es) {
+  for (int r = 0; r < nranks; ++r) {
     if (sendbufs[r] == nullptr || recvbufs[r] == nullptr) return RSX_ERR_INVALID_ARGUMENT;
+    if (!elem_aligned(sendbufs[r], es) || !elem_aligned(recvbufs[r], es)) return RSX_ERR_INVALID_ARGUMENT;
+  }
   return RSX_SUCCESS;
 }
 
@@ -249,9 +256,9 @@ rsx_status_t fuse_copy(const void* const* tens, const size_t* counts, int ntenso
     total += b;
   }
   if (total == 0) return RSX_SUCCESS;
-  if (tens == nullptr || fused == nullptr) return RSX_ERR_INVALID_ARGUMENT;
+  if (tens == nullptr || fused == nullptr || !elem_aligned(fused, es)) return RSX_ERR_INVALID_ARGUMENT;
   for (int i = 0; i < ntensors; ++i)
-    if (counts[i] != 0 && tens[i] == nullptr) return RSX_ERR_INVALID_ARGUMENT;
+    if (counts[i] != 0 && (tens[i] == nullptr || !elem_aligned(tens[i], es))) return RSX_ERR_INVALID_ARGUMENT;
   const Range fr = range_of(fused, total);
   if (wraps(fr)) return RSX_ERR_INVALID_ARGUMENT;
   for (int i = 0; i < ntensors; ++i) {
@@ -391,7 +398,7 @@ rsx_status_t rsx_reduce_scatter(const void* const* sendbufs, void* const* recvbu
   if (st != RSX_SUCCESS) return st;
   if (!valid_op(op)) return RSX_ERR_INVALID_OP;
   if (recvcount == 0) return RSX_SUCCESS;
-  if ((st = check_device_ptrs(sendbufs, recvbufs, nranks)) != RSX_SUCCESS) return st;
+  if ((st = check_device_ptrs(sendbufs, recvbufs, nranks, esize_of(dtype))) != RSX_SUCCESS) return st;
   const size_t es = esize_of(dtype);
   size_t n, seg_bytes, in_bytes;
   if (!mul_ok(recvcount, static_cast<size_t>(nranks), &n) || !mul_ok(recvcount, es, &seg_bytes) ||
@@ -440,7 +447,7 @@ rsx_status_t rsx_all_gather(const void* const* sendbufs, void* const* recvbufs, 
   // A gather reduces nothing: the half wire format applies to reductions only.
   if (dtype == RSX_FLOAT32_HALF_WIRE) return RSX_ERR_INVALID_TYPE;
   if (sendcount == 0) return RSX_SUCCESS;
-  if ((st = check_device_ptrs(sendbufs, recvbufs, nranks)) != RSX_SUCCESS) return st;
+  if ((st = check_device_ptrs(sendbufs, recvbufs, nranks, esize_of(dtype))) != RSX_SUCCESS) return st;
   const size_t es = esize_of(dtype);
   size_t piece_bytes, out_bytes;
   if (!mul_ok(sendcount, es, &piece_bytes) ||
@@ -476,7 +483,7 @@ rsx_status_t rsx_all_reduce(const void* const* sendbufs, void* const* recvbufs, 
       algo != RSX_ALGO_RING_FUSED && algo != RSX_ALGO_RING_SPLIT)
     return RSX_ERR_INVALID_ARGUMENT;
   if (count == 0) return RSX_SUCCESS;
-  if ((st = check_device_ptrs(sendbufs, recvbufs, nranks)) != RSX_SUCCESS) return st;
+  if ((st = check_device_ptrs(sendbufs, recvbufs, nranks, esize_of(dtype))) != RSX_SUCCESS) return st;
   const size_t es = esize_of(dtype);
   size_t bytes;
   if (!mul_ok(count, es, &bytes)) return RSX_ERR_UNSUPPORTED;
@@ -596,6 +603,7 @@ rsx_status_t rsx_fused_all_reduce(const void* const* sendtensors, void* const* r
       const void* sp = sendtensors[static_cast<size_t>(r) * ntensors + i];
       const void* rp = recvtensors[static_cast<size_t>(r) * ntensors + i];
       if (sp == nullptr || rp == nullptr) return RSX_ERR_INVALID_ARGUMENT;
+      if (!elem_aligned(sp, es) || !elem_aligned(rp, es)) return RSX_ERR_INVALID_ARGUMENT;
       const Range sr = range_of(sp, counts[i] * es), rr = range_of(rp, counts[i] * es);
       if (wraps(sr) || wraps(rr)) return RSX_ERR_INVALID_ARGUMENT;
       sends.push_back({sr.lo, sr.hi, i});

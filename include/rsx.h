@@ -35,8 +35,13 @@
  *     rsx_status_string(RSX_ERR_HIP) then names the HIP error (per thread).
  *   - Counts are elements, not bytes.  A count of 0 returns RSX_SUCCESS
  *     without launching anything [NC host launcher].
- *   - Buffers of 16-byte-aligned address take the dwordx4 kernels; other
- *     alignments are correct but slower.
+ *   - Every buffer must start at a multiple of its element size (4 for
+ *     fp32, 2 for bf16, ...); any other address returns
+ *     RSX_ERR_INVALID_ARGUMENT.  Buffers of 16-byte-aligned address take the
+ *     dwordx4 kernels; other element-aligned addresses are correct but slower.
+ *   - Bit-exact means equal bit patterns, except that NaN payloads are not
+ *     specified: where the result is a NaN, any NaN is correct (the pages fix
+ *     no NaN propagation rule; bf16 rounding quiets a NaN as sign|0x7FC0).
  *   - The dwordx4 reduction and gather kernels reserve LDS they do not use
  *     (up to 53 KiB per workgroup) to limit how many of their workgroups
  *     share a CU, unless the calling thread turned that off with
@@ -63,15 +68,18 @@ typedef enum {
   RSX_BFLOAT16 = 1,  /* bf16 in, widened exactly to fp32, fp32 fold, one RNE rounding to bf16 out */
   RSX_INT32 = 2,     /* int32, two's-complement wrapping sum and product */
   RSX_FLOAT64 = 3,   /* fp64 in, fp64 fold, fp64 out */
-  RSX_FLOAT16 = 4,   /* IEEE half in, widened exactly to fp32, fp32 fold, one RNE rounding out */
+  RSX_FLOAT16 = 4,   /* IEEE half in and out, folded in half: the ring partial is rounded (RNE)
+                        to half after every step, as the page's T-typed ring buffers hold it
+                        [NC ReduceScatterKernelArgs<T>, ThisBuffer / NextBuffer]; avg divides
+                        the half fold by W, the quotient rounded to half */
   RSX_INT64 = 5,     /* int64, wrapping */
   RSX_UINT64 = 6,    /* uint64, wrapping */
   RSX_INT8 = 7,      /* int8 (the page's char), wrapping */
   RSX_FLOAT32_HALF_WIRE = 8 /* fp32 in and out with IEEE half as the wire format
                                [Apache SINGA communicator.cc, synchHalf / fusedSynchHalf]:
-                               each input is rounded (RNE) to half and widened back, the
-                               halves are folded as RSX_FLOAT16 is (fp32, one rounding), and
-                               the half result is widened to fp32.  Reductions only:
+                               each input is rounded (RNE) to half, the halves are folded
+                               as RSX_FLOAT16 is (half partial at every ring step), and the
+                               half result is widened to fp32.  Reductions only:
                                rsx_all_gather rejects it with RSX_ERR_INVALID_TYPE; pack and
                                unpack treat it as fp32.  W = 1 still rounds through half. */
 } rsx_dtype_t;
@@ -94,7 +102,7 @@ typedef enum {
 
 typedef enum {
   RSX_SUCCESS = 0,
-  RSX_ERR_INVALID_ARGUMENT = 1, /* null pointer, rank count out of [1, RSX_MAX_RANKS], bad algo */
+  RSX_ERR_INVALID_ARGUMENT = 1, /* null or misaligned pointer, rank count out of [1, RSX_MAX_RANKS], bad algo */
   RSX_ERR_INVALID_TYPE = 2,     /* dtype outside rsx_dtype_t [NC: invalid type] */
   RSX_ERR_INVALID_OP = 3,       /* op outside rsx_op_t [NC: invalid operation] */
   RSX_ERR_UNSUPPORTED = 4,      /* sizes whose byte count or launch grid overflows */
@@ -151,7 +159,7 @@ rsx_status_t rsx_all_gather(const void* const* sendbufs, void* const* recvbufs,
  *   - two passes (RSX_ALGO_RING_SPLIT): a reduce-scatter writes segment k
  *     into recvbufs[k] at its own offset, then an all-gather copies it from
  *     there to the other W-1 outputs, (2W+1)/(2W) of the one-pass bytes.
- *     W must divide count (else RSX_ERR_UNSUPPORTED); any alignment.
+ *     W must divide count (else RSX_ERR_UNSUPPORTED); any element-aligned address.
  * RSX_ALGO_NAIVE: every element folded in rank order 0..W-1 [MX].
  * In place: recvbufs[r] == sendbufs[r] for every r (or a permutation of the
  * send buffers) is allowed; other overlaps return RSX_ERR_ALIASING.

@@ -185,6 +185,35 @@ def test_null_device_pointer(lib):
 
 
 @fake_ptrs
+def test_pointers_must_be_element_aligned(lib):
+    # A buffer that does not start at a multiple of its element size is refused
+    # before any HIP call (the kernels' element accesses are naturally aligned).
+    s, r = [A, A + MB], [A + 2 * MB, A + 3 * MB]
+    for i, dt, es in [(0, L.RSX_FLOAT32, 4), (1, L.RSX_BFLOAT16, 2), (2, L.RSX_FLOAT64, 8),
+                      (3, L.RSX_INT64, 8), (4, L.RSX_FLOAT16, 2), (5, L.RSX_INT32, 4)]:
+        for off in range(1, es):
+            bad_s = list(s)
+            bad_s[i % 2] += off
+            bad_r = list(r)
+            bad_r[(i + 1) % 2] += off
+            assert _rs(lib, bad_s, r, 2, 64, dt=dt) == 1, (dt, off)
+            assert _rs(lib, s, bad_r, 2, 64, dt=dt) == 1, (dt, off)
+            assert _ar(lib, bad_s, r, 2, 64, dt=dt) == 1, (dt, off)
+            assert _ar(lib, s, bad_r, 2, 64, dt=dt, algo=L.RSX_ALGO_NAIVE) == 1, (dt, off)
+            assert _ag(lib, bad_s, r, 2, 64, dt=dt) == 1, (dt, off)
+            counts = L.size_array([10, 7])
+            assert lib.rsx_fuse_pack(_arr(bad_s), counts, 2, A + 8 * MB, dt, None) == 1
+            assert lib.rsx_fuse_pack(_arr(s), counts, 2, A + 8 * MB + off, dt, None) == 1
+            assert lib.rsx_fuse_unpack(A + 8 * MB + off, _arr(r), counts, 2, dt, None) == 1
+            assert lib.rsx_fuse_unpack(A + 8 * MB, _arr(bad_r), counts, 2, dt, None) == 1
+            assert _far(lib, bad_s + [A + 4 * MB, A + 5 * MB], r + [A + 6 * MB, A + 7 * MB],
+                        [10, 7], 2, dt=dt) == 1, (dt, off)
+    # int8 has no alignment requirement; such a call gets past the check (to the
+    # aliasing rule here, which it breaks on purpose so that nothing launches)
+    assert _rs(lib, [A + 1, A + 1 + MB], [A + 1, A + 2], 2, 64, dt=L.RSX_INT8) == 5
+
+
+@fake_ptrs
 def test_single_rank_in_place_is_a_no_op(lib):
     assert _rs(lib, [A], [A], 1, 100) == 0
     assert _ar(lib, [A], [A], 1, 100) == 0

@@ -757,9 +757,9 @@ def test_full_c4_int32(op):
     dev = [to_dev(x, "i32") for x in xs]
     rsx.all_reduce(dev, None, op, "ring")
     torch.cuda.synchronize()
-    # sampled ranks only: every rank receives the same result
     want = oracle.all_reduce(xs, op, "i32")
-    for r in (0, 7, w.world - 1):
+    # every rank, one host copy at a time (each rank's output has its own stores)
+    for r in range(w.world):
         assert_parity(to_host(dev[r], "i32"), want[r], "i32", f"ar rank {r}")
 
 
@@ -772,11 +772,11 @@ def test_full_c3_bf16_bucketed_avg():
     say("full cfg=3: 11 bucketed all-reduces")
     rsx.all_reduce_bucketed(dev, out, w.extra["bucket_elems"], "avg")
     torch.cuda.synchronize()
-    got = [to_host(out[r], "bf16") for r in (0, 3, 7)]
-    del dev, out
+    del dev
     say("full cfg=3: oracle")
     want = oracle.bucketed_all_reduce(xs, w.extra["bucket_elems"], "avg", "bf16")
-    stats = [assert_parity(g, want[r], "bf16", f"rank {r}") for g, r in zip(got, (0, 3, 7))]
+    # every rank, one host copy at a time
+    stats = [assert_parity(to_host(out[r], "bf16"), want[r], "bf16", f"rank {r}") for r in range(w.world)]
     say(f"bf16 exact fraction {stats[0]['exact'] / stats[0]['n']:.6f}")
 
 
