@@ -51,6 +51,8 @@ SIGNATURES = {
     "rsx_sparse_workspace_size": (_SZ, [_I, _SZ, _I, _I]),
     "rsx_sparse_all_reduce": (_I, [_PP, _PP, _PP, _I, _SZ, _I, ctypes.c_float, _SZ, _PP, _PP, _SZ,
                                    _P, _P, _SZ, _P]),
+    "rsx_sparse_all_reduce_noalloc": (_I, [_PP, _PP, _PP, _I, _SZ, _I, ctypes.c_float, _SZ, _PP, _PP,
+                                           _SZ, _P, _P]),
     "rsx_segment_begin": (_SZ, [_SZ, _I, _I]),
     "rsx_dtype_size": (_SZ, [_I]),
     "rsx_status_string": (ctypes.c_char_p, [_I]),

@@ -453,11 +453,14 @@ class SparseAllReduce:
     ``topk_count(count, fraction)``).  After a call, rank r's message is
     ``msg_idx[r][:n]`` / ``msg_val[r][:n]`` with ``n = nnz_host()[r]``.
     The message buffers, the lengths and the workspace are allocated here,
-    once, by PyTorch; calls allocate nothing.
+    once, by PyTorch; calls allocate nothing.  ``noalloc=True`` allocates no
+    workspace and calls ``rsx_sparse_all_reduce_noalloc``, which uses the
+    library's per-GPU scratch array (calls on one GPU must not overlap).
     """
 
     def __init__(self, grads, accums=None, outs=None, mode: str = "threshold",
-                 threshold: float = 0.0, k: int | None = None, fraction: float | None = None):
+                 threshold: float = 0.0, k: int | None = None, fraction: float | None = None,
+                 noalloc: bool = False):
         w = _ranks(grads)
         count = grads[0].numel()
         dev = grads[0].device
@@ -491,20 +494,25 @@ class SparseAllReduce:
         ws = lib.rsx_sparse_workspace_size(w, count, SPARSE_MODES[mode], int(accums is not None))
         if ws == 0:
             raise ValueError("rsx_sparse_workspace_size rejected the sizes")
-        self._ws = torch.empty(ws + 256, dtype=torch.uint8, device=dev)
-        ws_ptr = self._ws.data_ptr() + (-self._ws.data_ptr()) % 256
         self.args = (L.ptr_array([t.data_ptr() for t in grads]),
                      L.ptr_array([t.data_ptr() for t in accums]) if accums is not None else None,
                      L.ptr_array([t.data_ptr() for t in outs]),
                      w, count, SPARSE_MODES[mode], float(threshold), k,
                      L.ptr_array([t.data_ptr() for t in self.msg_idx]),
                      L.ptr_array([t.data_ptr() for t in self.msg_val]),
-                     cap, self.nnz.data_ptr(), ws_ptr, ws)
-        self.fn = lib.rsx_sparse_all_reduce
+                     cap, self.nnz.data_ptr())
+        if noalloc:
+            self._ws = None
+            self.name = "rsx_sparse_all_reduce_noalloc"
+        else:
+            self._ws = torch.empty(ws + 256, dtype=torch.uint8, device=dev)
+            self.args += (self._ws.data_ptr() + (-self._ws.data_ptr()) % 256, ws)
+            self.name = "rsx_sparse_all_reduce"
+        self.fn = getattr(lib, self.name)
         self.keep = (list(grads), accums, list(outs))
 
     def __call__(self, stream=None) -> None:
-        _launch(self, "rsx_sparse_all_reduce", stream)
+        _launch(self, self.name, stream)
 
     def nnz_host(self) -> list[int]:
         """Message lengths (synchronises with the device)."""
@@ -517,9 +525,10 @@ class SparseAllReduce:
 
 
 def sparse_all_reduce(grads, accums=None, outs=None, mode: str = "threshold", threshold: float = 0.0,
-                      k: int | None = None, fraction: float | None = None, stream=None) -> SparseAllReduce:
+                      k: int | None = None, fraction: float | None = None, stream=None,
+                      noalloc: bool = False) -> SparseAllReduce:
     """One sparsified all-reduce; returns the plan, whose buffers hold the messages."""
-    p = SparseAllReduce(grads, accums, outs, mode, threshold, k, fraction)
+    p = SparseAllReduce(grads, accums, outs, mode, threshold, k, fraction, noalloc)
     p(stream)
     return p
 

@@ -8,10 +8,18 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "rsx_internal.h"
 #include "sparse_internal.h"
+
+// The allocation-free sparsified all-reduce's workspace: one array per GPU,
+// held until the process ends, shared by every such call on that GPU.  In
+// host code `scratch` names a host-side stand-in, not the device memory: the
+// device address comes from hipGetSymbolAddress, once per device (with that
+// device current), and only that address is passed on.
+static __device__ __align__(256) unsigned char scratch[RSX_SPARSE_SCRATCH_BYTES];
 
 namespace rsx {
 namespace {
@@ -384,6 +392,131 @@ bool sparse_layout(int w, size_t count, int mode, bool accum, SparseLayout* l) {
   return true;
 }
 
+// Validation of a sparsified all-reduce, shared by both entry points; no HIP
+// call.  own_scratch: the library's scratch array takes the place of the
+// caller's workspace (no caller buffer can overlap it; its size is checked
+// by the entry point).
+rsx_status_t sparse_check(const float* const* grads, float* const* accums, float* const* outs,
+                          int nranks, size_t count, rsx_sparse_mode_t mode, size_t k,
+                          uint32_t* const* msg_idx, float* const* msg_val, size_t msg_capacity,
+                          uint32_t* nnz, const void* workspace, size_t workspace_bytes,
+                          bool own_scratch, SparseLayout* l) {
+  if (grads == nullptr || outs == nullptr || msg_idx == nullptr || msg_val == nullptr)
+    return RSX_ERR_INVALID_ARGUMENT;
+  if (nranks < 1 || nranks > RSX_MAX_RANKS) return RSX_ERR_INVALID_ARGUMENT;
+  if (mode != RSX_SPARSE_THRESHOLD && mode != RSX_SPARSE_TOPK) return RSX_ERR_INVALID_ARGUMENT;
+  if (count > UINT32_MAX) return RSX_ERR_UNSUPPORTED;
+  if (mode == RSX_SPARSE_TOPK && k > count) return RSX_ERR_INVALID_ARGUMENT;
+  if (nnz == nullptr || !aligned4(nnz)) return RSX_ERR_INVALID_ARGUMENT;
+  const Range nr = range_of(nnz, static_cast<size_t>(nranks) * 4);
+  if (wraps(nr)) return RSX_ERR_INVALID_ARGUMENT;
+  if (count == 0) return RSX_SUCCESS;
+
+  const bool has_acc = accums != nullptr;
+  const size_t sent_max = mode == RSX_SPARSE_THRESHOLD ? count : k;
+  if (msg_capacity < sent_max) return RSX_ERR_INVALID_ARGUMENT;
+  sparse_layout(nranks, count, mode, has_acc, l);
+  if (!own_scratch && (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & (kWsAlign - 1)) != 0 ||
+                       workspace_bytes < l->total))
+    return RSX_ERR_INVALID_ARGUMENT;
+  const size_t bytes = count * 4;
+  for (int r = 0; r < nranks; ++r) {
+    if (grads[r] == nullptr || outs[r] == nullptr || msg_idx[r] == nullptr || msg_val[r] == nullptr ||
+        (has_acc && accums[r] == nullptr))
+      return RSX_ERR_INVALID_ARGUMENT;
+    if (!aligned16(grads[r]) || !aligned16(outs[r]) || (has_acc && !aligned16(accums[r])) ||
+        !aligned4(msg_idx[r]) || !aligned4(msg_val[r]))
+      return RSX_ERR_INVALID_ARGUMENT;
+  }
+  // Everything written must be pairwise disjoint and apart from the
+  // gradients, except the outputs: they are written after every read of the
+  // gradients, so they may overlap them (in place: outs[r] == grads[r]).
+  std::vector<Range> writes, outs_r;
+  Range grads_r[RSX_MAX_RANKS];
+  for (int r = 0; r < nranks; ++r) {
+    grads_r[r] = range_of(grads[r], bytes);
+    outs_r.push_back(range_of(outs[r], bytes));
+    writes.push_back(outs_r.back());
+    if (has_acc) writes.push_back(range_of(accums[r], bytes));
+    writes.push_back(range_of(msg_idx[r], sent_max * 4));
+    writes.push_back(range_of(msg_val[r], sent_max * 4));
+    if (wraps(grads_r[r])) return RSX_ERR_INVALID_ARGUMENT;
+  }
+  writes.push_back(nr);
+  if (!own_scratch) writes.push_back(range_of(workspace, l->total));
+  for (const Range& w : writes)
+    if (wraps(w)) return RSX_ERR_INVALID_ARGUMENT;
+  if (!pairwise_disjoint(writes.data(), static_cast<int>(writes.size()))) return RSX_ERR_ALIASING;
+  for (const Range& w : writes) {
+    bool is_out = false;
+    for (const Range& o : outs_r) is_out = is_out || same(o, w);
+    if (is_out) continue;
+    for (int r = 0; r < nranks; ++r)
+      if (overlap(w, grads_r[r])) return RSX_ERR_ALIASING;
+  }
+  return RSX_SUCCESS;
+}
+
+// Kernel arguments of a checked sparsified all-reduce over the workspace `ws`
+// (laid out by `l`), and the launches.
+rsx_status_t sparse_launch(const float* const* grads, float* const* accums, float* const* outs,
+                           int nranks, size_t count, rsx_sparse_mode_t mode, float threshold,
+                           size_t k, uint32_t* const* msg_idx, float* const* msg_val,
+                           size_t msg_capacity, uint32_t* nnz, void* ws_base,
+                           const SparseLayout& l, hipStream_t stream) {
+  (void)msg_capacity;
+  const bool has_acc = accums != nullptr;
+  const size_t sent_max = mode == RSX_SPARSE_THRESHOLD ? count : k;
+  SparseArgs a;
+  memset(&a, 0, sizeof(a));
+  char* ws = static_cast<char*>(ws_base);
+  for (int r = 0; r < nranks; ++r) {
+    a.grad[r] = grads[r];
+    a.accum[r] = has_acc ? accums[r] : nullptr;
+    a.out[r] = outs[r];
+    a.msg_idx[r] = msg_idx[r];
+    a.msg_val[r] = msg_val[r];
+  }
+  a.nnz = nnz;
+  a.tile_slot = reinterpret_cast<uint32_t*>(ws + l.tile_slot);
+  a.tile_cnt = reinterpret_cast<uint32_t*>(ws + l.tile_cnt);
+  a.tile_eqc = reinterpret_cast<uint32_t*>(ws + l.tile_eqc);
+  a.tile_off = reinterpret_cast<uint32_t*>(ws + l.tile_off);
+  a.tile_eqb = reinterpret_cast<uint32_t*>(ws + l.tile_eqb);
+  a.gap_idx = reinterpret_cast<uint32_t*>(ws + l.gap_idx);
+  a.gap_val = reinterpret_cast<float*>(ws + l.gap_val);
+  a.hist = reinterpret_cast<uint32_t*>(ws + l.hist);
+  a.state = reinterpret_cast<uint32_t*>(ws + l.state);
+  a.count = count;
+  a.tiles = l.tiles;
+  a.world = static_cast<uint32_t>(nranks);
+  a.k = mode == RSX_SPARSE_TOPK ? static_cast<uint32_t>(k) : 0u;
+  a.cap = static_cast<uint32_t>(sent_max);
+  a.threshold = threshold;
+  return hip_status(launch_sparse(a, mode, has_acc, stream));
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+rsx_status_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return RSX_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (p == nullptr) return RSX_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RSX_SUCCESS;
+}
+
 }  // namespace
 }  // namespace rsx
 
@@ -734,88 +867,30 @@ rsx_status_t rsx_sparse_all_reduce(const float* const* grads, float* const* accu
                                    uint32_t* const* msg_idx, float* const* msg_val,
                                    size_t msg_capacity, uint32_t* nnz, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream) {
-  if (grads == nullptr || outs == nullptr || msg_idx == nullptr || msg_val == nullptr)
-    return RSX_ERR_INVALID_ARGUMENT;
-  if (nranks < 1 || nranks > RSX_MAX_RANKS) return RSX_ERR_INVALID_ARGUMENT;
-  if (mode != RSX_SPARSE_THRESHOLD && mode != RSX_SPARSE_TOPK) return RSX_ERR_INVALID_ARGUMENT;
-  if (count > UINT32_MAX) return RSX_ERR_UNSUPPORTED;
-  if (mode == RSX_SPARSE_TOPK && k > count) return RSX_ERR_INVALID_ARGUMENT;
-  if (nnz == nullptr || !aligned4(nnz)) return RSX_ERR_INVALID_ARGUMENT;
-  const Range nr = range_of(nnz, static_cast<size_t>(nranks) * 4);
-  if (wraps(nr)) return RSX_ERR_INVALID_ARGUMENT;
-  if (count == 0) return hip_status(launch_sparse_zero_nnz(nnz, nranks, stream));
-
-  const bool has_acc = accums != nullptr;
-  const size_t sent_max = mode == RSX_SPARSE_THRESHOLD ? count : k;
-  if (msg_capacity < sent_max) return RSX_ERR_INVALID_ARGUMENT;
   SparseLayout l;
-  sparse_layout(nranks, count, mode, has_acc, &l);
-  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & (kWsAlign - 1)) != 0 ||
-      workspace_bytes < l.total)
-    return RSX_ERR_INVALID_ARGUMENT;
-  const size_t bytes = count * 4;
-  for (int r = 0; r < nranks; ++r) {
-    if (grads[r] == nullptr || outs[r] == nullptr || msg_idx[r] == nullptr || msg_val[r] == nullptr ||
-        (has_acc && accums[r] == nullptr))
-      return RSX_ERR_INVALID_ARGUMENT;
-    if (!aligned16(grads[r]) || !aligned16(outs[r]) || (has_acc && !aligned16(accums[r])) ||
-        !aligned4(msg_idx[r]) || !aligned4(msg_val[r]))
-      return RSX_ERR_INVALID_ARGUMENT;
-  }
-  // Everything written must be pairwise disjoint and apart from the
-  // gradients, except the outputs: they are written after every read of the
-  // gradients, so they may overlap them (in place: outs[r] == grads[r]).
-  std::vector<Range> writes, outs_r;
-  Range grads_r[RSX_MAX_RANKS];
-  for (int r = 0; r < nranks; ++r) {
-    grads_r[r] = range_of(grads[r], bytes);
-    outs_r.push_back(range_of(outs[r], bytes));
-    writes.push_back(outs_r.back());
-    if (has_acc) writes.push_back(range_of(accums[r], bytes));
-    writes.push_back(range_of(msg_idx[r], sent_max * 4));
-    writes.push_back(range_of(msg_val[r], sent_max * 4));
-    if (wraps(grads_r[r])) return RSX_ERR_INVALID_ARGUMENT;
-  }
-  writes.push_back(nr);
-  writes.push_back(range_of(workspace, l.total));
-  for (const Range& w : writes)
-    if (wraps(w)) return RSX_ERR_INVALID_ARGUMENT;
-  if (!pairwise_disjoint(writes.data(), static_cast<int>(writes.size()))) return RSX_ERR_ALIASING;
-  for (const Range& w : writes) {
-    bool is_out = false;
-    for (const Range& o : outs_r) is_out = is_out || same(o, w);
-    if (is_out) continue;
-    for (int r = 0; r < nranks; ++r)
-      if (overlap(w, grads_r[r])) return RSX_ERR_ALIASING;
-  }
+  const rsx_status_t st = sparse_check(grads, accums, outs, nranks, count, mode, k, msg_idx, msg_val,
+                                       msg_capacity, nnz, workspace, workspace_bytes, false, &l);
+  if (st != RSX_SUCCESS) return st;
+  if (count == 0) return hip_status(launch_sparse_zero_nnz(nnz, nranks, stream));
+  return sparse_launch(grads, accums, outs, nranks, count, mode, threshold, k, msg_idx, msg_val,
+                       msg_capacity, nnz, workspace, l, stream);
+}
 
-  SparseArgs a;
-  memset(&a, 0, sizeof(a));
-  char* ws = static_cast<char*>(workspace);
-  for (int r = 0; r < nranks; ++r) {
-    a.grad[r] = grads[r];
-    a.accum[r] = has_acc ? accums[r] : nullptr;
-    a.out[r] = outs[r];
-    a.msg_idx[r] = msg_idx[r];
-    a.msg_val[r] = msg_val[r];
-  }
-  a.nnz = nnz;
-  a.tile_slot = reinterpret_cast<uint32_t*>(ws + l.tile_slot);
-  a.tile_cnt = reinterpret_cast<uint32_t*>(ws + l.tile_cnt);
-  a.tile_eqc = reinterpret_cast<uint32_t*>(ws + l.tile_eqc);
-  a.tile_off = reinterpret_cast<uint32_t*>(ws + l.tile_off);
-  a.tile_eqb = reinterpret_cast<uint32_t*>(ws + l.tile_eqb);
-  a.gap_idx = reinterpret_cast<uint32_t*>(ws + l.gap_idx);
-  a.gap_val = reinterpret_cast<float*>(ws + l.gap_val);
-  a.hist = reinterpret_cast<uint32_t*>(ws + l.hist);
-  a.state = reinterpret_cast<uint32_t*>(ws + l.state);
-  a.count = count;
-  a.tiles = l.tiles;
-  a.world = static_cast<uint32_t>(nranks);
-  a.k = mode == RSX_SPARSE_TOPK ? static_cast<uint32_t>(k) : 0u;
-  a.cap = static_cast<uint32_t>(sent_max);
-  a.threshold = threshold;
-  return hip_status(launch_sparse(a, mode, has_acc, stream));
+rsx_status_t rsx_sparse_all_reduce_noalloc(const float* const* grads, float* const* accums,
+                                           float* const* outs, int nranks, size_t count,
+                                           rsx_sparse_mode_t mode, float threshold, size_t k,
+                                           uint32_t* const* msg_idx, float* const* msg_val,
+                                           size_t msg_capacity, uint32_t* nnz, hipStream_t stream) {
+  SparseLayout l;
+  rsx_status_t st = sparse_check(grads, accums, outs, nranks, count, mode, k, msg_idx, msg_val,
+                                 msg_capacity, nnz, nullptr, 0, true, &l);
+  if (st != RSX_SUCCESS) return st;
+  if (count == 0) return hip_status(launch_sparse_zero_nnz(nnz, nranks, stream));
+  if (l.total > RSX_SPARSE_SCRATCH_BYTES) return RSX_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != RSX_SUCCESS) return st;
+  return sparse_launch(grads, accums, outs, nranks, count, mode, threshold, k, msg_idx, msg_val,
+                       msg_capacity, nnz, ws, l, stream);
 }
 
 size_t rsx_segment_begin(size_t count, int nranks, int k) {

@@ -62,6 +62,7 @@ extern "C" {
 #define RSX_MAX_RANKS 16         /* largest W a call accepts */
 #define RSX_NAIVE_MAX_BYTES 32768 /* RSX_ALGO_AUTO picks naive at or below this, per rank [MX] */
 #define RSX_FUSE_BATCH 128       /* tensors per pack/unpack launch */
+#define RSX_SPARSE_SCRATCH_BYTES 134217728 /* 128 MiB: scratch array of rsx_sparse_all_reduce_noalloc, per GPU */
 
 typedef enum {
   RSX_FLOAT32 = 0,   /* fp32 in, fp32 fold, fp32 out */
@@ -282,6 +283,29 @@ rsx_status_t rsx_sparse_all_reduce(const float* const* grads, float* const* accu
                                    uint32_t* const* msg_idx, float* const* msg_val,
                                    size_t msg_capacity, uint32_t* nnz, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The sparsified all-reduce above without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments, results,
+ * validation and errors as rsx_sparse_all_reduce; it calls no hipMalloc or
+ * hipFree and allocates nothing.
+ *
+ * Its workspace is a library-owned array of RSX_SPARSE_SCRATCH_BYTES in each
+ * GPU's memory, held from the first call on that GPU until the process ends.
+ * Sizes whose rsx_sparse_workspace_size(...) exceeds RSX_SPARSE_SCRATCH_BYTES
+ * return RSX_ERR_UNSUPPORTED (8 bytes per element of every rank plus a little:
+ * e.g. W * count up to about 16 M elements).  The kernels initialise what they
+ * read of it, so contents left by an earlier call do not matter.  Every call
+ * on one GPU uses the same array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race and give wrong results;
+ * serialise them.  Enqueues on `stream` and does not synchronise.
+ */
+rsx_status_t rsx_sparse_all_reduce_noalloc(const float* const* grads, float* const* accums,
+                                           float* const* outs, int nranks, size_t count,
+                                           rsx_sparse_mode_t mode, float threshold, size_t k,
+                                           uint32_t* const* msg_idx, float* const* msg_val,
+                                           size_t msg_capacity, uint32_t* nnz, hipStream_t stream);
 
 /*
  * Tensor-fusion planner [HV BackgroundThreadLoop, fusion of consecutive

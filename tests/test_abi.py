@@ -456,6 +456,48 @@ def test_sparse_aliasing(lib):
     assert _sp(lib, g, a, o, 2, n, nnz=A + 8) == 5                        # nnz inside a gradient
 
 
+def _spn(lib, grads, accs, outs, w, n, mode=0, thr=0.5, k=0, mi=None, mv=None, cap=None, nnz=None):
+    cap = n if cap is None else cap
+    mi = mi if mi is not None else [A + (2 * r) * (1 << 30) + (1 << 40) for r in range(w)]
+    mv = mv if mv is not None else [A + (2 * r + 1) * (1 << 30) + (1 << 40) for r in range(w)]
+    nnz = A + (1 << 41) if nnz is None else nnz
+    return lib.rsx_sparse_all_reduce_noalloc(_arr(grads), _arr(accs) if accs is not None else None,
+                                             _arr(outs), w, n, mode, thr, k, _arr(mi), _arr(mv), cap,
+                                             nnz, None)
+
+
+@fake_ptrs
+def test_sparse_noalloc_validation_and_size_limit(lib):
+    # The same checks as the workspace form, all before any HIP call; sizes
+    # whose workspace exceeds the scratch array are refused with
+    # RSX_ERR_UNSUPPORTED, also before any HIP call.
+    g, o, a = [A, A + MB], [A + 2 * MB, A + 3 * MB], [A + 4 * MB, A + 5 * MB]
+    n = 1000
+    assert _spn(lib, g, a, o, 0, n) == 1
+    assert _spn(lib, g, a, o, 2, n, mode=2) == 1
+    assert _spn(lib, g, a, o, 2, n, mode=1, k=n + 1) == 1
+    assert _spn(lib, g, a, o, 2, n, cap=n - 1) == 1
+    assert _spn(lib, [A + 4, A + MB], a, o, 2, n) == 1
+    assert _spn(lib, g, a, [A + 4 * MB, A + 3 * MB], 2, n) == 5            # output = accumulation
+    assert _spn(lib, g, a, o, 2, n, nnz=A + 8) == 5                        # nnz inside a gradient
+    assert _spn(lib, g, a, o, 2, 2 ** 32) == 4                             # indices are uint32
+    assert lib.rsx_sparse_all_reduce_noalloc(None, None, _arr(o), 2, n, 0, 0.5, 0, _arr([A] * 2),
+                                             _arr([A] * 2), n, A, None) == 1
+    limit = _header_int("RSX_SPARSE_SCRATCH_BYTES")
+    assert limit == 128 << 20
+    # the largest W = 8 count that fits, and the next size up, which does not
+    fits = max(c for c in range(0, 3 << 20, 4096)
+               if lib.rsx_sparse_workspace_size(8, c, 1, 1) <= limit)
+    assert fits >= (2 << 20) - 4096
+    assert lib.rsx_sparse_workspace_size(8, fits + 4096, 1, 1) > limit
+    G = 1 << 30
+    g8 = [A + r * G for r in range(8)]
+    o8 = [A + (8 + r) * G for r in range(8)]
+    a8 = [A + (16 + r) * G for r in range(8)]
+    for mode, k in ((0, 0), (1, 100)):
+        assert _spn(lib, g8, a8, o8, 8, fits + 4096, mode=mode, k=k) == 4
+
+
 def test_occupancy_caps_context_manager_restores_the_setting(lib):
     import collective_reduction_ring_amd as rsx
     assert lib.rsx_set_occupancy_caps(1) in (0, 1)      # start from "on"
