@@ -21,7 +21,7 @@ RSX_ALGO_RING, RSX_ALGO_NAIVE, RSX_ALGO_AUTO, RSX_ALGO_RING_FUSED, RSX_ALGO_RING
 RSX_SPARSE_THRESHOLD, RSX_SPARSE_TOPK = 0, 1
 RSX_MAX_RANKS = 16
 RSX_NAIVE_MAX_BYTES = 32768
-RSX_FUSE_BATCH = 128
+RSX_FUSE_BATCH = 248
 RSX_FUSION_THRESHOLD_DEFAULT = 64 * 1024 * 1024   # Horovod's default tensor_fusion_threshold
 
 STATUS = {

@@ -8,17 +8,21 @@
 // Pack/unpack (Apache SINGA communicator.cc fusedSynch; Horovod
 // operations.cc PerformOperation) copy many tensors to or from running
 // offsets of one fusion buffer.  One launch carries up to RSX_FUSE_BATCH
-// (src, dst, bytes) descriptors in its kernel arguments; a workgroup finds its
-// descriptor from the prefix sums of per-descriptor tile counts.  Offsets in
-// the fusion buffer are back to back, so src and dst of one copy are often
-// not 16-byte aligned relative to each other: every lane still stores
-// aligned dwordx4 vectors, assembling each from the two aligned source
-// vectors it straddles (v_alignbyte), so both sides move in 16-byte units.
-// Stores are non-temporal: on the 200-tensor fusion workload (W = 4) the
-// packs of all ranks take 180 us against 200 us with plain stores, the
-// unpacks 178 against 202 us.  Fetching the straddled neighbour chunk from
-// the next lane (a wave shuffle) instead of a second load was slower
-// (211 us).
+// copies in its kernel arguments (16 bytes each); a workgroup finds its copy
+// from the tile starts packed into the descriptors.  Offsets in the fusion
+// buffer are back to back, so source and destination of one copy are often
+// not 16-byte aligned relative to each other.  Every lane stores one aligned
+// dwordx4.  When the matching source address is a multiple of 4 bytes (every
+// fp32 / int32 / fp64 / int64 copy) the lane loads those 16 bytes with one
+// dword-aligned dwordx4 load, which the buffer unit serves in every
+// alignment mode; otherwise (2- and 1-byte elements at odd offsets) it
+// assembles them from the two aligned source vectors they straddle
+// (v_alignbyte).  Measured on the 200-tensor fusion workload (W = 4, four
+// packs, one launch each): 164 us with the two-load assembly for every
+// misaligned copy, 152 us with the dword-aligned load; the same copies with
+// every destination padded to 16 bytes take 145 us.  Exchanging the
+// straddled chunk through LDS instead was slower (175 us), and so was a wave
+// shuffle.  Stores are non-temporal (plain stores cost 10%).
 #include "mem.h"
 #include "rsx_internal.h"
 
@@ -140,17 +144,22 @@ __global__ __launch_bounds__(kBlock) void multicopy_kernel(const MultiCopyArgs a
   using E = typename Unit<ES>::T;
   constexpr int U = kCopyUnits;
   const uint32_t t = xcd_tile(blockIdx.x, gridDim.x);
-  if (t >= a.tile_start[a.n]) return;
-  // Descriptor of this tile: the last i with tile_start[i] <= t.
-  int lo = 0, hi = a.n - 1;
+  const uint32_t nd = a.n;
+  if (t >= static_cast<uint32_t>(a.d[nd].off_tile >> kOffBits)) return;
+  // Copy of this tile: the last i with tile_start(i) <= t.
+  uint32_t lo = 0, hi = nd - 1;
   while (lo < hi) {
-    const int mid = (lo + hi + 1) / 2;
-    if (a.tile_start[mid] <= t) lo = mid; else hi = mid - 1;
+    const uint32_t mid = (lo + hi + 1) / 2;
+    if (static_cast<uint32_t>(a.d[mid].off_tile >> kOffBits) <= t) lo = mid; else hi = mid - 1;
   }
-  const char* s = static_cast<const char*>(a.d[lo].src);
-  char* o = static_cast<char*>(a.d[lo].dst);
-  const uint64_t n = a.d[lo].bytes;
-  const uint32_t tile = t - a.tile_start[lo];
+  const uint64_t w0 = a.d[lo].off_tile;
+  const uint64_t off = w0 & kOffMask;
+  const uint64_t n = (a.d[lo + 1].off_tile & kOffMask) - off;
+  char* const fz = a.fused + off;
+  char* const tensor = static_cast<char*>(a.d[lo].tensor);
+  const char* s = a.unpack ? fz : tensor;
+  char* o = a.unpack ? tensor : fz;
+  const uint32_t tile = t - static_cast<uint32_t>(w0 >> kOffBits);
   const uint32_t tid = threadIdx.x;
 
   // [0, h): head bytes up to the first aligned destination byte;
@@ -165,7 +174,8 @@ __global__ __launch_bounds__(kBlock) void multicopy_kernel(const MultiCopyArgs a
     const uint32_t delta = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s1) & 15u);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(o1, nvt * 16);
     uint4 v[U];
-    if (delta == 0) {
+    if ((delta & 3u) == 0) {
+      // 16-byte or dword-aligned source: one load per vector.
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(s1, nvt * 16);
 #pragma unroll
       for (int u = 0; u < U; ++u) v[u] = load_stream(rs, tid * 16, u * kBlock * 16);
@@ -187,13 +197,15 @@ __global__ __launch_bounds__(kBlock) void multicopy_kernel(const MultiCopyArgs a
     for (int u = 0; u < U; ++u) store_b128<kStoreStream>(rd, tid * 16, u * kBlock * 16, v[u]);
   }
   if (tile == 0) {
+    // Head and tail elements (every pointer is element-aligned, so h and the
+    // tail are whole elements).
     const uint32_t nh = static_cast<uint32_t>(h / ES);
     const uint32_t nt = static_cast<uint32_t>((n - h - 16 * m) / ES);
     if (tid < nh) {
       reinterpret_cast<E*>(o)[tid] = reinterpret_cast<const E*>(s)[tid];
     } else if (tid < nh + nt) {
-      const uint64_t off = h + 16 * m;
-      reinterpret_cast<E*>(o + off)[tid - nh] = reinterpret_cast<const E*>(s + off)[tid - nh];
+      const uint64_t toff = h + 16 * m;
+      reinterpret_cast<E*>(o + toff)[tid - nh] = reinterpret_cast<const E*>(s + toff)[tid - nh];
     }
   }
 }
@@ -217,7 +229,7 @@ hipError_t launch_multicopy(int esize, const MultiCopyArgs& a, uint32_t lds, hip
     default:
       return hipErrorInvalidValue;
   }
-  const uint64_t tiles = a.tile_start[a.n];
+  const uint64_t tiles = a.d[a.n].off_tile >> kOffBits;
   return hipLaunchKernel(fn, dim3(static_cast<uint32_t>(xcd_grid(tiles))), dim3(kBlock), args, lds, s);
 }
 

@@ -280,35 +280,46 @@ rsx_status_t fuse_copy(const void* const* tens, const size_t* counts, int ntenso
     }
   }
 
-  // Batches of RSX_FUSE_BATCH descriptors per launch.
+  if (total > kOffMask) return RSX_ERR_UNSUPPORTED;
+
+  // Batches of up to RSX_FUSE_BATCH copies and kMaxCopyTiles tiles per
+  // launch; a tensor beyond 16 GiB is copied as several pieces.
+  constexpr uint64_t kPieceBytes = 1ull << 34;
+  MultiCopyArgs a;
+  memset(&a, 0, sizeof(a));
+  a.fused = static_cast<char*>(const_cast<void*>(fused));
+  a.unpack = pack ? 0u : 1u;
+  uint64_t tiles = 0;
   size_t off = 0;
-  int i = 0;
-  while (i < ntensors) {
-    MultiCopyArgs a;
-    memset(&a, 0, sizeof(a));
-    uint64_t tiles = 0;
-    while (i < ntensors && a.n < RSX_FUSE_BATCH) {
-      const size_t bytes = counts[i] * es;
-      if (bytes != 0) {
-        const char* fz = static_cast<const char*>(fused) + off;
-        CopyDesc& c = a.d[a.n];
-        c.src = pack ? tens[i] : static_cast<const void*>(fz);
-        c.dst = pack ? const_cast<char*>(fz) : const_cast<void*>(tens[i]);
-        c.bytes = bytes;
-        a.tile_start[a.n] = static_cast<uint32_t>(tiles);
-        tiles += copy_tiles(c.dst, bytes);
-        if (tiles > 0x7ffffff0ull) return RSX_ERR_UNSUPPORTED;
-        a.n += 1;
-      }
-      off += bytes;
-      ++i;
-    }
-    if (a.n == 0) continue;
-    a.tile_start[a.n] = static_cast<uint32_t>(tiles);
+  auto flush = [&]() -> rsx_status_t {
+    if (a.n == 0) return RSX_SUCCESS;
+    a.d[a.n].tensor = nullptr;
+    a.d[a.n].off_tile = off | (tiles << kOffBits);  // sentinel: end offset, tile total
     const rsx_status_t st = hip_status(launch_multicopy(static_cast<int>(es), a, 0u, stream));
-    if (st != RSX_SUCCESS) return st;
+    a.n = 0;
+    tiles = 0;
+    return st;
+  };
+  for (int i = 0; i < ntensors; ++i) {
+    const size_t bytes = counts[i] * es;
+    for (size_t done = 0; done < bytes;) {
+      const size_t piece = std::min<size_t>(bytes - done, kPieceBytes);
+      char* tp = static_cast<char*>(const_cast<void*>(tens[i])) + done;
+      const void* dst = pack ? static_cast<const void*>(a.fused + off) : static_cast<const void*>(tp);
+      const uint64_t pt = copy_tiles(dst, piece);
+      if (a.n == RSX_FUSE_BATCH || tiles + pt > kMaxCopyTiles) {
+        const rsx_status_t st = flush();
+        if (st != RSX_SUCCESS) return st;
+      }
+      a.d[a.n].tensor = tp;
+      a.d[a.n].off_tile = off | (tiles << kOffBits);
+      a.n += 1;
+      tiles += pt;
+      off += piece;
+      done += piece;
+    }
   }
-  return RSX_SUCCESS;
+  return flush();
 }
 
 // Overlap rules of the tensor-list all-reduce, in O(n log n) for n buffers.

@@ -63,19 +63,27 @@ struct GatherArgs {
   uint32_t tps_shift;
 };
 
-// One copy of a pack/unpack batch: `bytes` from src to dst, cut into
-// `copy_tiles(...)` tiles of 16-byte destination vectors.
+// Pack / unpack batch: copies between tensors and running offsets of one
+// fusion buffer.  Descriptor i holds tensor i's pointer and one word with
+// the byte offset of its data in the fusion buffer (low 40 bits) and its
+// first tile (high 24 bits); its length is the next descriptor's offset
+// minus its own, so entry n is a sentinel holding the end offset and the
+// tile total.  16 bytes per copy keep RSX_FUSE_BATCH copies in the 4 KiB of
+// kernel arguments.  Tiles are whole 16-byte destination vectors, kBlock per
+// tile; a tensor larger than a launch's tile budget is split into several
+// descriptors by the host.
 struct CopyDesc {
-  const void* src;
-  void* dst;
-  uint64_t bytes;
+  void* tensor;
+  uint64_t off_tile;
 };
-
-// A batch of copies; descriptor i owns tiles [tile_start[i], tile_start[i+1]).
+constexpr int kOffBits = 40;
+constexpr uint64_t kOffMask = (1ull << kOffBits) - 1;
+constexpr uint64_t kMaxCopyTiles = (1ull << (64 - kOffBits)) - 1;  // per launch
 struct MultiCopyArgs {
-  CopyDesc d[RSX_FUSE_BATCH];
-  uint32_t tile_start[RSX_FUSE_BATCH + 1];
-  int n;
+  char* fused;
+  uint32_t n;       // copies in this batch
+  uint32_t unpack;  // 0: tensor -> fused; 1: fused -> tensor
+  CopyDesc d[RSX_FUSE_BATCH + 1];
 };
 // Kernel arguments are limited to 4 KiB.
 static_assert(sizeof(MultiCopyArgs) <= 4096, "pack/unpack batch must fit the kernel arguments");

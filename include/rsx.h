@@ -61,7 +61,7 @@ extern "C" {
 #define RSX_VERSION 110          /* 1.1.0 */
 #define RSX_MAX_RANKS 16         /* largest W a call accepts */
 #define RSX_NAIVE_MAX_BYTES 32768 /* RSX_ALGO_AUTO picks naive at or below this, per rank [MX] */
-#define RSX_FUSE_BATCH 128       /* tensors per pack/unpack launch */
+#define RSX_FUSE_BATCH 248       /* tensors per pack/unpack launch */
 #define RSX_SPARSE_SCRATCH_BYTES 134217728 /* 128 MiB: scratch array of rsx_sparse_all_reduce_noalloc, per GPU */
 
 typedef enum {
@@ -176,7 +176,10 @@ rsx_status_t rsx_all_reduce(const void* const* sendbufs, void* const* recvbufs,
  * fused + (counts[0] + ... + counts[i-1]) elements: back to back, in list
  * order, with no padding.  `fused` must hold the sum of counts and must not
  * overlap any tensor (RSX_ERR_ALIASING).  ntensors >= 0; zero-count tensors
- * are skipped and may be null.  Launches ceil(ntensors / RSX_FUSE_BATCH) kernels.
+ * are skipped and may be null.  Launches one kernel per RSX_FUSE_BATCH
+ * non-empty tensors (a tensor above 16 GiB counts once per 16 GiB).  The sum
+ * of counts times the element size must stay below 2^40 bytes
+ * (RSX_ERR_UNSUPPORTED otherwise).
  */
 rsx_status_t rsx_fuse_pack(const void* const* tensors, const size_t* counts, int ntensors,
                            void* fused, rsx_dtype_t dtype, hipStream_t stream);

@@ -286,6 +286,8 @@ def test_fuse_validation(lib):
     assert lib.rsx_fuse_unpack(None, _arr([None, None]), zero, 2, 0, None) == 0
     assert lib.rsx_fuse_pack(None, zero, 0, None, 0, None) == 0
     assert lib.rsx_fuse_pack(_arr([A]), L.size_array([2 ** 62]), 1, A + MB, 0, None) == 4
+    # a fusion buffer of 2^40 bytes or more is refused (offsets are 40 bits)
+    assert lib.rsx_fuse_pack(_arr([A]), L.size_array([2 ** 38]), 1, A + 2 ** 42, 0, None) == 4
 
 
 def test_binding_refuses_missing_library(tmp_path, monkeypatch):

@@ -566,6 +566,42 @@ def test_fused_pack_allreduce_unpack(dtype):
             assert_parity(to_host(outs[r][i], dtype), want[r][i], dtype, f"rank {r} tensor {i}")
 
 
+@pytest.mark.parametrize("dtype", ["i8", "bf16", "f32", "f64"])
+def test_pack_unpack_many_tensors_every_alignment(dtype):
+    # 600 tensors (three launches of at most RSX_FUSE_BATCH copies), sizes 0
+    # to 20,000 elements, each a view at element offset 0..7 of a larger
+    # buffer and the fusion buffer at an element offset too, so source and
+    # destination meet at every relative alignment: 16-byte, dword, and
+    # (2- and 1-byte types) odd ones.
+    rng = np.random.default_rng(77)
+    sizes = rng.integers(0, 20_000, 600)
+    sizes[::37] = 0
+    sizes[5::41] = rng.integers(1, 9, len(sizes[5::41]))
+    host = [wl.draw(DIST[dtype], np.random.default_rng((78, i)), int(n)) for i, n in enumerate(sizes)]
+    offs = rng.integers(0, 8, len(sizes))
+    bases = [empty(int(n) + 8, dtype) for n in sizes]
+    tens = []
+    for b, o, h in zip(bases, offs, host):
+        v = b[int(o):int(o) + len(h)]
+        v.copy_(to_dev(h, dtype))
+        tens.append(v)
+    total = int(sizes.sum())
+    for foff in (0, 1, 3, 5):
+        fbase = empty(total + 8, dtype, fill=0x5A)
+        fused = fbase[foff:foff + total]
+        say(f"pack/unpack dtype={dtype} tensors={len(sizes)} fused offset={foff}")
+        rsx.fuse_pack(tens, fused)
+        torch.cuda.synchronize()
+        assert_parity(to_host(fused, dtype), oracle.fuse_pack(host), dtype, f"pack, fused offset {foff}")
+        outs = [b[int(o):int(o) + int(n)] for b, o, n in zip(
+            [empty(int(n) + 8, dtype, fill=0x33) for n in sizes], offs[::-1], sizes)]
+        rsx.fuse_unpack(fused, outs)
+        torch.cuda.synchronize()
+        want = oracle.fuse_unpack(oracle.fuse_pack(host), sizes)
+        for i, (o, wv) in enumerate(zip(outs, want)):
+            assert_parity(to_host(o, dtype), wv, dtype, f"unpack tensor {i}, fused offset {foff}")
+
+
 def _list_case(seed, w, sizes, dtype):
     return [[wl.draw(DIST[dtype], np.random.default_rng((seed, r, i)), int(n))
              for i, n in enumerate(sizes)] for r in range(w)]
