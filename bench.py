@@ -106,6 +106,78 @@ def cpu_baseline_threaded(xs, reps_budget_s: float):
     return out, statistics.median(times), len(times), threads
 
 
+def cpu_threads() -> tuple:
+    """(threads to use, cores in this process's affinity mask).  The threaded
+    baselines use every core of the mask, capped at the CPU share the machine
+    declares for this job in OMP_NUM_THREADS when that is set."""
+    aff = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    used = min(aff, int(share)) if share.isdigit() and int(share) > 0 else aff
+    return max(1, used), aff
+
+
+def threaded_folds(ex, threads: int, xs, segs, op: str, dtype: str) -> list:
+    """The oracle's fold of each segment (order, lo, hi), every segment's
+    element range cut into `threads` chunks run in the pool `ex`; each element
+    is still the oracle's fold of that element in the segment's order."""
+    import numpy as np
+
+    import oracle
+
+    tasks = []
+    for si, (order, lo, hi) in enumerate(segs):
+        step = max(1, -(-(hi - lo) // threads))
+        tasks += [(si, order, a, min(a + step, hi)) for a in range(lo, hi, step)] or [(si, order, lo, hi)]
+    parts = list(ex.map(lambda t: oracle.fold(xs, t[1], op, dtype, t[2], t[3]), tasks))
+    return [np.concatenate([p for t, p in zip(tasks, parts) if t[0] == si]) for si in range(len(segs))]
+
+
+def ring_segments(count: int, world: int) -> list:
+    import oracle
+    return [(oracle.ring_fold_order(k, world), lo, hi)
+            for k, (lo, hi) in enumerate(oracle.segment_bounds(count, world))]
+
+
+def oracle_baseline(single, threaded, nbytes: int, budget_s: float, sample: str, same=None) -> dict:
+    """Time the oracle on the host: `single()` (NumPy on one thread) in whole
+    passes for about `budget_s`, then `threaded(ex, threads)` on every core of
+    the job's share for about a third of that; medians.  `same(a, b)` checks
+    the two results agree bit for bit."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    def passes(fn, budget):
+        times, out = [], None
+        t_start = time.perf_counter()
+        while True:
+            t0 = time.perf_counter()
+            out = fn()
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_start >= budget or len(times) >= 200:
+                return out, statistics.median(times), len(times)
+
+    out1, t1, n1 = passes(single, budget_s)
+    threads, aff = cpu_threads()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        out_t, t_t, n_t = passes(lambda: threaded(ex, threads), max(1.0, budget_s / 3))
+    res = {"value": round(nbytes / t1 / 1e9, 3), "unit": "GB/s", "us_per_call": round(t1 * 1e6, 1),
+           "cores": 1, "kind": "oracle", "sample": f"{sample}; {n1} passes, median {t1:.4f} s, "
+                                                   "single-threaded NumPy",
+           "cpu_model": cpu_model(),
+           "threaded": {"value": round(nbytes / t_t / 1e9, 3), "unit": "GB/s",
+                        "us_per_call": round(t_t * 1e6, 1), "cores": threads, "affinity_cores": aff,
+                        "sample": f"the same, split over {threads} threads; {n_t} passes, "
+                                  f"median {t_t:.4f} s"}}
+    if same is not None:
+        res["threaded"]["bit_identical_to_single"] = bool(same(out1, out_t))
+    return res
+
+
+def _same_arrays(a, b) -> bool:
+    import numpy as np
+    return len(a) == len(b) and all(np.array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8))
+                                    for x, y in zip(a, b))
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -225,6 +297,17 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
                "all_reduce": _stat(time_launches(arp, reps, warm, torch), 2 * 4 * 4096 * 4)}
         res["reduce_scatter"]["graph_us_per_call"] = graph_us_per_call(rs, 100, 20, torch)
         res["all_reduce"]["graph_us_per_call"] = graph_us_per_call(arp, 100, 20, torch)
+        if not args.no_cpu_baseline:
+            import oracle
+            rs_segs = [(oracle.ring_fold_order(k, 4), k * 1024, (k + 1) * 1024) for k in range(4)]
+            res["reduce_scatter"]["cpu_baseline"] = oracle_baseline(
+                lambda: oracle.reduce_scatter(xs, "sum", "f32"),
+                lambda ex, t: threaded_folds(ex, t, xs, rs_segs, "sum", "f32"),
+                4 * 4096 * 4 + 4 * 1024 * 4, min(3.0, args.cpu_seconds), "the whole workload", _same_arrays)
+            res["all_reduce"]["cpu_baseline"] = oracle_baseline(
+                lambda: oracle.all_reduce(xs, "sum", "f32"),
+                lambda ex, t: oracle.all_gather(threaded_folds(ex, t, xs, ring_segments(4096, 4), "sum", "f32")),
+                2 * 4 * 4096 * 4, min(3.0, args.cpu_seconds), "the whole workload", _same_arrays)
         return res
     if name == "bf16_bucketed":
         w = wl.WORKLOADS[3]
@@ -234,18 +317,17 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
         _, dev = _arena(torch, torch.bfloat16, world, n)
         for d, x in zip(dev, xs):
             d.copy_(torch.from_numpy(x.view(np.int16)).view(torch.bfloat16))
+        sample = [x[:2 * bucket].copy() for x in xs]      # the first two buckets, for the oracle
         del xs
         _, out = _arena(torch, torch.bfloat16, world, n)
-        bounds = [(b0, min(b0 + bucket, n)) for b0 in range(0, n, bucket)]
+        nbuckets = -(-n // bucket)
 
         def bucketed(algo):
-            plans = [rsx.AllReduce([d[b0:b1] for d in dev], [o[b0:b1] for o in out], "avg", algo)
-                     for b0, b1 in bounds]
-            return lambda: [p() for p in plans]
+            return rsx.AllReduceBucketed(dev, out, bucket, "avg", algo)
         nb = 2 * world * n * 2
         step = bucketed("ring")
         res = {"workload": "all-reduce avg bf16 (fp32 accumulate), W=8, 134,217,728/rank, "
-                           f"{len(bounds)} buckets of <= 25 MiB in sequence on one stream; "
+                           f"{nbuckets} buckets of <= 25 MiB in sequence on one stream; "
                            "ring = one pass per bucket",
                "ring": _stat(time_launches(step, reps // 4 or 1, warm, torch), nb)}
         res["ring"]["graph_us_per_step"] = graph_us_per_call(step, 1, 10, torch)
@@ -257,6 +339,25 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
         # For comparison only: the same bytes as one all-reduce without buckets.
         whole = rsx.AllReduce(dev, out, "avg", "ring")
         res["unbucketed_one_call"] = _stat(time_launches(whole, reps // 4 or 1, warm, torch), nb)
+        if not args.no_cpu_baseline:
+            import oracle
+
+            def threaded(ex, t):
+                outs = [np.empty_like(x) for x in sample]
+                for b0 in (0, bucket):
+                    part = [x[b0:b0 + bucket] for x in sample]
+                    for r, o in enumerate(oracle.all_gather(
+                            threaded_folds(ex, t, part, ring_segments(bucket, world), "avg", "bf16"))):
+                        outs[r][b0:b0 + bucket] = o
+                return outs
+            del dev, out, whole, step
+            torch.cuda.empty_cache()
+            log("oracle baseline: two buckets")
+            res["ring"]["cpu_baseline"] = oracle_baseline(
+                lambda: oracle.bucketed_all_reduce(sample, bucket, "avg", "bf16"), threaded,
+                2 * world * 2 * bucket * 2, args.cpu_seconds,
+                f"the first 2 of the {nbuckets} buckets (2 x {bucket} bf16 per rank, W={world}), "
+                "bytes scaled to that sample", _same_arrays)
         return res
     if name == "int32_w16":
         w = wl.WORKLOADS[4]
@@ -266,7 +367,6 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
         _, dev = _arena(torch, torch.int32, world, n)
         for d, x in zip(dev, xs):
             d.copy_(torch.from_numpy(x))
-        del xs
         _, out = _arena(torch, torch.int32, world, seg)
         _, ar = _arena(torch, torch.int32, world, n)
         res = {"workload": "int32 W=16, 33,554,432/rank"}
@@ -277,6 +377,19 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
                                             2 * world * n * 4)
         res["all_reduce_sum_two_pass"] = _stat(time_launches(rsx.AllReduce(dev, ar, "sum", "ring_split"), reps,
                                                              warm, torch), 2 * world * n * 4)
+        if not args.no_cpu_baseline:
+            import oracle
+            rs_segs = [(oracle.ring_fold_order(k, world), k * seg, (k + 1) * seg) for k in range(world)]
+            for op in ("sum", "max"):
+                log(f"oracle baseline: int32 W=16 {op}")
+                res[f"reduce_scatter_{op}"]["cpu_baseline"] = oracle_baseline(
+                    lambda: oracle.reduce_scatter(xs, op, "i32"),
+                    lambda ex, t: threaded_folds(ex, t, xs, rs_segs, op, "i32"),
+                    world * n * 4 + world * seg * 4, args.cpu_seconds / 2, "the whole workload", _same_arrays)
+                res[f"all_reduce_{op}"]["cpu_baseline"] = oracle_baseline(
+                    lambda: oracle.all_reduce(xs, op, "i32"),
+                    lambda ex, t: oracle.all_gather(threaded_folds(ex, t, xs, ring_segments(n, world), op, "i32")),
+                    2 * world * n * 4, args.cpu_seconds / 2, "the whole workload", _same_arrays)
         return res
     if name == "fused":
         world = 4
@@ -295,7 +408,7 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
         nb = world * total * 4
         direct = rsx.TensorFusionAllReduce(tens, None, "sum", "ring")
         grouped = rsx.GroupedAllReduce(tens, None, "sum", "ring", 64 * 2 ** 20)
-        return {"workload": f"fused: W=4, {len(sizes)} fp32 tensors, {total} elements/rank",
+        res = {"workload": f"fused: W=4, {len(sizes)} fp32 tensors, {total} elements/rank",
                 "direct_tensor_fusion_all_reduce": _stat(time_launches(direct, reps, warm, torch), 2 * nb),
                 "grouped_64MiB_threshold": dict(
                     _stat(time_launches(grouped, reps, warm, torch), 2 * nb), groups=len(grouped.groups)),
@@ -303,6 +416,20 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
                 "all_reduce": _stat(time_launches(arp, reps, warm, torch), 2 * nb),
                 "unpack": _stat(time_launches(unpack, reps, warm, torch), 2 * nb),
                 "end_to_end": _stat(time_launches(e2e, reps, warm, torch), 6 * nb)}
+        if not args.no_cpu_baseline:
+            import oracle
+            counts = [int(c) for c in sizes]
+
+            def threaded(ex, t):
+                fused_h = list(ex.map(oracle.fuse_pack, per_rank))
+                red = oracle.all_gather(threaded_folds(ex, t, fused_h, ring_segments(total, world), "sum", "f32"))
+                return list(ex.map(lambda f: oracle.fuse_unpack(f, counts), red))
+            log("oracle baseline: pack, all-reduce, unpack")
+            res["end_to_end"]["cpu_baseline"] = oracle_baseline(
+                lambda: oracle.fused_all_reduce(per_rank, "sum", "f32"), threaded, 6 * nb, args.cpu_seconds,
+                "the whole workload: pack, all-reduce and unpack of every rank",
+                lambda a, b: all(_same_arrays(x, y) for x, y in zip(a, b)))
+        return res
     if name == "sweep":
         res = {"workload": "all-reduce sum fp32, W=4, 1-32 KiB per rank: naive vs ring"}
         for kib in wl.SWEEP_KIB:
@@ -323,6 +450,15 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
                 torch.cuda.synchronize()
                 row[algo]["wall_us_per_call"] = round((time.perf_counter() - t0) * 1e3, 2)
                 row[algo]["graph_us_per_call"] = graph_us_per_call(p, 100, 20, torch)
+                if not args.no_cpu_baseline:
+                    import oracle
+                    segs = ring_segments(n, 4) if algo == "ring" else [(list(range(4)), 0, n)]
+                    whole = oracle.all_reduce if algo == "ring" else oracle.naive_all_reduce
+                    row[algo]["cpu_baseline"] = oracle_baseline(
+                        lambda: whole(xs, "sum", "f32"),
+                        lambda ex, t: oracle.all_gather(threaded_folds(ex, t, xs, segs, "sum", "f32"))
+                        if algo == "ring" else [threaded_folds(ex, t, xs, segs, "sum", "f32")[0]] * 4,
+                        2 * 4 * n * 4, 0.5, "the whole call", _same_arrays)
             res[f"{kib}KiB"] = row
         return res
     if name == "sparse":
@@ -335,7 +471,6 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
             d.copy_(torch.from_numpy(x))
         for d, x in zip(a0, accs):
             d.copy_(torch.from_numpy(x))
-        del grads, accs
         a_all, a = _arena(torch, torch.float32, world, n)
         _, out = _arena(torch, torch.float32, world, n)
         res = {"workload": f"sparsified all-reduce with error feedback, W={world}, {n} fp32/rank, "
@@ -358,6 +493,35 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
             ms_g = time_from_state(graph.replay, reset, reps, warm, torch)
             st["graph_replay_median_us"] = round(statistics.median(ms_g) * 1e3, 2)
             res[mode] = st
+        if not args.no_cpu_baseline:
+            import oracle
+            k = oracle.topk_count(n, wl.SPARSE_TOPK_FRACTION)
+            for mode in ("threshold", "topk"):
+                fn, arg = ((oracle.sparsify_threshold, wl.SPARSE_THRESHOLD) if mode == "threshold"
+                           else (oracle.sparsify_topk, k))
+                nnz = res[mode]["nnz_total"]
+
+                def threaded(ex, t, fn=fn, arg=arg):
+                    per = list(ex.map(lambda r: fn(grads[r], accs[r], arg), range(world)))
+                    return [oracle.sparse_combine([(i, v) for i, v, _ in per], n)]
+                if mode == "threshold":
+                    single = lambda: oracle.sparse_all_reduce(grads, accs, "threshold",  # noqa: E731
+                                                              wl.SPARSE_THRESHOLD)[0][:1]
+                    sample, nbytes, budget = "the whole workload", world * n * 16 + 16 * nnz, args.cpu_seconds
+                else:
+                    # one rank's selection (a stable sort of 64 Mi values takes ~15 s) and the
+                    # combine of its message; the threaded leg runs all 8 ranks, one per thread
+                    single = lambda: [oracle.sparse_combine(  # noqa: E731
+                        [oracle.sparsify_topk(grads[0], accs[0], k)[:2]], n)]
+                    sample, nbytes, budget = ("rank 0 only (its sort, residual and combine); bytes "
+                                              "scaled to one rank", n * 16 + 16 * k, 1.0)
+                log(f"oracle baseline: sparse {mode}")
+                cb = oracle_baseline(single, threaded, nbytes, budget, sample)
+                if mode == "topk":   # the threaded leg did all W ranks: its bytes are W times one rank's
+                    cb["threaded"]["value"] = round(cb["threaded"]["value"] * world, 3)
+                    cb["threaded"]["sample"] = ("all 8 ranks, one per thread, then the combine; "
+                                                + cb["threaded"]["sample"].split("; ", 1)[1])
+                res[mode]["cpu_baseline"] = cb
         return res
     if name == "sparse_sweep":
         # The sparsified all-reduce across selection sizes and rank counts, at

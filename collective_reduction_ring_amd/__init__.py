@@ -5,7 +5,7 @@ library ``librsx.so`` (C ABI in ``include/rsx.h``), loaded on first use; the
 Python layer only marshals tensors into pointers and counts.
 """
 from .api import (  # noqa: F401
-    ALGOS, DTYPES, OPS, AllReduce, BucketedAllReduce, FusedAllReduce, FusePack, FuseUnpack, ReduceScatter,
+    ALGOS, DTYPES, OPS, AllReduce, AllReduceBucketed, BucketedAllReduce, FusedAllReduce, FusePack, FuseUnpack, ReduceScatter,
     GroupedAllReduce, TensorFusionAllReduce, fusion_groups, fusion_threshold,
     all_gather, all_reduce,
     all_reduce_bucketed, fuse_pack, fuse_unpack, fused_all_reduce, reduce_scatter,

@@ -179,6 +179,24 @@ def all_reduce(inputs, outputs=None, op: str = "sum", algo: str = "ring", stream
     AllReduce(inputs, outputs, op, algo, wire)(stream)
 
 
+class AllReduceBucketed(AllReduce):
+    """A prepared bucketed all-reduce (``rsx_all_reduce_bucketed``): consecutive
+    buckets of ``bucket_elems`` elements, each an all-reduce of its own with its
+    own segments, launched in order on one stream ("Distributed primitives",
+    bucketed ring all-reduce)."""
+
+    def __init__(self, inputs, outputs=None, bucket_elems: int = 13_107_200, op: str = "sum",
+                 algo: str = "ring", wire: str | None = None):
+        super().__init__(inputs, outputs, op, algo, wire)
+        if bucket_elems <= 0:
+            raise ValueError("bucket_elems must be positive")
+        self.args = self.args[:4] + (int(bucket_elems),) + self.args[4:]
+        self.fn = L.lib().rsx_all_reduce_bucketed
+
+    def __call__(self, stream=None) -> None:
+        _launch(self, "rsx_all_reduce_bucketed", stream)
+
+
 def all_reduce_bucketed(inputs, outputs=None, bucket_elems: int = 13_107_200, op: str = "sum",
                         algo: str = "ring", stream=None, wire: str | None = None) -> None:
     """All-reduce consecutive buckets of ``bucket_elems`` elements, one launch per bucket,
@@ -186,14 +204,7 @@ def all_reduce_bucketed(inputs, outputs=None, bucket_elems: int = 13_107_200, op
 
     Each bucket is an all-reduce of its own with its own segment split.
     """
-    outputs = inputs if outputs is None else outputs
-    n = inputs[0].numel()
-    if bucket_elems <= 0:
-        raise ValueError("bucket_elems must be positive")
-    for start in range(0, n, bucket_elems):
-        stop = min(start + bucket_elems, n)
-        AllReduce([t[start:stop] for t in inputs], [t[start:stop] for t in outputs], op, algo,
-                  wire)(stream)
+    AllReduceBucketed(inputs, outputs, bucket_elems, op, algo, wire)(stream)
 
 
 class occupancy_caps:
@@ -243,6 +254,7 @@ class BucketedAllReduce:
         self.bounds = [(b0, min(b0 + bucket_elems, n)) for b0 in range(0, n, bucket_elems)]
         self.plans = [AllReduce([t[b0:b1] for t in inputs], [t[b0:b1] for t in outputs], op, algo, wire)
                       for b0, b1 in self.bounds]
+        self.serial = AllReduceBucketed(inputs, outputs, bucket_elems, op, algo, wire)
         self.device = inputs[0].device
         self.stream = stream if stream is not None else torch.cuda.Stream(device=self.device)
         self.events = [torch.cuda.Event() for _ in self.plans]
@@ -265,10 +277,10 @@ class BucketedAllReduce:
         dst.wait_stream(self.stream)
 
     def __call__(self, stream=None) -> None:
-        """Every bucket at once, on `stream` (no overlap): the serial reference."""
+        """Every bucket at once, on `stream` (no overlap): the serial reference,
+        one rsx_all_reduce_bucketed call."""
         with occupancy_caps(self.occupancy_caps):
-            for p in self.plans:
-                p(stream)
+            self.serial(stream)
 
 
 class _FuseCopy:

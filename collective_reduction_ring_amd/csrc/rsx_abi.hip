@@ -528,6 +528,118 @@ rsx_status_t scratch_of_current_device(void** out) {
   return RSX_SUCCESS;
 }
 
+// An all-reduce of `count` elements fits the launch grid in every form
+// (one pass, naive, or reduce-scatter + all-gather: at most count/W + 1
+// whole-vector or element tiles per segment, W segments).
+bool all_reduce_grid_ok(int nranks, size_t count) {
+  const uint64_t seg = (count + nranks - 1) / nranks;
+  const uint64_t tiles = std::max(fold_tiles(seg, nranks, false, 1) * static_cast<uint64_t>(nranks),
+                                  fold_tiles(count, nranks, false, 1));
+  return tiles <= 0x7ffffff0ull;
+}
+
+// Checks of an all-reduce (no HIP call).  *nothing: valid, with no work.
+rsx_status_t all_reduce_check(const void* const* sendbufs, void* const* recvbufs, int nranks,
+                              size_t count, rsx_dtype_t dtype, rsx_op_t op, rsx_algo_t algo,
+                              bool* nothing) {
+  *nothing = false;
+  rsx_status_t st = check_common(sendbufs, recvbufs, nranks, dtype);
+  if (st != RSX_SUCCESS) return st;
+  if (!valid_op(op)) return RSX_ERR_INVALID_OP;
+  if (algo != RSX_ALGO_RING && algo != RSX_ALGO_NAIVE && algo != RSX_ALGO_AUTO &&
+      algo != RSX_ALGO_RING_FUSED && algo != RSX_ALGO_RING_SPLIT)
+    return RSX_ERR_INVALID_ARGUMENT;
+  if (count == 0) {
+    *nothing = true;
+    return RSX_SUCCESS;
+  }
+  if ((st = check_device_ptrs(sendbufs, recvbufs, nranks, esize_of(dtype))) != RSX_SUCCESS) return st;
+  const size_t es = esize_of(dtype);
+  size_t bytes;
+  if (!mul_ok(count, es, &bytes)) return RSX_ERR_UNSUPPORTED;
+  if (algo == RSX_ALGO_RING_SPLIT && count % static_cast<size_t>(nranks) != 0)
+    return RSX_ERR_UNSUPPORTED;
+  Range in[RSX_MAX_RANKS], out[RSX_MAX_RANKS];
+  bool in_place_all = true;
+  for (int r = 0; r < nranks; ++r) {
+    in[r] = range_of(sendbufs[r], bytes);
+    out[r] = range_of(recvbufs[r], bytes);
+    if (wraps(in[r]) || wraps(out[r])) return RSX_ERR_INVALID_ARGUMENT;
+  }
+  if (!reads_consistent(in, nranks) || !pairwise_disjoint(out, nranks)) return RSX_ERR_ALIASING;
+  for (int r = 0; r < nranks; ++r) {
+    in_place_all = in_place_all && same(out[r], in[r]);
+    for (int j = 0; j < nranks; ++j)
+      if (overlap(out[r], in[j]) && !same(out[r], in[j])) return RSX_ERR_ALIASING;
+  }
+  // One rank in place: nothing to do, except that a half wire still rounds.
+  *nothing = nranks == 1 && in_place_all && dtype != RSX_FLOAT32_HALF_WIRE;
+  if (!*nothing && !all_reduce_grid_ok(nranks, count)) return RSX_ERR_UNSUPPORTED;
+  return RSX_SUCCESS;
+}
+
+// Launches of a checked all-reduce.
+rsx_status_t all_reduce_launch(const void* const* sendbufs, void* const* recvbufs, int nranks,
+                               size_t count, rsx_dtype_t dtype, rsx_op_t op, rsx_algo_t algo,
+                               hipStream_t stream) {
+  const size_t es = esize_of(dtype);
+  const size_t bytes = count * es;
+  rsx_status_t st = RSX_SUCCESS;
+  const bool naive = algo == RSX_ALGO_NAIVE || (algo == RSX_ALGO_AUTO && bytes <= RSX_NAIVE_MAX_BYTES);
+  bool vec = true;
+  for (int r = 0; r < nranks; ++r) vec = vec && aligned16(sendbufs[r]) && aligned16(recvbufs[r]);
+
+  // Two passes on request ("Distributed primitives": Ring AllReduce =
+  // ReduceScatter + AllGather): the reduce-scatter stores segment k into
+  // recvbufs[k] at its own offset, and the all-gather copies it from there to
+  // the other ranks.  Each lane of the reduce-scatter reads its element of
+  // every input before it stores, and touches no other segment, so every
+  // alias the one-pass form accepts is still safe; the all-gather runs after
+  // the last read of the inputs, in stream order.  With the occupancy caps
+  // the two forms are within a few percent of each other as whole calls
+  // (W = 8 fp32, 256 MiB per rank: 734 against 729 us; W = 4: one pass up
+  // to 9% ahead; W = 16 at 256 MiB: two passes 4% ahead), so RSX_ALGO_RING
+  // takes the one-pass form, which moves the fewest bytes.
+  if (algo == RSX_ALGO_RING_SPLIT) {
+    const size_t seg = count / static_cast<size_t>(nranks);
+    const bool rs_vec = vec && (seg * es) % kVecBytes == 0;
+    FoldArgs a;
+    memset(&a, 0, sizeof(a));
+    const void* pieces[RSX_MAX_RANKS];
+    for (int r = 0; r < nranks; ++r) {
+      a.src[r] = sendbufs[r];
+      a.dst[r] = static_cast<char*>(recvbufs[r]) + static_cast<size_t>(r) * seg * es;
+      pieces[r] = a.dst[r];
+    }
+    a.count = count;
+    a.seg = seg;
+    a.rot = 1;
+    const int vl = static_cast<int>(kVecBytes / es);
+    // The all-gather's grid has no more tiles than the reduce-scatter's (the
+    // same segments, in 16-byte units whenever the reduce-scatter's are), so
+    // its size check cannot fail after the reduce-scatter has launched.
+    st = launch_fold_any(dtype, op, nranks, true, rs_vec, a, fold_tiles(seg, nranks, rs_vec, vl),
+                         static_cast<uint32_t>(nranks), stream);
+    if (st != RSX_SUCCESS) return st;
+    return launch_gather_any(pieces, recvbufs, nranks, seg, es, stream);
+  }
+
+  FoldArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int r = 0; r < nranks; ++r) {
+    a.src[r] = sendbufs[r];
+    a.dst[r] = recvbufs[r];
+  }
+  a.count = count;
+  const uint64_t seg = naive ? count : (count + nranks - 1) / nranks;
+  a.seg = seg;
+  a.rot = naive ? 0 : 1;
+  const uint32_t nseg = naive ? 1 : static_cast<uint32_t>(nranks);
+  const int vl = static_cast<int>(kVecBytes / es);
+  return launch_fold_any(dtype, op, nranks, false, vec, a, fold_tiles(seg, nranks, vec, vl), nseg,
+                         stream);
+}
+
 }  // namespace
 }  // namespace rsx
 
@@ -620,88 +732,38 @@ rsx_status_t rsx_all_gather(const void* const* sendbufs, void* const* recvbufs, 
 rsx_status_t rsx_all_reduce(const void* const* sendbufs, void* const* recvbufs, int nranks,
                             size_t count, rsx_dtype_t dtype, rsx_op_t op, rsx_algo_t algo,
                             hipStream_t stream) {
-  rsx_status_t st = check_common(sendbufs, recvbufs, nranks, dtype);
-  if (st != RSX_SUCCESS) return st;
-  if (!valid_op(op)) return RSX_ERR_INVALID_OP;
-  if (algo != RSX_ALGO_RING && algo != RSX_ALGO_NAIVE && algo != RSX_ALGO_AUTO &&
-      algo != RSX_ALGO_RING_FUSED && algo != RSX_ALGO_RING_SPLIT)
-    return RSX_ERR_INVALID_ARGUMENT;
-  if (count == 0) return RSX_SUCCESS;
-  if ((st = check_device_ptrs(sendbufs, recvbufs, nranks, esize_of(dtype))) != RSX_SUCCESS) return st;
+  bool nothing = false;
+  const rsx_status_t st = all_reduce_check(sendbufs, recvbufs, nranks, count, dtype, op, algo, &nothing);
+  if (st != RSX_SUCCESS || nothing) return st;
+  return all_reduce_launch(sendbufs, recvbufs, nranks, count, dtype, op, algo, stream);
+}
+
+rsx_status_t rsx_all_reduce_bucketed(const void* const* sendbufs, void* const* recvbufs, int nranks,
+                                     size_t count, size_t bucket_elems, rsx_dtype_t dtype, rsx_op_t op,
+                                     rsx_algo_t algo, hipStream_t stream) {
+  if (bucket_elems == 0) return RSX_ERR_INVALID_ARGUMENT;
+  bool nothing = false;
+  rsx_status_t st = all_reduce_check(sendbufs, recvbufs, nranks, count, dtype, op, algo, &nothing);
+  if (st != RSX_SUCCESS || nothing) return st;
+  // The two-pass form needs W to divide every bucket: the full ones and the last.
+  const size_t w = static_cast<size_t>(nranks);
+  const size_t full = std::min(bucket_elems, count), last = count % bucket_elems;
+  if (algo == RSX_ALGO_RING_SPLIT && (full % w != 0 || last % w != 0)) return RSX_ERR_UNSUPPORTED;
+  // Every launch's grid is checked before the first one: the largest bucket's.
+  if (!all_reduce_grid_ok(nranks, full)) return RSX_ERR_UNSUPPORTED;
   const size_t es = esize_of(dtype);
-  size_t bytes;
-  if (!mul_ok(count, es, &bytes)) return RSX_ERR_UNSUPPORTED;
-  if (algo == RSX_ALGO_RING_SPLIT && count % static_cast<size_t>(nranks) != 0)
-    return RSX_ERR_UNSUPPORTED;
-  Range in[RSX_MAX_RANKS], out[RSX_MAX_RANKS];
-  bool in_place_all = true;
-  for (int r = 0; r < nranks; ++r) {
-    in[r] = range_of(sendbufs[r], bytes);
-    out[r] = range_of(recvbufs[r], bytes);
-    if (wraps(in[r]) || wraps(out[r])) return RSX_ERR_INVALID_ARGUMENT;
-  }
-  if (!reads_consistent(in, nranks) || !pairwise_disjoint(out, nranks)) return RSX_ERR_ALIASING;
-  for (int r = 0; r < nranks; ++r) {
-    in_place_all = in_place_all && same(out[r], in[r]);
-    for (int j = 0; j < nranks; ++j)
-      if (overlap(out[r], in[j]) && !same(out[r], in[j])) return RSX_ERR_ALIASING;
-  }
-  // One rank in place: nothing to do, except that a half wire still rounds.
-  if (nranks == 1 && in_place_all && dtype != RSX_FLOAT32_HALF_WIRE) return RSX_SUCCESS;
-
-  const bool naive = algo == RSX_ALGO_NAIVE || (algo == RSX_ALGO_AUTO && bytes <= RSX_NAIVE_MAX_BYTES);
-  bool vec = true;
-  for (int r = 0; r < nranks; ++r) vec = vec && aligned16(sendbufs[r]) && aligned16(recvbufs[r]);
-
-  // Two passes on request ("Distributed primitives": Ring AllReduce =
-  // ReduceScatter + AllGather): the reduce-scatter stores segment k into
-  // recvbufs[k] at its own offset, and the all-gather copies it from there to
-  // the other ranks.  Each lane of the reduce-scatter reads its element of
-  // every input before it stores, and touches no other segment, so every
-  // alias the one-pass form accepts is still safe; the all-gather runs after
-  // the last read of the inputs, in stream order.  With the occupancy caps
-  // the two forms are within a few percent of each other as whole calls
-  // (W = 8 fp32, 256 MiB per rank: 734 against 729 us; W = 4: one pass up
-  // to 9% ahead; W = 16 at 256 MiB: two passes 4% ahead), so RSX_ALGO_RING
-  // takes the one-pass form, which moves the fewest bytes.
-  if (algo == RSX_ALGO_RING_SPLIT) {
-    const size_t seg = count / static_cast<size_t>(nranks);
-    const bool rs_vec = vec && (seg * es) % kVecBytes == 0;
-    FoldArgs a;
-    memset(&a, 0, sizeof(a));
-    const void* pieces[RSX_MAX_RANKS];
+  const void* src[RSX_MAX_RANKS];
+  void* dst[RSX_MAX_RANKS];
+  for (size_t b0 = 0; b0 < count;) {
+    const size_t n = std::min(bucket_elems, count - b0);
     for (int r = 0; r < nranks; ++r) {
-      a.src[r] = sendbufs[r];
-      a.dst[r] = static_cast<char*>(recvbufs[r]) + static_cast<size_t>(r) * seg * es;
-      pieces[r] = a.dst[r];
+      src[r] = static_cast<const char*>(sendbufs[r]) + b0 * es;
+      dst[r] = static_cast<char*>(recvbufs[r]) + b0 * es;
     }
-    a.count = count;
-    a.seg = seg;
-    a.rot = 1;
-    const int vl = static_cast<int>(kVecBytes / es);
-    // The all-gather's grid has no more tiles than the reduce-scatter's (the
-    // same segments, in 16-byte units whenever the reduce-scatter's are), so
-    // its size check cannot fail after the reduce-scatter has launched.
-    st = launch_fold_any(dtype, op, nranks, true, rs_vec, a, fold_tiles(seg, nranks, rs_vec, vl),
-                         static_cast<uint32_t>(nranks), stream);
-    if (st != RSX_SUCCESS) return st;
-    return launch_gather_any(pieces, recvbufs, nranks, seg, es, stream);
+    if ((st = all_reduce_launch(src, dst, nranks, n, dtype, op, algo, stream)) != RSX_SUCCESS) return st;
+    b0 += n;
   }
-
-  FoldArgs a;
-  memset(&a, 0, sizeof(a));
-  for (int r = 0; r < nranks; ++r) {
-    a.src[r] = sendbufs[r];
-    a.dst[r] = recvbufs[r];
-  }
-  a.count = count;
-  const uint64_t seg = naive ? count : (count + nranks - 1) / nranks;
-  a.seg = seg;
-  a.rot = naive ? 0 : 1;
-  const uint32_t nseg = naive ? 1 : static_cast<uint32_t>(nranks);
-  const int vl = static_cast<int>(kVecBytes / es);
-  return launch_fold_any(dtype, op, nranks, false, vec, a, fold_tiles(seg, nranks, vec, vl), nseg,
-                         stream);
+  return RSX_SUCCESS;
 }
 
 rsx_status_t rsx_fuse_pack(const void* const* tensors, const size_t* counts, int ntensors,

@@ -4,7 +4,9 @@
 // reduce-scatter (mostly reads) and an all-reduce (as many writes as reads)
 // can reach; reading 8 buffers into a sum written to a ninth, or to all 8
 // (in place) or to 8 other buffers, are the reduce-scatter's and the
-// all-reduce's own patterns at W = 8 without the ring order.  Two more
+// all-reduce's own patterns at W = 8 without the ring order; reading 16
+// buffers into a sum written to a seventeenth is the reduce-scatter's at
+// W = 16 (buffers 128 MiB apart, as 16 ranks of 128 MiB are).  Two more
 // patterns bound the sparsified all-reduce: reading two
 // buffers and writing the second in place (its compaction and gather), and
 // writing each tile to 8 buffers (its combine).  Every pattern runs with
@@ -41,11 +43,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p) {
 
 // MODE 0: read only; 1: copy; 2: write only; 3: dst += src (two reads, one
 // write in place); 4: write each tile to 8 buffers (dst cut in 8, the grid
-// covering one eighth); 5: the sum of a tile of 8 buffers (src cut in 8, the
-// grid covering one eighth) written to dst; 6: the same sum written back to
-// all 8 (in place).  B lanes of U vectors per tile; the grid is a multiple
-// of 8.
-template <int MODE, int LOAD_AUX, int STORE_AUX, int B, int U>
+// covering one eighth); 5: the sum of a tile of NB buffers (src cut in NB,
+// the grid covering one NB-th) written to dst; 6: the same sum (NB = 8)
+// written back to all 8 (in place); 7: to 8 other buffers.  B lanes of U
+// vectors per tile; the grid is a multiple of 8.
+template <int MODE, int LOAD_AUX, int STORE_AUX, int B, int U, int NB = 8>
 __global__ __launch_bounds__(B) void stream_kernel(const char* src, char* dst, float* sink) {
   constexpr int kUnits = U, kBlock = B;
   constexpr unsigned kTileBytes = B * U * 16;
@@ -67,9 +69,9 @@ __global__ __launch_bounds__(B) void stream_kernel(const char* src, char* dst, f
   }
   if (MODE == 5 || MODE == 6 || MODE == 7) {
     const size_t part = size_t(gridDim.x) * kTileBytes;
-    u32x4 w[8][kUnits];
+    u32x4 w[NB][kUnits];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
+    for (int b = 0; b < NB; ++b) {
       const __amdgpu_buffer_rsrc_t r = rsrc<kTileBytes>(src + b * part + off);
 #pragma unroll
       for (int u = 0; u < kUnits; ++u) w[b][u] = __builtin_amdgcn_raw_buffer_load_b128(r, voff, u * kBlock * 16, LOAD_AUX);
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(B) void stream_kernel(const char* src, char* dst, f
     for (int u = 0; u < kUnits; ++u) {
       v[u] = w[0][u];
 #pragma unroll
-      for (int b = 1; b < 8; ++b) v[u] += w[b][u];
+      for (int b = 1; b < NB; ++b) v[u] += w[b][u];
     }
     if (MODE == 5) {
       const __amdgpu_buffer_rsrc_t d = rsrc<kTileBytes>(dst + off);
@@ -159,11 +161,11 @@ struct Best {
 
 // Rate of one pattern in each lane configuration; the best and the first
 // (256 lanes of one vector).
-template <int MODE, int LA, int SA>
+template <int MODE, int LA, int SA, int NB = 8>
 Best measure(const char* src, char* dst, float* sink, size_t bytes, double moved) {
   Best best;
   auto one = [&](auto kernel, unsigned tile_bytes, unsigned block, const char* cfg, unsigned wg_per_cu = 8) {
-    const unsigned tiles = unsigned(bytes / tile_bytes) / (MODE >= 4 ? 8 : 1);  // a multiple of 8
+    const unsigned tiles = unsigned(bytes / tile_bytes) / (MODE >= 4 ? NB : 1);  // a multiple of 8
     const unsigned lds = wg_per_cu >= 8 ? 0u : (160u * 1024u / wg_per_cu) & ~1023u;
     const float ms = median_ms([&] { hipLaunchKernelGGL(kernel, dim3(tiles), dim3(block), lds, 0, src, dst, sink); });
     CHECK(hipGetLastError());
@@ -174,15 +176,15 @@ Best measure(const char* src, char* dst, float* sink, size_t bytes, double moved
       best.cfg = cfg;
     }
   };
-  one(stream_kernel<MODE, LA, SA, 256, 1>, 256 * 16, 256, "256x1");
-  one(stream_kernel<MODE, LA, SA, 512, 1>, 512 * 16, 512, "512x1");
-  one(stream_kernel<MODE, LA, SA, 1024, 1>, 1024 * 16, 1024, "1024x1");
-  one(stream_kernel<MODE, LA, SA, 256, 4>, 256 * 64, 256, "256x4");
-  one(stream_kernel<MODE, LA, SA, 256, 1>, 256 * 16, 256, "256x1, 6 WG/CU", 6);
-  one(stream_kernel<MODE, LA, SA, 256, 1>, 256 * 16, 256, "256x1, 5 WG/CU", 5);
-  one(stream_kernel<MODE, LA, SA, 256, 1>, 256 * 16, 256, "256x1, 4 WG/CU", 4);
-  one(stream_kernel<MODE, LA, SA, 256, 1>, 256 * 16, 256, "256x1, 3 WG/CU", 3);
-  one(stream_kernel<MODE, LA, SA, 256, 1>, 256 * 16, 256, "256x1, 2 WG/CU", 2);
+  one(stream_kernel<MODE, LA, SA, 256, 1, NB>, 256 * 16, 256, "256x1");
+  one(stream_kernel<MODE, LA, SA, 512, 1, NB>, 512 * 16, 512, "512x1");
+  one(stream_kernel<MODE, LA, SA, 1024, 1, NB>, 1024 * 16, 1024, "1024x1");
+  if (NB <= 8) one(stream_kernel<MODE, LA, SA, 256, 4, NB>, 256 * 64, 256, "256x4");
+  one(stream_kernel<MODE, LA, SA, 256, 1, NB>, 256 * 16, 256, "256x1, 6 WG/CU", 6);
+  one(stream_kernel<MODE, LA, SA, 256, 1, NB>, 256 * 16, 256, "256x1, 5 WG/CU", 5);
+  one(stream_kernel<MODE, LA, SA, 256, 1, NB>, 256 * 16, 256, "256x1, 4 WG/CU", 4);
+  one(stream_kernel<MODE, LA, SA, 256, 1, NB>, 256 * 16, 256, "256x1, 3 WG/CU", 3);
+  one(stream_kernel<MODE, LA, SA, 256, 1, NB>, 256 * 16, 256, "256x1, 2 WG/CU", 2);
   return best;
 }
 
@@ -214,6 +216,7 @@ int main() {
   const Best w8_plain = measure<4, 0, 0>(src, dst, sink, bytes, double(bytes));
   const Best w8_nt = measure<4, 0, 2>(src, dst, sink, bytes, double(bytes));
   const Best r8w1 = measure<5, 2, 16>(src, dst, sink, bytes, bytes + bytes / 8.0);
+  const Best r16w1 = measure<5, 2, 16, 16>(src, dst, sink, bytes, bytes + bytes / 16.0);
   const Best r8w8o = measure<7, 2, 2>(src, dst, sink, bytes, 2.0 * bytes);
   const Best r8w8 = measure<6, 2, 2>(src, dst, sink, bytes, 2.0 * bytes);  // last: it rewrites src
   printf("{\"ceilings\": \"HBM streaming, 2 GiB buffers; per pattern the best of 256x1, 512x1, 1024x1, "
@@ -232,6 +235,7 @@ int main() {
   put("write_8_buffers", w8_plain);
   put("write_8_buffers_nt", w8_nt);
   put("read_8_sum_write_1", r8w1);
+  put("read_16_sum_write_1", r16w1);
   put("read_8_sum_write_8_in_place", r8w8);
   put("read_8_sum_write_8_other_buffers", r8w8o);
   put("read_nt_zeroed_buffer", r_nt_zero);

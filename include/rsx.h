@@ -170,6 +170,26 @@ rsx_status_t rsx_all_reduce(const void* const* sendbufs, void* const* recvbufs,
                             rsx_algo_t algo, hipStream_t stream);
 
 /*
+ * Bucketed all-reduce ["Distributed primitives", In practice: the gradient
+ * is all-reduced in buckets, one after another].
+ *
+ * The `count` elements of every rank are cut into consecutive buckets of
+ * bucket_elems elements, the last one shorter: bucket b = [b*bucket_elems,
+ * min((b+1)*bucket_elems, count)).  Each bucket is an rsx_all_reduce of its
+ * own, with its own segments (S = ceil(len/W), ring order per segment) and
+ * its own RSX_ALGO_AUTO choice, launched in bucket order on `stream`.  The
+ * result equals rsx_all_reduce on each bucket in turn.
+ * Arguments, ownership, in-place and aliasing rules: as rsx_all_reduce, on
+ * the whole buffers.  bucket_elems = 0: RSX_ERR_INVALID_ARGUMENT.
+ * RSX_ALGO_RING_SPLIT needs W to divide every bucket (RSX_ERR_UNSUPPORTED).
+ * The whole call is validated before the first launch.
+ */
+rsx_status_t rsx_all_reduce_bucketed(const void* const* sendbufs, void* const* recvbufs,
+                                     int nranks, size_t count, size_t bucket_elems,
+                                     rsx_dtype_t dtype, rsx_op_t op, rsx_algo_t algo,
+                                     hipStream_t stream);
+
+/*
  * Tensor-fusion pack [SG fusedSynch(send=false); HV PerformOperation memcpy in].
  *
  * Copies tensors[i] (device, counts[i] elements) to

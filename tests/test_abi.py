@@ -184,6 +184,36 @@ def test_null_device_pointer(lib):
     assert _ar(lib, [A, A + MB], [A + 2 * MB, None], 2, 4) == 1
 
 
+def _arb(lib, sends, recvs, w, n, bucket, dt=0, op=0, algo=0):
+    return lib.rsx_all_reduce_bucketed(_arr(sends), _arr(recvs), w, n, bucket, dt, op, algo, None)
+
+
+@fake_ptrs
+def test_bucketed_all_reduce_validation(lib):
+    # The same checks as one all-reduce over the whole buffers, all before the
+    # first bucket's launch; plus the bucket size and, for the two-pass form,
+    # W dividing every bucket.
+    s, r = [A, A + MB], [A + 2 * MB, A + 3 * MB]
+    assert _arb(lib, s, r, 2, 1000, 0) == 1                               # no bucket size
+    assert _arb(lib, s, r, 2, 0, 100) == 0                                # nothing to do
+    assert lib.rsx_all_reduce_bucketed(None, _arr(r), 2, 1000, 100, 0, 0, 0, None) == 1
+    assert _arb(lib, s, r, 0, 1000, 100) == 1 and _arb(lib, s, r, 17, 1000, 100) == 1
+    assert _arb(lib, s, r, 2, 1000, 100, dt=9) == 2
+    assert _arb(lib, s, r, 2, 1000, 100, op=7) == 3
+    assert _arb(lib, s, r, 2, 1000, 100, algo=9) == 1
+    assert _arb(lib, s, [A + 2 * MB, A + 2 * MB + 64], 2, 1000, 100) == 5  # outputs overlap
+    assert _arb(lib, s, [A + 8, r[1]], 2, 1000, 100) == 5                 # output inside an input
+    assert _arb(lib, [A + 2, A + MB], r, 2, 1000, 100) == 1               # misaligned fp32 input
+    # two passes: W must divide every bucket (1000 = 3 * 300 + 100; 300 % 3 == 0, 100 % 3 != 0)
+    s3, r3 = [A, A + MB, A + 2 * MB], [A + 3 * MB, A + 4 * MB, A + 5 * MB]
+    assert _arb(lib, s3, r3, 3, 1000, 300, algo=L.RSX_ALGO_RING_SPLIT) == 4
+    assert _arb(lib, s3, r3, 3, 900, 301, algo=L.RSX_ALGO_RING_SPLIT) == 4
+    assert _arb(lib, s3, r3, 3, 1000, 10 ** 30 % 2 ** 60, algo=L.RSX_ALGO_RING_SPLIT) == 4
+    # one rank in place: valid and nothing to launch, whatever the bucket size
+    assert _arb(lib, [A], [A], 1, 1000, 7) == 0
+    assert _arb(lib, [A], [A], 1, 1000, 2 ** 63) == 0
+
+
 @fake_ptrs
 def test_pointers_must_be_element_aligned(lib):
     # A buffer that does not start at a multiple of its element size is refused

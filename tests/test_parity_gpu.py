@@ -799,6 +799,38 @@ def test_full_c4_int32(op):
         assert_parity(to_host(dev[r], "i32"), want[r], "i32", f"ar rank {r}")
 
 
+@pytest.mark.parametrize("dtype,op,w,n,bucket,algo", [
+    ("bf16", "avg", 8, 3 * 8192 + 4096 + 8, 8192, "ring"),       # ragged last bucket
+    ("f32", "sum", 3, 100_003, 7 * 4096 + 1, "ring"),            # buckets not a multiple of W
+    ("f32", "sum", 4, 4 * 30_000, 4 * 7_000, "ring_split"),      # W divides every bucket
+    ("i32", "max", 16, 50_000, 3_000, "auto"),                    # small buckets: naive per bucket
+    ("f16", "prod", 5, 20_000, 20_000, "naive"),                  # one bucket
+    ("f32h", "sum", 2, 9_000, 2_500, "ring"),                    # half wire
+    ("f32", "sum", 4, 1_000, 10 ** 9, "ring"),                    # bucket above count
+])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_all_reduce_bucketed_entry(dtype, op, w, n, bucket, algo, in_place):
+    # rsx_all_reduce_bucketed against the oracle's bucket-by-bucket all-reduce
+    xs = inputs(60, w, n, dtype)
+    dev = [to_dev(x, dtype) for x in xs]
+    out = None if in_place else [empty(n, dtype, fill=0x55) for _ in range(w)]
+    say(f"bucketed entry dtype={dtype} op={op} w={w} n={n} bucket={bucket} algo={algo} in_place={in_place}")
+    rsx.all_reduce_bucketed(dev, out, bucket, op, algo, wire=wire(dtype))
+    torch.cuda.synchronize()
+    ref_algo = "naive" if algo == "naive" else "ring"
+    want = [np.empty_like(x) for x in xs]
+    for b0 in range(0, n, bucket):
+        b1 = min(b0 + bucket, n)
+        part = [x[b0:b1] for x in xs]
+        nbytes = (b1 - b0) * ES[dtype]
+        naive = ref_algo == "naive" or (algo == "auto" and nbytes <= RSX_NAIVE_MAX_BYTES)
+        res = (oracle.naive_all_reduce if naive else oracle.all_reduce)(part, op, dtype)
+        for r in range(w):
+            want[r][b0:b1] = res[r]
+    for r in range(w):
+        assert_parity(to_host((dev if in_place else out)[r], dtype), want[r], dtype, f"rank {r}")
+
+
 def test_full_c3_bf16_bucketed_avg():
     w = wl.WORKLOADS[3]
     say("full cfg=3: generating")
