@@ -83,7 +83,7 @@ def cpu_baseline_threaded(xs, reps_budget_s: float):
 
     import oracle
 
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    threads = cpu_threads()[0]
     w = len(xs)
     s = len(xs[0]) // w
     step = -(-s // threads)
@@ -841,6 +841,7 @@ def main() -> int:
         same_t = all(np.array_equal(a.view(np.uint32), b.view(np.uint32)) for a, b in zip(want_t, want))
         result["cpu_baseline"]["threaded"] = {
             "value": round(bytes_per_step / t_thr / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "affinity_cores": cpu_threads()[1],
             "sample": f"the same workload, each segment's fold split over {threads} threads, "
                       f"{reps_t} passes, median {t_thr:.3f} s; bit-identical to the single-threaded "
                       f"oracle: {same_t}"}
