@@ -430,6 +430,33 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
                 "the whole workload: pack, all-reduce and unpack of every rank",
                 lambda a, b: all(_same_arrays(x, y) for x, y in zip(a, b)))
         return res
+    if name == "all_gather":
+        # W = 8 pieces of 8,388,608 fp32 (32 MiB) gathered into 8 outputs of 256 MiB
+        world, n = 8, 8388608
+        gen = np.random.default_rng((8, 0))
+        pieces_h = [gen.standard_normal(n, dtype=np.float32) for _ in range(world)]
+        _, pieces = _arena(torch, torch.float32, world, n)
+        for d, x in zip(pieces, pieces_h):
+            d.copy_(torch.from_numpy(x))
+        _, out = _arena(torch, torch.float32, world, world * n)
+        in_place_src = [out[k][k * n:(k + 1) * n] for k in range(world)]
+        res = {"workload": "all-gather fp32, W=8, pieces of 8,388,608 (32 MiB) into outputs of 256 MiB",
+               "out_of_place": _stat(time_launches(lambda: rsx.all_gather(pieces, out), reps, warm, torch),
+                                     world * n * 4 + world * world * n * 4),
+               "in_place": _stat(time_launches(lambda: rsx.all_gather(in_place_src, out), reps, warm, torch),
+                                 world * n * 4 + world * (world - 1) * n * 4)}
+        got = out[world - 1].cpu().numpy()
+        res["check_last_rank_equals_concatenation"] = bool(np.array_equal(got, np.concatenate(pieces_h)))
+        if not args.no_cpu_baseline:
+            import oracle
+
+            def threaded(ex, t):
+                return list(ex.map(lambda r: np.concatenate(pieces_h), range(world)))
+            res["out_of_place"]["cpu_baseline"] = oracle_baseline(
+                lambda: oracle.all_gather(pieces_h), threaded, world * n * 4 + world * world * n * 4,
+                args.cpu_seconds / 2, "the whole workload (the oracle concatenates the pieces once per rank)",
+                _same_arrays)
+        return res
     if name == "sweep":
         res = {"workload": "all-reduce sum fp32, W=4, 1-32 KiB per rank: naive vs ring"}
         for kib in wl.SWEEP_KIB:
@@ -697,7 +724,7 @@ def main() -> int:
     ap.add_argument("--layout", choices=("arena", "separate"), default="arena")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--workload", default="rs_w8_f32",
-                    choices=("rs_w8_f32", "small", "bf16_bucketed", "int32_w16", "fused", "sweep",
+                    choices=("rs_w8_f32", "small", "bf16_bucketed", "int32_w16", "fused", "sweep", "all_gather",
                              "sparse", "sparse_sweep", "dtypes", "overlap", "size_sweep", "ceilings"),
                     help="rs_w8_f32 (default) is the headline line; the others print timings only")
     args = ap.parse_args()

@@ -49,11 +49,13 @@ struct Unit<8> {
 
 // ------------------------------------------------------------ all-gather
 
-template <int ES, bool VEC>
-__global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a) {
+// TPW tiles per workgroup: with TPW = 2, a workgroup of 512 lanes copies two
+// consecutive tiles, one per half (workgroup_tile).
+template <int ES, bool VEC, int TPW>
+__global__ __launch_bounds__(kBlock * TPW) void gather_kernel(const GatherArgs a) {
   using T = typename std::conditional<VEC, uint4, typename Unit<ES>::T>::type;
   constexpr int U = kCopyUnits;
-  const uint32_t t = xcd_tile(blockIdx.x, gridDim.x);
+  const uint32_t t = workgroup_tile<TPW>();
   if (t >= a.tiles_total) return;
   const uint32_t k = static_cast<uint32_t>((static_cast<uint64_t>(t) * a.tps_magic) >> a.tps_shift);
   const uint32_t tile = t - k * a.tiles_per_piece;
@@ -61,7 +63,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a) {
   const uint64_t nu = nbytes / sizeof(T);
   const uint64_t t0 = static_cast<uint64_t>(tile) * (U * kBlock);
   if (t0 >= nu) return;
-  const uint32_t tid = threadIdx.x;
+  const uint32_t tid = TPW == 1 ? threadIdx.x : threadIdx.x % kBlock;
   const char* srcb = static_cast<const char*>(a.src[k]);
   if constexpr (VEC) {
     // Whole 16-byte vectors; the descriptor range drops lanes past the piece.
@@ -95,21 +97,25 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const GatherArgs a) {
   }
 }
 
-hipError_t launch_gather(int esize, bool vec, const GatherArgs& a, dim3 grid, uint32_t lds, hipStream_t s) {
+// Two tiles per workgroup exist for the dwordx4 kernel only.
+hipError_t launch_gather(int esize, bool vec, int tpw, const GatherArgs& a, dim3 grid, uint32_t lds,
+                         hipStream_t s) {
   void* args[] = {const_cast<GatherArgs*>(&a)};
+  if (tpw != 1 && !(tpw == 2 && vec)) return hipErrorInvalidValue;
   const void* fn;
   switch (esize) {
-#define RSX_ES(n)                                                              \
-  case n:                                                                      \
-    fn = vec ? reinterpret_cast<const void*>(&gather_kernel<n, true>)          \
-             : reinterpret_cast<const void*>(&gather_kernel<n, false>);        \
+#define RSX_ES(n)                                                                     \
+  case n:                                                                             \
+    fn = !vec        ? reinterpret_cast<const void*>(&gather_kernel<n, false, 1>)     \
+         : tpw == 2 ? reinterpret_cast<const void*>(&gather_kernel<n, true, 2>)       \
+                    : reinterpret_cast<const void*>(&gather_kernel<n, true, 1>);      \
     break;
     RSX_ES(1) RSX_ES(2) RSX_ES(4) RSX_ES(8)
 #undef RSX_ES
     default:
       return hipErrorInvalidValue;
   }
-  return hipLaunchKernel(fn, grid, dim3(kBlock), args, lds, s);
+  return hipLaunchKernel(fn, grid, dim3(kBlock * tpw), args, lds, s);
 }
 
 // -------------------------------------------------------- pack / unpack

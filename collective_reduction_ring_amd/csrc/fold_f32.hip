@@ -3,9 +3,9 @@
 
 namespace rsx {
 
-hipError_t launch_fold_f32(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid, uint32_t lds,
+hipError_t launch_fold_f32(int op, int world, bool rs, bool vec, int tpw, const FoldArgs& a, dim3 grid, uint32_t lds,
                            hipStream_t s) {
-  return launch_fold<F32T>(op, world, rs, vec, a, grid, lds, s);
+  return launch_fold<F32T>(op, world, rs, vec, tpw, a, grid, lds, s);
 }
 
 hipError_t launch_list_f32(int op, int world, const ListArgs& a, dim3 grid, uint32_t lds, hipStream_t s) {

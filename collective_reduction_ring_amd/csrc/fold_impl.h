@@ -358,11 +358,10 @@ __device__ __forceinline__ uint4 fold_vectors(const uint4 (&v)[W]) {
 template <class D, int OP, int W, int ND, int STORE_AUX, bool VEC, bool WHOLE>
 __device__ __forceinline__ void fold_tile(const typename D::S* const (&src)[W],
                                           typename D::S* const (&dst)[ND], uint64_t shift,
-                                          uint64_t b, uint64_t e, uint32_t tile) {
+                                          uint64_t b, uint64_t e, uint32_t tile, uint32_t tid) {
   using S = typename D::S;
   constexpr int U = fold_units(W);
   constexpr int VL = D::kVL;
-  const uint32_t tid = threadIdx.x;
 
   auto fold_element = [&](uint64_t idx) {
     S x[W];
@@ -436,9 +435,11 @@ __device__ __forceinline__ void fold_tile(const typename D::S* const (&src)[W],
 
 // ------------------------------------------------------------------ kernels
 
-// Reduce-scatter (RS) or all-reduce over W rank buffers (FoldArgs).
-template <class D, int OP, int W, bool RS, bool VEC>
-__global__ __launch_bounds__(kBlock) void fold_kernel(const FoldArgs a) {
+// Reduce-scatter (RS) or all-reduce over W rank buffers (FoldArgs).  TPW
+// tiles per workgroup: with TPW = 2, a workgroup of 512 lanes runs two
+// consecutive tiles of 256 lanes, one per half (see pair_tiles).
+template <class D, int OP, int W, bool RS, bool VEC, int TPW>
+__global__ __launch_bounds__(kBlock * TPW) void fold_kernel(const FoldArgs a) {
   using S = typename D::S;
 
   // Every scalar argument in one round of kernarg loads.  A workgroup runs a
@@ -450,7 +451,8 @@ __global__ __launch_bounds__(kBlock) void fold_kernel(const FoldArgs a) {
   const uint32_t tps = a.tiles_per_seg;
   const uint32_t rot = RS ? 1u : a.rot;
   const uint64_t seg = a.seg, count = a.count;
-  const uint32_t t = xcd_tile(blockIdx.x, gridDim.x);
+  const uint32_t t = workgroup_tile<TPW>();
+  const uint32_t tid = TPW == 1 ? threadIdx.x : threadIdx.x % kBlock;
   asm volatile("" ::"s"(magic), "s"(shift), "s"(tps), "s"(rot), "s"(seg), "s"(count), "s"(t));
   if (t >= tiles_total) return;
   const uint32_t k = static_cast<uint32_t>((static_cast<uint64_t>(t) * magic) >> shift);
@@ -471,12 +473,12 @@ __global__ __launch_bounds__(kBlock) void fold_kernel(const FoldArgs a) {
 
   if constexpr (RS) {
     S* const dst[1] = {static_cast<S*>(a.dst[k])};
-    fold_tile<D, OP, W, 1, kStoreThrough, VEC, true>(src, dst, b, b, e, tile);
+    fold_tile<D, OP, W, 1, kStoreThrough, VEC, true>(src, dst, b, b, e, tile, tid);
   } else {
     S* dst[W];
 #pragma unroll
     for (int d = 0; d < W; ++d) dst[d] = static_cast<S*>(a.dst[d]);
-    fold_tile<D, OP, W, W, kStoreStream, VEC, false>(src, dst, 0, b, e, tile);
+    fold_tile<D, OP, W, W, kStoreStream, VEC, false>(src, dst, 0, b, e, tile, tid);
   }
 }
 
@@ -485,7 +487,7 @@ template <class D, int OP, int W>
 __global__ __launch_bounds__(kBlock) void list_fold_kernel(const ListArgs a) {
   using S = typename D::S;
   const uint32_t n = a.npieces;
-  const uint32_t t = xcd_tile(blockIdx.x, gridDim.x);
+  const uint32_t t = xcd_tile(blockIdx.x, gridDim.x);  // one tile per workgroup
   if (t >= a.tile_start[n]) return;
   // Piece of this tile: the last i with tile_start[i] <= t.
   uint32_t lo = 0, hi = n - 1;
@@ -509,34 +511,42 @@ __global__ __launch_bounds__(kBlock) void list_fold_kernel(const ListArgs a) {
     dst[j] = static_cast<S*>(a.ptr[dbase + j]);
   }
   if (pc.vec) {
-    fold_tile<D, OP, W, W, kStoreStream, true, false>(src, dst, 0, pc.lo, pc.hi, tile);
+    fold_tile<D, OP, W, W, kStoreStream, true, false>(src, dst, 0, pc.lo, pc.hi, tile, threadIdx.x);
   } else {
-    fold_tile<D, OP, W, W, kStoreStream, false, false>(src, dst, 0, pc.lo, pc.hi, tile);
+    fold_tile<D, OP, W, W, kStoreStream, false, false>(src, dst, 0, pc.lo, pc.hi, tile, threadIdx.x);
   }
 }
 
 // --------------------------------------------------------------- dispatch
 
+// Two tiles per workgroup exist for the dwordx4 all-reduce only (the launch
+// chooses them; see rsx_abi.hip).
 template <class D, int OP, int W>
-hipError_t launch_world(bool rs, bool vec, const FoldArgs& a, dim3 grid, uint32_t lds, hipStream_t s) {
+hipError_t launch_world(bool rs, bool vec, int tpw, const FoldArgs& a, dim3 grid, uint32_t lds,
+                        hipStream_t s) {
   void* args[] = {const_cast<FoldArgs*>(&a)};
   const void* fn;
-  if (rs) {
-    fn = vec ? reinterpret_cast<const void*>(&fold_kernel<D, OP, W, true, true>)
-             : reinterpret_cast<const void*>(&fold_kernel<D, OP, W, true, false>);
+  if (!rs && vec && tpw == 2) {
+    fn = reinterpret_cast<const void*>(&fold_kernel<D, OP, W, false, true, 2>);
+  } else if (tpw != 1) {
+    return hipErrorInvalidValue;
+  } else if (rs) {
+    fn = vec ? reinterpret_cast<const void*>(&fold_kernel<D, OP, W, true, true, 1>)
+             : reinterpret_cast<const void*>(&fold_kernel<D, OP, W, true, false, 1>);
   } else {
-    fn = vec ? reinterpret_cast<const void*>(&fold_kernel<D, OP, W, false, true>)
-             : reinterpret_cast<const void*>(&fold_kernel<D, OP, W, false, false>);
+    fn = vec ? reinterpret_cast<const void*>(&fold_kernel<D, OP, W, false, true, 1>)
+             : reinterpret_cast<const void*>(&fold_kernel<D, OP, W, false, false, 1>);
   }
-  return hipLaunchKernel(fn, grid, dim3(kBlock), args, lds, s);
+  return hipLaunchKernel(fn, grid, dim3(kBlock * tpw), args, lds, s);
 }
 
 template <class D, int OP>
-hipError_t launch_op(int world, bool rs, bool vec, const FoldArgs& a, dim3 grid, uint32_t lds, hipStream_t s) {
+hipError_t launch_op(int world, bool rs, bool vec, int tpw, const FoldArgs& a, dim3 grid, uint32_t lds,
+                     hipStream_t s) {
   switch (world) {
 #define RSX_W(n) \
   case n:        \
-    return launch_world<D, OP, n>(rs, vec, a, grid, lds, s);
+    return launch_world<D, OP, n>(rs, vec, tpw, a, grid, lds, s);
     RSX_W(1) RSX_W(2) RSX_W(3) RSX_W(4) RSX_W(5) RSX_W(6) RSX_W(7) RSX_W(8)
     RSX_W(9) RSX_W(10) RSX_W(11) RSX_W(12) RSX_W(13) RSX_W(14) RSX_W(15) RSX_W(16)
 #undef RSX_W
@@ -582,19 +592,19 @@ hipError_t launch_list(int op, int world, const ListArgs& a, dim3 grid, uint32_t
 }
 
 template <class D>
-hipError_t launch_fold(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid, uint32_t lds,
-                       hipStream_t s) {
+hipError_t launch_fold(int op, int world, bool rs, bool vec, int tpw, const FoldArgs& a, dim3 grid,
+                       uint32_t lds, hipStream_t s) {
   switch (op) {
     case RSX_SUM:
-      return launch_op<D, RSX_SUM>(world, rs, vec, a, grid, lds, s);
+      return launch_op<D, RSX_SUM>(world, rs, vec, tpw, a, grid, lds, s);
     case RSX_MAX:
-      return launch_op<D, RSX_MAX>(world, rs, vec, a, grid, lds, s);
+      return launch_op<D, RSX_MAX>(world, rs, vec, tpw, a, grid, lds, s);
     case RSX_MIN:
-      return launch_op<D, RSX_MIN>(world, rs, vec, a, grid, lds, s);
+      return launch_op<D, RSX_MIN>(world, rs, vec, tpw, a, grid, lds, s);
     case RSX_AVG:
-      return launch_op<D, RSX_AVG>(world, rs, vec, a, grid, lds, s);
+      return launch_op<D, RSX_AVG>(world, rs, vec, tpw, a, grid, lds, s);
     case RSX_PROD:
-      return launch_op<D, RSX_PROD>(world, rs, vec, a, grid, lds, s);
+      return launch_op<D, RSX_PROD>(world, rs, vec, tpw, a, grid, lds, s);
     default:
       return hipErrorInvalidValue;
   }

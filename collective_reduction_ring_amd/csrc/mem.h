@@ -41,6 +41,21 @@ __device__ __forceinline__ uint32_t xcd_tile(uint32_t b, uint32_t nblocks) {
   return (b % kXcds) * per + b / kXcds;
 }
 
+// Tile of this wave's half of the workgroup when a workgroup of TPW * 256
+// lanes runs TPW consecutive tiles of 256 lanes (workgroup b takes tiles
+// TPW * xcd_tile(b) ..., so each XCD's region stays contiguous).  The half
+// index is the same for all 64 lanes of a wave; readfirstlane makes that
+// explicit, so the tile and everything derived from it stay scalar.
+template <int TPW>
+__device__ __forceinline__ uint32_t workgroup_tile() {
+  const uint32_t base = xcd_tile(blockIdx.x, gridDim.x) * TPW;
+  if constexpr (TPW == 1) {
+    return base;
+  } else {
+    return base + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / 256u)));
+  }
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
                                            kRawBufferWord3);

@@ -76,10 +76,11 @@ bool valid_op(int op) { return op >= RSX_SUM && op <= RSX_PROD; }
 constexpr uint32_t kLdsPerCu = 160u * 1024u;
 thread_local bool t_caps = true;
 uint32_t lds_for_cap(uint32_t wg_per_cu) {
-  return (!t_caps || wg_per_cu >= 8) ? 0u : (kLdsPerCu / wg_per_cu) & ~1023u;
+  if (!t_caps || wg_per_cu >= 8) return 0u;
+  // One per CU: any reservation above half the CU's LDS does it.
+  if (wg_per_cu == 1) return 96u * 1024u;
+  return (kLdsPerCu / wg_per_cu) & ~1023u;
 }
-uint32_t rs_cap(int w) { return w <= 2 ? 8u : w <= 10 ? 5u : 3u; }
-uint32_t ar_cap(int w) { return w <= 1 ? 8u : w == 2 ? 5u : 3u; }
 uint32_t ag_cap(int w, bool in_place) {
   if (!in_place) return w <= 5 ? 5u : 3u;
   if (w <= 2) return 8u;
@@ -87,29 +88,73 @@ uint32_t ag_cap(int w, bool in_place) {
   return w <= 9 ? 5u : 3u;
 }
 uint32_t list_cap(int w) { return w <= 1 ? 8u : w <= 4 ? 5u : 3u; }
+// Write-heavy kernels (the one-pass all-reduce, the all-gather) run faster
+// at larger W with fewer, larger workgroups: two 256-lane tiles per 512-lane
+// workgroup, one workgroup per CU ("pairs").  Measured in one process, 256
+// MiB per rank, one tile per workgroup at the caps above against pairs:
+//   one-pass all-reduce fp32, W = 3..16: W = 3, 4 +0.9 / +0.8%; W = 5, 6, 7,
+//     8 +3.0 / +5.0 / +5.2 / +1.4%; W = 10, 12, 14, 16 +1.6 / +2.3 / -0.7 /
+//     +1.7% (W = 8 at 256 MiB per rank: 732 -> 722 us; other boxes 735 ->
+//     682-715 us);
+//   all-gather out of place, W = 6, 7, 8: +14.7 / +14.3 / +8.9% (W = 8:
+//     448 -> 409 us); W = 10..16: -0.6 .. +3.7%; W <= 5: -3 .. -18%;
+//   all-gather in place, W = 7, 8: +5.9 / +10.1%; W = 10..16: +2.1 .. +4.8%;
+//     W = 6: -2.5%; W <= 5: -11 .. -47%.
+// Pairs at two workgroups per CU lose almost everywhere (up to -16%), and the
+// reduce-scatter loses with pairs (W = 8: 369 -> 379 us at two per CU, 433
+// us at one).  Pairs are a form of the occupancy cap: with the caps off
+// (launches that overlap other work) every kernel runs one tile per
+// workgroup.
+bool ar_pairs(int w) { return t_caps && w >= 5; }
+// The ring all-reduce as two passes (a reduce-scatter, then an all-gather in
+// place) against one pass, whole calls, same process (fp32 and bf16; ratio
+// of two-pass to one-pass time): W = 8, 4 / 16 / 64 / 256 MiB per rank:
+// 0.96 / 0.91 / 0.97 / 0.97 (256 MiB: 721 -> 699 us); W = 7, 10, 12 from 4
+// MiB: 0.92 .. 1.0; W = 16: 0.93-0.95 at 4 MiB, 0.97 at 128 MiB (int32,
+// 774 -> 752 us), 0.95-0.97 at 256 MiB, but 1.06 at 64 MiB; W <= 6: one
+// pass ahead (up to 8%); below 4 MiB per rank the second launch costs more
+// than it saves (1 MiB: 1.2-1.5).  Without the occupancy caps the
+// all-gather has no pairs and one pass is kept.
+bool two_passes_pay(int w, size_t count, size_t es, bool vec) {
+  const size_t seg = count / static_cast<size_t>(w);
+  return t_caps && vec && w >= 7 && count % static_cast<size_t>(w) == 0 && (seg * es) % kVecBytes == 0 &&
+         count * es >= (4u << 20);
+}
+// All-gather: tiles per workgroup and workgroups per CU.
+void ag_shape(int w, bool in_place, int* tpw, uint32_t* cap) {
+  if (t_caps && (w >= 7 || (w == 6 && !in_place))) {
+    *tpw = 2;
+    *cap = 1;
+    return;
+  }
+  *tpw = 1;
+  *cap = ag_cap(w, in_place);
+}
+uint32_t rs_cap(int w) { return w <= 2 ? 8u : w <= 10 ? 5u : 3u; }
+uint32_t ar_cap(int w) { return w <= 1 ? 8u : w == 2 ? 5u : 3u; }
 
 // Per element type launchers (one translation unit each).
-hipError_t launch_fold_by_type(int dtype, int op, int world, bool rs, bool vec, const FoldArgs& a,
+hipError_t launch_fold_by_type(int dtype, int op, int world, bool rs, bool vec, int tpw, const FoldArgs& a,
                                dim3 grid, uint32_t lds, hipStream_t s) {
   switch (dtype) {
     case RSX_FLOAT32:
-      return launch_fold_f32(op, world, rs, vec, a, grid, lds, s);
+      return launch_fold_f32(op, world, rs, vec, tpw, a, grid, lds, s);
     case RSX_BFLOAT16:
-      return launch_fold_bf16(op, world, rs, vec, a, grid, lds, s);
+      return launch_fold_bf16(op, world, rs, vec, tpw, a, grid, lds, s);
     case RSX_INT32:
-      return launch_fold_i32(op, world, rs, vec, a, grid, lds, s);
+      return launch_fold_i32(op, world, rs, vec, tpw, a, grid, lds, s);
     case RSX_FLOAT64:
-      return launch_fold_f64(op, world, rs, vec, a, grid, lds, s);
+      return launch_fold_f64(op, world, rs, vec, tpw, a, grid, lds, s);
     case RSX_FLOAT16:
-      return launch_fold_f16(op, world, rs, vec, a, grid, lds, s);
+      return launch_fold_f16(op, world, rs, vec, tpw, a, grid, lds, s);
     case RSX_INT64:
-      return launch_fold_i64(op, world, rs, vec, a, grid, lds, s);
+      return launch_fold_i64(op, world, rs, vec, tpw, a, grid, lds, s);
     case RSX_UINT64:
-      return launch_fold_u64(op, world, rs, vec, a, grid, lds, s);
+      return launch_fold_u64(op, world, rs, vec, tpw, a, grid, lds, s);
     case RSX_INT8:
-      return launch_fold_i8(op, world, rs, vec, a, grid, lds, s);
+      return launch_fold_i8(op, world, rs, vec, tpw, a, grid, lds, s);
     case RSX_FLOAT32_HALF_WIRE:
-      return launch_fold_f32h(op, world, rs, vec, a, grid, lds, s);
+      return launch_fold_f32h(op, world, rs, vec, tpw, a, grid, lds, s);
     default:
       return hipErrorInvalidValue;
   }
@@ -191,9 +236,12 @@ rsx_status_t launch_fold_any(int dtype, int op, int world, bool rs, bool vec, Fo
   a.tiles_per_seg = static_cast<uint32_t>(tiles_per_seg);
   a.tiles_total = static_cast<uint32_t>(total);
   split_magic(a.tiles_per_seg, &a.tps_magic, &a.tps_shift);
-  const dim3 grid(static_cast<uint32_t>(xcd_grid(total)));
-  const uint32_t lds = vec ? lds_for_cap(rs ? rs_cap(world) : ar_cap(world)) : 0u;
-  return hip_status(launch_fold_by_type(dtype, op, world, rs, vec, a, grid, lds, s));
+  // The dwordx4 all-reduce at W >= 5 runs two tiles per workgroup, one
+  // workgroup per CU (ar_pairs); everything else one tile per workgroup.
+  const int tpw = (!rs && vec && ar_pairs(world)) ? 2 : 1;
+  const dim3 grid(static_cast<uint32_t>(xcd_grid((total + tpw - 1) / tpw)));
+  const uint32_t lds = !vec ? 0u : tpw == 2 ? lds_for_cap(1) : lds_for_cap(rs ? rs_cap(world) : ar_cap(world));
+  return hip_status(launch_fold_by_type(dtype, op, world, rs, vec, tpw, a, grid, lds, s));
 }
 
 // All-gather launch over validated buffers: piece k = src[k] goes to
@@ -224,9 +272,12 @@ rsx_status_t launch_gather_any(const void* const* src, void* const* dst, int nra
   a.tiles_per_piece = static_cast<uint32_t>(tiles);
   a.tiles_total = static_cast<uint32_t>(total);
   split_magic(a.tiles_per_piece, &a.tps_magic, &a.tps_shift);
-  return hip_status(launch_gather(static_cast<int>(es), vec, a,
-                                  dim3(static_cast<uint32_t>(xcd_grid(total))),
-                                  vec ? lds_for_cap(ag_cap(nranks, in_place)) : 0u, stream));
+  int tpw = 1;
+  uint32_t cap = 8;  // the element-wise kernel runs uncapped
+  if (vec) ag_shape(nranks, in_place, &tpw, &cap);
+  return hip_status(launch_gather(static_cast<int>(es), vec, tpw, a,
+                                  dim3(static_cast<uint32_t>(xcd_grid((total + tpw - 1) / tpw))),
+                                  lds_for_cap(cap), stream));
 }
 
 // Shared validation of the pointer arrays and enums of the collectives.
@@ -588,19 +639,18 @@ rsx_status_t all_reduce_launch(const void* const* sendbufs, void* const* recvbuf
   const bool naive = algo == RSX_ALGO_NAIVE || (algo == RSX_ALGO_AUTO && bytes <= RSX_NAIVE_MAX_BYTES);
   bool vec = true;
   for (int r = 0; r < nranks; ++r) vec = vec && aligned16(sendbufs[r]) && aligned16(recvbufs[r]);
+  const bool split = algo == RSX_ALGO_RING_SPLIT ||
+                     (!naive && algo != RSX_ALGO_RING_FUSED && two_passes_pay(nranks, count, es, vec));
 
-  // Two passes on request ("Distributed primitives": Ring AllReduce =
-  // ReduceScatter + AllGather): the reduce-scatter stores segment k into
-  // recvbufs[k] at its own offset, and the all-gather copies it from there to
-  // the other ranks.  Each lane of the reduce-scatter reads its element of
-  // every input before it stores, and touches no other segment, so every
-  // alias the one-pass form accepts is still safe; the all-gather runs after
-  // the last read of the inputs, in stream order.  With the occupancy caps
-  // the two forms are within a few percent of each other as whole calls
-  // (W = 8 fp32, 256 MiB per rank: 734 against 729 us; W = 4: one pass up
-  // to 9% ahead; W = 16 at 256 MiB: two passes 4% ahead), so RSX_ALGO_RING
-  // takes the one-pass form, which moves the fewest bytes.
-  if (algo == RSX_ALGO_RING_SPLIT) {
+  // Two passes ("Distributed primitives": Ring AllReduce = ReduceScatter +
+  // AllGather): the reduce-scatter stores segment k into recvbufs[k] at its
+  // own offset, and the all-gather copies it from there to the other ranks.
+  // Each lane of the reduce-scatter reads its element of every input before
+  // it stores, and touches no other segment, so every alias the one-pass
+  // form accepts is still safe; the all-gather runs after the last read of
+  // the inputs, in stream order.  RSX_ALGO_RING takes this form where it
+  // measured faster (two_passes_pay), RSX_ALGO_RING_SPLIT always.
+  if (split) {
     const size_t seg = count / static_cast<size_t>(nranks);
     const bool rs_vec = vec && (seg * es) % kVecBytes == 0;
     FoldArgs a;

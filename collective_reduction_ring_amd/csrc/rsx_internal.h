@@ -145,23 +145,23 @@ struct ListArgs {
 // Launchers, one per dtype translation unit.  `rs` selects the reduce-scatter
 // store (block k to dst[k]) over the all-reduce store (every element to every
 // dst[r]); `vec` selects the dwordx4 kernel.  Return the launch status.
-hipError_t launch_fold_f32(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid, uint32_t lds,
+hipError_t launch_fold_f32(int op, int world, bool rs, bool vec, int tpw, const FoldArgs& a, dim3 grid, uint32_t lds,
                            hipStream_t s);
-hipError_t launch_fold_bf16(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid, uint32_t lds,
+hipError_t launch_fold_bf16(int op, int world, bool rs, bool vec, int tpw, const FoldArgs& a, dim3 grid, uint32_t lds,
                            hipStream_t s);
-hipError_t launch_fold_i32(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid, uint32_t lds,
+hipError_t launch_fold_i32(int op, int world, bool rs, bool vec, int tpw, const FoldArgs& a, dim3 grid, uint32_t lds,
                            hipStream_t s);
-hipError_t launch_fold_f64(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid, uint32_t lds,
+hipError_t launch_fold_f64(int op, int world, bool rs, bool vec, int tpw, const FoldArgs& a, dim3 grid, uint32_t lds,
                            hipStream_t s);
-hipError_t launch_fold_f16(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid, uint32_t lds,
+hipError_t launch_fold_f16(int op, int world, bool rs, bool vec, int tpw, const FoldArgs& a, dim3 grid, uint32_t lds,
                            hipStream_t s);
-hipError_t launch_fold_i64(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid, uint32_t lds,
+hipError_t launch_fold_i64(int op, int world, bool rs, bool vec, int tpw, const FoldArgs& a, dim3 grid, uint32_t lds,
                            hipStream_t s);
-hipError_t launch_fold_u64(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid, uint32_t lds,
+hipError_t launch_fold_u64(int op, int world, bool rs, bool vec, int tpw, const FoldArgs& a, dim3 grid, uint32_t lds,
                            hipStream_t s);
-hipError_t launch_fold_i8(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid, uint32_t lds,
+hipError_t launch_fold_i8(int op, int world, bool rs, bool vec, int tpw, const FoldArgs& a, dim3 grid, uint32_t lds,
                            hipStream_t s);
-hipError_t launch_fold_f32h(int op, int world, bool rs, bool vec, const FoldArgs& a, dim3 grid, uint32_t lds,
+hipError_t launch_fold_f32h(int op, int world, bool rs, bool vec, int tpw, const FoldArgs& a, dim3 grid, uint32_t lds,
                             hipStream_t s);
 hipError_t launch_list_f32(int op, int world, const ListArgs& a, dim3 grid, uint32_t lds, hipStream_t s);
 hipError_t launch_list_bf16(int op, int world, const ListArgs& a, dim3 grid, uint32_t lds, hipStream_t s);
@@ -173,7 +173,8 @@ hipError_t launch_list_u64(int op, int world, const ListArgs& a, dim3 grid, uint
 hipError_t launch_list_i8(int op, int world, const ListArgs& a, dim3 grid, uint32_t lds, hipStream_t s);
 hipError_t launch_list_f32h(int op, int world, const ListArgs& a, dim3 grid, uint32_t lds, hipStream_t s);
 
-hipError_t launch_gather(int esize, bool vec, const GatherArgs& a, dim3 grid, uint32_t lds, hipStream_t s);
+hipError_t launch_gather(int esize, bool vec, int tpw, const GatherArgs& a, dim3 grid, uint32_t lds,
+                         hipStream_t s);
 hipError_t launch_multicopy(int esize, const MultiCopyArgs& a, uint32_t lds, hipStream_t s);
 
 }  // namespace rsx

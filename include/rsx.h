@@ -94,10 +94,11 @@ typedef enum {
 } rsx_op_t;
 
 typedef enum {
-  RSX_ALGO_RING = 0,       /* segment k folded in ring order (k+1)%W, ..., k; then gathered */
+  RSX_ALGO_RING = 0,       /* segment k folded in ring order (k+1)%W, ..., k; then gathered, in
+                              one pass or two (the faster form for the shape; same bits) */
   RSX_ALGO_NAIVE = 1,      /* every element folded in rank order 0..W-1 [MX] */
   RSX_ALGO_AUTO = 2,       /* NAIVE when count * element size <= RSX_NAIVE_MAX_BYTES, else RING */
-  RSX_ALGO_RING_FUSED = 3, /* RING as one pass (fold, then store to every rank); RING takes it too */
+  RSX_ALGO_RING_FUSED = 3, /* RING, always as one pass (fold, then store to every rank) */
   RSX_ALGO_RING_SPLIT = 4  /* RING, always as a reduce-scatter, then an all-gather [DP] */
 } rsx_algo_t;
 
@@ -154,13 +155,15 @@ rsx_status_t rsx_all_gather(const void* const* sendbufs, void* const* recvbufs,
  *   written to every rank: the result equals rsx_all_gather applied to the
  *   reduce-scatter output whenever W divides count.  Two forms give the
  *   same bits (the same folds in the same order):
- *   - one pass (RSX_ALGO_RING, RSX_ALGO_RING_FUSED): each lane folds its
- *     element of all W inputs in registers and stores the result to all W
- *     outputs;
+ *   - one pass (RSX_ALGO_RING_FUSED): each lane folds its element of all W
+ *     inputs in registers and stores the result to all W outputs;
  *   - two passes (RSX_ALGO_RING_SPLIT): a reduce-scatter writes segment k
  *     into recvbufs[k] at its own offset, then an all-gather copies it from
  *     there to the other W-1 outputs, (2W+1)/(2W) of the one-pass bytes.
  *     W must divide count (else RSX_ERR_UNSUPPORTED); any element-aligned address.
+ *   RSX_ALGO_RING takes two passes when W >= 7, W divides count, every
+ *   buffer and segment is 16-byte aligned and a rank holds at least 4 MiB
+ *   (measured faster there), one pass otherwise.
  * RSX_ALGO_NAIVE: every element folded in rank order 0..W-1 [MX].
  * In place: recvbufs[r] == sendbufs[r] for every r (or a permutation of the
  * send buffers) is allowed; other overlaps return RSX_ERR_ALIASING.
