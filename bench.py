@@ -844,7 +844,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": recorded_traffic(),
-            "kernel": "rsx::fold_kernel<F32T, RSX_SUM, 8, rs, dwordx4>",
+            "kernel": "rsx::fold_kernel<F32T, RSX_SUM, 8, reduce-scatter, dwordx4, 1 tile per workgroup>",
             "avg_launch_us": round(avg_launch_s * 1e6, 2),
             "single_launch_median_us": round(statistics.median(launch_ms) * 1e3, 2),
             "algorithmic_bytes_per_launch": bytes_per_step,

@@ -11,6 +11,9 @@
   only while the kernel is unchanged.
 * ``traffic-table``: the same scaled bytes for several kernels of one run, as
   a markdown table against each kernel's algorithmic bytes.
+* ``traffic-grid``: the same, summed over every dispatch of each kernel, with
+  each dispatch's algorithmic bytes from its grid size (for runs that launch
+  one kernel at several sizes).
 
 Usage::
 
@@ -153,6 +156,48 @@ def traffic_table(fetch: str, write: str, cal_fetch: str, cal_write: str, cal_ke
     return "\n".join(lines) + "\n"
 
 
+def _dispatches(path: str, counter: str, kernel: str) -> list[tuple[int, float]]:
+    """(grid size in work-items, counter value) of every dispatch whose name contains `kernel`."""
+    return [(int(r["Grid_Size"]), float(r["Counter_Value"])) for r in _rows(path)
+            if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]]
+
+
+def traffic_grid_table(fetch: str, write: str, cal_fetch: str, cal_write: str, cal_kernel: str,
+                       cal_bytes: int, kernels: list[tuple[str, str, int]], commands: str) -> str:
+    """HBM bytes against algorithmic bytes summed over every dispatch of each kernel.
+
+    `kernels`: (name, "lane" | "dispatch", bytes): the algorithmic bytes of a
+    dispatch are its grid size times `bytes` ("lane": the kernel moves a fixed
+    number of 16-byte vectors per work-item) or `bytes` itself ("dispatch").
+    Summing over dispatches handles runs that launch one kernel at several
+    sizes (buckets of different lengths)."""
+    cf = counter_per_dispatch(cal_fetch, "FETCH_SIZE", cal_kernel)
+    cw = counter_per_dispatch(cal_write, "WRITE_SIZE", cal_kernel)
+    if not (cf and cw):
+        raise SystemExit("missing counter rows for the calibration kernel")
+    f_scale = cal_bytes / (statistics.mean(cf) * 1024.0)
+    w_scale = cal_bytes / (statistics.mean(cw) * 1024.0)
+    lines = ["# rocprofv3 HBM traffic, summed over every dispatch", "", "Commands:", "", "```", commands, "```",
+             "", f"Scale factors from the calibration kernel `{cal_kernel}` ({cal_bytes} bytes read and written "
+             f"per dispatch): FETCH_SIZE x {f_scale:.5f}, WRITE_SIZE x {w_scale:.5f}.", "",
+             "| kernel | dispatches | grid sizes | fetch bytes | write bytes | traffic | algorithmic | "
+             "traffic / algorithmic |", "|---|---|---|---|---|---|---|---|"]
+    for kernel, unit, nbytes in kernels:
+        f = _dispatches(fetch, "FETCH_SIZE", kernel)
+        w = _dispatches(write, "WRITE_SIZE", kernel)
+        if not (f and w):
+            raise SystemExit(f"missing counter rows for {kernel}")
+        fb = sum(v for _, v in f) * 1024.0 * f_scale
+        wb = sum(v for _, v in w) * 1024.0 * w_scale
+        if sorted(g for g, _ in f) != sorted(g for g, _ in w):
+            raise SystemExit(f"{kernel}: the FETCH_SIZE and WRITE_SIZE runs launched different dispatches")
+        algo = sum((g * nbytes if unit == "lane" else nbytes) for g, _ in f)
+        grids = sorted({g for g, _ in f})
+        lines.append(f"| `{kernel}` | {len(f)} | {', '.join(f'{g:,}' for g in grids)} | {fb:,.0f} | "
+                     f"{wb:,.0f} | {fb + wb:,.0f} | {algo:,.0f} | {(fb + wb) / algo:.4f} |")
+    return "\n".join(lines) + "\n"
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -175,8 +220,25 @@ def main() -> None:
     tt.add_argument("--cal-bytes", type=int, required=True)
     tt.add_argument("--kernel", action="append", required=True,
                     help="NAME=ALGORITHMIC_BYTES (NAME matches a substring of the kernel name); repeatable")
+    tg = sub.add_parser("traffic-grid")
+    for name in ("fetch", "write", "cal-fetch", "cal-write", "cal-kernel", "commands", "out"):
+        tg.add_argument(f"--{name}", required=True)
+    tg.add_argument("--cal-bytes", type=int, required=True)
+    tg.add_argument("--kernel", action="append", required=True,
+                    help="NAME=lane:BYTES or NAME=dispatch:BYTES (NAME matches a substring); repeatable")
     a = ap.parse_args()
-    if a.cmd == "traffic-table":
+    if a.cmd == "traffic-grid":
+        trip = []
+        for k in a.kernel:
+            name, spec = k.rsplit("=", 1)
+            unit, nbytes = spec.split(":")
+            trip.append((name, unit, int(nbytes)))
+        text = traffic_grid_table(a.fetch, a.write, a.cal_fetch, a.cal_write, a.cal_kernel, a.cal_bytes,
+                                  trip, a.commands)
+        with open(a.out, "w") as f:
+            f.write(text)
+        print(text)
+    elif a.cmd == "traffic-table":
         pairs = [(k.rsplit("=", 1)[0], int(k.rsplit("=", 1)[1])) for k in a.kernel]
         text = traffic_table(a.fetch, a.write, a.cal_fetch, a.cal_write, a.cal_kernel, a.cal_bytes,
                              pairs, a.commands)
