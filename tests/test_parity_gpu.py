@@ -138,6 +138,16 @@ def test_all_reduce_two_pass_every_op(op, dtype):
     (3, "f32", 3 << 20, False, "ring_split"),
     (11, "f32", 11 << 18, False, "ring_split"),
     (2, "f32", 1 << 21, False, "ring_split"),
+    # the shapes where the launch shape changes: the one-pass all-reduce runs
+    # two tiles per 512-lane workgroup from W = 5; `ring` takes two passes
+    # (its all-gather in place with pairs) from W = 7 and 4 MiB per rank
+    (5, "f32", 5 << 18, False, "ring"),
+    (6, "f32", 6 << 18, True, "ring"),
+    (7, "f32", 7 << 18, False, "ring"),
+    (7, "bf16", 7 << 19, True, "ring_fused"),
+    (12, "i32", 12 << 18, False, "ring"),
+    (16, "f32", 16 << 16, True, "ring"),           # exactly 4 MiB per rank
+    (16, "f32", (16 << 16) - 16, False, "ring"),   # just below: one pass
 ])
 @pytest.mark.parametrize("caps", [True, False])
 def test_large_grids_with_occupancy_caps(w, dtype, count, in_place, algo, caps):
@@ -515,7 +525,7 @@ def test_all_gather_in_place_and_composition():
         assert_parity(to_host(dev[r], "f32"), want[r], "f32", f"rank {r}")
 
 
-@pytest.mark.parametrize("w", [2, 3, 4, 5, 8, 12, 16])
+@pytest.mark.parametrize("w", [2, 3, 4, 5, 6, 7, 8, 12, 16])
 @pytest.mark.parametrize("in_place", [False, True])
 @pytest.mark.parametrize("caps", [True, False])
 def test_all_gather_large_grids(w, in_place, caps):
