@@ -446,7 +446,7 @@ bool sparse_layout(int w, size_t count, int mode, bool accum, SparseLayout* l) {
   l->gap_val = off;
   off += slot_bytes;
   l->hist = off;
-  off += ws_align(ws * kSpBins * 4);
+  off += ws_align(kHistCount * ws * kSpBins * 4);
   l->state = off;
   off += ws_align(ws * kSpState * 4);
   (void)accum;  // the slots hold everything either mode keeps

@@ -23,15 +23,25 @@ constexpr uint32_t kSpTileBlock = kSpTile / (4 * kSpUnits);  // lanes of the per
 constexpr uint32_t kSpBins = 2048;      // radix-select histogram bins (11-bit digits)
 constexpr uint32_t kSpScanBlock = 1024; // threads of the per-rank offset scan
 
-// Per-rank selection state, kSpState words per rank.
+// Per-rank selection state, kSpState words per rank.  The radix search
+// records its cut after each pass in a field of its own, so that the pass
+// that computes it never overwrites what its other workgroups read.
 enum : uint32_t {
-  kStCut = 0,       // top-K: the K-th largest key (its prefix while the search runs)
+  kStCut = 0,       // top-K: the K-th largest key (after the last pass)
   kStNeed = 1,      // top-K: entries still to take at the cut
   kStBound = 2,     // top-K: every key at or above it is gathered into the slots
-  kStFallback = 3,  // top-K: 1 if the sampled bound missed and the exact fallback runs
+  kStCand = 3,      // top-K: candidates the first gather found (fewer than K: the exact fallback runs)
   kStGuess = 4,     // top-K: keys at or above it get the sent-entry residual at the gather
-  kSpState = 8
+  kStCut0 = 5,      // top-K: the cut's prefix after the first digit
+  kStNeed0 = 6,     //        and the entries still to take below it
+  kStCut1 = 7,      // top-K: the same after the second digit
+  kStNeed1 = 8,
+  kSpState = 16
 };
+// Histograms, kSpBins words per rank each: the three slot passes' and the
+// fallback's (kHistFallback), [kHistCount][W][kSpBins].
+constexpr uint32_t kHistFallback = 3;
+constexpr uint32_t kHistCount = 4;
 
 struct SparseArgs {
   const float* grad[RSX_MAX_RANKS];
@@ -47,7 +57,7 @@ struct SparseArgs {
   uint32_t* tile_eqb;                // [W][tiles + 1] per tile: ties in earlier tiles
   uint32_t* gap_idx;                 // [W][tiles][kSpTile] one slot of entries per tile:
   float* gap_val;                    //   (tile-local index, g value)
-  uint32_t* hist;                    // [W][kSpBins]
+  uint32_t* hist;                    // [kHistCount][W][kSpBins]
   uint32_t* state;                   // [W][kSpState]: kSt* fields
   uint64_t count;                    // elements per rank
   uint32_t tiles;                    // tiles per rank

@@ -172,13 +172,27 @@ struct Digit {
 
 // ----------------------------------------------------------------- kernels
 
-// Per rank: zero the histogram and the per-tile counts, and set the
-// selection state: cut key 0 with K still to find, no fallback.  K = 0
+// Histogram `pass` of rank r: the slot passes' (0, 1, 2) and the fallback's.
+__device__ __forceinline__ uint32_t* hist_of(const SparseArgs& a, uint32_t pass, uint32_t r) {
+  return a.hist + (static_cast<uint64_t>(pass) * a.world + r) * kSpBins;
+}
+
+// Top-K: a rank whose first gather holds fewer than K candidates (its sampled
+// bound missed) takes the exact fallback.
+__device__ __forceinline__ bool needs_fallback(const SparseArgs& a, uint32_t r) {
+  return a.state[kSpState * r + kStCand] < a.k;
+}
+
+// Per rank: zero the histograms and the per-tile counts, and set the
+// selection state: cut key 0 with K still to find, no candidate yet.  K = 0
 // selects nothing: the cut key, the gather bound and the guess are then
 // above every key.
 __global__ __launch_bounds__(kBlock) void sp_init_kernel(const SparseArgs a) {
   const uint32_t r = blockIdx.x;
-  for (uint32_t i = threadIdx.x; i < kSpBins; i += kBlock) a.hist[r * kSpBins + i] = 0;
+  for (uint32_t p = 0; p < kHistCount; ++p) {
+    uint32_t* h = hist_of(a, p, r);
+    for (uint32_t i = threadIdx.x; i < kSpBins; i += kBlock) h[i] = 0;
+  }
   const uint32_t nt = a.tiles + 1;
   for (uint32_t i = threadIdx.x; i < nt; i += kBlock) {
     a.tile_slot[r * nt + i] = 0;
@@ -191,7 +205,7 @@ __global__ __launch_bounds__(kBlock) void sp_init_kernel(const SparseArgs a) {
     st[kStCut] = none;
     st[kStNeed] = a.k;
     st[kStBound] = none;
-    st[kStFallback] = 0;
+    st[kStCand] = 0;
     st[kStGuess] = none;
   }
 }
@@ -210,6 +224,71 @@ __device__ __forceinline__ void zero_hist(uint32_t* h) {
   __syncthreads();
 }
 
+// One step of the radix select: the bin of a BINS-bin histogram (of the keys
+// matching the cut's higher digits) in which the need-th largest key lies,
+// walking the bins from the top: the first bin at which the running count
+// reaches `need` (1 <= need <= the histogram's total).  Every one of the NT
+// lanes gets the bin and the count of keys in the bins above it.  `scratch`
+// is NT / 64 words of LDS, `sh` two.
+template <uint32_t BINS, uint32_t NT>
+__device__ __forceinline__ void find_digit(const uint32_t* gh, uint32_t need, uint32_t* scratch, uint32_t* sh,
+                                           uint32_t& bin, uint32_t& above_bin) {
+  constexpr uint32_t kPer = BINS / NT;
+  static_assert(kPer * NT == BINS, "whole bins per lane");
+  // thread i holds bins top, top-1, ..., top-kPer+1 (thread 0 the highest)
+  const uint32_t top = BINS - 1 - threadIdx.x * kPer;
+  uint32_t c[kPer];
+  uint32_t sum = 0;
+#pragma unroll
+  for (uint32_t i = 0; i < kPer; ++i) {
+    c[i] = gh[top - i];
+    sum += c[i];
+  }
+  if (threadIdx.x == 0) {
+    sh[0] = 0;
+    sh[1] = 0;
+  }
+  uint32_t total;
+  const uint32_t above = block_excl<NT / 64>(sum, scratch, total);  // barriers order sh's reset first
+  if (above < need && need <= above + sum) {
+    uint32_t run = above;
+    for (uint32_t i = 0; i < kPer; ++i) {
+      if (run + c[i] >= need) {
+        sh[0] = top - i;
+        sh[1] = run;
+        break;
+      }
+      run += c[i];
+    }
+  }
+  __syncthreads();
+  bin = sh[0];
+  above_bin = sh[1];
+}
+
+// The cut after radix pass P: the cut so far and the entries still to take
+// (before pass 0: no digit fixed, K), extended by the digit of pass P in
+// which the needed key lies, from pass P's complete histogram.  Every
+// workgroup of the kernel after pass P computes it for itself; the rank's
+// first workgroup records it (fields kStCut0 / kStCut1 / kStCut and their
+// counts) for the kernels after that one.
+template <int P>
+__device__ __forceinline__ uint32_t pick_cut(const SparseArgs& a, uint32_t r, uint32_t grp, uint32_t* scratch,
+                                             uint32_t* sh) {
+  using Dg = Digit<P>;
+  uint32_t* st = a.state + kSpState * r;
+  const uint32_t prefix = P == 0 ? 0u : st[P == 1 ? kStCut0 : kStCut1];
+  const uint32_t need = P == 0 ? a.k : st[P == 1 ? kStNeed0 : kStNeed1];
+  uint32_t bin, above;
+  find_digit<Dg::kBins, kBlock>(hist_of(a, P, r), need, scratch, sh, bin, above);
+  const uint32_t cut = prefix | (bin << Dg::kShift);
+  if (grp == 0 && threadIdx.x == 0) {
+    st[P == 0 ? kStCut0 : (P == 1 ? kStCut1 : kStCut)] = cut;
+    st[P == 0 ? kStNeed0 : (P == 1 ? kStNeed1 : kStNeed)] = need - above;
+  }
+  return cut;
+}
+
 // Top-K fallback, over every element of a rank whose sampled bound missed:
 // histogram of the top digit of g.  With an accumulation the first gather
 // left, at each of its candidates, the residual of a sent entry in the
@@ -222,7 +301,7 @@ __global__ __launch_bounds__(kSpTileBlock) void sp_hist0_fb_kernel(const SparseA
   __shared__ uint32_t h[kSpBins];
   __shared__ uint32_t cand[kSpTile / 32];  // the tile's first-gather candidates
   const uint32_t r = blockIdx.x / a.hist_groups;
-  if (a.state[kSpState * r + kStFallback] == 0) return;
+  if (!needs_fallback(a, r)) return;
   const uint32_t grp = blockIdx.x - r * a.hist_groups;
   zero_hist<kSpTileBlock>(h);
   const float* key = ACC ? a.accum[r] : a.grad[r];
@@ -257,7 +336,7 @@ __global__ __launch_bounds__(kSpTileBlock) void sp_hist0_fb_kernel(const SparseA
       }
     if constexpr (ACC) __syncthreads();  // the bitmap is reused by the next tile
   }
-  merge_hist<Dg::kBins, kSpTileBlock>(h, a.hist + r * kSpBins);
+  merge_hist<Dg::kBins, kSpTileBlock>(h, hist_of(a, kHistFallback, r));
 }
 
 // Top-K sample of a rank of n keys: m = min(n, kSampleMax) keys, in runs
@@ -309,7 +388,6 @@ __global__ __launch_bounds__(kSampleBlock) void sp_sample_kernel(const SparseArg
     if (threadIdx.x == 0) {
       a.state[kSpState * r + kStBound] = 0;
       a.state[kSpState * r + kStGuess] = 0;
-      a.state[kSpState * r + kStFallback] = 0;
     }
     return;
   }
@@ -355,10 +433,7 @@ __global__ __launch_bounds__(kSampleBlock) void sp_sample_kernel(const SparseArg
     }
     return bin << kShift;
   };
-  if (above < p.j && p.j <= above + sum) {
-    a.state[kSpState * r + kStBound] = bin_of(p.j);
-    a.state[kSpState * r + kStFallback] = 0;
-  }
+  if (above < p.j && p.j <= above + sum) a.state[kSpState * r + kStBound] = bin_of(p.j);
   if (above < p.kk && p.kk <= above + sum) a.state[kSpState * r + kStGuess] = bin_of(p.kk);
 }
 
@@ -393,7 +468,9 @@ __device__ __forceinline__ bool rank_tile(const SparseArgs& a, uint32_t& r, uint
 }
 
 // Every key of tile t of rank r at or above `lo` into the tile's slot, in
-// index order.
+// index order.  COUNT: also add the tile's count to the rank's candidates
+// (the first gather; the fallback's test reads the sum).
+template <bool COUNT>
 __device__ __forceinline__ void gather_tile(const SparseArgs& a, uint32_t r, uint32_t t, uint32_t lo,
                                             const float (&x)[kSpUnits][4], uint32_t n, uint32_t* scratch) {
   uint32_t f[kSpUnits][4];
@@ -403,7 +480,10 @@ __device__ __forceinline__ void gather_tile(const SparseArgs& a, uint32_t r, uin
     for (int j = 0; j < 4; ++j) f[u][j] = (in_tile(u, j, n) && order_key(x[u][j]) >= lo) ? 1u : 0u;
   const uint64_t slot = (static_cast<uint64_t>(r) * a.tiles + t) * kSpTile;
   const uint32_t cnt = compact_to_slot(a, slot, f, x, scratch);
-  if (threadIdx.x == 0) a.tile_slot[r * (a.tiles + 1) + t] = cnt;
+  if (threadIdx.x == 0) {
+    a.tile_slot[r * (a.tiles + 1) + t] = cnt;
+    if (COUNT && cnt != 0) atomicAdd(&a.state[kSpState * r + kStCand], cnt);
+  }
 }
 
 // What the accumulation buffer holds after a gather: at keys from the guess
@@ -435,21 +515,33 @@ __global__ __launch_bounds__(kSpTileBlock) void sp_gather_kernel(const SparseArg
   float x[kSpUnits][4];
   load_tile<ACC>(a.grad[r], ACC ? a.accum[r] : nullptr, base, n, x);
   if constexpr (ACC) store_residual(a.accum[r], base, n, a.state[kSpState * r + kStGuess], x);
-  gather_tile(a, r, t, lo, x, n, scratch);
+  gather_tile<true>(a, r, t, lo, x, n, scratch);
 }
 
 // The fallback's gather, for a rank whose sampled bound missed (its groups
 // walk the rank's tiles; other ranks leave at once), from g: the gradient,
 // or the accumulation buffer as the fallback's histogram restored it, which
 // then gets the guessed residuals as the first gather would store them.
+// Its bound is the lower edge of the K-th largest key's top-digit bin in the
+// fallback's histogram, which every workgroup finds for itself; the guess is
+// raised to it if below, so that every key given the sent residual is
+// gathered (the rank's first workgroup records both).
 template <bool ACC>
 __global__ __launch_bounds__(kSpTileBlock) void sp_gather_fb_kernel(const SparseArgs a) {
   __shared__ uint32_t scratch[kSpTileBlock / 64];
+  __shared__ uint32_t sh[2];
   const uint32_t r = blockIdx.x / a.hist_groups;
-  if (a.state[kSpState * r + kStFallback] == 0) return;
+  if (!needs_fallback(a, r)) return;
   const uint32_t grp = blockIdx.x - r * a.hist_groups;
-  const uint32_t lo = a.state[kSpState * r + kStBound];
-  const uint32_t guess = a.state[kSpState * r + kStGuess];  // at least lo
+  uint32_t bin, above;
+  find_digit<Digit<0>::kBins, kSpTileBlock>(hist_of(a, kHistFallback, r), a.k, scratch, sh, bin, above);
+  const uint32_t lo = bin << Digit<0>::kShift;
+  // the recorded guess is either the sample's or already raised to lo: the same max
+  const uint32_t guess = max(a.state[kSpState * r + kStGuess], lo);
+  if (grp == 0 && threadIdx.x == 0) {
+    a.state[kSpState * r + kStBound] = lo;
+    a.state[kSpState * r + kStGuess] = guess;
+  }
   const float* key = ACC ? a.accum[r] : a.grad[r];
   const uint32_t t1 = min(a.tiles, (grp + 1) * a.hist_chunk);
   for (uint32_t t = grp * a.hist_chunk; t < t1; ++t) {
@@ -457,22 +549,8 @@ __global__ __launch_bounds__(kSpTileBlock) void sp_gather_fb_kernel(const Sparse
     float x[kSpUnits][4];
     load_tile<false>(key, nullptr, static_cast<uint64_t>(t) * kSpTile, n, x);
     if constexpr (ACC) store_residual(a.accum[r], static_cast<uint64_t>(t) * kSpTile, n, guess, x);
-    gather_tile(a, r, t, lo, x, n, scratch);
+    gather_tile<false>(a, r, t, lo, x, n, scratch);
   }
-}
-
-// Top-K, one workgroup per rank: did the first gather hold at least K keys?
-// If not, flag the rank for the exact fallback.
-__global__ __launch_bounds__(kSpScanBlock) void sp_check_kernel(const SparseArgs a) {
-  __shared__ uint32_t scratch[kSpScanBlock / 64];
-  const uint32_t r = blockIdx.x;
-  const uint32_t* cnt = a.tile_slot + r * (a.tiles + 1);
-  uint32_t sum = 0;
-#pragma unroll 8
-  for (uint32_t i = threadIdx.x; i < a.tiles; i += kSpScanBlock) sum += cnt[i];
-  uint32_t total;
-  block_excl<kSpScanBlock / 64>(sum, scratch, total);
-  if (threadIdx.x == 0) a.state[kSpState * r + kStFallback] = total < a.k ? 1u : 0u;
 }
 
 // Sum over the 64 lanes of a wave, in every lane.
@@ -534,71 +612,24 @@ __device__ __forceinline__ void walk_slots(const SparseArgs& a, uint32_t r, uint
 
 // Top-K, over the slots: histogram of digit PASS among the keys matching
 // the cut's higher digits.
+// Passes 1 and 2 first take the previous pass's digit (pick_cut).
 template <int PASS>
 __global__ __launch_bounds__(kBlock) void sp_hist_slots_kernel(const SparseArgs a) {
   using Dg = Digit<PASS>;
   __shared__ uint32_t h[kSpBins];
+  __shared__ uint32_t scratch[kBlock / 64];
+  __shared__ uint32_t sh[2];
   const uint32_t r = blockIdx.x / a.hist_groups;
   const uint32_t grp = blockIdx.x - r * a.hist_groups;
+  uint32_t prefix = 0;
+  if constexpr (PASS > 0) prefix = pick_cut<PASS - 1>(a, r, grp, scratch, sh);
   zero_hist(h);
-  const uint32_t prefix = a.state[kSpState * r + kStCut];
   const uint32_t t0 = grp * a.hist_chunk;
   walk_slots(a, r, t0, min(a.tiles, t0 + a.hist_chunk), [&](uint32_t, float v, bool valid, bool) {
     const uint32_t k = order_key(v);
     if (valid && (k & Dg::kHigh) == prefix) atomicAdd(&h[(k >> Dg::kShift) & (Dg::kBins - 1)], 1u);
   });
-  merge_hist<Dg::kBins>(h, a.hist + r * kSpBins);
-}
-
-// The digit at which the K-th largest key lies: walking the bins from the
-// top, the first bin at which the running count reaches the number still to
-// find.  The keys of the bins above it are all selected; the search goes on
-// inside that bin.  One workgroup per rank; clears the histogram afterwards.
-// BOUND: the fallback's pick of the top digit, for a rank whose sampled
-// bound missed: the lower edge of the K-th largest key's top-digit bin
-// becomes the gather bound (and the least guess); the cut itself is still
-// found later.
-template <int PASS, bool BOUND = false>
-__global__ __launch_bounds__(kBlock) void sp_pick_kernel(const SparseArgs a) {
-  using Dg = Digit<PASS>;
-  constexpr uint32_t kPer = Dg::kBins / kBlock;
-  __shared__ uint32_t scratch[kBlock / 64];
-  const uint32_t r = blockIdx.x;
-  uint32_t* gh = a.hist + r * kSpBins;
-  uint32_t* st = a.state + kSpState * r;
-  if (BOUND && st[kStFallback] == 0) return;
-  const uint32_t prefix = BOUND ? 0u : st[kStCut];
-  const uint32_t need = BOUND ? a.k : st[kStNeed];
-  // thread i holds bins top, top-1, ..., top-kPer+1 (thread 0 the highest)
-  const uint32_t top = Dg::kBins - 1 - threadIdx.x * kPer;
-  uint32_t c[kPer];
-  uint32_t sum = 0;
-#pragma unroll
-  for (uint32_t i = 0; i < kPer; ++i) {
-    c[i] = gh[top - i];
-    sum += c[i];
-  }
-  uint32_t total;
-  const uint32_t above = block_excl<kBlock / 64>(sum, scratch, total);
-  if (above < need && need <= above + sum) {
-    uint32_t run = above;
-    for (uint32_t i = 0; i < kPer; ++i) {
-      if (run + c[i] >= need) {
-        if (BOUND) {
-          const uint32_t bound = (top - i) << Dg::kShift;
-          st[kStBound] = bound;
-          st[kStGuess] = max(st[kStGuess], bound);  // every key given the residual is gathered
-        } else {
-          st[kStCut] = prefix | ((top - i) << Dg::kShift);
-          st[kStNeed] = need - run;
-        }
-        break;
-      }
-      run += c[i];
-    }
-  }
-#pragma unroll
-  for (uint32_t i = 0; i < kPer; ++i) gh[top - i] = 0;
+  merge_hist<Dg::kBins>(h, hist_of(a, PASS, r));
 }
 
 // Flags of a top-K candidate against the cut: 1 = above it (sent), 0x10000 =
@@ -609,11 +640,13 @@ __device__ __forceinline__ uint32_t cut_flags(float v, uint32_t cut) {
 }
 
 // Top-K, over the slots: per tile, the candidates above the cut and those
-// equal to it.
+// equal to it, after taking the last digit of the cut (pick_cut).
 __global__ __launch_bounds__(kBlock) void sp_slot_count_kernel(const SparseArgs a) {
+  __shared__ uint32_t scratch[kBlock / 64];
+  __shared__ uint32_t sh[2];
   const uint32_t r = blockIdx.x / a.hist_groups;
   const uint32_t grp = blockIdx.x - r * a.hist_groups;
-  const uint32_t cut = a.state[kSpState * r + kStCut];
+  const uint32_t cut = pick_cut<2>(a, r, grp, scratch, sh);
   const uint32_t t0 = grp * a.hist_chunk;
   uint32_t f = 0;  // this lane's flags in the current tile
   walk_slots(a, r, t0, min(a.tiles, t0 + a.hist_chunk), [&](uint32_t t, float v, bool valid, bool last) {
@@ -876,16 +909,11 @@ hipError_t launch_mode(SparseArgs a, hipStream_t s) {
     // even when K = 0 has nothing to select.
     if ((a.k > 0 || ACC) && e == hipSuccess) e = go(fn(&sp_gather_kernel<ACC>), rt, kSpTileBlock);
     if (a.k > 0) {
-      if (e == hipSuccess) e = go(fn(&sp_check_kernel), a.world, kSpScanBlock);
       if (e == hipSuccess) e = go(fn(&sp_hist0_fb_kernel<ACC>), hg, kSpTileBlock);
-      if (e == hipSuccess) e = go(fn(&sp_pick_kernel<0, true>), a.world, kBlock);
       if (e == hipSuccess) e = go(fn(&sp_gather_fb_kernel<ACC>), hg, kSpTileBlock);
       if (e == hipSuccess) e = go(fn(&sp_hist_slots_kernel<0>), hg, kBlock);
-      if (e == hipSuccess) e = go(fn(&sp_pick_kernel<0>), a.world, kBlock);
       if (e == hipSuccess) e = go(fn(&sp_hist_slots_kernel<1>), hg, kBlock);
-      if (e == hipSuccess) e = go(fn(&sp_pick_kernel<1>), a.world, kBlock);
       if (e == hipSuccess) e = go(fn(&sp_hist_slots_kernel<2>), hg, kBlock);
-      if (e == hipSuccess) e = go(fn(&sp_pick_kernel<2>), a.world, kBlock);
       if (e == hipSuccess) e = go(fn(&sp_slot_count_kernel), hg, kBlock);
     }
   } else {

@@ -520,7 +520,7 @@ def test_sparse_noalloc_validation_and_size_limit(lib):
     # the largest W = 8 count that fits, and the next size up, which does not
     fits = max(c for c in range(0, 3 << 20, 4096)
                if lib.rsx_sparse_workspace_size(8, c, 1, 1) <= limit)
-    assert fits >= (2 << 20) - 4096
+    assert fits >= 2_000_000
     assert lib.rsx_sparse_workspace_size(8, fits + 4096, 1, 1) > limit
     G = 1 << 30
     g8 = [A + r * G for r in range(8)]
