@@ -64,7 +64,10 @@ __global__ __launch_bounds__(kBlock * TPW) void gather_kernel(const GatherArgs a
   const uint64_t t0 = static_cast<uint64_t>(tile) * (U * kBlock);
   if (t0 >= nu) return;
   const uint32_t tid = TPW == 1 ? threadIdx.x : threadIdx.x % kBlock;
-  const char* srcb = static_cast<const char*>(a.src[k]);
+  // Piece k is block k mod W of group k div W (GatherArgs).
+  const uint32_t world = static_cast<uint32_t>(a.world);
+  const uint32_t kr = k < world ? k : k % world;
+  const char* srcb = static_cast<const char*>(a.src[kr]) + static_cast<uint64_t>(k - kr) * nbytes;
   if constexpr (VEC) {
     // Whole 16-byte vectors; the descriptor range drops lanes past the piece.
     const uint32_t bytes = static_cast<uint32_t>(min<uint64_t>(U * kBlock, nu - t0)) * kVecBytes;

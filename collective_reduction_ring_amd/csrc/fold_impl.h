@@ -472,8 +472,12 @@ __global__ __launch_bounds__(kBlock * TPW) void fold_kernel(const FoldArgs a) {
   for (int j = 0; j < W; ++j) src[j] = static_cast<const S*>(a.src[(first + j) % W]);
 
   if constexpr (RS) {
-    S* const dst[1] = {static_cast<S*>(a.dst[k])};
-    fold_tile<D, OP, W, 1, kStoreThrough, VEC, true>(src, dst, b, b, e, tile, tid);
+    // Segment k goes to rank k mod W, at its offset within its group of W
+    // segments (one group per bucket when a launch covers several).
+    const uint32_t kr = k % W;
+    S* const dst[1] = {static_cast<S*>(a.dst[kr])};
+    fold_tile<D, OP, W, 1, kStoreThrough, VEC, true>(src, dst, static_cast<uint64_t>(kr) * seg, b, e, tile,
+                                                      tid);
   } else {
     S* dst[W];
 #pragma unroll

@@ -115,10 +115,12 @@ bool ar_pairs(int w) { return t_caps && w >= 5; }
 // pass ahead (up to 8%); below 4 MiB per rank the second launch costs more
 // than it saves (1 MiB: 1.2-1.5).  Without the occupancy caps the
 // all-gather has no pairs and one pass is kept.
-bool two_passes_pay(int w, size_t count, size_t es, bool vec) {
+// `count` is one bucket's elements; a launch may cover `groups` equal
+// buckets, and its size is what the measurements above key on.
+bool two_passes_pay(int w, size_t count, size_t groups, size_t es, bool vec) {
   const size_t seg = count / static_cast<size_t>(w);
   return t_caps && vec && w >= 7 && count % static_cast<size_t>(w) == 0 && (seg * es) % kVecBytes == 0 &&
-         count * es >= (4u << 20);
+         count * groups * es >= (4u << 20);
 }
 // All-gather: tiles per workgroup and workgroups per CU.
 void ag_shape(int w, bool in_place, int* tpw, uint32_t* cap) {
@@ -246,9 +248,10 @@ rsx_status_t launch_fold_any(int dtype, int op, int world, bool rs, bool vec, Fo
 
 // All-gather launch over validated buffers: piece k = src[k] goes to
 // dst[r] + k * n elements for every r.  A piece already in place (src[k] ==
-// dst[k] + k * n) is read but not written back.
+// dst[k] + k * n) is read but not written back.  With groups > 1 the same
+// is done for each of `groups` consecutive blocks of W * n elements.
 rsx_status_t launch_gather_any(const void* const* src, void* const* dst, int nranks, size_t n,
-                               size_t es, hipStream_t stream) {
+                               size_t es, hipStream_t stream, uint64_t groups = 1) {
   const size_t piece_bytes = n * es;
   bool vec = (piece_bytes % kVecBytes) == 0;
   bool in_place = true;
@@ -267,7 +270,7 @@ rsx_status_t launch_gather_any(const void* const* src, void* const* dst, int nra
   const uint64_t units = vec ? piece_bytes / kVecBytes : n;
   const uint64_t per = static_cast<uint64_t>(kCopyUnits) * kBlock;
   const uint64_t tiles = std::max<uint64_t>(1, (units + per - 1) / per);
-  const uint64_t total = tiles * static_cast<uint64_t>(nranks);
+  const uint64_t total = tiles * static_cast<uint64_t>(nranks) * groups;
   if (total > 0x7ffffff0ull) return RSX_ERR_UNSUPPORTED;
   a.tiles_per_piece = static_cast<uint32_t>(tiles);
   a.tiles_total = static_cast<uint32_t>(total);
@@ -579,14 +582,15 @@ rsx_status_t scratch_of_current_device(void** out) {
   return RSX_SUCCESS;
 }
 
-// An all-reduce of `count` elements fits the launch grid in every form
-// (one pass, naive, or reduce-scatter + all-gather: at most count/W + 1
-// whole-vector or element tiles per segment, W segments).
-bool all_reduce_grid_ok(int nranks, size_t count) {
+// An all-reduce of `groups` buckets of `count` elements each fits the
+// launch grid in every form (one pass, naive, or reduce-scatter +
+// all-gather: at most count/W + 1 whole-vector or element tiles per
+// segment, W segments per bucket).
+bool all_reduce_grid_ok(int nranks, size_t count, uint64_t groups = 1) {
   const uint64_t seg = (count + nranks - 1) / nranks;
-  const uint64_t tiles = std::max(fold_tiles(seg, nranks, false, 1) * static_cast<uint64_t>(nranks),
-                                  fold_tiles(count, nranks, false, 1));
-  return tiles <= 0x7ffffff0ull;
+  const uint64_t per = fold_tiles(seg, nranks, false, 1) * static_cast<uint64_t>(nranks);
+  if (per > 0x7ffffff0ull / groups) return false;
+  return per * groups <= 0x7ffffff0ull && fold_tiles(count * groups, nranks, false, 1) <= 0x7ffffff0ull;
 }
 
 // Checks of an all-reduce (no HIP call).  *nothing: valid, with no work.
@@ -629,18 +633,21 @@ rsx_status_t all_reduce_check(const void* const* sendbufs, void* const* recvbufs
   return RSX_SUCCESS;
 }
 
-// Launches of a checked all-reduce.
+// Launches of a checked all-reduce of `count` elements per rank, or of
+// `groups` consecutive buckets of `count` elements each, every bucket
+// all-reduced as one call on it would (W must divide count when groups >
+// 1, so that the buckets' ring segments tile the whole range).
 rsx_status_t all_reduce_launch(const void* const* sendbufs, void* const* recvbufs, int nranks,
                                size_t count, rsx_dtype_t dtype, rsx_op_t op, rsx_algo_t algo,
-                               hipStream_t stream) {
+                               hipStream_t stream, uint64_t groups = 1) {
   const size_t es = esize_of(dtype);
-  const size_t bytes = count * es;
+  const size_t bytes = count * es;  // one bucket: the naive choice is per bucket
   rsx_status_t st = RSX_SUCCESS;
   const bool naive = algo == RSX_ALGO_NAIVE || (algo == RSX_ALGO_AUTO && bytes <= RSX_NAIVE_MAX_BYTES);
   bool vec = true;
   for (int r = 0; r < nranks; ++r) vec = vec && aligned16(sendbufs[r]) && aligned16(recvbufs[r]);
   const bool split = algo == RSX_ALGO_RING_SPLIT ||
-                     (!naive && algo != RSX_ALGO_RING_FUSED && two_passes_pay(nranks, count, es, vec));
+                     (!naive && algo != RSX_ALGO_RING_FUSED && two_passes_pay(nranks, count, groups, es, vec));
 
   // Two passes ("Distributed primitives": Ring AllReduce = ReduceScatter +
   // AllGather): the reduce-scatter stores segment k into recvbufs[k] at its
@@ -661,7 +668,7 @@ rsx_status_t all_reduce_launch(const void* const* sendbufs, void* const* recvbuf
       a.dst[r] = static_cast<char*>(recvbufs[r]) + static_cast<size_t>(r) * seg * es;
       pieces[r] = a.dst[r];
     }
-    a.count = count;
+    a.count = count * groups;
     a.seg = seg;
     a.rot = 1;
     const int vl = static_cast<int>(kVecBytes / es);
@@ -669,9 +676,9 @@ rsx_status_t all_reduce_launch(const void* const* sendbufs, void* const* recvbuf
     // same segments, in 16-byte units whenever the reduce-scatter's are), so
     // its size check cannot fail after the reduce-scatter has launched.
     st = launch_fold_any(dtype, op, nranks, true, rs_vec, a, fold_tiles(seg, nranks, rs_vec, vl),
-                         static_cast<uint32_t>(nranks), stream);
+                         static_cast<uint32_t>(nranks * groups), stream);
     if (st != RSX_SUCCESS) return st;
-    return launch_gather_any(pieces, recvbufs, nranks, seg, es, stream);
+    return launch_gather_any(pieces, recvbufs, nranks, seg, es, stream, groups);
   }
 
   FoldArgs a;
@@ -680,11 +687,12 @@ rsx_status_t all_reduce_launch(const void* const* sendbufs, void* const* recvbuf
     a.src[r] = sendbufs[r];
     a.dst[r] = recvbufs[r];
   }
-  a.count = count;
-  const uint64_t seg = naive ? count : (count + nranks - 1) / nranks;
+  a.count = count * groups;
+  // Rank order is the same for every bucket: one segment over all of them.
+  const uint64_t seg = naive ? count * groups : (count + nranks - 1) / nranks;
   a.seg = seg;
   a.rot = naive ? 0 : 1;
-  const uint32_t nseg = naive ? 1 : static_cast<uint32_t>(nranks);
+  const uint32_t nseg = naive ? 1 : static_cast<uint32_t>(nranks * groups);
   const int vl = static_cast<int>(kVecBytes / es);
   return launch_fold_any(dtype, op, nranks, false, vec, a, fold_tiles(seg, nranks, vec, vl), nseg,
                          stream);
@@ -804,7 +812,18 @@ rsx_status_t rsx_all_reduce_bucketed(const void* const* sendbufs, void* const* r
   const size_t es = esize_of(dtype);
   const void* src[RSX_MAX_RANKS];
   void* dst[RSX_MAX_RANKS];
-  for (size_t b0 = 0; b0 < count;) {
+  size_t b0 = 0;
+  // Equal buckets whose ring segments line up (W divides the bucket) are
+  // reduced by one launch per pass; each bucket keeps its own ring segments
+  // and fold order, so the result is the same as one call per bucket.
+  const size_t nfull = count / bucket_elems;
+  if (nfull > 1 && bucket_elems % w == 0 && all_reduce_grid_ok(nranks, bucket_elems, nfull)) {
+    if ((st = all_reduce_launch(sendbufs, recvbufs, nranks, bucket_elems, dtype, op, algo, stream, nfull)) !=
+        RSX_SUCCESS)
+      return st;
+    b0 = nfull * bucket_elems;
+  }
+  while (b0 < count) {
     const size_t n = std::min(bucket_elems, count - b0);
     for (int r = 0; r < nranks; ++r) {
       src[r] = static_cast<const char*>(sendbufs[r]) + b0 * es;

@@ -20,7 +20,12 @@ constexpr int kVecBytes = 16;      // one dwordx4 per lane per source
 // min((k+1)*seg,count)).  Segment k folds rank (k+rot)%W first, then the ranks
 // after it in ring order, so rot=1 is the ring (the block a ring position
 // starts at step 0 is the one owned by the position before it) and
-// rot=0 with one segment is rank order.
+// rot=0 with one segment is rank order.  A launch may cover several equal
+// buckets of W segments each (nseg = buckets * W, each bucket its own ring).
+// The reduce-scatter form stores element i of segment k at
+// dst[k%W][i - (k%W)*seg]: each rank's own block with W segments, and with
+// several buckets and dst[r] at block r of the first bucket, every block at
+// its own offset in its rank's buffer.
 //
 // Workgroups: `tiles_per_seg` tiles per segment, `tiles_total` = nseg *
 // tiles_per_seg in all, launched as a 1-D grid rounded up to a multiple of
@@ -51,7 +56,11 @@ inline void split_magic(uint32_t d, uint32_t* magic, uint32_t* shift) {
 }
 
 // All-gather: dst[r][k*n + i] = src[k][i].  Tiles as in FoldArgs: piece k
-// owns tiles [k*tiles_per_piece, (k+1)*tiles_per_piece).
+// owns tiles [k*tiles_per_piece, (k+1)*tiles_per_piece).  A launch may cover
+// several groups of W pieces laid out back to back (the in-place all-gathers
+// of several equal buckets): piece k >= W is read from src[k mod W] +
+// (k - k mod W)*n elements and written at k*n, so tiles_total / tiles_per_piece
+// counts the pieces.
 struct GatherArgs {
   const void* src[RSX_MAX_RANKS];
   void* dst[RSX_MAX_RANKS];

@@ -25,12 +25,14 @@
 //                        into the tile's slot, in index order; into the
 //                        accumulation buffer g = grad + acc, or from a
 //                        guessed cut up the residual of a sent entry
-//               check    per rank: fewer than K keys gathered?  Then an exact
-//                        fallback for that rank alone: a top-digit histogram
-//                        over every element, its bound, and the gather again
-//               hist0-2  (slots) top-, middle- and low-digit histograms
-//               pick     after each histogram: the digit of the K-th key
-//               count    (slots) per tile, candidates above / equal to the cut
+//               fallback per rank, only when the gather found fewer than K
+//                        keys: a top-digit histogram over every element,
+//                        and the gather again from its exact bound
+//               hist0-2  (slots) top-, middle- and low-digit histograms;
+//                        each pass first finds the previous digit of the
+//                        K-th key in the finished histogram before it
+//               count    (slots) the last digit, then per tile the
+//                        candidates above / equal to the cut
 //   both:       scan     per rank: each tile's offset in the message (one
 //                        workgroup per 4096 tiles)
 //               combine  per output tile: for each rank in order, its sent

@@ -181,7 +181,10 @@ rsx_status_t rsx_all_reduce(const void* const* sendbufs, void* const* recvbufs,
  * min((b+1)*bucket_elems, count)).  Each bucket is an rsx_all_reduce of its
  * own, with its own segments (S = ceil(len/W), ring order per segment) and
  * its own RSX_ALGO_AUTO choice, launched in bucket order on `stream`.  The
- * result equals rsx_all_reduce on each bucket in turn.
+ * result equals rsx_all_reduce on each bucket in turn.  When W divides
+ * bucket_elems, the full buckets share one launch per pass (each bucket
+ * still folded over its own segments in its own ring order) and the shorter
+ * last bucket follows.
  * Arguments, ownership, in-place and aliasing rules: as rsx_all_reduce, on
  * the whole buffers.  bucket_elems = 0: RSX_ERR_INVALID_ARGUMENT.
  * RSX_ALGO_RING_SPLIT needs W to divide every bucket (RSX_ERR_UNSUPPORTED).

@@ -817,6 +817,14 @@ def test_full_c4_int32(op):
     ("f16", "prod", 5, 20_000, 20_000, "naive"),                  # one bucket
     ("f32h", "sum", 2, 9_000, 2_500, "ring"),                    # half wire
     ("f32", "sum", 4, 1_000, 10 ** 9, "ring"),                    # bucket above count
+    # W divides the bucket: the full buckets share one launch per pass
+    ("f32", "sum", 8, 5 * 8 * 65536 + 1000, 8 * 65536, "ring"),   # two passes over 5 buckets, ragged last
+    ("bf16", "avg", 8, 4 * 8 * 1001 + 8, 8 * 1001, "ring"),       # one pass, segments not 16-byte multiples
+    ("i32", "max", 16, 3 * 16 * 70_000, 16 * 70_000, "ring_split"),  # two passes, no last bucket
+    ("f32", "sum", 12, 4 * 12 * 40_000 + 12, 12 * 40_000, "ring"),   # two passes at W = 12
+    ("f16", "sum", 7, 6 * 7 * 3000 + 5, 7 * 3000, "ring_fused"),  # one pass at W = 7
+    ("f32", "prod", 5, 3 * 5 * 4096 + 77, 5 * 4096, "naive"),     # rank order over every bucket
+    ("i32", "sum", 8, 4 * 8 * 512, 8 * 512, "auto"),              # small buckets: naive, shared launch
 ])
 @pytest.mark.parametrize("in_place", [False, True])
 def test_all_reduce_bucketed_entry(dtype, op, w, n, bucket, algo, in_place):
@@ -839,6 +847,23 @@ def test_all_reduce_bucketed_entry(dtype, op, w, n, bucket, algo, in_place):
             want[r][b0:b1] = res[r]
     for r in range(w):
         assert_parity(to_host((dev if in_place else out)[r], dtype), want[r], dtype, f"rank {r}")
+
+
+@pytest.mark.parametrize("algo", ["ring", "ring_split", "ring_fused"])
+def test_all_reduce_bucketed_unaligned(algo):
+    # 4-byte offsets: element kernels in both passes, several buckets per launch
+    w, bucket = 8, 8 * 3001
+    n = 4 * bucket + 8 * 17
+    xs = inputs(61, w, n, "f32")
+    bases = [to_dev(np.concatenate([np.zeros(1, np.float32), x]), "f32") for x in xs]
+    dev = [b[1:] for b in bases]
+    outs = [empty(n + 3, "f32", fill=0x55)[3:] for _ in range(w)]
+    say(f"bucketed unaligned algo={algo}")
+    rsx.all_reduce_bucketed(dev, outs, bucket, "sum", algo)
+    torch.cuda.synchronize()
+    want = oracle.bucketed_all_reduce(xs, bucket, "sum", "f32")
+    for r in range(w):
+        assert_parity(to_host(outs[r], "f32"), want[r], "f32", f"rank {r}")
 
 
 def test_full_c3_bf16_bucketed_avg():
