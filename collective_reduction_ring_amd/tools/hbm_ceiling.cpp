@@ -170,6 +170,7 @@ Best measure(const char* src, char* dst, float* sink, size_t bytes, double moved
     const float ms = median_ms([&] { hipLaunchKernelGGL(kernel, dim3(tiles), dim3(block), lds, 0, src, dst, sink); });
     CHECK(hipGetLastError());
     const double g = moved / (ms * 1e-3) / 1e9;
+    fprintf(stderr, "pattern %d/%d/%d/%d  %-16s %8.1f GB/s\n", MODE, LA, SA, NB, cfg, g);
     if (best.first == 0) best.first = g;
     if (g > best.gbs) {
       best.gbs = g;
