@@ -532,6 +532,10 @@ hipError_t launch_world(bool rs, bool vec, int tpw, const FoldArgs& a, dim3 grid
   const void* fn;
   if (!rs && vec && tpw == 2) {
     fn = reinterpret_cast<const void*>(&fold_kernel<D, OP, W, false, true, 2>);
+  } else if (rs && vec && tpw == 2) {
+    // paired reduce-scatter tiles exist from W = 10 (rs_pairs)
+    if constexpr (W >= 10) fn = reinterpret_cast<const void*>(&fold_kernel<D, OP, W, true, true, 2>);
+    else return hipErrorInvalidValue;
   } else if (tpw != 1) {
     return hipErrorInvalidValue;
   } else if (rs) {

@@ -100,12 +100,18 @@ uint32_t list_cap(int w) { return w <= 1 ? 8u : w <= 4 ? 5u : 3u; }
 //     448 -> 409 us); W = 10..16: -0.6 .. +3.7%; W <= 5: -3 .. -18%;
 //   all-gather in place, W = 7, 8: +5.9 / +10.1%; W = 10..16: +2.1 .. +4.8%;
 //     W = 6: -2.5%; W <= 5: -11 .. -47%.
-// Pairs at two workgroups per CU lose almost everywhere (up to -16%), and the
-// reduce-scatter loses with pairs (W = 8: 369 -> 379 us at two per CU, 433
-// us at one).  Pairs are a form of the occupancy cap: with the caps off
-// (launches that overlap other work) every kernel runs one tile per
-// workgroup.
+// For these write-heavy kernels pairs at two workgroups per CU lose almost
+// everywhere (up to -16%); the reduce-scatter is the other way round (below).
+// Pairs are a form of the occupancy cap: with the caps off (launches that
+// overlap other work) every kernel runs one tile per workgroup.
 bool ar_pairs(int w) { return t_caps && w >= 5; }
+// The reduce-scatter (dwordx4) in pairs at two workgroups per CU against one
+// tile per workgroup at rs_cap, int32 sum, 128 MiB per rank, same process:
+// W = 10 248 -> 245 us, 11 280 -> 264, 12 309 -> 294, 13 331 -> 321, 14 345
+// -> 337, 15 362 -> 357, 16 375 -> 368; W = 9 229 -> 231.  At W = 8 it
+// wins at 128 MiB per rank (199 -> 194 us) but loses at 256 MiB (366 -> 379
+// us), so W = 8 keeps single tiles.
+bool rs_pairs(int w) { return t_caps && w >= 10; }
 // The ring all-reduce as two passes (a reduce-scatter, then an all-gather in
 // place) against one pass, whole calls, same process (fp32 and bf16; ratio
 // of two-pass to one-pass time): W = 8, 4 / 16 / 64 / 256 MiB per rank:
@@ -239,10 +245,13 @@ rsx_status_t launch_fold_any(int dtype, int op, int world, bool rs, bool vec, Fo
   a.tiles_total = static_cast<uint32_t>(total);
   split_magic(a.tiles_per_seg, &a.tps_magic, &a.tps_shift);
   // The dwordx4 all-reduce at W >= 5 runs two tiles per workgroup, one
-  // workgroup per CU (ar_pairs); everything else one tile per workgroup.
-  const int tpw = (!rs && vec && ar_pairs(world)) ? 2 : 1;
+  // workgroup per CU (ar_pairs), the dwordx4 reduce-scatter at W >= 10 two
+  // per workgroup, two workgroups per CU (rs_pairs); everything else one
+  // tile per workgroup.
+  const bool pairs = vec && (rs ? rs_pairs(world) : ar_pairs(world));
+  const int tpw = pairs ? 2 : 1;
   const dim3 grid(static_cast<uint32_t>(xcd_grid((total + tpw - 1) / tpw)));
-  const uint32_t lds = !vec ? 0u : tpw == 2 ? lds_for_cap(1) : lds_for_cap(rs ? rs_cap(world) : ar_cap(world));
+  const uint32_t lds = !vec ? 0u : pairs ? lds_for_cap(rs ? 2u : 1u) : lds_for_cap(rs ? rs_cap(world) : ar_cap(world));
   return hip_status(launch_fold_by_type(dtype, op, world, rs, vec, tpw, a, grid, lds, s));
 }
 

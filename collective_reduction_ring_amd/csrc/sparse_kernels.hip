@@ -188,15 +188,15 @@ __device__ __forceinline__ bool needs_fallback(const SparseArgs& a, uint32_t r) 
 // Per rank: zero the histograms and the per-tile counts, and set the
 // selection state: cut key 0 with K still to find, no candidate yet.  K = 0
 // selects nothing: the cut key, the gather bound and the guess are then
-// above every key.
-__global__ __launch_bounds__(kBlock) void sp_init_kernel(const SparseArgs a) {
-  const uint32_t r = blockIdx.x;
+// above every key.  NT lanes of a workgroup of the rank.
+template <uint32_t NT>
+__device__ __forceinline__ void init_rank(const SparseArgs& a, uint32_t r) {
   for (uint32_t p = 0; p < kHistCount; ++p) {
     uint32_t* h = hist_of(a, p, r);
-    for (uint32_t i = threadIdx.x; i < kSpBins; i += kBlock) h[i] = 0;
+    for (uint32_t i = threadIdx.x; i < kSpBins; i += NT) h[i] = 0;
   }
   const uint32_t nt = a.tiles + 1;
-  for (uint32_t i = threadIdx.x; i < nt; i += kBlock) {
+  for (uint32_t i = threadIdx.x; i < nt; i += NT) {
     a.tile_slot[r * nt + i] = 0;
     a.tile_cnt[r * nt + i] = 0;
     a.tile_eqc[r * nt + i] = 0;
@@ -211,6 +211,9 @@ __global__ __launch_bounds__(kBlock) void sp_init_kernel(const SparseArgs a) {
     st[kStGuess] = none;
   }
 }
+
+// One workgroup per rank (top-K with K > 0: the sampling kernel does it).
+__global__ __launch_bounds__(kBlock) void sp_init_kernel(const SparseArgs a) { init_rank<kBlock>(a, blockIdx.x); }
 
 // Workgroup-local histogram -> the rank's histogram in HBM (NT lanes).
 template <uint32_t BINS, uint32_t NT = kBlock>
@@ -385,6 +388,10 @@ __global__ __launch_bounds__(kSampleBlock) void sp_sample_kernel(const SparseArg
   __shared__ uint32_t h[kBins];
   __shared__ uint32_t scratch[kWaves];
   const uint32_t r = blockIdx.x;
+  // The rank's initial state first; the barrier orders its stores before
+  // the bound and guess below.
+  init_rank<kSampleBlock>(a, r);
+  __syncthreads();
   const SamplePlan p(a);
   if (p.j > p.m) {  // everything is gathered, and guessed sent
     if (threadIdx.x == 0) {
@@ -439,9 +446,6 @@ __global__ __launch_bounds__(kSampleBlock) void sp_sample_kernel(const SparseArg
   if (above < p.kk && p.kk <= above + sum) a.state[kSpState * r + kStGuess] = bin_of(p.kk);
 }
 
-// Copy this tile's flagged elements, in index order, to its slot; returns
-// how many there are.  Lane l holds elements 4l .. 4l + 3, so one block scan
-// of the lanes' counts places every entry.
 static_assert(kSpUnits == 1, "compact_to_slot takes one element group per lane");
 
 // Lanes below this one whose bit is set in a wave-wide mask.
@@ -654,8 +658,8 @@ __device__ __forceinline__ void walk_slots(const SparseArgs& a, uint32_t r, uint
 }
 
 // Top-K, over the slots: histogram of digit PASS among the keys matching
-// the cut's higher digits.
-// Passes 1 and 2 first take the previous pass's digit (pick_cut).
+// the cut's higher digits.  Passes 1 and 2 first take the previous pass's
+// digit (pick_cut).
 template <int PASS>
 __global__ __launch_bounds__(kBlock) void sp_hist_slots_kernel(const SparseArgs a) {
   using Dg = Digit<PASS>;
@@ -944,9 +948,11 @@ hipError_t launch_mode(SparseArgs a, hipStream_t s) {
   };
   const uint64_t hg = static_cast<uint64_t>(a.world) * a.hist_groups;
   const uint64_t rt = xcd_grid(static_cast<uint64_t>(a.world) * a.tiles);
-  hipError_t e = go(reinterpret_cast<const void*>(&sp_init_kernel), a.world, kBlock);
+  hipError_t e = hipSuccess;
+  if (MODE != RSX_SPARSE_TOPK || a.k == 0) e = go(reinterpret_cast<const void*>(&sp_init_kernel), a.world, kBlock);
   if constexpr (MODE == RSX_SPARSE_TOPK) {
     auto fn = [](auto k) { return reinterpret_cast<const void*>(k); };
+    // the sample kernel also initialises each rank (init_rank)
     if (a.k > 0 && e == hipSuccess) e = go(fn(&sp_sample_kernel<ACC>), a.world, kSampleBlock);
     // The first gather also leaves g in the accumulation buffer, so it runs
     // even when K = 0 has nothing to select.
