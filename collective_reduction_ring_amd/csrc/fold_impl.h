@@ -352,8 +352,11 @@ __device__ __forceinline__ uint4 fold_vectors(const uint4 (&v)[W]) {
 //
 // VEC: all source and destination bases are 16-byte aligned, so element
 // offsets divisible by VL are too; the tile is U*256 whole vectors of the
-// range and tile 0 also folds the unaligned head and tail elements (none
-// when WHOLE, i.e. b and e are multiples of VL).  Otherwise the tile is
+// range and tile 0 also folds the unaligned head and tail elements.  WHOLE
+// (the reduce-scatter): the vectors start at b itself, whose destination
+// (dst + b - shift) is 16-byte aligned and whose sources are at least
+// 4-byte aligned (multi-dword buffer loads need only dword alignment), and
+// tile 0 folds the last (e - b) mod VL elements.  Otherwise the tile is
 // U*256 elements, one per lane per unit, still coalesced.
 template <class D, int OP, int W, int ND, int STORE_AUX, bool VEC, bool WHOLE>
 __device__ __forceinline__ void fold_tile(const typename D::S* const (&src)[W],
@@ -374,7 +377,7 @@ __device__ __forceinline__ void fold_tile(const typename D::S* const (&src)[W],
 
   if constexpr (VEC) {
     const uint64_t hb = WHOLE ? b : min((b + VL - 1) / VL * VL, e);
-    const uint64_t be = WHOLE ? e : max(hb, e / VL * VL);
+    const uint64_t be = WHOLE ? b + (e - b) / VL * VL : max(hb, e / VL * VL);
     const uint64_t nv = (be - hb) / VL;
     const uint64_t v0 = static_cast<uint64_t>(tile) * (U * kBlock);
     // A whole segment's tiles all hold vectors: the grid has ceil(nv / tile)
@@ -403,7 +406,9 @@ __device__ __forceinline__ void fold_tile(const typename D::S* const (&src)[W],
         for (int u = 0; u < U; ++u) store_b128<STORE_AUX>(r, voff, u * kBlock * kVecBytes, o[u]);
       }
     }
-    if (!WHOLE && tile == 0) {
+    if (WHOLE && tile == 0) {
+      if (tid < e - be) fold_element(be + tid);
+    } else if (!WHOLE && tile == 0) {
       const uint32_t nh = static_cast<uint32_t>(hb - b);
       const uint32_t nt = static_cast<uint32_t>(e - be);
       if (tid < nh) {

@@ -668,7 +668,7 @@ rsx_status_t all_reduce_launch(const void* const* sendbufs, void* const* recvbuf
   // measured faster (two_passes_pay), RSX_ALGO_RING_SPLIT always.
   if (split) {
     const size_t seg = count / static_cast<size_t>(nranks);
-    const bool rs_vec = vec && (seg * es) % kVecBytes == 0;
+    const bool rs_vec = vec && (seg * es) % 4 == 0;
     FoldArgs a;
     memset(&a, 0, sizeof(a));
     const void* pieces[RSX_MAX_RANKS];
@@ -746,7 +746,7 @@ rsx_status_t rsx_reduce_scatter(const void* const* sendbufs, void* const* recvbu
   // One rank in place: nothing to do, except that a half wire still rounds.
   if (nranks == 1 && in_place_all && dtype != RSX_FLOAT32_HALF_WIRE) return RSX_SUCCESS;
 
-  bool vec = (seg_bytes % kVecBytes) == 0;
+  bool vec = (seg_bytes % 4) == 0;  // dword-aligned block starts; the fold kernel takes any tail
   for (int r = 0; r < nranks; ++r) vec = vec && aligned16(sendbufs[r]) && aligned16(recvbufs[r]);
 
   FoldArgs a;

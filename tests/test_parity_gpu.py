@@ -172,13 +172,16 @@ def test_large_grids_with_occupancy_caps(w, dtype, count, in_place, algo, caps):
 
 
 @pytest.mark.parametrize("w,dtype,extra", [(3, "f32", 1), (8, "f32", 3), (16, "f32", 2), (8, "bf16", 5),
-                                           (5, "i8", 11), (8, "f64", 1), (2, "f16", 7), (8, "i32", 2)])
+                                           (5, "i8", 11), (8, "f64", 1), (2, "f16", 7), (8, "i32", 2),
+                                           (12, "f32", 1), (8, "bf16", 6), (4, "i8", 12), (11, "i64", 1)])
 @pytest.mark.parametrize("caps", [True, False])
 def test_reduce_scatter_blocks_of_partial_vectors(w, dtype, extra, caps):
     # Block length a whole number of vectors plus `extra` elements, on
     # 16-byte-aligned buffers: every block but the first starts mid-vector in
-    # the sources (the element-wise kernel), the last reaches the end of
-    # them; thousands of workgroups.
+    # the sources, the last reaches the end of them; thousands of
+    # workgroups.  Blocks whose byte length is a multiple of 4 take the
+    # dwordx4 kernel (dword-aligned loads, a tail per block; W >= 10 in
+    # pairs when capped), the others the element-wise kernel.
     recvcount = (1 << 17) + extra
     xs = inputs(27, w, w * recvcount, dtype)
     say(f"rs partial-vector blocks w={w} dtype={dtype} recvcount={recvcount} caps={caps}")
