@@ -100,18 +100,77 @@ __global__ __launch_bounds__(kBlock * TPW) void gather_kernel(const GatherArgs a
   }
 }
 
-// Two tiles per workgroup exist for the dwordx4 kernel only.
-hipError_t launch_gather(int esize, bool vec, int tpw, const GatherArgs& a, dim3 grid, uint32_t lds,
+// The all-gather of pieces of whole dwords that are not whole 16-byte
+// vectors (16-byte-aligned buffers): piece k starts k * n elements into every
+// destination, at an offset that is a multiple of 4 but not always of 16.
+// The bytes before the piece's first 16-byte-aligned destination byte, and
+// those after its last whole vector, are copied element by element by tile 0;
+// the vectors between are read with dword-aligned dwordx4 loads (multi-dword
+// buffer loads need only dword alignment) and stored aligned.  The
+// descriptor range drops lanes past the last vector.
+template <int ES, int TPW>
+__global__ __launch_bounds__(kBlock * TPW) void gather_dword_kernel(const GatherArgs a) {
+  using E = typename Unit<ES>::T;
+  constexpr int U = kCopyUnits;
+  const uint32_t t = workgroup_tile<TPW>();
+  if (t >= a.tiles_total) return;
+  const uint32_t k = static_cast<uint32_t>((static_cast<uint64_t>(t) * a.tps_magic) >> a.tps_shift);
+  const uint32_t tile = t - k * a.tiles_per_piece;
+  const uint64_t nbytes = a.n * ES;
+  const uint64_t doff = static_cast<uint64_t>(k) * nbytes;  // the piece's offset in every destination
+  const uint64_t h = min<uint64_t>((16u - (doff & 15u)) & 15u, nbytes);
+  const uint64_t nu = (nbytes - h) / kVecBytes;
+  const uint64_t t0 = static_cast<uint64_t>(tile) * (U * kBlock);
+  const uint32_t tid = TPW == 1 ? threadIdx.x : threadIdx.x % kBlock;
+  const uint32_t world = static_cast<uint32_t>(a.world);
+  const uint32_t kr = k < world ? k : k % world;
+  const char* srcb = static_cast<const char*>(a.src[kr]) + static_cast<uint64_t>(k - kr) * nbytes;
+  if (t0 < nu) {
+    const uint32_t bytes = static_cast<uint32_t>(min<uint64_t>(U * kBlock, nu - t0)) * kVecBytes;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(srcb + h + t0 * kVecBytes, bytes);
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = load_stream(rs, tid * kVecBytes, u * kBlock * kVecBytes);
+    for (int r = 0; r < a.world; ++r) {
+      char* base = static_cast<char*>(a.dst[r]) + doff;
+      if (base == srcb) continue;  // in-place piece
+      const __amdgpu_buffer_rsrc_t rd = make_rsrc(base + h + t0 * kVecBytes, bytes);
+#pragma unroll
+      for (int u = 0; u < U; ++u) store_b128<kStoreStream>(rd, tid * kVecBytes, u * kBlock * kVecBytes, v[u]);
+    }
+  }
+  if (tile == 0) {
+    const uint32_t nh = static_cast<uint32_t>(h / ES);
+    const uint64_t tail = h + nu * kVecBytes;
+    const uint32_t nt = static_cast<uint32_t>((nbytes - tail) / ES);
+    if (tid < nh + nt) {
+      const uint64_t e = tid < nh ? tid : tail / ES + (tid - nh);
+      const E v = reinterpret_cast<const E*>(srcb)[e];
+      for (int r = 0; r < a.world; ++r) {
+        char* base = static_cast<char*>(a.dst[r]) + doff;
+        if (base == srcb) continue;
+        reinterpret_cast<E*>(base)[e] = v;
+      }
+    }
+  }
+}
+
+// kind 0: element-wise; 1: whole 16-byte vectors; 2: pieces of whole
+// dwords (gather_dword_kernel).  Two tiles per workgroup exist for kinds 1
+// and 2.
+hipError_t launch_gather(int esize, int kind, int tpw, const GatherArgs& a, dim3 grid, uint32_t lds,
                          hipStream_t s) {
   void* args[] = {const_cast<GatherArgs*>(&a)};
-  if (tpw != 1 && !(tpw == 2 && vec)) return hipErrorInvalidValue;
+  if (kind < 0 || kind > 2 || (tpw != 1 && !(tpw == 2 && kind != 0))) return hipErrorInvalidValue;
   const void* fn;
   switch (esize) {
-#define RSX_ES(n)                                                                     \
-  case n:                                                                             \
-    fn = !vec        ? reinterpret_cast<const void*>(&gather_kernel<n, false, 1>)     \
-         : tpw == 2 ? reinterpret_cast<const void*>(&gather_kernel<n, true, 2>)       \
-                    : reinterpret_cast<const void*>(&gather_kernel<n, true, 1>);      \
+#define RSX_ES(n)                                                                                   \
+  case n:                                                                                           \
+    fn = kind == 0   ? reinterpret_cast<const void*>(&gather_kernel<n, false, 1>)                   \
+         : kind == 1 ? (tpw == 2 ? reinterpret_cast<const void*>(&gather_kernel<n, true, 2>)        \
+                                 : reinterpret_cast<const void*>(&gather_kernel<n, true, 1>))       \
+                     : (tpw == 2 ? reinterpret_cast<const void*>(&gather_dword_kernel<n, 2>)        \
+                                 : reinterpret_cast<const void*>(&gather_dword_kernel<n, 1>));      \
     break;
     RSX_ES(1) RSX_ES(2) RSX_ES(4) RSX_ES(8)
 #undef RSX_ES

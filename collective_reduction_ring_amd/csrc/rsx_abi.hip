@@ -262,7 +262,10 @@ rsx_status_t launch_fold_any(int dtype, int op, int world, bool rs, bool vec, Fo
 rsx_status_t launch_gather_any(const void* const* src, void* const* dst, int nranks, size_t n,
                                size_t es, hipStream_t stream, uint64_t groups = 1) {
   const size_t piece_bytes = n * es;
-  bool vec = (piece_bytes % kVecBytes) == 0;
+  // whole dwords: the dwordx4 kernels (dword-aligned loads where the pieces
+  // are not whole vectors, aligned stores)
+  bool vec = (piece_bytes % 4) == 0;
+  const bool whole = (piece_bytes % kVecBytes) == 0;
   bool in_place = true;
   for (int r = 0; r < nranks; ++r) {
     vec = vec && aligned16(src[r]) && aligned16(dst[r]);
@@ -287,7 +290,7 @@ rsx_status_t launch_gather_any(const void* const* src, void* const* dst, int nra
   int tpw = 1;
   uint32_t cap = 8;  // the element-wise kernel runs uncapped
   if (vec) ag_shape(nranks, in_place, &tpw, &cap);
-  return hip_status(launch_gather(static_cast<int>(es), vec, tpw, a,
+  return hip_status(launch_gather(static_cast<int>(es), !vec ? 0 : whole ? 1 : 2, tpw, a,
                                   dim3(static_cast<uint32_t>(xcd_grid((total + tpw - 1) / tpw))),
                                   lds_for_cap(cap), stream));
 }

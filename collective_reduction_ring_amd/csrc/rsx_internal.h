@@ -182,7 +182,8 @@ hipError_t launch_list_u64(int op, int world, const ListArgs& a, dim3 grid, uint
 hipError_t launch_list_i8(int op, int world, const ListArgs& a, dim3 grid, uint32_t lds, hipStream_t s);
 hipError_t launch_list_f32h(int op, int world, const ListArgs& a, dim3 grid, uint32_t lds, hipStream_t s);
 
-hipError_t launch_gather(int esize, bool vec, int tpw, const GatherArgs& a, dim3 grid, uint32_t lds,
+// kind 0: element-wise, 1: whole 16-byte vectors, 2: pieces of whole dwords.
+hipError_t launch_gather(int esize, int kind, int tpw, const GatherArgs& a, dim3 grid, uint32_t lds,
                          hipStream_t s);
 hipError_t launch_multicopy(int esize, const MultiCopyArgs& a, uint32_t lds, hipStream_t s);
 

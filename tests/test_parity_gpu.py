@@ -531,11 +531,14 @@ def test_all_gather_in_place_and_composition():
 @pytest.mark.parametrize("w", [2, 3, 4, 5, 6, 7, 8, 12, 16])
 @pytest.mark.parametrize("in_place", [False, True])
 @pytest.mark.parametrize("caps", [True, False])
-def test_all_gather_large_grids(w, in_place, caps):
+@pytest.mark.parametrize("extra", [4, 3])
+def test_all_gather_large_grids(w, in_place, caps, extra):
     # Pieces of 512 Ki + 4 fp32 (a ragged last tile), thousands of workgroups:
     # every occupancy cap the all-gather uses (in place and out of place,
-    # W = 2..16), and none.
-    n = (1 << 19) + 4
+    # W = 2..16), and none.  With 512 Ki + 3 the pieces sit at offsets that
+    # are not 16-byte multiples in the outputs: an element head, dword-aligned
+    # vector loads and an element tail per piece.
+    n = (1 << 19) + extra
     pieces = inputs(9, w, n, "f32")
     out = [empty(w * n, "f32", fill=0x11) for _ in range(w)]
     if in_place:
@@ -544,7 +547,7 @@ def test_all_gather_large_grids(w, in_place, caps):
         src = [out[k][k * n:(k + 1) * n] for k in range(w)]
     else:
         src = [to_dev(p, "f32") for p in pieces]
-    say(f"ag large grid w={w} in_place={in_place} caps={caps}")
+    say(f"ag large grid w={w} n={n} in_place={in_place} caps={caps}")
     with rsx.occupancy_caps(caps):
         rsx.all_gather(src, out)
     torch.cuda.synchronize()
