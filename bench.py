@@ -236,12 +236,16 @@ def time_from_state(fn, reset, reps: int, warmup: int, torch) -> list:
     return [a.elapsed_time(b) for a, b in zip(st, en)]
 
 
-def capture(fn, torch):
-    """`fn` captured once in a HIP graph (after warm-up calls on a side stream)."""
+def capture(fn, torch, reset=None):
+    """`fn` captured once in a HIP graph (after warm-up calls on a side stream,
+    each after `reset()` when given, so that every call starts from the same
+    state)."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         for _ in range(3):
+            if reset is not None:
+                reset()
             fn()
     torch.cuda.current_stream().wait_stream(side)
     g = torch.cuda.CUDAGraph()
@@ -516,7 +520,7 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
             st = _stat(ms, world * n * 16 + 16 * sum(nnz))
             st.update(k=plan.k, nnz_rank0=nnz[0], nnz_total=sum(nnz), params=kw)
             # the whole call captured in one HIP graph (its ~15 launches replayed at once)
-            graph = capture(plan, torch)
+            graph = capture(plan, torch, reset)
             ms_g = time_from_state(graph.replay, reset, reps, warm, torch)
             st["graph_replay_median_us"] = round(statistics.median(ms_g) * 1e3, 2)
             res[mode] = st
