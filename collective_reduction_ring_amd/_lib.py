@@ -44,6 +44,8 @@ SIGNATURES = {
     "rsx_all_gather": (_I, [_PP, _PP, _I, _SZ, _I, _P]),
     "rsx_all_reduce": (_I, [_PP, _PP, _I, _SZ, _I, _I, _I, _P]),
     "rsx_all_reduce_bucketed": (_I, [_PP, _PP, _I, _SZ, _SZ, _I, _I, _I, _P]),
+    "rsx_all_reduce_bucket": (_I, [_PP, _PP, _I, _SZ, _SZ, _SZ, _I, _I, _I, _P]),
+    "rsx_bucket_count": (_SZ, [_SZ, _SZ]),
     "rsx_fuse_pack": (_I, [_PP, ctypes.POINTER(_SZ), _I, _P, _I, _P]),
     "rsx_fuse_unpack": (_I, [_P, _PP, ctypes.POINTER(_SZ), _I, _I, _P]),
     "rsx_fused_all_reduce": (_I, [_PP, _PP, ctypes.POINTER(_SZ), _I, _I, _I, _I, _I, _P]),

@@ -182,8 +182,9 @@ def all_reduce(inputs, outputs=None, op: str = "sum", algo: str = "ring", stream
 class AllReduceBucketed(AllReduce):
     """A prepared bucketed all-reduce (``rsx_all_reduce_bucketed``): consecutive
     buckets of ``bucket_elems`` elements, each an all-reduce of its own with its
-    own segments, launched in order on one stream ("Distributed primitives",
-    bucketed ring all-reduce)."""
+    own segments, in order on one stream ("Distributed primitives", bucketed
+    ring all-reduce).  When W divides the bucket the full buckets share one
+    launch per pass; the result is the same."""
 
     def __init__(self, inputs, outputs=None, bucket_elems: int = 13_107_200, op: str = "sum",
                  algo: str = "ring", wire: str | None = None):
@@ -197,10 +198,23 @@ class AllReduceBucketed(AllReduce):
         _launch(self, "rsx_all_reduce_bucketed", stream)
 
 
+class _OneBucket(AllReduce):
+    """A prepared ``rsx_all_reduce_bucket``: bucket b of a bucketed all-reduce."""
+
+    def __init__(self, inputs, outputs, bucket_elems: int, bucket: int, op: str, algo: str,
+                 wire: str | None):
+        super().__init__(inputs, outputs, op, algo, wire)
+        self.args = self.args[:4] + (int(bucket_elems), int(bucket)) + self.args[4:]
+        self.fn = L.lib().rsx_all_reduce_bucket
+
+    def __call__(self, stream=None) -> None:
+        _launch(self, "rsx_all_reduce_bucket", stream)
+
+
 def all_reduce_bucketed(inputs, outputs=None, bucket_elems: int = 13_107_200, op: str = "sum",
                         algo: str = "ring", stream=None, wire: str | None = None) -> None:
-    """All-reduce consecutive buckets of ``bucket_elems`` elements, one launch per bucket,
-    in order on one stream ("Distributed primitives", bucketed ring all-reduce).
+    """All-reduce consecutive buckets of ``bucket_elems`` elements in order on one
+    stream ("Distributed primitives", bucketed ring all-reduce).
 
     Each bucket is an all-reduce of its own with its own segment split.
     """
@@ -250,10 +264,8 @@ class BucketedAllReduce:
         if bucket_elems <= 0:
             raise ValueError("bucket_elems must be positive")
         outputs = inputs if outputs is None else outputs
-        n = inputs[0].numel()
-        self.bounds = [(b0, min(b0 + bucket_elems, n)) for b0 in range(0, n, bucket_elems)]
-        self.plans = [AllReduce([t[b0:b1] for t in inputs], [t[b0:b1] for t in outputs], op, algo, wire)
-                      for b0, b1 in self.bounds]
+        nb = L.lib().rsx_bucket_count(inputs[0].numel(), bucket_elems)
+        self.plans = [_OneBucket(inputs, outputs, bucket_elems, b, op, algo, wire) for b in range(nb)]
         self.serial = AllReduceBucketed(inputs, outputs, bucket_elems, op, algo, wire)
         self.device = inputs[0].device
         self.stream = stream if stream is not None else torch.cuda.Stream(device=self.device)

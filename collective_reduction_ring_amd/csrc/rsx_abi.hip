@@ -710,6 +710,22 @@ rsx_status_t all_reduce_launch(const void* const* sendbufs, void* const* recvbuf
                          stream);
 }
 
+// Checks of a bucketed all-reduce (no HIP call): one all-reduce over the
+// whole buffers, the bucket size, W dividing every bucket in the two-pass
+// form, and every bucket's launch grid (the largest bucket's).
+rsx_status_t bucketed_check(const void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
+                            size_t bucket_elems, rsx_dtype_t dtype, rsx_op_t op, rsx_algo_t algo,
+                            bool* nothing) {
+  if (bucket_elems == 0) return RSX_ERR_INVALID_ARGUMENT;
+  rsx_status_t st = all_reduce_check(sendbufs, recvbufs, nranks, count, dtype, op, algo, nothing);
+  if (st != RSX_SUCCESS || *nothing) return st;
+  const size_t w = static_cast<size_t>(nranks);
+  const size_t full = std::min(bucket_elems, count), last = count % bucket_elems;
+  if (algo == RSX_ALGO_RING_SPLIT && (full % w != 0 || last % w != 0)) return RSX_ERR_UNSUPPORTED;
+  if (!all_reduce_grid_ok(nranks, full)) return RSX_ERR_UNSUPPORTED;
+  return RSX_SUCCESS;
+}
+
 }  // namespace
 }  // namespace rsx
 
@@ -808,19 +824,36 @@ rsx_status_t rsx_all_reduce(const void* const* sendbufs, void* const* recvbufs, 
   return all_reduce_launch(sendbufs, recvbufs, nranks, count, dtype, op, algo, stream);
 }
 
+size_t rsx_bucket_count(size_t count, size_t bucket_elems) {
+  return bucket_elems == 0 ? 0 : count / bucket_elems + (count % bucket_elems != 0 ? 1 : 0);
+}
+
+rsx_status_t rsx_all_reduce_bucket(const void* const* sendbufs, void* const* recvbufs, int nranks,
+                                   size_t count, size_t bucket_elems, size_t bucket, rsx_dtype_t dtype,
+                                   rsx_op_t op, rsx_algo_t algo, hipStream_t stream) {
+  bool nothing = false;
+  rsx_status_t st = bucketed_check(sendbufs, recvbufs, nranks, count, bucket_elems, dtype, op, algo, &nothing);
+  if (st != RSX_SUCCESS) return st;
+  if (count > 0 && bucket >= rsx_bucket_count(count, bucket_elems)) return RSX_ERR_INVALID_ARGUMENT;
+  if (nothing) return RSX_SUCCESS;
+  const size_t es = esize_of(dtype);
+  const size_t b0 = bucket * bucket_elems, n = std::min(bucket_elems, count - b0);
+  const void* src[RSX_MAX_RANKS];
+  void* dst[RSX_MAX_RANKS];
+  for (int r = 0; r < nranks; ++r) {
+    src[r] = static_cast<const char*>(sendbufs[r]) + b0 * es;
+    dst[r] = static_cast<char*>(recvbufs[r]) + b0 * es;
+  }
+  return all_reduce_launch(src, dst, nranks, n, dtype, op, algo, stream);
+}
+
 rsx_status_t rsx_all_reduce_bucketed(const void* const* sendbufs, void* const* recvbufs, int nranks,
                                      size_t count, size_t bucket_elems, rsx_dtype_t dtype, rsx_op_t op,
                                      rsx_algo_t algo, hipStream_t stream) {
-  if (bucket_elems == 0) return RSX_ERR_INVALID_ARGUMENT;
   bool nothing = false;
-  rsx_status_t st = all_reduce_check(sendbufs, recvbufs, nranks, count, dtype, op, algo, &nothing);
+  rsx_status_t st = bucketed_check(sendbufs, recvbufs, nranks, count, bucket_elems, dtype, op, algo, &nothing);
   if (st != RSX_SUCCESS || nothing) return st;
-  // The two-pass form needs W to divide every bucket: the full ones and the last.
   const size_t w = static_cast<size_t>(nranks);
-  const size_t full = std::min(bucket_elems, count), last = count % bucket_elems;
-  if (algo == RSX_ALGO_RING_SPLIT && (full % w != 0 || last % w != 0)) return RSX_ERR_UNSUPPORTED;
-  // Every launch's grid is checked before the first one: the largest bucket's.
-  if (!all_reduce_grid_ok(nranks, full)) return RSX_ERR_UNSUPPORTED;
   const size_t es = esize_of(dtype);
   const void* src[RSX_MAX_RANKS];
   void* dst[RSX_MAX_RANKS];

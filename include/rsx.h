@@ -196,6 +196,28 @@ rsx_status_t rsx_all_reduce_bucketed(const void* const* sendbufs, void* const* r
                                      hipStream_t stream);
 
 /*
+ * One bucket of a bucketed all-reduce ["Distributed primitives", In
+ * practice: each bucket is all-reduced as soon as the backward pass has
+ * produced it, on a stream of its own].
+ *
+ * The all-reduce of bucket `bucket` alone, [bucket*bucket_elems,
+ * min((bucket+1)*bucket_elems, count)), with that bucket's own segments and
+ * RSX_ALGO_AUTO choice: the result equals what rsx_all_reduce_bucketed
+ * stores for it.  For callers that enqueue each bucket when its inputs are
+ * ready.  Arguments and validation as rsx_all_reduce_bucketed, on the whole
+ * buffers; bucket >= rsx_bucket_count(count, bucket_elems):
+ * RSX_ERR_INVALID_ARGUMENT (count = 0: nothing to do, RSX_SUCCESS).
+ */
+rsx_status_t rsx_all_reduce_bucket(const void* const* sendbufs, void* const* recvbufs,
+                                   int nranks, size_t count, size_t bucket_elems, size_t bucket,
+                                   rsx_dtype_t dtype, rsx_op_t op, rsx_algo_t algo,
+                                   hipStream_t stream);
+
+/* Buckets of a bucketed all-reduce: ceil(count / bucket_elems); 0 when
+ * bucket_elems is 0. */
+size_t rsx_bucket_count(size_t count, size_t bucket_elems);
+
+/*
  * Tensor-fusion pack [SG fusedSynch(send=false); HV PerformOperation memcpy in].
  *
  * Copies tensors[i] (device, counts[i] elements) to

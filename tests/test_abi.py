@@ -214,6 +214,37 @@ def test_bucketed_all_reduce_validation(lib):
     assert _arb(lib, [A], [A], 1, 1000, 2 ** 63) == 0
 
 
+def test_bucket_count(lib):
+    assert lib.rsx_bucket_count(1000, 100) == 10
+    assert lib.rsx_bucket_count(1001, 100) == 11
+    assert lib.rsx_bucket_count(99, 100) == 1
+    assert lib.rsx_bucket_count(0, 100) == 0
+    assert lib.rsx_bucket_count(1000, 0) == 0
+    assert lib.rsx_bucket_count(2 ** 64 - 1, 2 ** 63) == 2
+
+
+def _ar1(lib, sends, recvs, w, n, bucket_elems, bucket, dt=0, op=0, algo=0):
+    return lib.rsx_all_reduce_bucket(_arr(sends), _arr(recvs), w, n, bucket_elems, bucket, dt, op, algo, None)
+
+
+@fake_ptrs
+def test_single_bucket_validation(lib):
+    # rsx_all_reduce_bucket: the bucketed call's checks on the whole buffers,
+    # then the bucket index (every check before any HIP call).
+    s, r = [A, A + MB], [A + 2 * MB, A + 3 * MB]
+    assert _ar1(lib, s, r, 2, 1000, 0, 0) == 1                             # no bucket size
+    assert _ar1(lib, s, r, 2, 1000, 100, 10) == 1                          # past the last bucket
+    assert _ar1(lib, s, r, 2, 1001, 100, 11) == 1
+    assert _ar1(lib, s, r, 2, 0, 100, 0) == 0                              # nothing to do
+    assert _ar1(lib, s, r, 2, 1000, 100, 3, dt=9) == 2
+    assert _ar1(lib, s, r, 2, 1000, 100, 3, op=7) == 3
+    assert _ar1(lib, s, [A + 2 * MB, A + 2 * MB + 64], 2, 1000, 100, 3) == 5
+    s3, r3 = [A, A + MB, A + 2 * MB], [A + 3 * MB, A + 4 * MB, A + 5 * MB]
+    assert _ar1(lib, s3, r3, 3, 1000, 300, 0, algo=L.RSX_ALGO_RING_SPLIT) == 4  # last bucket of 100
+    assert _ar1(lib, [A], [A], 1, 1000, 7, 142) == 0                       # one rank in place: nothing
+    assert _ar1(lib, [A], [A], 1, 1000, 7, 143) == 1                       # but the index is still checked
+
+
 @fake_ptrs
 def test_pointers_must_be_element_aligned(lib):
     # A buffer that does not start at a multiple of its element size is refused

@@ -855,6 +855,36 @@ def test_all_reduce_bucketed_entry(dtype, op, w, n, bucket, algo, in_place):
         assert_parity(to_host((dev if in_place else out)[r], dtype), want[r], dtype, f"rank {r}")
 
 
+@pytest.mark.parametrize("dtype,op,w,n,bucket,algo", [
+    ("f32", "sum", 8, 5 * 8 * 65536 + 1000, 8 * 65536, "ring"),
+    ("bf16", "avg", 8, 3 * 8192 + 4096 + 8, 8192, "ring"),
+    ("i32", "max", 16, 50_000, 3_000, "auto"),
+    ("f16", "sum", 7, 6 * 7 * 3000 + 5, 7 * 3000, "ring_fused"),
+])
+def test_single_bucket_calls(dtype, op, w, n, bucket, algo):
+    # rsx_all_reduce_bucket, one call per bucket in reverse order (each
+    # bucket's result depends on nothing else), against the oracle's
+    # bucket-by-bucket all-reduce
+    xs = inputs(62, w, n, dtype)
+    dev = [to_dev(x, dtype) for x in xs]
+    out = [empty(n, dtype, fill=0x55) for _ in range(w)]
+    plan = rsx.BucketedAllReduce(dev, out, bucket, op, algo, wire=wire(dtype),
+                                 stream=torch.cuda.current_stream())
+    say(f"single buckets dtype={dtype} op={op} w={w} n={n} bucket={bucket} algo={algo} buckets={len(plan)}")
+    assert len(plan) == -(-n // bucket)
+    for b in reversed(range(len(plan))):
+        plan.ready(b)
+    torch.cuda.synchronize()
+    ref_algo = "naive" if algo == "naive" else "ring"
+    for b0 in range(0, n, bucket):
+        b1 = min(b0 + bucket, n)
+        part = [x[b0:b1] for x in xs]
+        naive = ref_algo == "naive" or (algo == "auto" and (b1 - b0) * ES[dtype] <= RSX_NAIVE_MAX_BYTES)
+        res = (oracle.naive_all_reduce if naive else oracle.all_reduce)(part, op, dtype)
+        for r in range(w):
+            assert_parity(to_host(out[r], dtype)[b0:b1], res[r], dtype, f"rank {r} bucket at {b0}")
+
+
 @pytest.mark.parametrize("algo", ["ring", "ring_split", "ring_fused"])
 def test_all_reduce_bucketed_unaligned(algo):
     # 4-byte offsets: element kernels in both passes, several buckets per launch
@@ -904,7 +934,8 @@ def test_bucket_overlap_on_a_side_stream(dtype, op):
     assert plan.stream != torch.cuda.current_stream() and len(plan) == 4
     a = torch.randn(1024, 1024, device="cuda:0")
     say(f"bucket overlap dtype={dtype} op={op} buckets={len(plan)}")
-    for b, (b0, b1) in enumerate(plan.bounds):
+    for b in range(len(plan)):
+        b0, b1 = b * bucket, min((b + 1) * bucket, n)
         for _ in range(4):
             a = torch.mm(a, a) * 1e-3         # producer busy before bucket b exists
         for r in range(w):
