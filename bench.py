@@ -324,7 +324,7 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
         sample = [x[:2 * bucket].copy() for x in xs]      # the first two buckets, for the oracle
         del xs
         _, out = _arena(torch, torch.bfloat16, world, n)
-        nbuckets = -(-n // bucket)
+        nbuckets = rsx.bucket_count(n, bucket)
 
         def bucketed(algo):
             return rsx.AllReduceBucketed(dev, out, bucket, "avg", algo)
@@ -332,7 +332,8 @@ def other_workload(name: str, args, rsx, wl, torch, np) -> dict:
         step = bucketed("ring")
         res = {"workload": "all-reduce avg bf16 (fp32 accumulate), W=8, 134,217,728/rank, "
                            f"{nbuckets} buckets of <= 25 MiB in sequence on one stream; "
-                           "ring = one pass per bucket",
+                           "ring = RSX_ALGO_RING (two passes at this shape; the full buckets share "
+                           "one launch per pass)",
                "ring": _stat(time_launches(step, reps // 4 or 1, warm, torch), nb)}
         res["ring"]["graph_us_per_step"] = graph_us_per_call(step, 1, 10, torch)
         # The two-pass form (reduce-scatter, then all-gather); the same bits.

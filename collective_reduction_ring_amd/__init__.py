@@ -8,7 +8,7 @@ from .api import (  # noqa: F401
     ALGOS, DTYPES, OPS, AllReduce, AllReduceBucketed, BucketedAllReduce, FusedAllReduce, FusePack, FuseUnpack, ReduceScatter,
     GroupedAllReduce, TensorFusionAllReduce, fusion_groups, fusion_threshold,
     all_gather, all_reduce,
-    all_reduce_bucketed, fuse_pack, fuse_unpack, fused_all_reduce, reduce_scatter,
+    all_reduce_bucketed, bucket_count, fuse_pack, fuse_unpack, fused_all_reduce, reduce_scatter,
     segment_begin, version, SparseAllReduce, sparse_all_reduce, topk_count, SPARSE_MODES,
     occupancy_caps,
 )

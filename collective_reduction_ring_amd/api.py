@@ -211,6 +211,11 @@ class _OneBucket(AllReduce):
         _launch(self, "rsx_all_reduce_bucket", stream)
 
 
+def bucket_count(count: int, bucket_elems: int) -> int:
+    """Buckets of a bucketed all-reduce of ``count`` elements (``rsx_bucket_count``)."""
+    return int(L.lib().rsx_bucket_count(int(count), int(bucket_elems)))
+
+
 def all_reduce_bucketed(inputs, outputs=None, bucket_elems: int = 13_107_200, op: str = "sum",
                         algo: str = "ring", stream=None, wire: str | None = None) -> None:
     """All-reduce consecutive buckets of ``bucket_elems`` elements in order on one
