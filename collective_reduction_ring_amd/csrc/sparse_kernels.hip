@@ -188,8 +188,10 @@ __device__ __forceinline__ bool needs_fallback(const SparseArgs& a, uint32_t r) 
 // Per rank: zero the histograms and the per-tile counts, and set the
 // selection state: cut key 0 with K still to find, no candidate yet.  K = 0
 // selects nothing: the cut key, the gather bound and the guess are then
-// above every key.  NT lanes of a workgroup of the rank.
-template <uint32_t NT>
+// above every key.  NT lanes of a workgroup of the rank.  SAMPLED: the
+// sampling kernel calls it and then sets the gather bound and the guess
+// itself, so those two fields are left alone here (one writer each).
+template <uint32_t NT, bool SAMPLED = false>
 __device__ __forceinline__ void init_rank(const SparseArgs& a, uint32_t r) {
   for (uint32_t p = 0; p < kHistCount; ++p) {
     uint32_t* h = hist_of(a, p, r);
@@ -206,9 +208,11 @@ __device__ __forceinline__ void init_rank(const SparseArgs& a, uint32_t r) {
     const uint32_t none = a.k == 0 ? 0xFFFFFFFFu : 0u;  // K = 0: above every key
     st[kStCut] = none;
     st[kStNeed] = a.k;
-    st[kStBound] = none;
     st[kStCand] = 0;
-    st[kStGuess] = none;
+    if constexpr (!SAMPLED) {
+      st[kStBound] = none;
+      st[kStGuess] = none;
+    }
   }
 }
 
@@ -388,9 +392,9 @@ __global__ __launch_bounds__(kSampleBlock) void sp_sample_kernel(const SparseArg
   __shared__ uint32_t h[kBins];
   __shared__ uint32_t scratch[kWaves];
   const uint32_t r = blockIdx.x;
-  // The rank's initial state first; the barrier orders its stores before
-  // the bound and guess below.
-  init_rank<kSampleBlock>(a, r);
+  // The rank's initial state first (all but the bound and the guess, which
+  // are set below whatever the sample holds).
+  init_rank<kSampleBlock, true>(a, r);
   __syncthreads();
   const SamplePlan p(a);
   if (p.j > p.m) {  // everything is gathered, and guessed sent
@@ -548,7 +552,7 @@ __device__ __forceinline__ void store_residual(float* acc, uint64_t base, uint32
 }
 
 // Top-K gather, one workgroup per tile, against the sampled bound
-// (state[2]).  It forms g = grad + acc, and with an accumulation stores the
+// (kStBound).  It forms g = grad + acc, and with an accumulation stores the
 // residual each entry has if the candidates are exactly the entries sent
 // (g - 0 = g for the rest).  Later kernels read the slots only.
 template <bool ACC>
