@@ -320,6 +320,54 @@ def test_random_configurations(case):
         assert_parity(got[r], want[r], dtype, f"ar rank {r}")
 
 
+def _offset_dev(x, dtype, off):
+    # x on the device starting `off` elements into its allocation
+    base = to_dev(np.concatenate([np.zeros(off, dtype=x.dtype), x]), dtype)
+    return base[off:]
+
+
+@pytest.mark.parametrize("case", range(30))
+def test_random_bucketed_and_all_gather(case):
+    # Seeded random mixes for the bucketed all-reduce (bucket sizes that W
+    # divides or not, every algorithm, in place or not, buffers 0, 1 or 4
+    # elements past an aligned address) and the all-gather (random piece
+    # lengths and offsets).
+    rng = np.random.default_rng((73, case))
+    w = int(rng.integers(1, 17))
+    dtype = str(rng.choice(ALL_DTYPES))
+    op = str(rng.choice(OPS))
+    te = tile_elems(w, dtype)
+    bucket = int(rng.integers(1, 4 * te)) * (w if rng.random() < 0.5 else 1)
+    count = int(rng.integers(1, 5)) * bucket + int(rng.integers(0, bucket))
+    algo = str(rng.choice(["ring", "ring_fused", "naive", "auto"]))
+    in_place = bool(rng.random() < 0.5)
+    off = int(rng.choice([0, 1, 4]))
+    xs = inputs(900 + case, w, count, dtype)
+    dev = [_offset_dev(x, dtype, off) for x in xs]
+    out = None if in_place else [_offset_dev(np.zeros_like(x), dtype, off) for x in xs]
+    say(f"random {case}: bucketed w={w} dtype={dtype} op={op} count={count} bucket={bucket} algo={algo} "
+        f"in_place={in_place} off={off}")
+    rsx.all_reduce_bucketed(dev, out, bucket, op, algo, wire=wire(dtype))
+    torch.cuda.synchronize()
+    for r in range(w):
+        got = to_host((dev if in_place else out)[r], dtype)
+        for b0 in range(0, count, bucket):
+            b1 = min(b0 + bucket, count)
+            naive = algo == "naive" or (algo == "auto" and (b1 - b0) * ES[dtype] <= RSX_NAIVE_MAX_BYTES)
+            want = (oracle.naive_all_reduce if naive else oracle.all_reduce)([x[b0:b1] for x in xs], op, dtype)
+            assert_parity(got[b0:b1], want[r], dtype, f"rank {r} bucket at {b0}")
+    n = int(rng.integers(1, 3 * te))
+    pieces = inputs(950 + case, w, n, dtype)
+    src = [_offset_dev(p, dtype, off) for p in pieces]
+    dst = [_offset_dev(np.zeros(w * n, dtype=pieces[0].dtype), dtype, int(rng.choice([0, 1, 4]))) for _ in range(w)]
+    say(f"random {case}: ag w={w} dtype={dtype} n={n} off={off}")
+    rsx.all_gather(src, dst)
+    torch.cuda.synchronize()
+    want = oracle.all_gather(pieces)
+    for r in range(w):
+        assert_parity(to_host(dst[r], dtype), want[r], dtype, f"ag rank {r}")
+
+
 @pytest.mark.parametrize("count", [1, 2, 3, 7, 8, 9, 15, 16, 17, 31, 33, 100, 1023])
 @pytest.mark.parametrize("w", [2, 4, 16])
 def test_all_reduce_small_and_ragged(w, count):
