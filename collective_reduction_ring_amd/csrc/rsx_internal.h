@@ -132,8 +132,8 @@ inline uint64_t copy_tiles(const void* dst, uint64_t bytes) {
 // the tensors themselves.  Each launch carries up to kListPieces pieces; a
 // piece is the part of one tensor that lies in one segment of the fused
 // layout, so its fold order is uniform.
-constexpr int kListPtrs = 256;   // pointer slots per launch, 2*W per tensor
-constexpr int kListPieces = 48;  // pieces per launch
+constexpr int kListPtrs = 288;   // pointer slots per launch, 2*W per tensor (W in place)
+constexpr int kListPieces = 63;  // pieces per launch (the two limits fill the 4 KiB of kernel arguments)
 struct ListPiece {
   uint64_t lo, hi;   // tensor-local element range
   uint32_t tensor;   // the tensor's pointers start at slot tensor * 2W (tensor * W in place)
@@ -150,6 +150,7 @@ struct ListArgs {
   // at [t*2W + W, t*2W + 2W); in place, sources only, at [t*W, t*W + W).
   void* ptr[kListPtrs];
 };
+static_assert(sizeof(ListArgs) <= 4096, "a tensor-list launch must fit the kernel arguments");
 
 // Launchers, one per dtype translation unit.  `rs` selects the reduce-scatter
 // store (block k to dst[k]) over the all-reduce store (every element to every
