@@ -38,12 +38,15 @@
  *   - Every buffer must start at a multiple of its element size (4 for
  *     fp32, 2 for bf16, ...); any other address returns
  *     RSX_ERR_INVALID_ARGUMENT.  Buffers of 16-byte-aligned address take the
- *     dwordx4 kernels; other element-aligned addresses are correct but slower.
+ *     dwordx4 kernels (for reduce-scatter blocks and all-gather pieces whose
+ *     byte length is a multiple of 4, with dword-aligned loads where they are
+ *     not whole 16-byte vectors); other element-aligned addresses are correct
+ *     but slower.
  *   - Bit-exact means equal bit patterns, except that NaN payloads are not
  *     specified: where the result is a NaN, any NaN is correct (the pages fix
  *     no NaN propagation rule; bf16 rounding quiets a NaN as sign|0x7FC0).
  *   - The dwordx4 reduction and gather kernels reserve LDS they do not use
- *     (up to 53 KiB per workgroup) to limit how many of their workgroups
+ *     (up to 96 KiB per workgroup) to limit how many of their workgroups
  *     share a CU, unless the calling thread turned that off with
  *     rsx_set_occupancy_caps (for launches that overlap other kernels).
  */
