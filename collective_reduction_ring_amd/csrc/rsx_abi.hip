@@ -62,7 +62,8 @@ bool valid_op(int op) { return op >= RSX_SUM && op <= RSX_PROD; }
 // workgroups resident per CU.  Measured best caps (fp32, 256 MiB per rank,
 // W = 2..16; W = 8 reduce-scatter 381 -> 362-371 us, one-pass all-reduce
 // 805 -> 725-732 us, all-gather 426 -> 380-383 us):
-//   reduce-scatter (W+1 streams per workgroup): 8 at W <= 2, 5 up to W = 10, 3 above;
+//   reduce-scatter (W+1 streams per workgroup): 8 at W <= 2, 5 up to W = 9
+//     (from W = 10 it runs in pairs, two per CU: rs_pairs);
 //   all-reduce, one pass (2W streams): 8 at W = 1, 5 at W = 2, 3 from W = 3;
 //   all-gather, every piece in place (1 + (W-1)): 8 at W <= 2, 6 at W = 4, 6, 8,
 //     otherwise 5 up to W = 9, 3 above;
@@ -138,7 +139,7 @@ void ag_shape(int w, bool in_place, int* tpw, uint32_t* cap) {
   *tpw = 1;
   *cap = ag_cap(w, in_place);
 }
-uint32_t rs_cap(int w) { return w <= 2 ? 8u : w <= 10 ? 5u : 3u; }
+uint32_t rs_cap(int w) { return w <= 2 ? 8u : 5u; }  // W >= 10 runs in pairs (rs_pairs)
 uint32_t ar_cap(int w) { return w <= 1 ? 8u : w == 2 ? 5u : 3u; }
 
 // Per element type launchers (one translation unit each).
