@@ -254,6 +254,49 @@ def test_two_pass_graph_capture_replays():
             assert_parity(to_host(out[r], "bf16"), want[r], "bf16", f"replay {rep} rank {r}")
 
 
+@pytest.mark.parametrize("kind", ["bucketed", "gather_dword"])
+def test_graph_capture_replays_grouped_buckets_and_dword_gather(kind):
+    # The grouped bucket launches (W divides the bucket: one launch per pass
+    # over the full buckets, then the last bucket) and the all-gather of
+    # pieces that are whole dwords but not whole vectors, captured in a HIP
+    # graph and replayed with eager work in between.
+    w = 8
+    if kind == "bucketed":
+        bucket = 8 * 5000
+        n = 3 * bucket + 8 * 123
+        xs = inputs(27, w, n, "bf16")
+        dev = [to_dev(x, "bf16") for x in xs]
+        out = [empty(n, "bf16") for _ in range(w)]
+        plan = rsx.AllReduceBucketed(dev, out, bucket, "avg", "ring_split")
+        want = oracle.bucketed_all_reduce(xs, bucket, "avg", "bf16")
+        dt = "bf16"
+    else:
+        n = 4096 + 3
+        pieces = inputs(28, w, n, "f32")
+        src = [to_dev(p, "f32") for p in pieces]
+        out = [empty(w * n, "f32") for _ in range(w)]
+        plan = lambda: rsx.all_gather(src, out)  # noqa: E731
+        want = oracle.all_gather(pieces)
+        dt = "f32"
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    say(f"graph capture {kind}")
+    with torch.cuda.graph(g):
+        plan()
+    for rep in range(4):
+        for o in out:
+            o.fill_(3.0)                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for r in range(w):
+            assert_parity(to_host(out[r], dt), want[r], dt, f"replay {rep} rank {r}")
+
+
 def _with_ieee_specials(xs, dtype, seed):
     """Normal data with IEEE specials planted: +-inf, NaN, +-0, the smallest
     subnormal and values near the top of the range (sums and products then
